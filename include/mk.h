@@ -1,0 +1,183 @@
+/*
+ * mk.h -- C ABI of the persistent decode megakernel for MI355X (gfx950).
+ *
+ * One call of mk_decode_step runs one decode step of a Llama-style decoder
+ * (every layer, then the LM head) for a batch of sequences in ONE persistent
+ * kernel launch.  The method is the GPU interpreter of the megakernel chapter
+ * "L'interpréteur sur GPU": each compute unit's workgroup runs a queue of
+ * instructions that the host scheduled before launch (section 3.2), drawn
+ * from seven fused instructions (table of section 3.2): RMSNorm + QKV + RoPE,
+ * attention, attention reduction, O-projection + residual, RMSNorm +
+ * up/gate + SiLU, down-projection + residual, RMSNorm + LM head.  Kernel
+ * boundaries are replaced by counters in global memory (section 3.4) and the
+ * next instruction's weights stream into a paged on-chip buffer while the
+ * current one finishes (section 3.3).
+ *
+ * Conventions for every entry point:
+ *   - All pointers marked "device" are HIP device pointers on the device that
+ *     was current when mk_create ran; "host" pointers are ordinary memory.
+ *   - Integer status: 0 = MK_OK, negative = error (see MK_ERR_*).  Errors a
+ *     host check can find are returned synchronously and nothing is launched.
+ *   - The library never keeps a pointer to caller host memory after a call
+ *     returns, and never writes caller device memory except where stated.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define MK_OK                   0
+#define MK_ERR_INVALID_ARG     (-1)  /* null pointer, out-of-range argument   */
+#define MK_ERR_UNSUPPORTED     (-2)  /* shape the decomposition cannot express */
+#define MK_ERR_OOM             (-3)  /* device allocation failed              */
+#define MK_ERR_HIP             (-4)  /* a HIP runtime call failed             */
+#define MK_ERR_NOT_CORESIDENT  (-5)  /* the grid cannot be co-resident        */
+#define MK_ERR_NO_DEVICE       (-6)  /* no usable GPU                         */
+#define MK_ERR_DEVICE_TIMEOUT  (-10) /* a counter wait exceeded the watchdog  */
+#define MK_ERR_BAD_TOKEN       (-11) /* tokens[b] outside [0, vocab)          */
+#define MK_ERR_BAD_POSITION    (-12) /* positions[b] outside [0, max_seq)     */
+
+/* ---- flags ------------------------------------------------------------- */
+#define MK_FLAG_TRACE    1u   /* record per-instruction timestamps           */
+
+/* ---- model and schedule configuration ---------------------------------- */
+/* All sizes in elements.  The model is a pre-norm Llama-style decoder with
+ * grouped-query attention, SwiGLU FFN and half-split RoPE; qk_norm adds a
+ * per-head RMSNorm on q and k (Qwen3-style). */
+typedef struct mk_config {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+  float   rms_eps, rope_theta;
+  int32_t tied_embeddings;   /* 1: LM head is the embedding matrix          */
+  int32_t qk_norm;           /* 1: per-head q/k RMSNorm before RoPE          */
+  int32_t max_batch;         /* capacity of kv_cache and scratch (sequences) */
+  int32_t max_seq;           /* KV slots per sequence                        */
+  int32_t mlp_chunks;        /* counters on the up/gate -> down edge, 0 = 4  */
+  int32_t kv_splits;         /* attention splits per (seq, KV head), 0 = auto*/
+  int32_t num_cus;           /* workgroups (one per CU), 0 = every CU        */
+  int32_t watchdog_ms;       /* bound on any single wait, 0 = 2000 ms        */
+  uint32_t flags;            /* MK_FLAG_*                                    */
+} mk_config;
+
+/* Device pointers to bf16 weights, row-major [out][in] (nn.Linear layout).
+ * Norm weights are [hidden] (q_norm/k_norm: [head_dim]). */
+typedef struct mk_layer_weights {
+  const void *attn_norm, *wq, *wk, *wv;
+  const void *q_norm, *k_norm;          /* NULL unless qk_norm              */
+  const void *wo, *ffn_norm, *w_gate, *w_up, *w_down;
+} mk_layer_weights;
+
+typedef struct mk_weights {
+  const void *embed;                    /* [vocab][hidden]                  */
+  const void *final_norm;               /* [hidden]                         */
+  const void *lm_head;                  /* [vocab][hidden]; NULL iff tied   */
+  const mk_layer_weights *layers;       /* host array of n_layers entries   */
+} mk_weights;
+
+typedef struct mk_handle mk_handle;
+
+/* mk_create -- validate the configuration, query the device, allocate the
+ * library's scratch (counters, activations, partials, RoPE table, queues)
+ * and build the instruction schedule (chapter 3, section 3.2: queues are
+ * planned on the host before launch).
+ *   cfg, w  : host pointers, read during the call only.  The weight device
+ *             pointers inside must stay valid and unmodified until
+ *             mk_destroy; the library reads them in place and never copies,
+ *             repacks or writes them.
+ *   out     : receives the handle (NULL on error).
+ * Errors: MK_ERR_INVALID_ARG, MK_ERR_UNSUPPORTED, MK_ERR_NO_DEVICE,
+ *         MK_ERR_OOM, MK_ERR_HIP, MK_ERR_NOT_CORESIDENT. */
+int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out);
+
+/* mk_decode_step -- one decode step for sequences b < batch, as ONE kernel
+ * launch on `stream` (asynchronous; the call returns after enqueueing).
+ *   tokens    : device int32 [batch], the token fed at this step.
+ *   positions : device int32 [batch], the KV slot of that token; slots
+ *               0..positions[b]-1 must already hold the sequence's K/V.
+ *   kv_cache  : device bf16 [n_layers][2][max_batch][n_kv_heads][max_seq]
+ *               [head_dim] (index 0 = K after RoPE, 1 = V).  The step writes
+ *               slot positions[b] of every layer for every b < batch and
+ *               nothing else.
+ *   logits    : device fp32 [batch][vocab], fully written.
+ *   stream    : hipStream_t (NULL = the null stream).
+ * One step may be in flight per handle; stream order serialises steps.
+ * The handle is not thread-safe.  Device-side errors (watchdog, bad token or
+ * position) are reported by mk_sync_status after the stream is synchronised.
+ * Errors returned here: MK_ERR_INVALID_ARG (null pointer, batch outside
+ * [1, max_batch]), MK_ERR_UNSUPPORTED, MK_ERR_HIP, MK_ERR_OOM. */
+int mk_decode_step(mk_handle *h, int32_t batch, const int32_t *tokens,
+                   const int32_t *positions, void *kv_cache, float *logits,
+                   void *stream);
+
+/* mk_sync_status -- synchronise the device and return the first device-side
+ * error of the steps since the last call (MK_OK if none).  After an error
+ * the library re-zeroes its counters so the next step starts clean; a
+ * decode step is idempotent (it rewrites slot p and the logits), so the
+ * caller may simply run it again. */
+int mk_sync_status(mk_handle *h);
+
+/* mk_destroy -- free everything mk_create allocated.  NULL-safe.  The
+ * caller must have synchronised any stream the handle was used on. */
+void mk_destroy(mk_handle *h);
+
+/* mk_strerror -- static text for a status code (never NULL). */
+const char *mk_strerror(int code);
+
+/* ---- host-only planning and diagnostics --------------------------------- */
+
+/* Summary of a schedule built for `num_cus` workgroups without touching any
+ * GPU. */
+typedef struct mk_plan_report {
+  int32_t num_cus, batch, kv_splits, mlp_chunks;
+  int32_t n_instr;            /* descriptors over all queues                 */
+  int32_t n_groups;           /* counter groups                              */
+  int32_t n_pages;            /* 16 KB weight pages over all queues          */
+  int32_t max_queue;          /* longest per-CU queue                        */
+  int64_t weight_bytes;       /* bf16 weight bytes streamed per step         */
+  int64_t max_cu_bytes;       /* largest per-CU weight stream                */
+  int32_t sim_runs;           /* interleavings simulated                     */
+  int32_t sim_errors;         /* missing dependencies or deadlocks found     */
+  char    msg[256];           /* first error found, if any                   */
+} mk_plan_report;
+
+/* mk_plan_check -- build the schedule for (cfg, batch) on `num_cus`
+ * workgroups, validate it statically (every read is covered by a wait on
+ * every writer of that data; counter targets match their producers) and run
+ * `sim_runs` seeded interleavings of the per-CU queues that respect only the
+ * counter waits (some adversarial: one CU delayed, stage-reversed
+ * priorities), checking that every read sees its producers finished and that
+ * no interleaving deadlocks.  `corrupt` != 0 deliberately breaks the plan
+ * (1: drop a signal, 2: lower a wait target, 3: drop a wait) so tests can
+ * check that the validator catches it.  Host only; no GPU needed.
+ * Returns MK_OK if the plan is valid, MK_ERR_UNSUPPORTED for shapes the
+ * decomposition rejects, MK_ERR_INVALID_ARG otherwise; rep is filled. */
+int mk_plan_check(const mk_config *cfg, int32_t batch, int32_t num_cus,
+                  int32_t sim_runs, int32_t corrupt, uint64_t seed,
+                  mk_plan_report *rep);
+
+/* Internal activation buffers, for stage-by-stage comparison in tests. */
+#define MK_BUF_H      1   /* fp32 [2L+1][max_batch][hidden]: index 2l+1 is the
+                             residual after attention of layer l, 2l+2 after
+                             its FFN (index 0 unused)                         */
+#define MK_BUF_Q      2   /* fp32 [L][max_batch][n_q][head_dim], after RoPE    */
+#define MK_BUF_ATTN   3   /* fp32 [L][max_batch][n_q*head_dim]                 */
+#define MK_BUF_A      4   /* fp32 [L][max_batch][ffn_dim], SiLU(gate)*up       */
+#define MK_BUF_TRACE  5   /* uint64 trace records (MK_FLAG_TRACE)              */
+
+/* mk_get_buffer -- device pointer and size in bytes of an internal buffer.
+ * The memory belongs to the library; read it only after the step that wrote
+ * it has completed.  Returns MK_ERR_INVALID_ARG for an unknown id. */
+int mk_get_buffer(mk_handle *h, int32_t which, void **ptr, size_t *bytes);
+
+/* mk_version -- ABI version of this header (major*100 + minor). */
+int mk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

@@ -1,0 +1,62 @@
+"""Build the C-ABI library ``_lib/libmk.so`` in-tree for gfx950.
+
+Device code is compiled with hipcc for gfx950 only; the host-side scheduler
+and ABI are plain C++ (g++) against the HIP runtime headers.  Packed fp32
+instructions are disabled for all device code.
+
+    python -m persistent_interpreter_amd.build
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+OUT_DIR = os.path.join(HERE, "_lib")
+LIB = os.path.join(OUT_DIR, "libmk.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+ARCH = "gfx950"
+
+DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__",
+              f"-I{ROCM}/include", "-Wall", "-Wno-unused-function"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                       text=True)
+    out = "\n".join(l for l in r.stdout.splitlines()
+                    if "packed-fp32-ops" not in l and "unknown target feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the library; returns its path."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    objs = []
+    k_obj = os.path.join(OUT_DIR, "mk_kernel.o")
+    _run([HIPCC, *DEVICE_FLAGS, "-c", os.path.join(CSRC, "mk_kernel.hip"),
+          "-o", k_obj])
+    objs.append(k_obj)
+    for src in ("mk_sched.cpp", "mk_abi.cpp"):
+        o = os.path.join(OUT_DIR, src.replace(".cpp", ".o"))
+        _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", o])
+        objs.append(o)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp,
+          f"-L{ROCM}/lib", "-lamdhip64"])
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

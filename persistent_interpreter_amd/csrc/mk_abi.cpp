@@ -1,0 +1,356 @@
+// mk_abi.cpp -- the C ABI of include/mk.h: configuration checks, device
+// buffers, per-batch plans and the single launch per decode step.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_plan.hpp"
+#include "mk_sched.hpp"
+
+namespace mk {
+hipError_t kernel_setup(int *blocks_per_cu);
+hipError_t kernel_launch(const Args &a, int grid, hipStream_t stream);
+}  // namespace mk
+
+using namespace mk;
+
+namespace {
+
+struct DevPlan {
+  Plan plan;
+  Instr *d_instr = nullptr;
+  uint32_t *d_qoff = nullptr;
+  Wait *d_waits = nullptr;
+  uint64_t *d_rowtab = nullptr;
+  uint32_t *d_ctr = nullptr;
+  uint32_t *d_target = nullptr;
+  float *d_part = nullptr;
+  size_t ctr_bytes = 0;
+  uint32_t epoch = 0;
+};
+
+template <class T>
+int dev_alloc(T **p, size_t bytes) {
+  if (bytes == 0) bytes = 16;
+  if (hipMalloc((void **)p, bytes) != hipSuccess) {
+    *p = nullptr;
+    return MK_ERR_OOM;
+  }
+  return MK_OK;
+}
+
+template <class T>
+int upload(T **p, const std::vector<T> &v) {
+  int rc = dev_alloc(p, v.size() * sizeof(T));
+  if (rc) return rc;
+  if (!v.empty() && hipMemcpy(*p, v.data(), v.size() * sizeof(T), hipMemcpyHostToDevice) != hipSuccess)
+    return MK_ERR_HIP;
+  return MK_OK;
+}
+
+void free_plan(DevPlan &p) {
+  hipFree(p.d_instr);
+  hipFree(p.d_qoff);
+  hipFree(p.d_waits);
+  hipFree(p.d_rowtab);
+  hipFree(p.d_ctr);
+  hipFree(p.d_target);
+  hipFree(p.d_part);
+}
+
+int check_config(const mk_config *c, std::string &err) {
+  if (!c) { err = "null config"; return MK_ERR_INVALID_ARG; }
+  if (c->n_layers < 1 || c->hidden < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1 ||
+      c->ffn_dim < 1 || c->vocab < 1 || c->max_batch < 1 || c->max_seq < 1) {
+    err = "every size must be >= 1";
+    return MK_ERR_INVALID_ARG;
+  }
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) { err = "bad rms_eps or rope_theta"; return MK_ERR_INVALID_ARG; }
+  if (c->n_q_heads % c->n_kv_heads) { err = "n_q_heads must be a multiple of n_kv_heads"; return MK_ERR_UNSUPPORTED; }
+  if (c->head_dim != 64 && c->head_dim != 128) { err = "head_dim must be 64 or 128"; return MK_ERR_UNSUPPORTED; }
+  if (c->n_q_heads / c->n_kv_heads > kNCW) { err = "at most 8 query heads per KV head"; return MK_ERR_UNSUPPORTED; }
+  if (c->hidden % 8 || c->ffn_dim % 8) { err = "hidden and ffn_dim must be multiples of 8"; return MK_ERR_UNSUPPORTED; }
+  if (c->kv_splits > kMaxSplits || c->kv_splits < 0) { err = "kv_splits must be in [0, 64]"; return MK_ERR_UNSUPPORTED; }
+  if (c->mlp_chunks < 0 || c->num_cus < 0 || c->watchdog_ms < 0) { err = "negative knob"; return MK_ERR_INVALID_ARG; }
+  if ((int64_t)c->vocab * c->hidden >= (1ll << 40)) { err = "model too large"; return MK_ERR_UNSUPPORTED; }
+  return MK_OK;
+}
+
+}  // namespace
+
+struct mk_handle {
+  mk_config cfg;
+  int device = 0;
+  int num_cus = 0;
+  std::vector<mk_layer_weights> layers;
+  mk_weights w;
+  DevCtx hctx;
+  DevCtx *d_ctx = nullptr;
+  DevLayer *d_layers = nullptr;
+  float *h_buf = nullptr, *q_buf = nullptr, *attn_buf = nullptr, *a_buf = nullptr, *rope = nullptr;
+  uint32_t *status = nullptr;
+  size_t h_bytes = 0, q_bytes = 0, attn_bytes = 0, a_bytes = 0;
+  std::map<int, std::unique_ptr<DevPlan>> plans;
+  bool error_pending = false;
+};
+
+extern "C" {
+
+int mk_version(void) { return 100; }
+
+const char *mk_strerror(int code) {
+  switch (code) {
+    case MK_OK: return "ok";
+    case MK_ERR_INVALID_ARG: return "invalid argument";
+    case MK_ERR_UNSUPPORTED: return "unsupported shape or configuration";
+    case MK_ERR_OOM: return "device allocation failed";
+    case MK_ERR_HIP: return "HIP runtime call failed";
+    case MK_ERR_NOT_CORESIDENT: return "the persistent grid cannot be co-resident";
+    case MK_ERR_NO_DEVICE: return "no usable GPU";
+    case MK_ERR_DEVICE_TIMEOUT: return "a counter wait exceeded the watchdog";
+    case MK_ERR_BAD_TOKEN: return "token id outside [0, vocab)";
+    case MK_ERR_BAD_POSITION: return "position outside [0, max_seq)";
+    default: return "unknown status code";
+  }
+}
+
+int mk_plan_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int32_t sim_runs, int32_t corrupt,
+                  uint64_t seed, mk_plan_report *rep) {
+  std::string err;
+  if (rep) std::memset(rep, 0, sizeof *rep);
+  int rc = check_config(cfg, err);
+  if (rc == MK_OK && (batch < 1 || batch > cfg->max_batch || num_cus < 1 || sim_runs < 0)) {
+    err = "batch, num_cus or sim_runs out of range";
+    rc = MK_ERR_INVALID_ARG;
+  }
+  Plan plan;
+  if (rc == MK_OK) rc = build_plan(*cfg, batch, num_cus, plan, err);
+  if (rc != MK_OK) {
+    if (rep) std::snprintf(rep->msg, sizeof rep->msg, "%s", err.c_str());
+    return rc;
+  }
+  if (rep) {
+    rep->num_cus = num_cus;
+    rep->batch = batch;
+    rep->kv_splits = plan.n_split;
+    rep->mlp_chunks = plan.mlp_chunks;
+    rep->n_instr = (int32_t)plan.instr.size();
+    rep->n_groups = plan.n_groups;
+    rep->n_pages = plan.n_pages;
+    int mq = 0;
+    for (int c = 0; c < num_cus; ++c) mq = std::max(mq, (int)(plan.q_off[c + 1] - plan.q_off[c]));
+    rep->max_queue = mq;
+    rep->weight_bytes = plan.weight_bytes;
+    rep->max_cu_bytes = plan.max_cu_bytes;
+  }
+  return check_plan(*cfg, plan, sim_runs, corrupt, seed, rep);
+}
+
+int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out) {
+  if (!out) return MK_ERR_INVALID_ARG;
+  *out = nullptr;
+  std::string err;
+  int rc = check_config(cfg, err);
+  if (rc) return rc;
+  if (!w || !w->embed || !w->final_norm || !w->layers) return MK_ERR_INVALID_ARG;
+  if (!cfg->tied_embeddings && !w->lm_head) return MK_ERR_INVALID_ARG;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const mk_layer_weights &ly = w->layers[l];
+    if (!ly.attn_norm || !ly.wq || !ly.wk || !ly.wv || !ly.wo || !ly.ffn_norm || !ly.w_gate || !ly.w_up ||
+        !ly.w_down)
+      return MK_ERR_INVALID_ARG;
+    if (cfg->qk_norm && (!ly.q_norm || !ly.k_norm)) return MK_ERR_INVALID_ARG;
+  }
+  if (cfg->qk_norm) return MK_ERR_UNSUPPORTED;  // per-head q/k norm: not built yet
+
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return MK_ERR_NO_DEVICE;
+  auto h = std::make_unique<mk_handle>();
+  h->cfg = *cfg;
+  if (hipGetDevice(&h->device) != hipSuccess) return MK_ERR_HIP;
+  int cus = 0, coop = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess ||
+      hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, h->device) != hipSuccess)
+    return MK_ERR_HIP;
+  if (!coop) return MK_ERR_NOT_CORESIDENT;
+  h->num_cus = cfg->num_cus > 0 ? std::min(cfg->num_cus, cus) : cus;
+  int per_cu = 0;
+  if (kernel_setup(&per_cu) != hipSuccess) return MK_ERR_HIP;
+  if (per_cu < 1) return MK_ERR_NOT_CORESIDENT;
+
+  h->layers.assign(w->layers, w->layers + cfg->n_layers);
+  h->w = *w;
+  h->w.layers = h->layers.data();
+
+  const int L = cfg->n_layers, MB = cfg->max_batch, H = cfg->hidden, nq = cfg->n_q_heads;
+  const int hd = cfg->head_dim, F = cfg->ffn_dim, S = cfg->max_seq;
+  h->h_bytes = (size_t)(2 * L + 1) * MB * H * 4;
+  h->q_bytes = (size_t)L * MB * nq * hd * 4;
+  h->attn_bytes = h->q_bytes;
+  h->a_bytes = (size_t)L * MB * F * 4;
+  std::vector<float> rope((size_t)S * (hd / 2) * 2);
+  for (int p = 0; p < S; ++p)
+    for (int i = 0; i < hd / 2; ++i) {
+      // angle p * theta^(-2i/hd) in double, cos/sin rounded to float
+      double ang = (double)p * std::pow((double)cfg->rope_theta, -2.0 * i / (double)hd);
+      rope[((size_t)p * (hd / 2) + i) * 2] = (float)std::cos(ang);
+      rope[((size_t)p * (hd / 2) + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  std::vector<DevLayer> dl(L);
+  for (int l = 0; l < L; ++l) {
+    const mk_layer_weights &s = w->layers[l];
+    dl[l] = DevLayer{(const uint16_t *)s.attn_norm, (const uint16_t *)s.wq, (const uint16_t *)s.wk,
+                     (const uint16_t *)s.wv, (const uint16_t *)s.q_norm, (const uint16_t *)s.k_norm,
+                     (const uint16_t *)s.wo, (const uint16_t *)s.ffn_norm, (const uint16_t *)s.w_gate,
+                     (const uint16_t *)s.w_up, (const uint16_t *)s.w_down};
+  }
+  if ((rc = dev_alloc(&h->h_buf, h->h_bytes)) || (rc = dev_alloc(&h->q_buf, h->q_bytes)) ||
+      (rc = dev_alloc(&h->attn_buf, h->attn_bytes)) || (rc = dev_alloc(&h->a_buf, h->a_bytes)) ||
+      (rc = upload(&h->rope, rope)) || (rc = dev_alloc(&h->status, 256)) || (rc = upload(&h->d_layers, dl))) {
+    mk_destroy(h.release());
+    return rc;
+  }
+  if (hipMemset(h->status, 0, 256) != hipSuccess || hipMemset(h->h_buf, 0, h->h_bytes) != hipSuccess) {
+    mk_destroy(h.release());
+    return MK_ERR_HIP;
+  }
+  DevCtx &c = h->hctx;
+  std::memset(&c, 0, sizeof c);
+  c.L = L; c.H = H; c.nq = nq; c.nkv = cfg->n_kv_heads; c.hd = hd; c.F = F; c.V = cfg->vocab;
+  c.G = nq / cfg->n_kv_heads; c.qk_norm = cfg->qk_norm; c.tied = cfg->tied_embeddings;
+  c.max_batch = MB; c.max_seq = S; c.num_cus = h->num_cus;
+  c.eps = cfg->rms_eps;
+  c.attn_scale = (float)(1.0 / std::sqrt((double)hd));
+  c.watchdog_ticks = (int64_t)(cfg->watchdog_ms > 0 ? cfg->watchdog_ms : 2000) * 100000;
+  c.embed = (const uint16_t *)w->embed;
+  c.final_norm = (const uint16_t *)w->final_norm;
+  c.lm_head = (const uint16_t *)w->lm_head;
+  c.layers = h->d_layers;
+  c.h_buf = h->h_buf; c.q_buf = h->q_buf; c.attn_buf = h->attn_buf; c.a_buf = h->a_buf;
+  c.rope = h->rope;
+  c.status = h->status;
+  c.trace = nullptr;
+  c.ring_pages = kRingPages;
+  c.flags = (int32_t)cfg->flags;
+  std::vector<DevCtx> one(1, c);
+  if ((rc = upload(&h->d_ctx, one))) {
+    mk_destroy(h.release());
+    return rc;
+  }
+  *out = h.release();
+  return MK_OK;
+}
+
+static int get_plan(mk_handle *h, int batch, DevPlan **out) {
+  auto it = h->plans.find(batch);
+  if (it != h->plans.end()) {
+    *out = it->second.get();
+    return MK_OK;
+  }
+  auto dp = std::make_unique<DevPlan>();
+  std::string err;
+  int rc = build_plan(h->cfg, batch, h->num_cus, dp->plan, err);
+  if (rc) return rc;
+  resolve_streams(h->cfg, h->w, dp->plan);
+  Plan &P = dp->plan;
+  dp->ctr_bytes = (size_t)P.n_groups * kXcds * kCtrStride * 4;
+  const size_t part = (size_t)h->cfg.n_layers * h->cfg.max_batch * h->cfg.n_q_heads * P.n_split *
+                      (h->cfg.head_dim + 4) * 4;
+  if ((rc = upload(&dp->d_instr, P.instr)) || (rc = upload(&dp->d_qoff, P.q_off)) ||
+      (rc = upload(&dp->d_waits, P.waits)) || (rc = upload(&dp->d_rowtab, P.rowtab)) ||
+      (rc = upload(&dp->d_target, P.grp_target)) || (rc = dev_alloc(&dp->d_ctr, dp->ctr_bytes)) ||
+      (rc = dev_alloc(&dp->d_part, part))) {
+    free_plan(*dp);
+    return rc;
+  }
+  if (hipMemset(dp->d_ctr, 0, dp->ctr_bytes) != hipSuccess) {
+    free_plan(*dp);
+    return MK_ERR_HIP;
+  }
+  *out = dp.get();
+  h->plans[batch] = std::move(dp);
+  return MK_OK;
+}
+
+int mk_decode_step(mk_handle *h, int32_t batch, const int32_t *tokens, const int32_t *positions, void *kv_cache,
+                   float *logits, void *stream) {
+  if (!h || !tokens || !positions || !kv_cache || !logits) return MK_ERR_INVALID_ARG;
+  if (batch < 1 || batch > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
+  if (batch != 1) return MK_ERR_UNSUPPORTED;  // batched projections: not built yet
+  DevPlan *dp = nullptr;
+  int rc = get_plan(h, batch, &dp);
+  if (rc) return rc;
+  dp->epoch += 1;
+  Args a;
+  a.ctx = h->d_ctx;
+  a.instr = dp->d_instr;
+  a.q_off = dp->d_qoff;
+  a.waits = dp->d_waits;
+  a.rowtab = dp->d_rowtab;
+  a.ctr = dp->d_ctr;
+  a.grp_target = dp->d_target;
+  a.part_buf = dp->d_part;
+  a.tokens = tokens;
+  a.positions = positions;
+  a.kv = (uint16_t *)kv_cache;
+  a.logits = logits;
+  a.epoch = dp->epoch;
+  a.batch = batch;
+  a.n_split = dp->plan.n_split;
+  a.split_len = dp->plan.split_len;
+  if (kernel_launch(a, h->num_cus, (hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
+  return MK_OK;
+}
+
+int mk_sync_status(mk_handle *h) {
+  if (!h) return MK_ERR_INVALID_ARG;
+  if (hipDeviceSynchronize() != hipSuccess) return MK_ERR_HIP;
+  uint32_t st[4] = {0, 0, 0, 0};
+  if (hipMemcpy(st, h->status, sizeof st, hipMemcpyDeviceToHost) != hipSuccess) return MK_ERR_HIP;
+  if (st[0] == 0) return MK_OK;
+  // a device error: clear it and re-zero every plan's counters
+  hipMemset(h->status, 0, 256);
+  for (auto &kv : h->plans) {
+    hipMemset(kv.second->d_ctr, 0, kv.second->ctr_bytes);
+    kv.second->epoch = 0;
+  }
+  hipDeviceSynchronize();
+  const uint32_t top = st[0] >> 24;
+  if (top == 0xE1) return MK_ERR_BAD_TOKEN;
+  if (top == 0xE2) return MK_ERR_BAD_POSITION;
+  return MK_ERR_DEVICE_TIMEOUT;
+}
+
+void mk_destroy(mk_handle *h) {
+  if (!h) return;
+  for (auto &kv : h->plans) free_plan(*kv.second);
+  hipFree(h->d_ctx);
+  hipFree(h->d_layers);
+  hipFree(h->h_buf);
+  hipFree(h->q_buf);
+  hipFree(h->attn_buf);
+  hipFree(h->a_buf);
+  hipFree(h->rope);
+  hipFree(h->status);
+  delete h;
+}
+
+int mk_get_buffer(mk_handle *h, int32_t which, void **ptr, size_t *bytes) {
+  if (!h || !ptr || !bytes) return MK_ERR_INVALID_ARG;
+  switch (which) {
+    case MK_BUF_H: *ptr = h->h_buf; *bytes = h->h_bytes; return MK_OK;
+    case MK_BUF_Q: *ptr = h->q_buf; *bytes = h->q_bytes; return MK_OK;
+    case MK_BUF_ATTN: *ptr = h->attn_buf; *bytes = h->attn_bytes; return MK_OK;
+    case MK_BUF_A: *ptr = h->a_buf; *bytes = h->a_bytes; return MK_OK;
+    default: *ptr = nullptr; *bytes = 0; return MK_ERR_INVALID_ARG;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,760 @@
+// mk_kernel.hip -- the persistent decode megakernel for gfx950 (MI355X).
+//
+// One workgroup per compute unit runs an interpreter over the queue of
+// instructions the host planned for it (megakernel chapter "L'interpréteur
+// sur GPU", section 3.2).  Dependencies between instructions on different
+// compute units are counters in global memory that producers increment and
+// consumers wait on (section 3.4).  Weights of the upcoming instructions
+// stream into a ring of 16 KB LDS pages while the current instruction
+// computes or waits (section 3.3: pages freed by one instruction are refilled
+// for the next at once).
+//
+// Roles of the waves of a workgroup (the loader/compute/storer split of the
+// section 3.2 template, recast for CDNA4, which has no TMA and no warp
+// specialisation hardware):
+//   * 2 loader waves walk the queue's weight streams in order and copy them
+//     global -> LDS with direct-to-LDS 128-bit loads, several pages in
+//     flight, refilling a page as soon as every compute wave released it;
+//   * 1 sync wave walks the same queue, waits on each instruction's counter
+//     groups, and writes the instruction's fp32 input vector (the RMSNorm'd
+//     residual, the attention output or an MLP chunk) into a small LDS ring;
+//   * 8 compute waves walk the same queue, take the pages' rows in turn,
+//     do the dot products and the instruction's epilogue, and the last wave
+//     to finish an instruction increments its counter groups.
+//
+// Cross-CU data (activations, partials, the new K/V slot) is written and
+// read with device-coherent (sc1) accesses and counters are incremented only
+// after the writer's stores completed (s_waitcnt vmcnt(0)); no L2-wide
+// writeback or invalidate is used.  Every wait is bounded by a watchdog.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk_plan.hpp"
+
+namespace mk {
+
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+extern "C" __shared__ __align__(16) char smem[];
+
+__device__ __forceinline__ uint32_t &lds_u32(int off) { return *reinterpret_cast<uint32_t *>(smem + off); }
+
+// --------------------------------------------------------------------------
+// bf16 helpers
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// --------------------------------------------------------------------------
+// device-coherent accesses (relaxed agent-scope atomics -> sc1)
+__device__ __forceinline__ float ld_c(const float *p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ float2 ld_c2(const float *p) {
+  uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+__device__ __forceinline__ void st_c(float *p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_c16(uint16_t *p, uint16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint16_t ld_c16(const uint16_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_cu(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// LDS control words for the C++ roles (sync and compute waves)
+__device__ __forceinline__ uint32_t lds_ld(int off) {
+  return __hip_atomic_load(&lds_u32(off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_st(int off, uint32_t v) {
+  __hip_atomic_store(&lds_u32(off), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// --------------------------------------------------------------------------
+// 64-lane reductions with DPP (quad perms, row rotates, row broadcasts)
+template <int CTRL, int RM>
+__device__ __forceinline__ float dpp0(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, RM, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp0<0xb1, 0xf>(v);    // quad_perm [1,0,3,2]
+  v += dpp0<0x4e, 0xf>(v);    // quad_perm [2,3,0,1]
+  v += dpp0<0x124, 0xf>(v);   // row_ror:4
+  v += dpp0<0x128, 0xf>(v);   // row_ror:8
+  v += dpp0<0x142, 0xa>(v);   // row_bcast:15 into rows 1, 3
+  v += dpp0<0x143, 0xc>(v);   // row_bcast:31 into rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  // all lanes hold valid values; the identity for the bcast steps is -inf
+  auto mx = [](float a, float b) { return fmaxf(a, b); };
+  v = mx(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0xb1, 0xf, 0xf, false)));
+  v = mx(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x4e, 0xf, 0xf, false)));
+  v = mx(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x124, 0xf, 0xf, false)));
+  v = mx(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x128, 0xf, 0xf, false)));
+  v = mx(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x142, 0xa, 0xf, false)));
+  v = mx(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x143, 0xc, 0xf, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+struct Env {
+  const DevCtx *__restrict__ cp;  // device context (scalar loads)
+  const Instr *q;    // this workgroup's queue
+  uint32_t nq;       // its length
+  int cu;
+  int64_t t0;
+};
+
+__device__ __forceinline__ int64_t now() { return (int64_t)wall_clock64(); }
+
+// Record the first device error and make every wave of this workgroup exit.
+__device__ void raise_error(const Env &e, uint32_t code, uint32_t info) {
+  if (__hip_atomic_load(&e.cp->status[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+    uint32_t zero = 0;
+    if (__hip_atomic_compare_exchange_strong(&e.cp->status[0], &zero, code, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+      __hip_atomic_store(&e.cp->status[1], info, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&e.cp->status[2], (uint32_t)e.cu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  lds_st(L_ABORT, 1);
+}
+
+// Spin on an LDS condition with the abort flag and the watchdog.
+template <class F>
+__device__ __forceinline__ bool spin_lds(const Env &e, F cond, uint32_t info) {
+  if (cond()) return true;
+  int64_t deadline = now() + e.cp->watchdog_ticks;
+  for (;;) {
+    if (cond()) return true;
+    if (lds_ld(L_ABORT)) return false;
+    if (now() > deadline) {
+      raise_error(e, 0xA0000000u | info, 0);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// --------------------------------------------------------------------------
+// Weight pieces: piece (k, r) of instruction d is K-range k of unit row
+// r = i*ipw + s (see Instr).  Pure arithmetic on descriptor fields plus, for
+// tabulated units, a load from the row table: the loader must not issue
+// vector loads whose waits would drain its outstanding direct-to-LDS loads,
+// so on its fast path these are scalar (uniform index, read-only table).
+__device__ __forceinline__ const char *piece_addr(const Instr &d, const uint64_t *__restrict__ rowtab,
+                                                  uint32_t k, uint32_t r) {
+  uint64_t base;
+  if (d.tab >= 0) base = rowtab[d.tab + r];
+  else if (d.ipw == 2) base = ((r & 1) ? d.w1 : d.w0) + (uint64_t)(d.item0 + (r >> 1)) * d.rowb;
+  else base = d.w0 + (uint64_t)(d.item0 + r) * d.rowb;
+  return reinterpret_cast<const char *>(base) + (size_t)k * d.pb;
+}
+
+__device__ __forceinline__ bool is_gemv(uint8_t op) {
+  return op == OP_QKV || op == OP_O || op == OP_FFN || op == OP_DOWN || op == OP_LM;
+}
+
+// --------------------------------------------------------------------------
+// Loader waves.  All of their LDS accesses are inline asm so the compiler's
+// wait-count insertion never ties them to the outstanding direct-to-LDS
+// loads; page completion is tracked with explicit vmcnt waits.
+__device__ __forceinline__ uint32_t lds_addr(int off) {
+  return (uint32_t)(uintptr_t)((LDS_AS char *)smem + off);
+}
+__device__ __forceinline__ uint32_t asm_lds_ld(uint32_t off) {
+  off = lds_addr((int)off);
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(off) : "memory");
+  return v;
+}
+__device__ __forceinline__ void asm_lds_st(uint32_t off, uint32_t v) {
+  off = lds_addr((int)off);
+  asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(off), "v"(v) : "memory");
+}
+
+constexpr int kDepth = 3;  // pages in flight per loader wave (48 loads <= 63)
+
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ void loader_role(const Env &e, const Args &a, int lw) {
+  const int lane = lane_id();
+  const uint32_t P = (uint32_t)e.cp->ring_pages;
+  // pages of this wave are lw, lw + kNLW, ...; the pending ones (issued,
+  // not yet published) are `oldest`, oldest + kNLW, ... (npend of them)
+  uint32_t oldest = 0;
+  int npend = 0;
+  auto publish_oldest = [&]() {
+    asm_lds_st(L_FILLED + 4 * (oldest % P), oldest + 1);
+    oldest += kNLW;
+    --npend;
+  };
+  auto drain = [&]() {
+    wait_vm0();
+    while (npend) publish_oldest();
+  };
+  auto min_cons = [&]() -> uint32_t {
+    uint32_t v = lane < kNCW ? asm_lds_ld(L_CONS + 4 * lane) : 0xffffffffu;
+    // minimum over lanes 0..7 with readlanes (no LDS-unit cross-lane ops)
+    uint32_t m = __builtin_amdgcn_readlane(v, 0);
+#pragma unroll
+    for (int i = 1; i < kNCW; ++i) m = min(m, (uint32_t)__builtin_amdgcn_readlane(v, i));
+    return m;
+  };
+  uint32_t n = 0;  // global page index
+  for (uint32_t qi = 0; qi < e.nq; ++qi) {
+    const Instr d = e.q[qi];
+    if (!is_gemv(d.op)) continue;
+    const uint32_t per = d.n_items * d.ipw;
+    const uint32_t npieces = per * d.nk;
+    for (uint32_t p = 0; p < d.pages; ++p, ++n) {
+      if ((int)(n % kNLW) != lw) continue;
+      if (n >= P) {
+        const uint32_t need = n - P + 1;
+        if (min_cons() < need) {
+          drain();
+          int64_t deadline = now() + e.cp->watchdog_ticks;
+          for (;;) {
+            if (min_cons() >= need) break;
+            if (asm_lds_ld(L_ABORT)) { wait_vm0(); return; }
+            if (now() > deadline) { raise_error(e, 0xB0000000u | qi, n); wait_vm0(); return; }
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+      }
+      // issue exactly 16 wave-loads (1 KB each) for page p into slot n % P;
+      // unused tail loads re-read the page's first piece so every page
+      // counts 16 in vmcnt
+      LDS_AS char *slot = (LDS_AS char *)smem + L_RING + (n % P) * kPageBytes;
+      const uint32_t t0 = p * d.ppp;
+      const uint32_t cnt = min((uint32_t)d.ppp, npieces - t0);
+      uint32_t k = t0 / per, r = t0 - k * per;
+      const char *first = piece_addr(d, a.rowtab, k, r);
+      if (d.pb >= 1024) {
+        const uint32_t lpp = d.pb >> 10;  // wave-loads per piece
+        uint32_t j = 0;
+        for (uint32_t q = 0; q < cnt; ++q) {
+          const char *src = piece_addr(d, a.rowtab, k, r) + lane * 16;
+          for (uint32_t sub = 0; sub < lpp; ++sub, ++j)
+            __builtin_amdgcn_global_load_lds(src + sub * 1024, (LDS_AS void *)(slot + j * 1024), 16, 0, 0);
+          if (++r == per) { r = 0; ++k; }
+        }
+        for (; j < 16; ++j)
+          __builtin_amdgcn_global_load_lds(first + lane * 16, (LDS_AS void *)(slot + j * 1024), 16, 0, 0);
+      } else {
+        const uint32_t sh = 31 - __builtin_clz(d.pb);  // pb is a power of two
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t o = (uint32_t)j * 1024 + lane * 16;
+          const uint32_t q = o >> sh, within = o & (d.pb - 1);
+          const uint32_t t = t0 + q;
+          const char *src = first;
+          if (t < npieces) {
+            const uint32_t kk = t / per;
+            src = piece_addr(d, a.rowtab, kk, t - kk * per) + within;
+          }
+          __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)(slot + j * 1024), 16, 0, 0);
+        }
+      }
+      if (npend++ == 0) oldest = n;
+      if (npend == kDepth + 1) {
+        wait_vm_n<16 * kDepth>();
+        publish_oldest();
+      }
+    }
+  }
+  drain();
+}
+
+// --------------------------------------------------------------------------
+// Sync wave: counter waits and activation pieces.
+
+// Poll one counter group until all its per-XCD counters reached
+// target * epoch.  Lanes 0..7 each own one XCD counter.
+__device__ bool wait_group(const Env &e, const Args &a, uint32_t grp, uint32_t qi) {
+  const int lane = lane_id();
+  const uint32_t *cp = a.ctr + ((size_t)grp * kXcds + (lane & 7)) * kCtrStride;
+  const uint32_t need = a.grp_target[grp * kXcds + (lane & 7)] * a.epoch;
+  int64_t deadline = 0;
+  for (uint32_t it = 0;; ++it) {
+    bool ok = true;
+    if (lane < kXcds) ok = (int32_t)(ld_cu(cp) - need) >= 0;
+    if (__all(ok)) return true;
+    if (it == 0) deadline = now() + e.cp->watchdog_ticks;
+    if ((it & 15) == 15) {
+      if (lds_ld(L_ABORT)) return false;
+      if (ld_cu(&e.cp->status[0]) != 0) { lds_st(L_ABORT, 1); return false; }
+      if (now() > deadline) {
+        raise_error(e, 0xC0000000u | grp, qi);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Input vector source of the RMSNorm'd instructions.
+__device__ __forceinline__ void norm_src(const Env &e, const Args &a, const Instr &d, int b,
+                                         const float *&h, const uint16_t *&emb, const uint16_t *&w) {
+  const DevCtx &c = *e.cp;
+  const size_t HB = (size_t)c.max_batch * c.H;
+  h = nullptr;
+  emb = nullptr;
+  if (d.op == OP_QKV) {
+    w = c.layers[d.layer].attn_norm;
+    if (d.layer == 0) emb = c.embed + (size_t)a.tokens[b] * c.H;
+    else h = c.h_buf + (size_t)(2 * d.layer) * HB + (size_t)b * c.H;
+  } else if (d.op == OP_FFN) {
+    w = c.layers[d.layer].ffn_norm;
+    h = c.h_buf + (size_t)(2 * d.layer + 1) * HB + (size_t)b * c.H;
+  } else {  // OP_LM
+    w = c.final_norm;
+    h = c.h_buf + (size_t)(2 * c.L) * HB + (size_t)b * c.H;
+  }
+}
+
+__device__ __forceinline__ f4 load_src4(const float *h, const uint16_t *emb, uint32_t i) {
+  if (emb) {
+    uint2 u = *reinterpret_cast<const uint2 *>(emb + i);
+    return f4{bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y)};
+  }
+  float2 p = ld_c2(h + i), q = ld_c2(h + i + 2);
+  return f4{p.x, p.y, q.x, q.y};
+}
+
+__device__ void sync_role(const Env &e, const Args &a) {
+  const DevCtx &c = *e.cp;
+  const int lane = lane_id();
+  // inputs are validated once per workgroup before anything depends on them
+  for (int b = 0; b < a.batch; ++b) {
+    int32_t tk = a.tokens[b], ps = a.positions[b];
+    if (tk < 0 || tk >= c.V) { raise_error(e, 0xE1000000u, (uint32_t)b); return; }
+    if (ps < 0 || ps >= c.max_seq) { raise_error(e, 0xE2000000u, (uint32_t)b); return; }
+  }
+  uint32_t seq = 0;
+  float rs = 0.f;
+  for (uint32_t qi = 0; qi < e.nq; ++qi) {
+    const Instr d = e.q[qi];
+    const uint32_t nx = is_gemv(d.op) ? d.nk : 1;
+    uint32_t wi = 0;
+    for (uint32_t k = 0; k < nx; ++k, ++seq) {
+      while (wi < d.wait_n) {
+        const Wait wt = a.waits[d.wait_off + wi];
+        if (wt.before_k > k) break;
+        if (!wait_group(e, a, wt.grp, qi)) return;
+        ++wi;
+      }
+      if (seq >= (uint32_t)kNXS) {
+        const uint32_t need = seq - kNXS + 1;
+        auto freed = [&]() {
+          uint32_t v = lane < kNCW ? lds_ld(L_XCONS + 4 * lane) : 0xffffffffu;
+          uint32_t m = __builtin_amdgcn_readlane(v, 0);
+#pragma unroll
+          for (int i = 1; i < kNCW; ++i) m = min(m, (uint32_t)__builtin_amdgcn_readlane(v, i));
+          return m >= need;
+        };
+        if (!spin_lds(e, freed, 0x100 | qi)) return;
+      }
+      float *xs = reinterpret_cast<float *>(smem + L_XS + (seq % kNXS) * kXSlotBytes);
+      const int b = 0;
+      if (d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM) {
+        const float *h;
+        const uint16_t *emb, *w;
+        norm_src(e, a, d, b, h, emb, w);
+        if (k == 0) {
+          float ss = 0.f;
+          for (uint32_t i = lane * 4; i < (uint32_t)c.H; i += 256) {
+            f4 v = load_src4(h, emb, i);
+            ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+          }
+          ss = wave_sum(ss);
+          rs = 1.0f / sqrtf(ss / (float)c.H + c.eps);
+        }
+        const uint32_t k0 = k * d.kc;
+        for (uint32_t i = lane * 4; i < d.kc; i += 256) {
+          f4 v = load_src4(h, emb, k0 + i);
+          uint2 wu = *reinterpret_cast<const uint2 *>(w + k0 + i);
+          f4 o = {v.x * rs * bf_lo(wu.x), v.y * rs * bf_hi(wu.x), v.z * rs * bf_lo(wu.y), v.w * rs * bf_hi(wu.y)};
+          *reinterpret_cast<f4 *>(xs + i) = o;
+        }
+      } else if (d.op == OP_O || d.op == OP_DOWN) {
+        const float *src = d.op == OP_O
+                               ? c.attn_buf + ((size_t)d.layer * c.max_batch + b) * (c.nq * c.hd)
+                               : c.a_buf + ((size_t)d.layer * c.max_batch + b) * c.F;
+        const uint32_t k0 = k * d.kc;
+        for (uint32_t i = lane * 4; i < d.kc; i += 256) {
+          float2 p = ld_c2(src + k0 + i), q = ld_c2(src + k0 + i + 2);
+          *reinterpret_cast<f4 *>(xs + i) = f4{p.x, p.y, q.x, q.y};
+        }
+      }
+      wait_lgkm0();
+      if (lane == 0) lds_st(L_XREADY, seq + 1);
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Compute waves.
+
+// Dot product of one weight piece (bf16, in LDS) with the activation piece
+// held in registers: lane l owns 16-byte groups l, l+64, l+128, l+192.
+__device__ __forceinline__ float dot_piece(const char *piece, const float (&xr)[32], uint32_t n16) {
+  const int lane = lane_id();
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t g = (uint32_t)lane + 64u * m;
+    if (g < n16) {
+      u4 w = *reinterpret_cast<const u4 *>(piece + g * 16);
+      a0 = fmaf(bf_lo(w.x), xr[m * 8 + 0], a0);
+      a1 = fmaf(bf_hi(w.x), xr[m * 8 + 1], a1);
+      a0 = fmaf(bf_lo(w.y), xr[m * 8 + 2], a0);
+      a1 = fmaf(bf_hi(w.y), xr[m * 8 + 3], a1);
+      a0 = fmaf(bf_lo(w.z), xr[m * 8 + 4], a0);
+      a1 = fmaf(bf_hi(w.z), xr[m * 8 + 5], a1);
+      a0 = fmaf(bf_lo(w.w), xr[m * 8 + 6], a0);
+      a1 = fmaf(bf_hi(w.w), xr[m * 8 + 7], a1);
+    }
+  }
+  return wave_sum(a0 + a1);
+}
+
+__device__ __forceinline__ void load_x(const float *xs, uint32_t n16, float (&xr)[32]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t g = (uint32_t)lane + 64u * m;
+    if (g < n16) {
+      f4 p = *reinterpret_cast<const f4 *>(xs + g * 8);
+      f4 q = *reinterpret_cast<const f4 *>(xs + g * 8 + 4);
+      xr[m * 8 + 0] = p.x; xr[m * 8 + 1] = p.y; xr[m * 8 + 2] = p.z; xr[m * 8 + 3] = p.w;
+      xr[m * 8 + 4] = q.x; xr[m * 8 + 5] = q.y; xr[m * 8 + 6] = q.z; xr[m * 8 + 7] = q.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xr[m * 8 + i] = 0.f;
+    }
+  }
+}
+
+__device__ __forceinline__ size_t kv_off(const DevCtx &c, int l, int t, int b, int g, int s) {
+  return ((((size_t)l * 2 + t) * c.max_batch + b) * c.nkv + g) * (size_t)c.max_seq * c.hd + (size_t)s * c.hd;
+}
+
+// Epilogue of one finished item (row or row pair), executed by lane 0.
+__device__ void epilogue(const Env &e, const Args &a, const Instr &d, uint32_t i, float v0, float v1) {
+  const DevCtx &c = *e.cp;
+  const int b = 0;
+  const size_t HB = (size_t)c.max_batch * c.H;
+  switch (d.op) {
+    case OP_QKV: {
+      const uint32_t half = (uint32_t)c.hd >> 1;
+      const uint32_t ppg = (uint32_t)(c.G + 2) * half;
+      const uint32_t pp = d.item0 + i;
+      const uint32_t g = pp / ppg;
+      const uint32_t rr = pp - g * ppg;
+      const uint32_t hs = rr / half;
+      const uint32_t ii = rr - hs * half;
+      const int p = a.positions[b];
+      if (hs <= (uint32_t)c.G) {
+        const float cs = c.rope[((size_t)p * half + ii) * 2], sn = c.rope[((size_t)p * half + ii) * 2 + 1];
+        const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
+        if (hs < (uint32_t)c.G) {
+          float *q = c.q_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + (g * c.G + hs)) * c.hd;
+          st_c(q + ii, r0);
+          st_c(q + ii + half, r1);
+        } else {
+          uint16_t *k = a.kv + kv_off(c, d.layer, 0, b, g, p);
+          st_c16(k + ii, f2bf(r0));
+          st_c16(k + ii + half, f2bf(r1));
+        }
+      } else {
+        uint16_t *v = a.kv + kv_off(c, d.layer, 1, b, g, p);
+        st_c16(v + ii, f2bf(v0));
+        st_c16(v + ii + half, f2bf(v1));
+      }
+      break;
+    }
+    case OP_O: {
+      const uint32_t r = d.item0 + i;
+      const float hin = d.layer == 0 ? bf16f(c.embed[(size_t)a.tokens[b] * c.H + r])
+                                     : ld_c(c.h_buf + (size_t)(2 * d.layer) * HB + (size_t)b * c.H + r);
+      st_c(c.h_buf + (size_t)(2 * d.layer + 1) * HB + (size_t)b * c.H + r, hin + v0);
+      break;
+    }
+    case OP_FFN: {
+      const uint32_t j = d.item0 + i;
+      const float sg = v0 / (1.0f + expf(-v0));
+      st_c(c.a_buf + ((size_t)d.layer * c.max_batch + b) * c.F + j, sg * v1);
+      break;
+    }
+    case OP_DOWN: {
+      const uint32_t r = d.item0 + i;
+      const float hm = ld_c(c.h_buf + (size_t)(2 * d.layer + 1) * HB + (size_t)b * c.H + r);
+      st_c(c.h_buf + (size_t)(2 * d.layer + 2) * HB + (size_t)b * c.H + r, hm + v0);
+      break;
+    }
+    default: {  // OP_LM
+      a.logits[(size_t)b * c.V + d.item0 + i] = v0;
+      break;
+    }
+  }
+}
+
+// I2: split-KV attention partials for query head (g*G + h) of sequence b.
+__device__ void attn_body(const Env &e, const Args &a, const Instr &d, int h, float *qs) {
+  const DevCtx &c = *e.cp;
+  const int lane = lane_id();
+  const int b = (int)d.b, g = (int)d.aux0, s = (int)d.aux1;
+  const int j = g * c.G + h;
+  const int hd = c.hd, dpl = hd >> 6;
+  const int p = a.positions[b];
+  const int lo = s * a.split_len;
+  const int hi = min(lo + a.split_len, p + 1);
+  const float *qp = c.q_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + j) * hd;
+  for (int m = 0; m < dpl; ++m) qs[lane + 64 * m] = ld_c(qp + lane + 64 * m);
+  wait_lgkm0();
+  float mrun = -INFINITY, lrun = 0.f, o[2] = {0.f, 0.f};
+  const uint16_t *K = a.kv + kv_off(c, d.layer, 0, b, g, 0);
+  const uint16_t *Vv = a.kv + kv_off(c, d.layer, 1, b, g, 0);
+  for (int c0 = lo; c0 < hi; c0 += 64) {
+    const int tau = c0 + lane;
+    float sc = -INFINITY;
+    if (tau < hi) {
+      float acc = 0.f;
+      const uint16_t *kr = K + (size_t)tau * hd;
+      if (tau == p) {
+        for (int d2 = 0; d2 < hd; d2 += 2) {
+          acc = fmaf(qs[d2], bf16f(ld_c16(kr + d2)), acc);
+          acc = fmaf(qs[d2 + 1], bf16f(ld_c16(kr + d2 + 1)), acc);
+        }
+      } else {
+        for (int d8 = 0; d8 < hd; d8 += 8) {
+          u4 w = *reinterpret_cast<const u4 *>(kr + d8);
+          f4 q0 = *reinterpret_cast<const f4 *>(qs + d8);
+          f4 q1 = *reinterpret_cast<const f4 *>(qs + d8 + 4);
+          acc = fmaf(q0.x, bf_lo(w.x), acc);
+          acc = fmaf(q0.y, bf_hi(w.x), acc);
+          acc = fmaf(q0.z, bf_lo(w.y), acc);
+          acc = fmaf(q0.w, bf_hi(w.y), acc);
+          acc = fmaf(q1.x, bf_lo(w.z), acc);
+          acc = fmaf(q1.y, bf_hi(w.z), acc);
+          acc = fmaf(q1.z, bf_lo(w.w), acc);
+          acc = fmaf(q1.w, bf_hi(w.w), acc);
+        }
+      }
+      sc = acc * c.attn_scale;
+    }
+    const float cm = wave_max(sc);
+    const float mn = fmaxf(mrun, cm);
+    const float pt = tau < hi ? expf(sc - mn) : 0.f;
+    const float scale = mrun == -INFINITY ? 0.f : expf(mrun - mn);
+    lrun = lrun * scale + wave_sum(pt);
+    o[0] *= scale;
+    o[1] *= scale;
+    const int nt = min(64, hi - c0);
+    for (int t = 0; t < nt; ++t) {
+      const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pt), t));
+      const uint16_t *vr = Vv + (size_t)(c0 + t) * hd;
+      if (c0 + t == p) {
+        for (int m = 0; m < dpl; ++m) o[m] = fmaf(wt, bf16f(ld_c16(vr + lane + 64 * m)), o[m]);
+      } else {
+        for (int m = 0; m < dpl; ++m) o[m] = fmaf(wt, bf16f(vr[lane + 64 * m]), o[m]);
+      }
+    }
+    mrun = mn;
+  }
+  float *out = a.part_buf + ((((size_t)d.layer * c.max_batch + b) * c.nq + j) * a.n_split + s) * (hd + 4);
+  for (int m = 0; m < dpl; ++m) st_c(out + lane + 64 * m, o[m]);
+  if (lane == 0) {
+    st_c(out + hd, mrun);
+    st_c(out + hd + 1, lrun);
+  }
+}
+
+// I3: log-sum-exp combine of the split partials of query head (g*G + h).
+__device__ void red_body(const Env &e, const Args &a, const Instr &d, int h) {
+  const DevCtx &c = *e.cp;
+  const int lane = lane_id();
+  const int b = (int)d.b, g = (int)d.aux0;
+  const int j = g * c.G + h;
+  const int hd = c.hd, dpl = hd >> 6, ns = a.n_split;
+  const float *base = a.part_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + j) * (size_t)ns * (hd + 4);
+  float ms = -INFINITY, ls = 0.f;
+  if (lane < ns) {
+    ms = ld_c(base + (size_t)lane * (hd + 4) + hd);
+    ls = ld_c(base + (size_t)lane * (hd + 4) + hd + 1);
+  }
+  const float mstar = wave_max(ms);
+  const float ws = ms == -INFINITY ? 0.f : expf(ms - mstar);
+  const float L = wave_sum(ws * ls);
+  float o[2] = {0.f, 0.f};
+  for (int sp = 0; sp < ns; ++sp) {
+    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ws), sp));
+    if (w != 0.f)
+      for (int m = 0; m < dpl; ++m) o[m] = fmaf(w, ld_c(base + (size_t)sp * (hd + 4) + lane + 64 * m), o[m]);
+  }
+  float *out = c.attn_buf + ((size_t)d.layer * c.max_batch + b) * (c.nq * hd) + (size_t)j * hd;
+  for (int m = 0; m < dpl; ++m) st_c(out + lane + 64 * m, o[m] / L);
+}
+
+__device__ void compute_role(const Env &e, const Args &a, int cw) {
+  const DevCtx &c = *e.cp;
+  const int lane = lane_id();
+  const uint32_t P = (uint32_t)c.ring_pages;
+  float *acc = reinterpret_cast<float *>(smem + L_ACC);
+  float *wscr = reinterpret_cast<float *>(smem + L_WSCR + cw * 512);
+  uint32_t n = 0, seq = 0;
+  float xr[32];
+  for (uint32_t qi = 0; qi < e.nq; ++qi) {
+    const Instr d = e.q[qi];
+    const bool gv = is_gemv(d.op);
+    const uint32_t nx = gv ? d.nk : 1;
+    // gate: the first activation piece of the instruction is produced
+    if (!spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq; }, 0x200 | qi)) return;
+    if (gv) {
+      const uint32_t per = d.n_items * d.ipw;
+      const uint32_t npieces = per * d.nk;
+      const uint32_t n16 = d.pb >> 4;
+      int cur_k = -1;
+      float pend = 0.f;
+      for (uint32_t p = 0; p < d.pages; ++p) {
+        const uint32_t pg = n + p;
+        const uint32_t t0 = p * d.ppp;
+        const uint32_t tn = min(t0 + d.ppp, npieces);
+        bool waited = false;
+        const char *page = smem + L_RING + (pg % P) * kPageBytes;
+        uint32_t k = t0 / per, r = t0 - k * per;
+        for (uint32_t t = t0; t < tn; ++t, r = (r + 1 == per) ? 0 : r + 1, k += (r == 0)) {
+          const uint32_t i = d.ipw == 2 ? (r >> 1) : r;
+          if ((i % kNCW) != (uint32_t)cw) continue;
+          const uint32_t s = r - i * d.ipw;
+          if (!waited) {
+            if (!spin_lds(e, [&]() { return lds_ld(L_FILLED + 4 * (pg % P)) >= pg + 1; }, 0x300 | qi)) return;
+            waited = true;
+          }
+          if ((int)k != cur_k) {
+            if (lane == 0) lds_st(L_XCONS + 4 * cw, seq + k);
+            if (!spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq + k; }, 0x400 | qi)) return;
+            load_x(reinterpret_cast<const float *>(smem + L_XS + ((seq + k) % kNXS) * kXSlotBytes), n16, xr);
+            cur_k = (int)k;
+          }
+          float v = dot_piece(page + (t - t0) * d.pb, xr, n16);
+          if (d.nk > 1) {
+            if (k > 0) v = acc[r] + v;
+            if (k + 1 < d.nk) {
+              if (lane == 0) acc[r] = v;
+              continue;
+            }
+          }
+          if (d.ipw == 2 && s == 0) {
+            pend = v;
+            continue;
+          }
+          if (lane == 0) epilogue(e, a, d, i, d.ipw == 2 ? pend : v, v);
+        }
+        wait_lgkm0();
+        if (lane == 0) lds_st(L_CONS + 4 * cw, pg + 1);
+      }
+    } else if (d.op == OP_ATTN) {
+      if (cw < c.G) attn_body(e, a, d, cw, wscr);
+    } else if (d.op == OP_RED) {
+      if (cw < c.G) red_body(e, a, d, cw);
+    }
+    n += d.pages;
+    seq += nx;
+    if (lane == 0) lds_st(L_XCONS + 4 * cw, seq);
+    // completion: the last wave to finish signals the counter groups
+    wait_vm0();
+    uint32_t old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(&lds_u32(L_DONE + 4 * (qi & 3)), 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old == kNCW - 1) {
+      if (lane == 0) {
+        lds_st(L_DONE + 4 * (qi & 3), 0);
+        const int x = e.cu % kXcds;
+        if (d.sig0 >= 0)
+          __hip_atomic_fetch_add(a.ctr + ((size_t)d.sig0 * kXcds + x) * kCtrStride, 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        if (d.sig1 >= 0)
+          __hip_atomic_fetch_add(a.ctr + ((size_t)d.sig1 * kXcds + x) * kCtrStride, 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads, 1)
+mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const uint32_t *__restrict__ q_off,
+          const Wait *__restrict__ waits, const uint64_t *__restrict__ rowtab, uint32_t *__restrict__ ctr, const uint32_t *__restrict__ grp_target,
+          float *__restrict__ part_buf, const int32_t *__restrict__ tokens,
+          const int32_t *__restrict__ positions, uint16_t *__restrict__ kv, float *__restrict__ logits,
+          uint32_t epoch, int32_t batch, int32_t n_split, int32_t split_len) {
+  const Args a{ctx, instr, q_off, waits, rowtab, ctr, grp_target, part_buf, tokens, positions, kv, logits,
+               epoch, batch, n_split, split_len};
+  Env e;
+  e.cp = a.ctx;
+  e.cu = (int)blockIdx.x;
+  const uint32_t q0 = a.q_off[e.cu], q1 = a.q_off[e.cu + 1];
+  e.q = a.instr + q0;
+  e.nq = q1 - q0;
+  e.t0 = now();
+  if (threadIdx.x < 64) lds_u32(threadIdx.x * 4) = 0;  // control words
+  __syncthreads();
+  const int w = (int)(threadIdx.x >> 6);
+  if (w < kNCW) compute_role(e, a, w);
+  else if (w < kNCW + kNLW) loader_role(e, a, w - kNCW);
+  else sync_role(e, a);
+}
+
+}  // namespace mk
+
+// --------------------------------------------------------------------------
+// Host-side launch helpers (the ABI layer is plain C++).
+namespace mk {
+
+hipError_t kernel_setup(int *blocks_per_cu) {
+  hipError_t e = hipFuncSetAttribute((const void *)mk_interp, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     kLdsBytes);
+  if (e != hipSuccess) return e;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, mk_interp, kThreads, kLdsBytes);
+}
+
+hipError_t kernel_launch(const Args &a0, int grid, hipStream_t stream) {
+  Args a = a0;
+  void *params[] = {&a.ctx, &a.instr, &a.q_off, &a.waits, &a.rowtab, &a.ctr, &a.grp_target, &a.part_buf,
+                    &a.tokens, &a.positions, &a.kv, &a.logits, &a.epoch, &a.batch, &a.n_split,
+                    &a.split_len};
+  return hipLaunchCooperativeKernel((const void *)mk_interp, dim3(grid), dim3(kThreads), params, kLdsBytes,
+                                    stream);
+}
+
+}  // namespace mk

@@ -1,0 +1,137 @@
+// mk_plan.hpp -- the instruction descriptors, wait table and device context
+// shared by the host scheduler and the persistent interpreter kernel.
+//
+// A plan is what the host pre-schedules before launch (megakernel chapter
+// "L'interpréteur sur GPU", section 3.2): for every workgroup (one per CU) a
+// queue of instruction descriptors, and for every dependency a counter group
+// in global memory (section 3.4).
+#pragma once
+#include <stdint.h>
+
+namespace mk {
+
+// Opcodes: the seven fused instructions of the section 3.2 table.
+enum Op : uint8_t {
+  OP_QKV = 1,   // RMSNorm + QKV (+ q/k norm) + RoPE, K/V written to the cache
+  OP_ATTN = 2,  // split-KV attention partials (m, l, o) for one KV head
+  OP_RED = 3,   // log-sum-exp reduction of the partials of one KV head
+  OP_O = 4,     // O projection + residual
+  OP_FFN = 5,   // RMSNorm + gate/up + SiLU
+  OP_DOWN = 6,  // down projection + residual
+  OP_LM = 7,    // final RMSNorm + LM head
+};
+
+constexpr int kWave = 64;
+constexpr int kNCW = 8;                  // compute waves per workgroup
+constexpr int kNLW = 2;                  // loader waves per workgroup
+constexpr int kThreads = (kNCW + kNLW + 1) * kWave;  // + 1 sync wave
+constexpr int kPageBytes = 16384;        // LDS page (16 KB, 16 wave-loads of 1 KB)
+constexpr int kMaxKc = 2048;             // elements per weight piece (<= 4 KB)
+constexpr int kXSlotBytes = kMaxKc * 4;  // one fp32 activation piece
+constexpr int kNXS = 2;                  // activation slots (double buffer)
+constexpr int kAccFloats = 1024;         // LDS accumulators for multi-piece rows
+constexpr int kLdsBytes = 163840;        // gfx950: 160 KB per CU
+constexpr int kCtrStride = 32;           // uint32 spacing of counters (128 B)
+constexpr int kXcds = 8;                 // counters per group (one per XCD)
+constexpr int kMaxSplits = 64;
+
+// One queued instruction (96 bytes).  An instruction's weight stream is the
+// sequence of pieces t = 0 .. n_items*ipw*nk - 1 in k-major order:
+//   k = t / (n_items*ipw), item i = (t % (n_items*ipw)) / ipw, s = t % ipw,
+// piece t is row-part (item i, sub-row s) x K-range [k*kc, (k+1)*kc).  Pieces
+// are packed `ppp` per 16 KB page.
+struct alignas(16) Instr {
+  uint8_t op;
+  uint8_t ipw;          // pieces (rows) per item: 2 for RoPE pairs / gate+up
+  uint16_t layer;
+  uint16_t nk;          // K pieces per row
+  uint16_t ppp;         // pieces per page
+  uint32_t kc;          // elements per piece
+  uint32_t pb;          // bytes per piece (2*kc)
+  uint32_t item0;       // first item of this unit
+  uint32_t n_items;
+  uint32_t pages;       // weight pages of this unit (0: no weight stream)
+  uint32_t wait_off;    // first entry in the wait table
+  uint32_t wait_n;      // number of wait entries
+  int32_t sig0, sig1;   // counter groups signalled on completion (-1: none)
+  uint32_t b;           // sequence index (attention units)
+  uint32_t aux0, aux1;  // ATTN: KV head, split; RED: KV head; QKV: G, head_dim
+  uint32_t unit;        // unit index within (layer, op), for tracing
+  // weight stream (host-resolved so the loader reads no context): row
+  // r = i*ipw + s of the unit starts at rowtab[tab + r] if tab >= 0, else at
+  // (s ? w1 : w0) + (item0 + i) * rowb.  FFN: w0 = w_gate, w1 = w_up.
+  uint64_t w0, w1;
+  int32_t tab;          // offset into the plan's row-address table, or -1
+  uint32_t rowb;        // bytes per weight row (K * 2)
+  uint64_t pad;
+};
+static_assert(sizeof(Instr) == 96, "descriptor size");
+
+// A wait: counter group `grp` must reach its per-step target before the
+// activation piece `before_k` of the instruction is produced.
+struct Wait {
+  uint32_t grp;
+  uint32_t before_k;
+};
+
+struct DevLayer {
+  const uint16_t *attn_norm, *wq, *wk, *wv, *q_norm, *k_norm;
+  const uint16_t *wo, *ffn_norm, *w_gate, *w_up, *w_down;
+};
+
+// Device context: everything the kernel needs besides the per-step
+// arguments.  Lives in device memory, read with scalar loads.
+struct DevCtx {
+  int32_t L, H, nq, nkv, hd, F, V, G, qk_norm, tied;
+  int32_t max_batch, max_seq, num_cus;
+  float eps, attn_scale;
+  int64_t watchdog_ticks;   // 100 MHz ticks
+  const uint16_t *embed, *final_norm, *lm_head;
+  const DevLayer *layers;
+  float *h_buf;       // [2L+1][max_batch][H]
+  float *q_buf;       // [L][max_batch][nq][hd]
+  float *attn_buf;    // [L][max_batch][nq*hd]
+  float *a_buf;       // [L][max_batch][F]
+  const float *rope;  // [max_seq][hd/2][2] (cos, sin)
+  uint32_t *status;   // [0] error code, [1..] details
+  uint64_t *trace;    // per-instruction records or NULL
+  int32_t ring_pages; // LDS weight pages per workgroup
+  int32_t flags;
+};
+
+// LDS layout of a workgroup (bytes).
+constexpr int L_FILLED = 0;     // u32[16]  page slot -> (page index + 1)
+constexpr int L_CONS = 64;      // u32[8]   pages released per compute wave
+constexpr int L_XCONS = 96;     // u32[8]   activation pieces released per wave
+constexpr int L_XREADY = 128;   // u32      activation pieces produced
+constexpr int L_DONE = 132;     // u32[4]   waves finished, per unit slot
+constexpr int L_ABORT = 148;    // u32      nonzero: every wave exits
+constexpr int L_WSCR = 256;     // per compute wave 512 B scratch
+constexpr int L_ACC = L_WSCR + kNCW * 512;              // fp32 accumulators
+constexpr int L_XS = L_ACC + kAccFloats * 4;            // activation ring
+constexpr int L_RING = ((L_XS + kNXS * kXSlotBytes + 1023) / 1024) * 1024;
+constexpr int kMaxRingPages = 16;
+constexpr int kRingPages = (kLdsBytes - L_RING) / kPageBytes < kMaxRingPages
+                               ? (kLdsBytes - L_RING) / kPageBytes : kMaxRingPages;
+static_assert(kRingPages >= 4, "LDS budget");
+
+// Kernel arguments of one decode step (one per-batch plan).
+struct Args {
+  const DevCtx *ctx;
+  const Instr *instr;         // all per-CU queues back to back
+  const uint32_t *q_off;      // [num_cus + 1]
+  const Wait *waits;
+  const uint64_t *rowtab;     // row start addresses for tabulated units
+  uint32_t *ctr;              // [n_groups][kXcds][kCtrStride]
+  const uint32_t *grp_target; // [n_groups][kXcds] arrivals per step
+  float *part_buf;            // [L][max_batch][nq][n_split][hd + 4] (o.., m, l)
+  const int32_t *tokens;
+  const int32_t *positions;
+  uint16_t *kv;
+  float *logits;
+  uint32_t epoch;
+  int32_t batch;
+  int32_t n_split, split_len;
+};
+
+}  // namespace mk

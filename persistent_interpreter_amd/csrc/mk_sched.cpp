@@ -1,0 +1,550 @@
+// mk_sched.cpp -- host instruction scheduler and plan validator.
+//
+// The host plans every workgroup's instruction queue before launch
+// (megakernel chapter "L'interpréteur sur GPU", section 3.2).  Each of the
+// seven instructions is cut into units spread over the compute units; each
+// dependency between units is a counter group that consumers wait on
+// (section 3.4), at the granularity the data is produced (the generalisation
+// closing section 3.4: dependency granularity follows production
+// granularity): per KV head from QKV to attention, per (sequence, KV head)
+// from attention to its reduction, per MLP chunk from up/gate to down (four
+// chunks by default, the chunked example of section 3.4), and whole-vector
+// edges where a RMSNorm needs every row.
+#include "mk_sched.hpp"
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <random>
+
+namespace mk {
+
+int choose_kc(int K) {
+  // piece bytes (2*kc) must be a multiple of 1 KB or divide 1 KB so that a
+  // 1 KB wave-load never straddles pieces unevenly
+  static const int cand[] = {2048, 1536, 1024, 512, 256, 128, 64, 32, 16, 8};
+  for (int kc : cand)
+    if (kc <= K && K % kc == 0) return kc;
+  return 0;
+}
+
+static inline uint32_t part_lo(uint64_t total, uint64_t n, uint64_t u) {
+  return (uint32_t)(total * u / n);
+}
+
+namespace {
+
+struct Unit {
+  Instr in;
+  int cu;
+  std::vector<Wait> waits;
+  std::vector<Access> reads, writes;
+  std::vector<int> sigs;
+};
+
+struct Builder {
+  const mk_config &c;
+  int B, C;
+  Plan &P;
+  std::vector<Unit> units;
+
+  Builder(const mk_config &cfg, int b, int cus, Plan &p) : c(cfg), B(b), C(cus), P(p) {}
+
+  int group() {
+    P.grp_target.resize(P.grp_target.size() + kXcds, 0);
+    P.grp_producers.push_back(0);
+    return P.n_groups++;
+  }
+
+  void add(Unit u) {
+    u.in.sig0 = u.sigs.size() > 0 ? u.sigs[0] : -1;
+    u.in.sig1 = u.sigs.size() > 1 ? u.sigs[1] : -1;
+    for (int g : u.sigs) {
+      P.grp_target[(size_t)g * kXcds + (u.cu % kXcds)] += 1;
+      P.grp_producers[g] += 1;
+    }
+    units.push_back(std::move(u));
+  }
+};
+
+Instr gemv(Op op, int layer, uint32_t item0, uint32_t n, int ipw, int K, int kc,
+           uint32_t unit) {
+  Instr in;
+  std::memset(&in, 0, sizeof in);
+  in.op = op;
+  in.layer = (uint16_t)layer;
+  in.ipw = (uint8_t)ipw;
+  in.kc = (uint32_t)kc;
+  in.pb = (uint32_t)(2 * kc);
+  in.nk = (uint16_t)(K / kc);
+  int ppp = kPageBytes / (int)in.pb;
+  in.ppp = (uint16_t)ppp;
+  in.item0 = item0;
+  in.n_items = n;
+  uint64_t pieces = (uint64_t)n * ipw * in.nk;
+  in.pages = (uint32_t)((pieces + ppp - 1) / ppp);
+  in.sig0 = in.sig1 = -1;
+  in.tab = -1;
+  in.rowb = (uint32_t)(2 * K);
+  in.unit = unit;
+  return in;
+}
+
+Instr plain(Op op, int layer, uint32_t unit) {
+  Instr in;
+  std::memset(&in, 0, sizeof in);
+  in.op = op;
+  in.layer = (uint16_t)layer;
+  in.sig0 = in.sig1 = -1;
+  in.tab = -1;
+  in.unit = unit;
+  return in;
+}
+
+}  // namespace
+
+int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
+  P = Plan();
+  const int L = c.n_layers, H = c.hidden, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const int hd = c.head_dim, F = c.ffn_dim, V = c.vocab, S = c.max_seq;
+  if (C < 1 || B < 1 || B > c.max_batch) {
+    err = "num_cus and batch must be >= 1 and batch <= max_batch";
+    return MK_ERR_INVALID_ARG;
+  }
+  const int G = nq / nkv, HALF = hd / 2;
+  const int kc_h = choose_kc(H), kc_o = choose_kc(nq * hd), kc_f = choose_kc(F);
+  if (!kc_h || !kc_o || !kc_f) {
+    err = "hidden, n_q_heads*head_dim and ffn_dim must be multiples of 8";
+    return MK_ERR_UNSUPPORTED;
+  }
+  const uint32_t PPG = (uint32_t)(G + 2) * HALF;     // QKV row pairs per KV head
+  const uint32_t TP = (uint32_t)nkv * PPG;
+  const int nk_f = F / kc_f;
+  int chunks = c.mlp_chunks > 0 ? c.mlp_chunks : 4;
+  chunks = std::min(chunks, nk_f);
+  int n_split = c.kv_splits;
+  if (n_split <= 0) {
+    n_split = std::max(1, std::min(kMaxSplits, C / std::max(1, B * nkv)));
+    n_split = std::min(n_split, std::max(1, (S + 15) / 16));
+  }
+  if (n_split > kMaxSplits) {
+    err = "kv_splits must be <= 64";
+    return MK_ERR_UNSUPPORTED;
+  }
+  const int split_len = (S + n_split - 1) / n_split;
+  P.num_cus = C;
+  P.batch = B;
+  P.n_split = n_split;
+  P.split_len = split_len;
+  P.mlp_chunks = chunks;
+
+  const uint32_t n_qkv = std::min<uint32_t>(TP, std::max<uint32_t>((uint32_t)nkv, std::min<uint32_t>(C, TP)));
+  const uint32_t n_o = std::min(C, H), n_down = std::min(C, H);
+  const uint32_t n_ffn = std::min<uint32_t>(F, std::max<uint32_t>((uint32_t)chunks, std::min<uint32_t>(C, F)));
+  const uint32_t n_lm = std::min(C, V);
+
+  auto chunk_k0 = [&](int ch) { return (uint32_t)((uint64_t)ch * nk_f / chunks); };
+
+  Builder bd(c, B, C, P);
+  std::vector<int> g_down_prev(1, -1);
+  int g_down = -1;
+  for (int l = 0; l < L; ++l) {
+    std::vector<int> g_qkv(nkv), g_attn((size_t)B * nkv), g_ffn(chunks);
+    for (auto &g : g_qkv) g = bd.group();
+    for (auto &g : g_attn) g = bd.group();
+    const int g_red = bd.group(), g_o = bd.group();
+    for (auto &g : g_ffn) g = bd.group();
+    const int g_dn = bd.group();
+
+    // I1: RMSNorm + QKV + RoPE.  Items are row pairs (i, i+hd/2) of one head
+    // in KV-head-major order: for KV head g, its G query heads, then K, V.
+    for (uint32_t u = 0; u < n_qkv; ++u) {
+      uint32_t p0 = part_lo(TP, n_qkv, u), p1 = part_lo(TP, n_qkv, u + 1);
+      Unit un;
+      un.in = gemv(OP_QKV, l, p0, p1 - p0, 2, H, kc_h, u);
+      un.in.aux0 = (uint32_t)G;
+      un.in.aux1 = (uint32_t)hd;
+      un.cu = (int)(u % C);
+      if (l > 0) un.waits.push_back({(uint32_t)g_down, 0});
+      for (int b = 0; b < B; ++b) {
+        if (l > 0) un.reads.push_back({R_HOUT, (uint16_t)(l - 1), (uint32_t)b, 0, (uint32_t)H, 0});
+        un.writes.push_back({R_QKV, (uint16_t)l, (uint32_t)b, p0, p1, 0});
+      }
+      int gfirst = (int)(p0 / PPG), glast = (int)((p1 - 1) / PPG);
+      if (glast - gfirst > 1) {
+        err = "internal: a QKV unit spans more than two KV heads";
+        return MK_ERR_UNSUPPORTED;
+      }
+      for (int g = gfirst; g <= glast; ++g) un.sigs.push_back(g_qkv[g]);
+      bd.add(std::move(un));
+    }
+    // I2: attention partials per (sequence, KV head, split).
+    for (int b = 0; b < B; ++b)
+      for (int g = 0; g < nkv; ++g)
+        for (int s = 0; s < n_split; ++s) {
+          uint32_t a = (uint32_t)((b * nkv + g) * n_split + s);
+          Unit un;
+          un.in = plain(OP_ATTN, l, a);
+          un.in.b = (uint32_t)b;
+          un.in.aux0 = (uint32_t)g;
+          un.in.aux1 = (uint32_t)s;
+          un.cu = (int)(a % C);
+          un.waits.push_back({(uint32_t)g_qkv[g], 0});
+          un.reads.push_back({R_QKV, (uint16_t)l, (uint32_t)b, g * PPG, (g + 1) * PPG, 0});
+          un.writes.push_back({R_PART, (uint16_t)l, (uint32_t)b, (uint32_t)(g * n_split + s),
+                               (uint32_t)(g * n_split + s + 1), 0});
+          un.sigs.push_back(g_attn[b * nkv + g]);
+          bd.add(std::move(un));
+        }
+    // I3: reduction of the partials per (sequence, KV head).
+    const int n_red = B * nkv;
+    for (int r = 0; r < n_red; ++r) {
+      int b = r / nkv, g = r % nkv;
+      Unit un;
+      un.in = plain(OP_RED, l, (uint32_t)r);
+      un.in.b = (uint32_t)b;
+      un.in.aux0 = (uint32_t)g;
+      un.cu = (int)(((uint64_t)r * C / n_red) % C);
+      un.waits.push_back({(uint32_t)g_attn[r], 0});
+      un.reads.push_back({R_PART, (uint16_t)l, (uint32_t)b, (uint32_t)(g * n_split),
+                          (uint32_t)((g + 1) * n_split), 0});
+      un.writes.push_back({R_ATTN, (uint16_t)l, (uint32_t)b, (uint32_t)(g * G * hd),
+                           (uint32_t)((g + 1) * G * hd), 0});
+      un.sigs.push_back(g_red);
+      bd.add(std::move(un));
+    }
+    // I4: O projection + residual, rows of H.
+    for (uint32_t u = 0; u < n_o; ++u) {
+      uint32_t r0 = part_lo(H, n_o, u), r1 = part_lo(H, n_o, u + 1);
+      Unit un;
+      un.in = gemv(OP_O, l, r0, r1 - r0, 1, nq * hd, kc_o, u);
+      un.cu = (int)(u % C);
+      un.waits.push_back({(uint32_t)g_red, 0});
+      for (int b = 0; b < B; ++b) {
+        un.reads.push_back({R_ATTN, (uint16_t)l, (uint32_t)b, 0, (uint32_t)(nq * hd), 0});
+        if (l > 0) un.reads.push_back({R_HOUT, (uint16_t)(l - 1), (uint32_t)b, r0, r1, 0});
+        un.writes.push_back({R_HMID, (uint16_t)l, (uint32_t)b, r0, r1, 0});
+      }
+      un.sigs.push_back(g_o);
+      bd.add(std::move(un));
+    }
+    // I5: RMSNorm + gate/up + SiLU; items are FFN rows j (gate row, up row).
+    for (uint32_t u = 0; u < n_ffn; ++u) {
+      uint32_t j0 = part_lo(F, n_ffn, u), j1 = part_lo(F, n_ffn, u + 1);
+      Unit un;
+      un.in = gemv(OP_FFN, l, j0, j1 - j0, 2, H, kc_h, u);
+      un.cu = (int)(u % C);
+      un.waits.push_back({(uint32_t)g_o, 0});
+      for (int b = 0; b < B; ++b) {
+        un.reads.push_back({R_HMID, (uint16_t)l, (uint32_t)b, 0, (uint32_t)H, 0});
+        un.writes.push_back({R_A, (uint16_t)l, (uint32_t)b, j0, j1, 0});
+      }
+      for (int ch = 0; ch < chunks; ++ch) {
+        uint32_t e0 = chunk_k0(ch) * kc_f, e1 = chunk_k0(ch + 1) * kc_f;
+        if (j0 < e1 && e0 < j1) un.sigs.push_back(g_ffn[ch]);
+      }
+      if (un.sigs.size() > 2) {
+        err = "internal: an FFN unit spans more than two MLP chunks";
+        return MK_ERR_UNSUPPORTED;
+      }
+      bd.add(std::move(un));
+    }
+    // I6: down projection + residual; consumes the MLP chunks in order.
+    for (uint32_t u = 0; u < n_down; ++u) {
+      uint32_t r0 = part_lo(H, n_down, u), r1 = part_lo(H, n_down, u + 1);
+      Unit un;
+      un.in = gemv(OP_DOWN, l, r0, r1 - r0, 1, F, kc_f, u);
+      un.cu = (int)(u % C);
+      for (int ch = 0; ch < chunks; ++ch) un.waits.push_back({(uint32_t)g_ffn[ch], chunk_k0(ch)});
+      for (int b = 0; b < B; ++b) {
+        for (int ch = 0; ch < chunks; ++ch)
+          un.reads.push_back({R_A, (uint16_t)l, (uint32_t)b, chunk_k0(ch) * kc_f,
+                              chunk_k0(ch + 1) * kc_f, chunk_k0(ch)});
+        un.reads.push_back({R_HMID, (uint16_t)l, (uint32_t)b, r0, r1, 0});
+        un.writes.push_back({R_HOUT, (uint16_t)l, (uint32_t)b, r0, r1, 0});
+      }
+      un.sigs.push_back(g_dn);
+      bd.add(std::move(un));
+    }
+    g_down = g_dn;
+    (void)g_down_prev;
+  }
+  // I7: final RMSNorm + LM head.
+  for (uint32_t u = 0; u < n_lm; ++u) {
+    uint32_t v0 = part_lo(V, n_lm, u), v1 = part_lo(V, n_lm, u + 1);
+    Unit un;
+    un.in = gemv(OP_LM, L, v0, v1 - v0, 1, H, kc_h, u);
+    un.in.layer = (uint16_t)L;
+    un.cu = (int)(u % C);
+    un.waits.push_back({(uint32_t)g_down, 0});
+    for (int b = 0; b < B; ++b)
+      un.reads.push_back({R_HOUT, (uint16_t)(L - 1), (uint32_t)b, 0, (uint32_t)H, 0});
+    bd.add(std::move(un));
+  }
+
+  // Per-CU queues in creation order (= stage order).
+  std::vector<std::vector<int>> per_cu(C);
+  for (size_t i = 0; i < bd.units.size(); ++i) per_cu[bd.units[i].cu].push_back((int)i);
+  P.q_off.assign(C + 1, 0);
+  std::vector<int64_t> cu_bytes(C, 0);
+  for (int cu = 0; cu < C; ++cu) {
+    P.q_off[cu] = (uint32_t)P.instr.size();
+    for (int ui : per_cu[cu]) {
+      Unit &un = bd.units[ui];
+      Instr in = un.in;
+      in.wait_off = (uint32_t)P.waits.size();
+      in.wait_n = (uint32_t)un.waits.size();
+      for (auto &w : un.waits) P.waits.push_back(w);
+      if (in.pages) {
+        int64_t bytes = (int64_t)in.n_items * in.ipw * in.nk * in.pb;
+        cu_bytes[cu] += bytes;
+        P.weight_bytes += bytes;
+        P.n_pages += (int)in.pages;
+        if (in.nk > 1 && (int64_t)in.n_items * in.ipw > kAccFloats) {
+          err = "internal: too many rows in a multi-piece unit";
+          return MK_ERR_UNSUPPORTED;
+        }
+      }
+      P.instr.push_back(in);
+      P.reads.push_back(un.reads);
+      P.writes.push_back(un.writes);
+    }
+  }
+  P.q_off[C] = (uint32_t)P.instr.size();
+  P.max_cu_bytes = *std::max_element(cu_bytes.begin(), cu_bytes.end());
+  return MK_OK;
+}
+
+void resolve_streams(const mk_config &c, const mk_weights &w, Plan &P) {
+  const int G = c.n_q_heads / c.n_kv_heads, hd = c.head_dim, half = hd / 2;
+  const uint64_t Hb = 2ull * c.hidden;
+  P.rowtab.clear();
+  for (Instr &in : P.instr) {
+    if (in.op == OP_ATTN || in.op == OP_RED) continue;
+    in.tab = -1;
+    if (in.op == OP_LM) {
+      in.w0 = (uint64_t)(uintptr_t)(c.tied_embeddings ? w.embed : w.lm_head);
+      continue;
+    }
+    const mk_layer_weights &ly = w.layers[in.layer];
+    switch (in.op) {
+      case OP_QKV: {
+        // rows of pair (i, i + hd/2) of one head, in the pair order of the
+        // unit: row r = 2*i + s
+        in.tab = (int32_t)P.rowtab.size();
+        const uint32_t ppg = (uint32_t)(G + 2) * half;
+        for (uint32_t i = 0; i < in.n_items; ++i)
+          for (uint32_t s = 0; s < 2; ++s) {
+            const uint32_t pp = in.item0 + i, g = pp / ppg, rr = pp % ppg;
+            const uint32_t hs = rr / half, ii = rr % half + s * half;
+            uint64_t base;
+            if (hs < (uint32_t)G) base = (uint64_t)(uintptr_t)ly.wq + ((uint64_t)(g * G + hs) * hd + ii) * Hb;
+            else if (hs == (uint32_t)G) base = (uint64_t)(uintptr_t)ly.wk + ((uint64_t)g * hd + ii) * Hb;
+            else base = (uint64_t)(uintptr_t)ly.wv + ((uint64_t)g * hd + ii) * Hb;
+            P.rowtab.push_back(base);
+          }
+        break;
+      }
+      case OP_O: in.w0 = (uint64_t)(uintptr_t)ly.wo; break;
+      case OP_FFN:
+        in.w0 = (uint64_t)(uintptr_t)ly.w_gate;
+        in.w1 = (uint64_t)(uintptr_t)ly.w_up;
+        break;
+      default: in.w0 = (uint64_t)(uintptr_t)ly.w_down; break;
+    }
+  }
+  if (P.rowtab.empty()) P.rowtab.push_back(0);
+}
+
+// ---------------------------------------------------------------------------
+// Validation: counter bookkeeping plus simulated interleavings.
+
+namespace {
+
+struct Sim {
+  const Plan &P;
+  int C;
+  std::vector<uint32_t> target;               // per group
+  std::vector<std::vector<int>> writers;      // per (read index) writer unit ids
+  std::vector<std::vector<std::pair<uint32_t, int>>> read_ix;  // per unit: (phase, read list index)
+  std::vector<std::vector<uint32_t>> phases;  // per unit: sorted distinct before_k
+  std::vector<std::vector<int>> sig;          // per unit groups signalled
+
+  explicit Sim(const Plan &p) : P(p), C(p.num_cus) {}
+};
+
+}  // namespace
+
+int check_plan(const mk_config &cfg, Plan &P, int sim_runs, int corrupt, uint64_t seed,
+               mk_plan_report *rep) {
+  (void)cfg;
+  const int C = P.num_cus;
+  const size_t NU = P.instr.size();
+  std::string first;
+  int errors = 0;
+  auto fail = [&](const std::string &m) {
+    if (first.empty()) first = m;
+    ++errors;
+  };
+  std::mt19937_64 rng(seed);
+
+  // Deliberate corruption for validator self-tests.
+  std::vector<uint32_t> target(P.n_groups, 0);
+  for (int g = 0; g < P.n_groups; ++g)
+    for (int x = 0; x < kXcds; ++x) target[g] += P.grp_target[(size_t)g * kXcds + x];
+  std::vector<std::vector<int>> sig(NU);
+  for (size_t u = 0; u < NU; ++u) {
+    if (P.instr[u].sig0 >= 0) sig[u].push_back(P.instr[u].sig0);
+    if (P.instr[u].sig1 >= 0) sig[u].push_back(P.instr[u].sig1);
+  }
+  std::vector<std::vector<Wait>> waits(NU);
+  for (size_t u = 0; u < NU; ++u)
+    for (uint32_t i = 0; i < P.instr[u].wait_n; ++i) waits[u].push_back(P.waits[P.instr[u].wait_off + i]);
+  if (corrupt) {
+    // pick a unit with both a signal and waiting consumers
+    std::vector<int> cand;
+    for (size_t u = 0; u < NU; ++u)
+      if (!sig[u].empty() && P.instr[u].op != OP_LM) cand.push_back((int)u);
+    int victim = cand.empty() ? -1 : cand[rng() % cand.size()];
+    if (corrupt == 1 && victim >= 0) sig[victim].clear();
+    if (corrupt == 2 && victim >= 0) target[sig[victim][0]] -= 1;
+    if (corrupt == 3) {
+      std::vector<int> w;
+      for (size_t u = 0; u < NU; ++u)
+        if (!waits[u].empty()) w.push_back((int)u);
+      if (!w.empty()) {
+        int u = w[rng() % w.size()];
+        waits[u].erase(waits[u].begin() + (rng() % waits[u].size()));
+      }
+    }
+  }
+
+  // Static: group targets equal the producers, per XCD placement.
+  {
+    std::vector<uint32_t> cnt((size_t)P.n_groups * kXcds, 0);
+    for (int cu = 0; cu < C; ++cu)
+      for (uint32_t u = P.q_off[cu]; u < P.q_off[cu + 1]; ++u)
+        for (int g : {P.instr[u].sig0, P.instr[u].sig1})
+          if (g >= 0) cnt[(size_t)g * kXcds + (cu % kXcds)]++;
+    if (cnt != P.grp_target) fail("counter targets differ from producer placement");
+    for (size_t u = 0; u < NU; ++u)
+      for (auto &w : waits[u])
+        if (w.grp >= (uint32_t)P.n_groups || P.grp_producers[w.grp] == 0)
+          fail("wait on a group without producers");
+  }
+
+  // Writers of every read.
+  struct Key { uint8_t res; uint16_t l; uint32_t b; };
+  auto key_of = [](const Access &a) { return ((uint64_t)a.res << 48) | ((uint64_t)a.layer << 32) | a.b; };
+  std::vector<std::pair<uint64_t, std::pair<uint32_t, int>>> wl;  // key -> (lo, unit)
+  for (size_t u = 0; u < NU; ++u)
+    for (auto &w : P.writes[u]) wl.push_back({key_of(w), {w.lo, (int)u}});
+  std::sort(wl.begin(), wl.end());
+  std::vector<std::vector<std::pair<uint32_t, std::vector<int>>>> rw(NU);  // per unit: (phase, writers)
+  for (size_t u = 0; u < NU; ++u)
+    for (auto &r : P.reads[u]) {
+      std::vector<int> ws;
+      uint64_t k = key_of(r);
+      auto it = std::lower_bound(wl.begin(), wl.end(), std::make_pair(k, std::make_pair(0u, -1)));
+      for (; it != wl.end() && it->first == k; ++it) {
+        int wu = it->second.second;
+        for (auto &w : P.writes[wu])
+          if (key_of(w) == k && w.lo < r.hi && r.lo < w.hi) { ws.push_back(wu); break; }
+      }
+      // every element of the read must have a writer
+      std::vector<std::pair<uint32_t, uint32_t>> iv;
+      for (int wu : ws)
+        for (auto &w : P.writes[wu])
+          if (key_of(w) == k) iv.push_back({std::max(w.lo, r.lo), std::min(w.hi, r.hi)});
+      std::sort(iv.begin(), iv.end());
+      uint32_t cov = r.lo;
+      for (auto &p : iv)
+        if (p.first <= cov) cov = std::max(cov, p.second);
+      if (cov < r.hi) fail("a read has elements no unit writes");
+      rw[u].push_back({r.phase, std::move(ws)});
+    }
+
+  // Phases of each unit: sorted distinct before_k values (always 0).
+  std::vector<std::vector<uint32_t>> phases(NU);
+  for (size_t u = 0; u < NU; ++u) {
+    phases[u].push_back(0);
+    for (auto &w : waits[u]) phases[u].push_back(w.before_k);
+    std::sort(phases[u].begin(), phases[u].end());
+    phases[u].erase(std::unique(phases[u].begin(), phases[u].end()), phases[u].end());
+  }
+
+  // Interleavings: each CU runs its queue strictly in order, phase by phase;
+  // a phase may start once its waits' groups reached their targets.
+  int runs = 0;
+  for (int run = 0; run < sim_runs && errors == 0; ++run, ++runs) {
+    int strategy = run % 4;
+    int delayed = (int)(rng() % C);
+    std::vector<uint32_t> count(P.n_groups, 0);
+    std::vector<char> done(NU, 0);
+    std::vector<uint32_t> pos(C), ph(C, 0);
+    for (int cu = 0; cu < C; ++cu) pos[cu] = P.q_off[cu];
+    size_t remaining = NU;
+    std::vector<int> ready;
+    while (remaining) {
+      ready.clear();
+      for (int cu = 0; cu < C; ++cu) {
+        if (pos[cu] >= P.q_off[cu + 1]) continue;
+        uint32_t u = pos[cu];
+        uint32_t phase = phases[u][ph[cu]];
+        bool ok = true;
+        for (auto &w : waits[u])
+          if (w.before_k == phase && count[w.grp] < target[w.grp]) { ok = false; break; }
+        if (ok) ready.push_back(cu);
+      }
+      if (ready.empty()) {
+        fail("deadlock: no workgroup can make progress");
+        break;
+      }
+      int cu;
+      if (strategy == 0) cu = ready[rng() % ready.size()];
+      else if (strategy == 1) {
+        std::vector<int> others;
+        for (int r : ready) if (r != delayed) others.push_back(r);
+        cu = others.empty() ? ready[0] : others[rng() % others.size()];
+      } else if (strategy == 2) {
+        // earliest stage first
+        cu = ready[0];
+        for (int r : ready) if (pos[r] - P.q_off[r] < pos[cu] - P.q_off[cu]) cu = r;
+      } else {
+        // run one workgroup as far as it can go
+        cu = ready[rng() % ready.size()];
+        int best = -1;
+        for (int r : ready) if (best < 0 || pos[r] - P.q_off[r] > pos[best] - P.q_off[best]) best = r;
+        if (rng() % 2) cu = best;
+      }
+      uint32_t u = pos[cu];
+      uint32_t phase = phases[u][ph[cu]];
+      for (auto &rp : rw[u])
+        if (rp.first == phase)
+          for (int wu : rp.second)
+            if (!done[wu]) {
+              char m[200];
+              std::snprintf(m, sizeof m, "unit %u (op %d layer %d) reads data of unit %d (op %d) before it finished",
+                            u, P.instr[u].op, P.instr[u].layer, wu, P.instr[wu].op);
+              fail(m);
+              break;
+            }
+      if (errors) break;
+      if (++ph[cu] == phases[u].size()) {
+        done[u] = 1;
+        --remaining;
+        for (int g : sig[u]) count[g]++;
+        ph[cu] = 0;
+        ++pos[cu];
+      }
+    }
+  }
+  if (rep) {
+    rep->sim_runs = runs;
+    rep->sim_errors = errors;
+    std::snprintf(rep->msg, sizeof rep->msg, "%s", first.c_str());
+  }
+  return errors ? MK_ERR_INVALID_ARG : MK_OK;
+}
+
+}  // namespace mk

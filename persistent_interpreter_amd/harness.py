@@ -1,0 +1,109 @@
+"""Glue for tests, the bench and the smoke run: upload seeded inputs to the
+GPU, own the step buffers, and drive greedy decoding through the C ABI.
+
+Nothing here computes any part of the decode step: the step itself is one
+``mk_decode_step`` launch; the greedy choice of the next token (an argmax
+over the logits the kernel wrote) and ``position + 1`` are harness work.
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import numpy as np
+
+from . import binding as B
+from . import synth
+
+
+def _t(a: Optional[np.ndarray], device):
+    import torch
+    if a is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+
+
+def upload_weights(W: dict, device="cuda") -> dict:
+    """bf16 bit arrays -> device int16 tensors (same bits)."""
+    return {"embed": _t(W["embed"], device), "final_norm": _t(W["final_norm"], device),
+            "lm_head": _t(W.get("lm_head"), device),
+            "layers": [{k: _t(v, device) for k, v in lw.items()} for lw in W["layers"]]}
+
+
+class Session:
+    """A megakernel handle plus device-resident step buffers."""
+
+    def __init__(self, mc: synth.ModelConfig, W: dict, kv: np.ndarray,
+                 batch: int = 1, device="cuda", **knobs):
+        import torch
+        self.mc = mc
+        self.batch = batch
+        self.device = device
+        self.dW = upload_weights(W, device) if not _is_device(W) else W
+        self.kv = _t(kv, device) if isinstance(kv, np.ndarray) else kv
+        max_batch = kv.shape[2]
+        max_seq = kv.shape[4]
+        self.cfg = B.make_config(mc, max_batch=max_batch, max_seq=max_seq, **knobs)
+        self.mk = B.Megakernel(self.cfg, self.dW)
+        self.tokens = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.positions = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.logits = torch.zeros(batch, mc.vocab, dtype=torch.float32, device=device)
+
+    def set_inputs(self, tokens, positions):
+        import torch
+        self.tokens.copy_(torch.as_tensor(np.asarray(tokens, np.int32)))
+        self.positions.copy_(torch.as_tensor(np.asarray(positions, np.int32)))
+
+    def step(self) -> int:
+        return self.mk.decode_step(self.batch, self.tokens, self.positions, self.kv, self.logits)
+
+    def step_checked(self):
+        rc = self.step()
+        if rc != B.MK_OK:
+            raise B.MkError(rc, "mk_decode_step")
+        rc = self.mk.sync_status()
+        if rc != B.MK_OK:
+            raise B.MkError(rc, "device")
+
+    def advance_greedy(self):
+        """Feed the arg max of the last logits at the next position."""
+        import torch
+        self.tokens.copy_(torch.argmax(self.logits, dim=-1).to(torch.int32))
+        self.positions.add_(1)
+
+    def kv_host(self) -> np.ndarray:
+        return self.kv.cpu().numpy().view(np.uint16)
+
+    def buffer(self, which: int, shape, dtype=np.float32) -> np.ndarray:
+        """Copy of one of the library's internal buffers (mk_get_buffer)."""
+        import ctypes
+        import torch
+        ptr, nbytes = self.mk.buffer(which)
+        out = np.empty(shape, dtype=dtype)
+        assert out.nbytes <= nbytes
+        torch.cuda.synchronize()
+        hip = ctypes.CDLL("libamdhip64.so")
+        rc = hip.hipMemcpy(ctypes.c_void_p(out.ctypes.data), ctypes.c_void_p(ptr),
+                           ctypes.c_size_t(out.nbytes), 2)  # device to host
+        assert rc == 0, rc
+        return out
+
+    def close(self):
+        self.mk.close()
+
+
+def _is_device(W) -> bool:
+    return not isinstance(W.get("embed"), np.ndarray)
+
+
+def greedy_run(sess: Session, tokens, positions, steps: int):
+    """Run ``steps`` greedy steps; returns (fed tokens, logits) per step on
+    the host."""
+    sess.set_inputs(tokens, positions)
+    fed: List[np.ndarray] = []
+    outs: List[np.ndarray] = []
+    for _ in range(steps):
+        fed.append(sess.tokens.cpu().numpy().copy())
+        sess.step_checked()
+        outs.append(sess.logits.cpu().numpy().copy())
+        sess.advance_greedy()
+    return fed, outs

@@ -1,0 +1,114 @@
+"""Host-only tests of the C-ABI library: it loads, exports every entry
+point include/mk.h declares, validates arguments without a GPU, and its
+scheduler's plans pass the static checks and simulated interleavings (and a
+deliberately broken plan is caught).  No compute call needs a GPU here."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from persistent_interpreter_amd import binding as B
+from persistent_interpreter_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(B.LIB_PATH):
+        from persistent_interpreter_amd import build
+        build.build()
+    return B.lib()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "mk.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mk_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert {"mk_create", "mk_decode_step", "mk_destroy"} <= set(names)
+    lib = C.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_version_and_strerror():
+    assert B.lib().mk_version() == 100
+    for code in (0, -1, -2, -3, -4, -5, -6, -10, -11, -12, -99):
+        assert len(B.strerror(code)) > 0
+
+
+def test_null_arguments_rejected_without_gpu():
+    L = B.lib()
+    out = C.c_void_p()
+    assert L.mk_create(None, None, C.byref(out)) == B.MK_ERR_INVALID_ARG
+    cfg = B.make_config(synth.CONFIGS["tiny"])
+    assert L.mk_create(C.byref(cfg), None, C.byref(out)) == B.MK_ERR_INVALID_ARG
+    assert L.mk_create(C.byref(cfg), None, None) == B.MK_ERR_INVALID_ARG
+    assert L.mk_decode_step(None, 1, None, None, None, None, None) == B.MK_ERR_INVALID_ARG
+    assert L.mk_sync_status(None) == B.MK_ERR_INVALID_ARG
+    L.mk_destroy(None)  # NULL-safe
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("n_kv_heads", 3, B.MK_ERR_UNSUPPORTED),     # 4 % 3 != 0
+    ("head_dim", 96, B.MK_ERR_UNSUPPORTED),
+    ("hidden", 260, B.MK_ERR_UNSUPPORTED),       # not a multiple of 8
+    ("kv_splits", 65, B.MK_ERR_UNSUPPORTED),
+    ("n_layers", 0, B.MK_ERR_INVALID_ARG),
+    ("max_seq", 0, B.MK_ERR_INVALID_ARG),
+])
+def test_bad_configs(field, value, code):
+    cfg = B.make_config(synth.CONFIGS["tiny"])
+    setattr(cfg, field, value)
+    rc, rep = B.plan_check(cfg, 1, 8)
+    assert rc == code, rep.msg
+
+
+def test_batch_out_of_range():
+    cfg = B.make_config(synth.CONFIGS["tiny"], max_batch=2)
+    assert B.plan_check(cfg, 3, 8)[0] == B.MK_ERR_INVALID_ARG
+    assert B.plan_check(cfg, 0, 8)[0] == B.MK_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name,cus,batch", [
+    ("tiny", 256, 1), ("tiny", 13, 1), ("tiny", 1, 1), ("tiny", 8, 3),
+    ("llama1b", 256, 1), ("llama1b", 31, 1), ("llama1b", 256, 8),
+    ("qwen3_8b", 256, 1), ("llama70b", 256, 4)])
+def test_plans_validate(name, cus, batch):
+    mc = synth.CONFIGS[name]
+    cfg = B.make_config(mc, max_batch=max(batch, 1))
+    runs = 4 if mc.n_layers > 2 else 40
+    rc, rep = B.plan_check(cfg, batch, cus, sim_runs=runs, seed=7)
+    assert rc == B.MK_OK, rep.msg
+    assert rep.sim_errors == 0 and rep.sim_runs == runs
+    # every weight byte of the model is streamed exactly once per step
+    norms = (2 * mc.n_layers + 1) * mc.hidden * 2
+    if mc.qk_norm:
+        norms += 2 * mc.n_layers * mc.head_dim * 2
+    expect = mc.weight_bytes() - norms
+    assert rep.weight_bytes == expect
+    assert rep.max_cu_bytes * cus >= rep.weight_bytes
+
+
+def test_adversarial_interleavings_7160():
+    """The count of adversarial schedules validated by the static
+    schedule-synthesis work cited on the megakernel index page."""
+    cfg = B.make_config(synth.CONFIGS["tiny"])
+    rc, rep = B.plan_check(cfg, 1, 16, sim_runs=7160, seed=2026)
+    assert rc == B.MK_OK, rep.msg
+    assert rep.sim_runs == 7160 and rep.sim_errors == 0
+
+
+@pytest.mark.parametrize("corrupt", [1, 2, 3])
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_corrupted_plans_are_caught(corrupt, seed):
+    cfg = B.make_config(synth.CONFIGS["tiny"])
+    rc, rep = B.plan_check(cfg, 1, 16, sim_runs=200, corrupt=corrupt, seed=seed)
+    assert rc != B.MK_OK
+    assert rep.sim_errors > 0 and rep.msg
