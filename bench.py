@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Decode benchmark of the persistent megakernel on one MI355X.
+
+Workload: the Llama-1B-shaped decoder (16 layers, hidden 2048, 32/8 heads,
+head_dim 64, SwiGLU 8192, vocab 128256, tied embeddings, RoPE theta 5e5) at
+batch 1 with 512 prior KV positions, greedy decoding.  Weights and the KV
+cache are seeded synthetic bf16 tensors (persistent_interpreter_amd.synth).
+
+A step is one ``mk_decode_step`` launch (the whole forward pass in one
+persistent kernel) followed by the harness's greedy argmax and position
+increment, all on one stream.  ``value`` is tokens/s over the K timed steps
+(inputs resident in HBM).  ``roofline`` prices the megakernel against
+MI355X's 8 TB/s: algorithmic bytes per launch (every weight byte once, the
+embedding row, K and V of slots 0..p) over its average duration measured
+with HIP events on the launch stream.  ``cpu_baseline`` times the CPU oracle
+on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 32] [--warmup 3]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "decode tokens/s at batch 1 (Llama-1B shape) + % of peak HBM GB/s"
+H100_STEP_S = 1.0e-3   # the pages' ~1 ms Llama-1B batch-1 forward on H100
+
+
+def overhead(t_real: float, t_min: float) -> float:
+    """Share of a step not explained by moving its bytes at peak bandwidth:
+    (t_real - t_min) / t_real (chapter "Quand ne pas le faire", section 9.1)."""
+    return (t_real - t_min) / t_real
+
+
+def recovered(t_before: float, t_after: float, t_min: float) -> float:
+    """Fraction of the removable time a faster implementation recovered."""
+    return (t_before - t_after) / (t_before - t_min)
+
+
+def algorithmic_bytes(mc, positions) -> int:
+    """Bytes a decode step must read: every weight tensor once, one
+    embedding row per sequence, and K and V of slots 0..p of every layer."""
+    b = mc.weight_bytes() + 2 * mc.hidden * len(positions)
+    for p in positions:
+        b += 2 * 2 * mc.n_layers * mc.n_kv_heads * mc.head_dim * (int(p) + 1)
+    return b
+
+
+def cpu_baseline(mc, W, kv0, tok, pos, fed, gpu_logits, budget_s=20.0):
+    """Time the CPU oracle on the first steps of the same greedy run (teacher
+    forced on the GPU's tokens) and compare its logits with the GPU's."""
+    import oracle as O
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    Wf = O.upcast_weights(W)            # one-time decode of bf16 weights
+    kv = kv0.copy()
+    times, worst, match = [], 0.0, 0
+    t_all = time.perf_counter()
+    for i in range(len(fed)):
+        t0 = time.perf_counter()
+        ref = O.decode_step(mc, Wf, fed[i], pos + i, kv)
+        times.append(time.perf_counter() - t0)
+        worst = max(worst, float(np.abs(ref - gpu_logits[i]).max()))
+        match += int(np.array_equal(np.argmax(ref, -1), np.argmax(gpu_logits[i], -1)))
+        if time.perf_counter() - t_all > budget_s and i >= 1:
+            break
+    n = len(times)
+    med = float(np.median(times))
+    return ({"value": round(len(tok) / med, 3), "unit": "tokens/s", "cores": threads,
+             "kind": "oracle",
+             "sample": f"{n} greedy decode steps of the same workload (numpy fp32 "
+                       f"oracle, weights decoded to fp32 once beforehand), median "
+                       f"{med * 1e3:.1f} ms/step"},
+            {"max_abs_dlogit": worst, "greedy_match": f"{match}/{n}"})
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama1b")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (for "
+                         "scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU "
+              "path (batched configs shard as independent replicas, see "
+              "DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
+        return
+
+    from persistent_interpreter_amd import harness, synth
+    mc = synth.CONFIGS[args.workload]
+    K, Wu = args.steps, args.warmup
+    mc = mc.replace(steps=max(K, 32))
+    W = synth.make_weights(mc, threads=16)
+    kv0 = synth.make_kv_cache(mc, filled=mc.prior)
+    tok, pos = synth.make_tokens(mc), synth.make_positions(mc)
+
+    sess = harness.Session(mc, W, kv0.copy())
+    # untimed greedy pass whose logits the oracle checks
+    n_check = min(K, 32)
+    fed, gpu_logits = harness.greedy_run(sess, tok, pos, n_check)
+
+    # warmup, then K timed greedy steps from the same start
+    stream = torch.cuda.current_stream()
+    sess.set_inputs(tok, pos)
+    for _ in range(Wu):
+        sess.step_checked()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    start_pos = torch.as_tensor(np.asarray(pos, np.int32)).cuda()
+    sess.set_inputs(tok, pos)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        if i and i % mc.steps == 0:
+            sess.positions.copy_(start_pos)
+        ev[i][0].record(stream)
+        rc = sess.step()
+        ev[i][1].record(stream)
+        if rc != 0:
+            raise RuntimeError(f"mk_decode_step failed: {rc}")
+        sess.advance_greedy()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = sess.mk.sync_status()
+    if st != 0:
+        raise RuntimeError(f"device error {st}")
+    kern = np.array([a.elapsed_time(b) * 1e-3 for a, b in ev])   # seconds
+
+    positions = [np.asarray(pos) + (i % mc.steps) for i in range(K)]
+    bytes_per = float(np.mean([algorithmic_bytes(mc, p) for p in positions]))
+    t_kern = float(np.mean(kern))
+    achieved = bytes_per / t_kern / 1e9
+    tok_s = mc.batch * K / wall
+    out = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": Wu,
+        "ms_per_step": round(wall / K * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tok_s / (1.0 / H100_STEP_S), 4),
+        "baseline_ref": "pages' ~1 ms Llama-1B batch-1 forward on H100 (context, other hardware)",
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{mc.name}: {mc.n_layers} layers, hidden {mc.hidden}, "
+                               f"{mc.n_q_heads}/{mc.n_kv_heads} heads x {mc.head_dim}, "
+                               f"FFN {mc.ffn_dim}, vocab {mc.vocab}, batch {mc.batch}, "
+                               f"{mc.prior} prior KV positions, greedy",
+                   "batch": mc.batch, "prior_positions": mc.prior, "accumulate": "fp32",
+                   "parallelism": "1 GPU, 1 persistent launch per step"},
+        "kernel_us": {"mean": round(t_kern * 1e6, 2),
+                      "median": round(float(np.median(kern)) * 1e6, 2),
+                      "p10": round(float(np.percentile(kern, 10)) * 1e6, 2),
+                      "p90": round(float(np.percentile(kern, 90)) * 1e6, 2)},
+        "hbm_pct_of_peak": round(100 * achieved / PEAK_HBM_GBS, 2),
+        "overhead": round(overhead(t_kern, bytes_per / (PEAK_HBM_GBS * 1e9)), 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None,
+                     "kernel": "mk::mk_interp",
+                     "bytes_per_launch": int(bytes_per)},
+    }
+    if not args.no_cpu:
+        cpu, parity = cpu_baseline(mc, W, kv0, tok, pos, fed, gpu_logits)
+        out["cpu_baseline"] = cpu
+        out["parity"] = parity
+    sess.close()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

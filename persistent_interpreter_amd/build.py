@@ -36,25 +36,29 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the library; returns its path."""
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every source and link the library; returns its path.
+    ``defines`` (e.g. ``["MK_DEPTH=2"]``) override compile-time knobs."""
+    out_dir = os.path.dirname(out)
+    os.makedirs(out_dir, exist_ok=True)
+    dflags = [f"-D{d}" for d in defines]
     objs = []
-    k_obj = os.path.join(OUT_DIR, "mk_kernel.o")
-    _run([HIPCC, *DEVICE_FLAGS, "-c", os.path.join(CSRC, "mk_kernel.hip"),
+    stem = os.path.splitext(os.path.basename(out))[0]
+    k_obj = os.path.join(out_dir, f"{stem}_kernel.o")
+    _run([HIPCC, *DEVICE_FLAGS, *dflags, "-c", os.path.join(CSRC, "mk_kernel.hip"),
           "-o", k_obj])
     objs.append(k_obj)
     for src in ("mk_sched.cpp", "mk_abi.cpp"):
-        o = os.path.join(OUT_DIR, src.replace(".cpp", ".o"))
-        _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", o])
+        o = os.path.join(out_dir, f"{stem}_" + src.replace(".cpp", ".o"))
+        _run(["g++", *HOST_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", o])
         objs.append(o)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp,
           f"-L{ROCM}/lib", "-lamdhip64"])
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

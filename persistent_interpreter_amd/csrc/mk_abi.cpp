@@ -32,7 +32,9 @@ struct DevPlan {
   uint32_t *d_ctr = nullptr;
   uint32_t *d_target = nullptr;
   float *d_part = nullptr;
-  size_t ctr_bytes = 0;
+  uint64_t *d_trace = nullptr;
+  size_t ctr_bytes = 0, trace_bytes = 0;
+  uint32_t trace_stride = 0;
   uint32_t epoch = 0;
 };
 
@@ -63,6 +65,7 @@ void free_plan(DevPlan &p) {
   hipFree(p.d_ctr);
   hipFree(p.d_target);
   hipFree(p.d_part);
+  hipFree(p.d_trace);
 }
 
 int check_config(const mk_config *c, std::string &err) {
@@ -98,6 +101,7 @@ struct mk_handle {
   uint32_t *status = nullptr;
   size_t h_bytes = 0, q_bytes = 0, attn_bytes = 0, a_bytes = 0;
   std::map<int, std::unique_ptr<DevPlan>> plans;
+  DevPlan *last_plan = nullptr;
   bool error_pending = false;
 };
 
@@ -274,6 +278,20 @@ static int get_plan(mk_handle *h, int batch, DevPlan **out) {
     free_plan(*dp);
     return MK_ERR_HIP;
   }
+  if (h->cfg.flags & MK_FLAG_TRACE) {
+    // header [num_cus, stride, 0, 0] then [num_cus][stride][4] records
+    uint32_t mq = 0;
+    for (int c = 0; c < h->num_cus; ++c) mq = std::max(mq, P.q_off[c + 1] - P.q_off[c]);
+    dp->trace_stride = mq;
+    dp->trace_bytes = (4 + (size_t)h->num_cus * mq * 4) * 8;
+    std::vector<uint64_t> init(dp->trace_bytes / 8, 0);
+    init[0] = (uint64_t)h->num_cus;
+    init[1] = mq;
+    if ((rc = upload(&dp->d_trace, init))) {
+      free_plan(*dp);
+      return rc;
+    }
+  }
   *out = dp.get();
   h->plans[batch] = std::move(dp);
   return MK_OK;
@@ -301,6 +319,9 @@ int mk_decode_step(mk_handle *h, int32_t batch, const int32_t *tokens, const int
   a.positions = positions;
   a.kv = (uint16_t *)kv_cache;
   a.logits = logits;
+  a.trace = dp->d_trace;
+  a.trace_stride = dp->trace_stride;
+  h->last_plan = dp;
   a.epoch = dp->epoch;
   a.batch = batch;
   a.n_split = dp->plan.n_split;
@@ -349,8 +370,16 @@ int mk_get_buffer(mk_handle *h, int32_t which, void **ptr, size_t *bytes) {
     case MK_BUF_Q: *ptr = h->q_buf; *bytes = h->q_bytes; return MK_OK;
     case MK_BUF_ATTN: *ptr = h->attn_buf; *bytes = h->attn_bytes; return MK_OK;
     case MK_BUF_A: *ptr = h->a_buf; *bytes = h->a_bytes; return MK_OK;
-    default: *ptr = nullptr; *bytes = 0; return MK_ERR_INVALID_ARG;
+    case MK_BUF_TRACE:
+      if (!h->last_plan || !h->last_plan->d_trace) break;
+      *ptr = h->last_plan->d_trace;
+      *bytes = h->last_plan->trace_bytes;
+      return MK_OK;
+    default: break;
   }
+  *ptr = nullptr;
+  *bytes = 0;
+  return MK_ERR_INVALID_ARG;
 }
 
 }  // extern "C"

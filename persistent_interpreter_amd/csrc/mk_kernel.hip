@@ -34,6 +34,15 @@
 namespace mk {
 
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
+// Global memory is always accessed through address-space-1 pointers: a
+// generic (flat) access would count against the LDS wait counter too, so a
+// later wait for an LDS flag would stall until a global store is
+// acknowledged.
+#define GAS __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ GAS T *G(T *p) { return (GAS T *)p; }
+template <class T>
+__device__ __forceinline__ const GAS T *G(const T *p) { return (const GAS T *)p; }
 typedef float f4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -56,27 +65,55 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 // --------------------------------------------------------------------------
 // device-coherent accesses (relaxed agent-scope atomics -> sc1)
 __device__ __forceinline__ float ld_c(const float *p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
+  return __uint_as_float(__hip_atomic_load(G(reinterpret_cast<const uint32_t *>(p)), __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT));
 }
 __device__ __forceinline__ float2 ld_c2(const float *p) {
-  uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+  uint64_t v = __hip_atomic_load(G(reinterpret_cast<const uint64_t *>(p)), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
   return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
 __device__ __forceinline__ void st_c(float *p, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+  __hip_atomic_store(G(reinterpret_cast<uint32_t *>(p)), __float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_c16(uint16_t *p, uint16_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(G(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint16_t ld_c16(const uint16_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(G(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t ld_cu(const uint32_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(G(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Non-atomic device-coherent (sc1) loads/stores through buffer resources:
+// the same cache policy as the atomics above, but the compiler may keep many
+// in flight.  Ordering against counters/flags is explicit (waitcnt, LDS
+// flags, compiler barriers around the waits).
+constexpr int kSC1 = 16;  // cache-policy bits: sc1
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t rsrc(const void *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ f4 ldc4(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSC1));
+}
+__device__ __forceinline__ u4 ldc4u(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSC1));
+}
+__device__ __forceinline__ float ldc1(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSC1));
+}
+__device__ __forceinline__ uint16_t ldc16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kSC1);
+}
+
+// Wake every sleeping wave of the workgroup (after publishing an LDS flag).
+__device__ __forceinline__ void wake() { asm volatile("s_wakeup" ::: "memory"); }
+#ifndef MK_SLEEP
+#define MK_SLEEP 10
+#endif
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -120,40 +157,75 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 struct Env {
   const DevCtx *__restrict__ cp;  // device context (scalar loads)
+  uint64_t *trace;                // this workgroup's records, or null
   const Instr *q;    // this workgroup's queue
   uint32_t nq;       // its length
   int cu;
-  int64_t t0;
 };
 
 __device__ __forceinline__ int64_t now() { return (int64_t)wall_clock64(); }
 
+// Trace record per queued instruction: [0] op | layer << 8 | unit << 24,
+// [1] sync wave: waits of the first piece satisfied, [2] compute wave 0
+// passed the unit's gate, [3] last compute wave finished (signal time).
+constexpr int kTraceWords = 4;
+__device__ __forceinline__ void trace_put(const Env &e, uint32_t qi, int word, uint64_t v) {
+  if (e.trace) G(e.trace)[(size_t)qi * kTraceWords + word] = v;
+}
+// timestamp record: the clock is only read when tracing
+__device__ __forceinline__ void trace_now(const Env &e, uint32_t qi, int word) {
+  if (e.trace) G(e.trace)[(size_t)qi * kTraceWords + word] = (uint64_t)now();
+}
+
 // Record the first device error and make every wave of this workgroup exit.
 __device__ void raise_error(const Env &e, uint32_t code, uint32_t info) {
-  if (__hip_atomic_load(&e.cp->status[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+  GAS uint32_t *st = G(e.cp->status);
+  if (__hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
     uint32_t zero = 0;
-    if (__hip_atomic_compare_exchange_strong(&e.cp->status[0], &zero, code, __ATOMIC_RELAXED,
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-      __hip_atomic_store(&e.cp->status[1], info, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&e.cp->status[2], (uint32_t)e.cu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__hip_atomic_compare_exchange_strong(st, &zero, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)) {
+      __hip_atomic_store(st + 1, info, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(st + 2, (uint32_t)e.cu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   lds_st(L_ABORT, 1);
 }
 
 // Spin on an LDS condition with the abort flag and the watchdog.
+// Watchdog for spin loops.  The clock (s_memrealtime) is a scalar-memory
+// round trip of about a microsecond under load, so it is read only every 256
+// polls and the deadline is set lazily at the first such read: a short wait
+// never touches the clock.
+struct Watchdog {
+  int64_t deadline = 0;
+  // true when the budget is exhausted
+  __device__ __forceinline__ bool expired(int64_t budget) {
+    const int64_t t = now();
+    if (deadline == 0) {
+      deadline = t + budget;
+      return false;
+    }
+    return t > deadline;
+  }
+};
+
+// Waits on LDS flags sleep between polls; the producer of every flag
+// executes s_wakeup, so a waiter normally resumes right after the flag is
+// set and polling does not flood the LDS queue or the issue slots.
 template <class F>
 __device__ __forceinline__ bool spin_lds(const Env &e, F cond, uint32_t info) {
   if (cond()) return true;
-  int64_t deadline = now() + e.cp->watchdog_ticks;
-  for (;;) {
+  Watchdog wd;
+  for (uint32_t it = 1;; ++it) {
+    __builtin_amdgcn_s_sleep(MK_SLEEP);
     if (cond()) return true;
-    if (lds_ld(L_ABORT)) return false;
-    if (now() > deadline) {
-      raise_error(e, 0xA0000000u | info, 0);
-      return false;
+    if ((it & 63) == 0) {
+      if (lds_ld(L_ABORT)) return false;
+      if (wd.expired(e.cp->watchdog_ticks)) {
+        raise_error(e, 0xA0000000u | info, 0);
+        return false;
+      }
     }
-    __builtin_amdgcn_s_sleep(1);
   }
 }
 
@@ -194,7 +266,10 @@ __device__ __forceinline__ void asm_lds_st(uint32_t off, uint32_t v) {
   asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(off), "v"(v) : "memory");
 }
 
-constexpr int kDepth = 3;  // pages in flight per loader wave (48 loads <= 63)
+#ifndef MK_DEPTH
+#define MK_DEPTH 3
+#endif
+constexpr int kDepth = MK_DEPTH;  // pages in flight per loader wave (16 loads each, <= 63)
 
 template <int N>
 __device__ __forceinline__ void wait_vm_n() {
@@ -212,6 +287,7 @@ __device__ void loader_role(const Env &e, const Args &a, int lw) {
   int npend = 0;
   auto publish_oldest = [&]() {
     asm_lds_st(L_FILLED + 4 * (oldest % P), oldest + 1);
+    wake();
     oldest += kNLW;
     --npend;
   };
@@ -239,12 +315,14 @@ __device__ void loader_role(const Env &e, const Args &a, int lw) {
         const uint32_t need = n - P + 1;
         if (min_cons() < need) {
           drain();
-          int64_t deadline = now() + e.cp->watchdog_ticks;
-          for (;;) {
+          Watchdog wd;
+          for (uint32_t it = 1;; ++it) {
+            __builtin_amdgcn_s_sleep(MK_SLEEP);
             if (min_cons() >= need) break;
-            if (asm_lds_ld(L_ABORT)) { wait_vm0(); return; }
-            if (now() > deadline) { raise_error(e, 0xB0000000u | qi, n); wait_vm0(); return; }
-            __builtin_amdgcn_s_sleep(1);
+            if ((it & 63) == 0) {
+              if (asm_lds_ld(L_ABORT)) { wait_vm0(); return; }
+              if (wd.expired(e.cp->watchdog_ticks)) { raise_error(e, 0xB0000000u | qi, n); wait_vm0(); return; }
+            }
           }
         }
       }
@@ -301,16 +379,15 @@ __device__ bool wait_group(const Env &e, const Args &a, uint32_t grp, uint32_t q
   const int lane = lane_id();
   const uint32_t *cp = a.ctr + ((size_t)grp * kXcds + (lane & 7)) * kCtrStride;
   const uint32_t need = a.grp_target[grp * kXcds + (lane & 7)] * a.epoch;
-  int64_t deadline = 0;
+  Watchdog wd;
   for (uint32_t it = 0;; ++it) {
     bool ok = true;
     if (lane < kXcds) ok = (int32_t)(ld_cu(cp) - need) >= 0;
     if (__all(ok)) return true;
-    if (it == 0) deadline = now() + e.cp->watchdog_ticks;
-    if ((it & 15) == 15) {
+    if ((it & 63) == 63) {
       if (lds_ld(L_ABORT)) return false;
       if (ld_cu(&e.cp->status[0]) != 0) { lds_st(L_ABORT, 1); return false; }
-      if (now() > deadline) {
+      if (wd.expired(e.cp->watchdog_ticks)) {
         raise_error(e, 0xC0000000u | grp, qi);
         return false;
       }
@@ -327,25 +404,16 @@ __device__ __forceinline__ void norm_src(const Env &e, const Args &a, const Inst
   h = nullptr;
   emb = nullptr;
   if (d.op == OP_QKV) {
-    w = c.layers[d.layer].attn_norm;
+    w = G(c.layers)[d.layer].attn_norm;
     if (d.layer == 0) emb = c.embed + (size_t)a.tokens[b] * c.H;
     else h = c.h_buf + (size_t)(2 * d.layer) * HB + (size_t)b * c.H;
   } else if (d.op == OP_FFN) {
-    w = c.layers[d.layer].ffn_norm;
+    w = G(c.layers)[d.layer].ffn_norm;
     h = c.h_buf + (size_t)(2 * d.layer + 1) * HB + (size_t)b * c.H;
   } else {  // OP_LM
     w = c.final_norm;
     h = c.h_buf + (size_t)(2 * c.L) * HB + (size_t)b * c.H;
   }
-}
-
-__device__ __forceinline__ f4 load_src4(const float *h, const uint16_t *emb, uint32_t i) {
-  if (emb) {
-    uint2 u = *reinterpret_cast<const uint2 *>(emb + i);
-    return f4{bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y)};
-  }
-  float2 p = ld_c2(h + i), q = ld_c2(h + i + 2);
-  return f4{p.x, p.y, q.x, q.y};
 }
 
 __device__ void sync_role(const Env &e, const Args &a) {
@@ -383,38 +451,118 @@ __device__ void sync_role(const Env &e, const Args &a) {
       }
       float *xs = reinterpret_cast<float *>(smem + L_XS + (seq % kNXS) * kXSlotBytes);
       const int b = 0;
+      if (k == 0 && lane == 0) {
+        trace_put(e, qi, 0, (uint64_t)d.op | ((uint64_t)d.layer << 8) | ((uint64_t)d.unit << 24));
+        trace_now(e, qi, 1);
+      }
+      if (k == 0 && (d.op == OP_O || d.op == OP_DOWN)) {
+        // residual input of the unit's rows, added to by the compute waves
+        float *accs = reinterpret_cast<float *>(smem + L_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4);
+        const size_t HB = (size_t)c.max_batch * c.H;
+        float rv[kAccFloats / 64];
+        if (d.op == OP_O && d.layer == 0) {
+          const GAS uint16_t *er = G(c.embed) + (size_t)a.tokens[b] * c.H + d.item0;
+#pragma unroll
+          for (int m = 0; m < kAccFloats / 64; ++m) {
+            const uint32_t r = (uint32_t)(lane + 64 * m);
+            rv[m] = r < d.n_items ? bf16f(er[r]) : 0.f;
+          }
+        } else {
+          const int idx = d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1;
+          const rsrc_t rr = rsrc(c.h_buf + (size_t)idx * HB + (size_t)b * c.H + d.item0);
+#pragma unroll
+          for (int m = 0; m < kAccFloats / 64; ++m) {
+            const uint32_t r = (uint32_t)(lane + 64 * m);
+            rv[m] = r < d.n_items ? ldc1(rr, r * 4) : 0.f;
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < kAccFloats / 64; ++m) {
+          const uint32_t r = (uint32_t)(lane + 64 * m);
+          if (r < d.n_items) accs[r] = rv[m];
+        }
+      }
       if (d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM) {
         const float *h;
         const uint16_t *emb, *w;
         norm_src(e, a, d, b, h, emb, w);
+        const rsrc_t hr = rsrc(h ? (const void *)h : (const void *)emb);
+        // one batch of up to 2048 elements (8 x 4 per lane) in flight
+        auto load_batch = [&](uint32_t e0, f4 (&v)[8]) {
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const uint32_t i = e0 + (uint32_t)(lane + 64 * m) * 4;
+            if (i < (uint32_t)c.H) {
+              if (emb) {
+                const uint64_t uu = *G(reinterpret_cast<const uint64_t *>(emb + i));
+                const uint2 u = make_uint2((uint32_t)uu, (uint32_t)(uu >> 32));
+                v[m] = f4{bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y)};
+              } else {
+                v[m] = ldc4(hr, i * 4);
+              }
+            } else {
+              v[m] = f4{0.f, 0.f, 0.f, 0.f};
+            }
+          }
+        };
+        f4 hv[8];
         if (k == 0) {
           float ss = 0.f;
-          for (uint32_t i = lane * 4; i < (uint32_t)c.H; i += 256) {
-            f4 v = load_src4(h, emb, i);
-            ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+          for (uint32_t e0 = 0; e0 < (uint32_t)c.H; e0 += 2048) {
+            load_batch(e0, hv);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) ss += hv[m].x * hv[m].x + hv[m].y * hv[m].y + hv[m].z * hv[m].z + hv[m].w * hv[m].w;
           }
           ss = wave_sum(ss);
           rs = 1.0f / sqrtf(ss / (float)c.H + c.eps);
         }
         const uint32_t k0 = k * d.kc;
-        for (uint32_t i = lane * 4; i < d.kc; i += 256) {
-          f4 v = load_src4(h, emb, k0 + i);
-          uint2 wu = *reinterpret_cast<const uint2 *>(w + k0 + i);
-          f4 o = {v.x * rs * bf_lo(wu.x), v.y * rs * bf_hi(wu.x), v.z * rs * bf_lo(wu.y), v.w * rs * bf_hi(wu.y)};
-          *reinterpret_cast<f4 *>(xs + i) = o;
+        // the last batch loaded is still in hv when H <= 2048 (then nk == 1)
+        for (uint32_t e0 = 0; e0 < d.kc; e0 += 2048) {
+          if (c.H > 2048 || k0 != 0) load_batch(k0 + e0, hv);
+          uint2 wu[8];
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const uint32_t i = e0 + (uint32_t)(lane + 64 * m) * 4;
+            wu[m] = make_uint2(0, 0);
+            if (i < d.kc) {
+              const uint64_t t = *G(reinterpret_cast<const uint64_t *>(w + k0 + i));
+              wu[m] = make_uint2((uint32_t)t, (uint32_t)(t >> 32));
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const uint32_t i = e0 + (uint32_t)(lane + 64 * m) * 4;
+            if (i < d.kc) {
+              const f4 v = hv[m];
+              f4 o = {v.x * rs * bf_lo(wu[m].x), v.y * rs * bf_hi(wu[m].x), v.z * rs * bf_lo(wu[m].y),
+                      v.w * rs * bf_hi(wu[m].y)};
+              *reinterpret_cast<f4 *>(xs + i) = o;
+            }
+          }
         }
       } else if (d.op == OP_O || d.op == OP_DOWN) {
         const float *src = d.op == OP_O
                                ? c.attn_buf + ((size_t)d.layer * c.max_batch + b) * (c.nq * c.hd)
                                : c.a_buf + ((size_t)d.layer * c.max_batch + b) * c.F;
-        const uint32_t k0 = k * d.kc;
-        for (uint32_t i = lane * 4; i < d.kc; i += 256) {
-          float2 p = ld_c2(src + k0 + i), q = ld_c2(src + k0 + i + 2);
-          *reinterpret_cast<f4 *>(xs + i) = f4{p.x, p.y, q.x, q.y};
+        const rsrc_t sr = rsrc(src + k * d.kc);
+        for (uint32_t e0 = 0; e0 < d.kc; e0 += 2048) {
+          f4 v[8];
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const uint32_t i = e0 + (uint32_t)(lane + 64 * m) * 4;
+            if (i < d.kc) v[m] = ldc4(sr, i * 4);
+          }
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const uint32_t i = e0 + (uint32_t)(lane + 64 * m) * 4;
+            if (i < d.kc) *reinterpret_cast<f4 *>(xs + i) = v[m];
+          }
         }
       }
       wait_lgkm0();
       if (lane == 0) lds_st(L_XREADY, seq + 1);
+      wake();
     }
   }
 }
@@ -424,23 +572,39 @@ __device__ void sync_role(const Env &e, const Args &a) {
 
 // Dot product of one weight piece (bf16, in LDS) with the activation piece
 // held in registers: lane l owns 16-byte groups l, l+64, l+128, l+192.
+// The page reads are one inline-asm block: the compiler's wait-count pass,
+// seeing the loaders' direct-to-LDS loads in the same kernel, would otherwise
+// put a vmcnt(0) before each read and make every row wait for the wave's
+// outstanding global stores.  Lanes past the piece read other LDS bytes of
+// the ring (in bounds) and are zeroed.
 __device__ __forceinline__ float dot_piece(const char *piece, const float (&xr)[32], uint32_t n16) {
   const int lane = lane_id();
+  const uint32_t addr = (uint32_t)(uintptr_t)((LDS_AS const char *)piece) + (uint32_t)lane * 16;
+  u4 w[4];
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\t"
+      "ds_read_b128 %3, %4 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(w[0]), "=v"(w[1]), "=v"(w[2]), "=v"(w[3])
+      : "v"(addr));
+  if (n16 < 256) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if ((uint32_t)lane + 64u * m >= n16) w[m] = u4{0u, 0u, 0u, 0u};
+  }
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const uint32_t g = (uint32_t)lane + 64u * m;
-    if (g < n16) {
-      u4 w = *reinterpret_cast<const u4 *>(piece + g * 16);
-      a0 = fmaf(bf_lo(w.x), xr[m * 8 + 0], a0);
-      a1 = fmaf(bf_hi(w.x), xr[m * 8 + 1], a1);
-      a0 = fmaf(bf_lo(w.y), xr[m * 8 + 2], a0);
-      a1 = fmaf(bf_hi(w.y), xr[m * 8 + 3], a1);
-      a0 = fmaf(bf_lo(w.z), xr[m * 8 + 4], a0);
-      a1 = fmaf(bf_hi(w.z), xr[m * 8 + 5], a1);
-      a0 = fmaf(bf_lo(w.w), xr[m * 8 + 6], a0);
-      a1 = fmaf(bf_hi(w.w), xr[m * 8 + 7], a1);
-    }
+    a0 = fmaf(bf_lo(w[m].x), xr[m * 8 + 0], a0);
+    a1 = fmaf(bf_hi(w[m].x), xr[m * 8 + 1], a1);
+    a0 = fmaf(bf_lo(w[m].y), xr[m * 8 + 2], a0);
+    a1 = fmaf(bf_hi(w[m].y), xr[m * 8 + 3], a1);
+    a0 = fmaf(bf_lo(w[m].z), xr[m * 8 + 4], a0);
+    a1 = fmaf(bf_hi(w[m].z), xr[m * 8 + 5], a1);
+    a0 = fmaf(bf_lo(w[m].w), xr[m * 8 + 6], a0);
+    a1 = fmaf(bf_hi(w[m].w), xr[m * 8 + 7], a1);
   }
   return wave_sum(a0 + a1);
 }
@@ -466,160 +630,250 @@ __device__ __forceinline__ size_t kv_off(const DevCtx &c, int l, int t, int b, i
   return ((((size_t)l * 2 + t) * c.max_batch + b) * c.nkv + g) * (size_t)c.max_seq * c.hd + (size_t)s * c.hd;
 }
 
-// Epilogue of one finished item (row or row pair), executed by lane 0.
-__device__ void epilogue(const Env &e, const Args &a, const Instr &d, uint32_t i, float v0, float v1) {
+// Epilogue of a finished GEMV instruction, run by its last compute wave
+// over the staged row results R (LDS): row i*ipw + s of the unit.  The
+// outputs of 64 rows go out in one vector store.
+//   QKV : RoPE on q/k pairs (i, i + hd/2), q -> fp32 scratch, k/v -> bf16
+//         cache slot p;   O, DOWN: R already holds residual + dot;
+//   FFN : a = silu(gate) * up;   LM: logits.
+__device__ void unit_epilogue(const Env &e, const Args &a, const Instr &d, const float *R) {
   const DevCtx &c = *e.cp;
+  const int lane = lane_id();
   const int b = 0;
   const size_t HB = (size_t)c.max_batch * c.H;
-  switch (d.op) {
-    case OP_QKV: {
-      const uint32_t half = (uint32_t)c.hd >> 1;
-      const uint32_t ppg = (uint32_t)(c.G + 2) * half;
-      const uint32_t pp = d.item0 + i;
-      const uint32_t g = pp / ppg;
-      const uint32_t rr = pp - g * ppg;
-      const uint32_t hs = rr / half;
-      const uint32_t ii = rr - hs * half;
-      const int p = a.positions[b];
-      if (hs <= (uint32_t)c.G) {
-        const float cs = c.rope[((size_t)p * half + ii) * 2], sn = c.rope[((size_t)p * half + ii) * 2 + 1];
-        const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
-        if (hs < (uint32_t)c.G) {
-          float *q = c.q_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + (g * c.G + hs)) * c.hd;
-          st_c(q + ii, r0);
-          st_c(q + ii + half, r1);
+  for (uint32_t i = (uint32_t)lane; i < d.n_items; i += 64) {
+    switch (d.op) {
+      case OP_QKV: {
+        const float v0 = R[2 * i], v1 = R[2 * i + 1];
+        const uint32_t half = (uint32_t)c.hd >> 1;
+        const uint32_t ppg = (uint32_t)(c.G + 2) * half;
+        const uint32_t pp = d.item0 + i;
+        const uint32_t g = pp / ppg;
+        const uint32_t rr = pp - g * ppg;
+        const uint32_t hs = rr / half;
+        const uint32_t ii = rr - hs * half;
+        const int p = a.positions[b];
+        if (hs <= (uint32_t)c.G) {
+          const float cs = G(c.rope)[((size_t)p * half + ii) * 2], sn = G(c.rope)[((size_t)p * half + ii) * 2 + 1];
+          const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
+          if (hs < (uint32_t)c.G) {
+            float *q = c.q_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + (g * c.G + hs)) * c.hd;
+            st_c(q + ii, r0);
+            st_c(q + ii + half, r1);
+          } else {
+            uint16_t *k = a.kv + kv_off(c, d.layer, 0, b, g, p);
+            st_c16(k + ii, f2bf(r0));
+            st_c16(k + ii + half, f2bf(r1));
+          }
         } else {
-          uint16_t *k = a.kv + kv_off(c, d.layer, 0, b, g, p);
-          st_c16(k + ii, f2bf(r0));
-          st_c16(k + ii + half, f2bf(r1));
+          uint16_t *v = a.kv + kv_off(c, d.layer, 1, b, g, p);
+          st_c16(v + ii, f2bf(v0));
+          st_c16(v + ii + half, f2bf(v1));
         }
-      } else {
-        uint16_t *v = a.kv + kv_off(c, d.layer, 1, b, g, p);
-        st_c16(v + ii, f2bf(v0));
-        st_c16(v + ii + half, f2bf(v1));
+        break;
       }
-      break;
-    }
-    case OP_O: {
-      const uint32_t r = d.item0 + i;
-      const float hin = d.layer == 0 ? bf16f(c.embed[(size_t)a.tokens[b] * c.H + r])
-                                     : ld_c(c.h_buf + (size_t)(2 * d.layer) * HB + (size_t)b * c.H + r);
-      st_c(c.h_buf + (size_t)(2 * d.layer + 1) * HB + (size_t)b * c.H + r, hin + v0);
-      break;
-    }
-    case OP_FFN: {
-      const uint32_t j = d.item0 + i;
-      const float sg = v0 / (1.0f + expf(-v0));
-      st_c(c.a_buf + ((size_t)d.layer * c.max_batch + b) * c.F + j, sg * v1);
-      break;
-    }
-    case OP_DOWN: {
-      const uint32_t r = d.item0 + i;
-      const float hm = ld_c(c.h_buf + (size_t)(2 * d.layer + 1) * HB + (size_t)b * c.H + r);
-      st_c(c.h_buf + (size_t)(2 * d.layer + 2) * HB + (size_t)b * c.H + r, hm + v0);
-      break;
-    }
-    default: {  // OP_LM
-      a.logits[(size_t)b * c.V + d.item0 + i] = v0;
-      break;
+      case OP_O:
+        st_c(c.h_buf + (size_t)(2 * d.layer + 1) * HB + (size_t)b * c.H + d.item0 + i, R[i]);
+        break;
+      case OP_FFN: {
+        const float gt = R[2 * i], up = R[2 * i + 1];
+        st_c(c.a_buf + ((size_t)d.layer * c.max_batch + b) * c.F + d.item0 + i, gt / (1.0f + expf(-gt)) * up);
+        break;
+      }
+      case OP_DOWN:
+        st_c(c.h_buf + (size_t)(2 * d.layer + 2) * HB + (size_t)b * c.H + d.item0 + i, R[i]);
+        break;
+      default:  // OP_LM
+        G(a.logits)[(size_t)b * c.V + d.item0 + i] = R[i];
+        break;
     }
   }
 }
 
-// I2: split-KV attention partials for query head (g*G + h) of sequence b.
-__device__ void attn_body(const Env &e, const Args &a, const Instr &d, int h, float *qs) {
+// The first PF positions of the split that precede p are step-invariant
+// (written by earlier steps), so their K/V are loaded before the unit's
+// dependency gate; q and the new slot p are loaded after it.
+template <int DPL, class Gate>
+__device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Gate gate) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
   const int b = (int)d.b, g = (int)d.aux0, s = (int)d.aux1;
   const int j = g * c.G + h;
-  const int hd = c.hd, dpl = hd >> 6;
+  constexpr int hd = 64 * DPL, PF = 20 / DPL;  // prefetch depth (register budget)
   const int p = a.positions[b];
   const int lo = s * a.split_len;
   const int hi = min(lo + a.split_len, p + 1);
-  const float *qp = c.q_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + j) * hd;
-  for (int m = 0; m < dpl; ++m) qs[lane + 64 * m] = ld_c(qp + lane + 64 * m);
-  wait_lgkm0();
-  float mrun = -INFINITY, lrun = 0.f, o[2] = {0.f, 0.f};
-  const uint16_t *K = a.kv + kv_off(c, d.layer, 0, b, g, 0);
-  const uint16_t *Vv = a.kv + kv_off(c, d.layer, 1, b, g, 0);
-  for (int c0 = lo; c0 < hi; c0 += 64) {
-    const int tau = c0 + lane;
-    float sc = -INFINITY;
-    if (tau < hi) {
-      float acc = 0.f;
-      const uint16_t *kr = K + (size_t)tau * hd;
-      if (tau == p) {
-        for (int d2 = 0; d2 < hd; d2 += 2) {
-          acc = fmaf(qs[d2], bf16f(ld_c16(kr + d2)), acc);
-          acc = fmaf(qs[d2 + 1], bf16f(ld_c16(kr + d2 + 1)), acc);
-        }
-      } else {
-        for (int d8 = 0; d8 < hd; d8 += 8) {
-          u4 w = *reinterpret_cast<const u4 *>(kr + d8);
-          f4 q0 = *reinterpret_cast<const f4 *>(qs + d8);
-          f4 q1 = *reinterpret_cast<const f4 *>(qs + d8 + 4);
-          acc = fmaf(q0.x, bf_lo(w.x), acc);
-          acc = fmaf(q0.y, bf_hi(w.x), acc);
-          acc = fmaf(q0.z, bf_lo(w.y), acc);
-          acc = fmaf(q0.w, bf_hi(w.y), acc);
-          acc = fmaf(q1.x, bf_lo(w.z), acc);
-          acc = fmaf(q1.y, bf_hi(w.z), acc);
-          acc = fmaf(q1.z, bf_lo(w.w), acc);
-          acc = fmaf(q1.w, bf_hi(w.w), acc);
-        }
-      }
-      sc = acc * c.attn_scale;
-    }
-    const float cm = wave_max(sc);
-    const float mn = fmaxf(mrun, cm);
-    const float pt = tau < hi ? expf(sc - mn) : 0.f;
-    const float scale = mrun == -INFINITY ? 0.f : expf(mrun - mn);
-    lrun = lrun * scale + wave_sum(pt);
-    o[0] *= scale;
-    o[1] *= scale;
-    const int nt = min(64, hi - c0);
-    for (int t = 0; t < nt; ++t) {
-      const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pt), t));
-      const uint16_t *vr = Vv + (size_t)(c0 + t) * hd;
-      if (c0 + t == p) {
-        for (int m = 0; m < dpl; ++m) o[m] = fmaf(wt, bf16f(ld_c16(vr + lane + 64 * m)), o[m]);
-      } else {
-        for (int m = 0; m < dpl; ++m) o[m] = fmaf(wt, bf16f(vr[lane + 64 * m]), o[m]);
+  const int nt0 = max(0, min(hi - lo, PF));
+  const rsrc_t Kr = rsrc(a.kv + kv_off(c, d.layer, 0, b, g, lo));
+  const rsrc_t Vr = rsrc(a.kv + kv_off(c, d.layer, 1, b, g, lo));
+  uint16_t kk[PF][DPL], vv[PF][DPL];
+  if (nt0 > 0) {
+#pragma unroll
+    for (int t = 0; t < PF; ++t) {
+      const int tt = min(t, nt0 - 1);  // in bounds; unused beyond nt0
+#pragma unroll
+      for (int m = 0; m < DPL; ++m) {
+        kk[t][m] = ldc16(Kr, (uint32_t)(tt * hd + lane + 64 * m) * 2);
+        vv[t][m] = ldc16(Vr, (uint32_t)(tt * hd + lane + 64 * m) * 2);
       }
     }
-    mrun = mn;
+  }
+  if (!gate()) return false;
+  float mrun = -INFINITY, lrun = 0.f, o[DPL], q[DPL];
+  uint16_t kp[DPL], vp[DPL];
+#pragma unroll
+  for (int m = 0; m < DPL; ++m) o[m] = 0.f;
+  if (lo < hi) {
+    // lane = head dimension (dims lane + 64*m) for q, K and V
+    const rsrc_t qr = rsrc(c.q_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + j) * hd);
+    const bool has_p = p < hi;  // the new slot p (written this step) is in the split
+#pragma unroll
+    for (int m = 0; m < DPL; ++m) {
+      q[m] = ldc1(qr, (uint32_t)(lane + 64 * m) * 4);
+      kp[m] = has_p ? ldc16(Kr, (uint32_t)((p - lo) * hd + lane + 64 * m) * 2) : (uint16_t)0;
+      vp[m] = has_p ? ldc16(Vr, (uint32_t)((p - lo) * hd + lane + 64 * m) * 2) : (uint16_t)0;
+    }
+    // first PF positions from the prefetched registers
+    {
+      float sc = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < PF; ++t) {
+        const bool isp = lo + t == p;
+        float pr = 0.f;
+#pragma unroll
+        for (int m = 0; m < DPL; ++m) pr = fmaf(q[m], bf16f(isp ? kp[m] : kk[t][m]), pr);
+        const float st = wave_sum(pr) * c.attn_scale;
+        if (lane == t && t < nt0) sc = st;
+      }
+      const float cm = wave_max(sc);
+      const float pt = lane < nt0 ? expf(sc - cm) : 0.f;
+      lrun = wave_sum(pt);
+#pragma unroll
+      for (int t = 0; t < PF; ++t) {
+        const bool isp = lo + t == p;
+        const float wt = t < nt0 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pt), t)) : 0.f;
+#pragma unroll
+        for (int m = 0; m < DPL; ++m) o[m] = fmaf(wt, bf16f(isp ? vp[m] : vv[t][m]), o[m]);
+      }
+      mrun = cm;
+    }
+    // remaining positions in chunks of 64, 8 rows in flight
+#pragma unroll 1
+    for (int c0 = lo + PF; c0 < hi; c0 += 64) {
+      const int nt = min(64, hi - c0);
+      float sc = -INFINITY;
+#pragma unroll 1
+      for (int t0 = 0; t0 < nt; t0 += 8) {
+        uint16_t k8[8][DPL];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int tt = min(t0 + t, nt - 1);
+#pragma unroll
+          for (int m = 0; m < DPL; ++m)
+            k8[t][m] = ldc16(Kr, (uint32_t)((c0 - lo + tt) * hd + lane + 64 * m) * 2);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          float pr = 0.f;
+#pragma unroll
+          for (int m = 0; m < DPL; ++m) pr = fmaf(q[m], bf16f(k8[t][m]), pr);
+          const float st = wave_sum(pr) * c.attn_scale;
+          if (lane == t0 + t && t0 + t < nt) sc = st;
+        }
+      }
+      const bool valid = lane < nt;
+      const float cm = wave_max(sc);
+      const float mn = fmaxf(mrun, cm);
+      const float pt = valid ? expf(sc - mn) : 0.f;
+      const float scale = mrun == -INFINITY ? 0.f : expf(mrun - mn);
+      lrun = lrun * scale + wave_sum(pt);
+#pragma unroll
+      for (int m = 0; m < DPL; ++m) o[m] *= scale;
+#pragma unroll 1
+      for (int t0 = 0; t0 < nt; t0 += 8) {
+        uint16_t v8[8][DPL];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int tt = min(t0 + t, nt - 1);  // in bounds; weight 0 beyond nt
+#pragma unroll
+          for (int m = 0; m < DPL; ++m)
+            v8[t][m] = ldc16(Vr, (uint32_t)((c0 - lo + tt) * hd + lane + 64 * m) * 2);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float wt = t0 + t < nt
+                               ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pt), min(t0 + t, 63)))
+                               : 0.f;
+#pragma unroll
+          for (int m = 0; m < DPL; ++m) o[m] = fmaf(wt, bf16f(v8[t][m]), o[m]);
+        }
+      }
+      mrun = mn;
+    }
   }
   float *out = a.part_buf + ((((size_t)d.layer * c.max_batch + b) * c.nq + j) * a.n_split + s) * (hd + 4);
-  for (int m = 0; m < dpl; ++m) st_c(out + lane + 64 * m, o[m]);
+#pragma unroll
+  for (int m = 0; m < DPL; ++m) st_c(out + lane + 64 * m, o[m]);
   if (lane == 0) {
     st_c(out + hd, mrun);
     st_c(out + hd + 1, lrun);
   }
+  return true;
 }
 
-// I3: log-sum-exp combine of the split partials of query head (g*G + h).
+// I3: log-sum-exp combine of the split partials of query head (g*G + h):
+// m* = max m_s, w_s = exp(m_s - m*), out = sum w_s o_s / sum w_s l_s; empty
+// splits (m = -inf) get weight 0.
+template <int DPL>
 __device__ void red_body(const Env &e, const Args &a, const Instr &d, int h) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
   const int b = (int)d.b, g = (int)d.aux0;
   const int j = g * c.G + h;
-  const int hd = c.hd, dpl = hd >> 6, ns = a.n_split;
+  constexpr int hd = 64 * DPL, dpl = DPL;
+  const int ns = a.n_split;
   const float *base = a.part_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + j) * (size_t)ns * (hd + 4);
+  const rsrc_t pr = rsrc(base);
+  const uint32_t rowb = (uint32_t)(hd + 4) * 4;
+  // m, l of every split and the first RB splits' o in one round trip
+  constexpr int RB = 16 / DPL;
   float ms = -INFINITY, ls = 0.f;
+  float ov[RB][dpl];
   if (lane < ns) {
-    ms = ld_c(base + (size_t)lane * (hd + 4) + hd);
-    ls = ld_c(base + (size_t)lane * (hd + 4) + hd + 1);
+    ms = ldc1(pr, lane * rowb + hd * 4);
+    ls = ldc1(pr, lane * rowb + hd * 4 + 4);
+  }
+#pragma unroll
+  for (int t = 0; t < RB; ++t) {
+    const int ss = min(t, ns - 1);  // in bounds; weight 0 beyond ns
+#pragma unroll
+    for (int m = 0; m < dpl; ++m) ov[t][m] = ldc1(pr, ss * rowb + (uint32_t)(lane + 64 * m) * 4);
   }
   const float mstar = wave_max(ms);
   const float ws = ms == -INFINITY ? 0.f : expf(ms - mstar);
   const float L = wave_sum(ws * ls);
-  float o[2] = {0.f, 0.f};
-  for (int sp = 0; sp < ns; ++sp) {
-    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ws), sp));
-    if (w != 0.f)
-      for (int m = 0; m < dpl; ++m) o[m] = fmaf(w, ld_c(base + (size_t)sp * (hd + 4) + lane + 64 * m), o[m]);
+  float o[dpl];
+#pragma unroll
+  for (int m = 0; m < dpl; ++m) o[m] = 0.f;
+#pragma unroll 1
+  for (int s0 = 0; s0 < ns; s0 += RB) {
+    if (s0 > 0) {
+#pragma unroll
+      for (int t = 0; t < RB; ++t) {
+        const int ss = min(s0 + t, ns - 1);
+#pragma unroll
+        for (int m = 0; m < dpl; ++m) ov[t][m] = ldc1(pr, ss * rowb + (uint32_t)(lane + 64 * m) * 4);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < RB; ++t) {
+      const float w = s0 + t < ns ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ws), min(s0 + t, 63))) : 0.f;
+#pragma unroll
+      for (int m = 0; m < dpl; ++m) o[m] = fmaf(w, ov[t][m], o[m]);
+    }
   }
   float *out = c.attn_buf + ((size_t)d.layer * c.max_batch + b) * (c.nq * hd) + (size_t)j * hd;
+#pragma unroll
   for (int m = 0; m < dpl; ++m) st_c(out + lane + 64 * m, o[m] / L);
 }
 
@@ -628,21 +882,29 @@ __device__ void compute_role(const Env &e, const Args &a, int cw) {
   const int lane = lane_id();
   const uint32_t P = (uint32_t)c.ring_pages;
   float *acc = reinterpret_cast<float *>(smem + L_ACC);
-  float *wscr = reinterpret_cast<float *>(smem + L_WSCR + cw * 512);
   uint32_t n = 0, seq = 0;
-  float xr[32];
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
     const bool gv = is_gemv(d.op);
     const uint32_t nx = gv ? d.nk : 1;
     // gate: the first activation piece of the instruction is produced
-    if (!spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq; }, 0x200 | qi)) return;
+    auto gate = [&]() { return spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq; }, 0x200 | qi); };
+    if (d.op == OP_ATTN && cw < c.G) {
+      const bool ok = c.hd == 64 ? attn_body<1>(e, a, d, cw, gate) : attn_body<2>(e, a, d, cw, gate);
+      if (!ok) return;
+    } else if (!gate()) {
+      return;
+    }
+    if (cw == 0 && lane == 0) trace_now(e, qi, 2);
+    // this unit's staged row results
+    float *acc = reinterpret_cast<float *>(smem + L_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4);
     if (gv) {
       const uint32_t per = d.n_items * d.ipw;
       const uint32_t npieces = per * d.nk;
       const uint32_t n16 = d.pb >> 4;
       int cur_k = -1;
-      float pend = 0.f;
+      const bool has_resid = d.op == OP_O || d.op == OP_DOWN;  // acc preloaded
+      float xr[32];
       for (uint32_t p = 0; p < d.pages; ++p) {
         const uint32_t pg = n + p;
         const uint32_t t0 = p * d.ppp;
@@ -660,51 +922,52 @@ __device__ void compute_role(const Env &e, const Args &a, int cw) {
           }
           if ((int)k != cur_k) {
             if (lane == 0) lds_st(L_XCONS + 4 * cw, seq + k);
+            wake();
             if (!spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq + k; }, 0x400 | qi)) return;
             load_x(reinterpret_cast<const float *>(smem + L_XS + ((seq + k) % kNXS) * kXSlotBytes), n16, xr);
             cur_k = (int)k;
           }
           float v = dot_piece(page + (t - t0) * d.pb, xr, n16);
-          if (d.nk > 1) {
-            if (k > 0) v = acc[r] + v;
-            if (k + 1 < d.nk) {
-              if (lane == 0) acc[r] = v;
-              continue;
-            }
-          }
-          if (d.ipw == 2 && s == 0) {
-            pend = v;
-            continue;
-          }
-          if (lane == 0) epilogue(e, a, d, i, d.ipw == 2 ? pend : v, v);
+          if (k > 0 || has_resid) v = acc[r] + v;  // k order fixed: deterministic
+          if (lane == 0) acc[r] = v;
+          (void)s;
         }
         wait_lgkm0();
         if (lane == 0) lds_st(L_CONS + 4 * cw, pg + 1);
+        if (waited) wake();  // the loader may wait for this slot
       }
-    } else if (d.op == OP_ATTN) {
-      if (cw < c.G) attn_body(e, a, d, cw, wscr);
     } else if (d.op == OP_RED) {
-      if (cw < c.G) red_body(e, a, d, cw);
+      if (cw < c.G) {
+        if (c.hd == 64) red_body<1>(e, a, d, cw);
+        else red_body<2>(e, a, d, cw);
+      }
     }
     n += d.pages;
     seq += nx;
     if (lane == 0) lds_st(L_XCONS + 4 * cw, seq);
-    // completion: the last wave to finish signals the counter groups
-    wait_vm0();
+    wake();
+    // completion: the last wave to finish runs the epilogue and signals
+    if (!gv) wait_vm0();  // attention stores of this wave
+    wait_lgkm0();         // staged results are in LDS
     uint32_t old = 0;
     if (lane == 0)
       old = __hip_atomic_fetch_add(&lds_u32(L_DONE + 4 * (qi & 3)), 1u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
     old = __builtin_amdgcn_readfirstlane(old);
     if (old == kNCW - 1) {
+      if (gv) {
+        unit_epilogue(e, a, d, acc);
+        wait_vm0();
+      }
       if (lane == 0) {
+        trace_now(e, qi, 3);
         lds_st(L_DONE + 4 * (qi & 3), 0);
         const int x = e.cu % kXcds;
         if (d.sig0 >= 0)
-          __hip_atomic_fetch_add(a.ctr + ((size_t)d.sig0 * kXcds + x) * kCtrStride, 1u, __ATOMIC_RELAXED,
+          __hip_atomic_fetch_add(G(a.ctr) + ((size_t)d.sig0 * kXcds + x) * kCtrStride, 1u, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
         if (d.sig1 >= 0)
-          __hip_atomic_fetch_add(a.ctr + ((size_t)d.sig1 * kXcds + x) * kCtrStride, 1u, __ATOMIC_RELAXED,
+          __hip_atomic_fetch_add(G(a.ctr) + ((size_t)d.sig1 * kXcds + x) * kCtrStride, 1u, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -717,16 +980,17 @@ mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const
           const Wait *__restrict__ waits, const uint64_t *__restrict__ rowtab, uint32_t *__restrict__ ctr, const uint32_t *__restrict__ grp_target,
           float *__restrict__ part_buf, const int32_t *__restrict__ tokens,
           const int32_t *__restrict__ positions, uint16_t *__restrict__ kv, float *__restrict__ logits,
-          uint32_t epoch, int32_t batch, int32_t n_split, int32_t split_len) {
+          uint64_t *__restrict__ trace, uint32_t trace_stride, uint32_t epoch, int32_t batch, int32_t n_split,
+          int32_t split_len) {
   const Args a{ctx, instr, q_off, waits, rowtab, ctr, grp_target, part_buf, tokens, positions, kv, logits,
-               epoch, batch, n_split, split_len};
+               trace, trace_stride, epoch, batch, n_split, split_len};
   Env e;
   e.cp = a.ctx;
   e.cu = (int)blockIdx.x;
   const uint32_t q0 = a.q_off[e.cu], q1 = a.q_off[e.cu + 1];
   e.q = a.instr + q0;
   e.nq = q1 - q0;
-  e.t0 = now();
+  e.trace = a.trace ? a.trace + 4 + (size_t)e.cu * a.trace_stride * kTraceWords : nullptr;
   if (threadIdx.x < 64) lds_u32(threadIdx.x * 4) = 0;  // control words
   __syncthreads();
   const int w = (int)(threadIdx.x >> 6);
@@ -751,8 +1015,8 @@ hipError_t kernel_setup(int *blocks_per_cu) {
 hipError_t kernel_launch(const Args &a0, int grid, hipStream_t stream) {
   Args a = a0;
   void *params[] = {&a.ctx, &a.instr, &a.q_off, &a.waits, &a.rowtab, &a.ctr, &a.grp_target, &a.part_buf,
-                    &a.tokens, &a.positions, &a.kv, &a.logits, &a.epoch, &a.batch, &a.n_split,
-                    &a.split_len};
+                    &a.tokens, &a.positions, &a.kv, &a.logits, &a.trace, &a.trace_stride, &a.epoch,
+                    &a.batch, &a.n_split, &a.split_len};
   return hipLaunchCooperativeKernel((const void *)mk_interp, dim3(grid), dim3(kThreads), params, kLdsBytes,
                                     stream);
 }

@@ -23,13 +23,17 @@ enum Op : uint8_t {
 
 constexpr int kWave = 64;
 constexpr int kNCW = 8;                  // compute waves per workgroup
-constexpr int kNLW = 2;                  // loader waves per workgroup
+#ifndef MK_NLW
+#define MK_NLW 2
+#endif
+constexpr int kNLW = MK_NLW;             // loader waves per workgroup
 constexpr int kThreads = (kNCW + kNLW + 1) * kWave;  // + 1 sync wave
 constexpr int kPageBytes = 16384;        // LDS page (16 KB, 16 wave-loads of 1 KB)
 constexpr int kMaxKc = 2048;             // elements per weight piece (<= 4 KB)
 constexpr int kXSlotBytes = kMaxKc * 4;  // one fp32 activation piece
 constexpr int kNXS = 2;                  // activation slots (double buffer)
-constexpr int kAccFloats = 1024;         // LDS accumulators for multi-piece rows
+constexpr int kAccFloats = 512;          // LDS row results of one unit (rows*ipw)
+constexpr int kAccSlots = 4;             // units in flight per workgroup
 constexpr int kLdsBytes = 163840;        // gfx950: 160 KB per CU
 constexpr int kCtrStride = 32;           // uint32 spacing of counters (128 B)
 constexpr int kXcds = 8;                 // counters per group (one per XCD)
@@ -106,9 +110,8 @@ constexpr int L_XCONS = 96;     // u32[8]   activation pieces released per wave
 constexpr int L_XREADY = 128;   // u32      activation pieces produced
 constexpr int L_DONE = 132;     // u32[4]   waves finished, per unit slot
 constexpr int L_ABORT = 148;    // u32      nonzero: every wave exits
-constexpr int L_WSCR = 256;     // per compute wave 512 B scratch
-constexpr int L_ACC = L_WSCR + kNCW * 512;              // fp32 accumulators
-constexpr int L_XS = L_ACC + kAccFloats * 4;            // activation ring
+constexpr int L_ACC = 256;      // fp32 row results, kAccSlots x kAccFloats
+constexpr int L_XS = L_ACC + kAccSlots * kAccFloats * 4;  // activation ring
 constexpr int L_RING = ((L_XS + kNXS * kXSlotBytes + 1023) / 1024) * 1024;
 constexpr int kMaxRingPages = 16;
 constexpr int kRingPages = (kLdsBytes - L_RING) / kPageBytes < kMaxRingPages
@@ -129,6 +132,8 @@ struct Args {
   const int32_t *positions;
   uint16_t *kv;
   float *logits;
+  uint64_t *trace;            // [1 + num_cus * trace_stride][4] or null
+  uint32_t trace_stride;      // records per workgroup (longest queue)
   uint32_t epoch;
   int32_t batch;
   int32_t n_split, split_len;

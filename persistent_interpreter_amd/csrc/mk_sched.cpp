@@ -138,10 +138,17 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
   P.split_len = split_len;
   P.mlp_chunks = chunks;
 
-  const uint32_t n_qkv = std::min<uint32_t>(TP, std::max<uint32_t>((uint32_t)nkv, std::min<uint32_t>(C, TP)));
-  const uint32_t n_o = std::min(C, H), n_down = std::min(C, H);
-  const uint32_t n_ffn = std::min<uint32_t>(F, std::max<uint32_t>((uint32_t)chunks, std::min<uint32_t>(C, F)));
-  const uint32_t n_lm = std::min(C, V);
+  // units: at least one per CU (when there are rows for it), at most
+  // kAccFloats row results each (their LDS staging slot)
+  auto units_for = [&](uint32_t rows, uint32_t ipw, uint32_t at_least) {
+    uint32_t n = std::max<uint32_t>(std::min<uint32_t>((uint32_t)C, rows), at_least);
+    n = std::max<uint32_t>(n, (uint32_t)((uint64_t)rows * ipw + kAccFloats - 1) / kAccFloats);
+    return std::min<uint32_t>(n, rows);
+  };
+  const uint32_t n_qkv = units_for(TP, 2, (uint32_t)nkv);
+  const uint32_t n_o = units_for(H, 1, 1), n_down = units_for(H, 1, 1);
+  const uint32_t n_ffn = units_for(F, 2, (uint32_t)chunks);
+  const uint32_t n_lm = units_for(V, 1, 1);
 
   auto chunk_k0 = [&](int ch) { return (uint32_t)((uint64_t)ch * nk_f / chunks); };
 
@@ -300,8 +307,8 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
         cu_bytes[cu] += bytes;
         P.weight_bytes += bytes;
         P.n_pages += (int)in.pages;
-        if (in.nk > 1 && (int64_t)in.n_items * in.ipw > kAccFloats) {
-          err = "internal: too many rows in a multi-piece unit";
+        if ((int64_t)in.n_items * in.ipw > kAccFloats) {
+          err = "internal: too many rows in a unit";
           return MK_ERR_UNSUPPORTED;
         }
       }
