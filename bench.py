@@ -42,8 +42,17 @@ def overhead(t_real: float, t_min: float) -> float:
 
 
 def recovered(t_before: float, t_after: float, t_min: float) -> float:
-    """Fraction of the removable time a faster implementation recovered."""
+    """Fraction of the removable time (t - t_min) a faster implementation
+    recovered; the reading behind the section's MPK figure."""
     return (t_before - t_after) / (t_before - t_min)
+
+
+def overhead_drop(bw_frac_before: float, bw_frac_after: float) -> float:
+    """Relative drop of the overhead fraction when the share of peak
+    bandwidth rises (t_min / t_real is that share); the reading behind the
+    section's Hazy Research figure."""
+    o0, o1 = 1.0 - bw_frac_before, 1.0 - bw_frac_after
+    return (o0 - o1) / o0
 
 
 def algorithmic_bytes(mc, positions) -> int:
@@ -53,6 +62,37 @@ def algorithmic_bytes(mc, positions) -> int:
     for p in positions:
         b += 2 * 2 * mc.n_layers * mc.n_kv_heads * mc.head_dim * (int(p) + 1)
     return b
+
+
+def source_digest() -> str:
+    """sha256 prefix over the kernel library's sources; a stored traffic
+    figure is reported only for the source it was measured on."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "persistent_interpreter_amd", "csrc", "*"))) + \
+            [os.path.join(ROOT, "include", "mk.h")]:
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary of this workload (copy-calibrated), or None when that summary is
+    missing or was measured on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"mk_interp_{workload}_b1_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    digest, val = None, None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("Kernel source digest:"):
+                digest = line.split(":", 1)[1].strip()
+            elif line.startswith("traffic_bytes_per_launch:"):
+                val = int(line.split(":", 1)[1].strip())
+    return val if digest == source_digest() and val else None
 
 
 def cpu_baseline(mc, W, kv0, tok, pos, fed, gpu_logits, budget_s=20.0):
@@ -182,7 +222,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None,
+                     "traffic": stored_traffic(args.workload),
                      "kernel": "mk::mk_interp",
                      "bytes_per_launch": int(bytes_per)},
     }

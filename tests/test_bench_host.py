@@ -1,0 +1,54 @@
+"""Host-side pieces of bench.py: the overhead formula of the megakernels
+chapter on when not to build one (section 9.1), pinned to the two recoveries
+the section prints, the algorithmic byte count, and the stored-traffic
+lookup."""
+import json
+import os
+
+import pytest
+
+import bench
+from persistent_interpreter_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "overhead_examples.json")
+
+
+def _golden():
+    with open(GOLD) as f:
+        return json.load(f)
+
+
+def test_overhead_definition():
+    assert bench.overhead(2.0, 1.0) == pytest.approx(0.5)
+    assert bench.overhead(1.0, 1.0) == 0.0
+
+
+def test_mpk_recovery_matches_printed_value():
+    g = _golden()["mpk_qwen3_8b_a100"]
+    r = bench.recovered(g["t_before_ms"], g["t_after_ms"], g["t_min_ms"])
+    assert round(r, g["printed_digits"]) == g["recovered_printed"]
+
+
+def test_hazy_recovery_matches_printed_value():
+    g = _golden()["hazy_llama_1b"]
+    r = bench.overhead_drop(g["bw_frac_before"], g["bw_frac_after"])
+    assert round(r, g["printed_digits"]) == g["overhead_drop_printed"]
+
+
+def test_algorithmic_bytes_llama1b():
+    mc = synth.CONFIGS["llama1b"]
+    # weights (bf16) + one embedding row + K and V of slots 0..512, 16 layers
+    w = 2 * (mc.vocab * mc.hidden + mc.hidden
+             + mc.n_layers * (2 * mc.hidden
+                              + mc.hidden * (mc.n_q_heads + 2 * mc.n_kv_heads) * mc.head_dim
+                              + mc.n_q_heads * mc.head_dim * mc.hidden
+                              + 3 * mc.hidden * mc.ffn_dim))
+    kv = 2 * 2 * mc.n_layers * mc.n_kv_heads * mc.head_dim * 513
+    assert bench.algorithmic_bytes(mc, [512]) == w + 2 * mc.hidden + kv
+    assert 2.4884e9 < bench.algorithmic_bytes(mc, [512]) < 2.4885e9  # 2,488.4 MB
+
+
+def test_stored_traffic_only_for_matching_sources(monkeypatch):
+    monkeypatch.setattr(bench, "source_digest", lambda: "0" * 16)
+    assert bench.stored_traffic("llama1b") is None
+    assert bench.stored_traffic("no_such_workload") is None
