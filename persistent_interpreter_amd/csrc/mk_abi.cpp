@@ -264,7 +264,7 @@ static int get_plan(mk_handle *h, int batch, DevPlan **out) {
   if (rc) return rc;
   resolve_streams(h->cfg, h->w, dp->plan);
   Plan &P = dp->plan;
-  dp->ctr_bytes = (size_t)P.n_groups * kXcds * kCtrStride * 4;
+  dp->ctr_bytes = (size_t)P.n_groups * kSlots * kCtrStride * 4;
   const size_t part = (size_t)h->cfg.n_layers * h->cfg.max_batch * h->cfg.n_q_heads * P.n_split *
                       (h->cfg.head_dim + 4) * 4;
   if ((rc = upload(&dp->d_instr, P.instr)) || (rc = upload(&dp->d_qoff, P.q_off)) ||

@@ -111,6 +111,9 @@ __device__ __forceinline__ uint16_t ldc16(rsrc_t r, uint32_t off) {
 
 // Wake every sleeping wave of the workgroup (after publishing an LDS flag).
 __device__ __forceinline__ void wake() { asm volatile("s_wakeup" ::: "memory"); }
+#ifndef MK_WSLEEP
+#define MK_WSLEEP 1  // counter polls: s_sleep units (64 clocks) between polls
+#endif
 #ifndef MK_SLEEP
 #define MK_SLEEP 10
 #endif
@@ -119,7 +122,14 @@ __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" :
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // LDS control words for the C++ roles (sync and compute waves)
+// Flags are wave-uniform: the value is moved to a scalar register so every
+// branch on it is a scalar branch, not an exec-mask region.
 __device__ __forceinline__ uint32_t lds_ld(int off) {
+  return __builtin_amdgcn_readfirstlane(
+      __hip_atomic_load(&lds_u32(off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+}
+// Per-lane load (lanes may read different words).
+__device__ __forceinline__ uint32_t lds_ld_lane(int off) {
   return __hip_atomic_load(&lds_u32(off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 __device__ __forceinline__ void lds_st(int off, uint32_t v) {
@@ -267,7 +277,7 @@ __device__ __forceinline__ void asm_lds_st(uint32_t off, uint32_t v) {
 }
 
 #ifndef MK_DEPTH
-#define MK_DEPTH 3
+#define MK_DEPTH 2
 #endif
 constexpr int kDepth = MK_DEPTH;  // pages in flight per loader wave (16 loads each, <= 63)
 
@@ -295,6 +305,16 @@ __device__ void loader_role(const Env &e, const Args &a, int lw) {
     wait_vm0();
     while (npend) publish_oldest();
   };
+  // wait until the oldest pending page has landed (16 loads per page)
+  auto wait_oldest = [&]() {
+    static_assert(kDepth <= 3, "vmcnt immediates below cover 4 pending pages");
+    switch (npend) {
+      case 1: wait_vm_n<0>(); break;
+      case 2: wait_vm_n<16>(); break;
+      case 3: wait_vm_n<32>(); break;
+      default: wait_vm_n<48>(); break;
+    }
+  };
   auto min_cons = [&]() -> uint32_t {
     uint32_t v = lane < kNCW ? asm_lds_ld(L_CONS + 4 * lane) : 0xffffffffu;
     // minimum over lanes 0..7 with readlanes (no LDS-unit cross-lane ops)
@@ -312,15 +332,23 @@ __device__ void loader_role(const Env &e, const Args &a, int lw) {
     for (uint32_t p = 0; p < d.pages; ++p, ++n) {
       if ((int)(n % kNLW) != lw) continue;
       if (n >= P) {
+        // slot n % P is free once every compute wave released page n - P;
+        // meanwhile publish this wave's pending pages one by one as they
+        // land (a compute wave may be waiting on one of them), keeping the
+        // younger ones in flight
         const uint32_t need = n - P + 1;
         if (min_cons() < need) {
-          drain();
           Watchdog wd;
           for (uint32_t it = 1;; ++it) {
-            __builtin_amdgcn_s_sleep(MK_SLEEP);
+            if (npend) {
+              wait_oldest();
+              publish_oldest();
+            } else {
+              __builtin_amdgcn_s_sleep(MK_SLEEP);
+            }
             if (min_cons() >= need) break;
             if ((it & 63) == 0) {
-              if (asm_lds_ld(L_ABORT)) { wait_vm0(); return; }
+              if (__builtin_amdgcn_readfirstlane(asm_lds_ld(L_ABORT))) { wait_vm0(); return; }
               if (wd.expired(e.cp->watchdog_ticks)) { raise_error(e, 0xB0000000u | qi, n); wait_vm0(); return; }
             }
           }
@@ -339,8 +367,19 @@ __device__ void loader_role(const Env &e, const Args &a, int lw) {
         uint32_t j = 0;
         for (uint32_t q = 0; q < cnt; ++q) {
           const char *src = piece_addr(d, a.rowtab, k, r) + lane * 16;
-          for (uint32_t sub = 0; sub < lpp; ++sub, ++j)
-            __builtin_amdgcn_global_load_lds(src + sub * 1024, (LDS_AS void *)(slot + j * 1024), 16, 0, 0);
+          LDS_AS char *dst = slot + j * 1024;
+          uint32_t sub = 0;
+          // the immediate offset moves both the global source and the LDS
+          // destination, so four loads share one M0 and one address
+          for (; sub + 4 <= lpp; sub += 4, src += 4096, dst += 4096) {
+            __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)dst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)dst, 16, 1024, 0);
+            __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)dst, 16, 2048, 0);
+            __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)dst, 16, 3072, 0);
+          }
+          for (; sub < lpp; ++sub, src += 1024, dst += 1024)
+            __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)dst, 16, 0, 0);
+          j += lpp;
           if (++r == per) { r = 0; ++k; }
         }
         for (; j < 16; ++j)
@@ -373,16 +412,18 @@ __device__ void loader_role(const Env &e, const Args &a, int lw) {
 // --------------------------------------------------------------------------
 // Sync wave: counter waits and activation pieces.
 
-// Poll one counter group until all its per-XCD counters reached
-// target * epoch.  Lanes 0..7 each own one XCD counter.
-__device__ bool wait_group(const Env &e, const Args &a, uint32_t grp, uint32_t qi) {
+// Poll one counter group until each of its counter slots reached
+// target * epoch.  Lane i polls slot i (i < nslot).
+__device__ bool wait_group(const Env &e, const Args &a, const Wait &wt, uint32_t qi) {
   const int lane = lane_id();
-  const uint32_t *cp = a.ctr + ((size_t)grp * kXcds + (lane & 7)) * kCtrStride;
-  const uint32_t need = a.grp_target[grp * kXcds + (lane & 7)] * a.epoch;
+  const uint32_t grp = wt.grp;
+  const bool mine = lane < (int)wt.nslot;
+  const uint32_t *cp = a.ctr + ((size_t)grp * kSlots + (lane & (kSlots - 1))) * kCtrStride;
+  const uint32_t need = mine ? a.grp_target[grp * kSlots + lane] * a.epoch : 0u;
   Watchdog wd;
   for (uint32_t it = 0;; ++it) {
     bool ok = true;
-    if (lane < kXcds) ok = (int32_t)(ld_cu(cp) - need) >= 0;
+    if (mine) ok = (int32_t)(ld_cu(cp) - need) >= 0;
     if (__all(ok)) return true;
     if ((it & 63) == 63) {
       if (lds_ld(L_ABORT)) return false;
@@ -392,7 +433,7 @@ __device__ bool wait_group(const Env &e, const Args &a, uint32_t grp, uint32_t q
         return false;
       }
     }
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(MK_WSLEEP);
   }
 }
 
@@ -435,13 +476,13 @@ __device__ void sync_role(const Env &e, const Args &a) {
       while (wi < d.wait_n) {
         const Wait wt = a.waits[d.wait_off + wi];
         if (wt.before_k > k) break;
-        if (!wait_group(e, a, wt.grp, qi)) return;
+        if (!wait_group(e, a, wt, qi)) return;
         ++wi;
       }
       if (seq >= (uint32_t)kNXS) {
         const uint32_t need = seq - kNXS + 1;
         auto freed = [&]() {
-          uint32_t v = lane < kNCW ? lds_ld(L_XCONS + 4 * lane) : 0xffffffffu;
+          uint32_t v = lane < kNCW ? lds_ld_lane(L_XCONS + 4 * lane) : 0xffffffffu;
           uint32_t m = __builtin_amdgcn_readlane(v, 0);
 #pragma unroll
           for (int i = 1; i < kNCW; ++i) m = min(m, (uint32_t)__builtin_amdgcn_readlane(v, i));
@@ -899,43 +940,54 @@ __device__ void compute_role(const Env &e, const Args &a, int cw) {
     // this unit's staged row results
     float *acc = reinterpret_cast<float *>(smem + L_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4);
     if (gv) {
+      // This wave owns items i = cw, cw + kNCW, ... (all ipw sub-rows of
+      // each) and visits only its own pieces, in stream order: piece
+      // t = k*per + r lies at position t % ppp of the unit's page t / ppp.
+      // Pages before the next own piece are released before waiting on it.
       const uint32_t per = d.n_items * d.ipw;
-      const uint32_t npieces = per * d.nk;
+      const uint32_t ppp = d.ppp;
       const uint32_t n16 = d.pb >> 4;
-      int cur_k = -1;
+      const uint32_t step_far = 1 + (kNCW - 1) * d.ipw;  // last sub-row -> next own item
+      const uint32_t r0 = (uint32_t)cw * d.ipw;
       const bool has_resid = d.op == OP_O || d.op == OP_DOWN;  // acc preloaded
+      uint32_t rel = n, wpg = 0xffffffffu;
       float xr[32];
-      for (uint32_t p = 0; p < d.pages; ++p) {
-        const uint32_t pg = n + p;
-        const uint32_t t0 = p * d.ppp;
-        const uint32_t tn = min(t0 + d.ppp, npieces);
-        bool waited = false;
-        const char *page = smem + L_RING + (pg % P) * kPageBytes;
-        uint32_t k = t0 / per, r = t0 - k * per;
-        for (uint32_t t = t0; t < tn; ++t, r = (r + 1 == per) ? 0 : r + 1, k += (r == 0)) {
-          const uint32_t i = d.ipw == 2 ? (r >> 1) : r;
-          if ((i % kNCW) != (uint32_t)cw) continue;
-          const uint32_t s = r - i * d.ipw;
-          if (!waited) {
+      for (uint32_t k = 0; k < d.nk; ++k) {
+        if (k > 0) {
+          if (lane == 0) lds_st(L_XCONS + 4 * cw, seq + k);
+          wake();  // the sync wave may wait for this activation slot
+        }
+        if (r0 >= per) continue;
+        if (!spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq + k; }, 0x400 | qi)) return;
+        load_x(reinterpret_cast<const float *>(smem + L_XS + ((seq + k) % kNXS) * kXSlotBytes), n16, xr);
+        const uint32_t t = k * per + r0;
+        uint32_t pi = t / ppp, o = t - pi * ppp;
+        for (uint32_t r = r0; r < per;) {
+          const uint32_t pg = n + pi;
+          if (pg != wpg) {
+            if (pg > rel) {
+              if (lane == 0) lds_st(L_CONS + 4 * cw, pg);
+              rel = pg;
+              wake();  // a loader may wait for a released slot
+            }
             if (!spin_lds(e, [&]() { return lds_ld(L_FILLED + 4 * (pg % P)) >= pg + 1; }, 0x300 | qi)) return;
-            waited = true;
+            wpg = pg;
           }
-          if ((int)k != cur_k) {
-            if (lane == 0) lds_st(L_XCONS + 4 * cw, seq + k);
-            wake();
-            if (!spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq + k; }, 0x400 | qi)) return;
-            load_x(reinterpret_cast<const float *>(smem + L_XS + ((seq + k) % kNXS) * kXSlotBytes), n16, xr);
-            cur_k = (int)k;
-          }
-          float v = dot_piece(page + (t - t0) * d.pb, xr, n16);
+          float v = dot_piece(smem + L_RING + (pg % P) * kPageBytes + o * d.pb, xr, n16);
           if (k > 0 || has_resid) v = acc[r] + v;  // k order fixed: deterministic
           if (lane == 0) acc[r] = v;
-          (void)s;
+          const uint32_t step = (d.ipw == 2 && (r & 1) == 0) ? 1u : step_far;
+          r += step;
+          o += step;
+          while (o >= ppp) {
+            o -= ppp;
+            ++pi;
+          }
         }
-        wait_lgkm0();
-        if (lane == 0) lds_st(L_CONS + 4 * cw, pg + 1);
-        if (waited) wake();  // the loader may wait for this slot
       }
+      wait_lgkm0();
+      if (lane == 0) lds_st(L_CONS + 4 * cw, n + d.pages);
+      wake();
     } else if (d.op == OP_RED) {
       if (cw < c.G) {
         if (c.hd == 64) red_body<1>(e, a, d, cw);
@@ -962,12 +1014,11 @@ __device__ void compute_role(const Env &e, const Args &a, int cw) {
       if (lane == 0) {
         trace_now(e, qi, 3);
         lds_st(L_DONE + 4 * (qi & 3), 0);
-        const int x = e.cu % kXcds;
         if (d.sig0 >= 0)
-          __hip_atomic_fetch_add(G(a.ctr) + ((size_t)d.sig0 * kXcds + x) * kCtrStride, 1u, __ATOMIC_RELAXED,
+          __hip_atomic_fetch_add(G(a.ctr) + ((size_t)d.sig0 * kSlots + d.slot0) * kCtrStride, 1u, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
         if (d.sig1 >= 0)
-          __hip_atomic_fetch_add(G(a.ctr) + ((size_t)d.sig1 * kXcds + x) * kCtrStride, 1u, __ATOMIC_RELAXED,
+          __hip_atomic_fetch_add(G(a.ctr) + ((size_t)d.sig1 * kSlots + d.slot1) * kCtrStride, 1u, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
       }
     }

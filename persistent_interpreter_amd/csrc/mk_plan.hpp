@@ -24,7 +24,7 @@ enum Op : uint8_t {
 constexpr int kWave = 64;
 constexpr int kNCW = 8;                  // compute waves per workgroup
 #ifndef MK_NLW
-#define MK_NLW 2
+#define MK_NLW 3
 #endif
 constexpr int kNLW = MK_NLW;             // loader waves per workgroup
 constexpr int kThreads = (kNCW + kNLW + 1) * kWave;  // + 1 sync wave
@@ -36,7 +36,11 @@ constexpr int kAccFloats = 512;          // LDS row results of one unit (rows*ip
 constexpr int kAccSlots = 4;             // units in flight per workgroup
 constexpr int kLdsBytes = 163840;        // gfx950: 160 KB per CU
 constexpr int kCtrStride = 32;           // uint32 spacing of counters (128 B)
-constexpr int kXcds = 8;                 // counters per group (one per XCD)
+// A counter group is split over up to kSlots counters so that no counter
+// takes more than kAtomicsPerSlot increments per step: atomics on one
+// address serialise at the memory side (a few hundred ns each under load).
+constexpr int kSlots = 64;
+constexpr int kAtomicsPerSlot = 4;
 constexpr int kMaxSplits = 64;
 
 // One queued instruction (96 bytes).  An instruction's weight stream is the
@@ -67,15 +71,17 @@ struct alignas(16) Instr {
   uint64_t w0, w1;
   int32_t tab;          // offset into the plan's row-address table, or -1
   uint32_t rowb;        // bytes per weight row (K * 2)
-  uint64_t pad;
+  uint32_t slot0, slot1;  // counter slot of sig0 / sig1 within its group
 };
 static_assert(sizeof(Instr) == 96, "descriptor size");
 
-// A wait: counter group `grp` must reach its per-step target before the
-// activation piece `before_k` of the instruction is produced.
+// A wait: counter group `grp` (its `nslot` counters) must reach its per-step
+// targets before the activation piece `before_k` of the instruction is
+// produced.
 struct Wait {
   uint32_t grp;
-  uint32_t before_k;
+  uint16_t before_k;
+  uint16_t nslot;
 };
 
 struct DevLayer {
@@ -125,8 +131,8 @@ struct Args {
   const uint32_t *q_off;      // [num_cus + 1]
   const Wait *waits;
   const uint64_t *rowtab;     // row start addresses for tabulated units
-  uint32_t *ctr;              // [n_groups][kXcds][kCtrStride]
-  const uint32_t *grp_target; // [n_groups][kXcds] arrivals per step
+  uint32_t *ctr;              // [n_groups][kSlots][kCtrStride]
+  const uint32_t *grp_target; // [n_groups][kSlots] arrivals per step
   float *part_buf;            // [L][max_batch][nq][n_split][hd + 4] (o.., m, l)
   const int32_t *tokens;
   const int32_t *positions;

@@ -51,19 +51,38 @@ struct Builder {
   Builder(const mk_config &cfg, int b, int cus, Plan &p) : c(cfg), B(b), C(cus), P(p) {}
 
   int group() {
-    P.grp_target.resize(P.grp_target.size() + kXcds, 0);
+    P.grp_target.resize(P.grp_target.size() + kSlots, 0);
     P.grp_producers.push_back(0);
+    P.grp_nslot.push_back(0);
     return P.n_groups++;
   }
 
   void add(Unit u) {
     u.in.sig0 = u.sigs.size() > 0 ? u.sigs[0] : -1;
     u.in.sig1 = u.sigs.size() > 1 ? u.sigs[1] : -1;
-    for (int g : u.sigs) {
-      P.grp_target[(size_t)g * kXcds + (u.cu % kXcds)] += 1;
-      P.grp_producers[g] += 1;
-    }
+    for (int g : u.sigs) P.grp_producers[g] += 1;
     units.push_back(std::move(u));
+  }
+
+  // Once every unit exists: size each group's counter slots so that no
+  // slot takes more than kAtomicsPerSlot increments, deal the producers
+  // round-robin over the slots and give every wait its group's slot count.
+  void assign_slots() {
+    for (int g = 0; g < P.n_groups; ++g) {
+      uint32_t need = (P.grp_producers[g] + kAtomicsPerSlot - 1) / kAtomicsPerSlot, n = 1;
+      while (n < need && n < (uint32_t)kSlots) n <<= 1;
+      P.grp_nslot[g] = n;
+    }
+    std::vector<uint32_t> next(P.n_groups, 0);
+    for (Unit &u : units) {
+      for (int i = 0; i < (int)u.sigs.size() && i < 2; ++i) {
+        const int g = u.sigs[i];
+        const uint32_t slot = next[g]++ % P.grp_nslot[g];
+        P.grp_target[(size_t)g * kSlots + slot] += 1;
+        (i == 0 ? u.in.slot0 : u.in.slot1) = slot;
+      }
+      for (Wait &w : u.waits) w.nslot = (uint16_t)P.grp_nslot[w.grp];
+    }
   }
 };
 
@@ -289,6 +308,7 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
     bd.add(std::move(un));
   }
 
+  bd.assign_slots();
   // Per-CU queues in creation order (= stage order).
   std::vector<std::vector<int>> per_cu(C);
   for (size_t i = 0; i < bd.units.size(); ++i) per_cu[bd.units[i].cu].push_back((int)i);
@@ -398,7 +418,7 @@ int check_plan(const mk_config &cfg, Plan &P, int sim_runs, int corrupt, uint64_
   // Deliberate corruption for validator self-tests.
   std::vector<uint32_t> target(P.n_groups, 0);
   for (int g = 0; g < P.n_groups; ++g)
-    for (int x = 0; x < kXcds; ++x) target[g] += P.grp_target[(size_t)g * kXcds + x];
+    for (int x = 0; x < kSlots; ++x) target[g] += P.grp_target[(size_t)g * kSlots + x];
   std::vector<std::vector<int>> sig(NU);
   for (size_t u = 0; u < NU; ++u) {
     if (P.instr[u].sig0 >= 0) sig[u].push_back(P.instr[u].sig0);
@@ -426,18 +446,34 @@ int check_plan(const mk_config &cfg, Plan &P, int sim_runs, int corrupt, uint64_
     }
   }
 
-  // Static: group targets equal the producers, per XCD placement.
+  // Static: slot targets equal the producers dealt to each slot, every slot
+  // in use, none over its atomic budget, and waits poll every used slot.
   {
-    std::vector<uint32_t> cnt((size_t)P.n_groups * kXcds, 0);
-    for (int cu = 0; cu < C; ++cu)
-      for (uint32_t u = P.q_off[cu]; u < P.q_off[cu + 1]; ++u)
-        for (int g : {P.instr[u].sig0, P.instr[u].sig1})
-          if (g >= 0) cnt[(size_t)g * kXcds + (cu % kXcds)]++;
+    std::vector<uint32_t> cnt((size_t)P.n_groups * kSlots, 0);
+    for (size_t u = 0; u < NU; ++u) {
+      const Instr &in = P.instr[u];
+      if (in.sig0 >= 0) {
+        if (in.slot0 >= P.grp_nslot[in.sig0]) fail("signal slot outside its group");
+        else cnt[(size_t)in.sig0 * kSlots + in.slot0]++;
+      }
+      if (in.sig1 >= 0) {
+        if (in.slot1 >= P.grp_nslot[in.sig1]) fail("signal slot outside its group");
+        else cnt[(size_t)in.sig1 * kSlots + in.slot1]++;
+      }
+    }
     if (cnt != P.grp_target) fail("counter targets differ from producer placement");
+    for (int g = 0; g < P.n_groups; ++g)
+      for (uint32_t x = 0; x < P.grp_nslot[g]; ++x) {
+        const uint32_t t = P.grp_target[(size_t)g * kSlots + x];
+        if (t == 0) fail("unused counter slot");
+        if (t > (uint32_t)kAtomicsPerSlot && P.grp_nslot[g] < (uint32_t)kSlots) fail("slot over its atomic budget");
+      }
     for (size_t u = 0; u < NU; ++u)
-      for (auto &w : waits[u])
+      for (auto &w : waits[u]) {
         if (w.grp >= (uint32_t)P.n_groups || P.grp_producers[w.grp] == 0)
           fail("wait on a group without producers");
+        else if (w.nslot != P.grp_nslot[w.grp]) fail("wait polls a different slot count");
+      }
   }
 
   // Writers of every read.

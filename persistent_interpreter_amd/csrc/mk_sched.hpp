@@ -36,7 +36,8 @@ struct Plan {
   std::vector<Instr> instr;         // all per-CU queues back to back
   std::vector<uint32_t> q_off;      // [num_cus + 1]
   std::vector<Wait> waits;
-  std::vector<uint32_t> grp_target; // [n_groups][kXcds]
+  std::vector<uint32_t> grp_target; // [n_groups][kSlots]
+  std::vector<uint32_t> grp_nslot;  // [n_groups] counters in use
   std::vector<uint32_t> grp_producers;  // [n_groups] total producer units
   std::vector<uint64_t> rowtab;     // row start addresses of tabulated units
   // validation metadata, parallel to instr
