@@ -466,11 +466,46 @@ __device__ void sync_role(const Env &e, const Args &a) {
     if (tk < 0 || tk >= c.V) { raise_error(e, 0xE1000000u, (uint32_t)b); return; }
     if (ps < 0 || ps >= c.max_seq) { raise_error(e, 0xE2000000u, (uint32_t)b); return; }
   }
+  const int b = 0;
+  const int pos = a.positions[b];
+  const size_t HB = (size_t)c.max_batch * c.H;
   uint32_t seq = 0;
   float rs = 0.f;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
     const uint32_t nx = is_gemv(d.op) ? d.nk : 1;
+    const bool normed = d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM;
+    float *accs = reinterpret_cast<float *>(smem + L_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4);
+
+    // Step-invariant inputs are fetched before the unit's dependency waits,
+    // so that their round trips overlap the wait: the norm weights of the
+    // first activation piece, and for QKV the RoPE cos/sin of position p
+    // for the unit's pairs (staged in the upper half of its result slot,
+    // once the unit that used the slot before has finished its epilogue).
+    const float *h = nullptr;
+    const uint16_t *emb = nullptr, *nw = nullptr;
+    uint64_t *nwl = reinterpret_cast<uint64_t *>(smem + L_NW);  // norm weights, 4 per word
+    auto stage_norm_weights = [&](uint32_t k0) {
+      for (uint32_t i = (uint32_t)lane * 4; i < d.kc; i += 256)
+        nwl[i >> 2] = *G(reinterpret_cast<const uint64_t *>(nw + k0 + i));
+    };
+    if (normed) {
+      norm_src(e, a, d, b, h, emb, nw);
+      stage_norm_weights(0);
+    }
+    if (d.op == OP_QKV) {
+      if (qi >= (uint32_t)kAccSlots &&
+          !spin_lds(e, [&]() { return lds_ld(L_EPI) + kAccSlots > qi; }, 0x500 | qi))
+        return;
+      const uint32_t half = (uint32_t)c.hd >> 1, ppg = (uint32_t)(c.G + 2) * half;
+      for (uint32_t i = (uint32_t)lane; i < d.n_items; i += 64) {
+        const uint32_t ii = ((d.item0 + i) % ppg) % half;
+        const uint64_t cs = *G(reinterpret_cast<const uint64_t *>(c.rope + ((size_t)pos * half + ii) * 2));
+        accs[kAccFloats / 2 + 2 * i] = __uint_as_float((uint32_t)cs);
+        accs[kAccFloats / 2 + 2 * i + 1] = __uint_as_float((uint32_t)(cs >> 32));
+      }
+    }
+
     uint32_t wi = 0;
     for (uint32_t k = 0; k < nx; ++k, ++seq) {
       while (wi < d.wait_n) {
@@ -491,42 +526,11 @@ __device__ void sync_role(const Env &e, const Args &a) {
         if (!spin_lds(e, freed, 0x100 | qi)) return;
       }
       float *xs = reinterpret_cast<float *>(smem + L_XS + (seq % kNXS) * kXSlotBytes);
-      const int b = 0;
       if (k == 0 && lane == 0) {
         trace_put(e, qi, 0, (uint64_t)d.op | ((uint64_t)d.layer << 8) | ((uint64_t)d.unit << 24));
         trace_now(e, qi, 1);
       }
-      if (k == 0 && (d.op == OP_O || d.op == OP_DOWN)) {
-        // residual input of the unit's rows, added to by the compute waves
-        float *accs = reinterpret_cast<float *>(smem + L_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4);
-        const size_t HB = (size_t)c.max_batch * c.H;
-        float rv[kAccFloats / 64];
-        if (d.op == OP_O && d.layer == 0) {
-          const GAS uint16_t *er = G(c.embed) + (size_t)a.tokens[b] * c.H + d.item0;
-#pragma unroll
-          for (int m = 0; m < kAccFloats / 64; ++m) {
-            const uint32_t r = (uint32_t)(lane + 64 * m);
-            rv[m] = r < d.n_items ? bf16f(er[r]) : 0.f;
-          }
-        } else {
-          const int idx = d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1;
-          const rsrc_t rr = rsrc(c.h_buf + (size_t)idx * HB + (size_t)b * c.H + d.item0);
-#pragma unroll
-          for (int m = 0; m < kAccFloats / 64; ++m) {
-            const uint32_t r = (uint32_t)(lane + 64 * m);
-            rv[m] = r < d.n_items ? ldc1(rr, r * 4) : 0.f;
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < kAccFloats / 64; ++m) {
-          const uint32_t r = (uint32_t)(lane + 64 * m);
-          if (r < d.n_items) accs[r] = rv[m];
-        }
-      }
-      if (d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM) {
-        const float *h;
-        const uint16_t *emb, *w;
-        norm_src(e, a, d, b, h, emb, w);
+      if (normed) {
         const rsrc_t hr = rsrc(h ? (const void *)h : (const void *)emb);
         // one batch of up to 2048 elements (8 x 4 per lane) in flight
         auto load_batch = [&](uint32_t e0, f4 (&v)[8]) {
@@ -536,8 +540,8 @@ __device__ void sync_role(const Env &e, const Args &a) {
             if (i < (uint32_t)c.H) {
               if (emb) {
                 const uint64_t uu = *G(reinterpret_cast<const uint64_t *>(emb + i));
-                const uint2 u = make_uint2((uint32_t)uu, (uint32_t)(uu >> 32));
-                v[m] = f4{bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y)};
+                v[m] = f4{bf_lo((uint32_t)uu), bf_hi((uint32_t)uu), bf_lo((uint32_t)(uu >> 32)),
+                          bf_hi((uint32_t)(uu >> 32))};
               } else {
                 v[m] = ldc4(hr, i * 4);
               }
@@ -557,48 +561,63 @@ __device__ void sync_role(const Env &e, const Args &a) {
           ss = wave_sum(ss);
           rs = 1.0f / sqrtf(ss / (float)c.H + c.eps);
         }
+        // pieces hold at most 2048 elements; the last batch loaded is still
+        // in hv when H <= 2048 (then nk == 1)
         const uint32_t k0 = k * d.kc;
-        // the last batch loaded is still in hv when H <= 2048 (then nk == 1)
-        for (uint32_t e0 = 0; e0 < d.kc; e0 += 2048) {
-          if (c.H > 2048 || k0 != 0) load_batch(k0 + e0, hv);
-          uint2 wu[8];
+        if (c.H > 2048 || k0 != 0) load_batch(k0, hv);
+        if (k > 0) stage_norm_weights(k0);
 #pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const uint32_t i = e0 + (uint32_t)(lane + 64 * m) * 4;
-            wu[m] = make_uint2(0, 0);
-            if (i < d.kc) {
-              const uint64_t t = *G(reinterpret_cast<const uint64_t *>(w + k0 + i));
-              wu[m] = make_uint2((uint32_t)t, (uint32_t)(t >> 32));
-            }
-          }
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const uint32_t i = e0 + (uint32_t)(lane + 64 * m) * 4;
-            if (i < d.kc) {
-              const f4 v = hv[m];
-              f4 o = {v.x * rs * bf_lo(wu[m].x), v.y * rs * bf_hi(wu[m].x), v.z * rs * bf_lo(wu[m].y),
-                      v.w * rs * bf_hi(wu[m].y)};
-              *reinterpret_cast<f4 *>(xs + i) = o;
-            }
+        for (int m = 0; m < 8; ++m) {
+          const uint32_t i = (uint32_t)(lane + 64 * m) * 4;
+          if (i < d.kc) {
+            const f4 v = hv[m];
+            const uint64_t w4 = nwl[i >> 2];
+            const uint32_t w0 = (uint32_t)w4, w1 = (uint32_t)(w4 >> 32);
+            f4 o = {v.x * rs * bf_lo(w0), v.y * rs * bf_hi(w0), v.z * rs * bf_lo(w1), v.w * rs * bf_hi(w1)};
+            *reinterpret_cast<f4 *>(xs + i) = o;
           }
         }
       } else if (d.op == OP_O || d.op == OP_DOWN) {
+        // the activation piece and (first piece) the unit's residual rows,
+        // loaded together: one round trip
         const float *src = d.op == OP_O
                                ? c.attn_buf + ((size_t)d.layer * c.max_batch + b) * (c.nq * c.hd)
                                : c.a_buf + ((size_t)d.layer * c.max_batch + b) * c.F;
         const rsrc_t sr = rsrc(src + k * d.kc);
-        for (uint32_t e0 = 0; e0 < d.kc; e0 += 2048) {
-          f4 v[8];
+        f4 v[8];
 #pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const uint32_t i = e0 + (uint32_t)(lane + 64 * m) * 4;
-            if (i < d.kc) v[m] = ldc4(sr, i * 4);
+        for (int m = 0; m < 8; ++m) {
+          const uint32_t i = (uint32_t)(lane + 64 * m) * 4;
+          if (i < d.kc) v[m] = ldc4(sr, i * 4);
+        }
+        if (k == 0) {
+          float rv[kAccFloats / 64];
+          if (d.op == OP_O && d.layer == 0) {
+            const GAS uint16_t *er = G(c.embed) + (size_t)a.tokens[b] * c.H + d.item0;
+#pragma unroll
+            for (int m = 0; m < kAccFloats / 64; ++m) {
+              const uint32_t r = (uint32_t)(lane + 64 * m);
+              rv[m] = r < d.n_items ? bf16f(er[r]) : 0.f;
+            }
+          } else {
+            const int idx = d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1;
+            const rsrc_t rr = rsrc(c.h_buf + (size_t)idx * HB + (size_t)b * c.H + d.item0);
+#pragma unroll
+            for (int m = 0; m < kAccFloats / 64; ++m) {
+              const uint32_t r = (uint32_t)(lane + 64 * m);
+              rv[m] = r < d.n_items ? ldc1(rr, r * 4) : 0.f;
+            }
           }
 #pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const uint32_t i = e0 + (uint32_t)(lane + 64 * m) * 4;
-            if (i < d.kc) *reinterpret_cast<f4 *>(xs + i) = v[m];
+          for (int m = 0; m < kAccFloats / 64; ++m) {
+            const uint32_t r = (uint32_t)(lane + 64 * m);
+            if (r < d.n_items) accs[r] = rv[m];
           }
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const uint32_t i = (uint32_t)(lane + 64 * m) * 4;
+          if (i < d.kc) *reinterpret_cast<f4 *>(xs + i) = v[m];
         }
       }
       wait_lgkm0();
@@ -695,7 +714,7 @@ __device__ void unit_epilogue(const Env &e, const Args &a, const Instr &d, const
         const uint32_t ii = rr - hs * half;
         const int p = a.positions[b];
         if (hs <= (uint32_t)c.G) {
-          const float cs = G(c.rope)[((size_t)p * half + ii) * 2], sn = G(c.rope)[((size_t)p * half + ii) * 2 + 1];
+          const float cs = R[kAccFloats / 2 + 2 * i], sn = R[kAccFloats / 2 + 2 * i + 1];
           const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
           if (hs < (uint32_t)c.G) {
             float *q = c.q_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + (g * c.G + hs)) * c.hd;
@@ -1014,6 +1033,7 @@ __device__ void compute_role(const Env &e, const Args &a, int cw) {
       if (lane == 0) {
         trace_now(e, qi, 3);
         lds_st(L_DONE + 4 * (qi & 3), 0);
+        lds_st(L_EPI, qi + 1);
         if (d.sig0 >= 0)
           __hip_atomic_fetch_add(G(a.ctr) + ((size_t)d.sig0 * kSlots + d.slot0) * kCtrStride, 1u, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);

@@ -116,6 +116,7 @@ constexpr int L_XCONS = 96;     // u32[8]   activation pieces released per wave
 constexpr int L_XREADY = 128;   // u32      activation pieces produced
 constexpr int L_DONE = 132;     // u32[4]   waves finished, per unit slot
 constexpr int L_ABORT = 148;    // u32      nonzero: every wave exits
+constexpr int L_EPI = 152;      // u32      units whose epilogue has finished
 constexpr int L_ACC = 256;      // fp32 row results, kAccSlots x kAccFloats
 constexpr int L_XS = L_ACC + kAccSlots * kAccFloats * 4;  // activation ring
 constexpr int L_RING = ((L_XS + kNXS * kXSlotBytes + 1023) / 1024) * 1024;
@@ -123,6 +124,8 @@ constexpr int kMaxRingPages = 16;
 constexpr int kRingPages = (kLdsBytes - L_RING) / kPageBytes < kMaxRingPages
                                ? (kLdsBytes - L_RING) / kPageBytes : kMaxRingPages;
 static_assert(kRingPages >= 4, "LDS budget");
+constexpr int L_NW = L_RING + kRingPages * kPageBytes;  // bf16 norm weights of one piece
+static_assert(L_NW + kMaxKc * 2 <= kLdsBytes, "LDS budget");
 
 // Kernel arguments of one decode step (one per-batch plan).
 struct Args {

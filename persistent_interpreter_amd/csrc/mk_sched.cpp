@@ -327,7 +327,8 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
         cu_bytes[cu] += bytes;
         P.weight_bytes += bytes;
         P.n_pages += (int)in.pages;
-        if ((int64_t)in.n_items * in.ipw > kAccFloats) {
+        if ((int64_t)in.n_items * in.ipw > kAccFloats ||
+            (in.op == OP_QKV && (int64_t)in.n_items * in.ipw > kAccFloats / 2)) {
           err = "internal: too many rows in a unit";
           return MK_ERR_UNSUPPORTED;
         }
