@@ -164,7 +164,9 @@ int mk_plan_check(const mk_config *cfg, int32_t batch, int32_t num_cus,
 #define MK_BUF_H      1   /* fp32 [2L+1][max_batch][hidden]: index 2l+1 is the
                              residual after attention of layer l, 2l+2 after
                              its FFN (index 0 unused)                         */
-#define MK_BUF_Q      2   /* fp32 [L][max_batch][n_q][head_dim], after RoPE    */
+#define MK_BUF_Q      2   /* [L][max_batch][n_q][head_dim], after RoPE, as
+                             64-bit words: fp32 value in the low 32 bits, the
+                             tag of the step that wrote it in the high 32     */
 #define MK_BUF_ATTN   3   /* fp32 [L][max_batch][n_q*head_dim]                 */
 #define MK_BUF_A      4   /* fp32 [L][max_batch][ffn_dim], SiLU(gate)*up       */
 #define MK_BUF_TRACE  5   /* uint64 trace records (MK_FLAG_TRACE)              */

@@ -97,11 +97,14 @@ struct mk_handle {
   DevCtx hctx;
   DevCtx *d_ctx = nullptr;
   DevLayer *d_layers = nullptr;
-  float *h_buf = nullptr, *q_buf = nullptr, *attn_buf = nullptr, *a_buf = nullptr, *rope = nullptr;
+  float *h_buf = nullptr, *attn_buf = nullptr, *a_buf = nullptr;
+  uint64_t *q_buf = nullptr, *kvn_buf = nullptr;  // tagged words, see DevCtx
+  float *rope = nullptr;
   uint32_t *status = nullptr;
-  size_t h_bytes = 0, q_bytes = 0, attn_bytes = 0, a_bytes = 0;
+  size_t h_bytes = 0, q_bytes = 0, attn_bytes = 0, a_bytes = 0, kvn_bytes = 0;
   std::map<int, std::unique_ptr<DevPlan>> plans;
   DevPlan *last_plan = nullptr;
+  uint32_t tag = 0;  // activation tag of the last step (never 0; never reset)
   bool error_pending = false;
 };
 
@@ -196,9 +199,10 @@ int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out) {
   const int L = cfg->n_layers, MB = cfg->max_batch, H = cfg->hidden, nq = cfg->n_q_heads;
   const int hd = cfg->head_dim, F = cfg->ffn_dim, S = cfg->max_seq;
   h->h_bytes = (size_t)(2 * L + 1) * MB * H * 4;
-  h->q_bytes = (size_t)L * MB * nq * hd * 4;
-  h->attn_bytes = h->q_bytes;
+  h->q_bytes = (size_t)L * MB * nq * hd * 8;
+  h->attn_bytes = (size_t)L * MB * nq * hd * 4;
   h->a_bytes = (size_t)L * MB * F * 4;
+  h->kvn_bytes = (size_t)L * MB * cfg->n_kv_heads * 2 * hd * 8;
   std::vector<float> rope((size_t)S * (hd / 2) * 2);
   for (int p = 0; p < S; ++p)
     for (int i = 0; i < hd / 2; ++i) {
@@ -217,11 +221,15 @@ int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out) {
   }
   if ((rc = dev_alloc(&h->h_buf, h->h_bytes)) || (rc = dev_alloc(&h->q_buf, h->q_bytes)) ||
       (rc = dev_alloc(&h->attn_buf, h->attn_bytes)) || (rc = dev_alloc(&h->a_buf, h->a_bytes)) ||
-      (rc = upload(&h->rope, rope)) || (rc = dev_alloc(&h->status, 256)) || (rc = upload(&h->d_layers, dl))) {
+      (rc = dev_alloc(&h->kvn_buf, h->kvn_bytes)) || (rc = upload(&h->rope, rope)) ||
+      (rc = dev_alloc(&h->status, 256)) || (rc = upload(&h->d_layers, dl))) {
     mk_destroy(h.release());
     return rc;
   }
-  if (hipMemset(h->status, 0, 256) != hipSuccess || hipMemset(h->h_buf, 0, h->h_bytes) != hipSuccess) {
+  // tag 0 never matches a step's tag (tags start at 1)
+  if (hipMemset(h->status, 0, 256) != hipSuccess || hipMemset(h->h_buf, 0, h->h_bytes) != hipSuccess ||
+      hipMemset(h->q_buf, 0, h->q_bytes) != hipSuccess || hipMemset(h->attn_buf, 0, h->attn_bytes) != hipSuccess ||
+      hipMemset(h->a_buf, 0, h->a_bytes) != hipSuccess || hipMemset(h->kvn_buf, 0, h->kvn_bytes) != hipSuccess) {
     mk_destroy(h.release());
     return MK_ERR_HIP;
   }
@@ -238,6 +246,7 @@ int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out) {
   c.lm_head = (const uint16_t *)w->lm_head;
   c.layers = h->d_layers;
   c.h_buf = h->h_buf; c.q_buf = h->q_buf; c.attn_buf = h->attn_buf; c.a_buf = h->a_buf;
+  c.kvn_buf = h->kvn_buf;
   c.rope = h->rope;
   c.status = h->status;
   c.trace = nullptr;
@@ -274,19 +283,21 @@ static int get_plan(mk_handle *h, int batch, DevPlan **out) {
     free_plan(*dp);
     return rc;
   }
-  if (hipMemset(dp->d_ctr, 0, dp->ctr_bytes) != hipSuccess) {
+  if (hipMemset(dp->d_ctr, 0, dp->ctr_bytes) != hipSuccess || hipMemset(dp->d_part, 0, part) != hipSuccess) {
     free_plan(*dp);
     return MK_ERR_HIP;
   }
   if (h->cfg.flags & MK_FLAG_TRACE) {
-    // header [num_cus, stride, 0, 0] then [num_cus][stride][4] records
+    // header [num_cus, stride, words per record, 0] then
+    // [num_cus][stride][8] records
     uint32_t mq = 0;
     for (int c = 0; c < h->num_cus; ++c) mq = std::max(mq, P.q_off[c + 1] - P.q_off[c]);
     dp->trace_stride = mq;
-    dp->trace_bytes = (4 + (size_t)h->num_cus * mq * 4) * 8;
+    dp->trace_bytes = (4 + (size_t)h->num_cus * mq * 8) * 8;
     std::vector<uint64_t> init(dp->trace_bytes / 8, 0);
     init[0] = (uint64_t)h->num_cus;
     init[1] = mq;
+    init[2] = 8;
     if ((rc = upload(&dp->d_trace, init))) {
       free_plan(*dp);
       return rc;
@@ -323,6 +334,8 @@ int mk_decode_step(mk_handle *h, int32_t batch, const int32_t *tokens, const int
   a.trace_stride = dp->trace_stride;
   h->last_plan = dp;
   a.epoch = dp->epoch;
+  h->tag = h->tag + 1 == 0 ? 1 : h->tag + 1;
+  a.tag = h->tag;
   a.batch = batch;
   a.n_split = dp->plan.n_split;
   a.split_len = dp->plan.split_len;
@@ -358,6 +371,7 @@ void mk_destroy(mk_handle *h) {
   hipFree(h->q_buf);
   hipFree(h->attn_buf);
   hipFree(h->a_buf);
+  hipFree(h->kvn_buf);
   hipFree(h->rope);
   hipFree(h->status);
   delete h;

@@ -109,8 +109,27 @@ __device__ __forceinline__ uint16_t ldc16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kSC1);
 }
 
+// Tagged activation words: value in the low half, the step's tag in the
+// high half, written as one 64-bit store.  A producer stores them and
+// signals its counter without waiting for the stores to be acknowledged;
+// a consumer that found the counter complete re-reads any word whose tag
+// is not yet this step's.
+__device__ __forceinline__ void st_tag(uint64_t *p, float v, uint32_t tag) {
+  __hip_atomic_store(G(p), ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ldt(rsrc_t r, uint32_t word) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, word * 8, 0, kSC1);
+  return ((uint64_t)v[1] << 32) | v[0];
+}
+__device__ __forceinline__ float tval(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ bool tok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+
 // Wake every sleeping wave of the workgroup (after publishing an LDS flag).
 __device__ __forceinline__ void wake() { asm volatile("s_wakeup" ::: "memory"); }
+#ifndef MK_PRIO
+#define MK_PRIO 0  // wave issue priorities by role (s_setprio)
+#endif
 #ifndef MK_WSLEEP
 #define MK_WSLEEP 1  // counter polls: s_sleep units (64 clocks) between polls
 #endif
@@ -171,14 +190,20 @@ struct Env {
   const Instr *q;    // this workgroup's queue
   uint32_t nq;       // its length
   int cu;
+  int pos0;          // positions[0], read once at kernel start (batch 1)
 };
 
 __device__ __forceinline__ int64_t now() { return (int64_t)wall_clock64(); }
 
-// Trace record per queued instruction: [0] op | layer << 8 | unit << 24,
-// [1] sync wave: waits of the first piece satisfied, [2] compute wave 0
-// passed the unit's gate, [3] last compute wave finished (signal time).
-constexpr int kTraceWords = 4;
+// Trace record per queued instruction (100 MHz wall clock):
+//   [0] op | layer << 8 | unit << 24
+//   [1] sync wave: waits of the first activation piece satisfied
+//   [2] compute wave 0 passed the unit's gate
+//   [3] last compute wave: epilogue done, about to signal
+//   [4] sync wave: started the instruction (before its waits)
+//   [5] sync wave: first activation piece published
+//   [6] last compute wave: its own pieces done, epilogue starting
+constexpr int kTraceWords = 8;
 __device__ __forceinline__ void trace_put(const Env &e, uint32_t qi, int word, uint64_t v) {
   if (e.trace) G(e.trace)[(size_t)qi * kTraceWords + word] = v;
 }
@@ -236,6 +261,24 @@ __device__ __forceinline__ bool spin_lds(const Env &e, F cond, uint32_t info) {
         return false;
       }
     }
+  }
+}
+
+// Re-run `load` (it re-reads tagged words and returns, per lane, whether all
+// of them carry this step's tag) until every lane is satisfied.
+template <class F>
+__device__ __forceinline__ bool until_tagged(const Env &e, F load, uint32_t info) {
+  Watchdog wd;
+  for (uint32_t it = 0;; ++it) {
+    if (__all(load())) return true;
+    if ((it & 63) == 63) {
+      if (lds_ld(L_ABORT)) return false;
+      if (wd.expired(e.cp->watchdog_ticks)) {
+        raise_error(e, 0xD0000000u | info, 0);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(1);
   }
 }
 
@@ -507,6 +550,7 @@ __device__ void sync_role(const Env &e, const Args &a) {
     }
 
     uint32_t wi = 0;
+    if (lane == 0) trace_now(e, qi, 4);
     for (uint32_t k = 0; k < nx; ++k, ++seq) {
       while (wi < d.wait_n) {
         const Wait wt = a.waits[d.wait_off + wi];
@@ -623,6 +667,7 @@ __device__ void sync_role(const Env &e, const Args &a) {
       wait_lgkm0();
       if (lane == 0) lds_st(L_XREADY, seq + 1);
       wake();
+      if (k == 0 && lane == 0) trace_now(e, qi, 5);
     }
   }
 }
@@ -712,23 +757,31 @@ __device__ void unit_epilogue(const Env &e, const Args &a, const Instr &d, const
         const uint32_t rr = pp - g * ppg;
         const uint32_t hs = rr / half;
         const uint32_t ii = rr - hs * half;
-        const int p = a.positions[b];
+        const int p = e.pos0;
         if (hs <= (uint32_t)c.G) {
           const float cs = R[kAccFloats / 2 + 2 * i], sn = R[kAccFloats / 2 + 2 * i + 1];
           const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
           if (hs < (uint32_t)c.G) {
-            float *q = c.q_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + (g * c.G + hs)) * c.hd;
-            st_c(q + ii, r0);
-            st_c(q + ii + half, r1);
+            uint64_t *q = c.q_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + (g * c.G + hs)) * c.hd;
+            st_tag(q + ii, r0, a.tag);
+            st_tag(q + ii + half, r1, a.tag);
           } else {
             uint16_t *k = a.kv + kv_off(c, d.layer, 0, b, g, p);
-            st_c16(k + ii, f2bf(r0));
-            st_c16(k + ii + half, f2bf(r1));
+            const uint16_t k0 = f2bf(r0), k1 = f2bf(r1);
+            st_c16(k + ii, k0);
+            st_c16(k + ii + half, k1);
+            uint64_t *kn = c.kvn_buf + (((size_t)d.layer * c.max_batch + b) * c.nkv + g) * 2 * c.hd;
+            st_tag(kn + ii, bf16f(k0), a.tag);
+            st_tag(kn + ii + half, bf16f(k1), a.tag);
           }
         } else {
           uint16_t *v = a.kv + kv_off(c, d.layer, 1, b, g, p);
-          st_c16(v + ii, f2bf(v0));
-          st_c16(v + ii + half, f2bf(v1));
+          const uint16_t u0 = f2bf(v0), u1 = f2bf(v1);
+          st_c16(v + ii, u0);
+          st_c16(v + ii + half, u1);
+          uint64_t *vn = c.kvn_buf + ((((size_t)d.layer * c.max_batch + b) * c.nkv + g) * 2 + 1) * c.hd;
+          st_tag(vn + ii, bf16f(u0), a.tag);
+          st_tag(vn + ii + half, bf16f(u1), a.tag);
         }
         break;
       }
@@ -760,7 +813,7 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Ga
   const int b = (int)d.b, g = (int)d.aux0, s = (int)d.aux1;
   const int j = g * c.G + h;
   constexpr int hd = 64 * DPL, PF = 20 / DPL;  // prefetch depth (register budget)
-  const int p = a.positions[b];
+  const int p = e.pos0;
   const int lo = s * a.split_len;
   const int hi = min(lo + a.split_len, p + 1);
   const int nt0 = max(0, min(hi - lo, PF));
@@ -786,13 +839,28 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Ga
   if (lo < hi) {
     // lane = head dimension (dims lane + 64*m) for q, K and V
     const rsrc_t qr = rsrc(c.q_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + j) * hd);
-    const bool has_p = p < hi;  // the new slot p (written this step) is in the split
+    // the new slot p (written this step) comes from the tagged copy, never
+    // from the cache
+    const rsrc_t nr = rsrc(c.kvn_buf + (((size_t)d.layer * c.max_batch + b) * c.nkv + g) * 2 * hd);
+    const bool has_p = p < hi;
+    auto load = [&]() -> bool {
+      bool ok = true;
 #pragma unroll
-    for (int m = 0; m < DPL; ++m) {
-      q[m] = ldc1(qr, (uint32_t)(lane + 64 * m) * 4);
-      kp[m] = has_p ? ldc16(Kr, (uint32_t)((p - lo) * hd + lane + 64 * m) * 2) : (uint16_t)0;
-      vp[m] = has_p ? ldc16(Vr, (uint32_t)((p - lo) * hd + lane + 64 * m) * 2) : (uint16_t)0;
-    }
+      for (int m = 0; m < DPL; ++m) {
+        const uint64_t wq = ldt(qr, (uint32_t)(lane + 64 * m));
+        q[m] = tval(wq);
+        ok = ok && tok(wq, a.tag);
+        kp[m] = vp[m] = 0;
+        if (has_p) {
+          const uint64_t wk = ldt(nr, (uint32_t)(lane + 64 * m)), wv = ldt(nr, (uint32_t)(hd + lane + 64 * m));
+          kp[m] = (uint16_t)((uint32_t)wk >> 16);  // exact: the value is a bf16
+          vp[m] = (uint16_t)((uint32_t)wv >> 16);
+          ok = ok && tok(wk, a.tag) && tok(wv, a.tag);
+        }
+      }
+      return ok;
+    };
+    if (!until_tagged(e, load, 0x800 | d.unit)) return false;
     // first PF positions from the prefetched registers
     {
       float sc = -INFINITY;
@@ -830,7 +898,7 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Ga
           const int tt = min(t0 + t, nt - 1);
 #pragma unroll
           for (int m = 0; m < DPL; ++m)
-            k8[t][m] = ldc16(Kr, (uint32_t)((c0 - lo + tt) * hd + lane + 64 * m) * 2);
+            k8[t][m] = c0 + tt == p ? kp[m] : ldc16(Kr, (uint32_t)((c0 - lo + tt) * hd + lane + 64 * m) * 2);
         }
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -857,7 +925,7 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Ga
           const int tt = min(t0 + t, nt - 1);  // in bounds; weight 0 beyond nt
 #pragma unroll
           for (int m = 0; m < DPL; ++m)
-            v8[t][m] = ldc16(Vr, (uint32_t)((c0 - lo + tt) * hd + lane + 64 * m) * 2);
+            v8[t][m] = c0 + tt == p ? vp[m] : ldc16(Vr, (uint32_t)((c0 - lo + tt) * hd + lane + 64 * m) * 2);
         }
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -1017,8 +1085,11 @@ __device__ void compute_role(const Env &e, const Args &a, int cw) {
     seq += nx;
     if (lane == 0) lds_st(L_XCONS + 4 * cw, seq);
     wake();
-    // completion: the last wave to finish runs the epilogue and signals
-    if (!gv) wait_vm0();  // attention stores of this wave
+    // completion: the last wave to finish runs the epilogue and signals.
+    // Results that other workgroups read as tagged words (q and the new K/V
+    // slot, from QKV units) need no acknowledgement; plain fp32 results are
+    // acknowledged before the counter moves.
+    if (!gv) wait_vm0();  // attention partials / reduction output of this wave
     wait_lgkm0();         // staged results are in LDS
     uint32_t old = 0;
     if (lane == 0)
@@ -1026,9 +1097,13 @@ __device__ void compute_role(const Env &e, const Args &a, int cw) {
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
     old = __builtin_amdgcn_readfirstlane(old);
     if (old == kNCW - 1) {
+#if MK_PRIO
+      __builtin_amdgcn_s_setprio(3);  // the epilogue is on the critical path
+#endif
+      if (lane == 0) trace_now(e, qi, 6);
       if (gv) {
         unit_epilogue(e, a, d, acc);
-        wait_vm0();
+        if (d.op != OP_QKV) wait_vm0();
       }
       if (lane == 0) {
         trace_now(e, qi, 3);
@@ -1041,6 +1116,9 @@ __device__ void compute_role(const Env &e, const Args &a, int cw) {
           __hip_atomic_fetch_add(G(a.ctr) + ((size_t)d.sig1 * kSlots + d.slot1) * kCtrStride, 1u, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
       }
+#if MK_PRIO
+      __builtin_amdgcn_s_setprio(1);
+#endif
     }
   }
 }
@@ -1051,10 +1129,10 @@ mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const
           const Wait *__restrict__ waits, const uint64_t *__restrict__ rowtab, uint32_t *__restrict__ ctr, const uint32_t *__restrict__ grp_target,
           float *__restrict__ part_buf, const int32_t *__restrict__ tokens,
           const int32_t *__restrict__ positions, uint16_t *__restrict__ kv, float *__restrict__ logits,
-          uint64_t *__restrict__ trace, uint32_t trace_stride, uint32_t epoch, int32_t batch, int32_t n_split,
+          uint64_t *__restrict__ trace, uint32_t trace_stride, uint32_t epoch, uint32_t tag, int32_t batch, int32_t n_split,
           int32_t split_len) {
   const Args a{ctx, instr, q_off, waits, rowtab, ctr, grp_target, part_buf, tokens, positions, kv, logits,
-               trace, trace_stride, epoch, batch, n_split, split_len};
+               trace, trace_stride, epoch, tag, batch, n_split, split_len};
   Env e;
   e.cp = a.ctx;
   e.cu = (int)blockIdx.x;
@@ -1062,9 +1140,16 @@ mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const
   e.q = a.instr + q0;
   e.nq = q1 - q0;
   e.trace = a.trace ? a.trace + 4 + (size_t)e.cu * a.trace_stride * kTraceWords : nullptr;
+  e.pos0 = a.positions[0];
   if (threadIdx.x < 64) lds_u32(threadIdx.x * 4) = 0;  // control words
   __syncthreads();
   const int w = (int)(threadIdx.x >> 6);
+#if MK_PRIO
+  // issue priority: the sync wave (critical-path waits and activation
+  // pieces) first, compute waves next, weight streaming last
+  if (w >= kNCW + kNLW) __builtin_amdgcn_s_setprio(3);
+  else if (w < kNCW) __builtin_amdgcn_s_setprio(1);
+#endif
   if (w < kNCW) compute_role(e, a, w);
   else if (w < kNCW + kNLW) loader_role(e, a, w - kNCW);
   else sync_role(e, a);
@@ -1086,7 +1171,7 @@ hipError_t kernel_setup(int *blocks_per_cu) {
 hipError_t kernel_launch(const Args &a0, int grid, hipStream_t stream) {
   Args a = a0;
   void *params[] = {&a.ctx, &a.instr, &a.q_off, &a.waits, &a.rowtab, &a.ctr, &a.grp_target, &a.part_buf,
-                    &a.tokens, &a.positions, &a.kv, &a.logits, &a.trace, &a.trace_stride, &a.epoch,
+                    &a.tokens, &a.positions, &a.kv, &a.logits, &a.trace, &a.trace_stride, &a.epoch, &a.tag,
                     &a.batch, &a.n_split, &a.split_len};
   return hipLaunchCooperativeKernel((const void *)mk_interp, dim3(grid), dim3(kThreads), params, kLdsBytes,
                                     stream);

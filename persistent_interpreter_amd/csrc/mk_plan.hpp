@@ -99,9 +99,11 @@ struct DevCtx {
   const uint16_t *embed, *final_norm, *lm_head;
   const DevLayer *layers;
   float *h_buf;       // [2L+1][max_batch][H]
-  float *q_buf;       // [L][max_batch][nq][hd]
   float *attn_buf;    // [L][max_batch][nq*hd]
   float *a_buf;       // [L][max_batch][F]
+  // tagged words (fp32 value in the low 32 bits, the step's tag above)
+  uint64_t *q_buf;    // [L][max_batch][nq][hd]
+  uint64_t *kvn_buf;  // [L][max_batch][nkv][2][hd] this step's K/V slot (bf16-rounded)
   const float *rope;  // [max_seq][hd/2][2] (cos, sin)
   uint32_t *status;   // [0] error code, [1..] details
   uint64_t *trace;    // per-instruction records or NULL
@@ -143,7 +145,8 @@ struct Args {
   float *logits;
   uint64_t *trace;            // [1 + num_cus * trace_stride][4] or null
   uint32_t trace_stride;      // records per workgroup (longest queue)
-  uint32_t epoch;
+  uint32_t epoch;             // this plan's launch count: counter targets scale with it
+  uint32_t tag;               // this step's activation tag (handle-wide, never 0)
   int32_t batch;
   int32_t n_split, split_len;
 };

@@ -73,18 +73,25 @@ class Session:
     def kv_host(self) -> np.ndarray:
         return self.kv.cpu().numpy().view(np.uint16)
 
+    TAGGED = (2,)  # MK_BUF_Q holds (value, tag) words
+
     def buffer(self, which: int, shape, dtype=np.float32) -> np.ndarray:
-        """Copy of one of the library's internal buffers (mk_get_buffer)."""
+        """Copy of one of the library's internal buffers (mk_get_buffer).
+        Tagged buffers hold 64-bit words (fp32 value in the low half, the
+        step's tag in the high half); their values are returned."""
         import ctypes
         import torch
         ptr, nbytes = self.mk.buffer(which)
-        out = np.empty(shape, dtype=dtype)
+        tagged = which in self.TAGGED
+        out = np.empty(shape, dtype=np.uint64 if tagged else dtype)
         assert out.nbytes <= nbytes
         torch.cuda.synchronize()
         hip = ctypes.CDLL("libamdhip64.so")
         rc = hip.hipMemcpy(ctypes.c_void_p(out.ctypes.data), ctypes.c_void_p(ptr),
                            ctypes.c_size_t(out.nbytes), 2)  # device to host
         assert rc == 0, rc
+        if tagged:
+            out = (out & np.uint64(0xFFFFFFFF)).astype(np.uint32).view(np.float32)
         return out
 
     def close(self):
