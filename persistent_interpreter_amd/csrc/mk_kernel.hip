@@ -964,7 +964,7 @@ __device__ void red_body(const Env &e, const Args &a, const Instr &d, int h) {
   const rsrc_t pr = rsrc(base);
   const uint32_t rowb = (uint32_t)(hd + 4) * 4;
   // m, l of every split and the first RB splits' o in one round trip
-  constexpr int RB = 16 / DPL;
+  constexpr int RB = 32 / DPL;  // splits per round trip (all 32 at head_dim 64)
   float ms = -INFINITY, ls = 0.f;
   float ov[RB][dpl];
   if (lane < ns) {
@@ -1027,15 +1027,15 @@ __device__ void compute_role(const Env &e, const Args &a, int cw) {
     // this unit's staged row results
     float *acc = reinterpret_cast<float *>(smem + L_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4);
     if (gv) {
-      // This wave owns items i = cw, cw + kNCW, ... (all ipw sub-rows of
-      // each) and visits only its own pieces, in stream order: piece
-      // t = k*per + r lies at position t % ppp of the unit's page t / ppp.
-      // Pages before the next own piece are released before waiting on it.
+      // This wave owns unit rows r = cw, cw + kNCW, ... and visits only its
+      // own pieces, in stream order: piece t = k*per + r lies at position
+      // t % ppp of the unit's page t / ppp, so consecutive pieces of a page
+      // belong to different waves and a page is released after one dot of
+      // each.  Pages before the next own piece are released before waiting.
       const uint32_t per = d.n_items * d.ipw;
       const uint32_t ppp = d.ppp;
       const uint32_t n16 = d.pb >> 4;
-      const uint32_t step_far = 1 + (kNCW - 1) * d.ipw;  // last sub-row -> next own item
-      const uint32_t r0 = (uint32_t)cw * d.ipw;
+      const uint32_t r0 = (uint32_t)cw;
       const bool has_resid = d.op == OP_O || d.op == OP_DOWN;  // acc preloaded
       uint32_t rel = n, wpg = 0xffffffffu;
       float xr[32];
@@ -1063,9 +1063,8 @@ __device__ void compute_role(const Env &e, const Args &a, int cw) {
           float v = dot_piece(smem + L_RING + (pg % P) * kPageBytes + o * d.pb, xr, n16);
           if (k > 0 || has_resid) v = acc[r] + v;  // k order fixed: deterministic
           if (lane == 0) acc[r] = v;
-          const uint32_t step = (d.ipw == 2 && (r & 1) == 0) ? 1u : step_far;
-          r += step;
-          o += step;
+          r += kNCW;
+          o += kNCW;
           while (o >= ppp) {
             o -= ppp;
             ++pi;
