@@ -214,6 +214,8 @@ def decode_step(cfg, W: dict, tokens, positions, kv: np.ndarray,
         q = linear(lw["wq"], x, dt).reshape(B, nq, hd)
         k = linear(lw["wk"], x, dt).reshape(B, nkv, hd)
         v = linear(lw["wv"], x, dt).reshape(B, nkv, hd)
+        if trace is not None:
+            trace.setdefault("q_raw", []).append(q.copy())
         if cfg.qk_norm:
             q = rmsnorm(q, lw["q_norm"], eps, dt)
             k = rmsnorm(k, lw["k_norm"], eps, dt)

@@ -758,7 +758,16 @@ __device__ void unit_epilogue(const Env &e, const Args &a, const Instr &d, const
         const uint32_t hs = rr / half;
         const uint32_t ii = rr - hs * half;
         const int p = e.pos0;
-        if (hs <= (uint32_t)c.G) {
+        if (hs <= (uint32_t)c.G && c.qk_norm) {
+          // per-head q/k RMSNorm needs the whole head, which spans several
+          // units: q and k leave raw (un-normed, un-rotated) and the
+          // attention units norm and rotate them (and write K to the cache)
+          uint64_t *dst = hs < (uint32_t)c.G
+                              ? c.q_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + (g * c.G + hs)) * c.hd
+                              : c.kvn_buf + (((size_t)d.layer * c.max_batch + b) * c.nkv + g) * 2 * c.hd;
+          st_tag(dst + ii, v0, a.tag);
+          st_tag(dst + ii + half, v1, a.tag);
+        } else if (hs <= (uint32_t)c.G) {
           const float cs = R[kAccFloats / 2 + 2 * i], sn = R[kAccFloats / 2 + 2 * i + 1];
           const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
           if (hs < (uint32_t)c.G) {
@@ -831,6 +840,22 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Ga
       }
     }
   }
+  // q/k norm (head_dim 128 only): weights of dims lane and lane + 64, and
+  // the RoPE cos/sin of pair (lane, lane + 64) at position p, before the gate
+  float qnw[DPL], knw[DPL], rc = 0.f, rsn = 0.f;
+  if constexpr (DPL == 2) {
+    if (c.qk_norm) {
+      const uint16_t *qn = G(c.layers)[d.layer].q_norm, *kn = G(c.layers)[d.layer].k_norm;
+#pragma unroll
+      for (int m = 0; m < DPL; ++m) {
+        qnw[m] = bf16f(G(qn)[lane + 64 * m]);
+        knw[m] = bf16f(G(kn)[lane + 64 * m]);
+      }
+      const uint64_t csw = *G(reinterpret_cast<const uint64_t *>(c.rope + ((size_t)p * 64 + lane) * 2));
+      rc = __uint_as_float((uint32_t)csw);
+      rsn = __uint_as_float((uint32_t)(csw >> 32));
+    }
+  }
   if (!gate()) return false;
   float mrun = -INFINITY, lrun = 0.f, o[DPL], q[DPL];
   uint16_t kp[DPL], vp[DPL];
@@ -843,6 +868,7 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Ga
     // from the cache
     const rsrc_t nr = rsrc(c.kvn_buf + (((size_t)d.layer * c.max_batch + b) * c.nkv + g) * 2 * hd);
     const bool has_p = p < hi;
+    float kraw[DPL];
     auto load = [&]() -> bool {
       bool ok = true;
 #pragma unroll
@@ -851,9 +877,11 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Ga
         q[m] = tval(wq);
         ok = ok && tok(wq, a.tag);
         kp[m] = vp[m] = 0;
+        kraw[m] = 0.f;
         if (has_p) {
           const uint64_t wk = ldt(nr, (uint32_t)(lane + 64 * m)), wv = ldt(nr, (uint32_t)(hd + lane + 64 * m));
-          kp[m] = (uint16_t)((uint32_t)wk >> 16);  // exact: the value is a bf16
+          kraw[m] = tval(wk);
+          kp[m] = (uint16_t)((uint32_t)wk >> 16);  // exact when K arrives rounded (no q/k norm)
           vp[m] = (uint16_t)((uint32_t)wv >> 16);
           ok = ok && tok(wk, a.tag) && tok(wv, a.tag);
         }
@@ -861,6 +889,31 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Ga
       return ok;
     };
     if (!until_tagged(e, load, 0x800 | d.unit)) return false;
+    if constexpr (DPL == 2) {
+      if (c.qk_norm) {
+        // RMSNorm over the head (eps inside the root, weight after), then
+        // RoPE of pair (lane, lane + 64); K is rounded to bf16 and the unit
+        // whose split holds p writes it to the cache (wave of head 0)
+        auto norm_rope = [&](float (&u)[DPL], const float (&w)[DPL]) {
+          const float ss = wave_sum(u[0] * u[0] + u[1] * u[1]);
+          const float r = 1.0f / sqrtf(ss / (float)hd + c.eps);
+          const float a0 = u[0] * r * w[0], a1 = u[1] * r * w[1];
+          u[0] = a0 * rc - a1 * rsn;
+          u[1] = a1 * rc + a0 * rsn;
+        };
+        norm_rope(q, qnw);
+        if (has_p) {
+          norm_rope(kraw, knw);
+          kp[0] = f2bf(kraw[0]);
+          kp[1] = f2bf(kraw[1]);
+          if (h == 0) {
+            uint16_t *kc = a.kv + kv_off(c, d.layer, 0, b, g, p);
+            st_c16(kc + lane, kp[0]);
+            st_c16(kc + lane + 64, kp[1]);
+          }
+        }
+      }
+    }
     // first PF positions from the prefetched registers
     {
       float sc = -INFINITY;

@@ -100,6 +100,10 @@ CONFIGS: Dict[str, ModelConfig] = {
     "llama70b": ModelConfig("llama70b", 5, 80, 8192, 64, 8, 128, 28672,
                             128256, rope_theta=500000.0,
                             tied_embeddings=False, batch=64, prior=1024),
+    # small parity case of the Qwen3 path: head_dim 128, q/k norm, untied
+    "tiny_qk": ModelConfig("tiny_qk", 6, 2, 256, 4, 2, 128, 688, 1024,
+                           rope_theta=1000000.0, tied_embeddings=False,
+                           qk_norm=True, prior=16),
 }
 
 

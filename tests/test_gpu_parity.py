@@ -45,20 +45,30 @@ def _run_one(name, **over):
     return mc, W, sess, lg, ref, ref_kv, trace, tok, pos
 
 
-def test_tiny_one_step_stages_and_logits():
-    mc, W, sess, lg, ref, ref_kv, trace, tok, pos = _run_one("tiny")
+QK_SKIP = pytest.mark.skip(reason="q/k-norm path switched off: a 32-step run of it faulted "
+                                   "the GPU; cause not found yet (the library returns "
+                                   "MK_ERR_UNSUPPORTED for q/k norm)")
+
+
+@pytest.mark.parametrize("name", ["tiny", pytest.param("tiny_qk", marks=QK_SKIP)])
+def test_tiny_one_step_stages_and_logits(name):
+    """Stage by stage against the oracle's intermediates.  With q/k norm the
+    q buffer holds the raw projection (the attention units norm and rotate
+    it), so it is compared with the oracle's projection output."""
+    mc, W, sess, lg, ref, ref_kv, trace, tok, pos = _run_one(name)
+    qref = trace["q_raw"] if mc.qk_norm else trace["q"]
     L, H, F = mc.n_layers, mc.hidden, mc.ffn_dim
     hb = sess.buffer(1, (2 * L + 1, 1, H))
     ab = sess.buffer(4, (L, 1, F))
     qb = sess.buffer(2, (L, 1, mc.n_q_heads, mc.head_dim))
     att = sess.buffer(3, (L, 1, mc.n_q_heads * mc.head_dim))
     for l in range(L):
-        print(f"layer {l}: q {np.abs(qb[l] - trace['q'][l]).max():.2e} "
+        print(f"layer {l}: q {np.abs(qb[l] - qref[l]).max():.2e} "
               f"attn {np.abs(att[l] - trace['attn'][l]).max():.2e} "
               f"h_mid {np.abs(hb[2*l+1] - trace['h_mid'][l]).max():.2e} "
               f"a {np.abs(ab[l] - trace['a'][l]).max():.2e} "
               f"h_out {np.abs(hb[2*l+2] - trace['h_out'][l]).max():.2e}")
-        np.testing.assert_allclose(qb[l], trace["q"][l], atol=1e-4, rtol=1e-4)
+        np.testing.assert_allclose(qb[l], qref[l], atol=1e-4, rtol=1e-4)
         np.testing.assert_allclose(att[l], trace["attn"][l], atol=1e-4, rtol=1e-4)
         np.testing.assert_allclose(hb[2 * l + 1], trace["h_mid"][l], atol=1e-4, rtol=1e-4)
         np.testing.assert_allclose(ab[l], trace["a"][l], atol=1e-4, rtol=1e-4)
@@ -75,7 +85,8 @@ def test_tiny_one_step_stages_and_logits():
     sess.close()
 
 
-@pytest.mark.parametrize("name,steps", [("tiny", 32), ("llama1b", 32)])
+@pytest.mark.parametrize("name,steps", [("tiny", 32), pytest.param("tiny_qk", 32, marks=QK_SKIP),
+                                        ("llama1b", 32)])
 def test_greedy_tokens_identical(name, steps):
     """Greedy decoding: the oracle, teacher-forced on the GPU's tokens with
     its own KV cache, picks the same token at every step and its logits stay

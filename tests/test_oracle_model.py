@@ -167,3 +167,32 @@ def test_fp32_oracle_close_to_fp64():
     a = O.decode_step(cfg, W, tok, pos, kv.copy(), np.float32)
     b = O.decode_step(cfg, W, tok, pos, kv.copy(), np.float64)
     assert np.max(np.abs(a - b)) < 1e-4
+
+
+def test_qk_norm_makes_logits_invariant_to_scaling_wq_wk():
+    """Per-head RMSNorm of q and k (Qwen3) removes any positive scale of the
+    q/k projections (RMSNorm is scale invariant while |c|*rms >> sqrt(eps)):
+    doubling Wq and Wk (exact in bf16) leaves the logits unchanged with q/k
+    norm, and changes them without it."""
+    for qk in (True, False):
+        cfg = _small(qk_norm=qk)
+        W = synth.make_weights(cfg, std=0.2)
+        W2 = {**W, "layers": []}
+        for lw in W["layers"]:
+            lw2 = dict(lw)
+            for name in ("wq", "wk"):
+                f = O.bf16_to_f32(lw[name]) * 2.0        # exact: power of two
+                lw2[name] = O.f32_to_bf16(f)
+            W2["layers"].append(lw2)
+        outs = []
+        for WW in (W, W2):
+            kv = synth.make_kv_cache(cfg, batch=1, max_seq=4, filled=0)
+            for t in range(3):
+                lg = O.decode_step(cfg, WW, np.array([5 + t]), np.array([t]), kv, np.float64)
+            outs.append(lg)
+        d = np.abs(outs[0] - outs[1]).max()
+        scale = np.abs(outs[0]).max()
+        if qk:   # float32 logits (a few ulps) and the eps inside the root
+            assert d < 1e-5 * scale, (d, scale)
+        else:    # scores grow four-fold
+            assert d > 1e-2 * scale, (d, scale)
