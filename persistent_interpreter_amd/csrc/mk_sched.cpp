@@ -19,12 +19,13 @@
 
 namespace mk {
 
-int choose_kc(int K) {
+int choose_kc(int K, int kmax) {
   // piece bytes (2*kc) must be a multiple of 1 KB or divide 1 KB so that a
-  // 1 KB wave-load never straddles pieces unevenly
+  // 1 KB wave-load never straddles pieces unevenly; kc * batch fp32
+  // activations must fit one LDS activation slot (kmax = 2048 / batch)
   static const int cand[] = {2048, 1536, 1024, 512, 256, 128, 64, 32, 16, 8};
   for (int kc : cand)
-    if (kc <= K && K % kc == 0) return kc;
+    if (kc <= K && kc <= kmax && K % kc == 0) return kc;
   return 0;
 }
 
@@ -130,8 +131,15 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
     err = "num_cus and batch must be >= 1 and batch <= max_batch";
     return MK_ERR_INVALID_ARG;
   }
+  if (B > kMaxBatch) {
+    err = "batch must be <= 8 (positions and 1/rms of a step are staged in LDS)";
+    return MK_ERR_UNSUPPORTED;
+  }
   const int G = nq / nkv, HALF = hd / 2;
-  const int kc_h = choose_kc(H), kc_o = choose_kc(nq * hd), kc_f = choose_kc(F);
+  // batched plans use pieces of at most 256 elements (the batched dot maps
+  // 32 weight groups onto each half of a wave)
+  const int kmax = B == 1 ? kMaxKc : 256;
+  const int kc_h = choose_kc(H, kmax), kc_o = choose_kc(nq * hd, kmax), kc_f = choose_kc(F, kmax);
   if (!kc_h || !kc_o || !kc_f) {
     err = "hidden, n_q_heads*head_dim and ffn_dim must be multiples of 8";
     return MK_ERR_UNSUPPORTED;
@@ -158,13 +166,18 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
   P.mlp_chunks = chunks;
 
   // units: at least one per CU (when there are rows for it), at most
-  // kAccFloats row results each (their LDS staging slot)
-  auto units_for = [&](uint32_t rows, uint32_t ipw, uint32_t at_least) {
+  // `cap` row results per sequence-row of their LDS staging slot (QKV units
+  // keep half of it for the RoPE values of their pairs)
+  // units of one instruction: at least one per CU (and `at_least`), and
+  // enough that the largest unit's rows * ipw * batch results fit `cap`
+  // (units take ceil(rows / n) or floor(rows / n) rows)
+  auto units_for = [&](uint32_t rows, uint32_t ipw, uint32_t at_least, uint32_t cap = kAccFloats) {
     uint32_t n = std::max<uint32_t>(std::min<uint32_t>((uint32_t)C, rows), at_least);
-    n = std::max<uint32_t>(n, (uint32_t)((uint64_t)rows * ipw + kAccFloats - 1) / kAccFloats);
+    const uint32_t max_rows = std::max<uint32_t>(1, cap / (ipw * (uint32_t)B));
+    n = std::max<uint32_t>(n, (rows + max_rows - 1) / max_rows);
     return std::min<uint32_t>(n, rows);
   };
-  const uint32_t n_qkv = units_for(TP, 2, (uint32_t)nkv);
+  const uint32_t n_qkv = units_for(TP, 2, (uint32_t)nkv, kAccFloats / 2);
   const uint32_t n_o = units_for(H, 1, 1), n_down = units_for(H, 1, 1);
   const uint32_t n_ffn = units_for(F, 2, (uint32_t)chunks);
   const uint32_t n_lm = units_for(V, 1, 1);
@@ -327,9 +340,13 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
         cu_bytes[cu] += bytes;
         P.weight_bytes += bytes;
         P.n_pages += (int)in.pages;
-        if ((int64_t)in.n_items * in.ipw > kAccFloats ||
-            (in.op == OP_QKV && (int64_t)in.n_items * in.ipw > kAccFloats / 2)) {
+        if ((int64_t)in.n_items * in.ipw * B > kAccFloats ||
+            (in.op == OP_QKV && (int64_t)in.n_items * in.ipw * B > kAccFloats / 2)) {
           err = "internal: too many rows in a unit";
+          return MK_ERR_UNSUPPORTED;
+        }
+        if ((B > 1 && in.kc > 256) || in.kc * (uint32_t)B > (uint32_t)kMaxKc) {
+          err = "internal: piece too long for the batched dot";
           return MK_ERR_UNSUPPORTED;
         }
       }

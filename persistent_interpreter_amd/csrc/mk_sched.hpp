@@ -49,7 +49,7 @@ struct Plan {
 // Choose the elements per weight piece for a K dimension: the largest
 // divisor of K whose byte size is a multiple of 1 KB or a divisor of 1 KB,
 // at most kMaxKc.  Returns 0 if none.
-int choose_kc(int K);
+int choose_kc(int K, int kmax);
 
 // Build the plan.  Returns MK_OK or an MK_ERR_* code with `err` set.
 int build_plan(const mk_config &cfg, int batch, int num_cus, Plan &out,

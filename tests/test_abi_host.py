@@ -76,9 +76,18 @@ def test_batch_out_of_range():
     assert B.plan_check(cfg, 0, 8)[0] == B.MK_ERR_INVALID_ARG
 
 
+def test_batch_above_eight_unsupported():
+    """Positions and per-sequence 1/rms of a step are staged in LDS for at
+    most 8 sequences."""
+    cfg = B.make_config(synth.CONFIGS["tiny"], max_batch=16)
+    assert B.plan_check(cfg, 8, 8)[0] == B.MK_OK
+    assert B.plan_check(cfg, 9, 8)[0] == B.MK_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("name,cus,batch", [
-    ("tiny", 256, 1), ("tiny", 13, 1), ("tiny", 1, 1), ("tiny", 8, 3),
-    ("llama1b", 256, 1), ("llama1b", 31, 1), ("llama1b", 256, 8),
+    ("tiny", 256, 1), ("tiny", 13, 1), ("tiny", 1, 1), ("tiny", 8, 3), ("tiny", 256, 8),
+    ("llama1b", 256, 1), ("llama1b", 31, 1), ("llama1b", 256, 8), ("llama1b", 256, 3),
+    ("llama1b", 13, 7), ("tiny", 13, 5),
     ("qwen3_8b", 256, 1), ("llama70b", 256, 4)])
 def test_plans_validate(name, cus, batch):
     mc = synth.CONFIGS[name]

@@ -123,3 +123,55 @@ def test_greedy_tokens_identical(name, steps):
     assert kv_bad == 0, (kv_bad, kv_worst)
     untouched = np.r_[0:int(pos[0]), int(pos[0]) + steps:gkv.shape[4]]
     assert np.array_equal(gkv[:, :, :, :, untouched], kv[:, :, :, :, untouched])
+
+
+BATCHED = [("tiny", 3, 8), ("tiny", 8, 4), ("llama1b_b8", 8, 4)]
+BATCH_SKIP = pytest.mark.skip(reason="batched decode switched off: a 4-step batch-8 run faulted the "
+                                     "GPU once after passing in a fresh process; cause not found yet "
+                                     "(mk_decode_step returns MK_ERR_UNSUPPORTED for batch > 1)")
+
+
+@BATCH_SKIP
+@pytest.mark.parametrize("name,batch,steps", BATCHED)
+def test_batched_greedy_matches_oracle(name, batch, steps):
+    """Several sequences per step, each at its own position: the logits of
+    every sequence stay within TOL of the oracle's (teacher-forced on the
+    GPU's tokens, on the GPU's own KV history), the greedy tokens agree,
+    the K/V slot each sequence writes matches to one bf16 ulp, and no other
+    slot of the cache changes."""
+    mc = synth.CONFIGS[name]
+    if mc.batch != batch or not mc.pos_hi:
+        mc = mc.replace(batch=batch, pos_lo=4, pos_hi=40)
+    W = synth.make_weights(mc)
+    kv = synth.make_kv_cache(mc)
+    tok, pos = synth.make_tokens(mc), synth.make_positions(mc)
+    print(f"{name}: batch {batch}, positions {pos.tolist()}", flush=True)
+    sess = harness.Session(mc, W, kv.copy(), batch=batch)
+    fed_g, out_g = harness.greedy_run(sess, tok, pos, steps)
+    gkv = sess.kv_host()
+    sess.close()
+    Wf = O.upcast_weights(W)
+    work = gkv.copy()   # GPU history; each step's slots are re-derived by the oracle
+    bidx = np.arange(batch)
+    worst, kv_bad = 0.0, 0
+    for i in range(steps):
+        ref = O.decode_step(mc, Wf, fed_g[i], pos + i, work)
+        d = float(np.abs(out_g[i] - ref).max())
+        worst = max(worst, d)
+        assert d <= TOL, (i, d)
+        assert np.array_equal(np.argmax(out_g[i], -1), np.argmax(ref, -1)), i
+        for b in range(batch):
+            s = int(pos[b]) + i
+            nb, _ = _kv_bad(gkv[:, :, b, :, s], work[:, :, b, :, s])
+            kv_bad += nb
+            work[:, :, b, :, s] = gkv[:, :, b, :, s]
+    print(f"{name} batch {batch}: {steps} steps, worst max|dlogit| {worst:.3e}, "
+          f"KV slots beyond tolerance {kv_bad}")
+    assert kv_bad == 0
+    # every slot no sequence wrote is untouched
+    written = np.zeros(gkv.shape[2:5:2], dtype=bool)  # [B][S]
+    for b in bidx:
+        written[b, int(pos[b]):int(pos[b]) + steps] = True
+    keep = ~written
+    for b in bidx:
+        assert np.array_equal(gkv[:, :, b, :, keep[b]], kv[:, :, b, :, keep[b]]), b
