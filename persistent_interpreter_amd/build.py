@@ -38,7 +38,7 @@ def _run(cmd):
 
 def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     """Compile every source and link the library; returns its path.
-    ``defines`` (e.g. ``["MK_DEPTH=2"]``) override compile-time knobs."""
+    ``defines`` (e.g. ``["MK_SDEPTH=2"]``) override compile-time knobs."""
     out_dir = os.path.dirname(out)
     os.makedirs(out_dir, exist_ok=True)
     dflags = [f"-D{d}" for d in defines]

@@ -32,6 +32,7 @@ struct DevPlan {
   uint32_t *d_ctr = nullptr;
   uint32_t *d_target = nullptr;
   float *d_part = nullptr;
+  uint32_t *d_iota = nullptr;
   uint64_t *d_trace = nullptr;
   size_t ctr_bytes = 0, trace_bytes = 0;
   uint32_t trace_stride = 0;
@@ -65,6 +66,7 @@ void free_plan(DevPlan &p) {
   hipFree(p.d_ctr);
   hipFree(p.d_target);
   hipFree(p.d_part);
+  hipFree(p.d_iota);
   hipFree(p.d_trace);
 }
 
@@ -279,7 +281,17 @@ static int get_plan(mk_handle *h, int batch, DevPlan **out) {
   dp->ctr_bytes = (size_t)P.n_groups * kSlots * kCtrStride * 4;
   const size_t part = (size_t)h->cfg.n_layers * h->cfg.max_batch * h->cfg.n_q_heads * P.n_split *
                       (h->cfg.head_dim + 4) * 4;
+  // page sentinels: iota[i] = i for every page index of the longest queue
+  uint32_t max_pages = 0;
+  for (int c = 0; c < h->num_cus; ++c) {
+    uint32_t np = 0;
+    for (uint32_t q = P.q_off[c]; q < P.q_off[c + 1]; ++q) np += P.instr[q].pages;
+    max_pages = std::max(max_pages, np);
+  }
+  std::vector<uint32_t> iota(max_pages + 1);
+  for (uint32_t i = 0; i <= max_pages; ++i) iota[i] = i;
   if ((rc = upload(&dp->d_instr, P.instr)) || (rc = upload(&dp->d_qoff, P.q_off)) ||
+      (rc = upload(&dp->d_iota, iota)) ||
       (rc = upload(&dp->d_waits, P.waits)) || (rc = upload(&dp->d_rowtab, P.rowtab)) ||
       (rc = upload(&dp->d_target, P.grp_target)) || (rc = dev_alloc(&dp->d_ctr, dp->ctr_bytes)) ||
       (rc = dev_alloc(&dp->d_part, part))) {
@@ -333,6 +345,7 @@ int mk_decode_step(mk_handle *h, int32_t batch, const int32_t *tokens, const int
   a.ctr = dp->d_ctr;
   a.grp_target = dp->d_target;
   a.part_buf = dp->d_part;
+  a.iota = dp->d_iota;
   a.tokens = tokens;
   a.positions = positions;
   a.kv = (uint16_t *)kv_cache;

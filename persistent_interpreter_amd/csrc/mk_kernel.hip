@@ -263,6 +263,25 @@ __device__ __forceinline__ bool spin_lds(const Env &e, F cond, uint32_t info) {
   }
 }
 
+// The same with a short sleep: for waits whose producer cannot wake the
+// waiter (a page sentinel written by a direct-to-LDS load).
+template <class F>
+__device__ __forceinline__ bool spin_lds_fast(const Env &e, F cond, uint32_t info) {
+  if (cond()) return true;
+  Watchdog wd;
+  for (uint32_t it = 1;; ++it) {
+    __builtin_amdgcn_s_sleep(1);
+    if (cond()) return true;
+    if ((it & 255) == 0) {
+      if (lds_ld(L_ABORT)) return false;
+      if (wd.expired(e.cp->watchdog_ticks)) {
+        raise_error(e, 0xA0000000u | info, 0);
+        return false;
+      }
+    }
+  }
+}
+
 // Re-run `load` (it re-reads tagged words and returns, per lane, whether all
 // of them carry this step's tag) until every lane is satisfied.
 template <class F>
@@ -313,15 +332,6 @@ __device__ __forceinline__ uint32_t asm_lds_ld(uint32_t off) {
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(off) : "memory");
   return v;
 }
-__device__ __forceinline__ void asm_lds_st(uint32_t off, uint32_t v) {
-  off = lds_addr((int)off);
-  asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(off), "v"(v) : "memory");
-}
-
-#ifndef MK_DEPTH
-#define MK_DEPTH 2
-#endif
-constexpr int kDepth = MK_DEPTH;  // pages in flight per loader wave (16 loads each, <= 63)
 
 template <int N>
 __device__ __forceinline__ void wait_vm_n() {
@@ -330,33 +340,20 @@ __device__ __forceinline__ void wait_vm_n() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+#ifndef MK_SDEPTH
+#define MK_SDEPTH 3
+#endif
+constexpr int kSentDepth = MK_SDEPTH;  // pages in flight per loader wave (17 loads each, <= 63)
+static_assert(kSentDepth >= 1 && 17 * kSentDepth <= 63, "load counter range");
+// Each loader wave keeps up to kSentDepth pages in flight (17 loads each: 16
+// weight loads and the page's sentinel).  A page is never published by the
+// loader: its sentinel lands after its data, so the loader only waits for a
+// free ring slot (compute waves' releases) and, to bound its load counter,
+// for its oldest page once kSentDepth are in flight.
 __device__ void loader_role(const Env &e, const Args &a, int lw) {
   const int lane = lane_id();
   const uint32_t P = (uint32_t)e.cp->ring_pages;
-  // pages of this wave are lw, lw + kNLW, ...; the pending ones (issued,
-  // not yet published) are `oldest`, oldest + kNLW, ... (npend of them)
-  uint32_t oldest = 0;
   int npend = 0;
-  auto publish_oldest = [&]() {
-    asm_lds_st(L_FILLED + 4 * (oldest % P), oldest + 1);
-    wake();
-    oldest += kNLW;
-    --npend;
-  };
-  auto drain = [&]() {
-    wait_vm0();
-    while (npend) publish_oldest();
-  };
-  // wait until the oldest pending page has landed (16 loads per page)
-  auto wait_oldest = [&]() {
-    static_assert(kDepth <= 3, "vmcnt immediates below cover 4 pending pages");
-    switch (npend) {
-      case 1: wait_vm_n<0>(); break;
-      case 2: wait_vm_n<16>(); break;
-      case 3: wait_vm_n<32>(); break;
-      default: wait_vm_n<48>(); break;
-    }
-  };
   auto min_cons = [&]() -> uint32_t {
     uint32_t v = lane < kNCW ? asm_lds_ld(L_CONS + 4 * lane) : 0xffffffffu;
     // minimum over lanes 0..7 with readlanes (no LDS-unit cross-lane ops)
@@ -373,32 +370,25 @@ __device__ void loader_role(const Env &e, const Args &a, int lw) {
     const uint32_t npieces = per * d.nk;
     for (uint32_t p = 0; p < d.pages; ++p, ++n) {
       if ((int)(n % kNLW) != lw) continue;
-      if (n >= P) {
-        // slot n % P is free once every compute wave released page n - P;
-        // meanwhile publish this wave's pending pages one by one as they
-        // land (a compute wave may be waiting on one of them), keeping the
-        // younger ones in flight
+      if (n >= P && min_cons() < n - P + 1) {
+        // slot n % P is free once every compute wave released page n - P
         const uint32_t need = n - P + 1;
-        if (min_cons() < need) {
-          Watchdog wd;
-          for (uint32_t it = 1;; ++it) {
-            if (npend) {
-              wait_oldest();
-              publish_oldest();
-            } else {
-              __builtin_amdgcn_s_sleep(MK_SLEEP);
-            }
-            if (min_cons() >= need) break;
-            if ((it & 63) == 0) {
-              if (__builtin_amdgcn_readfirstlane(asm_lds_ld(L_ABORT))) { wait_vm0(); return; }
-              if (wd.expired(e.cp->watchdog_ticks)) { raise_error(e, 0xB0000000u | qi, n); wait_vm0(); return; }
-            }
+        Watchdog wd;
+        for (uint32_t it = 1;; ++it) {
+          __builtin_amdgcn_s_sleep(1);
+          if (min_cons() >= need) break;
+          if ((it & 63) == 0) {
+            if (__builtin_amdgcn_readfirstlane(asm_lds_ld(L_ABORT))) { wait_vm0(); return; }
+            if (wd.expired(e.cp->watchdog_ticks)) { raise_error(e, 0xB0000000u | qi, n); wait_vm0(); return; }
           }
         }
       }
-      // issue exactly 16 wave-loads (1 KB each) for page p into slot n % P;
-      // unused tail loads re-read the page's first piece so every page
-      // counts 16 in vmcnt
+      if (npend == kSentDepth) {
+        wait_vm_n<17 * (kSentDepth - 1)>();  // the oldest page of this wave has landed
+        --npend;
+      }
+      // issue exactly 16 wave-loads (1 KB each) for page p into slot n % P,
+      // then its sentinel; unused tail loads re-read the page's first piece
       LDS_AS char *slot = (LDS_AS char *)smem + L_RING + (n % P) * kPageBytes;
       const uint32_t t0 = p * d.ppp;
       const uint32_t cnt = min((uint32_t)d.ppp, npieces - t0);
@@ -441,14 +431,11 @@ __device__ void loader_role(const Env &e, const Args &a, int lw) {
           __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)(slot + j * 1024), 16, 0, 0);
         }
       }
-      if (npend++ == 0) oldest = n;
-      if (npend == kDepth + 1) {
-        wait_vm_n<16 * kDepth>();
-        publish_oldest();
-      }
+      __builtin_amdgcn_global_load_lds(a.iota + n, (LDS_AS void *)(smem + L_SENT + (n % P) * kSentBytes), 4, 0, 0);
+      ++npend;
     }
   }
-  drain();
+  wait_vm0();
 }
 
 // --------------------------------------------------------------------------
@@ -522,6 +509,7 @@ __device__ void sync_role(const Env &e, const Args &a) {
   }
   const size_t HB = (size_t)c.max_batch * c.H;
   float *rsl = reinterpret_cast<float *>(smem + L_RS);  // per-sequence 1/rms of the current norm
+  float rs0 = 0.f;                                       // batch 1: the one 1/rms
   uint32_t seq = 0;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
@@ -612,11 +600,14 @@ __device__ void sync_role(const Env &e, const Args &a) {
         };
         f4 hv[8];
         if (k == 0) {
-          // 1/rms of every sequence's full vector
+          // 1/rms of every sequence's full vector (batch 1: kept in rs0)
           for (int b = 0; b < B; ++b) {
-            const float *h;
-            const uint16_t *emb, *w_unused;
-            norm_src(e, a, d, b, h, emb, w_unused);
+            const float *h = h0;
+            const uint16_t *emb = emb0;
+            if (b > 0) {
+              const uint16_t *w_unused;
+              norm_src(e, a, d, b, h, emb, w_unused);
+            }
             float ss = 0.f;
             for (uint32_t e0 = 0; e0 < (uint32_t)c.H; e0 += 2048) {
               load_batch(h, emb, e0, hv);
@@ -625,9 +616,11 @@ __device__ void sync_role(const Env &e, const Args &a) {
                 ss += hv[m].x * hv[m].x + hv[m].y * hv[m].y + hv[m].z * hv[m].z + hv[m].w * hv[m].w;
             }
             ss = wave_sum(ss);
-            if (lane == 0) rsl[b] = 1.0f / sqrtf(ss / (float)c.H + c.eps);
+            const float r = 1.0f / sqrtf(ss / (float)c.H + c.eps);
+            if (b == 0) rs0 = r;
+            if (B > 1 && lane == 0) rsl[b] = r;
           }
-          wait_lgkm0();
+          if (B > 1) wait_lgkm0();
         }
         const uint32_t k0 = k * d.kc;
         if (k > 0) stage_norm_weights(k0);
@@ -658,7 +651,7 @@ __device__ void sync_role(const Env &e, const Args &a) {
           const uint32_t f = (uint32_t)(lane + 64 * m) * 4;
           if (f < nflat) {
             const uint32_t b = qdiv(f, mk), i = f - b * d.kc;
-            const float rs = rsl[b];
+            const float rs = B == 1 ? rs0 : rsl[b];
             const f4 v = hv[m];
             const uint64_t w4 = nwl[i >> 2];
             const uint32_t w0 = (uint32_t)w4, w1 = (uint32_t)(w4 >> 32);
@@ -1216,7 +1209,7 @@ __device__ void compute_role(const Env &e, const Args &a, int cw) {
               rel = pg;
               wake();  // a loader may wait for a released slot
             }
-            if (!spin_lds(e, [&]() { return lds_ld(L_FILLED + 4 * (pg % P)) >= pg + 1; }, 0x300 | qi)) return;
+            if (!spin_lds_fast(e, [&]() { return lds_ld(L_SENT + (pg % P) * kSentBytes) == pg; }, 0x300 | qi)) return;
             wpg = pg;
           }
           const char *piece = smem + L_RING + (pg % P) * kPageBytes + o * d.pb;
@@ -1300,11 +1293,11 @@ __device__ void compute_role(const Env &e, const Args &a, int cw) {
 __global__ void __launch_bounds__(kThreads, 1)
 mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const uint32_t *__restrict__ q_off,
           const Wait *__restrict__ waits, const uint64_t *__restrict__ rowtab, uint32_t *__restrict__ ctr, const uint32_t *__restrict__ grp_target,
-          float *__restrict__ part_buf, const int32_t *__restrict__ tokens,
+          float *__restrict__ part_buf, const uint32_t *__restrict__ iota, const int32_t *__restrict__ tokens,
           const int32_t *__restrict__ positions, uint16_t *__restrict__ kv, float *__restrict__ logits,
           uint64_t *__restrict__ trace, uint32_t trace_stride, uint32_t epoch, uint32_t tag, int32_t batch, int32_t n_split,
           int32_t split_len) {
-  const Args a{ctx, instr, q_off, waits, rowtab, ctr, grp_target, part_buf, tokens, positions, kv, logits,
+  const Args a{ctx, instr, q_off, waits, rowtab, ctr, grp_target, part_buf, iota, tokens, positions, kv, logits,
                trace, trace_stride, epoch, tag, batch, n_split, split_len};
   Env e;
   e.cp = a.ctx;
@@ -1325,6 +1318,9 @@ mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const
     }
     lds_u32(threadIdx.x * 4) = (uint32_t)p;
   }
+  // no page has landed: sentinels hold an index no page has
+  for (int i = (int)threadIdx.x; i < kRingPages * kSentBytes / 4; i += kThreads)
+    lds_u32(L_SENT + 4 * i) = 0xffffffffu;
   __syncthreads();
   const int w = (int)(threadIdx.x >> 6);
 #if MK_PRIO
@@ -1353,7 +1349,7 @@ hipError_t kernel_setup(int *blocks_per_cu) {
 
 hipError_t kernel_launch(const Args &a0, int grid, hipStream_t stream) {
   Args a = a0;
-  void *params[] = {&a.ctx, &a.instr, &a.q_off, &a.waits, &a.rowtab, &a.ctr, &a.grp_target, &a.part_buf,
+  void *params[] = {&a.ctx, &a.instr, &a.q_off, &a.waits, &a.rowtab, &a.ctr, &a.grp_target, &a.part_buf, &a.iota,
                     &a.tokens, &a.positions, &a.kv, &a.logits, &a.trace, &a.trace_stride, &a.epoch, &a.tag,
                     &a.batch, &a.n_split, &a.split_len};
   return hipLaunchCooperativeKernel((const void *)mk_interp, dim3(grid), dim3(kThreads), params, kLdsBytes,

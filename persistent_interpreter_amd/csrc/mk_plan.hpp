@@ -112,7 +112,7 @@ struct DevCtx {
 };
 
 // LDS layout of a workgroup (bytes).
-constexpr int L_FILLED = 0;     // u32[16]  page slot -> (page index + 1)
+// (bytes 0..63 unused)
 constexpr int L_CONS = 64;      // u32[8]   pages released per compute wave
 constexpr int L_XCONS = 96;     // u32[8]   activation pieces released per wave
 constexpr int L_XREADY = 128;   // u32      activation pieces produced
@@ -130,7 +130,13 @@ constexpr int kRingPages = (kLdsBytes - L_RING) / kPageBytes < kMaxRingPages
                                ? (kLdsBytes - L_RING) / kPageBytes : kMaxRingPages;
 static_assert(kRingPages >= 4, "LDS budget");
 constexpr int L_NW = L_RING + kRingPages * kPageBytes;  // bf16 norm weights of one piece
-static_assert(L_NW + kMaxKc * 2 <= kLdsBytes, "LDS budget");
+// Page sentinels: after a page's 16 weight loads the loader issues one more
+// direct-to-LDS load of the page's index (from a table holding i at i) into
+// the slot's sentinel (64 lanes x 4 bytes).  Loads return in issue order, so
+// a sentinel equal to n means page n has landed.
+constexpr int kSentBytes = 256;
+constexpr int L_SENT = L_NW + kMaxKc * 2;
+static_assert(L_SENT + kRingPages * kSentBytes <= kLdsBytes, "LDS budget");
 
 // Kernel arguments of one decode step (one per-batch plan).
 struct Args {
@@ -142,6 +148,7 @@ struct Args {
   uint32_t *ctr;              // [n_groups][kSlots][kCtrStride]
   const uint32_t *grp_target; // [n_groups][kSlots] arrivals per step
   float *part_buf;            // [L][max_batch][nq][n_split][hd + 4] (o.., m, l)
+  const uint32_t *iota;       // iota[i] = i for every page index of the longest queue
   const int32_t *tokens;
   const int32_t *positions;
   uint16_t *kv;
