@@ -350,7 +350,7 @@ static_assert(kSentDepth >= 1 && 17 * kSentDepth <= 63, "load counter range");
 // loader: its sentinel lands after its data, so the loader only waits for a
 // free ring slot (compute waves' releases) and, to bound its load counter,
 // for its oldest page once kSentDepth are in flight.
-__device__ void loader_role(const Env &e, const Args &a, int lw) {
+__device__ __forceinline__ void loader_role(const Env &e, const Args &a, int lw) {
   const int lane = lane_id();
   const uint32_t P = (uint32_t)e.cp->ring_pages;
   int npend = 0;
@@ -441,29 +441,49 @@ __device__ void loader_role(const Env &e, const Args &a, int lw) {
 // --------------------------------------------------------------------------
 // Sync wave: counter waits and activation pieces.
 
-// Poll one counter group until each of its counter slots reached
-// target * epoch.  Lane i polls slot i (i < nslot).
-__device__ bool wait_group(const Env &e, const Args &a, const Wait &wt, uint32_t qi) {
+// Poll counter groups w[0..n) until each of their counter slots reached
+// target * epoch.  Lane l polls slot l - c_i of the group i whose slots
+// [c_i, c_i + nslot_i) contain l, so every group of a unit whose slots fit
+// one wave (64 in total) is checked in the same round trip; further groups
+// are taken in later rounds of the same loop.
+__device__ __forceinline__ bool wait_groups(const Env &e, const Args &a, const Wait *w, uint32_t n, uint32_t qi) {
   const int lane = lane_id();
-  const uint32_t grp = wt.grp;
-  const bool mine = lane < (int)wt.nslot;
-  const uint32_t *cp = a.ctr + ((size_t)grp * kSlots + (lane & (kSlots - 1))) * kCtrStride;
-  const uint32_t need = mine ? a.grp_target[grp * kSlots + lane] * a.epoch : 0u;
-  Watchdog wd;
-  for (uint32_t it = 0;; ++it) {
-    bool ok = true;
-    if (mine) ok = (int32_t)(ld_cu(cp) - need) >= 0;
-    if (__all(ok)) return true;
-    if ((it & 63) == 63) {
-      if (lds_ld(L_ABORT)) return false;
-      if (ld_cu(&e.cp->status[0]) != 0) { lds_st(L_ABORT, 1); return false; }
-      if (wd.expired(e.cp->watchdog_ticks)) {
-        raise_error(e, 0xC0000000u | grp, qi);
-        return false;
+  uint32_t i0 = 0;
+  while (i0 < n) {
+    // groups i0 .. i1 - 1 fill at most one wave (a single group always fits)
+    uint32_t i1 = i0, tot = 0;
+    while (i1 < n && (i1 == i0 || tot + w[i1].nslot <= (uint32_t)kSlots)) tot += w[i1++].nslot;
+    uint32_t grp = 0, slot = 0, cum = 0;
+    bool mine = false;
+    for (uint32_t i = i0; i < i1; ++i) {
+      const uint32_t ns = w[i].nslot;
+      if ((uint32_t)lane >= cum && (uint32_t)lane < cum + ns) {
+        grp = w[i].grp;
+        slot = (uint32_t)lane - cum;
+        mine = true;
       }
+      cum += ns;
     }
-    __builtin_amdgcn_s_sleep(MK_WSLEEP);
+    const uint32_t *cp = a.ctr + ((size_t)grp * kSlots + slot) * kCtrStride;
+    const uint32_t need = mine ? a.grp_target[grp * kSlots + slot] * a.epoch : 0u;
+    Watchdog wd;
+    for (uint32_t it = 0;; ++it) {
+      bool ok = true;
+      if (mine) ok = (int32_t)(ld_cu(cp) - need) >= 0;
+      if (__all(ok)) break;
+      if ((it & 63) == 63) {
+        if (lds_ld(L_ABORT)) return false;
+        if (ld_cu(&e.cp->status[0]) != 0) { lds_st(L_ABORT, 1); return false; }
+        if (wd.expired(e.cp->watchdog_ticks)) {
+          raise_error(e, 0xC0000000u | w[i0].grp, qi);
+          return false;
+        }
+      }
+      __builtin_amdgcn_s_sleep(MK_WSLEEP);
+    }
+    i0 = i1;
   }
+  return true;
 }
 
 // Input vector source of the RMSNorm'd instructions for sequence b: the
@@ -497,7 +517,7 @@ __device__ __forceinline__ uint32_t qdiv(uint32_t f, uint32_t m) { return (f * m
 // Position of sequence b (staged in LDS at kernel start).
 __device__ __forceinline__ int pos_of(int b) { return (int)lds_ld(L_POS + 4 * b); }
 
-__device__ void sync_role(const Env &e, const Args &a) {
+__device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
   const int B = a.batch;
@@ -552,12 +572,84 @@ __device__ void sync_role(const Env &e, const Args &a) {
 
     uint32_t wi = 0;
     if (lane == 0) trace_now(e, qi, 4);
+    const bool dma_pieces = (d.op == OP_DOWN || (d.op == OP_O && d.layer > 0)) && d.n_items * (uint32_t)B <= 64;
+    if (dma_pieces) {
+      // O and DOWN units (but layer 0's O, whose residual is the bf16
+      // embedding row): the activation pieces are plain fp32 copies of attn
+      // / a and the residual rows copies of h, so they go to LDS by
+      // direct-to-LDS loads, two pieces in flight, with every counter of the
+      // unit polled in one round trip first.  A piece is exactly 8 wave-loads
+      // (1 KB each, clamped lanes re-read the piece start), piece 0 one more
+      // for the residual rows, so `vmcnt` tells when the older one landed.
+      if (d.wait_n && !wait_groups(e, a, a.waits + d.wait_off, d.wait_n, qi)) return;
+      if (lane == 0) {
+        trace_put(e, qi, 0, (uint64_t)d.op | ((uint64_t)d.layer << 8) | ((uint64_t)d.unit << 24));
+        trace_now(e, qi, 1);
+      }
+      const uint32_t SB = d.op == OP_O ? (uint32_t)(c.nq * c.hd) : (uint32_t)c.F;
+      const float *src = (d.op == OP_O ? c.attn_buf : c.a_buf) + (size_t)d.layer * c.max_batch * SB;
+      const uint32_t nflat = d.kc * (uint32_t)B;
+      const uint32_t mk = B > 1 ? div_magic(d.kc) : 0u;
+      uint32_t off[8];  // element offsets of this lane's 16 bytes in each wave-load
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t f = (uint32_t)(j * 256 + lane * 4);
+        const uint32_t b = qdiv(f, mk), i = f - b * d.kc;
+        off[j] = f < nflat ? b * SB + i : 0u;
+      }
+      const uint32_t nres = d.n_items * (uint32_t)B;
+      const uint32_t mi = B > 1 ? div_magic(d.n_items) : 0u;
+      const uint32_t rb = qdiv((uint32_t)lane, mi), rr = (uint32_t)lane - rb * d.n_items;
+      const float *res = c.h_buf + (size_t)(d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1) * HB +
+                         (size_t)rb * c.H + d.item0 + rr;
+      auto issue = [&](uint32_t k, uint32_t sq) {
+        if (k == 0 && lane < (int)nres)
+          __builtin_amdgcn_global_load_lds(res, (LDS_AS void *)((LDS_AS char *)smem + L_ACC +
+                                                                (qi & (kAccSlots - 1)) * kAccFloats * 4),
+                                           4, 0, kSC1);
+        LDS_AS char *slot = (LDS_AS char *)smem + L_XS + (sq % kNXS) * kXSlotBytes;
+        const float *base = src + (size_t)k * d.kc;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          __builtin_amdgcn_global_load_lds(base + off[j], (LDS_AS void *)(slot + j * 1024), 16, 0, kSC1);
+      };
+      uint32_t issued = 0, done = 0;
+      while (done < nx) {
+        if (issued < nx && issued - done < (uint32_t)kNXS) {
+          const uint32_t sq = seq + issued;
+          if (sq >= (uint32_t)kNXS) {
+            const uint32_t need = sq - kNXS + 1;
+            auto freed = [&]() {
+              uint32_t v = lane < kNCW ? lds_ld_lane(L_XCONS + 4 * lane) : 0xffffffffu;
+              uint32_t m = __builtin_amdgcn_readlane(v, 0);
+#pragma unroll
+              for (int i = 1; i < kNCW; ++i) m = min(m, (uint32_t)__builtin_amdgcn_readlane(v, i));
+              return m >= need;
+            };
+            if (!spin_lds(e, freed, 0x100 | qi)) { wait_vm0(); return; }
+          }
+          issue(issued, sq);
+          ++issued;
+          continue;
+        }
+        if (issued - done >= 2) wait_vm_n<8>();
+        else wait_vm0();
+        if (lane == 0) lds_st(L_XREADY, seq + done + 1);
+        wake();
+        if (lane == 0 && done == 0) trace_now(e, qi, 5);
+        if (lane == 0 && done + 1 == nx) trace_now(e, qi, 7);
+        ++done;
+      }
+      seq += nx;
+    }
+    // (a `continue` above instead of this test makes the compiler spill)
+    if (!dma_pieces)
     for (uint32_t k = 0; k < nx; ++k, ++seq) {
-      while (wi < d.wait_n) {
-        const Wait wt = a.waits[d.wait_off + wi];
-        if (wt.before_k > k) break;
-        if (!wait_group(e, a, wt, qi)) return;
-        ++wi;
+      {
+        uint32_t wn = wi;
+        while (wn < d.wait_n && a.waits[d.wait_off + wn].before_k <= k) ++wn;
+        if (wn > wi && !wait_groups(e, a, a.waits + d.wait_off + wi, wn - wi, qi)) return;
+        wi = wn;
       }
       if (seq >= (uint32_t)kNXS) {
         const uint32_t need = seq - kNXS + 1;
@@ -710,6 +802,7 @@ __device__ void sync_role(const Env &e, const Args &a) {
       if (lane == 0) lds_st(L_XREADY, seq + 1);
       wake();
       if (k == 0 && lane == 0) trace_now(e, qi, 5);
+      if (k + 1 == nx && lane == 0) trace_now(e, qi, 7);
     }
   }
 }
@@ -734,7 +827,7 @@ __device__ __forceinline__ float dot_piece(const char *piece, const float (&xr)[
       "ds_read_b128 %2, %4 offset:2048\n\t"
       "ds_read_b128 %3, %4 offset:3072\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(w[0]), "=v"(w[1]), "=v"(w[2]), "=v"(w[3])
+      : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3])  // early-clobber: later reads use addr
       : "v"(addr));
   if (n16 < 256) {
 #pragma unroll
@@ -834,7 +927,7 @@ __device__ __forceinline__ size_t kv_off(const DevCtx &c, int l, int t, int b, i
 //   QKV : RoPE on q/k pairs (i, i + hd/2), q -> fp32 scratch, k/v -> bf16
 //         cache slot p;   O, DOWN: R already holds residual + dot;
 //   FFN : a = silu(gate) * up;   LM: logits.
-__device__ void unit_epilogue(const Env &e, const Args &a, const Instr &d, const float *R) {
+__device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const Instr &d, const float *R) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
   const size_t HB = (size_t)c.max_batch * c.H;
@@ -1102,7 +1195,7 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Ga
 // m* = max m_s, w_s = exp(m_s - m*), out = sum w_s o_s / sum w_s l_s; empty
 // splits (m = -inf) get weight 0.
 template <int DPL>
-__device__ void red_body(const Env &e, const Args &a, const Instr &d, int h) {
+__device__ __forceinline__ void red_body(const Env &e, const Args &a, const Instr &d, int h) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
   const int b = (int)d.b, g = (int)d.aux0;
@@ -1154,7 +1247,7 @@ __device__ void red_body(const Env &e, const Args &a, const Instr &d, int h) {
   for (int m = 0; m < dpl; ++m) st_c(out + lane + 64 * m, o[m] / L);
 }
 
-__device__ void compute_role(const Env &e, const Args &a, int cw) {
+__device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
   const uint32_t P = (uint32_t)c.ring_pages;

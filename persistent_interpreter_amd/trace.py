@@ -17,7 +17,7 @@ OPS = {1: "qkv", 2: "attn", 3: "attn_red", 4: "o_proj", 5: "ffn_gate_up",
 TICK_US = 0.01  # 100 MHz
 
 
-FIELDS = ("t_wait", "t_start", "t_done", "t_begin", "t_xready", "t_epi")
+FIELDS = ("t_wait", "t_start", "t_done", "t_begin", "t_xready", "t_epi", "t_xlast")
 
 
 def decode(raw: np.ndarray) -> np.ndarray:
@@ -29,7 +29,8 @@ def decode(raw: np.ndarray) -> np.ndarray:
     t_xready the first activation piece was published in LDS
     t_start  compute wave 0 passed the unit's gate
     t_epi    the last compute wave finished its pieces (epilogue starts)
-    t_done   epilogue done, counters about to be signalled"""
+    t_done   epilogue done, counters about to be signalled
+    t_xlast  the last activation piece was published (= t_xready for one)"""
     raw = np.asarray(raw, dtype=np.uint64)
     ncu, stride = int(raw[0]), int(raw[1])
     words = int(raw[2]) or 4
@@ -40,11 +41,11 @@ def decode(raw: np.ndarray) -> np.ndarray:
             r = rec[cu, i]
             if r[0] == 0 or r[1] == 0 or r[3] == 0:
                 continue
-            ext = [r[4], r[5], r[6]] if words >= 8 else [r[1], r[1], r[3]]
+            ext = [r[4], r[5], r[6], r[7]] if words >= 8 else [r[1], r[1], r[3], r[1]]
             out.append((cu, i, r[0] & 0xFF, (r[0] >> 8) & 0xFFFF, r[0] >> 24, r[1], r[2], r[3], *ext))
     dt = np.dtype([("cu", "i4"), ("idx", "i4"), ("op", "i4"), ("layer", "i4"), ("unit", "i4"),
                    ("t_wait", "f8"), ("t_start", "f8"), ("t_done", "f8"),
-                   ("t_begin", "f8"), ("t_xready", "f8"), ("t_epi", "f8")])
+                   ("t_begin", "f8"), ("t_xready", "f8"), ("t_epi", "f8"), ("t_xlast", "f8")])
     a = np.array(out, dtype=dt)
     if len(a):
         valid = [a[f][a[f] > 0] for f in FIELDS]
