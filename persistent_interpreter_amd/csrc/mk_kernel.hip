@@ -190,6 +190,7 @@ struct Env {
   const Instr *q;    // this workgroup's queue
   uint32_t nq;       // its length
   int cu;
+  int pos0;          // positions[0], read once at kernel start (batch 1)
 };
 
 __device__ __forceinline__ int64_t now() { return (int64_t)wall_clock64(); }
@@ -332,7 +333,6 @@ __device__ __forceinline__ uint32_t asm_lds_ld(uint32_t off) {
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(off) : "memory");
   return v;
 }
-
 template <int N>
 __device__ __forceinline__ void wait_vm_n() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -441,53 +441,32 @@ __device__ __forceinline__ void loader_role(const Env &e, const Args &a, int lw)
 // --------------------------------------------------------------------------
 // Sync wave: counter waits and activation pieces.
 
-// Poll counter groups w[0..n) until each of their counter slots reached
-// target * epoch.  Lane l polls slot l - c_i of the group i whose slots
-// [c_i, c_i + nslot_i) contain l, so every group of a unit whose slots fit
-// one wave (64 in total) is checked in the same round trip; further groups
-// are taken in later rounds of the same loop.
-__device__ __forceinline__ bool wait_groups(const Env &e, const Args &a, const Wait *w, uint32_t n, uint32_t qi) {
+// Poll one counter group until each of its counter slots reached
+// target * epoch.  Lane i polls slot i (i < nslot).
+__device__ __forceinline__ bool wait_group(const Env &e, const Args &a, const Wait &wt, uint32_t qi) {
   const int lane = lane_id();
-  uint32_t i0 = 0;
-  while (i0 < n) {
-    // groups i0 .. i1 - 1 fill at most one wave (a single group always fits)
-    uint32_t i1 = i0, tot = 0;
-    while (i1 < n && (i1 == i0 || tot + w[i1].nslot <= (uint32_t)kSlots)) tot += w[i1++].nslot;
-    uint32_t grp = 0, slot = 0, cum = 0;
-    bool mine = false;
-    for (uint32_t i = i0; i < i1; ++i) {
-      const uint32_t ns = w[i].nslot;
-      if ((uint32_t)lane >= cum && (uint32_t)lane < cum + ns) {
-        grp = w[i].grp;
-        slot = (uint32_t)lane - cum;
-        mine = true;
+  const uint32_t grp = wt.grp;
+  const bool mine = lane < (int)wt.nslot;
+  const uint32_t *cp = a.ctr + ((size_t)grp * kSlots + (lane & (kSlots - 1))) * kCtrStride;
+  const uint32_t need = mine ? a.grp_target[grp * kSlots + lane] * a.epoch : 0u;
+  Watchdog wd;
+  for (uint32_t it = 0;; ++it) {
+    bool ok = true;
+    if (mine) ok = (int32_t)(ld_cu(cp) - need) >= 0;
+    if (__all(ok)) return true;
+    if ((it & 63) == 63) {
+      if (lds_ld(L_ABORT)) return false;
+      if (ld_cu(&e.cp->status[0]) != 0) { lds_st(L_ABORT, 1); return false; }
+      if (wd.expired(e.cp->watchdog_ticks)) {
+        raise_error(e, 0xC0000000u | grp, qi);
+        return false;
       }
-      cum += ns;
     }
-    const uint32_t *cp = a.ctr + ((size_t)grp * kSlots + slot) * kCtrStride;
-    const uint32_t need = mine ? a.grp_target[grp * kSlots + slot] * a.epoch : 0u;
-    Watchdog wd;
-    for (uint32_t it = 0;; ++it) {
-      bool ok = true;
-      if (mine) ok = (int32_t)(ld_cu(cp) - need) >= 0;
-      if (__all(ok)) break;
-      if ((it & 63) == 63) {
-        if (lds_ld(L_ABORT)) return false;
-        if (ld_cu(&e.cp->status[0]) != 0) { lds_st(L_ABORT, 1); return false; }
-        if (wd.expired(e.cp->watchdog_ticks)) {
-          raise_error(e, 0xC0000000u | w[i0].grp, qi);
-          return false;
-        }
-      }
-      __builtin_amdgcn_s_sleep(MK_WSLEEP);
-    }
-    i0 = i1;
+    __builtin_amdgcn_s_sleep(MK_WSLEEP);
   }
-  return true;
 }
 
-// Input vector source of the RMSNorm'd instructions for sequence b: the
-// residual stream (fp32) or, at layer 0, the embedding row of the token.
+// Input vector source of the RMSNorm'd instructions.
 __device__ __forceinline__ void norm_src(const Env &e, const Args &a, const Instr &d, int b,
                                          const float *&h, const uint16_t *&emb, const uint16_t *&w) {
   const DevCtx &c = *e.cp;
@@ -507,30 +486,20 @@ __device__ __forceinline__ void norm_src(const Env &e, const Args &a, const Inst
   }
 }
 
-// Division of a flat index f < 2048 by a per-unit size n <= 512 without a
-// per-lane integer divide: q = (f * m) >> 20 with m = ceil(2^20 / n) is
-// exact there because f * (m * n - 2^20) < 2048 * 512 = 2^20.  m = 0 gives
-// q = 0 (batch 1, where every flat index belongs to sequence 0).
-__device__ __forceinline__ uint32_t div_magic(uint32_t n) { return ((1u << 20) + n - 1) / n; }
-__device__ __forceinline__ uint32_t qdiv(uint32_t f, uint32_t m) { return (f * m) >> 20; }
-
-// Position of sequence b (staged in LDS at kernel start).
-__device__ __forceinline__ int pos_of(int b) { return (int)lds_ld(L_POS + 4 * b); }
-
 __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
-  const int B = a.batch;
   // inputs are validated once per workgroup before anything depends on them
-  for (int b = 0; b < B; ++b) {
+  for (int b = 0; b < a.batch; ++b) {
     int32_t tk = a.tokens[b], ps = a.positions[b];
     if (tk < 0 || tk >= c.V) { raise_error(e, 0xE1000000u, (uint32_t)b); return; }
     if (ps < 0 || ps >= c.max_seq) { raise_error(e, 0xE2000000u, (uint32_t)b); return; }
   }
+  const int b = 0;
+  const int pos = a.positions[b];
   const size_t HB = (size_t)c.max_batch * c.H;
-  float *rsl = reinterpret_cast<float *>(smem + L_RS);  // per-sequence 1/rms of the current norm
-  float rs0 = 0.f;                                       // batch 1: the one 1/rms
   uint32_t seq = 0;
+  float rs = 0.f;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
     const uint32_t nx = is_gemv(d.op) ? d.nk : 1;
@@ -539,19 +508,18 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
 
     // Step-invariant inputs are fetched before the unit's dependency waits,
     // so that their round trips overlap the wait: the norm weights of the
-    // first activation piece, and for QKV the RoPE cos/sin of each
-    // sequence's position for the unit's pairs (staged in the upper half of
-    // its result slot, once the unit that used the slot before has finished
-    // its epilogue).
-    const float *h0 = nullptr;
-    const uint16_t *emb0 = nullptr, *nw = nullptr;
+    // first activation piece, and for QKV the RoPE cos/sin of position p
+    // for the unit's pairs (staged in the upper half of its result slot,
+    // once the unit that used the slot before has finished its epilogue).
+    const float *h = nullptr;
+    const uint16_t *emb = nullptr, *nw = nullptr;
     uint64_t *nwl = reinterpret_cast<uint64_t *>(smem + L_NW);  // norm weights, 4 per word
     auto stage_norm_weights = [&](uint32_t k0) {
       for (uint32_t i = (uint32_t)lane * 4; i < d.kc; i += 256)
         nwl[i >> 2] = *G(reinterpret_cast<const uint64_t *>(nw + k0 + i));
     };
     if (normed) {
-      norm_src(e, a, d, 0, h0, emb0, nw);
+      norm_src(e, a, d, b, h, emb, nw);
       stage_norm_weights(0);
     }
     if (d.op == OP_QKV) {
@@ -559,63 +527,62 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
           !spin_lds(e, [&]() { return lds_ld(L_EPI) + kAccSlots > qi; }, 0x500 | qi))
         return;
       const uint32_t half = (uint32_t)c.hd >> 1, ppg = (uint32_t)(c.G + 2) * half;
-      const uint32_t mi = B > 1 ? div_magic(d.n_items) : 0u;
-      for (uint32_t f = (uint32_t)lane; f < d.n_items * (uint32_t)B; f += 64) {
-        const uint32_t b = qdiv(f, mi), i = f - b * d.n_items;
+      for (uint32_t i = (uint32_t)lane; i < d.n_items; i += 64) {
         const uint32_t ii = ((d.item0 + i) % ppg) % half;
-        const int pos = (int)lds_ld_lane(L_POS + 4 * (int)b);
         const uint64_t cs = *G(reinterpret_cast<const uint64_t *>(c.rope + ((size_t)pos * half + ii) * 2));
-        accs[kAccFloats / 2 + 2 * f] = __uint_as_float((uint32_t)cs);
-        accs[kAccFloats / 2 + 2 * f + 1] = __uint_as_float((uint32_t)(cs >> 32));
+        accs[kAccFloats / 2 + 2 * i] = __uint_as_float((uint32_t)cs);
+        accs[kAccFloats / 2 + 2 * i + 1] = __uint_as_float((uint32_t)(cs >> 32));
       }
     }
 
     uint32_t wi = 0;
     if (lane == 0) trace_now(e, qi, 4);
-    const bool dma_pieces = (d.op == OP_DOWN || (d.op == OP_O && d.layer > 0)) && d.n_items * (uint32_t)B <= 64;
+    // O and DOWN units of at most 64 rows (but layer 0's O, whose residual
+    // is the bf16 embedding row): the activation pieces are plain fp32
+    // copies of attn / a and the residual rows copies of h, so they go to
+    // LDS by direct-to-LDS loads, two pieces in flight; the counter waits of
+    // piece k + 1 overlap the loads of piece k.  A piece is exactly 8
+    // wave-loads (1 KB each; lanes past the piece re-read its start), piece
+    // 0 one more for the residual rows, so `vmcnt` tells when the older of
+    // two pieces has landed.
+    const bool dma_pieces = (d.op == OP_DOWN || (d.op == OP_O && d.layer > 0)) && d.n_items <= 64;
     if (dma_pieces) {
-      // O and DOWN units (but layer 0's O, whose residual is the bf16
-      // embedding row): the activation pieces are plain fp32 copies of attn
-      // / a and the residual rows copies of h, so they go to LDS by
-      // direct-to-LDS loads, two pieces in flight, with every counter of the
-      // unit polled in one round trip first.  A piece is exactly 8 wave-loads
-      // (1 KB each, clamped lanes re-read the piece start), piece 0 one more
-      // for the residual rows, so `vmcnt` tells when the older one landed.
-      if (d.wait_n && !wait_groups(e, a, a.waits + d.wait_off, d.wait_n, qi)) return;
+      const uint32_t SB = d.op == OP_O ? (uint32_t)(c.nq * c.hd) : (uint32_t)c.F;
+      const float *src = (d.op == OP_O ? c.attn_buf : c.a_buf) + ((size_t)d.layer * c.max_batch + b) * SB;
+      const float *res = c.h_buf + (size_t)(d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1) * HB +
+                         (size_t)b * c.H + d.item0 + lane;
+      LDS_AS char *accl = (LDS_AS char *)smem + L_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4;
+      auto issue = [&](uint32_t k, uint32_t sq) {
+        if (k == 0 && lane < (int)d.n_items) __builtin_amdgcn_global_load_lds(res, (LDS_AS void *)accl, 4, 0, kSC1);
+        LDS_AS char *slot = (LDS_AS char *)smem + L_XS + (sq % kNXS) * kXSlotBytes;
+        const float *base = src + (size_t)k * d.kc;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t f = (uint32_t)(j * 256 + lane * 4);
+          __builtin_amdgcn_global_load_lds(base + (f < d.kc ? f : 0u), (LDS_AS void *)(slot + j * 1024), 16, 0, kSC1);
+        }
+      };
+      // piece 0's waits, then the pipeline (later pieces' waits inside it)
+      while (wi < d.wait_n) {
+        const Wait wt = a.waits[d.wait_off + wi];
+        if (wt.before_k > 0) break;
+        if (!wait_group(e, a, wt, qi)) return;
+        ++wi;
+      }
       if (lane == 0) {
         trace_put(e, qi, 0, (uint64_t)d.op | ((uint64_t)d.layer << 8) | ((uint64_t)d.unit << 24));
         trace_now(e, qi, 1);
       }
-      const uint32_t SB = d.op == OP_O ? (uint32_t)(c.nq * c.hd) : (uint32_t)c.F;
-      const float *src = (d.op == OP_O ? c.attn_buf : c.a_buf) + (size_t)d.layer * c.max_batch * SB;
-      const uint32_t nflat = d.kc * (uint32_t)B;
-      const uint32_t mk = B > 1 ? div_magic(d.kc) : 0u;
-      uint32_t off[8];  // element offsets of this lane's 16 bytes in each wave-load
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t f = (uint32_t)(j * 256 + lane * 4);
-        const uint32_t b = qdiv(f, mk), i = f - b * d.kc;
-        off[j] = f < nflat ? b * SB + i : 0u;
-      }
-      const uint32_t nres = d.n_items * (uint32_t)B;
-      const uint32_t mi = B > 1 ? div_magic(d.n_items) : 0u;
-      const uint32_t rb = qdiv((uint32_t)lane, mi), rr = (uint32_t)lane - rb * d.n_items;
-      const float *res = c.h_buf + (size_t)(d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1) * HB +
-                         (size_t)rb * c.H + d.item0 + rr;
-      auto issue = [&](uint32_t k, uint32_t sq) {
-        if (k == 0 && lane < (int)nres)
-          __builtin_amdgcn_global_load_lds(res, (LDS_AS void *)((LDS_AS char *)smem + L_ACC +
-                                                                (qi & (kAccSlots - 1)) * kAccFloats * 4),
-                                           4, 0, kSC1);
-        LDS_AS char *slot = (LDS_AS char *)smem + L_XS + (sq % kNXS) * kXSlotBytes;
-        const float *base = src + (size_t)k * d.kc;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          __builtin_amdgcn_global_load_lds(base + off[j], (LDS_AS void *)(slot + j * 1024), 16, 0, kSC1);
-      };
+      int64_t t_first = 0, t_last = 0;  // trace words 5 and 7, stored after the loop
       uint32_t issued = 0, done = 0;
       while (done < nx) {
         if (issued < nx && issued - done < (uint32_t)kNXS) {
+          while (wi < d.wait_n) {
+            const Wait wt = a.waits[d.wait_off + wi];
+            if (wt.before_k > issued) break;
+            if (!wait_group(e, a, wt, qi)) { wait_vm0(); return; }
+            ++wi;
+          }
           const uint32_t sq = seq + issued;
           if (sq >= (uint32_t)kNXS) {
             const uint32_t need = sq - kNXS + 1;
@@ -630,26 +597,30 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
           }
           issue(issued, sq);
           ++issued;
-          continue;
+        } else {
+          if (issued - done >= 2) wait_vm_n<8>();
+          else wait_vm0();
+          if (lane == 0) lds_st(L_XREADY, seq + done + 1);
+          wake();
+          if (done == 0) t_first = now();
+          if (done + 1 == nx) t_last = now();
+          ++done;
         }
-        if (issued - done >= 2) wait_vm_n<8>();
-        else wait_vm0();
-        if (lane == 0) lds_st(L_XREADY, seq + done + 1);
-        wake();
-        if (lane == 0 && done == 0) trace_now(e, qi, 5);
-        if (lane == 0 && done + 1 == nx) trace_now(e, qi, 7);
-        ++done;
+      }
+      if (lane == 0) {
+        trace_put(e, qi, 5, (uint64_t)t_first);
+        trace_put(e, qi, 7, (uint64_t)t_last);
       }
       seq += nx;
     }
     // (a `continue` above instead of this test makes the compiler spill)
     if (!dma_pieces)
     for (uint32_t k = 0; k < nx; ++k, ++seq) {
-      {
-        uint32_t wn = wi;
-        while (wn < d.wait_n && a.waits[d.wait_off + wn].before_k <= k) ++wn;
-        if (wn > wi && !wait_groups(e, a, a.waits + d.wait_off + wi, wn - wi, qi)) return;
-        wi = wn;
+      while (wi < d.wait_n) {
+        const Wait wt = a.waits[d.wait_off + wi];
+        if (wt.before_k > k) break;
+        if (!wait_group(e, a, wt, qi)) return;
+        ++wi;
       }
       if (seq >= (uint32_t)kNXS) {
         const uint32_t need = seq - kNXS + 1;
@@ -662,18 +633,15 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
         };
         if (!spin_lds(e, freed, 0x100 | qi)) return;
       }
-      // activation piece layout: [sequence][kc] fp32 (kc * batch <= 2048)
       float *xs = reinterpret_cast<float *>(smem + L_XS + (seq % kNXS) * kXSlotBytes);
-      const uint32_t nflat = d.kc * (uint32_t)B;
-      const uint32_t mk = B > 1 ? div_magic(d.kc) : 0u;  // batched pieces: kc <= 256
       if (k == 0 && lane == 0) {
         trace_put(e, qi, 0, (uint64_t)d.op | ((uint64_t)d.layer << 8) | ((uint64_t)d.unit << 24));
         trace_now(e, qi, 1);
       }
       if (normed) {
-        // one batch of up to 2048 elements (8 x 4 per lane) of one sequence
-        auto load_batch = [&](const float *h, const uint16_t *emb, uint32_t e0, f4 (&v)[8]) {
-          const rsrc_t hr = rsrc(h ? (const void *)h : (const void *)emb);
+        const rsrc_t hr = rsrc(h ? (const void *)h : (const void *)emb);
+        // one batch of up to 2048 elements (8 x 4 per lane) in flight
+        auto load_batch = [&](uint32_t e0, f4 (&v)[8]) {
 #pragma unroll
           for (int m = 0; m < 8; ++m) {
             const uint32_t i = e0 + (uint32_t)(lane + 64 * m) * 4;
@@ -692,110 +660,72 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
         };
         f4 hv[8];
         if (k == 0) {
-          // 1/rms of every sequence's full vector (batch 1: kept in rs0)
-          for (int b = 0; b < B; ++b) {
-            const float *h = h0;
-            const uint16_t *emb = emb0;
-            if (b > 0) {
-              const uint16_t *w_unused;
-              norm_src(e, a, d, b, h, emb, w_unused);
-            }
-            float ss = 0.f;
-            for (uint32_t e0 = 0; e0 < (uint32_t)c.H; e0 += 2048) {
-              load_batch(h, emb, e0, hv);
+          float ss = 0.f;
+          for (uint32_t e0 = 0; e0 < (uint32_t)c.H; e0 += 2048) {
+            load_batch(e0, hv);
 #pragma unroll
-              for (int m = 0; m < 8; ++m)
-                ss += hv[m].x * hv[m].x + hv[m].y * hv[m].y + hv[m].z * hv[m].z + hv[m].w * hv[m].w;
-            }
-            ss = wave_sum(ss);
-            const float r = 1.0f / sqrtf(ss / (float)c.H + c.eps);
-            if (b == 0) rs0 = r;
-            if (B > 1 && lane == 0) rsl[b] = r;
+            for (int m = 0; m < 8; ++m) ss += hv[m].x * hv[m].x + hv[m].y * hv[m].y + hv[m].z * hv[m].z + hv[m].w * hv[m].w;
           }
-          if (B > 1) wait_lgkm0();
+          ss = wave_sum(ss);
+          rs = 1.0f / sqrtf(ss / (float)c.H + c.eps);
         }
+        // pieces hold at most 2048 elements; the last batch loaded is still
+        // in hv when H <= 2048 (then nk == 1)
         const uint32_t k0 = k * d.kc;
+        if (c.H > 2048 || k0 != 0) load_batch(k0, hv);
         if (k > 0) stage_norm_weights(k0);
-        // the piece: element f of the flat [sequence][kc] layout; the last
-        // batch loaded is still in hv when batch 1 and H <= 2048 (nk == 1)
-        if (B > 1 || c.H > 2048 || k0 != 0) {
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const uint32_t f = (uint32_t)(lane + 64 * m) * 4;
-            hv[m] = f4{0.f, 0.f, 0.f, 0.f};
-            if (f < nflat) {
-              // sequence b's vector starts c.H elements after sequence b-1's
-              // (one uniform buffer base, per-lane offsets)
-              const uint32_t b = qdiv(f, mk), i = f - b * d.kc;
-              if (emb0) {
-                const uint16_t *eb = c.embed + (size_t)a.tokens[b] * c.H;
-                const uint64_t uu = *G(reinterpret_cast<const uint64_t *>(eb + k0 + i));
-                hv[m] = f4{bf_lo((uint32_t)uu), bf_hi((uint32_t)uu), bf_lo((uint32_t)(uu >> 32)),
-                           bf_hi((uint32_t)(uu >> 32))};
-              } else {
-                hv[m] = ldc4(rsrc(h0), (b * (uint32_t)c.H + k0 + i) * 4);
-              }
-            }
-          }
-        }
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          const uint32_t f = (uint32_t)(lane + 64 * m) * 4;
-          if (f < nflat) {
-            const uint32_t b = qdiv(f, mk), i = f - b * d.kc;
-            const float rs = B == 1 ? rs0 : rsl[b];
+          const uint32_t i = (uint32_t)(lane + 64 * m) * 4;
+          if (i < d.kc) {
             const f4 v = hv[m];
             const uint64_t w4 = nwl[i >> 2];
             const uint32_t w0 = (uint32_t)w4, w1 = (uint32_t)(w4 >> 32);
             f4 o = {v.x * rs * bf_lo(w0), v.y * rs * bf_hi(w0), v.z * rs * bf_lo(w1), v.w * rs * bf_hi(w1)};
-            *reinterpret_cast<f4 *>(xs + f) = o;
+            *reinterpret_cast<f4 *>(xs + i) = o;
           }
         }
       } else if (d.op == OP_O || d.op == OP_DOWN) {
         // the activation piece and (first piece) the unit's residual rows,
         // loaded together: one round trip
-        const uint32_t SB = d.op == OP_O ? (uint32_t)(c.nq * c.hd) : (uint32_t)c.F;
-        const float *src = (d.op == OP_O ? c.attn_buf : c.a_buf) + (size_t)d.layer * c.max_batch * SB;
-        const rsrc_t sr = rsrc(src + (size_t)k * d.kc);
+        const float *src = d.op == OP_O
+                               ? c.attn_buf + ((size_t)d.layer * c.max_batch + b) * (c.nq * c.hd)
+                               : c.a_buf + ((size_t)d.layer * c.max_batch + b) * c.F;
+        const rsrc_t sr = rsrc(src + k * d.kc);
         f4 v[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          const uint32_t f = (uint32_t)(lane + 64 * m) * 4;
-          if (f < nflat) {
-            const uint32_t b = qdiv(f, mk), i = f - b * d.kc;
-            v[m] = ldc4(sr, (b * SB + i) * 4);
-          }
+          const uint32_t i = (uint32_t)(lane + 64 * m) * 4;
+          if (i < d.kc) v[m] = ldc4(sr, i * 4);
         }
         if (k == 0) {
-          // residual rows: flat [sequence][n_items] (n_items * batch <= 512)
-          const uint32_t nres = d.n_items * (uint32_t)B;
-          const uint32_t mi = B > 1 ? div_magic(d.n_items) : 0u;
           float rv[kAccFloats / 64];
-          const int idx = d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1;
-          const bool from_embed = d.op == OP_O && d.layer == 0;
-          const rsrc_t rr = rsrc(c.h_buf + (size_t)idx * HB + d.item0);
+          if (d.op == OP_O && d.layer == 0) {
+            const GAS uint16_t *er = G(c.embed) + (size_t)a.tokens[b] * c.H + d.item0;
 #pragma unroll
-          for (int m = 0; m < kAccFloats / 64; ++m) {
-            const uint32_t f = (uint32_t)(lane + 64 * m);
-            rv[m] = 0.f;
-            if (f < nres) {
-              const uint32_t b = qdiv(f, mi), r = f - b * d.n_items;
-              if (from_embed)
-                rv[m] = bf16f(G(c.embed)[(size_t)a.tokens[b] * c.H + d.item0 + r]);
-              else
-                rv[m] = ldc1(rr, (b * (uint32_t)c.H + r) * 4);
+            for (int m = 0; m < kAccFloats / 64; ++m) {
+              const uint32_t r = (uint32_t)(lane + 64 * m);
+              rv[m] = r < d.n_items ? bf16f(er[r]) : 0.f;
+            }
+          } else {
+            const int idx = d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1;
+            const rsrc_t rr = rsrc(c.h_buf + (size_t)idx * HB + (size_t)b * c.H + d.item0);
+#pragma unroll
+            for (int m = 0; m < kAccFloats / 64; ++m) {
+              const uint32_t r = (uint32_t)(lane + 64 * m);
+              rv[m] = r < d.n_items ? ldc1(rr, r * 4) : 0.f;
             }
           }
 #pragma unroll
           for (int m = 0; m < kAccFloats / 64; ++m) {
-            const uint32_t f = (uint32_t)(lane + 64 * m);
-            if (f < nres) accs[f] = rv[m];
+            const uint32_t r = (uint32_t)(lane + 64 * m);
+            if (r < d.n_items) accs[r] = rv[m];
           }
         }
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          const uint32_t f = (uint32_t)(lane + 64 * m) * 4;
-          if (f < nflat) *reinterpret_cast<f4 *>(xs + f) = v[m];
+          const uint32_t i = (uint32_t)(lane + 64 * m) * 4;
+          if (i < d.kc) *reinterpret_cast<f4 *>(xs + i) = v[m];
         }
       }
       wait_lgkm0();
@@ -866,79 +796,25 @@ __device__ __forceinline__ void load_x(const float *xs, uint32_t n16, float (&xr
   }
 }
 
-// Batched pieces (batch 2..8, at most 256 elements = 32 groups of 8):
-// lanes l and l + 32 read the same 16-byte weight group l & 31 and lane
-// half hf = l >> 5 serves sequences 4*hf .. 4*hf + 3.
-__device__ __forceinline__ void load_xb(const float *xs, uint32_t kc, int B, float (&xr)[32]) {
-  const int lane = lane_id();
-  const uint32_t g = (uint32_t)lane & 31u;
-  const int hb = (lane >> 5) * 4;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int b = hb + j;
-    if (b < B && g * 8 < kc) {
-      const f4 p = *reinterpret_cast<const f4 *>(xs + (size_t)b * kc + g * 8);
-      const f4 q = *reinterpret_cast<const f4 *>(xs + (size_t)b * kc + g * 8 + 4);
-      xr[8 * j + 0] = p.x; xr[8 * j + 1] = p.y; xr[8 * j + 2] = p.z; xr[8 * j + 3] = p.w;
-      xr[8 * j + 4] = q.x; xr[8 * j + 5] = q.y; xr[8 * j + 6] = q.z; xr[8 * j + 7] = q.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xr[8 * j + i] = 0.f;
-    }
-  }
-}
-
-// Sum over the 32 lanes of each half wave: lane 31 ends with the sum of
-// lanes 0..31, lane 63 with the sum of lanes 32..63.
-__device__ __forceinline__ float half_wave_sum(float v) {
-  v += dpp0<0xb1, 0xf>(v);    // quad_perm [1,0,3,2]
-  v += dpp0<0x4e, 0xf>(v);    // quad_perm [2,3,0,1]
-  v += dpp0<0x124, 0xf>(v);   // row_ror:4
-  v += dpp0<0x128, 0xf>(v);   // row_ror:8
-  v += dpp0<0x142, 0xa>(v);   // row_bcast:15 into rows 1, 3
-  return v;
-}
-
-__device__ __forceinline__ void dot_piece_b(const char *piece, const float (&xr)[32], uint32_t n16, float (&s)[4]) {
-  const int lane = lane_id();
-  const uint32_t g = (uint32_t)lane & 31u;
-  const uint32_t addr = (uint32_t)(uintptr_t)((LDS_AS const char *)piece) + g * 16;
-  u4 w;
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(w) : "v"(addr));
-  if (g >= n16) w = u4{0u, 0u, 0u, 0u};
-  const float wf[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y), bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fmaf(wf[i], xr[8 * j + i], acc);
-    s[j] = half_wave_sum(acc);
-  }
-}
-
 __device__ __forceinline__ size_t kv_off(const DevCtx &c, int l, int t, int b, int g, int s) {
   return ((((size_t)l * 2 + t) * c.max_batch + b) * c.nkv + g) * (size_t)c.max_seq * c.hd + (size_t)s * c.hd;
 }
 
 // Epilogue of a finished GEMV instruction, run by its last compute wave
-// over the staged row results R (LDS): row i*ipw + s of the unit for
-// sequence b is R[b * rows + i*ipw + s].  Lanes take (sequence, item)
-// pairs; the outputs of 64 of them go out in one vector store.
+// over the staged row results R (LDS): row i*ipw + s of the unit.  The
+// outputs of 64 rows go out in one vector store.
 //   QKV : RoPE on q/k pairs (i, i + hd/2), q -> fp32 scratch, k/v -> bf16
 //         cache slot p;   O, DOWN: R already holds residual + dot;
 //   FFN : a = silu(gate) * up;   LM: logits.
 __device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const Instr &d, const float *R) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
+  const int b = 0;
   const size_t HB = (size_t)c.max_batch * c.H;
-  const uint32_t rows = d.n_items * d.ipw;
-  const uint32_t mi = a.batch > 1 ? div_magic(d.n_items) : 0u;
-  for (uint32_t f = (uint32_t)lane; f < d.n_items * (uint32_t)a.batch; f += 64) {
-    const uint32_t b = qdiv(f, mi), i = f - b * d.n_items;
-    const float *Rb = R + b * rows;
+  for (uint32_t i = (uint32_t)lane; i < d.n_items; i += 64) {
     switch (d.op) {
       case OP_QKV: {
-        const float v0 = Rb[2 * i], v1 = Rb[2 * i + 1];
+        const float v0 = R[2 * i], v1 = R[2 * i + 1];
         const uint32_t half = (uint32_t)c.hd >> 1;
         const uint32_t ppg = (uint32_t)(c.G + 2) * half;
         const uint32_t pp = d.item0 + i;
@@ -946,7 +822,7 @@ __device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const
         const uint32_t rr = pp - g * ppg;
         const uint32_t hs = rr / half;
         const uint32_t ii = rr - hs * half;
-        const int p = (int)lds_ld_lane(L_POS + 4 * (int)b);
+        const int p = e.pos0;
         if (hs <= (uint32_t)c.G && c.qk_norm) {
           // per-head q/k RMSNorm needs the whole head, which spans several
           // units: q and k leave raw (un-normed, un-rotated) and the
@@ -957,7 +833,7 @@ __device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const
           st_tag(dst + ii, v0, a.tag);
           st_tag(dst + ii + half, v1, a.tag);
         } else if (hs <= (uint32_t)c.G) {
-          const float cs = R[kAccFloats / 2 + 2 * f], sn = R[kAccFloats / 2 + 2 * f + 1];
+          const float cs = R[kAccFloats / 2 + 2 * i], sn = R[kAccFloats / 2 + 2 * i + 1];
           const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
           if (hs < (uint32_t)c.G) {
             uint64_t *q = c.q_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + (g * c.G + hs)) * c.hd;
@@ -984,18 +860,18 @@ __device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const
         break;
       }
       case OP_O:
-        st_c(c.h_buf + (size_t)(2 * d.layer + 1) * HB + (size_t)b * c.H + d.item0 + i, Rb[i]);
+        st_c(c.h_buf + (size_t)(2 * d.layer + 1) * HB + (size_t)b * c.H + d.item0 + i, R[i]);
         break;
       case OP_FFN: {
-        const float gt = Rb[2 * i], up = Rb[2 * i + 1];
+        const float gt = R[2 * i], up = R[2 * i + 1];
         st_c(c.a_buf + ((size_t)d.layer * c.max_batch + b) * c.F + d.item0 + i, gt / (1.0f + expf(-gt)) * up);
         break;
       }
       case OP_DOWN:
-        st_c(c.h_buf + (size_t)(2 * d.layer + 2) * HB + (size_t)b * c.H + d.item0 + i, Rb[i]);
+        st_c(c.h_buf + (size_t)(2 * d.layer + 2) * HB + (size_t)b * c.H + d.item0 + i, R[i]);
         break;
       default:  // OP_LM
-        G(a.logits)[(size_t)b * c.V + d.item0 + i] = Rb[i];
+        G(a.logits)[(size_t)b * c.V + d.item0 + i] = R[i];
         break;
     }
   }
@@ -1011,7 +887,7 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Ga
   const int b = (int)d.b, g = (int)d.aux0, s = (int)d.aux1;
   const int j = g * c.G + h;
   constexpr int hd = 64 * DPL, PF = 20 / DPL;  // prefetch depth (register budget)
-  const int p = pos_of(b);
+  const int p = e.pos0;
   const int lo = s * a.split_len;
   const int hi = min(lo + a.split_len, p + 1);
   const int nt0 = max(0, min(hi - lo, PF));
@@ -1280,8 +1156,7 @@ __device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw
       const uint32_t r0 = (uint32_t)cw;
       const bool has_resid = d.op == OP_O || d.op == OP_DOWN;  // acc preloaded
       uint32_t rel = n, wpg = 0xffffffffu;
-      const int B = a.batch;
-      float xr[32];  // batch 1: this lane's x groups; batched: 4 sequences x 8
+      float xr[32];
       for (uint32_t k = 0; k < d.nk; ++k) {
         if (k > 0) {
           if (lane == 0) lds_st(L_XCONS + 4 * cw, seq + k);
@@ -1289,9 +1164,7 @@ __device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw
         }
         if (r0 >= per) continue;
         if (!spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq + k; }, 0x400 | qi)) return;
-        const float *xs = reinterpret_cast<const float *>(smem + L_XS + ((seq + k) % kNXS) * kXSlotBytes);
-        if (B == 1) load_x(xs, n16, xr);
-        else load_xb(xs, d.kc, B, xr);
+        load_x(reinterpret_cast<const float *>(smem + L_XS + ((seq + k) % kNXS) * kXSlotBytes), n16, xr);
         const uint32_t t = k * per + r0;
         uint32_t pi = t / ppp, o = t - pi * ppp;
         for (uint32_t r = r0; r < per;) {
@@ -1305,24 +1178,9 @@ __device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw
             if (!spin_lds_fast(e, [&]() { return lds_ld(L_SENT + (pg % P) * kSentBytes) == pg; }, 0x300 | qi)) return;
             wpg = pg;
           }
-          const char *piece = smem + L_RING + (pg % P) * kPageBytes + o * d.pb;
-          if (B == 1) {
-            float v = dot_piece(piece, xr, n16);
-            if (k > 0 || has_resid) v = acc[r] + v;  // k order fixed: deterministic
-            if (lane == 0) acc[r] = v;
-          } else {
-            float sb[4];
-            dot_piece_b(piece, xr, n16, sb);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int bl = (lane >> 5) * 4 + j;
-              if ((lane & 31) == 31 && bl < B) {
-                float v = sb[j];
-                if (k > 0 || has_resid) v = acc[bl * per + r] + v;
-                acc[bl * per + r] = v;
-              }
-            }
-          }
+          float v = dot_piece(smem + L_RING + (pg % P) * kPageBytes + o * d.pb, xr, n16);
+          if (k > 0 || has_resid) v = acc[r] + v;  // k order fixed: deterministic
+          if (lane == 0) acc[r] = v;
           r += kNCW;
           o += kNCW;
           while (o >= ppp) {
@@ -1399,18 +1257,12 @@ mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const
   e.q = a.instr + q0;
   e.nq = q1 - q0;
   e.trace = a.trace ? a.trace + 4 + (size_t)e.cu * a.trace_stride * kTraceWords : nullptr;
-  // control words zeroed; the sequences' positions staged.  An out-of-range
-  // position is staged as 0 so that every cache access stays in bounds; the
-  // sync wave reports it as an input error and the step is abandoned.
-  if (threadIdx.x < 64) {
-    const int pw = (int)threadIdx.x - L_POS / 4;
-    int32_t p = 0;
-    if (pw >= 0 && pw < a.batch && pw < kMaxBatch) {
-      p = a.positions[pw];
-      if (p < 0 || p >= e.cp->max_seq) p = 0;
-    }
-    lds_u32(threadIdx.x * 4) = (uint32_t)p;
-  }
+  // an out-of-range position is replaced by 0 so that every cache access
+  // stays in bounds; the sync wave reports it as an input error and the
+  // step is abandoned
+  e.pos0 = a.positions[0];
+  if (e.pos0 < 0 || e.pos0 >= e.cp->max_seq) e.pos0 = 0;
+  if (threadIdx.x < 64) lds_u32(threadIdx.x * 4) = 0;  // control words
   // no page has landed: sentinels hold an index no page has
   for (int i = (int)threadIdx.x; i < kRingPages * kSentBytes / 4; i += kThreads)
     lds_u32(L_SENT + 4 * i) = 0xffffffffu;

@@ -119,9 +119,7 @@ constexpr int L_XREADY = 128;   // u32      activation pieces produced
 constexpr int L_DONE = 132;     // u32[4]   waves finished, per unit slot
 constexpr int L_ABORT = 148;    // u32      nonzero: every wave exits
 constexpr int L_EPI = 152;      // u32      units whose epilogue has finished
-constexpr int L_POS = 160;      // i32[8]   positions of the sequences (kernel start)
-constexpr int L_RS = 192;       // f32[8]   per-sequence 1/rms of the current norm
-constexpr int kMaxBatch = 8;
+constexpr int kMaxBatch = 8;    // sequences per step the plans are built for
 constexpr int L_ACC = 256;      // fp32 row results, kAccSlots x kAccFloats
 constexpr int L_XS = L_ACC + kAccSlots * kAccFloats * 4;  // activation ring
 constexpr int L_RING = ((L_XS + kNXS * kXSlotBytes + 1023) / 1024) * 1024;
