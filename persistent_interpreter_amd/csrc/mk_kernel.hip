@@ -203,6 +203,7 @@ __device__ __forceinline__ int64_t now() { return (int64_t)wall_clock64(); }
 //   [4] sync wave: started the instruction (before its waits)
 //   [5] sync wave: first activation piece published
 //   [6] last compute wave: its own pieces done, epilogue starting
+//   [7] sync wave: last activation piece published
 constexpr int kTraceWords = 8;
 __device__ __forceinline__ void trace_put(const Env &e, uint32_t qi, int word, uint64_t v) {
   if (e.trace) G(e.trace)[(size_t)qi * kTraceWords + word] = v;
