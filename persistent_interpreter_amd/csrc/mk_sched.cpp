@@ -188,8 +188,7 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
   std::vector<int> g_down_prev(1, -1);
   int g_down = -1;
   for (int l = 0; l < L; ++l) {
-    std::vector<int> g_qkv(nkv), g_attn((size_t)B * nkv), g_ffn(chunks);
-    for (auto &g : g_qkv) g = bd.group();
+    std::vector<int> g_attn((size_t)B * nkv), g_ffn(chunks);
     for (auto &g : g_attn) g = bd.group();
     const int g_red = bd.group(), g_o = bd.group();
     for (auto &g : g_ffn) g = bd.group();
@@ -209,12 +208,8 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
         if (l > 0) un.reads.push_back({R_HOUT, (uint16_t)(l - 1), (uint32_t)b, 0, (uint32_t)H, 0});
         un.writes.push_back({R_QKV, (uint16_t)l, (uint32_t)b, p0, p1, 0});
       }
-      int gfirst = (int)(p0 / PPG), glast = (int)((p1 - 1) / PPG);
-      if (glast - gfirst > 1) {
-        err = "internal: a QKV unit spans more than two KV heads";
-        return MK_ERR_UNSUPPORTED;
-      }
-      for (int g = gfirst; g <= glast; ++g) un.sigs.push_back(g_qkv[g]);
+      // no counter: q and this step's K/V slot are tagged words that the
+      // attention units read until every word carries the step's tag
       bd.add(std::move(un));
     }
     // I2: attention partials per (sequence, KV head, split).
@@ -228,8 +223,7 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
           un.in.aux0 = (uint32_t)g;
           un.in.aux1 = (uint32_t)s;
           un.cu = (int)(a % C);
-          un.waits.push_back({(uint32_t)g_qkv[g], 0});
-          un.reads.push_back({R_QKV, (uint16_t)l, (uint32_t)b, g * PPG, (g + 1) * PPG, 0});
+          un.reads.push_back({R_QKV, (uint16_t)l, (uint32_t)b, g * PPG, (g + 1) * PPG, 0, 1});
           un.writes.push_back({R_PART, (uint16_t)l, (uint32_t)b, (uint32_t)(g * n_split + s),
                                (uint32_t)(g * n_split + s + 1), 0});
           un.sigs.push_back(g_attn[b * nkv + g]);
@@ -454,9 +448,12 @@ int check_plan(const mk_config &cfg, Plan &P, int sim_runs, int corrupt, uint64_
     if (corrupt == 1 && victim >= 0) sig[victim].clear();
     if (corrupt == 2 && victim >= 0) target[sig[victim][0]] -= 1;
     if (corrupt == 3) {
+      // a wait nothing else implies: reduction and gate/up units wait on
+      // exactly the producers of what they read (other units' waits may be
+      // implied through a chain, and dropping those is harmless)
       std::vector<int> w;
       for (size_t u = 0; u < NU; ++u)
-        if (!waits[u].empty()) w.push_back((int)u);
+        if (!waits[u].empty() && (P.instr[u].op == OP_RED || P.instr[u].op == OP_FFN)) w.push_back((int)u);
       if (!w.empty()) {
         int u = w[rng() % w.size()];
         waits[u].erase(waits[u].begin() + (rng() % waits[u].size()));
@@ -501,7 +498,8 @@ int check_plan(const mk_config &cfg, Plan &P, int sim_runs, int corrupt, uint64_
   for (size_t u = 0; u < NU; ++u)
     for (auto &w : P.writes[u]) wl.push_back({key_of(w), {w.lo, (int)u}});
   std::sort(wl.begin(), wl.end());
-  std::vector<std::vector<std::pair<uint32_t, std::vector<int>>>> rw(NU);  // per unit: (phase, writers)
+  // per unit: (phase, writers) of counter-guarded reads and of tagged reads
+  std::vector<std::vector<std::pair<uint32_t, std::vector<int>>>> rw(NU), rt(NU);
   for (size_t u = 0; u < NU; ++u)
     for (auto &r : P.reads[u]) {
       std::vector<int> ws;
@@ -522,7 +520,7 @@ int check_plan(const mk_config &cfg, Plan &P, int sim_runs, int corrupt, uint64_
       for (auto &p : iv)
         if (p.first <= cov) cov = std::max(cov, p.second);
       if (cov < r.hi) fail("a read has elements no unit writes");
-      rw[u].push_back({r.phase, std::move(ws)});
+      (r.tagged ? rt : rw)[u].push_back({r.phase, std::move(ws)});
     }
 
   // Phases of each unit: sorted distinct before_k values (always 0).
@@ -555,6 +553,11 @@ int check_plan(const mk_config &cfg, Plan &P, int sim_runs, int corrupt, uint64_
         bool ok = true;
         for (auto &w : waits[u])
           if (w.before_k == phase && count[w.grp] < target[w.grp]) { ok = false; break; }
+        // a tagged read spins until its writers' words are there
+        for (auto &rp : rt[u])
+          if (ok && rp.first == phase)
+            for (int wu : rp.second)
+              if (!done[wu]) { ok = false; break; }
         if (ok) ready.push_back(cu);
       }
       if (ready.empty()) {

@@ -28,6 +28,10 @@ struct Access {
   uint32_t b;
   uint32_t lo, hi;
   uint32_t phase;  // activation piece before which the read happens (reads)
+  // reads only: the data is tagged with its step and the reader re-reads
+  // until every word carries this step's tag, so no counter guards it (the
+  // reader waits for its writers by itself)
+  uint8_t tagged;
 };
 
 struct Plan {
