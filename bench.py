@@ -6,9 +6,11 @@ head_dim 64, SwiGLU 8192, vocab 128256, tied embeddings, RoPE theta 5e5) at
 batch 1 with 512 prior KV positions, greedy decoding.  Weights and the KV
 cache are seeded synthetic bf16 tensors (persistent_interpreter_amd.synth).
 
-A step is one ``mk_decode_step`` launch (the whole forward pass in one
-persistent kernel) followed by the harness's greedy argmax and position
-increment, all on one stream.  ``value`` is tokens/s over the K timed steps
+A step is one ``mk_decode_step_greedy`` launch: the whole forward pass and
+the greedy next token and position in one persistent kernel, which writes
+them over its own token and position buffers, so the timed steps chain on
+the device with no other kernel or host round trip in between.  ``value``
+is tokens/s over the K timed steps
 (inputs resident in HBM).  ``roofline`` prices the megakernel against
 MI355X's 8 TB/s: algorithmic bytes per launch (every weight byte once, the
 embedding row, K and V of slots 0..p) over its average duration measured
@@ -182,16 +184,22 @@ def main():
         if i and i % mc.steps == 0:
             sess.positions.copy_(start_pos)
         ev[i][0].record(stream)
-        rc = sess.step()
+        rc = sess.step_greedy()
         ev[i][1].record(stream)
         if rc != 0:
-            raise RuntimeError(f"mk_decode_step failed: {rc}")
-        sess.advance_greedy()
+            raise RuntimeError(f"mk_decode_step_greedy failed: {rc}")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     st = sess.mk.sync_status()
     if st != 0:
         raise RuntimeError(f"device error {st}")
+    # the device-chained run must feed the same tokens as the checked run
+    # (the kernel is deterministic: same schedule, same reduction order)
+    if K <= n_check:
+        end_tok = int(sess.tokens.cpu()[0])
+        want = int(np.argmax(gpu_logits[K - 1][0]))
+        if end_tok != want:
+            raise RuntimeError(f"in-kernel greedy chain diverged: {end_tok} != {want}")
     kern = np.array([a.elapsed_time(b) * 1e-3 for a, b in ev])   # seconds
 
     positions = [np.asarray(pos) + (i % mc.steps) for i in range(K)]
@@ -210,7 +218,7 @@ def main():
         "config": {"workload": f"{mc.name}: {mc.n_layers} layers, hidden {mc.hidden}, "
                                f"{mc.n_q_heads}/{mc.n_kv_heads} heads x {mc.head_dim}, "
                                f"FFN {mc.ffn_dim}, vocab {mc.vocab}, batch {mc.batch}, "
-                               f"{mc.prior} prior KV positions, greedy",
+                               f"{mc.prior} prior KV positions, greedy (in-kernel argmax)",
                    "batch": mc.batch, "prior_positions": mc.prior, "accumulate": "fp32",
                    "parallelism": "1 GPU, 1 persistent launch per step"},
         "kernel_us": {"mean": round(t_kern * 1e6, 2),

@@ -114,6 +114,28 @@ int mk_decode_step(mk_handle *h, int32_t batch, const int32_t *tokens,
                    const int32_t *positions, void *kv_cache, float *logits,
                    void *stream);
 
+/* mk_decode_step_greedy -- mk_decode_step plus the greedy next token,
+ * computed in the same launch after the LM head: every LM unit reduces its
+ * rows to one candidate and the last unit to finish reduces the candidates,
+ * so no further kernel or host round trip is needed.  The pages' path ends
+ * with the LM head (chapter "L'interpréteur sur GPU", table of section 3.2);
+ * picking the greedy token is not described there and is taken as the
+ * plainest step after it.
+ *   next_tokens    : device int32 [batch]: index of the largest logit of row
+ *                    b (the lowest index among equal logits; a NaN ranks
+ *                    above every number), computed from the fp32 logits
+ *                    this step writes.
+ *   next_positions : device int32 [batch]: positions[b] + 1.
+ * Both may be the same buffers as tokens and positions: every read of the
+ * inputs in the launch comes before these writes, so a caller can chain
+ * steps on the device with one pair of buffers.  Other arguments and errors
+ * as mk_decode_step (MK_ERR_INVALID_ARG also for a null output).  The
+ * outputs are unspecified after a device error. */
+int mk_decode_step_greedy(mk_handle *h, int32_t batch, const int32_t *tokens,
+                          const int32_t *positions, void *kv_cache,
+                          float *logits, int32_t *next_tokens,
+                          int32_t *next_positions, void *stream);
+
 /* mk_sync_status -- synchronise the device and return the first device-side
  * error of the steps since the last call (MK_OK if none).  After an error
  * the library re-zeroes its counters so the next step starts clean; a
@@ -176,7 +198,8 @@ int mk_plan_check(const mk_config *cfg, int32_t batch, int32_t num_cus,
  * it has completed.  Returns MK_ERR_INVALID_ARG for an unknown id. */
 int mk_get_buffer(mk_handle *h, int32_t which, void **ptr, size_t *bytes);
 
-/* mk_version -- ABI version of this header (major*100 + minor). */
+/* mk_version -- ABI version of this header (major*100 + minor): 101 adds
+ * mk_decode_step_greedy. */
 int mk_version(void);
 
 #ifdef __cplusplus

@@ -28,8 +28,9 @@ MK_FLAG_TRACE = 1
 
 MK_BUF_H, MK_BUF_Q, MK_BUF_ATTN, MK_BUF_A, MK_BUF_TRACE = 1, 2, 3, 4, 5
 
-EXPORTED = ("mk_create", "mk_decode_step", "mk_sync_status", "mk_destroy",
-            "mk_strerror", "mk_plan_check", "mk_get_buffer", "mk_version")
+EXPORTED = ("mk_create", "mk_decode_step", "mk_decode_step_greedy",
+            "mk_sync_status", "mk_destroy", "mk_strerror", "mk_plan_check",
+            "mk_get_buffer", "mk_version")
 
 
 class MkConfig(C.Structure):
@@ -84,6 +85,10 @@ def lib():
                                      C.c_void_p, C.c_void_p, C.c_void_p,
                                      C.c_void_p]
         L.mk_decode_step.restype = C.c_int
+        L.mk_decode_step_greedy.argtypes = [C.c_void_p, C.c_int32, C.c_void_p,
+                                            C.c_void_p, C.c_void_p, C.c_void_p,
+                                            C.c_void_p, C.c_void_p, C.c_void_p]
+        L.mk_decode_step_greedy.restype = C.c_int
         L.mk_sync_status.argtypes = [C.c_void_p]
         L.mk_sync_status.restype = C.c_int
         L.mk_destroy.argtypes = [C.c_void_p]
@@ -168,6 +173,19 @@ class Megakernel:
             stream = torch.cuda.current_stream().cuda_stream
         return lib().mk_decode_step(self.h, batch, _ptr(tokens), _ptr(positions),
                                     _ptr(kv), _ptr(logits), stream)
+
+    def decode_step_greedy(self, batch: int, tokens, positions, kv, logits,
+                           next_tokens, next_positions,
+                           stream: Optional[int] = None) -> int:
+        """Enqueue one decode step that also writes the greedy next token and
+        position (device int32 [batch] each; they may be `tokens` and
+        `positions` themselves); returns the synchronous status."""
+        if stream is None:
+            import torch
+            stream = torch.cuda.current_stream().cuda_stream
+        return lib().mk_decode_step_greedy(self.h, batch, _ptr(tokens), _ptr(positions),
+                                           _ptr(kv), _ptr(logits), _ptr(next_tokens),
+                                           _ptr(next_positions), stream)
 
     def sync_status(self) -> int:
         return lib().mk_sync_status(self.h)

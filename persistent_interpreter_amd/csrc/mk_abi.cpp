@@ -34,9 +34,13 @@ struct DevPlan {
   float *d_part = nullptr;
   uint32_t *d_iota = nullptr;
   uint64_t *d_trace = nullptr;
+  uint64_t *d_amax = nullptr;  // greedy candidates, one per LM unit
   size_t ctr_bytes = 0, trace_bytes = 0;
+  size_t amax_word = 0;        // index in d_ctr of the greedy arrival counter
   uint32_t trace_stride = 0;
   uint32_t epoch = 0;
+  uint32_t n_lm = 0;
+  uint32_t greedy_epoch = 0;   // greedy steps since the counters were zeroed
 };
 
 template <class T>
@@ -68,6 +72,7 @@ void free_plan(DevPlan &p) {
   hipFree(p.d_part);
   hipFree(p.d_iota);
   hipFree(p.d_trace);
+  hipFree(p.d_amax);
 }
 
 int check_config(const mk_config *c, std::string &err) {
@@ -112,7 +117,7 @@ struct mk_handle {
 
 extern "C" {
 
-int mk_version(void) { return 100; }
+int mk_version(void) { return 101; }
 
 const char *mk_strerror(int code) {
   switch (code) {
@@ -278,7 +283,10 @@ static int get_plan(mk_handle *h, int batch, DevPlan **out) {
   if (rc) return rc;
   resolve_streams(h->cfg, h->w, dp->plan);
   Plan &P = dp->plan;
-  dp->ctr_bytes = (size_t)P.n_groups * kSlots * kCtrStride * 4;
+  // the counter groups, then one padded word: the greedy arrival counter
+  dp->amax_word = (size_t)P.n_groups * kSlots * kCtrStride;
+  dp->ctr_bytes = (dp->amax_word + kCtrStride) * 4;
+  for (const Instr &in : P.instr) dp->n_lm += in.op == OP_LM ? 1u : 0u;
   const size_t part = (size_t)h->cfg.n_layers * h->cfg.max_batch * h->cfg.n_q_heads * P.n_split *
                       (h->cfg.head_dim + 4) * 4;
   // page sentinels: iota[i] = i for every page index of the longest queue
@@ -294,7 +302,8 @@ static int get_plan(mk_handle *h, int batch, DevPlan **out) {
       (rc = upload(&dp->d_iota, iota)) ||
       (rc = upload(&dp->d_waits, P.waits)) || (rc = upload(&dp->d_rowtab, P.rowtab)) ||
       (rc = upload(&dp->d_target, P.grp_target)) || (rc = dev_alloc(&dp->d_ctr, dp->ctr_bytes)) ||
-      (rc = dev_alloc(&dp->d_part, part))) {
+      (rc = dev_alloc(&dp->d_part, part)) ||
+      (rc = dev_alloc(&dp->d_amax, (size_t)dp->n_lm * h->cfg.max_batch * 8))) {
     free_plan(*dp);
     return rc;
   }
@@ -323,8 +332,9 @@ static int get_plan(mk_handle *h, int batch, DevPlan **out) {
   return MK_OK;
 }
 
-int mk_decode_step(mk_handle *h, int32_t batch, const int32_t *tokens, const int32_t *positions, void *kv_cache,
-                   float *logits, void *stream) {
+static int launch_step(mk_handle *h, int32_t batch, const int32_t *tokens, const int32_t *positions,
+                       void *kv_cache, float *logits, int32_t *next_tokens, int32_t *next_positions,
+                       void *stream) {
   if (!h || !tokens || !positions || !kv_cache || !logits) return MK_ERR_INVALID_ARG;
   if (batch < 1 || batch > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
   // Several sequences per step are switched off: a four-step run at batch 8
@@ -359,8 +369,30 @@ int mk_decode_step(mk_handle *h, int32_t batch, const int32_t *tokens, const int
   a.batch = batch;
   a.n_split = dp->plan.n_split;
   a.split_len = dp->plan.split_len;
+  a.amax = dp->d_amax;
+  a.amax_ctr = dp->d_ctr + dp->amax_word;
+  a.next_tok = next_tokens;
+  a.next_pos = next_positions;
+  a.n_lm = dp->n_lm;
+  a.amax_target = 0;
+  if (next_tokens) {
+    dp->greedy_epoch += 1;
+    a.amax_target = dp->greedy_epoch * dp->n_lm;
+  }
   if (kernel_launch(a, h->num_cus, (hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
   return MK_OK;
+}
+
+int mk_decode_step(mk_handle *h, int32_t batch, const int32_t *tokens, const int32_t *positions, void *kv_cache,
+                   float *logits, void *stream) {
+  return launch_step(h, batch, tokens, positions, kv_cache, logits, nullptr, nullptr, stream);
+}
+
+int mk_decode_step_greedy(mk_handle *h, int32_t batch, const int32_t *tokens, const int32_t *positions,
+                          void *kv_cache, float *logits, int32_t *next_tokens, int32_t *next_positions,
+                          void *stream) {
+  if (!next_tokens || !next_positions) return MK_ERR_INVALID_ARG;
+  return launch_step(h, batch, tokens, positions, kv_cache, logits, next_tokens, next_positions, stream);
 }
 
 int mk_sync_status(mk_handle *h) {
@@ -374,6 +406,7 @@ int mk_sync_status(mk_handle *h) {
   for (auto &kv : h->plans) {
     hipMemset(kv.second->d_ctr, 0, kv.second->ctr_bytes);
     kv.second->epoch = 0;
+    kv.second->greedy_epoch = 0;
   }
   hipDeviceSynchronize();
   const uint32_t top = st[0] >> 24;

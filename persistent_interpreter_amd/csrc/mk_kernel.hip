@@ -807,6 +807,27 @@ __device__ __forceinline__ size_t kv_off(const DevCtx &c, int l, int t, int b, i
 //   QKV : RoPE on q/k pairs (i, i + hd/2), q -> fp32 scratch, k/v -> bf16
 //         cache slot p;   O, DOWN: R already holds residual + dot;
 //   FFN : a = silu(gate) * up;   LM: logits.
+// Greedy order of (logit, vocabulary index) pairs: larger logit first, the
+// lower index among equal logits; a NaN ranks above every number (the
+// first NaN wins), as in the usual argmax of a float array.
+__device__ __forceinline__ bool amax_better(float v, uint32_t i, float bv, uint32_t bi) {
+  const bool vn = v != v, bn = bv != bv;
+  if (vn || bn) return vn && (!bn || i < bi);
+  return v > bv || (v == bv && i < bi);
+}
+// Butterfly over the 64 lanes: every lane ends with the wave's best pair.
+__device__ __forceinline__ void amax_reduce(float &bv, uint32_t &bi) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const uint32_t oi = (uint32_t)__shfl_xor((int)bi, off);
+    if (amax_better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+}
+
 __device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const Instr &d, const float *R) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
@@ -875,6 +896,50 @@ __device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const
         G(a.logits)[(size_t)b * c.V + d.item0 + i] = R[i];
         break;
     }
+  }
+  if (d.op == OP_LM && a.next_tok) {
+    // this unit's greedy candidate; each lane visits its rows in ascending
+    // order, so strict comparisons keep the lowest index among equals
+    float bv = -INFINITY;
+    uint32_t bi = 0xffffffffu;
+    for (uint32_t i = (uint32_t)lane; i < d.n_items; i += 64) {
+      const float v = R[i];
+      if (amax_better(v, d.item0 + i, bv, bi)) {
+        bv = v;
+        bi = d.item0 + i;
+      }
+    }
+    amax_reduce(bv, bi);
+    if (lane == 0) st_tag(a.amax + d.unit, bv, bi);
+  }
+}
+
+// The last LM unit of the step to count itself picks the greedy token from
+// every unit's candidate (each acknowledged before its unit counted) and
+// writes it with the next position.
+__device__ __forceinline__ void lm_greedy_finish(const Env &e, const Args &a) {
+  const int lane = lane_id();
+  uint32_t o = 0;
+  if (lane == 0)
+    o = __hip_atomic_fetch_add(G(a.amax_ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  o = __builtin_amdgcn_readfirstlane(o);
+  if (o + 1u != a.amax_target) return;
+  const rsrc_t r = rsrc(a.amax);
+  float bv = -INFINITY;
+  uint32_t bi = 0xffffffffu;
+  for (uint32_t u = (uint32_t)lane; u < a.n_lm; u += 64) {
+    const uint64_t w = ldt(r, u);
+    const float v = tval(w);
+    const uint32_t i = (uint32_t)(w >> 32);
+    if (amax_better(v, i, bv, bi)) {
+      bv = v;
+      bi = i;
+    }
+  }
+  amax_reduce(bv, bi);
+  if (lane == 0) {
+    G(a.next_tok)[0] = (int32_t)bi;
+    G(a.next_pos)[0] = e.pos0 + 1;
   }
 }
 
@@ -1223,6 +1288,7 @@ __device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw
         unit_epilogue(e, a, d, acc);
         if (d.op != OP_QKV) wait_vm0();
       }
+      if (d.op == OP_LM && a.next_tok) lm_greedy_finish(e, a);
       if (lane == 0) {
         trace_now(e, qi, 3);
         lds_st(L_DONE + 4 * (qi & 3), 0);
@@ -1248,9 +1314,11 @@ mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const
           float *__restrict__ part_buf, const uint32_t *__restrict__ iota, const int32_t *__restrict__ tokens,
           const int32_t *__restrict__ positions, uint16_t *__restrict__ kv, float *__restrict__ logits,
           uint64_t *__restrict__ trace, uint32_t trace_stride, uint32_t epoch, uint32_t tag, int32_t batch, int32_t n_split,
-          int32_t split_len) {
+          int32_t split_len, uint64_t *__restrict__ amax, uint32_t *__restrict__ amax_ctr, int32_t *__restrict__ next_tok,
+          int32_t *__restrict__ next_pos, uint32_t n_lm, uint32_t amax_target) {
   const Args a{ctx, instr, q_off, waits, rowtab, ctr, grp_target, part_buf, iota, tokens, positions, kv, logits,
-               trace, trace_stride, epoch, tag, batch, n_split, split_len};
+               trace, trace_stride, epoch, tag, batch, n_split, split_len, amax, amax_ctr, next_tok, next_pos,
+               n_lm, amax_target};
   Env e;
   e.cp = a.ctx;
   e.cu = (int)blockIdx.x;
@@ -1297,7 +1365,8 @@ hipError_t kernel_launch(const Args &a0, int grid, hipStream_t stream) {
   Args a = a0;
   void *params[] = {&a.ctx, &a.instr, &a.q_off, &a.waits, &a.rowtab, &a.ctr, &a.grp_target, &a.part_buf, &a.iota,
                     &a.tokens, &a.positions, &a.kv, &a.logits, &a.trace, &a.trace_stride, &a.epoch, &a.tag,
-                    &a.batch, &a.n_split, &a.split_len};
+                    &a.batch, &a.n_split, &a.split_len, &a.amax, &a.amax_ctr, &a.next_tok, &a.next_pos,
+                    &a.n_lm, &a.amax_target};
   return hipLaunchCooperativeKernel((const void *)mk_interp, dim3(grid), dim3(kThreads), params, kLdsBytes,
                                     stream);
 }

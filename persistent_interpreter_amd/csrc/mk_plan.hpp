@@ -157,6 +157,16 @@ struct Args {
   uint32_t tag;               // this step's activation tag (handle-wide, never 0)
   int32_t batch;
   int32_t n_split, split_len;
+  // greedy next token (next_tok null: off).  Each LM unit stores its
+  // candidate (largest logit of its rows, lowest index among equals) as one
+  // 64-bit word, logit bits | index << 32, and counts itself on amax_ctr;
+  // the unit that brings the counter to amax_target reduces the candidates.
+  uint64_t *amax;             // [n_lm]
+  uint32_t *amax_ctr;         // one counter word, zeroed with the others
+  int32_t *next_tok;          // [batch]: argmax of the step's logits
+  int32_t *next_pos;          // [batch]: positions + 1
+  uint32_t n_lm;              // LM units in the plan
+  uint32_t amax_target;       // counter value once this step's LM units are in
 };
 
 }  // namespace mk

@@ -2,8 +2,11 @@
 GPU, own the step buffers, and drive greedy decoding through the C ABI.
 
 Nothing here computes any part of the decode step: the step itself is one
-``mk_decode_step`` launch; the greedy choice of the next token (an argmax
-over the logits the kernel wrote) and ``position + 1`` are harness work.
+``mk_decode_step`` launch.  The greedy choice of the next token (an argmax
+over the logits the kernel wrote) and ``position + 1`` are harness work in
+``advance_greedy``, or kernel work in ``step_greedy``
+(``mk_decode_step_greedy``), which writes them over the step's own token and
+position buffers so that steps chain on the device.
 """
 from __future__ import annotations
 
@@ -55,6 +58,12 @@ class Session:
 
     def step(self) -> int:
         return self.mk.decode_step(self.batch, self.tokens, self.positions, self.kv, self.logits)
+
+    def step_greedy(self) -> int:
+        """One step that also replaces the tokens and positions with the
+        greedy next token and position (in the same launch)."""
+        return self.mk.decode_step_greedy(self.batch, self.tokens, self.positions, self.kv,
+                                          self.logits, self.tokens, self.positions)
 
     def step_checked(self):
         rc = self.step()

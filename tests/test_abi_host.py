@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert B.lib().mk_version() == 100
+    assert B.lib().mk_version() == 101
     for code in (0, -1, -2, -3, -4, -5, -6, -10, -11, -12, -99):
         assert len(B.strerror(code)) > 0
 
@@ -51,6 +51,8 @@ def test_null_arguments_rejected_without_gpu():
     assert L.mk_create(C.byref(cfg), None, C.byref(out)) == B.MK_ERR_INVALID_ARG
     assert L.mk_create(C.byref(cfg), None, None) == B.MK_ERR_INVALID_ARG
     assert L.mk_decode_step(None, 1, None, None, None, None, None) == B.MK_ERR_INVALID_ARG
+    assert L.mk_decode_step_greedy(None, 1, None, None, None, None, None, None,
+                                   None) == B.MK_ERR_INVALID_ARG
     assert L.mk_sync_status(None) == B.MK_ERR_INVALID_ARG
     L.mk_destroy(None)  # NULL-safe
 
