@@ -14,7 +14,10 @@ is tokens/s over the K timed steps
 (inputs resident in HBM).  ``roofline`` prices the megakernel against
 MI355X's 8 TB/s: algorithmic bytes per launch (every weight byte once, the
 embedding row, K and V of slots 0..p) over its average duration measured
-with HIP events on the launch stream.  ``cpu_baseline`` times the CPU oracle
+with HIP events on the launch stream.  ``stream_read`` is the chip's
+achievable streaming-read rate (``mk_stream_read`` over 2 GiB), the
+practical ceiling of a step that reads every weight once, and the step's
+share of it.  ``cpu_baseline`` times the CPU oracle
 on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 32] [--warmup 3]
@@ -128,6 +131,37 @@ def cpu_baseline(mc, W, kv0, tok, pos, fed, gpu_logits, budget_s=20.0):
             {"max_abs_dlogit": worst, "greedy_match": f"{match}/{n}"})
 
 
+STREAM_BYTES = 2 << 30
+
+
+def stream_read_gbs(torch, stream, launches: int = 10) -> float:
+    """The chip's achievable streaming-read rate (mk_stream_read over a
+    2 GiB buffer, HIP events on the launch stream, mean of `launches`)."""
+    import ctypes
+    from persistent_interpreter_amd import binding as B
+    L = B.lib()
+    buf = torch.empty(STREAM_BYTES, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(L.mk_stream_read_sink_words(), dtype=torch.int32, device="cuda")
+    h = stream.cuda_stream
+
+    def run():
+        rc = L.mk_stream_read(ctypes.c_void_p(buf.data_ptr()), STREAM_BYTES,
+                              ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(h))
+        if rc != 0:
+            raise RuntimeError(f"mk_stream_read failed: {rc}")
+
+    run()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(launches):
+        run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) * 1e-3 / launches
+    del buf, sink
+    return STREAM_BYTES / t / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,6 +236,8 @@ def main():
             raise RuntimeError(f"in-kernel greedy chain diverged: {end_tok} != {want}")
     kern = np.array([a.elapsed_time(b) * 1e-3 for a, b in ev])   # seconds
 
+    stream_gbs = stream_read_gbs(torch, stream)
+
     positions = [np.asarray(pos) + (i % mc.steps) for i in range(K)]
     bytes_per = float(np.mean([algorithmic_bytes(mc, p) for p in positions]))
     t_kern = float(np.mean(kern))
@@ -226,6 +262,9 @@ def main():
                       "p10": round(float(np.percentile(kern, 10)) * 1e6, 2),
                       "p90": round(float(np.percentile(kern, 90)) * 1e6, 2)},
         "hbm_pct_of_peak": round(100 * achieved / PEAK_HBM_GBS, 2),
+        "stream_read": {"gbs": round(stream_gbs, 1), "bytes": STREAM_BYTES,
+                        "pct_of_peak": round(100 * stream_gbs / PEAK_HBM_GBS, 2),
+                        "step_pct_of_stream": round(100 * achieved / stream_gbs, 2)},
         "overhead": round(overhead(t_kern, bytes_per / (PEAK_HBM_GBS * 1e9)), 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -198,8 +198,20 @@ int mk_plan_check(const mk_config *cfg, int32_t batch, int32_t num_cus,
  * it has completed.  Returns MK_ERR_INVALID_ARG for an unknown id. */
 int mk_get_buffer(mk_handle *h, int32_t which, void **ptr, size_t *bytes);
 
+/* mk_stream_read -- diagnostic: read `bytes` of device memory at `buf` once
+ * with 128-bit nontemporal loads from every CU (4096 workgroups), folding
+ * what each thread read into one word of `sink` so the loads cannot be
+ * dropped.  The time it takes gives the chip's achievable streaming-read
+ * rate, the practical ceiling of a step that reads every weight once.
+ *   buf  : device, 16-byte aligned; bytes a nonzero multiple of 16.
+ *   sink : device uint32 [mk_stream_read_sink_words()], overwritten.
+ * Asynchronous on `stream` (hipStream_t, NULL = the null stream).
+ * Errors: MK_ERR_INVALID_ARG, MK_ERR_HIP. */
+int mk_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+size_t mk_stream_read_sink_words(void);
+
 /* mk_version -- ABI version of this header (major*100 + minor): 101 adds
- * mk_decode_step_greedy. */
+ * mk_decode_step_greedy, 102 mk_stream_read. */
 int mk_version(void);
 
 #ifdef __cplusplus

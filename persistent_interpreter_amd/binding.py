@@ -30,7 +30,8 @@ MK_BUF_H, MK_BUF_Q, MK_BUF_ATTN, MK_BUF_A, MK_BUF_TRACE = 1, 2, 3, 4, 5
 
 EXPORTED = ("mk_create", "mk_decode_step", "mk_decode_step_greedy",
             "mk_sync_status", "mk_destroy", "mk_strerror", "mk_plan_check",
-            "mk_get_buffer", "mk_version")
+            "mk_get_buffer", "mk_version", "mk_stream_read",
+            "mk_stream_read_sink_words")
 
 
 class MkConfig(C.Structure):
@@ -89,6 +90,10 @@ def lib():
                                             C.c_void_p, C.c_void_p, C.c_void_p,
                                             C.c_void_p, C.c_void_p, C.c_void_p]
         L.mk_decode_step_greedy.restype = C.c_int
+        L.mk_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
+        L.mk_stream_read.restype = C.c_int
+        L.mk_stream_read_sink_words.argtypes = []
+        L.mk_stream_read_sink_words.restype = C.c_size_t
         L.mk_sync_status.argtypes = [C.c_void_p]
         L.mk_sync_status.restype = C.c_int
         L.mk_destroy.argtypes = [C.c_void_p]

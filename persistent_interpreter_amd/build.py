@@ -44,10 +44,10 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     dflags = [f"-D{d}" for d in defines]
     objs = []
     stem = os.path.splitext(os.path.basename(out))[0]
-    k_obj = os.path.join(out_dir, f"{stem}_kernel.o")
-    _run([HIPCC, *DEVICE_FLAGS, *dflags, "-c", os.path.join(CSRC, "mk_kernel.hip"),
-          "-o", k_obj])
-    objs.append(k_obj)
+    for src in ("mk_kernel.hip", "mk_probe.hip"):
+        o = os.path.join(out_dir, f"{stem}_" + src.replace(".hip", ".o"))
+        _run([HIPCC, *DEVICE_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", o])
+        objs.append(o)
     for src in ("mk_sched.cpp", "mk_abi.cpp"):
         o = os.path.join(out_dir, f"{stem}_" + src.replace(".cpp", ".o"))
         _run(["g++", *HOST_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", o])

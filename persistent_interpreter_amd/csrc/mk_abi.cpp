@@ -117,7 +117,7 @@ struct mk_handle {
 
 extern "C" {
 
-int mk_version(void) { return 101; }
+int mk_version(void) { return 102; }
 
 const char *mk_strerror(int code) {
   switch (code) {

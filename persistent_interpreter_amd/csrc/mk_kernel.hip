@@ -92,6 +92,13 @@ __device__ __forceinline__ uint32_t ld_cu(const uint32_t *p) {
 // in flight.  Ordering against counters/flags is explicit (waitcnt, LDS
 // flags, compiler barriers around the waits).
 constexpr int kSC1 = 16;  // cache-policy bits: sc1
+// The weight stream is read once per step: nontemporal loads keep it from
+// displacing the activations, partials and counters in the caches (3 % per
+// step on the Llama-1B shape).
+#ifndef MK_WPOL
+#define MK_WPOL 2
+#endif
+constexpr int kWPol = MK_WPOL;  // cache-policy bits of the weight stream (2 = nt)
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t rsrc(const void *base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, 0x00020000);
@@ -405,18 +412,18 @@ __device__ __forceinline__ void loader_role(const Env &e, const Args &a, int lw)
           // the immediate offset moves both the global source and the LDS
           // destination, so four loads share one M0 and one address
           for (; sub + 4 <= lpp; sub += 4, src += 4096, dst += 4096) {
-            __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)dst, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)dst, 16, 1024, 0);
-            __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)dst, 16, 2048, 0);
-            __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)dst, 16, 3072, 0);
+            __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)dst, 16, 0, kWPol);
+            __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)dst, 16, 1024, kWPol);
+            __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)dst, 16, 2048, kWPol);
+            __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)dst, 16, 3072, kWPol);
           }
           for (; sub < lpp; ++sub, src += 1024, dst += 1024)
-            __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)dst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)dst, 16, 0, kWPol);
           j += lpp;
           if (++r == per) { r = 0; ++k; }
         }
         for (; j < 16; ++j)
-          __builtin_amdgcn_global_load_lds(first + lane * 16, (LDS_AS void *)(slot + j * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(first + lane * 16, (LDS_AS void *)(slot + j * 1024), 16, 0, kWPol);
       } else {
         const uint32_t sh = 31 - __builtin_clz(d.pb);  // pb is a power of two
 #pragma unroll
@@ -429,7 +436,7 @@ __device__ __forceinline__ void loader_role(const Env &e, const Args &a, int lw)
             const uint32_t kk = t / per;
             src = piece_addr(d, a.rowtab, kk, t - kk * per) + within;
           }
-          __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)(slot + j * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)(slot + j * 1024), 16, 0, kWPol);
         }
       }
       __builtin_amdgcn_global_load_lds(a.iota + n, (LDS_AS void *)(smem + L_SENT + (n % P) * kSentBytes), 4, 0, 0);
