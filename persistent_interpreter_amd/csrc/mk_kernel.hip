@@ -140,6 +140,9 @@ __device__ __forceinline__ void wake() { asm volatile("s_wakeup" ::: "memory"); 
 #ifndef MK_WSLEEP
 #define MK_WSLEEP 1  // counter polls: s_sleep units (64 clocks) between polls
 #endif
+#ifndef MK_FSLEEP
+#define MK_FSLEEP 4  // page-sentinel spins: s_sleep units between polls
+#endif
 // LDS-flag spins: s_sleep units between polls (measured on the Llama-1B
 // shape: 1, 2, 3, 4, 6, 10, 20 give 948, 944, 942, 940, 944, 952, 964 us)
 #ifndef MK_SLEEP
@@ -281,7 +284,7 @@ __device__ __forceinline__ bool spin_lds_fast(const Env &e, F cond, uint32_t inf
   if (cond()) return true;
   Watchdog wd;
   for (uint32_t it = 1;; ++it) {
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(MK_FSLEEP);
     if (cond()) return true;
     if ((it & 255) == 0) {
       if (lds_ld(L_ABORT)) return false;

@@ -40,7 +40,10 @@ constexpr int kCtrStride = 32;           // uint32 spacing of counters (128 B)
 // takes more than kAtomicsPerSlot increments per step: atomics on one
 // address serialise at the memory side (a few hundred ns each under load).
 constexpr int kSlots = 64;
-constexpr int kAtomicsPerSlot = 4;
+#ifndef MK_APS
+#define MK_APS 1
+#endif
+constexpr int kAtomicsPerSlot = MK_APS;
 constexpr int kMaxSplits = 64;
 
 // One queued instruction (96 bytes).  An instruction's weight stream is the

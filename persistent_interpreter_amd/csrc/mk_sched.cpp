@@ -70,9 +70,8 @@ struct Builder {
   // round-robin over the slots and give every wait its group's slot count.
   void assign_slots() {
     for (int g = 0; g < P.n_groups; ++g) {
-      uint32_t need = (P.grp_producers[g] + kAtomicsPerSlot - 1) / kAtomicsPerSlot, n = 1;
-      while (n < need && n < (uint32_t)kSlots) n <<= 1;
-      P.grp_nslot[g] = n;
+      const uint32_t need = (P.grp_producers[g] + kAtomicsPerSlot - 1) / kAtomicsPerSlot;
+      P.grp_nslot[g] = std::max(1u, std::min(need, (uint32_t)kSlots));
     }
     std::vector<uint32_t> next(P.n_groups, 0);
     for (Unit &u : units) {
