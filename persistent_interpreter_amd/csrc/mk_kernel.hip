@@ -140,6 +140,12 @@ __device__ __forceinline__ void wake() { asm volatile("s_wakeup" ::: "memory"); 
 #ifndef MK_WSLEEP
 #define MK_WSLEEP 1  // counter polls: s_sleep units (64 clocks) between polls
 #endif
+#ifndef MK_TSLEEP
+#define MK_TSLEEP 1  // tagged-word re-reads: s_sleep units between them
+#endif
+#ifndef MK_LSLEEP
+#define MK_LSLEEP 1  // loader waiting for a free ring slot: s_sleep units between checks
+#endif
 #ifndef MK_FSLEEP
 #define MK_FSLEEP 4  // page-sentinel spins: s_sleep units between polls
 #endif
@@ -310,7 +316,7 @@ __device__ __forceinline__ bool until_tagged(const Env &e, F load, uint32_t info
         return false;
       }
     }
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(MK_TSLEEP);
   }
 }
 
@@ -388,7 +394,7 @@ __device__ __forceinline__ void loader_role(const Env &e, const Args &a, int lw)
         const uint32_t need = n - P + 1;
         Watchdog wd;
         for (uint32_t it = 1;; ++it) {
-          __builtin_amdgcn_s_sleep(1);
+          __builtin_amdgcn_s_sleep(MK_LSLEEP);
           if (min_cons() >= need) break;
           if ((it & 63) == 0) {
             if (__builtin_amdgcn_readfirstlane(asm_lds_ld(L_ABORT))) { wait_vm0(); return; }

@@ -35,7 +35,10 @@ constexpr int kNXS = 2;                  // activation slots (double buffer)
 constexpr int kAccFloats = 512;          // LDS row results of one unit (rows*ipw)
 constexpr int kAccSlots = 4;             // units in flight per workgroup
 constexpr int kLdsBytes = 163840;        // gfx950: 160 KB per CU
-constexpr int kCtrStride = 32;           // uint32 spacing of counters (128 B)
+#ifndef MK_CSTRIDE
+#define MK_CSTRIDE 32
+#endif
+constexpr int kCtrStride = MK_CSTRIDE;   // uint32 spacing of counters (128 B)
 // A counter group is split over up to kSlots counters so that no counter
 // takes more than kAtomicsPerSlot increments per step: atomics on one
 // address serialise at the memory side (a few hundred ns each under load).
