@@ -17,6 +17,10 @@
 #include <cstring>
 #include <random>
 
+#ifndef MK_XCDMAP
+#define MK_XCDMAP 0  // 1: XCD-aware CU placement (measured neutral on the Llama-1B shape)
+#endif
+
 namespace mk {
 
 int choose_kc(int K, int kmax) {
@@ -317,7 +321,18 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
   bd.assign_slots();
   // Per-CU queues in creation order (= stage order).
   std::vector<std::vector<int>> per_cu(C);
-  for (size_t i = 0; i < bd.units.size(); ++i) per_cu[bd.units[i].cu].push_back((int)i);
+  // Workgroup w of a one-workgroup-per-CU launch runs on XCD w mod 8.  The
+  // units are placed on logical CUs in blocks (QKV group g, its attention
+  // splits and its reduction on logical CUs g*C/8 .. (g+1)*C/8 - 1); logical
+  // CU x runs as workgroup (x / (C/8)) + 8 * (x % (C/8)), so each such block
+  // shares one XCD and its L2.
+  auto phys = [&](int x) {
+#if MK_XCDMAP
+    if (C % 8 == 0) return (x / (C / 8)) + 8 * (x % (C / 8));
+#endif
+    return x;
+  };
+  for (size_t i = 0; i < bd.units.size(); ++i) per_cu[phys(bd.units[i].cu)].push_back((int)i);
   P.q_off.assign(C + 1, 0);
   std::vector<int64_t> cu_bytes(C, 0);
   for (int cu = 0; cu < C; ++cu) {
