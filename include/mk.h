@@ -45,6 +45,14 @@ extern "C" {
 
 /* ---- flags ------------------------------------------------------------- */
 #define MK_FLAG_TRACE    1u   /* record per-instruction timestamps           */
+/* Launch each step as a cooperative launch.  Every step needs one
+ * workgroup per CU resident at once (mk_create checks that one fits).  By
+ * default a step is a plain launch, which places all of them at once when
+ * nothing else runs on the device; with other work on the device set this
+ * flag, so that the launch waits until the whole grid fits (about 23 us
+ * more per step on MI355X).  A plain launch whose workgroups cannot all run
+ * ends in the watchdog: mk_sync_status reports MK_ERR_DEVICE_TIMEOUT. */
+#define MK_FLAG_COOPERATIVE 2u
 
 /* ---- model and schedule configuration ---------------------------------- */
 /* All sizes in elements.  The model is a pre-norm Llama-style decoder with

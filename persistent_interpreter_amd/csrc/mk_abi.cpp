@@ -16,7 +16,7 @@
 
 namespace mk {
 hipError_t kernel_setup(int *blocks_per_cu);
-hipError_t kernel_launch(const Args &a, int grid, hipStream_t stream);
+hipError_t kernel_launch(const Args &a, int grid, bool cooperative, hipStream_t stream);
 }  // namespace mk
 
 using namespace mk;
@@ -379,7 +379,8 @@ static int launch_step(mk_handle *h, int32_t batch, const int32_t *tokens, const
     dp->greedy_epoch += 1;
     a.amax_target = dp->greedy_epoch * dp->n_lm;
   }
-  if (kernel_launch(a, h->num_cus, (hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
+  if (kernel_launch(a, h->num_cus, (h->cfg.flags & MK_FLAG_COOPERATIVE) != 0, (hipStream_t)stream) != hipSuccess)
+    return MK_ERR_HIP;
   return MK_OK;
 }
 

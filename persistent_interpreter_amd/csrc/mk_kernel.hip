@@ -1379,14 +1379,19 @@ hipError_t kernel_setup(int *blocks_per_cu) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, mk_interp, kThreads, kLdsBytes);
 }
 
-hipError_t kernel_launch(const Args &a0, int grid, hipStream_t stream) {
+hipError_t kernel_launch(const Args &a0, int grid, bool cooperative, hipStream_t stream) {
   Args a = a0;
   void *params[] = {&a.ctx, &a.instr, &a.q_off, &a.waits, &a.rowtab, &a.ctr, &a.grp_target, &a.part_buf, &a.iota,
                     &a.tokens, &a.positions, &a.kv, &a.logits, &a.trace, &a.trace_stride, &a.epoch, &a.tag,
                     &a.batch, &a.n_split, &a.split_len, &a.amax, &a.amax_ctr, &a.next_tok, &a.next_pos,
                     &a.n_lm, &a.amax_target};
-  return hipLaunchCooperativeKernel((const void *)mk_interp, dim3(grid), dim3(kThreads), params, kLdsBytes,
-                                    stream);
+  // One workgroup per CU fits (checked at create); a plain launch places all
+  // of them at once on an otherwise idle device, a cooperative one also
+  // waits for room when other work holds CUs (about 23 us more per launch).
+  if (cooperative)
+    return hipLaunchCooperativeKernel((const void *)mk_interp, dim3(grid), dim3(kThreads), params, kLdsBytes,
+                                      stream);
+  return hipLaunchKernel((const void *)mk_interp, dim3(grid), dim3(kThreads), params, kLdsBytes, stream);
 }
 
 }  // namespace mk

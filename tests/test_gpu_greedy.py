@@ -105,3 +105,19 @@ def test_exact_tie_goes_to_the_lower_index():
     assert int(s.tokens.cpu()[0]) == low
     assert int(s.positions.cpu()[0]) == int(pos[0]) + 1
     s.close()
+
+
+def test_cooperative_launch_gives_the_same_steps():
+    """MK_FLAG_COOPERATIVE only changes how the grid is launched."""
+    mc = synth.CONFIGS["tiny"]
+    W = synth.make_weights(mc)
+    kv = synth.make_kv_cache(mc, filled=mc.prior)
+    tok, pos = synth.make_tokens(mc), synth.make_positions(mc)
+    runs = []
+    for flags in (0, B.MK_FLAG_COOPERATIVE):
+        print(f"case: tiny 4 greedy steps, flags {flags}", flush=True)
+        s = harness.Session(mc, W, kv.copy(), flags=flags)
+        runs.append(harness.greedy_run(s, tok, pos, 4))
+        s.close()
+    for a, b in zip(runs[0][1], runs[1][1]):
+        assert np.array_equal(a, b)
