@@ -14,10 +14,10 @@ plainest reading is the standard pre-norm Llama decoder, which this module
 spells out.  The megakernel is an exact reorganisation of that forward pass
 (index page "Partie 8", one-sentence definition: one persistent kernel runs
 the whole model, kernel boundaries become counters), and its split attention
-gives "the same mathematical result" as plain attention (GPU-kernels primer,
+is mathematically identical to plain attention (GPU-kernels primer,
 FlashAttention paragraph).  So the oracle is the plain definition.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
   * RMSNorm: x * w / sqrt(mean(x^2) + eps), eps inside the root, weight after.
   * RoPE: half-split pairs (i, i + hd/2), angle p * theta^(-2i/hd), evaluated
     in float64 and rounded to float32 (cos and sin tables).
@@ -28,8 +28,8 @@ Readings where the pages are silent (each one is listed in the design doc):
   * SiLU(z) = z / (1 + exp(-z)); no biases; logits in float32.
   * q/k norm (only for models that have it): per head over hd, after the
     projection and before RoPE.
-  * Everything else is carried in ``dt`` (float32 by default, the precision
-    the task fixes for this oracle; float64 for tighter pins).
+  * Everything else is carried in ``dt`` (float32 by default; float64 for
+    tighter pins).
 
 Pins (tests/test_oracle_*.py, all CPU): exhaustive bf16 decode/encode against
 torch's conversion; matvec against float64 brute force within the textbook
