@@ -102,8 +102,11 @@ typedef struct mk_handle mk_handle;
  *         MK_ERR_OOM, MK_ERR_HIP, MK_ERR_NOT_CORESIDENT. */
 int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out);
 
-/* mk_decode_step -- one decode step for sequences b < batch, as ONE kernel
- * launch on `stream` (asynchronous; the call returns after enqueueing).
+/* mk_decode_step -- one decode step for sequences b < batch on `stream`
+ * (asynchronous; the call returns after enqueueing).  Each sequence is one
+ * launch of the persistent kernel running the whole forward pass, the
+ * launches back to back on the stream (a batch of B streams the weights B
+ * times; sequences share no work yet).
  *   tokens    : device int32 [batch], the token fed at this step.
  *   positions : device int32 [batch], the KV slot of that token; slots
  *               0..positions[b]-1 must already hold the sequence's K/V.

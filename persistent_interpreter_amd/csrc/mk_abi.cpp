@@ -337,50 +337,55 @@ static int launch_step(mk_handle *h, int32_t batch, const int32_t *tokens, const
                        void *stream) {
   if (!h || !tokens || !positions || !kv_cache || !logits) return MK_ERR_INVALID_ARG;
   if (batch < 1 || batch > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
-  // Several sequences per step are switched off: a four-step run at batch 8
-  // faulted the GPU once (the same run had passed in a fresh process) and
-  // the cause is not found yet.  Batched plans are still built and checked
-  // on the host (mk_plan_check).
-  if (batch > 1) return MK_ERR_UNSUPPORTED;
+  // One launch of the one-sequence schedule per sequence, back to back on the
+  // stream.  Sequence s reads tokens[s] and positions[s], writes logits row
+  // s and its own cache slice: in the cache layout [L][2][max_batch][n_kv]
+  // [max_seq][head_dim] the slice of sequence s starts n_kv*max_seq*head_dim
+  // elements after that of sequence 0 in every (layer, K/V) block, so moving
+  // the base by that much addresses it with the one-sequence offsets.
   DevPlan *dp = nullptr;
-  int rc = get_plan(h, batch, &dp);
+  int rc = get_plan(h, 1, &dp);
   if (rc) return rc;
-  dp->epoch += 1;
-  Args a;
-  a.ctx = h->d_ctx;
-  a.instr = dp->d_instr;
-  a.q_off = dp->d_qoff;
-  a.waits = dp->d_waits;
-  a.rowtab = dp->d_rowtab;
-  a.ctr = dp->d_ctr;
-  a.grp_target = dp->d_target;
-  a.part_buf = dp->d_part;
-  a.iota = dp->d_iota;
-  a.tokens = tokens;
-  a.positions = positions;
-  a.kv = (uint16_t *)kv_cache;
-  a.logits = logits;
-  a.trace = dp->d_trace;
-  a.trace_stride = dp->trace_stride;
-  h->last_plan = dp;
-  a.epoch = dp->epoch;
-  h->tag = h->tag + 1 == 0 ? 1 : h->tag + 1;
-  a.tag = h->tag;
-  a.batch = batch;
-  a.n_split = dp->plan.n_split;
-  a.split_len = dp->plan.split_len;
-  a.amax = dp->d_amax;
-  a.amax_ctr = dp->d_ctr + dp->amax_word;
-  a.next_tok = next_tokens;
-  a.next_pos = next_positions;
-  a.n_lm = dp->n_lm;
-  a.amax_target = 0;
-  if (next_tokens) {
-    dp->greedy_epoch += 1;
-    a.amax_target = dp->greedy_epoch * dp->n_lm;
+  const size_t kv_seq = (size_t)h->cfg.n_kv_heads * h->cfg.max_seq * h->cfg.head_dim;
+  for (int32_t s = 0; s < batch; ++s) {
+    dp->epoch += 1;
+    Args a;
+    a.ctx = h->d_ctx;
+    a.instr = dp->d_instr;
+    a.q_off = dp->d_qoff;
+    a.waits = dp->d_waits;
+    a.rowtab = dp->d_rowtab;
+    a.ctr = dp->d_ctr;
+    a.grp_target = dp->d_target;
+    a.part_buf = dp->d_part;
+    a.iota = dp->d_iota;
+    a.tokens = tokens + s;
+    a.positions = positions + s;
+    a.kv = (uint16_t *)kv_cache + (size_t)s * kv_seq;
+    a.logits = logits + (size_t)s * h->cfg.vocab;
+    a.trace = dp->d_trace;
+    a.trace_stride = dp->trace_stride;
+    h->last_plan = dp;
+    a.epoch = dp->epoch;
+    h->tag = h->tag + 1 == 0 ? 1 : h->tag + 1;
+    a.tag = h->tag;
+    a.batch = 1;
+    a.n_split = dp->plan.n_split;
+    a.split_len = dp->plan.split_len;
+    a.amax = dp->d_amax;
+    a.amax_ctr = dp->d_ctr + dp->amax_word;
+    a.next_tok = next_tokens ? next_tokens + s : nullptr;
+    a.next_pos = next_positions ? next_positions + s : nullptr;
+    a.n_lm = dp->n_lm;
+    a.amax_target = 0;
+    if (next_tokens) {
+      dp->greedy_epoch += 1;
+      a.amax_target = dp->greedy_epoch * dp->n_lm;
+    }
+    if (kernel_launch(a, h->num_cus, (h->cfg.flags & MK_FLAG_COOPERATIVE) != 0, (hipStream_t)stream) !=
+        hipSuccess)
+      return MK_ERR_HIP;
   }
-  if (kernel_launch(a, h->num_cus, (h->cfg.flags & MK_FLAG_COOPERATIVE) != 0, (hipStream_t)stream) != hipSuccess)
-    return MK_ERR_HIP;
   return MK_OK;
 }
 

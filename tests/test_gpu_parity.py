@@ -126,12 +126,6 @@ def test_greedy_tokens_identical(name, steps):
 
 
 BATCHED = [("tiny", 3, 8), ("tiny", 8, 4), ("llama1b_b8", 8, 4)]
-BATCH_SKIP = pytest.mark.skip(reason="batched decode switched off: a 4-step batch-8 run faulted the "
-                                     "GPU once after passing in a fresh process; cause not found yet "
-                                     "(mk_decode_step returns MK_ERR_UNSUPPORTED for batch > 1)")
-
-
-@BATCH_SKIP
 @pytest.mark.parametrize("name,batch,steps", BATCHED)
 def test_batched_greedy_matches_oracle(name, batch, steps):
     """Several sequences per step, each at its own position: the logits of
