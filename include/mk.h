@@ -120,7 +120,7 @@ int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out);
  * The handle is not thread-safe.  Device-side errors (watchdog, bad token or
  * position) are reported by mk_sync_status after the stream is synchronised.
  * Errors returned here: MK_ERR_INVALID_ARG (null pointer, batch outside
- * [1, max_batch]), MK_ERR_UNSUPPORTED, MK_ERR_HIP, MK_ERR_OOM. */
+ * [1, max_batch]), MK_ERR_HIP, MK_ERR_OOM. */
 int mk_decode_step(mk_handle *h, int32_t batch, const int32_t *tokens,
                    const int32_t *positions, void *kv_cache, float *logits,
                    void *stream);
