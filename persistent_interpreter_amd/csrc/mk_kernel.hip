@@ -140,6 +140,9 @@ __device__ __forceinline__ void wake() { asm volatile("s_wakeup" ::: "memory"); 
 #ifndef MK_WSLEEP
 #define MK_WSLEEP 1  // counter polls: s_sleep units (64 clocks) between polls
 #endif
+#ifndef MK_ARB
+#define MK_ARB 16  // attention: K/V rows in flight per batch beyond the prefetched ones (head_dim 64)
+#endif
 #ifndef MK_TSLEEP
 #define MK_TSLEEP 1  // tagged-word re-reads: s_sleep units between them
 #endif
@@ -1087,23 +1090,24 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Ga
       }
       mrun = cm;
     }
-    // remaining positions in chunks of 64, 8 rows in flight
+    // remaining positions in chunks of 64, NR rows in flight
+    constexpr int NR = DPL == 1 ? MK_ARB : 8;
 #pragma unroll 1
     for (int c0 = lo + PF; c0 < hi; c0 += 64) {
       const int nt = min(64, hi - c0);
       float sc = -INFINITY;
 #pragma unroll 1
-      for (int t0 = 0; t0 < nt; t0 += 8) {
-        uint16_t k8[8][DPL];
+      for (int t0 = 0; t0 < nt; t0 += NR) {
+        uint16_t k8[NR][DPL];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < NR; ++t) {
           const int tt = min(t0 + t, nt - 1);
 #pragma unroll
           for (int m = 0; m < DPL; ++m)
             k8[t][m] = c0 + tt == p ? kp[m] : ldc16(Kr, (uint32_t)((c0 - lo + tt) * hd + lane + 64 * m) * 2);
         }
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < NR; ++t) {
           float pr = 0.f;
 #pragma unroll
           for (int m = 0; m < DPL; ++m) pr = fmaf(q[m], bf16f(k8[t][m]), pr);
@@ -1120,17 +1124,17 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Ga
 #pragma unroll
       for (int m = 0; m < DPL; ++m) o[m] *= scale;
 #pragma unroll 1
-      for (int t0 = 0; t0 < nt; t0 += 8) {
-        uint16_t v8[8][DPL];
+      for (int t0 = 0; t0 < nt; t0 += NR) {
+        uint16_t v8[NR][DPL];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < NR; ++t) {
           const int tt = min(t0 + t, nt - 1);  // in bounds; weight 0 beyond nt
 #pragma unroll
           for (int m = 0; m < DPL; ++m)
             v8[t][m] = c0 + tt == p ? vp[m] : ldc16(Vr, (uint32_t)((c0 - lo + tt) * hd + lane + 64 * m) * 2);
         }
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < NR; ++t) {
           const float wt = t0 + t < nt
                                ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pt), min(t0 + t, 63)))
                                : 0.f;
