@@ -12,7 +12,7 @@
 // Roles of the waves of a workgroup (the loader/compute/storer split of the
 // section 3.2 template, recast for CDNA4, which has no TMA and no warp
 // specialisation hardware):
-//   * 2 loader waves walk the queue's weight streams in order and copy them
+//   * 3 loader waves (kNLW) walk the queue's weight streams in order and copy them
 //     global -> LDS with direct-to-LDS 128-bit loads, several pages in
 //     flight, refilling a page as soon as every compute wave released it;
 //   * 1 sync wave walks the same queue, waits on each instruction's counter
