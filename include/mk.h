@@ -99,7 +99,10 @@ typedef struct mk_handle mk_handle;
  *             repacks or writes them.
  *   out     : receives the handle (NULL on error).
  * Errors: MK_ERR_INVALID_ARG, MK_ERR_UNSUPPORTED, MK_ERR_NO_DEVICE,
- *         MK_ERR_OOM, MK_ERR_HIP, MK_ERR_NOT_CORESIDENT. */
+ *         MK_ERR_OOM, MK_ERR_HIP, MK_ERR_NOT_CORESIDENT.  MK_ERR_UNSUPPORTED
+ *         also for qk_norm = 1 and for head_dim 128: those attention paths
+ *         are compiled but switched off (a multi-step run of them faulted
+ *         the GPU, cause not yet found); mk_plan_check still accepts them. */
 int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out);
 
 /* mk_decode_step -- one decode step for sequences b < batch on `stream`

@@ -182,10 +182,10 @@ int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out) {
       return MK_ERR_INVALID_ARG;
     if (cfg->qk_norm && (!ly.q_norm || !ly.k_norm)) return MK_ERR_INVALID_ARG;
   }
-  // Per-head q/k norm (head_dim 128, normed and rotated in the attention
-  // units) is switched off: its multi-step run faulted the GPU and the
-  // cause is not found yet.
-  if (cfg->qk_norm) return MK_ERR_UNSUPPORTED;
+  // Per-head q/k norm (normed and rotated in the attention units) and the
+  // head_dim 128 attention code it ran on are switched off: a multi-step
+  // run of them faulted the GPU and the cause is not found yet.
+  if (cfg->qk_norm || cfg->head_dim != 64) return MK_ERR_UNSUPPORTED;
 
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return MK_ERR_NO_DEVICE;

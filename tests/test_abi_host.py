@@ -124,3 +124,22 @@ def test_corrupted_plans_are_caught(corrupt, seed):
     rc, rep = B.plan_check(cfg, 1, 16, sim_runs=200, corrupt=corrupt, seed=seed)
     assert rc != B.MK_OK
     assert rep.sim_errors > 0 and rep.msg
+
+
+@pytest.mark.parametrize("name", ["tiny_qk", "qwen3_8b", "llama70b"])
+def test_switched_off_attention_paths_refused_before_the_device(name):
+    """q/k norm and head_dim 128 are refused by mk_create (after the
+    argument checks, before any device call), so no caller reaches that
+    attention code; the planner still accepts the shapes."""
+    mc = synth.CONFIGS[name]
+    cfg = B.make_config(mc, max_batch=1, max_seq=64)
+    dummy = C.c_void_p(0x1000)  # never dereferenced on this path
+    layers = (B.MkLayerWeights * mc.n_layers)()
+    for ly in layers:
+        for f, _ in B.MkLayerWeights._fields_:
+            setattr(ly, f, dummy)
+    w = B.MkWeights(dummy, dummy, dummy, layers)
+    out = C.c_void_p()
+    assert B.lib().mk_create(C.byref(cfg), C.byref(w), C.byref(out)) == B.MK_ERR_UNSUPPORTED
+    assert not out.value
+    assert B.plan_check(cfg, 1, 256, sim_runs=0)[0] == B.MK_OK
