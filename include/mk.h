@@ -90,9 +90,10 @@ typedef struct mk_weights {
 typedef struct mk_handle mk_handle;
 
 /* mk_create -- validate the configuration, query the device, allocate the
- * library's scratch (counters, activations, partials, RoPE table, queues)
- * and build the instruction schedule (chapter 3, section 3.2: queues are
- * planned on the host before launch).
+ * library's scratch (counters, activations, partials, RoPE table).  The
+ * instruction schedule (chapter 3, section 3.2: queues are planned on the
+ * host before launch) of a batch size is built at its first step and passes
+ * the static checks of mk_plan_check before it is uploaded.
  *   cfg, w  : host pointers, read during the call only.  The weight device
  *             pointers inside must stay valid and unmodified until
  *             mk_destroy; the library reads them in place and never copies,
@@ -187,9 +188,12 @@ typedef struct mk_plan_report {
  * `sim_runs` seeded interleavings of the per-CU queues that respect only the
  * counter waits (some adversarial: one CU delayed, stage-reversed
  * priorities), checking that every read sees its producers finished and that
- * no interleaving deadlocks.  `corrupt` != 0 deliberately breaks the plan
- * (1: drop a signal, 2: lower a wait target, 3: drop a wait) so tests can
- * check that the validator catches it.  Host only; no GPU needed.
+ * no interleaving deadlocks; every unit's rows, heads, splits, row-table
+ * and wait entries and every recorded access must lie inside the buffers
+ * they index.  `corrupt` != 0 deliberately breaks the plan (1: drop a
+ * signal, 2: lower a wait target, 3: drop a wait, 4: move an attention unit
+ * one split past the last) so tests can check that the validator catches
+ * it.  Host only; no GPU needed.
  * Returns MK_OK if the plan is valid, MK_ERR_UNSUPPORTED for shapes the
  * decomposition rejects, MK_ERR_INVALID_ARG otherwise; rep is filled. */
 int mk_plan_check(const mk_config *cfg, int32_t batch, int32_t num_cus,

@@ -283,6 +283,9 @@ static int get_plan(mk_handle *h, int batch, DevPlan **out) {
   if (rc) return rc;
   resolve_streams(h->cfg, h->w, dp->plan);
   Plan &P = dp->plan;
+  // no plan reaches the device without the validator's static checks
+  // (coverage of every read by waits, counter targets, extents)
+  if (check_plan(h->cfg, P, 0, 0, 0, nullptr) != MK_OK) return MK_ERR_UNSUPPORTED;
   // the counter groups, then one padded word: the greedy arrival counter
   dp->amax_word = (size_t)P.n_groups * kSlots * kCtrStride;
   dp->ctr_bytes = (dp->amax_word + kCtrStride) * 4;

@@ -430,7 +430,6 @@ struct Sim {
 
 int check_plan(const mk_config &cfg, Plan &P, int sim_runs, int corrupt, uint64_t seed,
                mk_plan_report *rep) {
-  (void)cfg;
   const int C = P.num_cus;
   const size_t NU = P.instr.size();
   std::string first;
@@ -440,6 +439,62 @@ int check_plan(const mk_config &cfg, Plan &P, int sim_runs, int corrupt, uint64_
     ++errors;
   };
   std::mt19937_64 rng(seed);
+
+  // Extents: every index an instruction or a recorded access carries stays
+  // inside the buffer it addresses (the kernel forms its addresses from
+  // these fields, the step's position and the lane alone).
+  {
+    if (corrupt == 4)
+      for (Instr &in : P.instr)
+        if (in.op == OP_ATTN) {
+          in.aux1 = (uint32_t)P.n_split;  // one split past the last
+          break;
+        }
+    const uint32_t H = (uint32_t)cfg.hidden, F = (uint32_t)cfg.ffn_dim, V = (uint32_t)cfg.vocab;
+    const uint32_t nkv = (uint32_t)cfg.n_kv_heads, nq = (uint32_t)cfg.n_q_heads, hd = (uint32_t)cfg.head_dim;
+    const uint32_t G = nq / nkv, ppg = (G + 2) * (hd / 2), ns = (uint32_t)P.n_split;
+    if (P.n_split < 1 || P.n_split > kMaxSplits || P.split_len < 1 ||
+        (int64_t)P.n_split * P.split_len < cfg.max_seq)
+      fail("the KV splits do not cover max_seq slots");
+    auto limit = [&](uint8_t op) -> uint32_t {
+      switch (op) {
+        case OP_QKV: return nkv * ppg;
+        case OP_O: case OP_DOWN: return H;
+        case OP_FFN: return F;
+        case OP_LM: return V;
+        default: return 0;
+      }
+    };
+    for (size_t u = 0; u < NU; ++u) {
+      const Instr &in = P.instr[u];
+      if (in.layer >= (uint32_t)cfg.n_layers && in.op != OP_LM) fail("instruction layer out of range");
+      if (in.b >= (uint32_t)P.batch) fail("instruction sequence out of range");
+      if (in.op == OP_ATTN && (in.aux0 >= nkv || in.aux1 >= ns)) fail("attention unit head or split out of range");
+      if (in.op == OP_RED && in.aux0 >= nkv) fail("reduction unit head out of range");
+      const uint32_t lim = limit(in.op);
+      if (lim && ((uint64_t)in.item0 + in.n_items > lim || in.n_items == 0)) fail("unit rows out of range");
+      if (in.tab >= 0 && (size_t)in.tab + (size_t)in.n_items * in.ipw > P.rowtab.size())
+        fail("row table entries out of range");
+      if (in.wait_off + (uint64_t)in.wait_n > P.waits.size()) fail("wait entries out of range");
+    }
+    auto res_limit = [&](uint8_t res) -> uint32_t {
+      switch (res) {
+        case R_QKV: return nkv * ppg;
+        case R_PART: return nkv * ns;
+        case R_ATTN: return nq * hd;
+        case R_HMID: case R_HOUT: return H;
+        case R_A: return F;
+        default: return 0;
+      }
+    };
+    for (size_t u = 0; u < NU && u < P.reads.size(); ++u)
+      for (const auto *lst : {&P.reads[u], &P.writes[u]})
+        for (const Access &x : *lst) {
+          const uint32_t lim = res_limit(x.res);
+          if (!lim || x.lo > x.hi || x.hi > lim || x.layer >= (uint32_t)cfg.n_layers || x.b >= (uint32_t)P.batch)
+            fail("a recorded access lies outside its buffer");
+        }
+  }
 
   // Deliberate corruption for validator self-tests.
   std::vector<uint32_t> target(P.n_groups, 0);

@@ -126,6 +126,16 @@ def test_corrupted_plans_are_caught(corrupt, seed):
     assert rep.sim_errors > 0 and rep.msg
 
 
+@pytest.mark.parametrize("name", ["tiny", "llama1b", "tiny_qk", "llama70b"])
+def test_out_of_range_split_is_caught(name):
+    """The extent check: an attention unit whose split index is one past
+    the last would address partials and K/V rows outside their buffers."""
+    cfg = B.make_config(synth.CONFIGS[name], max_batch=1)
+    rc, rep = B.plan_check(cfg, 1, 256, corrupt=4)
+    assert rc != B.MK_OK
+    assert b"out of range" in rep.msg
+
+
 @pytest.mark.parametrize("name", ["tiny_qk", "qwen3_8b", "llama70b"])
 def test_switched_off_attention_paths_refused_before_the_device(name):
     """q/k norm and head_dim 128 are refused by mk_create (after the
