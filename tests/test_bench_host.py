@@ -52,3 +52,16 @@ def test_stored_traffic_only_for_matching_sources(monkeypatch):
     monkeypatch.setattr(bench, "source_digest", lambda: "0" * 16)
     assert bench.stored_traffic("llama1b") is None
     assert bench.stored_traffic("no_such_workload") is None
+
+
+def test_algorithmic_bytes_count_weights_once_per_step():
+    """At batch B the step's algorithmic bytes add only each extra
+    sequence's embedding row and K/V slots: the weights are read once per
+    step whatever the batch (the batch-8 roofline prices against that)."""
+    mc = synth.CONFIGS["llama1b_b8"]
+    one = bench.algorithmic_bytes(mc, [2000])
+    eight = bench.algorithmic_bytes(mc, [2000] * 8)
+    kv_row = 2 * 2 * mc.n_layers * mc.n_kv_heads * mc.head_dim  # K and V bf16, one slot
+    assert eight - one == 7 * (2 * mc.hidden + kv_row * 2001)
+    assert one - bench.algorithmic_bytes(mc, [1999]) == kv_row
+    assert bench.algorithmic_bytes(mc, []) == mc.weight_bytes()
