@@ -200,6 +200,40 @@ int mk_plan_check(const mk_config *cfg, int32_t batch, int32_t num_cus,
                   int32_t sim_runs, int32_t corrupt, uint64_t seed,
                   mk_plan_report *rep);
 
+/* Result of the address model below. */
+typedef struct mk_addr_report {
+  int64_t accesses;           /* global accesses evaluated (per lane)        */
+  int32_t violations;         /* accesses outside the buffer they address    */
+  char    msg[256];           /* the first violation: site, buffer, offset   */
+} mk_addr_report;
+
+/* mk_addr_check -- host model of the decode kernel's global memory accesses
+ * for `steps` consecutive steps of (cfg, batch) on `num_cus` workgroups,
+ * positions advancing by one per step from positions[b] and the tokens
+ * fixed at tokens[b].  It builds the plan the library would upload, gives
+ * every tensor and library buffer its size as mk_create and the plan upload
+ * allocate them, and walks every workgroup's queue the way each role of the
+ * kernel does (input checks, norm weights, RoPE rows, activation pieces,
+ * residual rows, weight pieces and page sentinels, attention K/V rows and
+ * the new slot, tagged q/K/V words, partials, reduction, epilogue stores,
+ * greedy candidates, counters), per lane, with the kernel's own offset
+ * arithmetic; every access must lie inside the buffer it addresses.  This is
+ * the gate every new kernel path passes before it runs on a GPU (the
+ * megakernel chapter "Quand ne pas le faire", section 9.3: an error of this
+ * kind shows as a rare wrong token or a fault, not as a failed assertion).
+ *   positions, tokens : host int32 [batch].
+ *   corrupt : 0, or a planted size error for the model's self-tests: the
+ *             model's copy of one buffer is one record short (1: the KV
+ *             cache's last slot, 2: the last attention partial, 3: the last
+ *             RoPE row, 4: the last q head, 5: the final residual row), so
+ *             a run that reaches that record must report it.
+ * Returns MK_OK if no access falls outside its buffer, MK_ERR_INVALID_ARG
+ * (rep->msg names the first) otherwise, or the plan's own error.  Host only. */
+int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cus,
+                  int32_t steps, const int32_t *positions,
+                  const int32_t *tokens, int32_t corrupt,
+                  mk_addr_report *rep);
+
 /* Internal activation buffers, for stage-by-stage comparison in tests. */
 #define MK_BUF_H      1   /* fp32 [2L+1][max_batch][hidden]: index 2l+1 is the
                              residual after attention of layer l, 2l+2 after

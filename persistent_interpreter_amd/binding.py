@@ -6,12 +6,17 @@ loudly if the library has not been built.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes as C
 import os
+import sys
+import weakref
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "_lib", "libmk.so")
+# MK_LIB_PATH selects another build of the same library (a compile-time knob
+# variant, for measurements); the default is the in-tree build.
+LIB_PATH = os.environ.get("MK_LIB_PATH") or os.path.join(_HERE, "_lib", "libmk.so")
 
 MK_OK = 0
 MK_ERR_INVALID_ARG = -1
@@ -32,7 +37,7 @@ MK_BUF_H, MK_BUF_Q, MK_BUF_ATTN, MK_BUF_A, MK_BUF_TRACE = 1, 2, 3, 4, 5
 EXPORTED = ("mk_create", "mk_decode_step", "mk_decode_step_greedy",
             "mk_sync_status", "mk_destroy", "mk_strerror", "mk_plan_check",
             "mk_get_buffer", "mk_version", "mk_stream_read",
-            "mk_stream_read_sink_words")
+            "mk_stream_read_sink_words", "mk_addr_check")
 
 
 class MkConfig(C.Structure):
@@ -65,6 +70,11 @@ class MkPlanReport(C.Structure):
                 ("n_pages", C.c_int32), ("max_queue", C.c_int32),
                 ("weight_bytes", C.c_int64), ("max_cu_bytes", C.c_int64),
                 ("sim_runs", C.c_int32), ("sim_errors", C.c_int32),
+                ("msg", C.c_char * 256)]
+
+
+class MkAddrReport(C.Structure):
+    _fields_ = [("accesses", C.c_int64), ("violations", C.c_int32),
                 ("msg", C.c_char * 256)]
 
 
@@ -109,6 +119,11 @@ def lib():
                                     C.POINTER(C.c_void_p),
                                     C.POINTER(C.c_size_t)]
         L.mk_get_buffer.restype = C.c_int
+        L.mk_addr_check.argtypes = [C.POINTER(MkConfig), C.c_int32, C.c_int32,
+                                    C.c_int32, C.POINTER(C.c_int32),
+                                    C.POINTER(C.c_int32), C.c_int32,
+                                    C.POINTER(MkAddrReport)]
+        L.mk_addr_check.restype = C.c_int
         L.mk_version.argtypes = []
         L.mk_version.restype = C.c_int
         _lib = L
@@ -144,8 +159,31 @@ def plan_check(cfg: MkConfig, batch: int, num_cus: int, sim_runs: int = 0,
     return rc, rep
 
 
+def addr_check(cfg: MkConfig, batch: int, num_cus: int, steps: int,
+               positions, tokens, corrupt: int = 0):
+    """Run the host address model (mk_addr_check); returns (rc, report)."""
+    rep = MkAddrReport()
+    pos = (C.c_int32 * batch)(*[int(x) for x in positions])
+    tok = (C.c_int32 * batch)(*[int(x) for x in tokens])
+    rc = lib().mk_addr_check(C.byref(cfg), batch, num_cus, steps, pos, tok,
+                             corrupt, C.byref(rep))
+    return rc, rep
+
+
 def _ptr(t) -> int:
     return 0 if t is None else int(t.data_ptr())
+
+
+# Every live handle, closed by an exit hook that runs before the interpreter
+# tears down its modules (and long before the HIP runtime's own exit-time
+# teardown), so mk_destroy never runs from a finalizer at shutdown.
+_LIVE: "weakref.WeakSet" = weakref.WeakSet()
+
+
+@atexit.register
+def _close_all():
+    for mk in list(_LIVE):
+        mk.close()
 
 
 class Megakernel:
@@ -170,6 +208,7 @@ class Megakernel:
         if rc != MK_OK:
             raise MkError(rc, "mk_create")
         self.h = h
+        _LIVE.add(self)
 
     def decode_step(self, batch: int, tokens, positions, kv, logits,
                     stream: Optional[int] = None) -> int:
@@ -204,11 +243,18 @@ class Megakernel:
         return p.value, n.value
 
     def close(self):
+        """Free the handle (synchronising the device first, so no step of it
+        is still running when its buffers go)."""
         if getattr(self, "h", None):
-            lib().mk_destroy(self.h)
-            self.h = None
+            h, self.h = self.h, None
+            lib().mk_sync_status(h)
+            lib().mk_destroy(h)
 
     def __del__(self):
+        # at interpreter shutdown the exit hook has already closed the
+        # handle; a finalizer that runs later must not call into HIP
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:

@@ -48,7 +48,7 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
         o = os.path.join(out_dir, f"{stem}_" + src.replace(".hip", ".o"))
         _run([HIPCC, *DEVICE_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", o])
         objs.append(o)
-    for src in ("mk_sched.cpp", "mk_abi.cpp"):
+    for src in ("mk_sched.cpp", "mk_abi.cpp", "mk_addr.cpp"):
         o = os.path.join(out_dir, f"{stem}_" + src.replace(".cpp", ".o"))
         _run(["g++", *HOST_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", o])
         objs.append(o)

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "../../include/mk.h"
+#include "mk_layout.hpp"
 #include "mk_plan.hpp"
 #include "mk_sched.hpp"
 
@@ -208,18 +209,18 @@ int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out) {
 
   const int L = cfg->n_layers, MB = cfg->max_batch, H = cfg->hidden, nq = cfg->n_q_heads;
   const int hd = cfg->head_dim, F = cfg->ffn_dim, S = cfg->max_seq;
-  h->h_bytes = (size_t)(2 * L + 1) * MB * H * 4;
-  h->q_bytes = (size_t)L * MB * nq * hd * 8;
-  h->attn_bytes = (size_t)L * MB * nq * hd * 4;
-  h->a_bytes = (size_t)L * MB * F * 4;
-  h->kvn_bytes = (size_t)L * MB * cfg->n_kv_heads * 2 * hd * 8;
-  std::vector<float> rope((size_t)S * (hd / 2) * 2);
+  h->h_bytes = lay::h_size(L, MB, H) * 4;
+  h->q_bytes = lay::q_size(L, MB, nq, hd) * 8;
+  h->attn_bytes = lay::attn_size(L, MB, nq, hd) * 4;
+  h->a_bytes = lay::a_size(L, MB, F) * 4;
+  h->kvn_bytes = lay::kvn_size(L, MB, cfg->n_kv_heads, hd) * 8;
+  std::vector<float> rope(lay::rope_size(S, hd));
   for (int p = 0; p < S; ++p)
     for (int i = 0; i < hd / 2; ++i) {
       // angle p * theta^(-2i/hd) in double, cos/sin rounded to float
       double ang = (double)p * std::pow((double)cfg->rope_theta, -2.0 * i / (double)hd);
-      rope[((size_t)p * (hd / 2) + i) * 2] = (float)std::cos(ang);
-      rope[((size_t)p * (hd / 2) + i) * 2 + 1] = (float)std::sin(ang);
+      rope[lay::rope(hd, p, i)] = (float)std::cos(ang);
+      rope[lay::rope(hd, p, i) + 1] = (float)std::sin(ang);
     }
   std::vector<DevLayer> dl(L);
   for (int l = 0; l < L; ++l) {
@@ -290,8 +291,8 @@ static int get_plan(mk_handle *h, int batch, DevPlan **out) {
   dp->amax_word = (size_t)P.n_groups * kSlots * kCtrStride;
   dp->ctr_bytes = (dp->amax_word + kCtrStride) * 4;
   for (const Instr &in : P.instr) dp->n_lm += in.op == OP_LM ? 1u : 0u;
-  const size_t part = (size_t)h->cfg.n_layers * h->cfg.max_batch * h->cfg.n_q_heads * P.n_split *
-                      (h->cfg.head_dim + 4) * 4;
+  const size_t part =
+      lay::part_size(h->cfg.n_layers, h->cfg.max_batch, h->cfg.n_q_heads, P.n_split, h->cfg.head_dim) * 4;
   // page sentinels: iota[i] = i for every page index of the longest queue
   uint32_t max_pages = 0;
   for (int c = 0; c < h->num_cus; ++c) {

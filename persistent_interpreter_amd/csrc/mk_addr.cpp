@@ -1,0 +1,492 @@
+// mk_addr.cpp -- host model of every global-memory access of the decode
+// kernel, checked against the extent of the buffer it belongs to.
+//
+// For a configuration, a batch size and a run of steps (positions advancing
+// by one per step, as in greedy decoding), the model builds the same plan the
+// library uploads, gives every caller tensor and library buffer a synthetic
+// base address (2^40 apart, so an overrun of one can never land in
+// another), and walks each workgroup's queue the way each role of the kernel
+// does: the sync wave's input checks, norm weights, RoPE values, activation
+// pieces and residual rows; the loader waves' weight pieces and page
+// sentinels; the compute waves' attention and reduction bodies, epilogues,
+// greedy candidates and counter signals.  Every access is evaluated per lane
+// with the offsets of mk_layout.hpp (the kernel's own arithmetic) and must
+// lie inside the one buffer it addresses.  The loop structure of each body is
+// mirrored from mk_kernel.hip; a change there must be made here too, and the
+// tests run this model for every shape the GPU tests run.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_layout.hpp"
+#include "mk_plan.hpp"
+#include "mk_sched.hpp"
+
+using namespace mk;
+
+namespace {
+
+constexpr int kShift = 40;
+
+struct Model {
+  struct Buf {
+    std::string name;
+    uint64_t bytes;
+  };
+  std::vector<Buf> bufs;
+  int64_t n = 0;
+  int bad = 0;
+  std::string first;
+
+  uint64_t add(const std::string &name, uint64_t bytes) {
+    bufs.push_back({name, bytes});
+    return (uint64_t)bufs.size() << kShift;
+  }
+  // an access of `bytes` at absolute synthetic address `addr`, which must lie
+  // in buffer `want` (0: any buffer, for weight streams whose tensor is
+  // resolved by the plan)
+  void at(uint64_t addr, uint32_t bytes, uint64_t want, const char *site) {
+    ++n;
+    const uint64_t id = addr >> kShift, off = addr & ((1ull << kShift) - 1);
+    const bool in = id >= 1 && id <= bufs.size() && off + bytes <= bufs[id - 1].bytes &&
+                    (want == 0 || (want >> kShift) == id);
+    if (!in) {
+      if (first.empty()) {
+        char m[256];
+        std::snprintf(m, sizeof m, "%s: %u bytes at %s+%llu (size %llu)%s%s", site, bytes,
+                      id >= 1 && id <= bufs.size() ? bufs[id - 1].name.c_str() : "?", (unsigned long long)off,
+                      id >= 1 && id <= bufs.size() ? (unsigned long long)bufs[id - 1].bytes : 0ull,
+                      want ? ", expected in " : "", want ? bufs[(want >> kShift) - 1].name.c_str() : "");
+        first = m;
+      }
+      ++bad;
+    }
+  }
+  // element access into buffer `base` (element size `es`)
+  void el(uint64_t base, uint64_t idx, uint32_t es, uint32_t bytes, const char *site) {
+    at(base + idx * es, bytes, base, site);
+  }
+};
+
+struct Bases {
+  uint64_t tokens, positions, kv, logits, next_tok, next_pos;
+  uint64_t h, q, kvn, attn, a, part, rope, status, ctr, target, amax, rowtab, iota;
+  uint64_t embed, lm_head, final_norm;
+  std::vector<uint64_t> attn_norm, q_norm, k_norm, ffn_norm;
+};
+
+}  // namespace
+
+extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int32_t steps,
+                             const int32_t *positions, const int32_t *tokens, int32_t corrupt,
+                             mk_addr_report *rep) {
+  if (rep) std::memset(rep, 0, sizeof *rep);
+  if (!cfg || !positions || !tokens || batch < 1 || num_cus < 1 || steps < 1) return MK_ERR_INVALID_ARG;
+  const mk_config &c = *cfg;
+  Plan P;
+  std::string err;
+  int rc = build_plan(c, batch, num_cus, P, err);
+  if (rc) {
+    if (rep) std::snprintf(rep->msg, sizeof rep->msg, "%s", err.c_str());
+    return rc;
+  }
+  const int L = c.n_layers, H = c.hidden, nq = c.n_q_heads, nkv = c.n_kv_heads, hd = c.head_dim;
+  const int F = c.ffn_dim, V = c.vocab, MB = c.max_batch, S = c.max_seq, G = nq / nkv, half = hd / 2;
+  const int ns = P.n_split;
+  Model M;
+  Bases B;
+  // caller tensors (bf16 weights, int32 inputs, the cache and the logits)
+  B.embed = M.add("embed", (uint64_t)V * H * 2);
+  B.lm_head = c.tied_embeddings ? B.embed : M.add("lm_head", (uint64_t)V * H * 2);
+  B.final_norm = M.add("final_norm", (uint64_t)H * 2);
+  std::vector<mk_layer_weights> lw(L);
+  for (int l = 0; l < L; ++l) {
+    auto w = [&](const char *nm, uint64_t bytes) {
+      return (const void *)(uintptr_t)M.add(std::string(nm) + "[" + std::to_string(l) + "]", bytes);
+    };
+    lw[l].attn_norm = w("attn_norm", (uint64_t)H * 2);
+    lw[l].wq = w("wq", (uint64_t)nq * hd * H * 2);
+    lw[l].wk = w("wk", (uint64_t)nkv * hd * H * 2);
+    lw[l].wv = w("wv", (uint64_t)nkv * hd * H * 2);
+    lw[l].q_norm = c.qk_norm ? w("q_norm", (uint64_t)hd * 2) : nullptr;
+    lw[l].k_norm = c.qk_norm ? w("k_norm", (uint64_t)hd * 2) : nullptr;
+    lw[l].wo = w("wo", (uint64_t)H * nq * hd * 2);
+    lw[l].ffn_norm = w("ffn_norm", (uint64_t)H * 2);
+    lw[l].w_gate = w("w_gate", (uint64_t)F * H * 2);
+    lw[l].w_up = w("w_up", (uint64_t)F * H * 2);
+    lw[l].w_down = w("w_down", (uint64_t)H * F * 2);
+    B.attn_norm.push_back((uint64_t)(uintptr_t)lw[l].attn_norm);
+    B.q_norm.push_back((uint64_t)(uintptr_t)lw[l].q_norm);
+    B.k_norm.push_back((uint64_t)(uintptr_t)lw[l].k_norm);
+    B.ffn_norm.push_back((uint64_t)(uintptr_t)lw[l].ffn_norm);
+  }
+  mk_weights W;
+  W.embed = (const void *)(uintptr_t)B.embed;
+  W.lm_head = c.tied_embeddings ? nullptr : (const void *)(uintptr_t)B.lm_head;
+  W.final_norm = (const void *)(uintptr_t)B.final_norm;
+  W.layers = lw.data();
+  resolve_streams(c, W, P);
+  if (check_plan(c, P, 0, 0, 0, nullptr) != MK_OK) {
+    if (rep) std::snprintf(rep->msg, sizeof rep->msg, "the plan fails its static checks");
+    return MK_ERR_UNSUPPORTED;
+  }
+  B.tokens = M.add("tokens", (uint64_t)batch * 4);
+  B.positions = M.add("positions", (uint64_t)batch * 4);
+  // planted size errors for the model's self-tests: one record short
+  const uint64_t short_kv = corrupt == 1 ? (uint64_t)hd * 2 : 0, short_part = corrupt == 2 ? (hd + 4) * 4 : 0;
+  const uint64_t short_rope = corrupt == 3 ? (uint64_t)hd * 4 : 0, short_q = corrupt == 4 ? (uint64_t)hd * 8 : 0;
+  const uint64_t short_h = corrupt == 5 ? (uint64_t)H * 4 : 0;
+  B.kv = M.add("kv_cache", lay::kv_size(L, MB, nkv, S, hd) * 2 - short_kv);
+  B.logits = M.add("logits", (uint64_t)batch * V * 4);
+  B.next_tok = M.add("next_tokens", (uint64_t)batch * 4);
+  B.next_pos = M.add("next_positions", (uint64_t)batch * 4);
+  // library buffers, sized as mk_create and the plan upload size them
+  B.h = M.add("h", lay::h_size(L, MB, H) * 4 - short_h);
+  B.q = M.add("q", lay::q_size(L, MB, nq, hd) * 8 - short_q);
+  B.kvn = M.add("kvn", lay::kvn_size(L, MB, nkv, hd) * 8);
+  B.attn = M.add("attn", lay::attn_size(L, MB, nq, hd) * 4);
+  B.a = M.add("a", lay::a_size(L, MB, F) * 4);
+  B.part = M.add("partials", lay::part_size(L, MB, nq, ns, hd) * 4 - short_part);
+  B.rope = M.add("rope", lay::rope_size(S, hd) * 4 - short_rope);
+  B.status = M.add("status", 256);
+  const uint64_t amax_word = (uint64_t)P.n_groups * kSlots * kCtrStride;
+  B.ctr = M.add("counters", (amax_word + kCtrStride) * 4);
+  B.target = M.add("targets", P.grp_target.size() * 4);
+  uint32_t n_lm = 0, max_pages = 0;
+  for (const Instr &in : P.instr) n_lm += in.op == OP_LM;
+  for (int cu = 0; cu < num_cus; ++cu) {
+    uint32_t np = 0;
+    for (uint32_t qi = P.q_off[cu]; qi < P.q_off[cu + 1]; ++qi) np += P.instr[qi].pages;
+    max_pages = std::max(max_pages, np);
+  }
+  B.amax = M.add("amax", (uint64_t)n_lm * MB * 8);
+  B.rowtab = M.add("rowtab", P.rowtab.size() * 8);
+  B.iota = M.add("iota", ((uint64_t)max_pages + 1) * 4);
+
+  for (int step = 0; step < steps; ++step) {
+    std::vector<int> pos(batch);
+    for (int b = 0; b < batch; ++b) pos[b] = positions[b] + step;
+    // the launch clamps an invalid position to 0 for the cache accesses (the
+    // sync wave reports it and abandons the step)
+    const int pos0 = (pos[0] < 0 || pos[0] >= S) ? 0 : pos[0];
+    bool inputs_ok = true;
+    for (int b = 0; b < batch; ++b)
+      if (tokens[b] < 0 || tokens[b] >= V || pos[b] < 0 || pos[b] >= S) inputs_ok = false;
+    M.el(B.positions, 0, 4, 4, "kernel start: positions[0]");
+
+    for (int cu = 0; cu < num_cus; ++cu) {
+      const uint32_t q0 = P.q_off[cu], q1 = P.q_off[cu + 1];
+      // ---- sync wave ----------------------------------------------------
+      for (int b = 0; b < batch; ++b) {
+        M.el(B.tokens, b, 4, 4, "sync: tokens[b]");
+        M.el(B.positions, b, 4, 4, "sync: positions[b]");
+      }
+      if (inputs_ok)
+        for (uint32_t qi = q0; qi < q1; ++qi) {
+          const Instr &d = P.instr[qi];
+          const bool gv = d.op == OP_QKV || d.op == OP_O || d.op == OP_FFN || d.op == OP_DOWN || d.op == OP_LM;
+          const uint32_t nx = gv ? d.nk : 1;
+          const bool normed = d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM;
+          const int b = 0;
+          uint64_t hbase = 0, emb = 0, nw = 0;
+          if (normed) {
+            if (d.op == OP_QKV) {
+              nw = B.attn_norm[d.layer];
+              if (d.layer == 0) emb = B.embed + (uint64_t)tokens[b] * H * 2;
+              else hbase = B.h + lay::h(MB, H, 2 * d.layer, b) * 4;
+            } else if (d.op == OP_FFN) {
+              nw = B.ffn_norm[d.layer];
+              hbase = B.h + lay::h(MB, H, 2 * d.layer + 1, b) * 4;
+            } else {
+              nw = B.final_norm;
+              hbase = B.h + lay::h(MB, H, 2 * L, b) * 4;
+            }
+            for (uint32_t k = 0; k < nx; ++k)
+              for (int lane = 0; lane < 64; ++lane)
+                for (uint32_t i = (uint32_t)lane * 4; i < d.kc; i += 256)
+                  M.at(nw + ((uint64_t)k * d.kc + i) * 2, 8, nw, "sync: norm weights");
+          }
+          if (d.op == OP_QKV) {
+            const uint32_t ppg = (uint32_t)(G + 2) * half;
+            for (uint32_t i = 0; i < d.n_items; ++i) {
+              const uint32_t ii = ((d.item0 + i) % ppg) % half;
+              M.el(B.rope, lay::rope(hd, pos0, (int)ii), 4, 8, "sync: RoPE of the unit's pairs");
+            }
+          }
+          for (uint32_t w = 0; w < d.wait_n; ++w) {
+            const Wait &wt = P.waits[d.wait_off + w];
+            for (uint32_t lane = 0; lane < wt.nslot; ++lane) {
+              M.el(B.ctr, ((uint64_t)wt.grp * kSlots + lane) * kCtrStride, 4, 4, "sync: counter poll");
+              M.el(B.target, (uint64_t)wt.grp * kSlots + lane, 4, 4, "sync: slot target");
+            }
+            M.el(B.status, 0, 4, 4, "sync: status poll");
+          }
+          const bool dma = (d.op == OP_DOWN || (d.op == OP_O && d.layer > 0)) && d.n_items <= 64;
+          if (dma) {
+            const uint64_t src = d.op == OP_O ? B.attn + lay::attn(MB, nq, hd, d.layer, b) * 4
+                                              : B.a + lay::a(MB, F, d.layer, b) * 4;
+            const uint64_t want = d.op == OP_O ? B.attn : B.a;
+            const uint64_t res =
+                B.h + (lay::h(MB, H, d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1, b) + d.item0) * 4;
+            for (int lane = 0; lane < (int)d.n_items; ++lane) M.at(res + lane * 4, 4, B.h, "sync: residual rows");
+            for (uint32_t k = 0; k < nx; ++k)
+              for (int j = 0; j < 8; ++j)
+                for (int lane = 0; lane < 64; ++lane) {
+                  const uint32_t f = (uint32_t)(j * 256 + lane * 4);
+                  M.at(src + ((uint64_t)k * d.kc + (f < d.kc ? f : 0u)) * 4, 16, want, "sync: activation piece (DMA)");
+                }
+          } else {
+            for (uint32_t k = 0; k < nx; ++k) {
+              if (normed) {
+                auto batch_ld = [&](uint32_t e0) {
+                  for (int lane = 0; lane < 64; ++lane)
+                    for (int m = 0; m < 8; ++m) {
+                      const uint32_t i = e0 + (uint32_t)(lane + 64 * m) * 4;
+                      if (i >= (uint32_t)H) continue;
+                      if (emb) M.at(emb + (uint64_t)i * 2, 8, B.embed, "sync: embedding row");
+                      else M.at(hbase + (uint64_t)i * 4, 16, B.h, "sync: residual for the norm");
+                    }
+                };
+                if (k == 0)
+                  for (uint32_t e0 = 0; e0 < (uint32_t)H; e0 += 2048) batch_ld(e0);
+                if (H > 2048 || k != 0) batch_ld(k * d.kc);
+              } else if (d.op == OP_O || d.op == OP_DOWN) {
+                const uint64_t src = d.op == OP_O ? B.attn + lay::attn(MB, nq, hd, d.layer, b) * 4
+                                                  : B.a + lay::a(MB, F, d.layer, b) * 4;
+                const uint64_t want = d.op == OP_O ? B.attn : B.a;
+                for (int lane = 0; lane < 64; ++lane)
+                  for (int m = 0; m < 8; ++m) {
+                    const uint32_t i = (uint32_t)(lane + 64 * m) * 4;
+                    if (i < d.kc) M.at(src + ((uint64_t)k * d.kc + i) * 4, 16, want, "sync: activation piece");
+                  }
+                if (k == 0)
+                  for (int lane = 0; lane < 64; ++lane)
+                    for (int m = 0; m < kAccFloats / 64; ++m) {
+                      const uint32_t r = (uint32_t)(lane + 64 * m);
+                      if (r >= d.n_items) continue;
+                      if (d.op == OP_O && d.layer == 0)
+                        M.at(B.embed + ((uint64_t)tokens[b] * H + d.item0 + r) * 2, 2, B.embed, "sync: embedding residual");
+                      else
+                        M.el(B.h, lay::h(MB, H, d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1, b) + d.item0 + r, 4, 4,
+                             "sync: residual rows");
+                    }
+              }
+            }
+          }
+        }
+
+      // ---- loader waves ---------------------------------------------------
+      uint32_t n = 0;
+      for (uint32_t qi = q0; qi < q1; ++qi) {
+        const Instr &d = P.instr[qi];
+        const bool gv = d.op == OP_QKV || d.op == OP_O || d.op == OP_FFN || d.op == OP_DOWN || d.op == OP_LM;
+        if (!gv) continue;
+        const uint32_t per = d.n_items * d.ipw, npieces = per * d.nk;
+        auto piece = [&](uint32_t k, uint32_t r) -> uint64_t {
+          uint64_t base;
+          if (d.tab >= 0) {
+            M.el(B.rowtab, (uint64_t)d.tab + r, 8, 8, "loader: row table");
+            base = (size_t)d.tab + r < P.rowtab.size() ? P.rowtab[d.tab + r] : 0;
+          } else if (d.ipw == 2) {
+            base = ((r & 1) ? d.w1 : d.w0) + (uint64_t)(d.item0 + (r >> 1)) * d.rowb;
+          } else {
+            base = d.w0 + (uint64_t)(d.item0 + r) * d.rowb;
+          }
+          return base + (uint64_t)k * d.pb;
+        };
+        for (uint32_t p = 0; p < d.pages; ++p, ++n) {
+          const uint32_t t0 = p * d.ppp;
+          const uint32_t cnt = std::min((uint32_t)d.ppp, npieces - t0);
+          uint32_t k = t0 / per, r = t0 - k * per;
+          const uint64_t first = piece(k, r);
+          if (d.pb >= 1024) {
+            const uint32_t lpp = d.pb >> 10;
+            uint32_t j = 0;
+            for (uint32_t qq = 0; qq < cnt; ++qq) {
+              const uint64_t src = piece(k, r);
+              const uint64_t row0 = src - (uint64_t)k * d.pb;  // the row's start: the piece must stay in its row
+              for (uint32_t sub = 0; sub < lpp; ++sub)
+                for (int lane = 0; lane < 64; ++lane) {
+                  const uint64_t ad = src + sub * 1024 + lane * 16;
+                  M.at(ad, 16, 0, "loader: weight piece");
+                  if (ad + 16 > row0 + d.rowb) M.at(~0ull, 16, 0, "loader: weight piece crosses its row");
+                }
+              j += lpp;
+              if (++r == per) { r = 0; ++k; }
+            }
+            for (; j < 16; ++j)
+              for (int lane = 0; lane < 64; ++lane) M.at(first + lane * 16, 16, 0, "loader: tail re-read");
+          } else {
+            const uint32_t sh = 31 - __builtin_clz(d.pb);
+            for (int j = 0; j < 16; ++j)
+              for (int lane = 0; lane < 64; ++lane) {
+                const uint32_t o = (uint32_t)j * 1024 + lane * 16;
+                const uint32_t qq = o >> sh, within = o & (d.pb - 1);
+                const uint32_t t = t0 + qq;
+                uint64_t src = first;
+                if (t < npieces) {
+                  const uint32_t kk = t / per;
+                  src = piece(kk, t - kk * per) + within;
+                }
+                M.at(src, 16, 0, "loader: weight piece (small)");
+              }
+          }
+          M.el(B.iota, n, 4, 4, "loader: page sentinel");
+        }
+      }
+
+      // ---- compute waves ----------------------------------------------------
+      if (!inputs_ok) continue;
+      for (uint32_t qi = q0; qi < q1; ++qi) {
+        const Instr &d = P.instr[qi];
+        const int b = (int)d.b;
+        if (d.op == OP_ATTN) {
+          const int g = (int)d.aux0, s = (int)d.aux1;
+          const int DPL = hd / 64, PF = 20 / DPL, NR = DPL == 1 ? 16 : 8;
+          const int p = pos0;
+          const int lo = s * P.split_len, hi = std::min(lo + P.split_len, p + 1);
+          const int nt0 = std::max(0, std::min(hi - lo, PF));
+          const uint64_t Kr = lay::kv(MB, nkv, S, hd, d.layer, 0, b, g, lo);
+          const uint64_t Vr = lay::kv(MB, nkv, S, hd, d.layer, 1, b, g, lo);
+          for (int h = 0; h < G; ++h) {
+            const int j = g * G + h;
+            for (int lane = 0; lane < 64; ++lane) {
+              if (nt0 > 0)
+                for (int t = 0; t < PF; ++t) {
+                  const int tt = std::min(t, nt0 - 1);
+                  for (int m = 0; m < DPL; ++m) {
+                    M.el(B.kv, Kr + (uint64_t)tt * hd + lane + 64 * m, 2, 2, "attn: prefetched K");
+                    M.el(B.kv, Vr + (uint64_t)tt * hd + lane + 64 * m, 2, 2, "attn: prefetched V");
+                  }
+                }
+              if (DPL == 2 && c.qk_norm) {
+                for (int m = 0; m < DPL; ++m) {
+                  M.el(B.q_norm[d.layer], lane + 64 * m, 2, 2, "attn: q_norm weight");
+                  M.el(B.k_norm[d.layer], lane + 64 * m, 2, 2, "attn: k_norm weight");
+                }
+                M.el(B.rope, lay::rope(hd, p, lane), 4, 8, "attn: RoPE of pair (lane, lane + 64)");
+              }
+              if (lo < hi) {
+                const bool has_p = p < hi;
+                for (int m = 0; m < DPL; ++m) {
+                  M.el(B.q, lay::q(MB, nq, hd, d.layer, b, j) + lane + 64 * m, 8, 8, "attn: tagged q");
+                  if (has_p) {
+                    M.el(B.kvn, lay::kvn(MB, nkv, hd, d.layer, b, g, 0) + lane + 64 * m, 8, 8, "attn: tagged new K");
+                    M.el(B.kvn, lay::kvn(MB, nkv, hd, d.layer, b, g, 0) + hd + lane + 64 * m, 8, 8,
+                         "attn: tagged new V");
+                  }
+                }
+                if (DPL == 2 && c.qk_norm && has_p && h == 0) {
+                  M.el(B.kv, lay::kv(MB, nkv, S, hd, d.layer, 0, b, g, p) + lane, 2, 2, "attn: K store at p");
+                  M.el(B.kv, lay::kv(MB, nkv, S, hd, d.layer, 0, b, g, p) + lane + 64, 2, 2, "attn: K store at p");
+                }
+                for (int c0 = lo + PF; c0 < hi; c0 += 64) {
+                  const int nt = std::min(64, hi - c0);
+                  for (int kvt = 0; kvt < 2; ++kvt)
+                    for (int t0 = 0; t0 < nt; t0 += NR)
+                      for (int t = 0; t < NR; ++t) {
+                        const int tt = std::min(t0 + t, nt - 1);
+                        if (c0 + tt == p) continue;
+                        for (int m = 0; m < DPL; ++m)
+                          M.el(B.kv, (kvt ? Vr : Kr) + (uint64_t)(c0 - lo + tt) * hd + lane + 64 * m, 2, 2,
+                               "attn: K/V row of the long split");
+                      }
+                }
+              }
+              const uint64_t out = lay::part(MB, nq, ns, hd, d.layer, b, j, s);
+              for (int m = 0; m < DPL; ++m) M.el(B.part, out + lane + 64 * m, 4, 4, "attn: partial o");
+              if (lane == 0) {
+                M.el(B.part, out + hd, 4, 4, "attn: partial m");
+                M.el(B.part, out + hd + 1, 4, 4, "attn: partial l");
+              }
+            }
+          }
+          M.el(B.ctr, ((uint64_t)d.sig0 * kSlots + d.slot0) * kCtrStride, 4, 4, "attn: counter signal");
+        } else if (d.op == OP_RED) {
+          const int g = (int)d.aux0, DPL = hd / 64, RB = 32 / DPL;
+          const uint32_t rowb = (uint32_t)(hd + 4) * 4;
+          for (int h = 0; h < G; ++h) {
+            const int j = g * G + h;
+            const uint64_t base = B.part + lay::part(MB, nq, ns, hd, d.layer, b, j, 0) * 4;
+            for (int lane = 0; lane < 64; ++lane) {
+              if (lane < ns) {
+                M.at(base + (uint64_t)lane * rowb + hd * 4, 4, B.part, "red: m of a split");
+                M.at(base + (uint64_t)lane * rowb + hd * 4 + 4, 4, B.part, "red: l of a split");
+              }
+              for (int s0 = 0; s0 < ns; s0 += RB)
+                for (int t = 0; t < RB; ++t) {
+                  const int ss = std::min(s0 + t, ns - 1);
+                  for (int m = 0; m < DPL; ++m)
+                    M.at(base + (uint64_t)ss * rowb + (uint64_t)(lane + 64 * m) * 4, 4, B.part, "red: o of a split");
+                }
+              for (int m = 0; m < DPL; ++m)
+                M.el(B.attn, lay::attn(MB, nq, hd, d.layer, b) + (uint64_t)j * hd + lane + 64 * m, 4, 4,
+                     "red: attention output");
+            }
+          }
+          M.el(B.ctr, ((uint64_t)d.sig0 * kSlots + d.slot0) * kCtrStride, 4, 4, "red: counter signal");
+        } else {
+          // GEMV epilogue (the last compute wave), lanes stride the items
+          const int p = pos0;
+          for (uint32_t i = 0; i < d.n_items; ++i) {
+            switch (d.op) {
+              case OP_QKV: {
+                const uint32_t ppg = (uint32_t)(G + 2) * half, pp = d.item0 + i, g = pp / ppg, rr = pp - g * ppg;
+                const uint32_t hs = rr / half, ii = rr - hs * half;
+                if (hs <= (uint32_t)G && c.qk_norm) {
+                  const uint64_t dst = hs < (uint32_t)G ? lay::q(MB, nq, hd, d.layer, b, (int)(g * G + hs))
+                                                        : lay::kvn(MB, nkv, hd, d.layer, b, (int)g, 0);
+                  const uint64_t buf = hs < (uint32_t)G ? B.q : B.kvn;
+                  M.el(buf, dst + ii, 8, 8, "epilogue: raw q/k word");
+                  M.el(buf, dst + ii + half, 8, 8, "epilogue: raw q/k word");
+                } else if (hs < (uint32_t)G) {
+                  const uint64_t qo = lay::q(MB, nq, hd, d.layer, b, (int)(g * G + hs));
+                  M.el(B.q, qo + ii, 8, 8, "epilogue: q word");
+                  M.el(B.q, qo + ii + half, 8, 8, "epilogue: q word");
+                } else {
+                  const int t = hs == (uint32_t)G ? 0 : 1;
+                  const uint64_t ko = lay::kv(MB, nkv, S, hd, d.layer, t, b, (int)g, p);
+                  M.el(B.kv, ko + ii, 2, 2, "epilogue: K/V slot p");
+                  M.el(B.kv, ko + ii + half, 2, 2, "epilogue: K/V slot p");
+                  const uint64_t no = lay::kvn(MB, nkv, hd, d.layer, b, (int)g, t);
+                  M.el(B.kvn, no + ii, 8, 8, "epilogue: tagged K/V word");
+                  M.el(B.kvn, no + ii + half, 8, 8, "epilogue: tagged K/V word");
+                }
+                break;
+              }
+              case OP_O: M.el(B.h, lay::h(MB, H, 2 * d.layer + 1, b) + d.item0 + i, 4, 4, "epilogue: O rows"); break;
+              case OP_FFN: M.el(B.a, lay::a(MB, F, d.layer, b) + d.item0 + i, 4, 4, "epilogue: FFN rows"); break;
+              case OP_DOWN:
+                M.el(B.h, lay::h(MB, H, 2 * d.layer + 2, b) + d.item0 + i, 4, 4, "epilogue: down rows");
+                break;
+              default: M.el(B.logits, lay::logits(V, b) + d.item0 + i, 4, 4, "epilogue: logits"); break;
+            }
+          }
+          if (d.op == OP_LM) {
+            M.el(B.amax, d.unit, 8, 8, "epilogue: greedy candidate");
+            M.el(B.ctr, amax_word, 4, 4, "greedy: arrival counter");
+            for (uint32_t u = 0; u < n_lm; ++u) M.el(B.amax, u, 8, 8, "greedy: candidates");
+            M.el(B.next_tok, 0, 4, 4, "greedy: next token");
+            M.el(B.next_pos, 0, 4, 4, "greedy: next position");
+          }
+          for (int sg : {d.sig0, d.sig1})
+            if (sg >= 0) {
+              const uint32_t slot = sg == d.sig0 ? d.slot0 : d.slot1;
+              M.el(B.ctr, ((uint64_t)sg * kSlots + slot) * kCtrStride, 4, 4, "epilogue: counter signal");
+            }
+        }
+      }
+      // error path: status words
+      M.el(B.status, 0, 4, 12, "raise_error: status words");
+    }
+  }
+  if (rep) {
+    rep->accesses = M.n;
+    rep->violations = M.bad;
+    std::snprintf(rep->msg, sizeof rep->msg, "%s", M.first.c_str());
+  }
+  return M.bad ? MK_ERR_INVALID_ARG : MK_OK;
+}

@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mk_layout.hpp"
 #include "mk_plan.hpp"
 
 namespace mk {
@@ -159,6 +160,42 @@ __device__ __forceinline__ void wake() { asm volatile("s_wakeup" ::: "memory"); 
 #endif
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Ordering of the cross-CU protocol.  A producer's results are written with
+// device-coherent (sc1) stores, which complete at the device's coherence
+// point; `s_waitcnt vmcnt(0)` waits for their acknowledgements before the
+// counter increment is issued, so every result is visible device-wide before
+// the increment is (the release half).  A consumer's poll is a device-
+// coherent load whose value decides a branch, so the wave issues nothing
+// after the poll until its value has returned, and everything it reads of
+// other CUs' results afterwards is again a device-coherent load, which reads
+// the coherence point rather than a possibly stale cached copy (the acquire
+// half, for exactly the locations the consumer reads).  What the hardware
+// does not need, the compiler still could break: relaxed atomics do not stop
+// it from moving a later plain (buffer) load above the poll, so every poll
+// exit is a compiler fence.  MK_ACQ=1 adds the memory model's own agent-scope
+// acquire fence at every poll exit and a release fence before every counter
+// increment (measured cost in the design notes).
+#ifndef MK_ACQ
+#define MK_ACQ 0
+#endif
+__device__ __forceinline__ void poll_exit() {
+#if MK_ACQ
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#else
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#endif
+}
+__device__ __forceinline__ void before_signal() {
+#if MK_ACQ
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+#else
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#endif
+}
+// LDS flags order data within the workgroup: a compiler fence suffices (LDS
+// operations of one wave complete in order).
+__device__ __forceinline__ void lds_poll_exit() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // LDS control words for the C++ roles (sync and compute waves)
@@ -271,11 +308,17 @@ struct Watchdog {
 // set and polling does not flood the LDS queue or the issue slots.
 template <class F>
 __device__ __forceinline__ bool spin_lds(const Env &e, F cond, uint32_t info) {
-  if (cond()) return true;
+  if (cond()) {
+    lds_poll_exit();
+    return true;
+  }
   Watchdog wd;
   for (uint32_t it = 1;; ++it) {
     __builtin_amdgcn_s_sleep(MK_SLEEP);
-    if (cond()) return true;
+    if (cond()) {
+      lds_poll_exit();
+      return true;
+    }
     if ((it & 63) == 0) {
       if (lds_ld(L_ABORT)) return false;
       if (wd.expired(e.cp->watchdog_ticks)) {
@@ -290,11 +333,17 @@ __device__ __forceinline__ bool spin_lds(const Env &e, F cond, uint32_t info) {
 // waiter (a page sentinel written by a direct-to-LDS load).
 template <class F>
 __device__ __forceinline__ bool spin_lds_fast(const Env &e, F cond, uint32_t info) {
-  if (cond()) return true;
+  if (cond()) {
+    lds_poll_exit();
+    return true;
+  }
   Watchdog wd;
   for (uint32_t it = 1;; ++it) {
     __builtin_amdgcn_s_sleep(MK_FSLEEP);
-    if (cond()) return true;
+    if (cond()) {
+      lds_poll_exit();
+      return true;
+    }
     if ((it & 255) == 0) {
       if (lds_ld(L_ABORT)) return false;
       if (wd.expired(e.cp->watchdog_ticks)) {
@@ -311,7 +360,10 @@ template <class F>
 __device__ __forceinline__ bool until_tagged(const Env &e, F load, uint32_t info) {
   Watchdog wd;
   for (uint32_t it = 0;; ++it) {
-    if (__all(load())) return true;
+    if (__all(load())) {
+      poll_exit();
+      return true;
+    }
     if ((it & 63) == 63) {
       if (lds_ld(L_ABORT)) return false;
       if (wd.expired(e.cp->watchdog_ticks)) {
@@ -475,7 +527,10 @@ __device__ __forceinline__ bool wait_group(const Env &e, const Args &a, const Wa
   for (uint32_t it = 0;; ++it) {
     bool ok = true;
     if (mine) ok = (int32_t)(ld_cu(cp) - need) >= 0;
-    if (__all(ok)) return true;
+    if (__all(ok)) {
+      poll_exit();
+      return true;
+    }
     if ((it & 63) == 63) {
       if (lds_ld(L_ABORT)) return false;
       if (ld_cu(&e.cp->status[0]) != 0) { lds_st(L_ABORT, 1); return false; }
@@ -492,19 +547,18 @@ __device__ __forceinline__ bool wait_group(const Env &e, const Args &a, const Wa
 __device__ __forceinline__ void norm_src(const Env &e, const Args &a, const Instr &d, int b,
                                          const float *&h, const uint16_t *&emb, const uint16_t *&w) {
   const DevCtx &c = *e.cp;
-  const size_t HB = (size_t)c.max_batch * c.H;
   h = nullptr;
   emb = nullptr;
   if (d.op == OP_QKV) {
     w = G(c.layers)[d.layer].attn_norm;
     if (d.layer == 0) emb = c.embed + (size_t)a.tokens[b] * c.H;
-    else h = c.h_buf + (size_t)(2 * d.layer) * HB + (size_t)b * c.H;
+    else h = c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer, b);
   } else if (d.op == OP_FFN) {
     w = G(c.layers)[d.layer].ffn_norm;
-    h = c.h_buf + (size_t)(2 * d.layer + 1) * HB + (size_t)b * c.H;
+    h = c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer + 1, b);
   } else {  // OP_LM
     w = c.final_norm;
-    h = c.h_buf + (size_t)(2 * c.L) * HB + (size_t)b * c.H;
+    h = c.h_buf + lay::h(c.max_batch, c.H, 2 * c.L, b);
   }
 }
 
@@ -518,8 +572,7 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
     if (ps < 0 || ps >= c.max_seq) { raise_error(e, 0xE2000000u, (uint32_t)b); return; }
   }
   const int b = 0;
-  const int pos = a.positions[b];
-  const size_t HB = (size_t)c.max_batch * c.H;
+  const int pos = e.pos0;
   uint32_t seq = 0;
   float rs = 0.f;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
@@ -551,7 +604,7 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
       const uint32_t half = (uint32_t)c.hd >> 1, ppg = (uint32_t)(c.G + 2) * half;
       for (uint32_t i = (uint32_t)lane; i < d.n_items; i += 64) {
         const uint32_t ii = ((d.item0 + i) % ppg) % half;
-        const uint64_t cs = *G(reinterpret_cast<const uint64_t *>(c.rope + ((size_t)pos * half + ii) * 2));
+        const uint64_t cs = *G(reinterpret_cast<const uint64_t *>(c.rope + lay::rope(c.hd, pos, (int)ii)));
         accs[kAccFloats / 2 + 2 * i] = __uint_as_float((uint32_t)cs);
         accs[kAccFloats / 2 + 2 * i + 1] = __uint_as_float((uint32_t)(cs >> 32));
       }
@@ -569,10 +622,10 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
     // two pieces has landed.
     const bool dma_pieces = (d.op == OP_DOWN || (d.op == OP_O && d.layer > 0)) && d.n_items <= 64;
     if (dma_pieces) {
-      const uint32_t SB = d.op == OP_O ? (uint32_t)(c.nq * c.hd) : (uint32_t)c.F;
-      const float *src = (d.op == OP_O ? c.attn_buf : c.a_buf) + ((size_t)d.layer * c.max_batch + b) * SB;
-      const float *res = c.h_buf + (size_t)(d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1) * HB +
-                         (size_t)b * c.H + d.item0 + lane;
+      const float *src = d.op == OP_O ? c.attn_buf + lay::attn(c.max_batch, c.nq, c.hd, d.layer, b)
+                                      : c.a_buf + lay::a(c.max_batch, c.F, d.layer, b);
+      const float *res = c.h_buf + lay::h(c.max_batch, c.H, d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1, b) +
+                         d.item0 + lane;
       LDS_AS char *accl = (LDS_AS char *)smem + L_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4;
       auto issue = [&](uint32_t k, uint32_t sq) {
         if (k == 0 && lane < (int)d.n_items) __builtin_amdgcn_global_load_lds(res, (LDS_AS void *)accl, 4, 0, kSC1);
@@ -710,9 +763,8 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
       } else if (d.op == OP_O || d.op == OP_DOWN) {
         // the activation piece and (first piece) the unit's residual rows,
         // loaded together: one round trip
-        const float *src = d.op == OP_O
-                               ? c.attn_buf + ((size_t)d.layer * c.max_batch + b) * (c.nq * c.hd)
-                               : c.a_buf + ((size_t)d.layer * c.max_batch + b) * c.F;
+        const float *src = d.op == OP_O ? c.attn_buf + lay::attn(c.max_batch, c.nq, c.hd, d.layer, b)
+                                        : c.a_buf + lay::a(c.max_batch, c.F, d.layer, b);
         const rsrc_t sr = rsrc(src + k * d.kc);
         f4 v[8];
 #pragma unroll
@@ -731,7 +783,7 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
             }
           } else {
             const int idx = d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1;
-            const rsrc_t rr = rsrc(c.h_buf + (size_t)idx * HB + (size_t)b * c.H + d.item0);
+            const rsrc_t rr = rsrc(c.h_buf + lay::h(c.max_batch, c.H, idx, b) + d.item0);
 #pragma unroll
             for (int m = 0; m < kAccFloats / 64; ++m) {
               const uint32_t r = (uint32_t)(lane + 64 * m);
@@ -819,7 +871,7 @@ __device__ __forceinline__ void load_x(const float *xs, uint32_t n16, float (&xr
 }
 
 __device__ __forceinline__ size_t kv_off(const DevCtx &c, int l, int t, int b, int g, int s) {
-  return ((((size_t)l * 2 + t) * c.max_batch + b) * c.nkv + g) * (size_t)c.max_seq * c.hd + (size_t)s * c.hd;
+  return lay::kv(c.max_batch, c.nkv, c.max_seq, c.hd, l, t, b, g, s);
 }
 
 // Epilogue of a finished GEMV instruction, run by its last compute wave
@@ -853,7 +905,6 @@ __device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
   const int b = 0;
-  const size_t HB = (size_t)c.max_batch * c.H;
   for (uint32_t i = (uint32_t)lane; i < d.n_items; i += 64) {
     switch (d.op) {
       case OP_QKV: {
@@ -871,15 +922,15 @@ __device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const
           // units: q and k leave raw (un-normed, un-rotated) and the
           // attention units norm and rotate them (and write K to the cache)
           uint64_t *dst = hs < (uint32_t)c.G
-                              ? c.q_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + (g * c.G + hs)) * c.hd
-                              : c.kvn_buf + (((size_t)d.layer * c.max_batch + b) * c.nkv + g) * 2 * c.hd;
+                              ? c.q_buf + lay::q(c.max_batch, c.nq, c.hd, d.layer, b, (int)(g * c.G + hs))
+                              : c.kvn_buf + lay::kvn(c.max_batch, c.nkv, c.hd, d.layer, b, (int)g, 0);
           st_tag(dst + ii, v0, a.tag);
           st_tag(dst + ii + half, v1, a.tag);
         } else if (hs <= (uint32_t)c.G) {
           const float cs = R[kAccFloats / 2 + 2 * i], sn = R[kAccFloats / 2 + 2 * i + 1];
           const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
           if (hs < (uint32_t)c.G) {
-            uint64_t *q = c.q_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + (g * c.G + hs)) * c.hd;
+            uint64_t *q = c.q_buf + lay::q(c.max_batch, c.nq, c.hd, d.layer, b, (int)(g * c.G + hs));
             st_tag(q + ii, r0, a.tag);
             st_tag(q + ii + half, r1, a.tag);
           } else {
@@ -887,7 +938,7 @@ __device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const
             const uint16_t k0 = f2bf(r0), k1 = f2bf(r1);
             st_c16(k + ii, k0);
             st_c16(k + ii + half, k1);
-            uint64_t *kn = c.kvn_buf + (((size_t)d.layer * c.max_batch + b) * c.nkv + g) * 2 * c.hd;
+            uint64_t *kn = c.kvn_buf + lay::kvn(c.max_batch, c.nkv, c.hd, d.layer, b, (int)g, 0);
             st_tag(kn + ii, bf16f(k0), a.tag);
             st_tag(kn + ii + half, bf16f(k1), a.tag);
           }
@@ -896,25 +947,25 @@ __device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const
           const uint16_t u0 = f2bf(v0), u1 = f2bf(v1);
           st_c16(v + ii, u0);
           st_c16(v + ii + half, u1);
-          uint64_t *vn = c.kvn_buf + ((((size_t)d.layer * c.max_batch + b) * c.nkv + g) * 2 + 1) * c.hd;
+          uint64_t *vn = c.kvn_buf + lay::kvn(c.max_batch, c.nkv, c.hd, d.layer, b, (int)g, 1);
           st_tag(vn + ii, bf16f(u0), a.tag);
           st_tag(vn + ii + half, bf16f(u1), a.tag);
         }
         break;
       }
       case OP_O:
-        st_c(c.h_buf + (size_t)(2 * d.layer + 1) * HB + (size_t)b * c.H + d.item0 + i, R[i]);
+        st_c(c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer + 1, b) + d.item0 + i, R[i]);
         break;
       case OP_FFN: {
         const float gt = R[2 * i], up = R[2 * i + 1];
-        st_c(c.a_buf + ((size_t)d.layer * c.max_batch + b) * c.F + d.item0 + i, gt / (1.0f + expf(-gt)) * up);
+        st_c(c.a_buf + lay::a(c.max_batch, c.F, d.layer, b) + d.item0 + i, gt / (1.0f + expf(-gt)) * up);
         break;
       }
       case OP_DOWN:
-        st_c(c.h_buf + (size_t)(2 * d.layer + 2) * HB + (size_t)b * c.H + d.item0 + i, R[i]);
+        st_c(c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer + 2, b) + d.item0 + i, R[i]);
         break;
       default:  // OP_LM
-        G(a.logits)[(size_t)b * c.V + d.item0 + i] = R[i];
+        G(a.logits)[lay::logits(c.V, b) + d.item0 + i] = R[i];
         break;
     }
   }
@@ -941,10 +992,12 @@ __device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const
 __device__ __forceinline__ void lm_greedy_finish(const Env &e, const Args &a) {
   const int lane = lane_id();
   uint32_t o = 0;
+  before_signal();
   if (lane == 0)
     o = __hip_atomic_fetch_add(G(a.amax_ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   o = __builtin_amdgcn_readfirstlane(o);
   if (o + 1u != a.amax_target) return;
+  poll_exit();  // the candidates read below were acknowledged before their units counted
   const rsrc_t r = rsrc(a.amax);
   float bv = -INFINITY;
   uint32_t bi = 0xffffffffu;
@@ -1003,7 +1056,7 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Ga
         qnw[m] = bf16f(G(qn)[lane + 64 * m]);
         knw[m] = bf16f(G(kn)[lane + 64 * m]);
       }
-      const uint64_t csw = *G(reinterpret_cast<const uint64_t *>(c.rope + ((size_t)p * 64 + lane) * 2));
+      const uint64_t csw = *G(reinterpret_cast<const uint64_t *>(c.rope + lay::rope(hd, p, lane)));
       rc = __uint_as_float((uint32_t)csw);
       rsn = __uint_as_float((uint32_t)(csw >> 32));
     }
@@ -1015,10 +1068,10 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Ga
   for (int m = 0; m < DPL; ++m) o[m] = 0.f;
   if (lo < hi) {
     // lane = head dimension (dims lane + 64*m) for q, K and V
-    const rsrc_t qr = rsrc(c.q_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + j) * hd);
+    const rsrc_t qr = rsrc(c.q_buf + lay::q(c.max_batch, c.nq, hd, d.layer, b, j));
     // the new slot p (written this step) comes from the tagged copy, never
     // from the cache
-    const rsrc_t nr = rsrc(c.kvn_buf + (((size_t)d.layer * c.max_batch + b) * c.nkv + g) * 2 * hd);
+    const rsrc_t nr = rsrc(c.kvn_buf + lay::kvn(c.max_batch, c.nkv, hd, d.layer, b, g, 0));
     const bool has_p = p < hi;
     float kraw[DPL];
     auto load = [&]() -> bool {
@@ -1145,7 +1198,7 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Ga
       mrun = mn;
     }
   }
-  float *out = a.part_buf + ((((size_t)d.layer * c.max_batch + b) * c.nq + j) * a.n_split + s) * (hd + 4);
+  float *out = a.part_buf + lay::part(c.max_batch, c.nq, a.n_split, hd, d.layer, b, j, s);
 #pragma unroll
   for (int m = 0; m < DPL; ++m) st_c(out + lane + 64 * m, o[m]);
   if (lane == 0) {
@@ -1166,7 +1219,7 @@ __device__ __forceinline__ void red_body(const Env &e, const Args &a, const Inst
   const int j = g * c.G + h;
   constexpr int hd = 64 * DPL, dpl = DPL;
   const int ns = a.n_split;
-  const float *base = a.part_buf + (((size_t)d.layer * c.max_batch + b) * c.nq + j) * (size_t)ns * (hd + 4);
+  const float *base = a.part_buf + lay::part(c.max_batch, c.nq, ns, hd, d.layer, b, j, 0);
   const rsrc_t pr = rsrc(base);
   const uint32_t rowb = (uint32_t)(hd + 4) * 4;
   // m, l of every split and the first RB splits' o in one round trip
@@ -1206,7 +1259,7 @@ __device__ __forceinline__ void red_body(const Env &e, const Args &a, const Inst
       for (int m = 0; m < dpl; ++m) o[m] = fmaf(w, ov[t][m], o[m]);
     }
   }
-  float *out = c.attn_buf + ((size_t)d.layer * c.max_batch + b) * (c.nq * hd) + (size_t)j * hd;
+  float *out = c.attn_buf + lay::attn(c.max_batch, c.nq, hd, d.layer, b) + (size_t)j * hd;
 #pragma unroll
   for (int m = 0; m < dpl; ++m) st_c(out + lane + 64 * m, o[m] / L);
 }
@@ -1311,6 +1364,7 @@ __device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw
         if (d.op != OP_QKV) wait_vm0();
       }
       if (d.op == OP_LM && a.next_tok) lm_greedy_finish(e, a);
+      before_signal();
       if (lane == 0) {
         trace_now(e, qi, 3);
         lds_st(L_DONE + 4 * (qi & 3), 0);

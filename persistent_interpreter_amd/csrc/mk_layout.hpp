@@ -1,0 +1,71 @@
+// mk_layout.hpp -- element offsets of every buffer the decode kernel
+// addresses, as plain index arithmetic usable on the host and the device.
+//
+// The kernel forms each global address as  base + offset(...)  with the
+// offsets below, and the host-side address model (mk_addr.cpp) evaluates the
+// same functions for every (unit, wave, lane, step) of a plan and checks the
+// result against the extent of the buffer it must fall in.  Keeping the
+// arithmetic in one place means the model cannot drift from the kernel on a
+// retyped formula; what the model mirrors by hand is only the loop
+// structure of each instruction body.
+//
+// Layouts (elements, row-major):
+//   kv cache  bf16 [L][2][max_batch][n_kv][max_seq][hd]   (0 = K, 1 = V)
+//   h         fp32 [2L+1][max_batch][H]  (index 2l: input of layer l,
+//                                         2l+1: after attention, 2L: final)
+//   q         u64  [L][max_batch][n_q][hd]       tagged words
+//   kvn       u64  [L][max_batch][n_kv][2][hd]   tagged words, this step's slot
+//   attn      fp32 [L][max_batch][n_q*hd]
+//   a         fp32 [L][max_batch][F]
+//   partials  fp32 [L][max_batch][n_q][n_split][hd+4]  (o[hd], m, l, pad)
+//   rope      fp32 [max_seq][hd/2][2]                  (cos, sin)
+//   logits    fp32 [batch][V]
+//   counters  u32  [n_groups][kSlots][kCtrStride]
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__HIPCC__) || defined(__HIP__)
+#define MK_HD __host__ __device__ __forceinline__
+#else
+#define MK_HD inline
+#endif
+
+namespace mk {
+namespace lay {
+
+MK_HD size_t kv(int MB, int nkv, int S, int hd, int l, int t, int b, int g, int s) {
+  return ((((size_t)l * 2 + t) * MB + b) * nkv + g) * (size_t)S * hd + (size_t)s * hd;
+}
+MK_HD size_t kv_size(int L, int MB, int nkv, int S, int hd) { return (size_t)L * 2 * MB * nkv * S * hd; }
+
+MK_HD size_t h(int MB, int H, int idx, int b) { return ((size_t)idx * MB + b) * H; }
+MK_HD size_t h_size(int L, int MB, int H) { return (size_t)(2 * L + 1) * MB * H; }
+
+MK_HD size_t q(int MB, int nq, int hd, int l, int b, int j) { return (((size_t)l * MB + b) * nq + j) * hd; }
+MK_HD size_t q_size(int L, int MB, int nq, int hd) { return (size_t)L * MB * nq * hd; }
+
+MK_HD size_t kvn(int MB, int nkv, int hd, int l, int b, int g, int t) {
+  return ((((size_t)l * MB + b) * nkv + g) * 2 + t) * hd;
+}
+MK_HD size_t kvn_size(int L, int MB, int nkv, int hd) { return (size_t)L * MB * nkv * 2 * hd; }
+
+MK_HD size_t attn(int MB, int nq, int hd, int l, int b) { return ((size_t)l * MB + b) * ((size_t)nq * hd); }
+MK_HD size_t attn_size(int L, int MB, int nq, int hd) { return (size_t)L * MB * nq * hd; }
+
+MK_HD size_t a(int MB, int F, int l, int b) { return ((size_t)l * MB + b) * F; }
+MK_HD size_t a_size(int L, int MB, int F) { return (size_t)L * MB * F; }
+
+// One partial record is hd + 4 floats: o[0..hd), m, l, two words of padding.
+MK_HD size_t part(int MB, int nq, int ns, int hd, int l, int b, int j, int s) {
+  return ((((size_t)l * MB + b) * nq + j) * ns + s) * (size_t)(hd + 4);
+}
+MK_HD size_t part_size(int L, int MB, int nq, int ns, int hd) { return (size_t)L * MB * nq * ns * (hd + 4); }
+
+MK_HD size_t rope(int hd, int p, int i) { return ((size_t)p * (hd / 2) + i) * 2; }
+MK_HD size_t rope_size(int S, int hd) { return (size_t)S * hd; }
+
+MK_HD size_t logits(int V, int b) { return (size_t)b * V; }
+
+}  // namespace lay
+}  // namespace mk

@@ -1,0 +1,68 @@
+"""Host address model of the decode kernel (mk_addr_check): every global
+access of every role, per lane, for every unit and step of a plan lies in the
+buffer it addresses.  This gates each kernel path before it runs on a GPU.
+
+The model's own sensitivity is pinned by planting size errors: a buffer one
+record short must be reported at the access site that reaches that record."""
+import pytest
+
+from persistent_interpreter_amd import binding as B, synth
+
+CUS = 256
+
+
+def _check(name, steps, batch=None, corrupt=0, **over):
+    mc = synth.CONFIGS[name]
+    if over:
+        mc = mc.replace(**over)
+    batch = batch or mc.batch
+    cfg = B.make_config(mc, max_batch=batch)
+    pos = synth.make_positions(mc, batch)
+    tok = synth.make_tokens(mc, batch)
+    return B.addr_check(cfg, batch, CUS, steps, pos, tok, corrupt)
+
+
+@pytest.mark.parametrize("name,steps", [("tiny", 32), ("tiny_qk", 32), ("llama1b", 2),
+                                        ("qwen3_8b", 1)])
+def test_every_access_in_bounds(name, steps):
+    """All steps of a greedy run (positions p .. p+steps-1, the last one the
+    cache's final slot for the tiny shapes)."""
+    rc, rep = _check(name, steps)
+    assert rep.accesses > 0
+    assert rc == 0 and rep.violations == 0, rep.msg.decode()
+
+
+def test_last_slot_and_position_zero():
+    """The first and the last cache slot (an empty cache; a full one)."""
+    mc = synth.CONFIGS["tiny_qk"]
+    cfg = B.make_config(mc)
+    for p in (0, mc.max_seq - 1):
+        rc, rep = B.addr_check(cfg, 1, CUS, 1, [p], [mc.vocab - 1])
+        assert rc == 0, (p, rep.msg.decode())
+
+
+def test_fewer_workgroups_and_splits():
+    """Other schedules of the same shape: 8 workgroups, 1 and 5 KV splits."""
+    mc = synth.CONFIGS["tiny_qk"]
+    for cus, splits in ((8, 0), (CUS, 1), (CUS, 5)):
+        cfg = B.make_config(mc, kv_splits=splits)
+        rc, rep = B.addr_check(cfg, 1, cus, 4, synth.make_positions(mc),
+                               synth.make_tokens(mc))
+        assert rc == 0, (cus, splits, rep.msg.decode())
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_qk"])
+@pytest.mark.parametrize("corrupt,site", [(1, "kv_cache"), (2, "partials"), (3, "rope"),
+                                          (4, "q"), (5, "h")])
+def test_planted_size_errors_are_found(name, corrupt, site):
+    rc, rep = _check(name, 32, corrupt=corrupt)
+    msg = rep.msg.decode()
+    assert rc != 0 and rep.violations > 0
+    assert f"at {site}+" in msg, msg
+
+
+def test_bad_arguments():
+    mc = synth.CONFIGS["tiny"]
+    cfg = B.make_config(mc)
+    assert B.addr_check(cfg, 1, CUS, 0, [16], [1])[0] == B.MK_ERR_INVALID_ARG
+    assert B.addr_check(cfg, 2, CUS, 1, [16, 16], [1, 1])[0] != 0   # batch > max_batch
