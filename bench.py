@@ -23,9 +23,13 @@ on a bounded sample of the same workload.
     python bench.py [--gpus 1] [--steps 32] [--warmup 3] [--workload llama1b]
 
 ``--workload llama1b_b8`` times the same shape at batch 8 (positions seeded
-per sequence in [1024, 4096]); a step there is one launch per sequence, back
-to back on the stream, and ``roofline`` prices the whole step's algorithmic
-bytes (every weight once, each sequence's K/V) over the step's duration.
+per sequence in [1024, 4096]); a step there is one launch of the batched
+kernel, whose projections run on the matrix cores (bf16 hi + lo activation
+splits), and ``roofline`` prices the whole step's algorithmic bytes (every
+weight once, each sequence's K/V) over the step's duration; ``mfma_util``
+gives the useful projection FLOP (2 x batch x weights) and the FLOP the
+MFMA instructions issue (16 A rows: hi and lo of up to 8 sequences, tiles
+padded to 16 weight rows) over the bf16 dense peak times the step time.
 """
 from __future__ import annotations
 
@@ -41,6 +45,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 METRIC = "decode tokens/s at batch 1 (Llama-1B shape) + % of peak HBM GB/s"
 H100_STEP_S = 1.0e-3   # the pages' ~1 ms Llama-1B batch-1 forward on H100
 
@@ -153,6 +158,24 @@ def cpu_baseline(mc, W, kv0, tok, pos, fed, gpu_logits, budget_s=20.0):
                        f"oracle, weights decoded to fp32 once beforehand), median "
                        f"{med * 1e3:.1f} ms/step"},
             {"max_abs_dlogit": worst, "greedy_match": f"{match}/{n}"})
+
+
+def mfma_util(mc, t_step: float) -> dict:
+    """MFMA utilisation of a batched step: useful projection FLOP
+    (2 x batch x projection weights) and the FLOP the 16x16x32 MFMAs issue
+    (16 A rows, units' rows padded to 16-row tiles, K padded to 256), each
+    over the dense bf16 peak times the step time."""
+    from persistent_interpreter_amd import binding as B
+    params = (mc.weight_bytes() // 2) - mc.hidden * (2 * mc.n_layers + 1)  # minus norm weights
+    useful = 2.0 * mc.batch * params
+    cfg = B.make_config(mc, max_batch=mc.batch)
+    rc, rep = B.plan_check(cfg, mc.batch, 256)
+    issued = 2.0 * 16 * rep.mfma_cols_k if rc == 0 else None
+    peak = PEAK_BF16_TFLOPS * 1e12 * t_step
+    return {"useful_tflop_per_step": round(useful / 1e12, 4),
+            "useful_frac": round(useful / peak, 5),
+            "issued_frac": round(issued / peak, 5) if issued else None,
+            "peak_tflops": PEAK_BF16_TFLOPS}
 
 
 STREAM_BYTES = 2 << 30
@@ -287,8 +310,7 @@ def main():
                                f"FFN {mc.ffn_dim}, vocab {mc.vocab}, batch {mc.batch}, "
                                f"{prior} prior KV positions, greedy (in-kernel argmax)",
                    "batch": mc.batch, "prior_positions": prior, "accumulate": "fp32",
-                   "parallelism": "1 GPU, 1 persistent launch per step"
-                                  + ("" if mc.batch == 1 else " per sequence")},
+                   "parallelism": "1 GPU, 1 persistent launch per step"},
         "kernel_us": {"mean": round(t_kern * 1e6, 2),
                       "median": round(float(np.median(kern)) * 1e6, 2),
                       "p10": round(float(np.percentile(kern, 10)) * 1e6, 2),
@@ -302,10 +324,12 @@ def main():
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": stored_traffic(args.workload),
-                     "kernel": "mk::mk_interp",
-                     "launches_per_step": mc.batch,
+                     "kernel": "mk::mk_interp" if mc.batch == 1 else "mk::mk_interp_b",
+                     "launches_per_step": 1,
                      "bytes_per_step": int(bytes_per)},
     }
+    if mc.batch > 1:
+        out["mfma_util"] = mfma_util(mc, t_kern)
     if not args.no_cpu:
         cpu, parity = cpu_baseline(mc, W, kv0, tok, pos, fed, gpu_logits)
         out["cpu_baseline"] = cpu

@@ -177,6 +177,10 @@ typedef struct mk_plan_report {
   int32_t max_queue;          /* longest per-CU queue                        */
   int64_t weight_bytes;       /* bf16 weight bytes streamed per step         */
   int64_t max_cu_bytes;       /* largest per-CU weight stream                */
+  int64_t mfma_cols_k;        /* batched plans: sum over units of weight rows
+                                 padded to 16-row tiles x K padded to 256
+                                 (the 16x16x32 MFMAs issue 2*16 FLOP per
+                                 unit of this); 0 for batch-1 plans          */
   int32_t sim_runs;           /* interleavings simulated                     */
   int32_t sim_errors;         /* missing dependencies or deadlocks found     */
   char    msg[256];           /* first error found, if any                   */
@@ -263,7 +267,8 @@ int mk_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 size_t mk_stream_read_sink_words(void);
 
 /* mk_version -- ABI version of this header (major*100 + minor): 101 adds
- * mk_decode_step_greedy, 102 mk_stream_read. */
+ * mk_decode_step_greedy, 102 mk_stream_read, 103 mk_addr_check, the batched
+ * (MFMA) kernel and mk_plan_report.mfma_cols_k. */
 int mk_version(void);
 
 #ifdef __cplusplus

@@ -69,6 +69,7 @@ class MkPlanReport(C.Structure):
                 ("n_instr", C.c_int32), ("n_groups", C.c_int32),
                 ("n_pages", C.c_int32), ("max_queue", C.c_int32),
                 ("weight_bytes", C.c_int64), ("max_cu_bytes", C.c_int64),
+                ("mfma_cols_k", C.c_int64),
                 ("sim_runs", C.c_int32), ("sim_errors", C.c_int32),
                 ("msg", C.c_char * 256)]
 

@@ -41,6 +41,7 @@ struct DevPlan {
   uint32_t trace_stride = 0;
   uint32_t epoch = 0;
   uint32_t n_lm = 0;
+  uint32_t n_arrive = 0;       // greedy candidates (and arrivals) per step
   uint32_t greedy_epoch = 0;   // greedy steps since the counters were zeroed
 };
 
@@ -108,6 +109,7 @@ struct mk_handle {
   float *h_buf = nullptr, *attn_buf = nullptr, *a_buf = nullptr;
   uint64_t *q_buf = nullptr, *kvn_buf = nullptr;  // tagged words, see DevCtx
   float *rope = nullptr;
+  uint16_t *zero = nullptr;  // zeros read for weights past K in padded MFMA pieces
   uint32_t *status = nullptr;
   size_t h_bytes = 0, q_bytes = 0, attn_bytes = 0, a_bytes = 0, kvn_bytes = 0;
   std::map<int, std::unique_ptr<DevPlan>> plans;
@@ -118,7 +120,7 @@ struct mk_handle {
 
 extern "C" {
 
-int mk_version(void) { return 102; }
+int mk_version(void) { return 103; }
 
 const char *mk_strerror(int code) {
   switch (code) {
@@ -164,6 +166,10 @@ int mk_plan_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int32_t 
     rep->max_queue = mq;
     rep->weight_bytes = plan.weight_bytes;
     rep->max_cu_bytes = plan.max_cu_bytes;
+    rep->mfma_cols_k = 0;
+    if (batch > 1)
+      for (const Instr &in : plan.instr)
+        if (in.pages) rep->mfma_cols_k += (int64_t)((in.ppp + 1) / 2) * 16 * in.nk * kMfmaKc;
   }
   return check_plan(*cfg, plan, sim_runs, corrupt, seed, rep);
 }
@@ -233,12 +239,14 @@ int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out) {
   if ((rc = dev_alloc(&h->h_buf, h->h_bytes)) || (rc = dev_alloc(&h->q_buf, h->q_bytes)) ||
       (rc = dev_alloc(&h->attn_buf, h->attn_bytes)) || (rc = dev_alloc(&h->a_buf, h->a_bytes)) ||
       (rc = dev_alloc(&h->kvn_buf, h->kvn_bytes)) || (rc = upload(&h->rope, rope)) ||
+      (rc = dev_alloc(&h->zero, 1024)) ||
       (rc = dev_alloc(&h->status, 256)) || (rc = upload(&h->d_layers, dl))) {
     mk_destroy(h.release());
     return rc;
   }
   // tag 0 never matches a step's tag (tags start at 1)
-  if (hipMemset(h->status, 0, 256) != hipSuccess || hipMemset(h->h_buf, 0, h->h_bytes) != hipSuccess ||
+  if (hipMemset(h->status, 0, 256) != hipSuccess || hipMemset(h->zero, 0, 1024) != hipSuccess ||
+      hipMemset(h->h_buf, 0, h->h_bytes) != hipSuccess ||
       hipMemset(h->q_buf, 0, h->q_bytes) != hipSuccess || hipMemset(h->attn_buf, 0, h->attn_bytes) != hipSuccess ||
       hipMemset(h->a_buf, 0, h->a_bytes) != hipSuccess || hipMemset(h->kvn_buf, 0, h->kvn_bytes) != hipSuccess) {
     mk_destroy(h.release());
@@ -259,6 +267,7 @@ int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out) {
   c.h_buf = h->h_buf; c.q_buf = h->q_buf; c.attn_buf = h->attn_buf; c.a_buf = h->a_buf;
   c.kvn_buf = h->kvn_buf;
   c.rope = h->rope;
+  c.zero = h->zero;
   c.status = h->status;
   c.trace = nullptr;
   c.ring_pages = kRingPages;
@@ -278,6 +287,8 @@ static int get_plan(mk_handle *h, int batch, DevPlan **out) {
     *out = it->second.get();
     return MK_OK;
   }
+  // the batched (MFMA) kernel has no per-head q/k norm
+  if (batch > 1 && h->cfg.qk_norm) return MK_ERR_UNSUPPORTED;
   auto dp = std::make_unique<DevPlan>();
   std::string err;
   int rc = build_plan(h->cfg, batch, h->num_cus, dp->plan, err);
@@ -291,6 +302,9 @@ static int get_plan(mk_handle *h, int batch, DevPlan **out) {
   dp->amax_word = (size_t)P.n_groups * kSlots * kCtrStride;
   dp->ctr_bytes = (dp->amax_word + kCtrStride) * 4;
   for (const Instr &in : P.instr) dp->n_lm += in.op == OP_LM ? 1u : 0u;
+  // greedy arrivals per step: one per LM unit (batch 1), one per workgroup
+  // holding LM units (batched)
+  dp->n_arrive = batch > 1 ? (uint32_t)P.n_lm_groups : dp->n_lm;
   const size_t part =
       lay::part_size(h->cfg.n_layers, h->cfg.max_batch, h->cfg.n_q_heads, P.n_split, h->cfg.head_dim) * 4;
   // page sentinels: iota[i] = i for every page index of the longest queue
@@ -341,55 +355,48 @@ static int launch_step(mk_handle *h, int32_t batch, const int32_t *tokens, const
                        void *stream) {
   if (!h || !tokens || !positions || !kv_cache || !logits) return MK_ERR_INVALID_ARG;
   if (batch < 1 || batch > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
-  // One launch of the one-sequence schedule per sequence, back to back on the
-  // stream.  Sequence s reads tokens[s] and positions[s], writes logits row
-  // s and its own cache slice: in the cache layout [L][2][max_batch][n_kv]
-  // [max_seq][head_dim] the slice of sequence s starts n_kv*max_seq*head_dim
-  // elements after that of sequence 0 in every (layer, K/V) block, so moving
-  // the base by that much addresses it with the one-sequence offsets.
+  // One launch for the whole batch: the batch-1 kernel (GEMV on the vector
+  // units) or, for 2..8 sequences, the batched kernel (MFMA), each running
+  // its batch size's plan.
   DevPlan *dp = nullptr;
-  int rc = get_plan(h, 1, &dp);
+  int rc = get_plan(h, batch, &dp);
   if (rc) return rc;
-  const size_t kv_seq = (size_t)h->cfg.n_kv_heads * h->cfg.max_seq * h->cfg.head_dim;
-  for (int32_t s = 0; s < batch; ++s) {
-    dp->epoch += 1;
-    Args a;
-    a.ctx = h->d_ctx;
-    a.instr = dp->d_instr;
-    a.q_off = dp->d_qoff;
-    a.waits = dp->d_waits;
-    a.rowtab = dp->d_rowtab;
-    a.ctr = dp->d_ctr;
-    a.grp_target = dp->d_target;
-    a.part_buf = dp->d_part;
-    a.iota = dp->d_iota;
-    a.tokens = tokens + s;
-    a.positions = positions + s;
-    a.kv = (uint16_t *)kv_cache + (size_t)s * kv_seq;
-    a.logits = logits + (size_t)s * h->cfg.vocab;
-    a.trace = dp->d_trace;
-    a.trace_stride = dp->trace_stride;
-    h->last_plan = dp;
-    a.epoch = dp->epoch;
-    h->tag = h->tag + 1 == 0 ? 1 : h->tag + 1;
-    a.tag = h->tag;
-    a.batch = 1;
-    a.n_split = dp->plan.n_split;
-    a.split_len = dp->plan.split_len;
-    a.amax = dp->d_amax;
-    a.amax_ctr = dp->d_ctr + dp->amax_word;
-    a.next_tok = next_tokens ? next_tokens + s : nullptr;
-    a.next_pos = next_positions ? next_positions + s : nullptr;
-    a.n_lm = dp->n_lm;
-    a.amax_target = 0;
-    if (next_tokens) {
-      dp->greedy_epoch += 1;
-      a.amax_target = dp->greedy_epoch * dp->n_lm;
-    }
-    if (kernel_launch(a, h->num_cus, (h->cfg.flags & MK_FLAG_COOPERATIVE) != 0, (hipStream_t)stream) !=
-        hipSuccess)
-      return MK_ERR_HIP;
+  dp->epoch += 1;
+  Args a;
+  a.ctx = h->d_ctx;
+  a.instr = dp->d_instr;
+  a.q_off = dp->d_qoff;
+  a.waits = dp->d_waits;
+  a.rowtab = dp->d_rowtab;
+  a.ctr = dp->d_ctr;
+  a.grp_target = dp->d_target;
+  a.part_buf = dp->d_part;
+  a.iota = dp->d_iota;
+  a.tokens = tokens;
+  a.positions = positions;
+  a.kv = (uint16_t *)kv_cache;
+  a.logits = logits;
+  a.trace = dp->d_trace;
+  a.trace_stride = dp->trace_stride;
+  h->last_plan = dp;
+  a.epoch = dp->epoch;
+  h->tag = h->tag + 1 == 0 ? 1 : h->tag + 1;
+  a.tag = h->tag;
+  a.batch = batch;
+  a.n_split = dp->plan.n_split;
+  a.split_len = dp->plan.split_len;
+  a.amax = dp->d_amax;
+  a.amax_ctr = dp->d_ctr + dp->amax_word;
+  a.next_tok = next_tokens;
+  a.next_pos = next_positions;
+  a.n_lm = dp->n_arrive;
+  a.amax_target = 0;
+  if (next_tokens) {
+    dp->greedy_epoch += 1;
+    a.amax_target = dp->greedy_epoch * dp->n_arrive;
   }
+  if (kernel_launch(a, h->num_cus, (h->cfg.flags & MK_FLAG_COOPERATIVE) != 0, (hipStream_t)stream) != hipSuccess)
+    return MK_ERR_HIP;
   return MK_OK;
 }
 
@@ -436,6 +443,7 @@ void mk_destroy(mk_handle *h) {
   hipFree(h->a_buf);
   hipFree(h->kvn_buf);
   hipFree(h->rope);
+  hipFree(h->zero);
   hipFree(h->status);
   delete h;
 }

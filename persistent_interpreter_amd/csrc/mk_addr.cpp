@@ -74,11 +74,278 @@ struct Model {
 struct Bases {
   uint64_t tokens, positions, kv, logits, next_tok, next_pos;
   uint64_t h, q, kvn, attn, a, part, rope, status, ctr, target, amax, rowtab, iota;
-  uint64_t embed, lm_head, final_norm;
+  uint64_t embed, lm_head, final_norm, zero;
   std::vector<uint64_t> attn_norm, q_norm, k_norm, ffn_norm;
 };
 
 }  // namespace
+
+// The batched (MFMA) kernel: sync_role_b, loader_role_b, compute_role_b and
+// unit_epilogue_b of mk_kernel.hip.
+static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_config &c, int batch, int num_cus,
+                         const std::vector<int> &pos_in, const int32_t *tokens, bool inputs_ok) {
+  const int L = c.n_layers, H = c.hidden, nq = c.n_q_heads, nkv = c.n_kv_heads, hd = c.head_dim;
+  const int F = c.ffn_dim, V = c.vocab, MB = c.max_batch, S = c.max_seq, G = nq / nkv, half = hd / 2;
+  const int ns = P.n_split;
+  std::vector<int> pos(batch);
+  for (int b = 0; b < batch; ++b) pos[b] = (pos_in[b] < 0 || pos_in[b] >= S) ? 0 : pos_in[b];
+  auto is_gemv = [](uint8_t op) { return op == OP_QKV || op == OP_O || op == OP_FFN || op == OP_DOWN || op == OP_LM; };
+  // input vector of a normed instruction for sequence b (norm_src)
+  auto norm_src = [&](const Instr &d, int b, uint64_t &h, uint64_t &emb, uint64_t &nw) {
+    h = emb = 0;
+    if (d.op == OP_QKV) {
+      nw = B.attn_norm[d.layer];
+      if (d.layer == 0) emb = B.embed + (uint64_t)tokens[b] * H * 2;
+      else h = B.h + lay::h(MB, H, 2 * d.layer, b) * 4;
+    } else if (d.op == OP_FFN) {
+      nw = B.ffn_norm[d.layer];
+      h = B.h + lay::h(MB, H, 2 * d.layer + 1, b) * 4;
+    } else {
+      nw = B.final_norm;
+      h = B.h + lay::h(MB, H, 2 * L, b) * 4;
+    }
+  };
+  for (int cu = 0; cu < num_cus; ++cu) {
+    const uint32_t q0 = P.q_off[cu], q1 = P.q_off[cu + 1];
+    // ---- sync wave
+    for (int b = 0; b < batch; ++b) {
+      M.el(B.tokens, b, 4, 4, "sync(b): tokens[b]");
+      M.el(B.positions, b, 4, 4, "sync(b): positions[b]");
+    }
+    if (inputs_ok)
+      for (uint32_t qi = q0; qi < q1; ++qi) {
+        const Instr &d = P.instr[qi];
+        const uint32_t nx = is_gemv(d.op) ? d.nk : 1;
+        const bool normed = d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM;
+        if (d.op == OP_QKV) {
+          const uint32_t ppg = (uint32_t)(G + 2) * half;
+          for (uint32_t x = 0; x < d.n_items * (uint32_t)batch; ++x) {
+            const uint32_t i = x / batch, b = x % batch, ii = ((d.item0 + i) % ppg) % half;
+            M.el(B.rope, lay::rope(hd, pos[b], (int)ii), 4, 8, "sync(b): RoPE of (pair, sequence)");
+          }
+        }
+        for (uint32_t w = 0; w < d.wait_n; ++w) {
+          const Wait &wt = P.waits[d.wait_off + w];
+          for (uint32_t lane = 0; lane < wt.nslot; ++lane) {
+            M.el(B.ctr, ((uint64_t)wt.grp * kSlots + lane) * kCtrStride, 4, 4, "sync(b): counter poll");
+            M.el(B.target, (uint64_t)wt.grp * kSlots + lane, 4, 4, "sync(b): slot target");
+          }
+          M.el(B.status, 0, 4, 4, "sync(b): status poll");
+        }
+        if (!is_gemv(d.op)) continue;
+        const uint32_t K = d.rowb >> 1;
+        for (uint32_t k = 0; k < nx; ++k) {
+          if (normed && k == 0)
+            for (int b = 0; b < batch; ++b) {
+              uint64_t h, emb, nw;
+              norm_src(d, b, h, emb, nw);
+              for (int lane = 0; lane < 64; ++lane)
+                for (uint32_t i0 = 0; i0 < (uint32_t)H; i0 += 2048)
+                  for (int m = 0; m < 8; ++m) {
+                    const uint32_t i = i0 + (uint32_t)(lane + 64 * m) * 4;
+                    if (i >= (uint32_t)H) continue;
+                    if (emb) M.at(emb + (uint64_t)i * 2, 8, B.embed, "sync(b): embedding row for 1/rms");
+                    else M.at(h + (uint64_t)i * 4, 16, B.h, "sync(b): residual for 1/rms");
+                  }
+            }
+          for (int lane = 0; lane < 64; ++lane) {
+            const int sl = lane & 7;
+            if (sl >= batch) continue;
+            const uint32_t kl = 8 * (uint32_t)(lane >> 4);
+            uint64_t src = 0, emb = 0, nw = 0, want = 0;
+            if (normed) {
+              norm_src(d, sl, src, emb, nw);
+              want = src ? B.h : B.embed;
+            } else if (d.op == OP_O) {
+              src = B.attn + lay::attn(MB, nq, hd, d.layer, sl) * 4;
+              want = B.attn;
+            } else {
+              src = B.a + lay::a(MB, F, d.layer, sl) * 4;
+              want = B.a;
+            }
+            for (int ks = 0; ks < 8; ++ks) {
+              const uint32_t kb = k * kMfmaKc + (uint32_t)ks * 32 + kl;
+              if (kb >= K) continue;
+              if (emb) {
+                M.at(emb + (uint64_t)kb * 2, 16, B.embed, "sync(b): embedding piece");
+              } else {
+                M.at(src + (uint64_t)kb * 4, 16, want, "sync(b): activation piece");
+                M.at(src + (uint64_t)kb * 4 + 16, 16, want, "sync(b): activation piece");
+              }
+              if (normed) M.at(nw + (uint64_t)kb * 2, 16, nw, "sync(b): norm weights");
+            }
+          }
+          if (k == 0 && (d.op == OP_O || d.op == OP_DOWN))
+            for (uint32_t x = 0; x < d.n_items * (uint32_t)batch; ++x) {
+              const uint32_t r = x / batch, b = x % batch;
+              if (d.op == OP_O && d.layer == 0)
+                M.at(B.embed + ((uint64_t)tokens[b] * H + d.item0 + r) * 2, 2, B.embed, "sync(b): embedding residual");
+              else
+                M.el(B.h, lay::h(MB, H, d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1, b) + d.item0 + r, 4, 4,
+                     "sync(b): residual rows");
+            }
+        }
+      }
+    // ---- loader waves
+    uint32_t n = 0;
+    for (uint32_t qi = q0; qi < q1; ++qi) {
+      const Instr &d = P.instr[qi];
+      if (!is_gemv(d.op)) continue;
+      const uint32_t R = d.n_items * d.ipw, nrb = d.ppp, K = d.rowb >> 1;
+      const uint32_t nblk = (uint32_t)d.nk * nrb * 4;
+      for (uint32_t p = 0; p < d.pages; ++p, ++n) {
+        for (uint32_t j = 0; j < 16; ++j) {
+          uint32_t Lb = p * 16 + j;
+          if (Lb >= nblk) Lb = 0;
+          const uint32_t kb = Lb & 3, rbk = Lb >> 2, rb = rbk % nrb, k = rbk / nrb;
+          if (d.tab >= 0)
+            for (uint32_t i = 0; i < 8; ++i)
+              M.el(B.rowtab, (uint64_t)d.tab + std::min(rb * 8 + i, R - 1), 8, 8, "loader(b): row table");
+          for (int lane = 0; lane < 64; ++lane) {
+            const uint32_t r = std::min(rb * 8 + (uint32_t)(lane & 7), R - 1);
+            uint64_t row;
+            if (d.tab >= 0) row = (size_t)d.tab + r < P.rowtab.size() ? P.rowtab[d.tab + r] : 0;
+            else if (d.ipw == 2) row = ((r & 1) ? d.w1 : d.w0) + (uint64_t)(d.item0 + (r >> 1)) * d.rowb;
+            else row = d.w0 + (uint64_t)(d.item0 + r) * d.rowb;
+            const uint32_t kk = k * kMfmaKc + kb * 64 + 8 * (uint32_t)(lane >> 3);
+            if (kk < K) {
+              M.at(row + (uint64_t)kk * 2, 16, 0, "loader(b): weight block");
+              if (kk + 8 > K) M.at(~0ull, 16, 0, "loader(b): weight block crosses its row");
+            } else {
+              M.at(B.zero, 16, B.zero, "loader(b): zero padding");
+            }
+          }
+        }
+        M.el(B.iota, n, 4, 4, "loader(b): page sentinel");
+      }
+    }
+    // ---- compute waves
+    if (!inputs_ok) continue;
+    for (uint32_t qi = q0; qi < q1; ++qi) {
+      const Instr &d = P.instr[qi];
+      const int b0 = (int)d.b;
+      if (d.op == OP_ATTN) {
+        const int g = (int)d.aux0, s = (int)d.aux1;
+        const int DPL = hd / 64, PF = 20 / DPL, NR = DPL == 1 ? 16 : 8;
+        const int p = pos[b0];
+        const int lo = s * P.split_len, hi = std::min(lo + P.split_len, p + 1);
+        const int nt0 = std::max(0, std::min(hi - lo, PF));
+        const uint64_t Kr = lay::kv(MB, nkv, S, hd, d.layer, 0, b0, g, lo);
+        const uint64_t Vr = lay::kv(MB, nkv, S, hd, d.layer, 1, b0, g, lo);
+        for (int h = 0; h < G; ++h) {
+          const int j = g * G + h;
+          for (int lane = 0; lane < 64; ++lane) {
+            if (nt0 > 0)
+              for (int t = 0; t < PF; ++t)
+                for (int m = 0; m < DPL; ++m) {
+                  const int tt = std::min(t, nt0 - 1);
+                  M.el(B.kv, Kr + (uint64_t)tt * hd + lane + 64 * m, 2, 2, "attn(b): prefetched K");
+                  M.el(B.kv, Vr + (uint64_t)tt * hd + lane + 64 * m, 2, 2, "attn(b): prefetched V");
+                }
+            if (lo < hi) {
+              const bool has_p = p < hi;
+              for (int m = 0; m < DPL; ++m) {
+                M.el(B.q, lay::q(MB, nq, hd, d.layer, b0, j) + lane + 64 * m, 8, 8, "attn(b): tagged q");
+                if (has_p) {
+                  M.el(B.kvn, lay::kvn(MB, nkv, hd, d.layer, b0, g, 0) + lane + 64 * m, 8, 8, "attn(b): tagged K");
+                  M.el(B.kvn, lay::kvn(MB, nkv, hd, d.layer, b0, g, 0) + hd + lane + 64 * m, 8, 8,
+                       "attn(b): tagged V");
+                }
+              }
+              for (int c0 = lo + PF; c0 < hi; c0 += 64) {
+                const int nt = std::min(64, hi - c0);
+                for (int kvt = 0; kvt < 2; ++kvt)
+                  for (int t0 = 0; t0 < nt; t0 += NR)
+                    for (int t = 0; t < NR; ++t) {
+                      const int tt = std::min(t0 + t, nt - 1);
+                      if (c0 + tt == p) continue;
+                      for (int m = 0; m < DPL; ++m)
+                        M.el(B.kv, (kvt ? Vr : Kr) + (uint64_t)(c0 - lo + tt) * hd + lane + 64 * m, 2, 2,
+                             "attn(b): K/V row of the long split");
+                    }
+              }
+            }
+            const uint64_t out = lay::part(MB, nq, ns, hd, d.layer, b0, j, s);
+            for (int m = 0; m < DPL; ++m) M.el(B.part, out + lane + 64 * m, 4, 4, "attn(b): partial o");
+            if (lane == 0) {
+              M.el(B.part, out + hd, 4, 4, "attn(b): partial m");
+              M.el(B.part, out + hd + 1, 4, 4, "attn(b): partial l");
+            }
+          }
+        }
+        M.el(B.ctr, ((uint64_t)d.sig0 * kSlots + d.slot0) * kCtrStride, 4, 4, "attn(b): counter signal");
+      } else if (d.op == OP_RED) {
+        const int g = (int)d.aux0, DPL = hd / 64, RB = 32 / DPL;
+        const uint32_t rowb = (uint32_t)(hd + 4) * 4;
+        for (int h = 0; h < G; ++h) {
+          const int j = g * G + h;
+          const uint64_t base = B.part + lay::part(MB, nq, ns, hd, d.layer, b0, j, 0) * 4;
+          for (int lane = 0; lane < 64; ++lane) {
+            if (lane < ns) {
+              M.at(base + (uint64_t)lane * rowb + hd * 4, 4, B.part, "red(b): m");
+              M.at(base + (uint64_t)lane * rowb + hd * 4 + 4, 4, B.part, "red(b): l");
+            }
+            for (int s0 = 0; s0 < ns; s0 += RB)
+              for (int t = 0; t < RB; ++t)
+                for (int m = 0; m < DPL; ++m)
+                  M.at(base + (uint64_t)std::min(s0 + t, ns - 1) * rowb + (uint64_t)(lane + 64 * m) * 4, 4, B.part,
+                       "red(b): o");
+            for (int m = 0; m < DPL; ++m)
+              M.el(B.attn, lay::attn(MB, nq, hd, d.layer, b0) + (uint64_t)j * hd + lane + 64 * m, 4, 4,
+                   "red(b): output");
+          }
+        }
+        M.el(B.ctr, ((uint64_t)d.sig0 * kSlots + d.slot0) * kCtrStride, 4, 4, "red(b): counter signal");
+      } else {
+        for (uint32_t x = 0; x < d.n_items * (uint32_t)batch; ++x) {
+          const uint32_t i = x / batch;
+          const int b = (int)(x % batch);
+          switch (d.op) {
+            case OP_QKV: {
+              const uint32_t ppg = (uint32_t)(G + 2) * half, pp = d.item0 + i, g = pp / ppg, rr = pp - g * ppg;
+              const uint32_t hs = rr / half, ii = rr - hs * half;
+              if (hs < (uint32_t)G) {
+                const uint64_t qo = lay::q(MB, nq, hd, d.layer, b, (int)(g * G + hs));
+                M.el(B.q, qo + ii, 8, 8, "epilogue(b): q word");
+                M.el(B.q, qo + ii + half, 8, 8, "epilogue(b): q word");
+              } else {
+                const int t = hs == (uint32_t)G ? 0 : 1;
+                const uint64_t ko = lay::kv(MB, nkv, S, hd, d.layer, t, b, (int)g, pos[b]);
+                M.el(B.kv, ko + ii, 2, 2, "epilogue(b): K/V slot p");
+                M.el(B.kv, ko + ii + half, 2, 2, "epilogue(b): K/V slot p");
+                const uint64_t no = lay::kvn(MB, nkv, hd, d.layer, b, (int)g, t);
+                M.el(B.kvn, no + ii, 8, 8, "epilogue(b): tagged K/V");
+                M.el(B.kvn, no + ii + half, 8, 8, "epilogue(b): tagged K/V");
+              }
+              break;
+            }
+            case OP_O: M.el(B.h, lay::h(MB, H, 2 * d.layer + 1, b) + d.item0 + i, 4, 4, "epilogue(b): O"); break;
+            case OP_FFN: M.el(B.a, lay::a(MB, F, d.layer, b) + d.item0 + i, 4, 4, "epilogue(b): FFN"); break;
+            case OP_DOWN: M.el(B.h, lay::h(MB, H, 2 * d.layer + 2, b) + d.item0 + i, 4, 4, "epilogue(b): down"); break;
+            default: M.el(B.logits, lay::logits(V, b) + d.item0 + i, 4, 4, "epilogue(b): logits"); break;
+          }
+        }
+        if (d.op == OP_LM && (d.aux1 & 2u)) {
+          for (int b = 0; b < batch; ++b)
+            M.el(B.amax, (uint64_t)d.aux0 * batch + b, 8, 8, "epilogue(b): workgroup greedy candidate");
+          M.el(B.ctr, (uint64_t)P.n_groups * kSlots * kCtrStride, 4, 4, "greedy(b): arrival counter");
+          for (int u = 0; u < P.n_lm_groups; ++u)
+            for (int b = 0; b < batch; ++b) M.el(B.amax, (uint64_t)u * batch + b, 8, 8, "greedy(b): candidates");
+          for (int b = 0; b < batch; ++b) {
+            M.el(B.next_tok, b, 4, 4, "greedy(b): next token");
+            M.el(B.next_pos, b, 4, 4, "greedy(b): next position");
+          }
+        }
+        for (int sg : {d.sig0, d.sig1})
+          if (sg >= 0) {
+            const uint32_t slot = sg == d.sig0 ? d.slot0 : d.slot1;
+            M.el(B.ctr, ((uint64_t)sg * kSlots + slot) * kCtrStride, 4, 4, "epilogue(b): counter signal");
+          }
+      }
+    }
+    M.el(B.status, 0, 4, 12, "raise_error: status words");
+  }
+}
 
 extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int32_t steps,
                              const int32_t *positions, const int32_t *tokens, int32_t corrupt,
@@ -163,6 +430,7 @@ extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cu
     max_pages = std::max(max_pages, np);
   }
   B.amax = M.add("amax", (uint64_t)n_lm * MB * 8);
+  B.zero = M.add("zero", 1024);
   B.rowtab = M.add("rowtab", P.rowtab.size() * 8);
   B.iota = M.add("iota", ((uint64_t)max_pages + 1) * 4);
 
@@ -177,6 +445,10 @@ extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cu
       if (tokens[b] < 0 || tokens[b] >= V || pos[b] < 0 || pos[b] >= S) inputs_ok = false;
     M.el(B.positions, 0, 4, 4, "kernel start: positions[0]");
 
+    if (batch > 1) {
+      walk_batched(M, B, P, c, batch, num_cus, pos, tokens, inputs_ok);
+      continue;
+    }
     for (int cu = 0; cu < num_cus; ++cu) {
       const uint32_t q0 = P.q_off[cu], q1 = P.q_off[cu + 1];
       // ---- sync wave ----------------------------------------------------

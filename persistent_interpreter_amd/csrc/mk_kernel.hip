@@ -1021,13 +1021,12 @@ __device__ __forceinline__ void lm_greedy_finish(const Env &e, const Args &a) {
 // (written by earlier steps), so their K/V are loaded before the unit's
 // dependency gate; q and the new slot p are loaded after it.
 template <int DPL, class Gate>
-__device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, Gate gate) {
+__device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, int p, Gate gate) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
   const int b = (int)d.b, g = (int)d.aux0, s = (int)d.aux1;
   const int j = g * c.G + h;
   constexpr int hd = 64 * DPL, PF = 20 / DPL;  // prefetch depth (register budget)
-  const int p = e.pos0;
   const int lo = s * a.split_len;
   const int hi = min(lo + a.split_len, p + 1);
   const int nt0 = max(0, min(hi - lo, PF));
@@ -1277,7 +1276,7 @@ __device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw
     // gate: the first activation piece of the instruction is produced
     auto gate = [&]() { return spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq; }, 0x200 | qi); };
     if (d.op == OP_ATTN && cw < c.G) {
-      const bool ok = c.hd == 64 ? attn_body<1>(e, a, d, cw, gate) : attn_body<2>(e, a, d, cw, gate);
+      const bool ok = c.hd == 64 ? attn_body<1>(e, a, d, cw, e.pos0, gate) : attn_body<2>(e, a, d, cw, e.pos0, gate);
       if (!ok) return;
     } else if (!gate()) {
       return;
@@ -1383,6 +1382,606 @@ __device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw
   }
 }
 
+// ==========================================================================
+// Batched steps (2 to 8 sequences).  Each GEMV instruction is then a small
+// dense contraction (the sequences x the unit's weight rows x K), which the
+// matrix cores take: v_mfma_f32_16x16x32_bf16 multiplies a 16 x 32 block A of
+// activations by a 32 x 16 block B of weights, accumulating in fp32
+// ("L'interpréteur sur GPU", section 3.6: with a batch, the projections
+// become compute-shaped products).  Activations stay fp32 between
+// instructions; each value x enters the product as a bf16 pair, hi = bf16(x)
+// and lo = bf16(x - hi), and the 16 rows of A are the hi parts of sequences
+// 0..7 (rows 0..7) and their lo parts (rows 8..15), so one MFMA forms both
+// halves of every product and the result of sequence s is D[s] + D[s + 8]
+// (the bf16 multi-term split of Henry, Tang and Heinecke, 2019).
+//
+// Weights stream through the same ring of 16 KB pages, in MFMA order: a 1 KB
+// block holds 8 weight rows x 64 elements, chunk-major (slot c*8 + r holds
+// elements 8c .. 8c+7 of row r).  The loader gathers a block with one
+// 16-byte load per lane, so every 8 lanes read one whole 128-byte line of a
+// row; a compute wave reads the B operand of 16 rows x 32 elements from two
+// blocks as eight 128-byte runs, free of LDS bank conflicts.  A unit's rows
+// form 16-row tiles; compute waves split the tiles, then the K steps of a
+// tile, and the last wave sums the waves' partial tiles in wave order, so the
+// sum order is fixed.
+
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+
+// LDS layout of the batched kernel (bytes; control words as above)
+constexpr int LB_AMAX = 192;    // u64[8]  running greedy best per sequence of this workgroup
+constexpr int LB_ACC = 256;     // f32 [kAccSlots][kAccFloats]: residual rows [row][seq], RoPE staging
+constexpr int LB_PART = LB_ACC + kAccSlots * kAccFloats * 4;  // f32 [2][kNCW][128] partial tiles
+constexpr int kXSlotB = 8 * 1024;                              // 8 k-steps x 1 KB A operands
+constexpr int LB_XS = LB_PART + 2 * kNCW * 128 * 4;
+constexpr int LB_RING = ((LB_XS + kNXS * kXSlotB + 1023) / 1024) * 1024;
+constexpr int kRingPagesB = 7;
+constexpr int LB_SENT = LB_RING + kRingPagesB * kPageBytes;
+static_assert(LB_SENT + kRingPagesB * kSentBytes <= kLdsBytes, "batched LDS budget");
+static_assert(LB_AMAX + 8 * 8 <= LB_ACC && L_EPI < LB_AMAX, "control words");
+
+__device__ __forceinline__ int seq_pos(const Args &a, const DevCtx &c, int b) {
+  const int p = a.positions[b];
+  return (p < 0 || p >= c.max_seq) ? 0 : p;
+}
+
+// Two 16-byte LDS reads in one asm block (see dot_piece for why inline asm).
+__device__ __forceinline__ void lds_read2x16(uint32_t a0, uint32_t a1, u4 &v0, u4 &v1) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1)
+      : "v"(a0), "v"(a1));
+}
+
+// 8 consecutive fp32 values as the A operand of one lane: their hi parts, or
+// (lo) what is left of each after its hi part, both bf16 (RNE).
+__device__ __forceinline__ u4 pack_hilo(const float (&x)[8], bool lo) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint16_t h0 = f2bf(x[2 * j]), h1 = f2bf(x[2 * j + 1]);
+    if (lo) {
+      h0 = f2bf(x[2 * j] - bf16f(h0));
+      h1 = f2bf(x[2 * j + 1] - bf16f(h1));
+    }
+    w[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+  }
+  return u4{w[0], w[1], w[2], w[3]};
+}
+
+// Start of weight row r of an MFMA unit, per lane (r < rows of the unit).
+// Tabulated units (QKV pairs) read the 8 row addresses of block `rb` with
+// uniform (scalar) loads and pick their own: a per-lane vector load would
+// join the loader's direct-to-LDS loads in its wait counter.
+__device__ __forceinline__ const char *row_start(const Instr &d, const uint64_t *__restrict__ rowtab, uint32_t rb,
+                                                 uint32_t R, int lane) {
+  const uint32_t r = min(rb * 8 + (uint32_t)(lane & 7), R - 1);
+  if (d.tab >= 0) {
+    uint64_t ent[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ent[i] = rowtab[d.tab + min(rb * 8 + (uint32_t)i, R - 1)];
+    uint64_t mine = ent[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+      if ((lane & 7) == i) mine = ent[i];
+    return reinterpret_cast<const char *>(mine);
+  }
+  uint64_t base;
+  if (d.ipw == 2) base = ((r & 1) ? d.w1 : d.w0) + (uint64_t)(d.item0 + (r >> 1)) * d.rowb;
+  else base = d.w0 + (uint64_t)(d.item0 + r) * d.rowb;
+  return reinterpret_cast<const char *>(base);
+}
+
+__device__ __forceinline__ void loader_role_b(const Env &e, const Args &a, int lw) {
+  const int lane = lane_id();
+  constexpr uint32_t P = kRingPagesB;
+  const char *zero = reinterpret_cast<const char *>(e.cp->zero);
+  int npend = 0;
+  auto min_cons = [&]() -> uint32_t {
+    uint32_t v = lane < kNCW ? asm_lds_ld(L_CONS + 4 * lane) : 0xffffffffu;
+    uint32_t m = __builtin_amdgcn_readlane(v, 0);
+#pragma unroll
+    for (int i = 1; i < kNCW; ++i) m = min(m, (uint32_t)__builtin_amdgcn_readlane(v, i));
+    return m;
+  };
+  uint32_t n = 0;
+  for (uint32_t qi = 0; qi < e.nq; ++qi) {
+    const Instr d = e.q[qi];
+    if (!is_gemv(d.op)) continue;
+    const uint32_t R = d.n_items * d.ipw, nrb = d.ppp, K = d.rowb >> 1;
+    const uint32_t nblk = (uint32_t)d.nk * nrb * 4;
+    uint32_t cur_rb = 0xffffffffu;
+    const char *rowp = nullptr;
+    for (uint32_t p = 0; p < d.pages; ++p, ++n) {
+      if ((int)(n % kNLW) != lw) continue;
+      if (n >= P && min_cons() < n - P + 1) {
+        const uint32_t need = n - P + 1;
+        Watchdog wd;
+        for (uint32_t it = 1;; ++it) {
+          __builtin_amdgcn_s_sleep(MK_LSLEEP);
+          if (min_cons() >= need) break;
+          if ((it & 63) == 0) {
+            if (__builtin_amdgcn_readfirstlane(asm_lds_ld(L_ABORT))) { wait_vm0(); return; }
+            if (wd.expired(e.cp->watchdog_ticks)) { raise_error(e, 0xB0000000u | qi, n); wait_vm0(); return; }
+          }
+        }
+      }
+      if (npend == kSentDepth) {
+        wait_vm_n<17 * (kSentDepth - 1)>();
+        --npend;
+      }
+      LDS_AS char *slot = (LDS_AS char *)smem + LB_RING + (n % P) * kPageBytes;
+      for (uint32_t j = 0; j < 16; ++j) {
+        uint32_t L = p * 16 + j;
+        if (L >= nblk) L = 0;  // tail of the last page: re-read the first block
+        const uint32_t kb = L & 3, rbk = L >> 2, rb = rbk % nrb, k = rbk / nrb;
+        if (rb != cur_rb) {
+          cur_rb = rb;
+          rowp = row_start(d, a.rowtab, rb, R, lane);
+        }
+        const uint32_t kk = k * kMfmaKc + kb * 64 + 8 * (uint32_t)(lane >> 3);
+        const char *src = kk < K ? rowp + (size_t)kk * 2 : zero;
+        __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)(slot + j * 1024), 16, 0, kWPol);
+      }
+      __builtin_amdgcn_global_load_lds(a.iota + n, (LDS_AS void *)(smem + LB_SENT + (n % P) * kSentBytes), 4, 0, 0);
+      ++npend;
+    }
+  }
+  wait_vm0();
+}
+
+__device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
+  const DevCtx &c = *e.cp;
+  const int lane = lane_id();
+  const int B = a.batch;
+  for (int b = 0; b < B; ++b) {
+    int32_t tk = a.tokens[b], ps = a.positions[b];
+    if (tk < 0 || tk >= c.V) { raise_error(e, 0xE1000000u, (uint32_t)b); return; }
+    if (ps < 0 || ps >= c.max_seq) { raise_error(e, 0xE2000000u, (uint32_t)b); return; }
+  }
+  // this lane's row of the A operand: sequence sl, hi or lo part, and its
+  // first element kl within a 32-element k-step
+  const int sl = lane & 7;
+  const bool lo = (lane & 15) >= 8;
+  const uint32_t kl = 8 * (uint32_t)(lane >> 4);
+  const bool live = sl < B;
+  uint32_t seq = 0;
+  for (uint32_t qi = 0; qi < e.nq; ++qi) {
+    const Instr d = e.q[qi];
+    const uint32_t nx = is_gemv(d.op) ? d.nk : 1;
+    const bool normed = d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM;
+    float *accs = reinterpret_cast<float *>(smem + LB_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4);
+    if (d.op == OP_QKV) {
+      // RoPE cos/sin of each (pair, sequence) at that sequence's position,
+      // staged before the waits (the slot's previous unit must be done)
+      if (qi >= (uint32_t)kAccSlots &&
+          !spin_lds(e, [&]() { return lds_ld(L_EPI) + kAccSlots > qi; }, 0x500 | qi))
+        return;
+      const uint32_t half = (uint32_t)c.hd >> 1, ppg = (uint32_t)(c.G + 2) * half;
+      for (uint32_t x = (uint32_t)lane; x < d.n_items * (uint32_t)B; x += 64) {
+        const uint32_t i = x / (uint32_t)B, b = x - i * (uint32_t)B;
+        const uint32_t ii = ((d.item0 + i) % ppg) % half;
+        const uint64_t cs =
+            *G(reinterpret_cast<const uint64_t *>(c.rope + lay::rope(c.hd, seq_pos(a, c, (int)b), (int)ii)));
+        accs[kAccFloats / 2 + 2 * x] = __uint_as_float((uint32_t)cs);
+        accs[kAccFloats / 2 + 2 * x + 1] = __uint_as_float((uint32_t)(cs >> 32));
+      }
+    }
+    if (lane == 0) trace_now(e, qi, 4);
+    // this lane's sequence: its input vector (and norm weights)
+    const uint32_t K = d.rowb >> 1;
+    const float *src = nullptr;
+    const uint16_t *emb = nullptr, *nw = nullptr;
+    if (normed) {
+      norm_src(e, a, d, live ? sl : 0, src, emb, nw);
+    } else if (d.op == OP_O) {
+      src = c.attn_buf + lay::attn(c.max_batch, c.nq, c.hd, d.layer, live ? sl : 0);
+    } else if (d.op == OP_DOWN) {
+      src = c.a_buf + lay::a(c.max_batch, c.F, d.layer, live ? sl : 0);
+    }
+    float rs = 1.f;
+    uint32_t wi = 0;
+    for (uint32_t k = 0; k < nx; ++k, ++seq) {
+      while (wi < d.wait_n) {
+        const Wait wt = a.waits[d.wait_off + wi];
+        if (wt.before_k > k) break;
+        if (!wait_group(e, a, wt, qi)) return;
+        ++wi;
+      }
+      if (k == 0 && lane == 0) {
+        trace_put(e, qi, 0, (uint64_t)d.op | ((uint64_t)d.layer << 8) | ((uint64_t)d.unit << 24));
+        trace_now(e, qi, 1);
+      }
+      if (!is_gemv(d.op)) {
+        // attention and reduction units take no activation piece
+        if (lane == 0) lds_st(L_XREADY, seq + 1);
+        wake();
+        continue;
+      }
+      if (seq >= (uint32_t)kNXS) {
+        const uint32_t need = seq - kNXS + 1;
+        auto freed = [&]() {
+          uint32_t v = lane < kNCW ? lds_ld_lane(L_XCONS + 4 * lane) : 0xffffffffu;
+          uint32_t m = __builtin_amdgcn_readlane(v, 0);
+#pragma unroll
+          for (int i = 1; i < kNCW; ++i) m = min(m, (uint32_t)__builtin_amdgcn_readlane(v, i));
+          return m >= need;
+        };
+        if (!spin_lds(e, freed, 0x100 | qi)) return;
+      }
+      if (normed && k == 0) {
+        // 1/rms of every sequence's input (each lane keeps its own)
+        for (int b = 0; b < B; ++b) {
+          const float *hb;
+          const uint16_t *eb, *wb;
+          norm_src(e, a, d, b, hb, eb, wb);
+          float ss = 0.f;
+          const rsrc_t hr = rsrc(hb ? (const void *)hb : (const void *)eb);
+          for (uint32_t i0 = 0; i0 < (uint32_t)c.H; i0 += 2048) {
+            f4 v[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+              const uint32_t i = i0 + (uint32_t)(lane + 64 * m) * 4;
+              if (i < (uint32_t)c.H) {
+                if (eb) {
+                  const uint64_t uu = *G(reinterpret_cast<const uint64_t *>(eb + i));
+                  v[m] = f4{bf_lo((uint32_t)uu), bf_hi((uint32_t)uu), bf_lo((uint32_t)(uu >> 32)),
+                            bf_hi((uint32_t)(uu >> 32))};
+                } else {
+                  v[m] = ldc4(hr, i * 4);
+                }
+              } else {
+                v[m] = f4{0.f, 0.f, 0.f, 0.f};
+              }
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m) ss += v[m].x * v[m].x + v[m].y * v[m].y + v[m].z * v[m].z + v[m].w * v[m].w;
+          }
+          ss = wave_sum(ss);
+          const float r = 1.0f / sqrtf(ss / (float)c.H + c.eps);
+          if (sl == b) rs = r;
+        }
+      }
+      // the piece's A operands: 8 k-steps of 32 elements
+      LDS_AS char *xs = (LDS_AS char *)smem + LB_XS + (seq % kNXS) * kXSlotB;
+      const rsrc_t sr = rsrc(src ? (const void *)src : (const void *)emb);
+#pragma unroll 2
+      for (int ks = 0; ks < 8; ++ks) {
+        const uint32_t kb = k * kMfmaKc + (uint32_t)ks * 32 + kl;
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = 0.f;
+        if (live && kb < K) {
+          if (emb) {
+            const u4 u = *G(reinterpret_cast<const u4 *>(emb + kb));
+            x[0] = bf_lo(u.x); x[1] = bf_hi(u.x); x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
+            x[4] = bf_lo(u.z); x[5] = bf_hi(u.z); x[6] = bf_lo(u.w); x[7] = bf_hi(u.w);
+          } else {
+            const f4 p0 = ldc4(sr, kb * 4), p1 = ldc4(sr, kb * 4 + 16);
+            x[0] = p0.x; x[1] = p0.y; x[2] = p0.z; x[3] = p0.w;
+            x[4] = p1.x; x[5] = p1.y; x[6] = p1.z; x[7] = p1.w;
+          }
+          if (normed) {
+            const u4 w = *G(reinterpret_cast<const u4 *>(nw + kb));
+            x[0] *= rs * bf_lo(w.x); x[1] *= rs * bf_hi(w.x); x[2] *= rs * bf_lo(w.y); x[3] *= rs * bf_hi(w.y);
+            x[4] *= rs * bf_lo(w.z); x[5] *= rs * bf_hi(w.z); x[6] *= rs * bf_lo(w.w); x[7] *= rs * bf_hi(w.w);
+          }
+        }
+        *reinterpret_cast<LDS_AS u4 *>(xs + ks * 1024 + lane * 16) = pack_hilo(x, lo);
+      }
+      if (k == 0 && (d.op == OP_O || d.op == OP_DOWN)) {
+        // residual rows of every sequence: accs[row * B + b]
+        for (uint32_t x = (uint32_t)lane; x < d.n_items * (uint32_t)B; x += 64) {
+          const uint32_t r = x / (uint32_t)B, b = x - r * (uint32_t)B;
+          float v;
+          if (d.op == OP_O && d.layer == 0)
+            v = bf16f(G(c.embed)[(size_t)a.tokens[b] * c.H + d.item0 + r]);
+          else
+            v = ld_c(c.h_buf + lay::h(c.max_batch, c.H, d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1, (int)b) +
+                     d.item0 + r);
+          accs[x] = v;
+        }
+      }
+      wait_lgkm0();
+      if (lane == 0) lds_st(L_XREADY, seq + 1);
+      wake();
+      if (k == 0 && lane == 0) trace_now(e, qi, 5);
+      if (k + 1 == nx && lane == 0) trace_now(e, qi, 7);
+    }
+  }
+}
+
+// The summed result of weight row r (within the unit) for sequence s, from
+// the waves' partial tiles: tile r / 16 was computed by waves t, t + T, ...
+// Within a wave's partial, lanes 0..31 hold D[s][n] for s = 4*(lane/16) + j
+// (register j), n = lane % 16, after the hi and lo halves were added.
+__device__ __forceinline__ float tile_sum(const float *Pb, uint32_t T, uint32_t r, uint32_t s) {
+  const uint32_t t = r >> 4, nn = r & 15;
+  const uint32_t idx = (((s >> 2) * 16 + nn) << 2) + (s & 3);
+  float v = Pb[t * 128 + idx];
+  for (uint32_t w = t + T; w < (uint32_t)kNCW; w += T) v += Pb[w * 128 + idx];
+  return v;
+}
+
+__device__ __forceinline__ void unit_epilogue_b(const Env &e, const Args &a, const Instr &d, const float *accs,
+                                                const float *Pb) {
+  const DevCtx &c = *e.cp;
+  const int lane = lane_id();
+  const uint32_t B = (uint32_t)a.batch;
+  const uint32_t T = ((uint32_t)d.ppp + 1) >> 1;
+  for (uint32_t x = (uint32_t)lane; x < d.n_items * B; x += 64) {
+    const uint32_t i = x / B, b = x - i * B;
+    switch (d.op) {
+      case OP_QKV: {
+        const float v0 = tile_sum(Pb, T, 2 * i, b), v1 = tile_sum(Pb, T, 2 * i + 1, b);
+        const uint32_t half = (uint32_t)c.hd >> 1;
+        const uint32_t ppg = (uint32_t)(c.G + 2) * half;
+        const uint32_t pp = d.item0 + i, g = pp / ppg, rr = pp - g * ppg;
+        const uint32_t hs = rr / half, ii = rr - hs * half;
+        const int p = seq_pos(a, c, (int)b);
+        if (hs <= (uint32_t)c.G) {
+          const float cs = accs[kAccFloats / 2 + 2 * x], sn = accs[kAccFloats / 2 + 2 * x + 1];
+          const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
+          if (hs < (uint32_t)c.G) {
+            uint64_t *q = c.q_buf + lay::q(c.max_batch, c.nq, c.hd, d.layer, (int)b, (int)(g * c.G + hs));
+            st_tag(q + ii, r0, a.tag);
+            st_tag(q + ii + half, r1, a.tag);
+          } else {
+            uint16_t *k = a.kv + kv_off(c, d.layer, 0, (int)b, (int)g, p);
+            const uint16_t k0 = f2bf(r0), k1 = f2bf(r1);
+            st_c16(k + ii, k0);
+            st_c16(k + ii + half, k1);
+            uint64_t *kn = c.kvn_buf + lay::kvn(c.max_batch, c.nkv, c.hd, d.layer, (int)b, (int)g, 0);
+            st_tag(kn + ii, bf16f(k0), a.tag);
+            st_tag(kn + ii + half, bf16f(k1), a.tag);
+          }
+        } else {
+          uint16_t *v = a.kv + kv_off(c, d.layer, 1, (int)b, (int)g, p);
+          const uint16_t u0 = f2bf(v0), u1 = f2bf(v1);
+          st_c16(v + ii, u0);
+          st_c16(v + ii + half, u1);
+          uint64_t *vn = c.kvn_buf + lay::kvn(c.max_batch, c.nkv, c.hd, d.layer, (int)b, (int)g, 1);
+          st_tag(vn + ii, bf16f(u0), a.tag);
+          st_tag(vn + ii + half, bf16f(u1), a.tag);
+        }
+        break;
+      }
+      case OP_O:
+        st_c(c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer + 1, (int)b) + d.item0 + i, accs[x] + tile_sum(Pb, T, i, b));
+        break;
+      case OP_FFN: {
+        const float gt = tile_sum(Pb, T, 2 * i, b), up = tile_sum(Pb, T, 2 * i + 1, b);
+        st_c(c.a_buf + lay::a(c.max_batch, c.F, d.layer, (int)b) + d.item0 + i, gt / (1.0f + expf(-gt)) * up);
+        break;
+      }
+      case OP_DOWN:
+        st_c(c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer + 2, (int)b) + d.item0 + i,
+             accs[x] + tile_sum(Pb, T, i, b));
+        break;
+      default:  // OP_LM
+        G(a.logits)[lay::logits(c.V, (int)b) + d.item0 + i] = tile_sum(Pb, T, i, b);
+        break;
+    }
+  }
+  if (d.op == OP_LM && a.next_tok) {
+    // per sequence: this unit's best row, merged into the workgroup's
+    // running best (LM units of a workgroup run their epilogues in queue
+    // order); the workgroup's last LM unit publishes it
+    uint64_t *run = reinterpret_cast<uint64_t *>(smem + LB_AMAX);
+    for (uint32_t b = 0; b < B; ++b) {
+      float bv = -INFINITY;
+      uint32_t bi = 0xffffffffu;
+      for (uint32_t i = (uint32_t)lane; i < d.n_items; i += 64) {
+        const float v = tile_sum(Pb, T, i, b);
+        if (amax_better(v, d.item0 + i, bv, bi)) {
+          bv = v;
+          bi = d.item0 + i;
+        }
+      }
+      amax_reduce(bv, bi);
+      if (!(d.aux1 & 1u)) {
+        const uint64_t w = run[b];
+        const float ov = __uint_as_float((uint32_t)w);
+        const uint32_t oi = (uint32_t)(w >> 32);
+        if (amax_better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if (lane == 0) run[b] = ((uint64_t)bi << 32) | __float_as_uint(bv);
+      if ((d.aux1 & 2u) && lane == 0) st_tag(a.amax + (size_t)d.aux0 * B + b, bv, bi);
+    }
+    wait_lgkm0();
+  }
+}
+
+// The last LM workgroup of the step to count itself picks every sequence's
+// greedy token from the workgroups' published candidates.
+__device__ __forceinline__ void lm_greedy_finish_b(const Env &e, const Args &a) {
+  const DevCtx &c = *e.cp;
+  const int lane = lane_id();
+  uint32_t o = 0;
+  before_signal();
+  if (lane == 0)
+    o = __hip_atomic_fetch_add(G(a.amax_ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  o = __builtin_amdgcn_readfirstlane(o);
+  if (o + 1u != a.amax_target) return;
+  poll_exit();
+  const rsrc_t r = rsrc(a.amax);
+  const uint32_t B = (uint32_t)a.batch;
+  for (uint32_t b = 0; b < B; ++b) {
+    float bv = -INFINITY;
+    uint32_t bi = 0xffffffffu;
+    for (uint32_t u = (uint32_t)lane; u < a.n_lm; u += 64) {
+      const uint64_t w = ldt(r, u * B + b);
+      const float v = tval(w);
+      const uint32_t i = (uint32_t)(w >> 32);
+      if (amax_better(v, i, bv, bi)) {
+        bv = v;
+        bi = i;
+      }
+    }
+    amax_reduce(bv, bi);
+    if (lane == 0) {
+      G(a.next_tok)[b] = (int32_t)bi;
+      G(a.next_pos)[b] = seq_pos(a, c, (int)b) + 1;
+    }
+  }
+}
+
+__device__ __forceinline__ void compute_role_b(const Env &e, const Args &a, int cw) {
+  const DevCtx &c = *e.cp;
+  const int lane = lane_id();
+  constexpr uint32_t P = kRingPagesB;
+  uint32_t n = 0, seq = 0;
+  for (uint32_t qi = 0; qi < e.nq; ++qi) {
+    const Instr d = e.q[qi];
+    const bool gv = is_gemv(d.op);
+    const uint32_t nx = gv ? d.nk : 1;
+    auto gate = [&]() { return spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq; }, 0x200 | qi); };
+    if (d.op == OP_ATTN && cw < c.G) {
+      const int p = seq_pos(a, c, (int)d.b);
+      const bool ok = c.hd == 64 ? attn_body<1>(e, a, d, cw, p, gate) : attn_body<2>(e, a, d, cw, p, gate);
+      if (!ok) return;
+    } else if (!gv && !gate()) {
+      return;
+    }
+    if (cw == 0 && lane == 0) trace_now(e, qi, 2);
+    const float *accs = reinterpret_cast<const float *>(smem + LB_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4);
+    float *Pb = reinterpret_cast<float *>(smem + LB_PART + (qi & 1) * kNCW * 128 * 4);
+    if (gv) {
+      const uint32_t nrb = d.ppp, T = (nrb + 1) >> 1;
+      const uint32_t t = (uint32_t)cw % T, nwt = ((uint32_t)kNCW - 1 - t) / T + 1, kg = (uint32_t)cw / T;
+      const uint32_t rb_lo = 2 * t, rb_hi = min(2 * t + 1, nrb - 1);
+      const bool upper = (lane & 15) >= 8;
+      // this lane's offsets within a block and an A operand
+      const uint32_t brow = (uint32_t)(((lane >> 4) * 8 + (lane & 7)) * 16);
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      uint32_t rel = n, v0 = 0xffffffffu, v1 = 0xffffffffu;
+      for (uint32_t k = 0; k < d.nk; ++k) {
+        if (k > 0) {
+          if (lane == 0) lds_st(L_XCONS + 4 * cw, seq + k);
+          wake();
+        }
+        bool ready = false;
+        for (uint32_t ks = 0; ks < 8; ++ks) {
+          if ((k * 8 + ks) % nwt != kg) continue;
+          if (!ready) {
+            if (!spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq + k; }, 0x400 | qi)) return;
+            ready = true;
+          }
+          const uint32_t L0 = (k * nrb + rb_lo) * 4 + (ks >> 1), L1 = (k * nrb + rb_hi) * 4 + (ks >> 1);
+          const uint32_t pg0 = n + (L0 >> 4), pg1 = n + (L1 >> 4);
+          if (pg0 > rel) {
+            if (lane == 0) lds_st(L_CONS + 4 * cw, pg0);
+            rel = pg0;
+            wake();
+          }
+          if (pg0 != v0) {
+            if (!spin_lds_fast(e, [&]() { return lds_ld(LB_SENT + (pg0 % P) * kSentBytes) == pg0; }, 0x300 | qi))
+              return;
+            v0 = pg0;
+          }
+          if (pg1 != v1 && pg1 != v0) {
+            if (!spin_lds_fast(e, [&]() { return lds_ld(LB_SENT + (pg1 % P) * kSentBytes) == pg1; }, 0x300 | qi))
+              return;
+          }
+          v1 = pg1;
+          const uint32_t mypg = upper ? pg1 : pg0, myL = upper ? L1 : L0;
+          const uint32_t aaddr = lds_addr(LB_XS + (int)(((seq + k) % kNXS) * kXSlotB + ks * 1024 + lane * 16));
+          const uint32_t baddr = lds_addr(LB_RING + (int)((mypg % P) * kPageBytes + (myL & 15) * 1024 +
+                                                          ((ks & 1) * 4 * 8 * 16) + brow));
+          u4 av, bv;
+          lds_read2x16(aaddr, baddr, av, bv);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, av), __builtin_bit_cast(bf8v, bv),
+                                                         acc, 0, 0, 0);
+        }
+      }
+      // hi + lo halves: rows s and s + 8 of D sit in lanes l and l + 32
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], 32);
+      // the partial-tile buffer (qi & 1) was last read by unit qi - 2's epilogue
+      if (qi >= 2 && !spin_lds(e, [&]() { return lds_ld(L_EPI) + 1 >= qi; }, 0x600 | qi)) return;
+      if (lane < 32) *reinterpret_cast<f4 *>(Pb + cw * 128 + lane * 4) = acc;
+      wait_lgkm0();
+      if (lane == 0) lds_st(L_CONS + 4 * cw, n + d.pages);
+      wake();
+    } else if (d.op == OP_RED) {
+      if (cw < c.G) {
+        if (c.hd == 64) red_body<1>(e, a, d, cw);
+        else red_body<2>(e, a, d, cw);
+      }
+    }
+    n += d.pages;
+    seq += nx;
+    if (lane == 0) lds_st(L_XCONS + 4 * cw, seq);
+    wake();
+    if (!gv) wait_vm0();
+    wait_lgkm0();
+    uint32_t old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(&lds_u32(L_DONE + 4 * (qi & 3)), 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old == kNCW - 1) {
+      lds_poll_exit();  // every wave's partial tile is in LDS
+      if (lane == 0) trace_now(e, qi, 6);
+      if (gv) {
+        unit_epilogue_b(e, a, d, accs, Pb);
+        if (d.op != OP_QKV) wait_vm0();
+      }
+      if (d.op == OP_LM && a.next_tok && (d.aux1 & 2u)) {
+        wait_vm0();  // the published candidates are acknowledged before counting
+        lm_greedy_finish_b(e, a);
+      }
+      before_signal();
+      if (lane == 0) {
+        trace_now(e, qi, 3);
+        lds_st(L_DONE + 4 * (qi & 3), 0);
+        lds_st(L_EPI, qi + 1);
+        if (d.sig0 >= 0)
+          __hip_atomic_fetch_add(G(a.ctr) + ((size_t)d.sig0 * kSlots + d.slot0) * kCtrStride, 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        if (d.sig1 >= 0)
+          __hip_atomic_fetch_add(G(a.ctr) + ((size_t)d.sig1 * kSlots + d.slot1) * kCtrStride, 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+      wake();
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kThreads, 1)
+mk_interp_b(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const uint32_t *__restrict__ q_off,
+            const Wait *__restrict__ waits, const uint64_t *__restrict__ rowtab, uint32_t *__restrict__ ctr,
+            const uint32_t *__restrict__ grp_target, float *__restrict__ part_buf, const uint32_t *__restrict__ iota,
+            const int32_t *__restrict__ tokens, const int32_t *__restrict__ positions, uint16_t *__restrict__ kv,
+            float *__restrict__ logits, uint64_t *__restrict__ trace, uint32_t trace_stride, uint32_t epoch,
+            uint32_t tag, int32_t batch, int32_t n_split, int32_t split_len, uint64_t *__restrict__ amax,
+            uint32_t *__restrict__ amax_ctr, int32_t *__restrict__ next_tok, int32_t *__restrict__ next_pos,
+            uint32_t n_lm, uint32_t amax_target) {
+  const Args a{ctx, instr, q_off, waits, rowtab, ctr, grp_target, part_buf, iota, tokens, positions, kv, logits,
+               trace, trace_stride, epoch, tag, batch, n_split, split_len, amax, amax_ctr, next_tok, next_pos,
+               n_lm, amax_target};
+  Env e;
+  e.cp = a.ctx;
+  e.cu = (int)blockIdx.x;
+  const uint32_t q0 = a.q_off[e.cu], q1 = a.q_off[e.cu + 1];
+  e.q = a.instr + q0;
+  e.nq = q1 - q0;
+  e.trace = a.trace ? a.trace + 4 + (size_t)e.cu * a.trace_stride * kTraceWords : nullptr;
+  e.pos0 = 0;  // unused: batched roles read each sequence's own position
+  if (threadIdx.x < 64) lds_u32(threadIdx.x * 4) = 0;  // control words
+  for (int i = (int)threadIdx.x; i < kRingPagesB * kSentBytes / 4; i += kThreads)
+    lds_u32(LB_SENT + 4 * i) = 0xffffffffu;
+  __syncthreads();
+  const int w = (int)(threadIdx.x >> 6);
+  if (w < kNCW) compute_role_b(e, a, w);
+  else if (w < kNCW + kNLW) loader_role_b(e, a, w - kNCW);
+  else sync_role_b(e, a);
+}
+
 // --------------------------------------------------------------------------
 __global__ void __launch_bounds__(kThreads, 1)
 mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const uint32_t *__restrict__ q_off,
@@ -1434,7 +2033,14 @@ hipError_t kernel_setup(int *blocks_per_cu) {
   hipError_t e = hipFuncSetAttribute((const void *)mk_interp, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      kLdsBytes);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, mk_interp, kThreads, kLdsBytes);
+  e = hipFuncSetAttribute((const void *)mk_interp_b, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (e != hipSuccess) return e;
+  int nb = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mk_interp_b, kThreads, kLdsBytes);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, mk_interp, kThreads, kLdsBytes);
+  if (nb < *blocks_per_cu) *blocks_per_cu = nb;
+  return e;
 }
 
 hipError_t kernel_launch(const Args &a0, int grid, bool cooperative, hipStream_t stream) {
@@ -1446,10 +2052,10 @@ hipError_t kernel_launch(const Args &a0, int grid, bool cooperative, hipStream_t
   // One workgroup per CU fits (checked at create); a plain launch places all
   // of them at once on an otherwise idle device, a cooperative one also
   // waits for room when other work holds CUs (about 23 us more per launch).
-  if (cooperative)
-    return hipLaunchCooperativeKernel((const void *)mk_interp, dim3(grid), dim3(kThreads), params, kLdsBytes,
-                                      stream);
-  return hipLaunchKernel((const void *)mk_interp, dim3(grid), dim3(kThreads), params, kLdsBytes, stream);
+  // batches of 2 or more sequences run the MFMA kernel
+  const void *fn = a.batch > 1 ? (const void *)mk_interp_b : (const void *)mk_interp;
+  if (cooperative) return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), params, kLdsBytes, stream);
+  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), params, kLdsBytes, stream);
 }
 
 }  // namespace mk

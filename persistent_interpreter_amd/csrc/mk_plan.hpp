@@ -48,6 +48,10 @@ constexpr int kSlots = 64;
 #endif
 constexpr int kAtomicsPerSlot = MK_APS;
 constexpr int kMaxSplits = 64;
+// Batched (MFMA) plans: pieces of 256 elements = 8 MFMA k-steps of 32, one
+// per compute wave; units of at most 64 weight rows (four 16-row tiles).
+constexpr int kMfmaKc = 256;
+constexpr int kMfmaRows = 64;
 
 // One queued instruction (96 bytes).  An instruction's weight stream is the
 // sequence of pieces t = 0 .. n_items*ipw*nk - 1 in k-major order:
@@ -111,6 +115,7 @@ struct DevCtx {
   uint64_t *q_buf;    // [L][max_batch][nq][hd]
   uint64_t *kvn_buf;  // [L][max_batch][nkv][2][hd] this step's K/V slot (bf16-rounded)
   const float *rope;  // [max_seq][hd/2][2] (cos, sin)
+  const uint16_t *zero;  // 1 KB of zeros: weights past K in zero-padded MFMA pieces
   uint32_t *status;   // [0] error code, [1..] details
   uint64_t *trace;    // per-instruction records or NULL
   int32_t ring_pages; // LDS weight pages per workgroup

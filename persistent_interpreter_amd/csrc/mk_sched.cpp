@@ -91,7 +91,7 @@ struct Builder {
 };
 
 Instr gemv(Op op, int layer, uint32_t item0, uint32_t n, int ipw, int K, int kc,
-           uint32_t unit) {
+           uint32_t unit, bool mfma) {
   Instr in;
   std::memset(&in, 0, sizeof in);
   in.op = op;
@@ -99,13 +99,25 @@ Instr gemv(Op op, int layer, uint32_t item0, uint32_t n, int ipw, int K, int kc,
   in.ipw = (uint8_t)ipw;
   in.kc = (uint32_t)kc;
   in.pb = (uint32_t)(2 * kc);
-  in.nk = (uint16_t)(K / kc);
-  int ppp = kPageBytes / (int)in.pb;
-  in.ppp = (uint16_t)ppp;
   in.item0 = item0;
   in.n_items = n;
-  uint64_t pieces = (uint64_t)n * ipw * in.nk;
-  in.pages = (uint32_t)((pieces + ppp - 1) / ppp);
+  if (mfma) {
+    // MFMA stream (batched plans): pieces of kMfmaKc elements (the last one
+    // zero-padded past K), 1 KB blocks of 8 rows x 64 elements (the last
+    // block's rows past the unit repeat its last row), 16 blocks per page;
+    // ppp holds the number of 8-row blocks
+    in.nk = (uint16_t)((K + kMfmaKc - 1) / kMfmaKc);
+    const uint32_t nrb = (n * ipw + 7) / 8;
+    in.ppp = (uint16_t)nrb;
+    const uint64_t blocks = (uint64_t)in.nk * nrb * (kMfmaKc / 64);
+    in.pages = (uint32_t)((blocks + 15) / 16);
+  } else {
+    in.nk = (uint16_t)(K / kc);
+    int ppp = kPageBytes / (int)in.pb;
+    in.ppp = (uint16_t)ppp;
+    uint64_t pieces = (uint64_t)n * ipw * in.nk;
+    in.pages = (uint32_t)((pieces + ppp - 1) / ppp);
+  }
   in.sig0 = in.sig1 = -1;
   in.tab = -1;
   in.rowb = (uint32_t)(2 * K);
@@ -139,17 +151,18 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
     return MK_ERR_UNSUPPORTED;
   }
   const int G = nq / nkv, HALF = hd / 2;
-  // batched plans use pieces of at most 256 elements (the batched dot maps
-  // 32 weight groups onto each half of a wave)
-  const int kmax = B == 1 ? kMaxKc : 256;
-  const int kc_h = choose_kc(H, kmax), kc_o = choose_kc(nq * hd, kmax), kc_f = choose_kc(F, kmax);
+  // batched plans (MFMA) use pieces of kMfmaKc elements, the last one
+  // zero-padded; batch-1 plans a divisor of K
+  const bool mfma = B > 1;
+  const int kc_h = mfma ? kMfmaKc : choose_kc(H, kMaxKc), kc_o = mfma ? kMfmaKc : choose_kc(nq * hd, kMaxKc);
+  const int kc_f = mfma ? kMfmaKc : choose_kc(F, kMaxKc);
   if (!kc_h || !kc_o || !kc_f) {
     err = "hidden, n_q_heads*head_dim and ffn_dim must be multiples of 8";
     return MK_ERR_UNSUPPORTED;
   }
   const uint32_t PPG = (uint32_t)(G + 2) * HALF;     // QKV row pairs per KV head
   const uint32_t TP = (uint32_t)nkv * PPG;
-  const int nk_f = F / kc_f;
+  const int nk_f = (F + kc_f - 1) / kc_f;
   int chunks = c.mlp_chunks > 0 ? c.mlp_chunks : 4;
   chunks = std::min(chunks, nk_f);
   int n_split = c.kv_splits;
@@ -176,7 +189,9 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
   // (units take ceil(rows / n) or floor(rows / n) rows)
   auto units_for = [&](uint32_t rows, uint32_t ipw, uint32_t at_least, uint32_t cap = kAccFloats) {
     uint32_t n = std::max<uint32_t>(std::min<uint32_t>((uint32_t)C, rows), at_least);
-    const uint32_t max_rows = std::max<uint32_t>(1, cap / (ipw * (uint32_t)B));
+    uint32_t max_rows = std::max<uint32_t>(1, cap / (ipw * (uint32_t)B));
+    // MFMA units hold at most kMfmaRows weight rows (four 16-row tiles)
+    if (mfma) max_rows = std::min<uint32_t>(max_rows, (uint32_t)kMfmaRows / ipw);
     n = std::max<uint32_t>(n, (rows + max_rows - 1) / max_rows);
     return std::min<uint32_t>(n, rows);
   };
@@ -186,6 +201,8 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
   const uint32_t n_lm = units_for(V, 1, 1);
 
   auto chunk_k0 = [&](int ch) { return (uint32_t)((uint64_t)ch * nk_f / chunks); };
+  // first element of chunk ch (F for ch == chunks)
+  auto chunk_e0 = [&](int ch) { return std::min<uint32_t>(chunk_k0(ch) * kc_f, (uint32_t)F); };
 
   Builder bd(c, B, C, P);
   std::vector<int> g_down_prev(1, -1);
@@ -202,7 +219,7 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
     for (uint32_t u = 0; u < n_qkv; ++u) {
       uint32_t p0 = part_lo(TP, n_qkv, u), p1 = part_lo(TP, n_qkv, u + 1);
       Unit un;
-      un.in = gemv(OP_QKV, l, p0, p1 - p0, 2, H, kc_h, u);
+      un.in = gemv(OP_QKV, l, p0, p1 - p0, 2, H, kc_h, u, mfma);
       un.in.aux0 = (uint32_t)G;
       un.in.aux1 = (uint32_t)hd;
       un.cu = (int)(u % C);
@@ -253,7 +270,7 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
     for (uint32_t u = 0; u < n_o; ++u) {
       uint32_t r0 = part_lo(H, n_o, u), r1 = part_lo(H, n_o, u + 1);
       Unit un;
-      un.in = gemv(OP_O, l, r0, r1 - r0, 1, nq * hd, kc_o, u);
+      un.in = gemv(OP_O, l, r0, r1 - r0, 1, nq * hd, kc_o, u, mfma);
       un.cu = (int)(u % C);
       un.waits.push_back({(uint32_t)g_red, 0});
       for (int b = 0; b < B; ++b) {
@@ -268,7 +285,7 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
     for (uint32_t u = 0; u < n_ffn; ++u) {
       uint32_t j0 = part_lo(F, n_ffn, u), j1 = part_lo(F, n_ffn, u + 1);
       Unit un;
-      un.in = gemv(OP_FFN, l, j0, j1 - j0, 2, H, kc_h, u);
+      un.in = gemv(OP_FFN, l, j0, j1 - j0, 2, H, kc_h, u, mfma);
       un.cu = (int)(u % C);
       un.waits.push_back({(uint32_t)g_o, 0});
       for (int b = 0; b < B; ++b) {
@@ -276,7 +293,7 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
         un.writes.push_back({R_A, (uint16_t)l, (uint32_t)b, j0, j1, 0});
       }
       for (int ch = 0; ch < chunks; ++ch) {
-        uint32_t e0 = chunk_k0(ch) * kc_f, e1 = chunk_k0(ch + 1) * kc_f;
+        uint32_t e0 = chunk_e0(ch), e1 = chunk_e0(ch + 1);
         if (j0 < e1 && e0 < j1) un.sigs.push_back(g_ffn[ch]);
       }
       if (un.sigs.size() > 2) {
@@ -289,13 +306,12 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
     for (uint32_t u = 0; u < n_down; ++u) {
       uint32_t r0 = part_lo(H, n_down, u), r1 = part_lo(H, n_down, u + 1);
       Unit un;
-      un.in = gemv(OP_DOWN, l, r0, r1 - r0, 1, F, kc_f, u);
+      un.in = gemv(OP_DOWN, l, r0, r1 - r0, 1, F, kc_f, u, mfma);
       un.cu = (int)(u % C);
       for (int ch = 0; ch < chunks; ++ch) un.waits.push_back({(uint32_t)g_ffn[ch], chunk_k0(ch)});
       for (int b = 0; b < B; ++b) {
         for (int ch = 0; ch < chunks; ++ch)
-          un.reads.push_back({R_A, (uint16_t)l, (uint32_t)b, chunk_k0(ch) * kc_f,
-                              chunk_k0(ch + 1) * kc_f, chunk_k0(ch)});
+          un.reads.push_back({R_A, (uint16_t)l, (uint32_t)b, chunk_e0(ch), chunk_e0(ch + 1), chunk_k0(ch)});
         un.reads.push_back({R_HMID, (uint16_t)l, (uint32_t)b, r0, r1, 0});
         un.writes.push_back({R_HOUT, (uint16_t)l, (uint32_t)b, r0, r1, 0});
       }
@@ -309,7 +325,7 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
   for (uint32_t u = 0; u < n_lm; ++u) {
     uint32_t v0 = part_lo(V, n_lm, u), v1 = part_lo(V, n_lm, u + 1);
     Unit un;
-    un.in = gemv(OP_LM, L, v0, v1 - v0, 1, H, kc_h, u);
+    un.in = gemv(OP_LM, L, v0, v1 - v0, 1, H, kc_h, u, mfma);
     un.in.layer = (uint16_t)L;
     un.cu = (int)(u % C);
     un.waits.push_back({(uint32_t)g_down, 0});
@@ -344,7 +360,7 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
       in.wait_n = (uint32_t)un.waits.size();
       for (auto &w : un.waits) P.waits.push_back(w);
       if (in.pages) {
-        int64_t bytes = (int64_t)in.n_items * in.ipw * in.nk * in.pb;
+        int64_t bytes = (int64_t)in.n_items * in.ipw * in.rowb;  // K elements per row (no padding)
         cu_bytes[cu] += bytes;
         P.weight_bytes += bytes;
         P.n_pages += (int)in.pages;
@@ -353,8 +369,8 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
           err = "internal: too many rows in a unit";
           return MK_ERR_UNSUPPORTED;
         }
-        if ((B > 1 && in.kc > 256) || in.kc * (uint32_t)B > (uint32_t)kMaxKc) {
-          err = "internal: piece too long for the batched dot";
+        if (mfma && (in.kc != (uint32_t)kMfmaKc || in.n_items * in.ipw > (uint32_t)kMfmaRows)) {
+          err = "internal: MFMA unit shape";
           return MK_ERR_UNSUPPORTED;
         }
       }
@@ -365,6 +381,26 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
   }
   P.q_off[C] = (uint32_t)P.instr.size();
   P.max_cu_bytes = *std::max_element(cu_bytes.begin(), cu_bytes.end());
+  // greedy candidates: the LM units of one workgroup keep a running best per
+  // sequence in LDS and its last LM unit publishes it, so the arrival
+  // counter counts workgroups (LM groups), not units.  aux0 = group index,
+  // aux1 bit 0: first LM unit of its workgroup, bit 1: last.
+  P.n_lm_groups = 0;
+  for (int cu = 0; cu < C; ++cu) {
+    int first = -1, last = -1;
+    for (uint32_t qi = P.q_off[cu]; qi < P.q_off[cu + 1]; ++qi)
+      if (P.instr[qi].op == OP_LM) {
+        if (first < 0) first = (int)qi;
+        last = (int)qi;
+      }
+    if (first < 0) continue;
+    for (int qi = first; qi <= last; ++qi)
+      if (P.instr[qi].op == OP_LM) {
+        P.instr[qi].aux0 = (uint32_t)P.n_lm_groups;
+        P.instr[qi].aux1 = (qi == first ? 1u : 0u) | (qi == last ? 2u : 0u);
+      }
+    ++P.n_lm_groups;
+  }
   return MK_OK;
 }
 

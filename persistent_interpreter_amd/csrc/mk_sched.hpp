@@ -37,6 +37,7 @@ struct Access {
 struct Plan {
   int num_cus = 0, batch = 0, n_split = 0, split_len = 0, mlp_chunks = 0;
   int n_groups = 0;
+  int n_lm_groups = 0;              // workgroups holding LM units
   std::vector<Instr> instr;         // all per-CU queues back to back
   std::vector<uint32_t> q_off;      // [num_cus + 1]
   std::vector<Wait> waits;

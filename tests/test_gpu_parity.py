@@ -14,19 +14,34 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-2
 
 
-def _kv_bad(a, b):
+def _kv_bad(a, b, split_k=0):
     """Elements of two bf16 KV caches that differ by more than one bf16 ulp
-    of the larger magnitude plus fp32 noise (1e-4 of the RMS of the written
-    values): the two sides round fp32 values computed in different orders,
-    so a value near a rounding boundary, or near zero, may land one ulp (or
-    a sign) apart."""
+    of the larger magnitude plus the arithmetic's own error.
+
+    fp32 activations (batch 1): fp32 noise, 1e-4 of the RMS of the values
+    that differ; the two sides round fp32 values computed in different
+    orders, so a value near a rounding boundary, or near zero, may land one
+    ulp (or a sign) apart.
+
+    bf16 hi + lo activations (the batched MFMA path, ``split_k`` = the
+    projection's K): each activation x enters as hi + lo with
+    |x - hi - lo| <= 2^-16 |x| (two 8-bit mantissas), so a K-term projection
+    moves by at most 2^-16 sum|w_i x_i|, which for random signs is about
+    2^-16 sqrt(K) times the RMS of the outputs; the bar takes twice that."""
     fa = O.bf16_to_f32(a).astype(np.float64)
     fb = O.bf16_to_f32(b).astype(np.float64)
     d = np.abs(fa - fb)
     mag = np.maximum(np.abs(fa), np.abs(fb))
     ulp = np.exp2(np.floor(np.log2(np.maximum(mag, 1e-30))) - 7)
-    rms = float(np.sqrt(np.mean(fb[d > 0] ** 2))) if np.any(d > 0) else 1.0
-    bad = d > ulp + 1e-4 * rms
+    if split_k:
+        slack = 2.0 ** -15 * np.sqrt(split_k) * float(np.sqrt(np.mean(fb ** 2)))
+    else:
+        slack = 1e-4 * (float(np.sqrt(np.mean(fb[d > 0] ** 2))) if np.any(d > 0) else 1.0)
+    bad = d > ulp + slack
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, d, -1)), d.shape)
+        print(f"  worst KV element {tuple(int(x) for x in i)}: {fa[i]!r} vs {fb[i]!r}, "
+              f"ulp {ulp[i]:.3e}, slack {slack:.3e}")
     return int(bad.sum()), float(d.max()) if d.size else 0.0
 
 
@@ -125,14 +140,18 @@ def test_greedy_tokens_identical(name, steps):
     assert np.array_equal(gkv[:, :, :, :, untouched], kv[:, :, :, :, untouched])
 
 
-BATCHED = [("tiny", 3, 8), ("tiny", 8, 4), ("llama1b_b8", 8, 4)]
+BATCHED = [("tiny", 2, 32), ("tiny", 3, 8), ("tiny", 8, 8),
+           pytest.param("llama1b_b8", 8, 32, marks=pytest.mark.timeout(900))]
+
+
 @pytest.mark.parametrize("name,batch,steps", BATCHED)
 def test_batched_greedy_matches_oracle(name, batch, steps):
-    """Several sequences per step, each at its own position: the logits of
-    every sequence stay within TOL of the oracle's (teacher-forced on the
-    GPU's tokens, on the GPU's own KV history), the greedy tokens agree,
-    the K/V slot each sequence writes matches to one bf16 ulp, and no other
-    slot of the cache changes."""
+    """Several sequences per step in one launch (the batched kernel: MFMA
+    projections on bf16 hi + lo activations), each at its own position: the
+    logits of every sequence stay within TOL of the oracle's (teacher-forced
+    on the GPU's tokens, on the GPU's own KV history), the greedy tokens
+    agree, the K/V slot each sequence writes matches to one bf16 ulp plus
+    the split's own error, and no other slot of the cache changes."""
     mc = synth.CONFIGS[name]
     if mc.batch != batch or not mc.pos_hi:
         mc = mc.replace(batch=batch, pos_lo=4, pos_hi=40)
@@ -156,7 +175,7 @@ def test_batched_greedy_matches_oracle(name, batch, steps):
         assert np.array_equal(np.argmax(out_g[i], -1), np.argmax(ref, -1)), i
         for b in range(batch):
             s = int(pos[b]) + i
-            nb, _ = _kv_bad(gkv[:, :, b, :, s], work[:, :, b, :, s])
+            nb, _ = _kv_bad(gkv[:, :, b, :, s], work[:, :, b, :, s], split_k=mc.hidden)
             kv_bad += nb
             work[:, :, b, :, s] = gkv[:, :, b, :, s]
     print(f"{name} batch {batch}: {steps} steps, worst max|dlogit| {worst:.3e}, "
