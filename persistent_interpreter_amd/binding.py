@@ -251,10 +251,11 @@ class Megakernel:
             lib().mk_sync_status(h)
             lib().mk_destroy(h)
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
         # at interpreter shutdown the exit hook has already closed the
-        # handle; a finalizer that runs later must not call into HIP
-        if sys.is_finalizing():
+        # handle; a finalizer that runs later (module globals may be gone,
+        # hence the bound default) must not call into HIP
+        if _finalizing():
             return
         try:
             self.close()

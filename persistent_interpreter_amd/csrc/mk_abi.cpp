@@ -17,7 +17,7 @@
 
 namespace mk {
 hipError_t kernel_setup(int *blocks_per_cu);
-hipError_t kernel_launch(const Args &a, int grid, bool cooperative, hipStream_t stream);
+hipError_t kernel_launch(const Args &a, int grid, bool cooperative, bool paged, hipStream_t stream);
 }  // namespace mk
 
 using namespace mk;
@@ -87,7 +87,11 @@ int check_config(const mk_config *c, std::string &err) {
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) { err = "bad rms_eps or rope_theta"; return MK_ERR_INVALID_ARG; }
   if (c->n_q_heads % c->n_kv_heads) { err = "n_q_heads must be a multiple of n_kv_heads"; return MK_ERR_UNSUPPORTED; }
   if (c->head_dim != 64 && c->head_dim != 128) { err = "head_dim must be 64 or 128"; return MK_ERR_UNSUPPORTED; }
-  if (c->n_q_heads / c->n_kv_heads > kNCW) { err = "at most 8 query heads per KV head"; return MK_ERR_UNSUPPORTED; }
+  if (kNCW % (c->n_q_heads / c->n_kv_heads)) {
+    err = "query heads per KV head must divide 8 (1, 2, 4 or 8)";
+    return MK_ERR_UNSUPPORTED;
+  }
+  if (c->qk_norm && c->head_dim != 128) { err = "q/k norm needs head_dim 128"; return MK_ERR_UNSUPPORTED; }
   if (c->hidden % 8 || c->ffn_dim % 8) { err = "hidden and ffn_dim must be multiples of 8"; return MK_ERR_UNSUPPORTED; }
   if (c->kv_splits > kMaxSplits || c->kv_splits < 0) { err = "kv_splits must be in [0, 64]"; return MK_ERR_UNSUPPORTED; }
   if (c->mlp_chunks < 0 || c->num_cus < 0 || c->watchdog_ms < 0) { err = "negative knob"; return MK_ERR_INVALID_ARG; }
@@ -189,10 +193,6 @@ int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out) {
       return MK_ERR_INVALID_ARG;
     if (cfg->qk_norm && (!ly.q_norm || !ly.k_norm)) return MK_ERR_INVALID_ARG;
   }
-  // Per-head q/k norm (normed and rotated in the attention units) and the
-  // head_dim 128 attention code it ran on are switched off: a multi-step
-  // run of them faulted the GPU and the cause is not found yet.
-  if (cfg->qk_norm || cfg->head_dim != 64) return MK_ERR_UNSUPPORTED;
 
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return MK_ERR_NO_DEVICE;
@@ -311,7 +311,11 @@ static int get_plan(mk_handle *h, int batch, DevPlan **out) {
   uint32_t max_pages = 0;
   for (int c = 0; c < h->num_cus; ++c) {
     uint32_t np = 0;
-    for (uint32_t q = P.q_off[c]; q < P.q_off[c + 1]; ++q) np += P.instr[q].pages;
+    for (uint32_t q = P.q_off[c]; q < P.q_off[c + 1]; ++q) {
+      const Instr &in = P.instr[q];
+      // a paged attention unit streams at most a whole split
+      np += in.op == OP_ATTN && in.ppp ? (uint32_t)((P.split_len + in.ppp - 1) / in.ppp) : in.pages;
+    }
     max_pages = std::max(max_pages, np);
   }
   std::vector<uint32_t> iota(max_pages + 1);
@@ -395,7 +399,8 @@ static int launch_step(mk_handle *h, int32_t batch, const int32_t *tokens, const
     dp->greedy_epoch += 1;
     a.amax_target = dp->greedy_epoch * dp->n_arrive;
   }
-  if (kernel_launch(a, h->num_cus, (h->cfg.flags & MK_FLAG_COOPERATIVE) != 0, (hipStream_t)stream) != hipSuccess)
+  if (kernel_launch(a, h->num_cus, (h->cfg.flags & MK_FLAG_COOPERATIVE) != 0, dp->plan.paged_kv,
+                    (hipStream_t)stream) != hipSuccess)
     return MK_ERR_HIP;
   return MK_OK;
 }

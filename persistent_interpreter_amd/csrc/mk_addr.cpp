@@ -80,6 +80,78 @@ struct Bases {
 
 }  // namespace
 
+// Paged attention (attn_paged and load_kv_page of mk_kernel.hip): the K/V
+// page loads of one unit, and the compute waves' global accesses.
+static void paged_kv_loads(Model &M, const Bases &B, const Plan &P, const mk_config &c, const Instr &d, int p,
+                           uint32_t &n) {
+  const int MB = c.max_batch, nkv = c.n_kv_heads, S = c.max_seq, hd = c.head_dim;
+  const int CPR = hd / 8, RPL = 64 / CPR, RPP = 8 * RPL;
+  const int lo = (int)d.aux1 * P.split_len, hi = std::min(lo + P.split_len, p + 1);
+  const uint32_t nr = (uint32_t)std::max(0, std::min(hi, p) - lo);
+  const uint32_t np = (nr + RPP - 1) / RPP;
+  const uint64_t Kb = lay::kv(MB, nkv, S, hd, d.layer, 0, (int)d.b, (int)d.aux0, lo);
+  const uint64_t Vb = lay::kv(MB, nkv, S, hd, d.layer, 1, (int)d.b, (int)d.aux0, lo);
+  for (uint32_t jp = 0; jp < np; ++jp, ++n) {
+    for (int kvt = 0; kvt < 2; ++kvt)
+      for (uint32_t jj = 0; jj < 8; ++jj)
+        for (int lane = 0; lane < 64; ++lane) {
+          const uint32_t t = jj * RPL + lane / CPR, cp = lane % CPR;
+          uint32_t r = jp * RPP + t;
+          if (r >= nr) r = 0;
+          const uint32_t ch = kvt ? cp : (cp ^ (t & 7));
+          if (r >= (uint32_t)(hi - lo)) M.at(~0ull, 16, 0, "loader: K/V row outside its split");
+          M.el(B.kv, (kvt ? Vb : Kb) + (uint64_t)r * hd + ch * 8, 2, 16, "loader: K/V page row");
+        }
+    M.el(B.iota, n, 4, 4, "loader: K/V page sentinel");
+  }
+}
+
+static void paged_attn_compute(Model &M, const Bases &B, const Plan &P, const mk_config &c, const Instr &d, int p) {
+  const int MB = c.max_batch, nq = c.n_q_heads, nkv = c.n_kv_heads, S = c.max_seq, hd = c.head_dim;
+  const int G = nq / nkv, WPH = kNCW / G, CPR = hd / 8, DPL = hd / 64, ns = P.n_split;
+  const int b = (int)d.b, g = (int)d.aux0, s = (int)d.aux1;
+  const int lo = s * P.split_len, hi = std::min(lo + P.split_len, p + 1);
+  const bool has_p = p >= lo && p < hi;
+  for (int cw = 0; cw < kNCW; ++cw) {
+    const int h = cw % G, rp = cw / G, j = g * G + h;
+    if (rp != 0) continue;  // the other waves read LDS only
+    for (int lane = 0; lane < 64; ++lane) {
+      if (lo < hi) {
+        if (c.qk_norm && DPL == 2) {
+          for (int m = 0; m < DPL; ++m) {
+            M.el(B.q_norm[d.layer], lane + 64 * m, 2, 2, "attn(paged): q_norm weight");
+            M.el(B.k_norm[d.layer], lane + 64 * m, 2, 2, "attn(paged): k_norm weight");
+          }
+          M.el(B.rope, lay::rope(hd, p, lane), 4, 8, "attn(paged): RoPE of (lane, lane + 64)");
+        }
+        for (int m = 0; m < DPL; ++m) {
+          M.el(B.q, lay::q(MB, nq, hd, d.layer, b, j) + lane + 64 * m, 8, 8, "attn(paged): tagged q");
+          if (has_p) {
+            M.el(B.kvn, lay::kvn(MB, nkv, hd, d.layer, b, g, 0) + lane + 64 * m, 8, 8, "attn(paged): tagged K");
+            M.el(B.kvn, lay::kvn(MB, nkv, hd, d.layer, b, g, 0) + hd + lane + 64 * m, 8, 8, "attn(paged): tagged V");
+          }
+        }
+        if (c.qk_norm && DPL == 2 && has_p && h == 0) {
+          M.el(B.kv, lay::kv(MB, nkv, S, hd, d.layer, 0, b, g, p) + lane, 2, 2, "attn(paged): K store at p");
+          M.el(B.kv, lay::kv(MB, nkv, S, hd, d.layer, 0, b, g, p) + lane + 64, 2, 2, "attn(paged): K store at p");
+        }
+      }
+      if (has_p)
+        for (int i = 0; i < 8; ++i)
+          M.el(B.kvn, lay::kvn(MB, nkv, hd, d.layer, b, g, 0) + hd + (lane % CPR) * 8 + i, 8, 8,
+               "attn(paged): V of row p");
+      const uint64_t out = lay::part(MB, nq, ns, hd, d.layer, b, j, s);
+      if (lane < CPR)
+        for (int i = 0; i < 8; ++i) M.el(B.part, out + lane * 8 + i, 4, 4, "attn(paged): partial o");
+      if (lane == 0) {
+        M.el(B.part, out + hd, 4, 4, "attn(paged): partial m");
+        M.el(B.part, out + hd + 1, 4, 4, "attn(paged): partial l");
+      }
+    }
+  }
+  M.el(B.ctr, ((uint64_t)d.sig0 * kSlots + d.slot0) * kCtrStride, 4, 4, "attn(paged): counter signal");
+}
+
 // The batched (MFMA) kernel: sync_role_b, loader_role_b, compute_role_b and
 // unit_epilogue_b of mk_kernel.hip.
 static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_config &c, int batch, int num_cus,
@@ -190,6 +262,10 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
     uint32_t n = 0;
     for (uint32_t qi = q0; qi < q1; ++qi) {
       const Instr &d = P.instr[qi];
+      if (d.op == OP_ATTN && d.ppp) {
+        paged_kv_loads(M, B, P, c, d, pos[d.b], n);
+        continue;
+      }
       if (!is_gemv(d.op)) continue;
       const uint32_t R = d.n_items * d.ipw, nrb = d.ppp, K = d.rowb >> 1;
       const uint32_t nblk = (uint32_t)d.nk * nrb * 4;
@@ -224,7 +300,9 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
     for (uint32_t qi = q0; qi < q1; ++qi) {
       const Instr &d = P.instr[qi];
       const int b0 = (int)d.b;
-      if (d.op == OP_ATTN) {
+      if (d.op == OP_ATTN && d.ppp) {
+        paged_attn_compute(M, B, P, c, d, pos[b0]);
+      } else if (d.op == OP_ATTN) {
         const int g = (int)d.aux0, s = (int)d.aux1;
         const int DPL = hd / 64, PF = 20 / DPL, NR = DPL == 1 ? 16 : 8;
         const int p = pos[b0];
@@ -426,7 +504,10 @@ extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cu
   for (const Instr &in : P.instr) n_lm += in.op == OP_LM;
   for (int cu = 0; cu < num_cus; ++cu) {
     uint32_t np = 0;
-    for (uint32_t qi = P.q_off[cu]; qi < P.q_off[cu + 1]; ++qi) np += P.instr[qi].pages;
+    for (uint32_t qi = P.q_off[cu]; qi < P.q_off[cu + 1]; ++qi) {
+      const Instr &in = P.instr[qi];
+      np += in.op == OP_ATTN && in.ppp ? (uint32_t)((P.split_len + in.ppp - 1) / in.ppp) : in.pages;
+    }
     max_pages = std::max(max_pages, np);
   }
   B.amax = M.add("amax", (uint64_t)n_lm * MB * 8);
@@ -554,6 +635,10 @@ extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cu
       uint32_t n = 0;
       for (uint32_t qi = q0; qi < q1; ++qi) {
         const Instr &d = P.instr[qi];
+        if (d.op == OP_ATTN && d.ppp) {
+          paged_kv_loads(M, B, P, c, d, pos0, n);
+          continue;
+        }
         const bool gv = d.op == OP_QKV || d.op == OP_O || d.op == OP_FFN || d.op == OP_DOWN || d.op == OP_LM;
         if (!gv) continue;
         const uint32_t per = d.n_items * d.ipw, npieces = per * d.nk;
@@ -615,7 +700,9 @@ extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cu
       for (uint32_t qi = q0; qi < q1; ++qi) {
         const Instr &d = P.instr[qi];
         const int b = (int)d.b;
-        if (d.op == OP_ATTN) {
+        if (d.op == OP_ATTN && d.ppp) {
+          paged_attn_compute(M, B, P, c, d, pos0);
+        } else if (d.op == OP_ATTN) {
           const int g = (int)d.aux0, s = (int)d.aux1;
           const int DPL = hd / 64, PF = 20 / DPL, NR = DPL == 1 ? 16 : 8;
           const int p = pos0;

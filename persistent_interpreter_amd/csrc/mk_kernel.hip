@@ -414,6 +414,56 @@ __device__ __forceinline__ void wait_vm_n() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// --------------------------------------------------------------------------
+// Paged attention.  The K/V rows a split has from earlier steps (its
+// positions below p) are read-only during a step, like the weights, so the
+// loader streams them through the same page ring ahead of the unit's
+// dependency wait (the megakernel chapter "L'interpréteur sur GPU", section
+// 3.3: the next instruction's inputs load while the current one computes).
+// A page holds RPP rows: 8 wave-loads of K, then 8 of V.  K row t of a page
+// sits in wave-load t / RPL, its 16-byte chunk c at position c ^ (t & 7) of
+// the row, so a wave reading one chunk of 8 consecutive rows (one lane per
+// row) hits 8 different bank groups; V rows are stored as they are.
+// Attention descriptors of paged plans carry RPP in `ppp` (0: the register
+// path of attn_body).
+__device__ __forceinline__ size_t kv_off(const DevCtx &c, int l, int t, int b, int g, int s) {
+  return lay::kv(c.max_batch, c.nkv, c.max_seq, c.hd, l, t, b, g, s);
+}
+
+__device__ __forceinline__ void attn_geom(const Args &a, const Instr &d, int p, int &lo, int &hi, uint32_t &nr) {
+  lo = (int)d.aux1 * a.split_len;
+  hi = min(lo + a.split_len, p + 1);
+  nr = (uint32_t)max(0, min(hi, p) - lo);  // rows before p: from the cache
+}
+__device__ __forceinline__ uint32_t attn_pages(const Args &a, const Instr &d, int p) {
+  int lo, hi;
+  uint32_t nr;
+  attn_geom(a, d, p, lo, hi, nr);
+  return (nr + d.ppp - 1) / d.ppp;
+}
+template <int CPR>
+__device__ __forceinline__ void load_kv_page(const char *Kb, const char *Vb, uint32_t jp, uint32_t nr,
+                                             LDS_AS char *slot, int lane) {
+  constexpr uint32_t RPL = 64 / CPR, RPP = 8 * RPL, RB = CPR * 16;
+  const uint32_t t0 = (uint32_t)lane / CPR, cp = (uint32_t)lane % CPR;
+#pragma unroll
+  for (uint32_t jj = 0; jj < 8; ++jj) {
+    const uint32_t t = jj * RPL + t0;
+    uint32_t r = jp * RPP + t;
+    if (r >= nr) r = 0;  // past the split's rows: re-read its first row
+    __builtin_amdgcn_global_load_lds(Kb + (size_t)r * RB + (cp ^ (t & 7)) * 16, (LDS_AS void *)(slot + jj * 1024),
+                                     16, 0, kSC1);
+  }
+#pragma unroll
+  for (uint32_t jj = 0; jj < 8; ++jj) {
+    const uint32_t t = jj * RPL + t0;
+    uint32_t r = jp * RPP + t;
+    if (r >= nr) r = 0;
+    __builtin_amdgcn_global_load_lds(Vb + (size_t)r * RB + cp * 16, (LDS_AS void *)(slot + 8192 + jj * 1024), 16,
+                                     0, kSC1);
+  }
+}
+
 #ifndef MK_SDEPTH
 #define MK_SDEPTH 3
 #endif
@@ -424,6 +474,7 @@ static_assert(kSentDepth >= 1 && 17 * kSentDepth <= 63, "load counter range");
 // loader: its sentinel lands after its data, so the loader only waits for a
 // free ring slot (compute waves' releases) and, to bound its load counter,
 // for its oldest page once kSentDepth are in flight.
+template <bool PAGED>
 __device__ __forceinline__ void loader_role(const Env &e, const Args &a, int lw) {
   const int lane = lane_id();
   const uint32_t P = (uint32_t)e.cp->ring_pages;
@@ -439,6 +490,40 @@ __device__ __forceinline__ void loader_role(const Env &e, const Args &a, int lw)
   uint32_t n = 0;  // global page index
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
+    if (PAGED && d.op == OP_ATTN) {
+      int lo, hi;
+      uint32_t nr;
+      attn_geom(a, d, e.pos0, lo, hi, nr);
+      const uint32_t np = (nr + d.ppp - 1) / d.ppp;
+      const DevCtx &c = *e.cp;
+      const char *Kb = reinterpret_cast<const char *>(a.kv + kv_off(c, d.layer, 0, (int)d.b, (int)d.aux0, lo));
+      const char *Vb = reinterpret_cast<const char *>(a.kv + kv_off(c, d.layer, 1, (int)d.b, (int)d.aux0, lo));
+      for (uint32_t jp = 0; jp < np; ++jp, ++n) {
+        if ((int)(n % kNLW) != lw) continue;
+        if (n >= P && min_cons() < n - P + 1) {
+          const uint32_t need = n - P + 1;
+          Watchdog wd;
+          for (uint32_t it = 1;; ++it) {
+            __builtin_amdgcn_s_sleep(MK_LSLEEP);
+            if (min_cons() >= need) break;
+            if ((it & 63) == 0) {
+              if (__builtin_amdgcn_readfirstlane(asm_lds_ld(L_ABORT))) { wait_vm0(); return; }
+              if (wd.expired(e.cp->watchdog_ticks)) { raise_error(e, 0xB0000000u | qi, n); wait_vm0(); return; }
+            }
+          }
+        }
+        if (npend == kSentDepth) {
+          wait_vm_n<17 * (kSentDepth - 1)>();
+          --npend;
+        }
+        LDS_AS char *slot = (LDS_AS char *)smem + L_RING + (n % P) * kPageBytes;
+        if (c.hd == 64) load_kv_page<8>(Kb, Vb, jp, nr, slot, lane);
+        else load_kv_page<16>(Kb, Vb, jp, nr, slot, lane);
+        __builtin_amdgcn_global_load_lds(a.iota + n, (LDS_AS void *)(smem + L_SENT + (n % P) * kSentBytes), 4, 0, 0);
+        ++npend;
+      }
+      continue;
+    }
     if (!is_gemv(d.op)) continue;
     const uint32_t per = d.n_items * d.ipw;
     const uint32_t npieces = per * d.nk;
@@ -870,9 +955,6 @@ __device__ __forceinline__ void load_x(const float *xs, uint32_t n16, float (&xr
   }
 }
 
-__device__ __forceinline__ size_t kv_off(const DevCtx &c, int l, int t, int b, int g, int s) {
-  return lay::kv(c.max_batch, c.nkv, c.max_seq, c.hd, l, t, b, g, s);
-}
 
 // Epilogue of a finished GEMV instruction, run by its last compute wave
 // over the staged row results R (LDS): row i*ipw + s of the unit.  The
@@ -1017,9 +1099,11 @@ __device__ __forceinline__ void lm_greedy_finish(const Env &e, const Args &a) {
   }
 }
 
-// The first PF positions of the split that precede p are step-invariant
-// (written by earlier steps), so their K/V are loaded before the unit's
-// dependency gate; q and the new slot p are loaded after it.
+// I2 on registers (head_dim 64, splits of at most PF positions beyond the
+// prefetch; the paged body takes every other case).  The first PF
+// positions of the split that precede p are step-invariant (written by
+// earlier steps), so their K/V are loaded before the unit's dependency
+// gate; q and the new slot p are loaded after it.
 template <int DPL, class Gate>
 __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, int p, Gate gate) {
   const DevCtx &c = *e.cp;
@@ -1044,22 +1128,6 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, in
       }
     }
   }
-  // q/k norm (head_dim 128 only): weights of dims lane and lane + 64, and
-  // the RoPE cos/sin of pair (lane, lane + 64) at position p, before the gate
-  float qnw[DPL], knw[DPL], rc = 0.f, rsn = 0.f;
-  if constexpr (DPL == 2) {
-    if (c.qk_norm) {
-      const uint16_t *qn = G(c.layers)[d.layer].q_norm, *kn = G(c.layers)[d.layer].k_norm;
-#pragma unroll
-      for (int m = 0; m < DPL; ++m) {
-        qnw[m] = bf16f(G(qn)[lane + 64 * m]);
-        knw[m] = bf16f(G(kn)[lane + 64 * m]);
-      }
-      const uint64_t csw = *G(reinterpret_cast<const uint64_t *>(c.rope + lay::rope(hd, p, lane)));
-      rc = __uint_as_float((uint32_t)csw);
-      rsn = __uint_as_float((uint32_t)(csw >> 32));
-    }
-  }
   if (!gate()) return false;
   float mrun = -INFINITY, lrun = 0.f, o[DPL], q[DPL];
   uint16_t kp[DPL], vp[DPL];
@@ -1072,7 +1140,6 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, in
     // from the cache
     const rsrc_t nr = rsrc(c.kvn_buf + lay::kvn(c.max_batch, c.nkv, hd, d.layer, b, g, 0));
     const bool has_p = p < hi;
-    float kraw[DPL];
     auto load = [&]() -> bool {
       bool ok = true;
 #pragma unroll
@@ -1081,11 +1148,9 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, in
         q[m] = tval(wq);
         ok = ok && tok(wq, a.tag);
         kp[m] = vp[m] = 0;
-        kraw[m] = 0.f;
         if (has_p) {
           const uint64_t wk = ldt(nr, (uint32_t)(lane + 64 * m)), wv = ldt(nr, (uint32_t)(hd + lane + 64 * m));
-          kraw[m] = tval(wk);
-          kp[m] = (uint16_t)((uint32_t)wk >> 16);  // exact when K arrives rounded (no q/k norm)
+          kp[m] = (uint16_t)((uint32_t)wk >> 16);  // exact: K and V arrive rounded to bf16
           vp[m] = (uint16_t)((uint32_t)wv >> 16);
           ok = ok && tok(wk, a.tag) && tok(wv, a.tag);
         }
@@ -1093,31 +1158,6 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, in
       return ok;
     };
     if (!until_tagged(e, load, 0x800 | d.unit)) return false;
-    if constexpr (DPL == 2) {
-      if (c.qk_norm) {
-        // RMSNorm over the head (eps inside the root, weight after), then
-        // RoPE of pair (lane, lane + 64); K is rounded to bf16 and the unit
-        // whose split holds p writes it to the cache (wave of head 0)
-        auto norm_rope = [&](float (&u)[DPL], const float (&w)[DPL]) {
-          const float ss = wave_sum(u[0] * u[0] + u[1] * u[1]);
-          const float r = 1.0f / sqrtf(ss / (float)hd + c.eps);
-          const float a0 = u[0] * r * w[0], a1 = u[1] * r * w[1];
-          u[0] = a0 * rc - a1 * rsn;
-          u[1] = a1 * rc + a0 * rsn;
-        };
-        norm_rope(q, qnw);
-        if (has_p) {
-          norm_rope(kraw, knw);
-          kp[0] = f2bf(kraw[0]);
-          kp[1] = f2bf(kraw[1]);
-          if (h == 0) {
-            uint16_t *kc = a.kv + kv_off(c, d.layer, 0, b, g, p);
-            st_c16(kc + lane, kp[0]);
-            st_c16(kc + lane + 64, kp[1]);
-          }
-        }
-      }
-    }
     // first PF positions from the prefetched registers
     {
       float sc = -INFINITY;
@@ -1207,6 +1247,264 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, in
   return true;
 }
 
+// I2 on paged K/V (head_dim 128, and splits longer than attn_body's register
+// prefetch).  All compute waves work: wave cw takes query head h = cw % G
+// and every WPH-th page of the split (WPH = 8 / G waves per head), so each
+// K/V page is read from HBM once and from LDS by the G waves of its heads.
+// Scores run one lane per row (a whole K row against q, no cross-lane
+// reduction), P.V one 16-byte V chunk per lane; each wave keeps a running
+// (m, l, o) and the WPH partials of a head are merged in LDS in wave order,
+// so the result does not depend on timing.  The waves of rp == 0 fetch q
+// (and, in the split holding p, this step's K/V from the tagged words),
+// apply the per-head q/k RMSNorm and RoPE when the model has them, write
+// the rotated, rounded K of slot p to the cache (head 0's wave), stage q in
+// LDS for the other waves of the head, and fold row p into their partial.
+// LDS: the unit's activation slot (an attention unit takes no activation
+// piece) holds q [G][hd] and the merge area [G][WPH-1][hd + 2].
+template <int DPL>
+__device__ bool attn_paged(const Env &e, const Args &a, const Instr &d, int cw, int p, uint32_t n, uint32_t seq,
+                           uint32_t &aq_t, uint32_t &am_t, int ring, int sent, uint32_t P, int xso) {
+  const DevCtx &c = *e.cp;
+  const int lane = lane_id();
+  constexpr int hd = 64 * DPL, CPR = hd / 8, RPL = 64 / CPR, RPP = 8 * RPL;
+  const int GQ = c.G, WPH = kNCW / GQ;
+  const int h = cw % GQ, rp = cw / GQ;
+  const int b = (int)d.b, g = (int)d.aux0, s = (int)d.aux1, j = g * GQ + h;
+  int lo, hi;
+  uint32_t nr;
+  attn_geom(a, d, p, lo, hi, nr);
+  const uint32_t np = (nr + RPP - 1) / RPP;
+  const bool has_p = p >= lo && p < hi;
+  float *Q = reinterpret_cast<float *>(smem + xso);
+  float *MG = Q + GQ * hd + h * (WPH - 1) * (hd + 2);
+  aq_t += (uint32_t)GQ;
+  am_t += (uint32_t)(GQ * (WPH - 1));
+  if (!spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq; }, 0x210)) return false;
+  float qv[DPL], kpv[DPL];
+#pragma unroll
+  for (int m = 0; m < DPL; ++m) qv[m] = kpv[m] = 0.f;
+  const rsrc_t nrr = rsrc(c.kvn_buf + lay::kvn(c.max_batch, c.nkv, hd, d.layer, b, g, 0));
+  if (rp == 0) {
+    if (lo < hi) {
+      float qnw[DPL], knw[DPL], rc = 0.f, rsn = 0.f;
+      if constexpr (DPL == 2) {
+        if (c.qk_norm) {
+          // norm weights of dims lane and lane + 64, RoPE of pair (lane, lane + 64)
+          const uint16_t *qn = G(c.layers)[d.layer].q_norm, *kn = G(c.layers)[d.layer].k_norm;
+#pragma unroll
+          for (int m = 0; m < DPL; ++m) {
+            qnw[m] = bf16f(G(qn)[lane + 64 * m]);
+            knw[m] = bf16f(G(kn)[lane + 64 * m]);
+          }
+          const uint64_t csw = *G(reinterpret_cast<const uint64_t *>(c.rope + lay::rope(hd, p, lane)));
+          rc = __uint_as_float((uint32_t)csw);
+          rsn = __uint_as_float((uint32_t)(csw >> 32));
+        }
+      }
+      const rsrc_t qr = rsrc(c.q_buf + lay::q(c.max_batch, c.nq, hd, d.layer, b, j));
+      auto load = [&]() -> bool {
+        bool ok = true;
+#pragma unroll
+        for (int m = 0; m < DPL; ++m) {
+          const uint64_t wq = ldt(qr, (uint32_t)(lane + 64 * m));
+          qv[m] = tval(wq);
+          ok = ok && tok(wq, a.tag);
+          if (has_p) {
+            const uint64_t wk = ldt(nrr, (uint32_t)(lane + 64 * m)), wv = ldt(nrr, (uint32_t)(hd + lane + 64 * m));
+            kpv[m] = tval(wk);
+            ok = ok && tok(wk, a.tag) && tok(wv, a.tag);
+          }
+        }
+        return ok;
+      };
+      if (!until_tagged(e, load, 0x800 | d.unit)) return false;
+      if constexpr (DPL == 2) {
+        if (c.qk_norm) {
+          // RMSNorm over the head (eps inside the root, weight after), RoPE of
+          // (lane, lane + 64); K of slot p is rounded to bf16 like the cache
+          auto norm_rope = [&](float (&u)[DPL], const float (&w)[DPL]) {
+            const float ss = wave_sum(u[0] * u[0] + u[1] * u[1]);
+            const float r = 1.0f / sqrtf(ss / (float)hd + c.eps);
+            const float a0 = u[0] * r * w[0], a1 = u[1] * r * w[1];
+            u[0] = a0 * rc - a1 * rsn;
+            u[1] = a1 * rc + a0 * rsn;
+          };
+          norm_rope(qv, qnw);
+          if (has_p) {
+            norm_rope(kpv, knw);
+            const uint16_t k0 = f2bf(kpv[0]), k1 = f2bf(kpv[1]);
+            kpv[0] = bf16f(k0);
+            kpv[1] = bf16f(k1);
+            if (h == 0) {
+              uint16_t *kc = a.kv + kv_off(c, d.layer, 0, b, g, p);
+              st_c16(kc + lane, k0);
+              st_c16(kc + lane + 64, k1);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < DPL; ++m) Q[h * hd + lane + 64 * m] = qv[m];
+    }
+    wait_lgkm0();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane == 0) __hip_atomic_fetch_add(&lds_u32(L_AQ), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    wake();
+  } else {
+    if (!spin_lds(e, [&]() { return lds_ld(L_AQ) >= aq_t; }, 0x710)) return false;
+  }
+  // this wave's pages: running (m, l) per head and o over the 8 dims of
+  // chunk lane % CPR, summed over the rows of lane / CPR
+  float m_run = -INFINITY, l_run = 0.f, o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  const float *Qh = Q + h * hd;
+  const uint32_t t = (uint32_t)lane % RPP, hh = (uint32_t)lane / RPP;  // row of a page, half of it (hd 128)
+  uint32_t rel = n;
+  for (uint32_t jp = (uint32_t)rp; jp < np; jp += (uint32_t)WPH) {
+    const uint32_t pg = n + jp;
+    if (pg > rel) {
+      if (lane == 0) lds_st(L_CONS + 4 * cw, pg);
+      rel = pg;
+      wake();
+    }
+    if (!spin_lds_fast(e, [&]() { return lds_ld(sent + (pg % P) * kSentBytes) == pg; }, 0x310)) return false;
+    const uint32_t pb = (uint32_t)ring + (pg % P) * kPageBytes;
+    // scores: lane t against K row t (chunks hh*8 .. hh*8+7), four chunks
+    // in flight at a time
+    const uint32_t rowa = lds_addr((int)(pb + (t / RPL) * 1024 + (t % RPL) * CPR * 16));
+    float sc0 = 0.f, sc1 = 0.f;
+#pragma unroll
+    for (int c0 = 0; c0 < 8; c0 += 4) {
+      u4 kc[4];
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %5\n\t"
+          "ds_read_b128 %2, %6\n\t"
+          "ds_read_b128 %3, %7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(kc[0]), "=&v"(kc[1]), "=&v"(kc[2]), "=&v"(kc[3])
+          : "v"(rowa + (((hh * 8 + c0 + 0) ^ (t & 7)) << 4)), "v"(rowa + (((hh * 8 + c0 + 1) ^ (t & 7)) << 4)),
+            "v"(rowa + (((hh * 8 + c0 + 2) ^ (t & 7)) << 4)), "v"(rowa + (((hh * 8 + c0 + 3) ^ (t & 7)) << 4)));
+#pragma unroll
+      for (int ci = 0; ci < 4; ++ci) {
+        const f4 q0 = *reinterpret_cast<const f4 *>(Qh + (hh * 8 + c0 + ci) * 8);
+        const f4 q1 = *reinterpret_cast<const f4 *>(Qh + (hh * 8 + c0 + ci) * 8 + 4);
+        sc0 = fmaf(q0.x, bf_lo(kc[ci].x), sc0);
+        sc1 = fmaf(q0.y, bf_hi(kc[ci].x), sc1);
+        sc0 = fmaf(q0.z, bf_lo(kc[ci].y), sc0);
+        sc1 = fmaf(q0.w, bf_hi(kc[ci].y), sc1);
+        sc0 = fmaf(q1.x, bf_lo(kc[ci].z), sc0);
+        sc1 = fmaf(q1.y, bf_hi(kc[ci].z), sc1);
+        sc0 = fmaf(q1.z, bf_lo(kc[ci].w), sc0);
+        sc1 = fmaf(q1.w, bf_hi(kc[ci].w), sc1);
+      }
+    }
+    float sc = sc0 + sc1;
+    if constexpr (DPL == 2) sc += __shfl_xor(sc, 32);
+    sc *= c.attn_scale;
+    const bool valid = (uint32_t)lane < (uint32_t)RPP && jp * RPP + t < nr;
+    const float cm = wave_max(valid ? sc : -INFINITY);
+    const float mn = fmaxf(m_run, cm);
+    const float pt = valid ? expf(sc - mn) : 0.f;
+    const float scl = m_run == -INFINITY ? 0.f : expf(m_run - mn);
+    l_run = l_run * scl + wave_sum(pt);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] *= scl;
+    m_run = mn;
+    // P.V: wave-load jv holds rows jv*RPL + lane / CPR, chunk lane % CPR
+    const uint32_t va = lds_addr((int)(pb + 8192 + lane * 16));
+#pragma unroll
+    for (int j0 = 0; j0 < 8; j0 += 4) {
+      u4 vc[4];
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %4 offset:1024\n\t"
+          "ds_read_b128 %2, %4 offset:2048\n\t"
+          "ds_read_b128 %3, %4 offset:3072\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(vc[0]), "=&v"(vc[1]), "=&v"(vc[2]), "=&v"(vc[3])
+          : "v"(va + j0 * 1024));
+#pragma unroll
+      for (int jv = 0; jv < 4; ++jv) {
+        const float w = __shfl(pt, (j0 + jv) * RPL + lane / CPR);
+        o[0] = fmaf(w, bf_lo(vc[jv].x), o[0]);
+        o[1] = fmaf(w, bf_hi(vc[jv].x), o[1]);
+        o[2] = fmaf(w, bf_lo(vc[jv].y), o[2]);
+        o[3] = fmaf(w, bf_hi(vc[jv].y), o[3]);
+        o[4] = fmaf(w, bf_lo(vc[jv].z), o[4]);
+        o[5] = fmaf(w, bf_hi(vc[jv].z), o[5]);
+        o[6] = fmaf(w, bf_lo(vc[jv].w), o[6]);
+        o[7] = fmaf(w, bf_hi(vc[jv].w), o[7]);
+      }
+    }
+  }
+  // one o per chunk: lanes of the same chunk hold different rows' sums
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    for (int off = CPR; off < 64; off <<= 1) o[i] += __shfl_xor(o[i], off);
+  if (rp == 0 && has_p) {
+    // row p: this step's K and V (the tagged words this wave verified)
+    float pr = 0.f;
+#pragma unroll
+    for (int m = 0; m < DPL; ++m) pr = fmaf(qv[m], kpv[m], pr);
+    const float sp = wave_sum(pr) * c.attn_scale;
+    const float mn = fmaxf(m_run, sp);
+    const float scl = m_run == -INFINITY ? 0.f : expf(m_run - mn);
+    const float wp = expf(sp - mn);
+    l_run = l_run * scl + wp;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = fmaf(wp, tval(ldt(nrr, (uint32_t)(hd + (lane % CPR) * 8 + i))), o[i] * scl);
+    m_run = mn;
+  }
+  // merge the head's WPH partials in wave order
+  if (WPH > 1) {
+    if (rp > 0) {
+      float *dst = MG + (rp - 1) * (hd + 2);
+      if (lane < CPR) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[lane * 8 + i] = o[i];
+      }
+      if (lane == 0) {
+        dst[hd] = m_run;
+        dst[hd + 1] = l_run;
+      }
+      wait_lgkm0();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (lane == 0) __hip_atomic_fetch_add(&lds_u32(L_AM), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      wake();
+    } else {
+      if (!spin_lds(e, [&]() { return lds_ld(L_AM) >= am_t; }, 0x720)) return false;
+      for (int r = 1; r < WPH; ++r) {
+        const float *src = MG + (r - 1) * (hd + 2);
+        const float mr = src[hd], lr = src[hd + 1];
+        if (mr == -INFINITY) continue;  // a part with no rows
+        const float M = fmaxf(m_run, mr);
+        const float fa = m_run == -INFINITY ? 0.f : expf(m_run - M), fb = expf(mr - M);
+        l_run = l_run * fa + lr * fb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = o[i] * fa + (lane < CPR ? src[lane * 8 + i] : 0.f) * fb;
+        m_run = M;
+      }
+    }
+  }
+  if (rp == 0) {
+    float *out = a.part_buf + lay::part(c.max_batch, c.nq, a.n_split, hd, d.layer, b, j, s);
+    if (lane < CPR) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st_c(out + lane * 8 + i, o[i]);
+    }
+    if (lane == 0) {
+      st_c(out + hd, m_run);
+      st_c(out + hd + 1, l_run);
+    }
+  }
+  wait_lgkm0();
+  if (lane == 0) lds_st(L_CONS + 4 * cw, n + np);
+  wake();
+  return true;
+}
+
 // I3: log-sum-exp combine of the split partials of query head (g*G + h):
 // m* = max m_s, w_s = exp(m_s - m*), out = sum w_s o_s / sum w_s l_s; empty
 // splits (m = -inf) get weight 0.
@@ -1263,21 +1561,32 @@ __device__ __forceinline__ void red_body(const Env &e, const Args &a, const Inst
   for (int m = 0; m < dpl; ++m) st_c(out + lane + 64 * m, o[m] / L);
 }
 
+template <bool PAGED>
 __device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
   const uint32_t P = (uint32_t)c.ring_pages;
   float *acc = reinterpret_cast<float *>(smem + L_ACC);
-  uint32_t n = 0, seq = 0;
+  uint32_t n = 0, seq = 0, aq_t = 0, am_t = 0;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
     const bool gv = is_gemv(d.op);
     const uint32_t nx = gv ? d.nk : 1;
+    uint32_t upages = d.pages;
     // gate: the first activation piece of the instruction is produced
     auto gate = [&]() { return spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq; }, 0x200 | qi); };
-    if (d.op == OP_ATTN && cw < c.G) {
-      const bool ok = c.hd == 64 ? attn_body<1>(e, a, d, cw, e.pos0, gate) : attn_body<2>(e, a, d, cw, e.pos0, gate);
+    if (PAGED && d.op == OP_ATTN) {
+      upages = attn_pages(a, d, e.pos0);
+      const int xso = L_XS + (int)((seq % kNXS) * kXSlotBytes);
+      bool ok = false;
+      if constexpr (PAGED)
+        ok = c.hd == 64 ? attn_paged<1>(e, a, d, cw, e.pos0, n, seq, aq_t, am_t, L_RING, L_SENT, P, xso)
+                        : attn_paged<2>(e, a, d, cw, e.pos0, n, seq, aq_t, am_t, L_RING, L_SENT, P, xso);
       if (!ok) return;
+    } else if (!PAGED && d.op == OP_ATTN && cw < c.G) {
+      // head_dim 64, splits within the register prefetch
+      if constexpr (!PAGED)
+        if (!attn_body<1>(e, a, d, cw, e.pos0, gate)) return;
     } else if (!gate()) {
       return;
     }
@@ -1338,7 +1647,7 @@ __device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw
         else red_body<2>(e, a, d, cw);
       }
     }
-    n += d.pages;
+    n += upages;
     seq += nx;
     if (lane == 0) lds_st(L_XCONS + 4 * cw, seq);
     wake();
@@ -1473,6 +1782,7 @@ __device__ __forceinline__ const char *row_start(const Instr &d, const uint64_t 
   return reinterpret_cast<const char *>(base);
 }
 
+template <bool PAGED>
 __device__ __forceinline__ void loader_role_b(const Env &e, const Args &a, int lw) {
   const int lane = lane_id();
   constexpr uint32_t P = kRingPagesB;
@@ -1488,6 +1798,40 @@ __device__ __forceinline__ void loader_role_b(const Env &e, const Args &a, int l
   uint32_t n = 0;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
+    if (PAGED && d.op == OP_ATTN) {
+      const DevCtx &c = *e.cp;
+      int lo, hi;
+      uint32_t nr;
+      attn_geom(a, d, seq_pos(a, c, (int)d.b), lo, hi, nr);
+      const uint32_t np = (nr + d.ppp - 1) / d.ppp;
+      const char *Kb = reinterpret_cast<const char *>(a.kv + kv_off(c, d.layer, 0, (int)d.b, (int)d.aux0, lo));
+      const char *Vb = reinterpret_cast<const char *>(a.kv + kv_off(c, d.layer, 1, (int)d.b, (int)d.aux0, lo));
+      for (uint32_t jp = 0; jp < np; ++jp, ++n) {
+        if ((int)(n % kNLW) != lw) continue;
+        if (n >= P && min_cons() < n - P + 1) {
+          const uint32_t need = n - P + 1;
+          Watchdog wd;
+          for (uint32_t it = 1;; ++it) {
+            __builtin_amdgcn_s_sleep(MK_LSLEEP);
+            if (min_cons() >= need) break;
+            if ((it & 63) == 0) {
+              if (__builtin_amdgcn_readfirstlane(asm_lds_ld(L_ABORT))) { wait_vm0(); return; }
+              if (wd.expired(e.cp->watchdog_ticks)) { raise_error(e, 0xB0000000u | qi, n); wait_vm0(); return; }
+            }
+          }
+        }
+        if (npend == kSentDepth) {
+          wait_vm_n<17 * (kSentDepth - 1)>();
+          --npend;
+        }
+        LDS_AS char *slot = (LDS_AS char *)smem + LB_RING + (n % P) * kPageBytes;
+        if (c.hd == 64) load_kv_page<8>(Kb, Vb, jp, nr, slot, lane);
+        else load_kv_page<16>(Kb, Vb, jp, nr, slot, lane);
+        __builtin_amdgcn_global_load_lds(a.iota + n, (LDS_AS void *)(smem + LB_SENT + (n % P) * kSentBytes), 4, 0, 0);
+        ++npend;
+      }
+      continue;
+    }
     if (!is_gemv(d.op)) continue;
     const uint32_t R = d.n_items * d.ipw, nrb = d.ppp, K = d.rowb >> 1;
     const uint32_t nblk = (uint32_t)d.nk * nrb * 4;
@@ -1593,12 +1937,9 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
         trace_put(e, qi, 0, (uint64_t)d.op | ((uint64_t)d.layer << 8) | ((uint64_t)d.unit << 24));
         trace_now(e, qi, 1);
       }
-      if (!is_gemv(d.op)) {
-        // attention and reduction units take no activation piece
-        if (lane == 0) lds_st(L_XREADY, seq + 1);
-        wake();
-        continue;
-      }
+      // the slot of this piece is free once every compute wave released
+      // the piece two before it (a paged attention unit uses its slot for q
+      // and its merge; a reduction unit takes no piece)
       if (seq >= (uint32_t)kNXS) {
         const uint32_t need = seq - kNXS + 1;
         auto freed = [&]() {
@@ -1609,6 +1950,11 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
           return m >= need;
         };
         if (!spin_lds(e, freed, 0x100 | qi)) return;
+      }
+      if (!is_gemv(d.op)) {
+        if (lane == 0) lds_st(L_XREADY, seq + 1);
+        wake();
+        continue;
       }
       if (normed && k == 0) {
         // 1/rms of every sequence's input (each lane keeps its own)
@@ -1830,20 +2176,30 @@ __device__ __forceinline__ void lm_greedy_finish_b(const Env &e, const Args &a) 
   }
 }
 
+template <bool PAGED>
 __device__ __forceinline__ void compute_role_b(const Env &e, const Args &a, int cw) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
   constexpr uint32_t P = kRingPagesB;
-  uint32_t n = 0, seq = 0;
+  uint32_t n = 0, seq = 0, aq_t = 0, am_t = 0;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
     const bool gv = is_gemv(d.op);
     const uint32_t nx = gv ? d.nk : 1;
+    uint32_t upages = d.pages;
     auto gate = [&]() { return spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq; }, 0x200 | qi); };
-    if (d.op == OP_ATTN && cw < c.G) {
+    if (PAGED && d.op == OP_ATTN) {
       const int p = seq_pos(a, c, (int)d.b);
-      const bool ok = c.hd == 64 ? attn_body<1>(e, a, d, cw, p, gate) : attn_body<2>(e, a, d, cw, p, gate);
+      upages = attn_pages(a, d, p);
+      const int xso = LB_XS + (int)((seq % kNXS) * kXSlotB);
+      bool ok = false;
+      if constexpr (PAGED)
+        ok = c.hd == 64 ? attn_paged<1>(e, a, d, cw, p, n, seq, aq_t, am_t, LB_RING, LB_SENT, P, xso)
+                        : attn_paged<2>(e, a, d, cw, p, n, seq, aq_t, am_t, LB_RING, LB_SENT, P, xso);
       if (!ok) return;
+    } else if (!PAGED && d.op == OP_ATTN && cw < c.G) {
+      if constexpr (!PAGED)
+        if (!attn_body<1>(e, a, d, cw, seq_pos(a, c, (int)d.b), gate)) return;
     } else if (!gv && !gate()) {
       return;
     }
@@ -1913,7 +2269,7 @@ __device__ __forceinline__ void compute_role_b(const Env &e, const Args &a, int 
         else red_body<2>(e, a, d, cw);
       }
     }
-    n += d.pages;
+    n += upages;
     seq += nx;
     if (lane == 0) lds_st(L_XCONS + 4 * cw, seq);
     wake();
@@ -1952,6 +2308,10 @@ __device__ __forceinline__ void compute_role_b(const Env &e, const Args &a, int 
   }
 }
 
+// PAGED: the plan's attention units stream their K/V through pages (each
+// plan is one or the other; separate instantiations keep the register
+// allocation of the register-path kernel unchanged)
+template <bool PAGED>
 __global__ void __launch_bounds__(kThreads, 1)
 mk_interp_b(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const uint32_t *__restrict__ q_off,
             const Wait *__restrict__ waits, const uint64_t *__restrict__ rowtab, uint32_t *__restrict__ ctr,
@@ -1977,12 +2337,13 @@ mk_interp_b(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, con
     lds_u32(LB_SENT + 4 * i) = 0xffffffffu;
   __syncthreads();
   const int w = (int)(threadIdx.x >> 6);
-  if (w < kNCW) compute_role_b(e, a, w);
-  else if (w < kNCW + kNLW) loader_role_b(e, a, w - kNCW);
+  if (w < kNCW) compute_role_b<PAGED>(e, a, w);
+  else if (w < kNCW + kNLW) loader_role_b<PAGED>(e, a, w - kNCW);
   else sync_role_b(e, a);
 }
 
 // --------------------------------------------------------------------------
+template <bool PAGED>
 __global__ void __launch_bounds__(kThreads, 1)
 mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const uint32_t *__restrict__ q_off,
           const Wait *__restrict__ waits, const uint64_t *__restrict__ rowtab, uint32_t *__restrict__ ctr, const uint32_t *__restrict__ grp_target,
@@ -2018,8 +2379,8 @@ mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const
   if (w >= kNCW + kNLW) __builtin_amdgcn_s_setprio(3);
   else if (w < kNCW) __builtin_amdgcn_s_setprio(1);
 #endif
-  if (w < kNCW) compute_role(e, a, w);
-  else if (w < kNCW + kNLW) loader_role(e, a, w - kNCW);
+  if (w < kNCW) compute_role<PAGED>(e, a, w);
+  else if (w < kNCW + kNLW) loader_role<PAGED>(e, a, w - kNCW);
   else sync_role(e, a);
 }
 
@@ -2029,21 +2390,23 @@ mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const
 // Host-side launch helpers (the ABI layer is plain C++).
 namespace mk {
 
+static const void *const kKernels[4] = {(const void *)mk_interp<false>, (const void *)mk_interp<true>,
+                                        (const void *)mk_interp_b<false>, (const void *)mk_interp_b<true>};
+
 hipError_t kernel_setup(int *blocks_per_cu) {
-  hipError_t e = hipFuncSetAttribute((const void *)mk_interp, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     kLdsBytes);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void *)mk_interp_b, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-  if (e != hipSuccess) return e;
-  int nb = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mk_interp_b, kThreads, kLdsBytes);
-  if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, mk_interp, kThreads, kLdsBytes);
-  if (nb < *blocks_per_cu) *blocks_per_cu = nb;
-  return e;
+  *blocks_per_cu = 1 << 30;
+  for (const void *fn : kKernels) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, kLdsBytes);
+    if (e != hipSuccess) return e;
+    if (nb < *blocks_per_cu) *blocks_per_cu = nb;
+  }
+  return hipSuccess;
 }
 
-hipError_t kernel_launch(const Args &a0, int grid, bool cooperative, hipStream_t stream) {
+hipError_t kernel_launch(const Args &a0, int grid, bool cooperative, bool paged, hipStream_t stream) {
   Args a = a0;
   void *params[] = {&a.ctx, &a.instr, &a.q_off, &a.waits, &a.rowtab, &a.ctr, &a.grp_target, &a.part_buf, &a.iota,
                     &a.tokens, &a.positions, &a.kv, &a.logits, &a.trace, &a.trace_stride, &a.epoch, &a.tag,
@@ -2052,8 +2415,9 @@ hipError_t kernel_launch(const Args &a0, int grid, bool cooperative, hipStream_t
   // One workgroup per CU fits (checked at create); a plain launch places all
   // of them at once on an otherwise idle device, a cooperative one also
   // waits for room when other work holds CUs (about 23 us more per launch).
-  // batches of 2 or more sequences run the MFMA kernel
-  const void *fn = a.batch > 1 ? (const void *)mk_interp_b : (const void *)mk_interp;
+  // batches of 2 or more sequences run the MFMA kernel; plans whose
+  // attention streams paged K/V run that instantiation
+  const void *fn = kKernels[(a.batch > 1 ? 2 : 0) + (paged ? 1 : 0)];
   if (cooperative) return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), params, kLdsBytes, stream);
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), params, kLdsBytes, stream);
 }

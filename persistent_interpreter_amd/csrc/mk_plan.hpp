@@ -51,6 +51,9 @@ constexpr int kMaxSplits = 64;
 // Batched (MFMA) plans: pieces of 256 elements = 8 MFMA k-steps of 32, one
 // per compute wave; units of at most 64 weight rows (four 16-row tiles).
 constexpr int kMfmaKc = 256;
+// Attention splits of at most this many positions run on registers (head
+// dim 64); longer ones, and head_dim 128, stream their K/V through pages.
+constexpr int kAttnRegRows = 20;
 constexpr int kMfmaRows = 64;
 
 // One queued instruction (96 bytes).  An instruction's weight stream is the
@@ -130,6 +133,8 @@ constexpr int L_XREADY = 128;   // u32      activation pieces produced
 constexpr int L_DONE = 132;     // u32[4]   waves finished, per unit slot
 constexpr int L_ABORT = 148;    // u32      nonzero: every wave exits
 constexpr int L_EPI = 152;      // u32      units whose epilogue has finished
+constexpr int L_AQ = 156;       // u32      paged attention: heads whose q is staged in LDS
+constexpr int L_AM = 160;       // u32      paged attention: partials written for the merge
 constexpr int kMaxBatch = 8;    // sequences per step the plans are built for
 constexpr int L_ACC = 256;      // fp32 row results, kAccSlots x kAccFloats
 constexpr int L_XS = L_ACC + kAccSlots * kAccFloats * 4;  // activation ring

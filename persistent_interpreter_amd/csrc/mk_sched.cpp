@@ -175,6 +175,11 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
     return MK_ERR_UNSUPPORTED;
   }
   const int split_len = (S + n_split - 1) / n_split;
+  // attention on paged K/V (loader-streamed) for head_dim 128 and for splits
+  // longer than the register path's prefetch; RPP rows per 16 KB page
+  const bool paged_kv = hd == 128 || split_len > kAttnRegRows;
+  const uint16_t rpp = (uint16_t)(hd == 128 ? 32 : 64);
+  P.paged_kv = paged_kv;
   P.num_cus = C;
   P.batch = B;
   P.n_split = n_split;
@@ -239,6 +244,7 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
           uint32_t a = (uint32_t)((b * nkv + g) * n_split + s);
           Unit un;
           un.in = plain(OP_ATTN, l, a);
+          un.in.ppp = paged_kv ? rpp : 0;
           un.in.b = (uint32_t)b;
           un.in.aux0 = (uint32_t)g;
           un.in.aux1 = (uint32_t)s;

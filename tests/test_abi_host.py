@@ -136,12 +136,16 @@ def test_out_of_range_split_is_caught(name):
     assert b"out of range" in rep.msg
 
 
-@pytest.mark.parametrize("name", ["tiny_qk", "qwen3_8b", "llama70b"])
-def test_switched_off_attention_paths_refused_before_the_device(name):
-    """q/k norm and head_dim 128 are refused by mk_create (after the
-    argument checks, before any device call), so no caller reaches that
-    attention code; the planner still accepts the shapes."""
-    mc = synth.CONFIGS[name]
+@pytest.mark.parametrize("name,over", [("tiny_qk", dict(head_dim=64)),      # q/k norm needs hd 128
+                                       ("tiny", dict(n_q_heads=6, n_kv_heads=2)),  # 3 q heads per KV head
+                                       ("tiny", dict(head_dim=96))])
+def test_unsupported_shapes_refused_before_the_device(name, over):
+    """Shapes the kernels cannot run are refused by mk_create after the
+    argument checks and before any device call: q/k norm only with head_dim
+    128 (the paged attention body norms and rotates pairs (d, d + 64)),
+    query heads per KV head dividing the 8 compute waves, head_dim 64 or
+    128."""
+    mc = synth.CONFIGS[name].replace(**over)
     cfg = B.make_config(mc, max_batch=1, max_seq=64)
     dummy = C.c_void_p(0x1000)  # never dereferenced on this path
     layers = (B.MkLayerWeights * mc.n_layers)()
@@ -152,4 +156,12 @@ def test_switched_off_attention_paths_refused_before_the_device(name):
     out = C.c_void_p()
     assert B.lib().mk_create(C.byref(cfg), C.byref(w), C.byref(out)) == B.MK_ERR_UNSUPPORTED
     assert not out.value
-    assert B.plan_check(cfg, 1, 256, sim_runs=0)[0] == B.MK_OK
+
+
+@pytest.mark.parametrize("name", ["tiny_qk", "qwen3_8b", "llama70b"])
+def test_head_dim_128_shapes_plan(name):
+    """The q/k-norm and head_dim-128 shapes plan and validate (their
+    attention runs on paged K/V)."""
+    cfg = B.make_config(synth.CONFIGS[name], max_batch=1)
+    rc, rep = B.plan_check(cfg, 1, 256, sim_runs=2)
+    assert rc == B.MK_OK, rep.msg

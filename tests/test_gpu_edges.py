@@ -49,11 +49,11 @@ def _slot_from_gpu_inputs(mc, Wf, h_in, p):
     return out
 
 
-def _one_step(mc, W, Wf, token, p):
+def _one_step(mc, W, Wf, token, p, **knobs):
     kv = synth.make_kv_cache(mc, filled=p)
     ref_kv = kv.copy()
     ref = O.decode_step(mc, Wf, np.array([token], np.int32), np.array([p], np.int32), ref_kv)
-    s = harness.Session(mc, W, kv.copy())
+    s = harness.Session(mc, W, kv.copy(), **knobs)
     s.set_inputs([token], [p])
     s.step_checked()
     lg = s.logits.cpu().numpy()
@@ -72,26 +72,30 @@ def _one_step(mc, W, Wf, token, p):
     return d
 
 
-@pytest.mark.parametrize("name", ["tiny", "llama1b"])
-def test_first_and_last_slot(name):
+# kv_splits=1: one split as long as the cache, so the paged attention body
+# (K/V streamed through LDS pages) takes the first and last slots too
+@pytest.mark.parametrize("name,splits", [("tiny", 0), ("tiny", 1), ("llama1b", 0)],
+                         ids=["tiny", "tiny-paged", "llama1b"])
+def test_first_and_last_slot(name, splits):
     base = synth.CONFIGS[name]
     W = synth.make_weights(base, threads=16)
     Wf = O.upcast_weights(W)
     last = base.max_seq - 1
     for token, p, mc in ((0, 0, base), (base.vocab - 1, last, base.replace(prior=last, steps=1))):
-        print(f"case: {name} token {token} position {p} (max_seq {mc.max_seq})", flush=True)
-        d = _one_step(mc, W, Wf, token, p)
+        print(f"case: {name} splits {splits} token {token} position {p} (max_seq {mc.max_seq})", flush=True)
+        d = _one_step(mc, W, Wf, token, p, kv_splits=splits)
         print(f"  max|dlogit| {d:.3e}", flush=True)
 
 
-def test_greedy_from_an_empty_cache():
+@pytest.mark.parametrize("splits", [0, 1], ids=["tiny", "tiny-paged"])
+def test_greedy_from_an_empty_cache(splits):
     mc = synth.CONFIGS["tiny"].replace(prior=0, steps=8)
     W = synth.make_weights(mc)
     kv = synth.make_kv_cache(mc, filled=0)
     tok, pos = synth.make_tokens(mc), synth.make_positions(mc)
     assert int(pos[0]) == 0
-    print("case: tiny 8 greedy steps from position 0", flush=True)
-    s = harness.Session(mc, W, kv.copy())
+    print(f"case: tiny splits {splits} 8 greedy steps from position 0", flush=True)
+    s = harness.Session(mc, W, kv.copy(), kv_splits=splits)
     fed, out = harness.greedy_run(s, tok, pos, mc.steps)
     s.close()
     Wf = O.upcast_weights(W)
