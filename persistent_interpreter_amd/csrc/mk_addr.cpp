@@ -179,7 +179,7 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
   };
   for (int cu = 0; cu < num_cus; ++cu) {
     const uint32_t q0 = P.q_off[cu], q1 = P.q_off[cu + 1];
-    // ---- sync wave
+    // ---- sync wave (sync_role_b: staging pipeline)
     for (int b = 0; b < batch; ++b) {
       M.el(B.tokens, b, 4, 4, "sync(b): tokens[b]");
       M.el(B.positions, b, 4, 4, "sync(b): positions[b]");
@@ -187,8 +187,10 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
     if (inputs_ok)
       for (uint32_t qi = q0; qi < q1; ++qi) {
         const Instr &d = P.instr[qi];
-        const uint32_t nx = is_gemv(d.op) ? d.nk : 1;
+        const bool gv = is_gemv(d.op);
+        const uint32_t nx = gv ? d.nk : 1;
         const bool normed = d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM;
+        const bool emb_in = d.op == OP_QKV && d.layer == 0;
         if (d.op == OP_QKV) {
           const uint32_t ppg = (uint32_t)(G + 2) * half;
           for (uint32_t x = 0; x < d.n_items * (uint32_t)batch; ++x) {
@@ -204,58 +206,43 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
           }
           M.el(B.status, 0, 4, 4, "sync(b): status poll");
         }
-        if (!is_gemv(d.op)) continue;
+        if (!gv) continue;
         const uint32_t K = d.rowb >> 1;
+        uint64_t nw = 0;
+        if (normed) {
+          uint64_t h, emb;
+          norm_src(d, 0, h, emb, nw);
+        }
         for (uint32_t k = 0; k < nx; ++k) {
-          if (normed && k == 0)
-            for (int b = 0; b < batch; ++b) {
-              uint64_t h, emb, nw;
-              norm_src(d, b, h, emb, nw);
-              for (int lane = 0; lane < 64; ++lane)
-                for (uint32_t i0 = 0; i0 < (uint32_t)H; i0 += 2048)
-                  for (int m = 0; m < 8; ++m) {
-                    const uint32_t i = i0 + (uint32_t)(lane + 64 * m) * 4;
-                    if (i >= (uint32_t)H) continue;
-                    if (emb) M.at(emb + (uint64_t)i * 2, 8, B.embed, "sync(b): embedding row for 1/rms");
-                    else M.at(h + (uint64_t)i * 4, 16, B.h, "sync(b): residual for 1/rms");
-                  }
-            }
           for (int lane = 0; lane < 64; ++lane) {
-            const int sl = lane & 7;
-            if (sl >= batch) continue;
-            const uint32_t kl = 8 * (uint32_t)(lane >> 4);
-            uint64_t src = 0, emb = 0, nw = 0, want = 0;
-            if (normed) {
-              norm_src(d, sl, src, emb, nw);
-              want = src ? B.h : B.embed;
-            } else if (d.op == OP_O) {
-              src = B.attn + lay::attn(MB, nq, hd, d.layer, sl) * 4;
-              want = B.attn;
-            } else {
-              src = B.a + lay::a(MB, F, d.layer, sl) * 4;
-              want = B.a;
-            }
-            for (int ks = 0; ks < 8; ++ks) {
-              const uint32_t kb = k * kMfmaKc + (uint32_t)ks * 32 + kl;
-              if (kb >= K) continue;
-              if (emb) {
-                M.at(emb + (uint64_t)kb * 2, 16, B.embed, "sync(b): embedding piece");
-              } else {
-                M.at(src + (uint64_t)kb * 4, 16, want, "sync(b): activation piece");
-                M.at(src + (uint64_t)kb * 4 + 16, 16, want, "sync(b): activation piece");
+            const uint32_t e0 = k * kMfmaKc + 4 * (uint32_t)lane;
+            for (int b = 0; b < batch; ++b) {
+              if (emb_in) {
+                if (e0 < K) M.at(B.embed + ((uint64_t)tokens[b] * H + e0) * 2, 8, B.embed, "sync(b): embedding piece");
+                continue;
               }
-              if (normed) M.at(nw + (uint64_t)kb * 2, 16, nw, "sync(b): norm weights");
+              uint64_t src, want;
+              if (d.op == OP_O) { src = B.attn + lay::attn(MB, nq, hd, d.layer, b) * 4; want = B.attn; }
+              else if (d.op == OP_DOWN) { src = B.a + lay::a(MB, F, d.layer, b) * 4; want = B.a; }
+              else { uint64_t emb, w; norm_src(d, b, src, emb, w); want = B.h; }
+              if (e0 < K) M.at(src + (uint64_t)e0 * 4, 16, want, "sync(b): staged activation");
+              else M.at(B.zero, 16, B.zero, "sync(b): zero padding");
+            }
+            if (normed && lane < 32) {
+              const uint32_t w0 = k * kMfmaKc + 8 * (uint32_t)lane;
+              if (w0 < K) M.at(nw + (uint64_t)w0 * 2, 16, nw, "sync(b): staged norm weights");
+              else M.at(B.zero, 16, B.zero, "sync(b): zero padding");
             }
           }
           if (k == 0 && (d.op == OP_O || d.op == OP_DOWN))
-            for (uint32_t x = 0; x < d.n_items * (uint32_t)batch; ++x) {
-              const uint32_t r = x / batch, b = x % batch;
-              if (d.op == OP_O && d.layer == 0)
-                M.at(B.embed + ((uint64_t)tokens[b] * H + d.item0 + r) * 2, 2, B.embed, "sync(b): embedding residual");
-              else
-                M.el(B.h, lay::h(MB, H, d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1, b) + d.item0 + r, 4, 4,
-                     "sync(b): residual rows");
-            }
+            for (int b = 0; b < batch; ++b)
+              for (uint32_t r = 0; r < d.n_items; ++r) {
+                if (d.op == OP_O && d.layer == 0)
+                  M.at(B.embed + ((uint64_t)tokens[b] * H + d.item0 + r) * 2, 2, B.embed, "sync(b): embedding residual");
+                else
+                  M.el(B.h, lay::h(MB, H, d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1, b) + d.item0 + r, 4, 4,
+                       "sync(b): residual rows");
+              }
         }
       }
     // ---- loader waves

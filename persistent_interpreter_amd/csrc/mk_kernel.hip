@@ -1720,9 +1720,16 @@ typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 constexpr int LB_AMAX = 192;    // u64[8]  running greedy best per sequence of this workgroup
 constexpr int LB_ACC = 256;     // f32 [kAccSlots][kAccFloats]: residual rows [row][seq], RoPE staging
 constexpr int LB_PART = LB_ACC + kAccSlots * kAccFloats * 4;  // f32 [2][kNCW][128] partial tiles
-constexpr int kXSlotB = 8 * 1024;                              // 8 k-steps x 1 KB A operands
+// Activation staging: a piece's fp32 inputs of up to 8 sequences (rows of
+// 256 elements, 1040 bytes apart so that the 8 sequences of one k-offset
+// fall in different LDS banks) and its 256 bf16 norm weights; three slots,
+// so that two pieces are in flight while the compute waves use a third.
+constexpr int kNXSB = 3;
+constexpr int kXRowB = 1040;
+constexpr int kXNwB = 8 * kXRowB;                              // norm weights within a slot
+constexpr int kXSlotB = kXNwB + 512;
 constexpr int LB_XS = LB_PART + 2 * kNCW * 128 * 4;
-constexpr int LB_RING = ((LB_XS + kNXS * kXSlotB + 1023) / 1024) * 1024;
+constexpr int LB_RING = ((LB_XS + kNXSB * kXSlotB + 1023) / 1024) * 1024;
 constexpr int kRingPagesB = 7;
 constexpr int LB_SENT = LB_RING + kRingPagesB * kPageBytes;
 static_assert(LB_SENT + kRingPagesB * kSentBytes <= kLdsBytes, "batched LDS budget");
@@ -1731,16 +1738,6 @@ static_assert(LB_AMAX + 8 * 8 <= LB_ACC && L_EPI < LB_AMAX, "control words");
 __device__ __forceinline__ int seq_pos(const Args &a, const DevCtx &c, int b) {
   const int p = a.positions[b];
   return (p < 0 || p >= c.max_seq) ? 0 : p;
-}
-
-// Two 16-byte LDS reads in one asm block (see dot_piece for why inline asm).
-__device__ __forceinline__ void lds_read2x16(uint32_t a0, uint32_t a1, u4 &v0, u4 &v1) {
-  asm volatile(
-      "ds_read_b128 %0, %2\n\t"
-      "ds_read_b128 %1, %3\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v0), "=&v"(v1)
-      : "v"(a0), "v"(a1));
 }
 
 // 8 consecutive fp32 values as the A operand of one lane: their hi parts, or
@@ -1875,6 +1872,40 @@ __device__ __forceinline__ void loader_role_b(const Env &e, const Args &a, int l
   wait_vm0();
 }
 
+// Load-count wait for the batched sync wave's pipeline (at most 2 pieces of
+// at most 2 * kMaxBatch + 1 loads each are in flight).
+__device__ __forceinline__ void wait_vm_le(uint32_t n) {
+  switch (n) {
+    case 0: wait_vm_n<0>(); break;
+    case 1: wait_vm_n<1>(); break;
+    case 2: wait_vm_n<2>(); break;
+    case 3: wait_vm_n<3>(); break;
+    case 4: wait_vm_n<4>(); break;
+    case 5: wait_vm_n<5>(); break;
+    case 6: wait_vm_n<6>(); break;
+    case 7: wait_vm_n<7>(); break;
+    case 8: wait_vm_n<8>(); break;
+    case 9: wait_vm_n<9>(); break;
+    case 10: wait_vm_n<10>(); break;
+    case 11: wait_vm_n<11>(); break;
+    case 12: wait_vm_n<12>(); break;
+    case 13: wait_vm_n<13>(); break;
+    case 14: wait_vm_n<14>(); break;
+    case 15: wait_vm_n<15>(); break;
+    case 16: wait_vm_n<16>(); break;
+    default: wait_vm_n<17>(); break;
+  }
+}
+
+// The batched sync wave.  For each GEMV unit it copies the activation pieces
+// (fp32 rows of every sequence, and the norm weights of normed units)
+// global -> LDS with direct-to-LDS loads, two pieces in flight, and
+// publishes each piece once it has landed.  RMSNorm's scale 1/rms is a
+// factor per sequence, so the product runs on the unnormalised h (times the
+// norm weight) and the epilogue applies the factor: W (rs * h * w) =
+// rs * (W (h * w)).  The sync wave accumulates each sequence's sum of
+// squares from the pieces as they land and stores rs before it publishes
+// the unit's last piece.  O and DOWN units also get their residual rows.
 __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
@@ -1884,17 +1915,14 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
     if (tk < 0 || tk >= c.V) { raise_error(e, 0xE1000000u, (uint32_t)b); return; }
     if (ps < 0 || ps >= c.max_seq) { raise_error(e, 0xE2000000u, (uint32_t)b); return; }
   }
-  // this lane's row of the A operand: sequence sl, hi or lo part, and its
-  // first element kl within a 32-element k-step
-  const int sl = lane & 7;
-  const bool lo = (lane & 15) >= 8;
-  const uint32_t kl = 8 * (uint32_t)(lane >> 4);
-  const bool live = sl < B;
+  const char *zero = reinterpret_cast<const char *>(c.zero);
   uint32_t seq = 0;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
-    const uint32_t nx = is_gemv(d.op) ? d.nk : 1;
+    const bool gv = is_gemv(d.op);
+    const uint32_t nx = gv ? d.nk : 1;
     const bool normed = d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM;
+    const bool emb_in = d.op == OP_QKV && d.layer == 0;  // bf16 embedding rows
     float *accs = reinterpret_cast<float *>(smem + LB_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4);
     if (d.op == OP_QKV) {
       // RoPE cos/sin of each (pair, sequence) at that sequence's position,
@@ -1913,35 +1941,20 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
       }
     }
     if (lane == 0) trace_now(e, qi, 4);
-    // this lane's sequence: its input vector (and norm weights)
-    const uint32_t K = d.rowb >> 1;
-    const float *src = nullptr;
-    const uint16_t *emb = nullptr, *nw = nullptr;
-    if (normed) {
-      norm_src(e, a, d, live ? sl : 0, src, emb, nw);
-    } else if (d.op == OP_O) {
-      src = c.attn_buf + lay::attn(c.max_batch, c.nq, c.hd, d.layer, live ? sl : 0);
-    } else if (d.op == OP_DOWN) {
-      src = c.a_buf + lay::a(c.max_batch, c.F, d.layer, live ? sl : 0);
-    }
-    float rs = 1.f;
     uint32_t wi = 0;
-    for (uint32_t k = 0; k < nx; ++k, ++seq) {
+    if (!gv) {
+      // attention and reduction units: their waits, then their piece (a
+      // paged attention unit keeps q and its merge in the slot)
       while (wi < d.wait_n) {
-        const Wait wt = a.waits[d.wait_off + wi];
-        if (wt.before_k > k) break;
-        if (!wait_group(e, a, wt, qi)) return;
+        if (!wait_group(e, a, a.waits[d.wait_off + wi], qi)) return;
         ++wi;
       }
-      if (k == 0 && lane == 0) {
+      if (lane == 0) {
         trace_put(e, qi, 0, (uint64_t)d.op | ((uint64_t)d.layer << 8) | ((uint64_t)d.unit << 24));
         trace_now(e, qi, 1);
       }
-      // the slot of this piece is free once every compute wave released
-      // the piece two before it (a paged attention unit uses its slot for q
-      // and its merge; a reduction unit takes no piece)
-      if (seq >= (uint32_t)kNXS) {
-        const uint32_t need = seq - kNXS + 1;
+      if (seq >= (uint32_t)kNXSB) {
+        const uint32_t need = seq - kNXSB + 1;
         auto freed = [&]() {
           uint32_t v = lane < kNCW ? lds_ld_lane(L_XCONS + 4 * lane) : 0xffffffffu;
           uint32_t m = __builtin_amdgcn_readlane(v, 0);
@@ -1951,90 +1964,157 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
         };
         if (!spin_lds(e, freed, 0x100 | qi)) return;
       }
-      if (!is_gemv(d.op)) {
-        if (lane == 0) lds_st(L_XREADY, seq + 1);
-        wake();
-        continue;
-      }
-      if (normed && k == 0) {
-        // 1/rms of every sequence's input (each lane keeps its own)
-        for (int b = 0; b < B; ++b) {
-          const float *hb;
-          const uint16_t *eb, *wb;
-          norm_src(e, a, d, b, hb, eb, wb);
-          float ss = 0.f;
-          const rsrc_t hr = rsrc(hb ? (const void *)hb : (const void *)eb);
-          for (uint32_t i0 = 0; i0 < (uint32_t)c.H; i0 += 2048) {
-            f4 v[8];
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-              const uint32_t i = i0 + (uint32_t)(lane + 64 * m) * 4;
-              if (i < (uint32_t)c.H) {
-                if (eb) {
-                  const uint64_t uu = *G(reinterpret_cast<const uint64_t *>(eb + i));
-                  v[m] = f4{bf_lo((uint32_t)uu), bf_hi((uint32_t)uu), bf_lo((uint32_t)(uu >> 32)),
-                            bf_hi((uint32_t)(uu >> 32))};
-                } else {
-                  v[m] = ldc4(hr, i * 4);
-                }
-              } else {
-                v[m] = f4{0.f, 0.f, 0.f, 0.f};
-              }
-            }
-#pragma unroll
-            for (int m = 0; m < 8; ++m) ss += v[m].x * v[m].x + v[m].y * v[m].y + v[m].z * v[m].z + v[m].w * v[m].w;
-          }
-          ss = wave_sum(ss);
-          const float r = 1.0f / sqrtf(ss / (float)c.H + c.eps);
-          if (sl == b) rs = r;
-        }
-      }
-      // the piece's A operands: 8 k-steps of 32 elements
-      LDS_AS char *xs = (LDS_AS char *)smem + LB_XS + (seq % kNXS) * kXSlotB;
-      const rsrc_t sr = rsrc(src ? (const void *)src : (const void *)emb);
-#pragma unroll 2
-      for (int ks = 0; ks < 8; ++ks) {
-        const uint32_t kb = k * kMfmaKc + (uint32_t)ks * 32 + kl;
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = 0.f;
-        if (live && kb < K) {
-          if (emb) {
-            const u4 u = *G(reinterpret_cast<const u4 *>(emb + kb));
-            x[0] = bf_lo(u.x); x[1] = bf_hi(u.x); x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
-            x[4] = bf_lo(u.z); x[5] = bf_hi(u.z); x[6] = bf_lo(u.w); x[7] = bf_hi(u.w);
-          } else {
-            const f4 p0 = ldc4(sr, kb * 4), p1 = ldc4(sr, kb * 4 + 16);
-            x[0] = p0.x; x[1] = p0.y; x[2] = p0.z; x[3] = p0.w;
-            x[4] = p1.x; x[5] = p1.y; x[6] = p1.z; x[7] = p1.w;
-          }
-          if (normed) {
-            const u4 w = *G(reinterpret_cast<const u4 *>(nw + kb));
-            x[0] *= rs * bf_lo(w.x); x[1] *= rs * bf_hi(w.x); x[2] *= rs * bf_lo(w.y); x[3] *= rs * bf_hi(w.y);
-            x[4] *= rs * bf_lo(w.z); x[5] *= rs * bf_hi(w.z); x[6] *= rs * bf_lo(w.w); x[7] *= rs * bf_hi(w.w);
-          }
-        }
-        *reinterpret_cast<LDS_AS u4 *>(xs + ks * 1024 + lane * 16) = pack_hilo(x, lo);
-      }
-      if (k == 0 && (d.op == OP_O || d.op == OP_DOWN)) {
-        // residual rows of every sequence: accs[row * B + b]
-        for (uint32_t x = (uint32_t)lane; x < d.n_items * (uint32_t)B; x += 64) {
-          const uint32_t r = x / (uint32_t)B, b = x - r * (uint32_t)B;
-          float v;
-          if (d.op == OP_O && d.layer == 0)
-            v = bf16f(G(c.embed)[(size_t)a.tokens[b] * c.H + d.item0 + r]);
-          else
-            v = ld_c(c.h_buf + lay::h(c.max_batch, c.H, d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1, (int)b) +
-                     d.item0 + r);
-          accs[x] = v;
-        }
-      }
-      wait_lgkm0();
       if (lane == 0) lds_st(L_XREADY, seq + 1);
       wake();
-      if (k == 0 && lane == 0) trace_now(e, qi, 5);
-      if (k + 1 == nx && lane == 0) trace_now(e, qi, 7);
+      ++seq;
+      continue;
     }
+    const uint32_t K = d.rowb >> 1;
+    // this lane's part of a piece: sequence b's elements 4*lane .. 4*lane+3
+    // (fp32 rows), norm weights 8*lane .. 8*lane+7 (lanes < 32)
+    auto src_of = [&](int b) -> const char * {
+      if (d.op == OP_O) return reinterpret_cast<const char *>(c.attn_buf + lay::attn(c.max_batch, c.nq, c.hd, d.layer, b));
+      if (d.op == OP_DOWN) return reinterpret_cast<const char *>(c.a_buf + lay::a(c.max_batch, c.F, d.layer, b));
+      const float *h;
+      const uint16_t *emb, *w;
+      norm_src(e, a, d, b, h, emb, w);
+      return reinterpret_cast<const char *>(h);
+    };
+    const uint16_t *nw = nullptr;
+    if (normed) {
+      const float *h;
+      const uint16_t *emb;
+      norm_src(e, a, d, 0, h, emb, nw);
+    }
+    const uint32_t loads = (emb_in ? 0u : (uint32_t)B) + (normed ? 1u : 0u);
+    float ss = 0.f;  // sum of squares of sequence lane >> 3, over this lane's part
+    auto issue = [&](uint32_t k, uint32_t sq) -> uint32_t {
+      LDS_AS char *slot = (LDS_AS char *)smem + LB_XS + (sq % kNXSB) * kXSlotB;
+      const uint32_t e0 = k * kMfmaKc + 4 * (uint32_t)lane;
+      uint32_t nl = 0;
+      if (!emb_in) {
+        for (int b = 0; b < B; ++b) {
+          const char *src = e0 < K ? src_of(b) + (size_t)e0 * 4 : zero;
+          __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)(slot + b * kXRowB), 16, 0, kSC1);
+          ++nl;
+        }
+      }
+      if (normed) {
+        const uint32_t w0 = k * kMfmaKc + 8 * (uint32_t)lane;
+        if (lane < 32)
+          __builtin_amdgcn_global_load_lds(w0 < K ? reinterpret_cast<const char *>(nw + w0) : zero,
+                                           (LDS_AS void *)(slot + kXNwB), 16, 0, 0);
+        ++nl;
+      }
+      if (k == 0 && (d.op == OP_O || d.op == OP_DOWN)) {
+        // residual rows [sequence][64]: lane r < rows takes row r
+        LDS_AS char *accl = (LDS_AS char *)smem + LB_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4;
+        for (int b = 0; b < B; ++b) {
+          if (d.op == OP_O && d.layer == 0) continue;  // bf16 embedding: loaded below
+          const float *res =
+              c.h_buf + lay::h(c.max_batch, c.H, d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1, b) + d.item0 + lane;
+          if (lane < (int)d.n_items)
+            __builtin_amdgcn_global_load_lds(res, (LDS_AS void *)(accl + b * 64 * 4), 4, 0, kSC1);
+          ++nl;
+        }
+      }
+      return nl;
+    };
+    // the landed piece in slot sq: embedding rows (layer 0), sums of squares
+    auto land = [&](uint32_t k, uint32_t sq) {
+      LDS_AS char *slot = (LDS_AS char *)smem + LB_XS + (sq % kNXSB) * kXSlotB;
+      if (emb_in) {
+        // bf16 embedding rows of every sequence, widened into the slot
+        for (int b = 0; b < B; ++b) {
+          const uint32_t e0 = k * kMfmaKc + 4 * (uint32_t)lane;
+          f4 v = {0.f, 0.f, 0.f, 0.f};
+          if (e0 < K) {
+            const uint64_t uu = *G(reinterpret_cast<const uint64_t *>(c.embed + (size_t)a.tokens[b] * c.H + e0));
+            v = f4{bf_lo((uint32_t)uu), bf_hi((uint32_t)uu), bf_lo((uint32_t)(uu >> 32)), bf_hi((uint32_t)(uu >> 32))};
+          }
+          *reinterpret_cast<LDS_AS f4 *>(slot + b * kXRowB + lane * 16) = v;
+        }
+        wait_lgkm0();
+      }
+      if (normed) {
+        // lane l: 32 elements of sequence l >> 3
+        const int b = lane >> 3;
+        if (b < B) {
+          const LDS_AS f4 *row = reinterpret_cast<const LDS_AS f4 *>(slot + b * kXRowB);
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const f4 v = row[m * 8 + (lane & 7)];
+            ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+          }
+        }
+      }
+    };
+    int64_t t_first = 0, t_last = 0;
+    uint32_t issued = 0, done = 0, n_prev = 0, n_cur = 0;
+    while (done < nx) {
+      if (issued < nx && issued - done < 2) {
+        // waits of piece `issued`, then a free slot (every compute wave
+        // released the piece kNXSB before it)
+        while (wi < d.wait_n) {
+          const Wait wt = a.waits[d.wait_off + wi];
+          if (wt.before_k > issued) break;
+          if (!wait_group(e, a, wt, qi)) { wait_vm0(); return; }
+          ++wi;
+        }
+        if (issued == 0 && lane == 0) {
+          trace_put(e, qi, 0, (uint64_t)d.op | ((uint64_t)d.layer << 8) | ((uint64_t)d.unit << 24));
+          trace_now(e, qi, 1);
+        }
+        const uint32_t sq = seq + issued;
+        if (sq >= (uint32_t)kNXSB) {
+          const uint32_t need = sq - kNXSB + 1;
+          auto freed = [&]() {
+            uint32_t v = lane < kNCW ? lds_ld_lane(L_XCONS + 4 * lane) : 0xffffffffu;
+            uint32_t m = __builtin_amdgcn_readlane(v, 0);
+#pragma unroll
+            for (int i = 1; i < kNCW; ++i) m = min(m, (uint32_t)__builtin_amdgcn_readlane(v, i));
+            return m >= need;
+          };
+          if (!spin_lds(e, freed, 0x100 | qi)) { wait_vm0(); return; }
+        }
+        n_prev = n_cur;
+        n_cur = issue(issued, sq);
+        ++issued;
+      } else {
+        // the oldest piece in flight has landed once only the younger
+        // piece's loads are outstanding
+        if (issued - done >= 2) wait_vm_le(n_cur);
+        else wait_vm0();
+        land(done, seq + done);
+        if (done + 1 == nx && normed) {
+          // every piece is in: 1/rms of each sequence (lanes 8b .. 8b+7
+          // hold sequence b's partial sums) into the unit's result slot
+          ss += __shfl_xor(ss, 1);
+          ss += __shfl_xor(ss, 2);
+          ss += __shfl_xor(ss, 4);
+          if ((lane & 7) == 0 && (lane >> 3) < B) accs[lane >> 3] = 1.0f / sqrtf(ss / (float)c.H + c.eps);
+        }
+        if (d.op == OP_O && d.layer == 0 && done == 0) {
+          // layer 0's residual is the bf16 embedding row
+          for (uint32_t x = (uint32_t)lane; x < d.n_items * (uint32_t)B; x += 64) {
+            const uint32_t b = x / d.n_items, r = x - b * d.n_items;
+            accs[b * 64 + r] = bf16f(G(c.embed)[(size_t)a.tokens[b] * c.H + d.item0 + r]);
+          }
+        }
+        wait_lgkm0();
+        if (lane == 0) lds_st(L_XREADY, seq + done + 1);
+        wake();
+        if (done == 0) t_first = now();
+        if (done + 1 == nx) t_last = now();
+        ++done;
+      }
+    }
+    (void)n_prev;
+    if (lane == 0) {
+      trace_put(e, qi, 5, (uint64_t)t_first);
+      trace_put(e, qi, 7, (uint64_t)t_last);
+    }
+    seq += nx;
   }
 }
 
@@ -2056,11 +2136,14 @@ __device__ __forceinline__ void unit_epilogue_b(const Env &e, const Args &a, con
   const int lane = lane_id();
   const uint32_t B = (uint32_t)a.batch;
   const uint32_t T = ((uint32_t)d.ppp + 1) >> 1;
+  // normed units: the sequence's 1/rms (accs[b]); O, DOWN: residual rows
+  // accs[b * 64 + row]
   for (uint32_t x = (uint32_t)lane; x < d.n_items * B; x += 64) {
     const uint32_t i = x / B, b = x - i * B;
     switch (d.op) {
       case OP_QKV: {
-        const float v0 = tile_sum(Pb, T, 2 * i, b), v1 = tile_sum(Pb, T, 2 * i + 1, b);
+        const float rsb = accs[b];
+        const float v0 = tile_sum(Pb, T, 2 * i, b) * rsb, v1 = tile_sum(Pb, T, 2 * i + 1, b) * rsb;
         const uint32_t half = (uint32_t)c.hd >> 1;
         const uint32_t ppg = (uint32_t)(c.G + 2) * half;
         const uint32_t pp = d.item0 + i, g = pp / ppg, rr = pp - g * ppg;
@@ -2094,19 +2177,20 @@ __device__ __forceinline__ void unit_epilogue_b(const Env &e, const Args &a, con
         break;
       }
       case OP_O:
-        st_c(c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer + 1, (int)b) + d.item0 + i, accs[x] + tile_sum(Pb, T, i, b));
+        st_c(c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer + 1, (int)b) + d.item0 + i,
+             accs[b * 64 + i] + tile_sum(Pb, T, i, b));
         break;
       case OP_FFN: {
-        const float gt = tile_sum(Pb, T, 2 * i, b), up = tile_sum(Pb, T, 2 * i + 1, b);
+        const float gt = tile_sum(Pb, T, 2 * i, b) * accs[b], up = tile_sum(Pb, T, 2 * i + 1, b) * accs[b];
         st_c(c.a_buf + lay::a(c.max_batch, c.F, d.layer, (int)b) + d.item0 + i, gt / (1.0f + expf(-gt)) * up);
         break;
       }
       case OP_DOWN:
         st_c(c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer + 2, (int)b) + d.item0 + i,
-             accs[x] + tile_sum(Pb, T, i, b));
+             accs[b * 64 + i] + tile_sum(Pb, T, i, b));
         break;
       default:  // OP_LM
-        G(a.logits)[lay::logits(c.V, (int)b) + d.item0 + i] = tile_sum(Pb, T, i, b);
+        G(a.logits)[lay::logits(c.V, (int)b) + d.item0 + i] = tile_sum(Pb, T, i, b) * accs[b];
         break;
     }
   }
@@ -2119,7 +2203,7 @@ __device__ __forceinline__ void unit_epilogue_b(const Env &e, const Args &a, con
       float bv = -INFINITY;
       uint32_t bi = 0xffffffffu;
       for (uint32_t i = (uint32_t)lane; i < d.n_items; i += 64) {
-        const float v = tile_sum(Pb, T, i, b);
+        const float v = tile_sum(Pb, T, i, b) * accs[b];
         if (amax_better(v, d.item0 + i, bv, bi)) {
           bv = v;
           bi = d.item0 + i;
@@ -2191,7 +2275,7 @@ __device__ __forceinline__ void compute_role_b(const Env &e, const Args &a, int 
     if (PAGED && d.op == OP_ATTN) {
       const int p = seq_pos(a, c, (int)d.b);
       upages = attn_pages(a, d, p);
-      const int xso = LB_XS + (int)((seq % kNXS) * kXSlotB);
+      const int xso = LB_XS + (int)((seq % kNXSB) * kXSlotB);
       bool ok = false;
       if constexpr (PAGED)
         ok = c.hd == 64 ? attn_paged<1>(e, a, d, cw, p, n, seq, aq_t, am_t, LB_RING, LB_SENT, P, xso)
@@ -2211,8 +2295,13 @@ __device__ __forceinline__ void compute_role_b(const Env &e, const Args &a, int 
       const uint32_t t = (uint32_t)cw % T, nwt = ((uint32_t)kNCW - 1 - t) / T + 1, kg = (uint32_t)cw / T;
       const uint32_t rb_lo = 2 * t, rb_hi = min(2 * t + 1, nrb - 1);
       const bool upper = (lane & 15) >= 8;
-      // this lane's offsets within a block and an A operand
+      // this lane's offsets within a block, and its A row: sequence sA's
+      // hi (rows 0..7) or lo (rows 8..15) part, elements kA .. kA+7 of a step
       const uint32_t brow = (uint32_t)(((lane >> 4) * 8 + (lane & 7)) * 16);
+      const int sA = lane & 7;
+      const bool loA = (lane & 15) >= 8, liveA = sA < a.batch;
+      const bool normed = d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM;
+      const uint32_t kA = 8 * (uint32_t)(lane >> 4);
       f4 acc = {0.f, 0.f, 0.f, 0.f};
       uint32_t rel = n, v0 = 0xffffffffu, v1 = 0xffffffffu;
       for (uint32_t k = 0; k < d.nk; ++k) {
@@ -2245,11 +2334,31 @@ __device__ __forceinline__ void compute_role_b(const Env &e, const Args &a, int 
           }
           v1 = pg1;
           const uint32_t mypg = upper ? pg1 : pg0, myL = upper ? L1 : L0;
-          const uint32_t aaddr = lds_addr(LB_XS + (int)(((seq + k) % kNXS) * kXSlotB + ks * 1024 + lane * 16));
+          const uint32_t slot = (uint32_t)LB_XS + ((seq + k) % kNXSB) * kXSlotB;
+          const uint32_t xaddr = lds_addr((int)(slot + sA * kXRowB + (ks * 32 + kA) * 4));
+          const uint32_t waddr = lds_addr((int)(slot + kXNwB + (ks * 32 + kA) * 2));
           const uint32_t baddr = lds_addr(LB_RING + (int)((mypg % P) * kPageBytes + (myL & 15) * 1024 +
                                                           ((ks & 1) * 4 * 8 * 16) + brow));
-          u4 av, bv;
-          lds_read2x16(aaddr, baddr, av, bv);
+          u4 x0, x1, wv, bv;
+          asm volatile(
+              "ds_read_b128 %0, %4\n\t"
+              "ds_read_b128 %1, %4 offset:16\n\t"
+              "ds_read_b128 %2, %5\n\t"
+              "ds_read_b128 %3, %6\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(x0), "=&v"(x1), "=&v"(wv), "=&v"(bv)
+              : "v"(xaddr), "v"(waddr), "v"(baddr));
+          float x[8] = {__uint_as_float(x0.x), __uint_as_float(x0.y), __uint_as_float(x0.z), __uint_as_float(x0.w),
+                        __uint_as_float(x1.x), __uint_as_float(x1.y), __uint_as_float(x1.z), __uint_as_float(x1.w)};
+          if (normed) {
+            x[0] *= bf_lo(wv.x); x[1] *= bf_hi(wv.x); x[2] *= bf_lo(wv.y); x[3] *= bf_hi(wv.y);
+            x[4] *= bf_lo(wv.z); x[5] *= bf_hi(wv.z); x[6] *= bf_lo(wv.w); x[7] *= bf_hi(wv.w);
+          }
+          if (!liveA) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = 0.f;
+          }
+          const u4 av = pack_hilo(x, loA);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, av), __builtin_bit_cast(bf8v, bv),
                                                          acc, 0, 0, 0);
         }
