@@ -48,6 +48,9 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 METRIC = "decode tokens/s at batch 1 (Llama-1B shape) + % of peak HBM GB/s"
 H100_STEP_S = 1.0e-3   # the pages' ~1 ms Llama-1B batch-1 forward on H100
+# attention splits per (sequence, KV head) of each workload (0: the planner's
+# choice)
+DEFAULT_SPLITS = {}
 
 
 def overhead(t_real: float, t_min: float) -> float:
@@ -216,6 +219,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama1b")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
+    ap.add_argument("--kv-splits", type=int, default=-1,
+                    help="attention splits per (sequence, KV head); -1: the workload's default")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (for "
                          "scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -245,7 +250,8 @@ def main():
     kv0 = synth.make_kv_cache(mc, filled=mc.prior)
     tok, pos = synth.make_tokens(mc), synth.make_positions(mc)
 
-    sess = harness.Session(mc, W, kv0.copy(), batch=mc.batch)
+    splits = DEFAULT_SPLITS.get(args.workload, 0) if args.kv_splits < 0 else args.kv_splits
+    sess = harness.Session(mc, W, kv0.copy(), batch=mc.batch, kv_splits=splits)
     # untimed greedy pass whose logits the oracle checks
     n_check = min(K, 32)
     fed, gpu_logits = harness.greedy_run(sess, tok, pos, n_check)
@@ -310,6 +316,7 @@ def main():
                                f"FFN {mc.ffn_dim}, vocab {mc.vocab}, batch {mc.batch}, "
                                f"{prior} prior KV positions, greedy (in-kernel argmax)",
                    "batch": mc.batch, "prior_positions": prior, "accumulate": "fp32",
+                   "kv_splits": sess.mk.plan_splits(mc.batch),
                    "parallelism": "1 GPU, 1 persistent launch per step"},
         "kernel_us": {"mean": round(t_kern * 1e6, 2),
                       "median": round(float(np.median(kern)) * 1e6, 2),

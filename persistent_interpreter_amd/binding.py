@@ -236,6 +236,11 @@ class Megakernel:
     def sync_status(self) -> int:
         return lib().mk_sync_status(self.h)
 
+    def plan_splits(self, batch: int) -> int:
+        """KV splits of this handle's plan for `batch` (host-side planner)."""
+        rc, rep = plan_check(self.cfg, batch, 256)
+        return int(rep.kv_splits) if rc == MK_OK else -1
+
     def buffer(self, which: int):
         p, n = C.c_void_p(), C.c_size_t()
         rc = lib().mk_get_buffer(self.h, which, C.byref(p), C.byref(n))

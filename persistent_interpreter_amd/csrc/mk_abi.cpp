@@ -354,6 +354,54 @@ static int get_plan(mk_handle *h, int batch, DevPlan **out) {
   return MK_OK;
 }
 
+// Scratch of one step: the counter groups (with the greedy arrival counter
+// after them), the attention partials and the greedy candidates, and the
+// launch counts their targets are scaled by.
+struct StepScratch {
+  uint32_t *ctr;
+  float *part;
+  uint64_t *amax;
+  uint32_t epoch, greedy_epoch;
+};
+
+static int launch_with(mk_handle *h, DevPlan *dp, int32_t batch, const int32_t *tokens, const int32_t *positions,
+                       void *kv_cache, float *logits, int32_t *next_tokens, int32_t *next_positions,
+                       const StepScratch &sc, void *stream) {
+  Args a;
+  a.ctx = h->d_ctx;
+  a.instr = dp->d_instr;
+  a.q_off = dp->d_qoff;
+  a.waits = dp->d_waits;
+  a.rowtab = dp->d_rowtab;
+  a.ctr = sc.ctr;
+  a.grp_target = dp->d_target;
+  a.part_buf = sc.part;
+  a.iota = dp->d_iota;
+  a.tokens = tokens;
+  a.positions = positions;
+  a.kv = (uint16_t *)kv_cache;
+  a.logits = logits;
+  a.trace = dp->d_trace;
+  a.trace_stride = dp->trace_stride;
+  h->last_plan = dp;
+  a.epoch = sc.epoch;
+  h->tag = h->tag + 1 == 0 ? 1 : h->tag + 1;
+  a.tag = h->tag;
+  a.batch = batch;
+  a.n_split = dp->plan.n_split;
+  a.split_len = dp->plan.split_len;
+  a.amax = sc.amax;
+  a.amax_ctr = sc.ctr + dp->amax_word;
+  a.next_tok = next_tokens;
+  a.next_pos = next_positions;
+  a.n_lm = dp->n_arrive;
+  a.amax_target = next_tokens ? sc.greedy_epoch * dp->n_arrive : 0;
+  if (kernel_launch(a, h->num_cus, (h->cfg.flags & MK_FLAG_COOPERATIVE) != 0, dp->plan.paged_kv,
+                    (hipStream_t)stream) != hipSuccess)
+    return MK_ERR_HIP;
+  return MK_OK;
+}
+
 static int launch_step(mk_handle *h, int32_t batch, const int32_t *tokens, const int32_t *positions,
                        void *kv_cache, float *logits, int32_t *next_tokens, int32_t *next_positions,
                        void *stream) {
@@ -366,43 +414,9 @@ static int launch_step(mk_handle *h, int32_t batch, const int32_t *tokens, const
   int rc = get_plan(h, batch, &dp);
   if (rc) return rc;
   dp->epoch += 1;
-  Args a;
-  a.ctx = h->d_ctx;
-  a.instr = dp->d_instr;
-  a.q_off = dp->d_qoff;
-  a.waits = dp->d_waits;
-  a.rowtab = dp->d_rowtab;
-  a.ctr = dp->d_ctr;
-  a.grp_target = dp->d_target;
-  a.part_buf = dp->d_part;
-  a.iota = dp->d_iota;
-  a.tokens = tokens;
-  a.positions = positions;
-  a.kv = (uint16_t *)kv_cache;
-  a.logits = logits;
-  a.trace = dp->d_trace;
-  a.trace_stride = dp->trace_stride;
-  h->last_plan = dp;
-  a.epoch = dp->epoch;
-  h->tag = h->tag + 1 == 0 ? 1 : h->tag + 1;
-  a.tag = h->tag;
-  a.batch = batch;
-  a.n_split = dp->plan.n_split;
-  a.split_len = dp->plan.split_len;
-  a.amax = dp->d_amax;
-  a.amax_ctr = dp->d_ctr + dp->amax_word;
-  a.next_tok = next_tokens;
-  a.next_pos = next_positions;
-  a.n_lm = dp->n_arrive;
-  a.amax_target = 0;
-  if (next_tokens) {
-    dp->greedy_epoch += 1;
-    a.amax_target = dp->greedy_epoch * dp->n_arrive;
-  }
-  if (kernel_launch(a, h->num_cus, (h->cfg.flags & MK_FLAG_COOPERATIVE) != 0, dp->plan.paged_kv,
-                    (hipStream_t)stream) != hipSuccess)
-    return MK_ERR_HIP;
-  return MK_OK;
+  if (next_tokens) dp->greedy_epoch += 1;
+  const StepScratch sc{dp->d_ctr, dp->d_part, dp->d_amax, dp->epoch, dp->greedy_epoch};
+  return launch_with(h, dp, batch, tokens, positions, kv_cache, logits, next_tokens, next_positions, sc, stream);
 }
 
 int mk_decode_step(mk_handle *h, int32_t batch, const int32_t *tokens, const int32_t *positions, void *kv_cache,

@@ -140,12 +140,19 @@ static void paged_attn_compute(Model &M, const Bases &B, const Plan &P, const mk
         for (int i = 0; i < 8; ++i)
           M.el(B.kvn, lay::kvn(MB, nkv, hd, d.layer, b, g, 0) + hd + (lane % CPR) * 8 + i, 8, 8,
                "attn(paged): V of row p");
-      const uint64_t out = lay::part(MB, nq, ns, hd, d.layer, b, j, s);
-      if (lane < CPR)
-        for (int i = 0; i < 8; ++i) M.el(B.part, out + lane * 8 + i, 4, 4, "attn(paged): partial o");
-      if (lane == 0) {
-        M.el(B.part, out + hd, 4, 4, "attn(paged): partial m");
-        M.el(B.part, out + hd + 1, 4, 4, "attn(paged): partial l");
+      if (ns == 1) {
+        if (lane < CPR)
+          for (int i = 0; i < 8; ++i)
+            M.el(B.attn, lay::attn(MB, nq, hd, d.layer, b) + (uint64_t)j * hd + lane * 8 + i, 4, 4,
+                 "attn(paged): output (single split)");
+      } else {
+        const uint64_t out = lay::part(MB, nq, ns, hd, d.layer, b, j, s);
+        if (lane < CPR)
+          for (int i = 0; i < 8; ++i) M.el(B.part, out + lane * 8 + i, 4, 4, "attn(paged): partial o");
+        if (lane == 0) {
+          M.el(B.part, out + hd, 4, 4, "attn(paged): partial m");
+          M.el(B.part, out + hd + 1, 4, 4, "attn(paged): partial l");
+        }
       }
     }
   }

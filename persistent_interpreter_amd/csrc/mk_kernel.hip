@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+
 #include "mk_layout.hpp"
 #include "mk_plan.hpp"
 
@@ -1489,14 +1490,25 @@ __device__ bool attn_paged(const Env &e, const Args &a, const Instr &d, int cw, 
     }
   }
   if (rp == 0) {
-    float *out = a.part_buf + lay::part(c.max_batch, c.nq, a.n_split, hd, d.layer, b, j, s);
-    if (lane < CPR) {
+    if (a.n_split == 1) {
+      // one split per KV head: the merged partial is the attention output
+      // (no reduction instruction follows)
+      float *out = c.attn_buf + lay::attn(c.max_batch, c.nq, hd, d.layer, b) + (size_t)j * hd;
+      const float inv = 1.0f / l_run;
+      if (lane < CPR) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) st_c(out + lane * 8 + i, o[i]);
-    }
-    if (lane == 0) {
-      st_c(out + hd, m_run);
-      st_c(out + hd + 1, l_run);
+        for (int i = 0; i < 8; ++i) st_c(out + lane * 8 + i, o[i] * inv);
+      }
+    } else {
+      float *out = a.part_buf + lay::part(c.max_batch, c.nq, a.n_split, hd, d.layer, b, j, s);
+      if (lane < CPR) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st_c(out + lane * 8 + i, o[i]);
+      }
+      if (lane == 0) {
+        st_c(out + hd, m_run);
+        st_c(out + hd + 1, l_run);
+      }
     }
   }
   wait_lgkm0();
@@ -1872,8 +1884,10 @@ __device__ __forceinline__ void loader_role_b(const Env &e, const Args &a, int l
   wait_vm0();
 }
 
-// Load-count wait for the batched sync wave's pipeline (at most 2 pieces of
-// at most 2 * kMaxBatch + 1 loads each are in flight).
+// Load-count wait for the batched sync wave's pipeline: the loads of the
+// younger pieces in flight (at most 2 pieces of at most kMaxBatch + 1
+// loads; piece 0 of O and DOWN adds kMaxBatch residual loads, but it is
+// never a younger piece).
 __device__ __forceinline__ void wait_vm_le(uint32_t n) {
   switch (n) {
     case 0: wait_vm_n<0>(); break;
@@ -1893,7 +1907,17 @@ __device__ __forceinline__ void wait_vm_le(uint32_t n) {
     case 14: wait_vm_n<14>(); break;
     case 15: wait_vm_n<15>(); break;
     case 16: wait_vm_n<16>(); break;
-    default: wait_vm_n<17>(); break;
+    case 17: wait_vm_n<17>(); break;
+    case 18: wait_vm_n<18>(); break;
+    case 19: wait_vm_n<19>(); break;
+    case 20: wait_vm_n<20>(); break;
+    case 21: wait_vm_n<21>(); break;
+    case 22: wait_vm_n<22>(); break;
+    case 23: wait_vm_n<23>(); break;
+    case 24: wait_vm_n<24>(); break;
+    case 25: wait_vm_n<25>(); break;
+    case 26: wait_vm_n<26>(); break;
+    default: wait_vm_n<27>(); break;
   }
 }
 
@@ -2050,9 +2074,10 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
       }
     };
     int64_t t_first = 0, t_last = 0;
-    uint32_t issued = 0, done = 0, n_prev = 0, n_cur = 0;
+    uint32_t issued = 0, done = 0;
+    uint32_t nl[kNXSB] = {0, 0, 0};  // loads of each piece in flight (by piece % kNXSB)
     while (done < nx) {
-      if (issued < nx && issued - done < 2) {
+      if (issued < nx && issued - done < 2) {  // two pieces in flight (three measured slower)
         // waits of piece `issued`, then a free slot (every compute wave
         // released the piece kNXSB before it)
         while (wi < d.wait_n) {
@@ -2077,14 +2102,14 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
           };
           if (!spin_lds(e, freed, 0x100 | qi)) { wait_vm0(); return; }
         }
-        n_prev = n_cur;
-        n_cur = issue(issued, sq);
+        nl[issued % kNXSB] = issue(issued, sq);
         ++issued;
       } else {
         // the oldest piece in flight has landed once only the younger
-        // piece's loads are outstanding
-        if (issued - done >= 2) wait_vm_le(n_cur);
-        else wait_vm0();
+        // pieces' loads are outstanding
+        uint32_t younger = 0;
+        for (uint32_t q = done + 1; q < issued; ++q) younger += nl[q % kNXSB];
+        wait_vm_le(younger);
         land(done, seq + done);
         if (done + 1 == nx && normed) {
           // every piece is in: 1/rms of each sequence (lanes 8b .. 8b+7
@@ -2109,7 +2134,6 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
         ++done;
       }
     }
-    (void)n_prev;
     if (lane == 0) {
       trace_put(e, qi, 5, (uint64_t)t_first);
       trace_put(e, qi, 7, (uint64_t)t_last);

@@ -180,6 +180,8 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
   const bool paged_kv = hd == 128 || split_len > kAttnRegRows;
   const uint16_t rpp = (uint16_t)(hd == 128 ? 32 : 64);
   P.paged_kv = paged_kv;
+  // a single split (paged) leaves nothing to reduce
+  const bool fused_attn = paged_kv && n_split == 1;
   P.num_cus = C;
   P.batch = B;
   P.n_split = n_split;
@@ -213,7 +215,7 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
   std::vector<int> g_down_prev(1, -1);
   int g_down = -1;
   for (int l = 0; l < L; ++l) {
-    std::vector<int> g_attn((size_t)B * nkv), g_ffn(chunks);
+    std::vector<int> g_attn(fused_attn ? 0 : (size_t)B * nkv), g_ffn(chunks);
     for (auto &g : g_attn) g = bd.group();
     const int g_red = bd.group(), g_o = bd.group();
     for (auto &g : g_ffn) g = bd.group();
@@ -250,13 +252,21 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
           un.in.aux1 = (uint32_t)s;
           un.cu = (int)(a % C);
           un.reads.push_back({R_QKV, (uint16_t)l, (uint32_t)b, g * PPG, (g + 1) * PPG, 0, 1});
-          un.writes.push_back({R_PART, (uint16_t)l, (uint32_t)b, (uint32_t)(g * n_split + s),
-                               (uint32_t)(g * n_split + s + 1), 0});
-          un.sigs.push_back(g_attn[b * nkv + g]);
+          if (fused_attn) {
+            // one (paged) split per KV head: the unit merges in LDS and
+            // writes the attention output itself
+            un.writes.push_back({R_ATTN, (uint16_t)l, (uint32_t)b, (uint32_t)(g * G * hd),
+                                 (uint32_t)((g + 1) * G * hd), 0});
+            un.sigs.push_back(g_red);
+          } else {
+            un.writes.push_back({R_PART, (uint16_t)l, (uint32_t)b, (uint32_t)(g * n_split + s),
+                                 (uint32_t)(g * n_split + s + 1), 0});
+            un.sigs.push_back(g_attn[b * nkv + g]);
+          }
           bd.add(std::move(un));
         }
     // I3: reduction of the partials per (sequence, KV head).
-    const int n_red = B * nkv;
+    const int n_red = fused_attn ? 0 : B * nkv;
     for (int r = 0; r < n_red; ++r) {
       int b = r / nkv, g = r % nkv;
       Unit un;
