@@ -39,6 +39,8 @@ extern "C" {
 #define MK_ERR_HIP             (-4)  /* a HIP runtime call failed             */
 #define MK_ERR_NOT_CORESIDENT  (-5)  /* the grid cannot be co-resident        */
 #define MK_ERR_NO_DEVICE       (-6)  /* no usable GPU                         */
+#define MK_ERR_NOT_PREPARED    (-7)  /* mk_decode_step_static: the batch
+                                        size's schedule is not built yet     */
 #define MK_ERR_DEVICE_TIMEOUT  (-10) /* a counter wait exceeded the watchdog  */
 #define MK_ERR_BAD_TOKEN       (-11) /* tokens[b] outside [0, vocab)          */
 #define MK_ERR_BAD_POSITION    (-12) /* positions[b] outside [0, max_seq)     */
@@ -147,6 +149,32 @@ int mk_decode_step(mk_handle *h, int32_t batch, const int32_t *tokens,
  * as mk_decode_step (MK_ERR_INVALID_ARG also for a null output).  The
  * outputs are unspecified after a device error. */
 int mk_decode_step_greedy(mk_handle *h, int32_t batch, const int32_t *tokens,
+                          const int32_t *positions, void *kv_cache,
+                          float *logits, int32_t *next_tokens,
+                          int32_t *next_positions, void *stream);
+
+/* mk_decode_step_static -- mk_decode_step_greedy for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  It calls no hipMalloc, hipFree
+ * or allocating library routine: the step's scratch (its counter groups and
+ * greedy arrival counter, the attention partials and the greedy candidates)
+ * is a static array of the library, one per GPU, of 32 MiB, held until the
+ * process ends, and the schedule of `batch` must already exist (built by an
+ * earlier mk_decode_step or mk_decode_step_greedy call of this handle with
+ * the same batch size).  Each call first clears the counters with a small
+ * fill kernel on `stream` (no memset node), then launches the step: two
+ * kernels in stream order.
+ *   next_tokens, next_positions : as mk_decode_step_greedy, or both NULL for
+ *                                 a step without the greedy choice.
+ *   Other arguments as mk_decode_step.
+ * Every call on one GPU, from any handle, shares that GPU's array: calls
+ * whose executions overlap on one GPU (several streams, several threads)
+ * race and give wrong results; serialise them.  Ordinary steps of the same
+ * handle use their own scratch and may be mixed with these calls freely.
+ * Errors: MK_ERR_INVALID_ARG, MK_ERR_NOT_PREPARED (no schedule for this
+ * batch size yet), MK_ERR_UNSUPPORTED (the schedule's scratch exceeds the
+ * 32 MiB array), MK_ERR_HIP; device-side errors through mk_sync_status. */
+int mk_decode_step_static(mk_handle *h, int32_t batch, const int32_t *tokens,
                           const int32_t *positions, void *kv_cache,
                           float *logits, int32_t *next_tokens,
                           int32_t *next_positions, void *stream);

@@ -25,6 +25,7 @@ MK_ERR_OOM = -3
 MK_ERR_HIP = -4
 MK_ERR_NOT_CORESIDENT = -5
 MK_ERR_NO_DEVICE = -6
+MK_ERR_NOT_PREPARED = -7
 MK_ERR_DEVICE_TIMEOUT = -10
 MK_ERR_BAD_TOKEN = -11
 MK_ERR_BAD_POSITION = -12
@@ -37,7 +38,8 @@ MK_BUF_H, MK_BUF_Q, MK_BUF_ATTN, MK_BUF_A, MK_BUF_TRACE = 1, 2, 3, 4, 5
 EXPORTED = ("mk_create", "mk_decode_step", "mk_decode_step_greedy",
             "mk_sync_status", "mk_destroy", "mk_strerror", "mk_plan_check",
             "mk_get_buffer", "mk_version", "mk_stream_read",
-            "mk_stream_read_sink_words", "mk_addr_check")
+            "mk_stream_read_sink_words", "mk_addr_check",
+            "mk_decode_step_static")
 
 
 class MkConfig(C.Structure):
@@ -102,6 +104,10 @@ def lib():
                                             C.c_void_p, C.c_void_p, C.c_void_p,
                                             C.c_void_p, C.c_void_p, C.c_void_p]
         L.mk_decode_step_greedy.restype = C.c_int
+        L.mk_decode_step_static.argtypes = [C.c_void_p, C.c_int32, C.c_void_p,
+                                            C.c_void_p, C.c_void_p, C.c_void_p,
+                                            C.c_void_p, C.c_void_p, C.c_void_p]
+        L.mk_decode_step_static.restype = C.c_int
         L.mk_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
         L.mk_stream_read.restype = C.c_int
         L.mk_stream_read_sink_words.argtypes = []
@@ -230,6 +236,18 @@ class Megakernel:
             import torch
             stream = torch.cuda.current_stream().cuda_stream
         return lib().mk_decode_step_greedy(self.h, batch, _ptr(tokens), _ptr(positions),
+                                           _ptr(kv), _ptr(logits), _ptr(next_tokens),
+                                           _ptr(next_positions), stream)
+
+    def decode_step_static(self, batch: int, tokens, positions, kv, logits,
+                           next_tokens=None, next_positions=None,
+                           stream: Optional[int] = None) -> int:
+        """mk_decode_step_static: the step on the library's static scratch
+        (no allocation); the batch size's schedule must already exist."""
+        if stream is None:
+            import torch
+            stream = torch.cuda.current_stream().cuda_stream
+        return lib().mk_decode_step_static(self.h, batch, _ptr(tokens), _ptr(positions),
                                            _ptr(kv), _ptr(logits), _ptr(next_tokens),
                                            _ptr(next_positions), stream)
 

@@ -18,6 +18,8 @@
 namespace mk {
 hipError_t kernel_setup(int *blocks_per_cu);
 hipError_t kernel_launch(const Args &a, int grid, bool cooperative, bool paged, hipStream_t stream);
+hipError_t static_scratch(int device, void **ptr);
+hipError_t fill_zero(void *p, size_t words, hipStream_t stream);
 }  // namespace mk
 
 using namespace mk;
@@ -118,6 +120,7 @@ struct mk_handle {
   size_t h_bytes = 0, q_bytes = 0, attn_bytes = 0, a_bytes = 0, kvn_bytes = 0;
   std::map<int, std::unique_ptr<DevPlan>> plans;
   DevPlan *last_plan = nullptr;
+  void *static_scratch = nullptr;  // this device's array for mk_decode_step_static
   uint32_t tag = 0;  // activation tag of the last step (never 0; never reset)
   bool error_pending = false;
 };
@@ -135,6 +138,7 @@ const char *mk_strerror(int code) {
     case MK_ERR_HIP: return "HIP runtime call failed";
     case MK_ERR_NOT_CORESIDENT: return "the persistent grid cannot be co-resident";
     case MK_ERR_NO_DEVICE: return "no usable GPU";
+    case MK_ERR_NOT_PREPARED: return "the batch size's schedule is not built yet (run one ordinary step first)";
     case MK_ERR_DEVICE_TIMEOUT: return "a counter wait exceeded the watchdog";
     case MK_ERR_BAD_TOKEN: return "token id outside [0, vocab)";
     case MK_ERR_BAD_POSITION: return "position outside [0, max_seq)";
@@ -208,6 +212,9 @@ int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out) {
   int per_cu = 0;
   if (kernel_setup(&per_cu) != hipSuccess) return MK_ERR_HIP;
   if (per_cu < 1) return MK_ERR_NOT_CORESIDENT;
+  // the device address of this GPU's static scratch (resolved once per
+  // device, with the device current)
+  if (static_scratch(h->device, &h->static_scratch) != hipSuccess) return MK_ERR_HIP;
 
   h->layers.assign(w->layers, w->layers + cfg->n_layers);
   h->w = *w;
@@ -429,6 +436,32 @@ int mk_decode_step_greedy(mk_handle *h, int32_t batch, const int32_t *tokens, co
                           void *stream) {
   if (!next_tokens || !next_positions) return MK_ERR_INVALID_ARG;
   return launch_step(h, batch, tokens, positions, kv_cache, logits, next_tokens, next_positions, stream);
+}
+
+int mk_decode_step_static(mk_handle *h, int32_t batch, const int32_t *tokens, const int32_t *positions,
+                          void *kv_cache, float *logits, int32_t *next_tokens, int32_t *next_positions,
+                          void *stream) {
+  if (!h || !tokens || !positions || !kv_cache || !logits) return MK_ERR_INVALID_ARG;
+  if (batch < 1 || batch > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
+  if ((next_tokens == nullptr) != (next_positions == nullptr)) return MK_ERR_INVALID_ARG;
+  // no allocation here: the schedule must already exist, and the step's
+  // scratch is this GPU's static array
+  auto it = h->plans.find(batch);
+  if (it == h->plans.end()) return MK_ERR_NOT_PREPARED;
+  DevPlan *dp = it->second.get();
+  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const size_t part_bytes =
+      lay::part_size(h->cfg.n_layers, h->cfg.max_batch, h->cfg.n_q_heads, dp->plan.n_split, h->cfg.head_dim) * 4;
+  const size_t amax_bytes = (size_t)dp->n_lm * h->cfg.max_batch * 8;
+  const size_t off_part = up(dp->ctr_bytes), off_amax = off_part + up(part_bytes);
+  if (off_amax + amax_bytes > kStaticScratchBytes) return MK_ERR_UNSUPPORTED;
+  char *base = (char *)h->static_scratch;
+  // counters start from zero on every call (the array keeps the previous
+  // call's contents); a fill kernel, not a memset, so the step may be
+  // captured into a graph
+  if (fill_zero(base, dp->ctr_bytes / 4, (hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
+  const StepScratch sc{(uint32_t *)base, (float *)(base + off_part), (uint64_t *)(base + off_amax), 1u, 1u};
+  return launch_with(h, dp, batch, tokens, positions, kv_cache, logits, next_tokens, next_positions, sc, stream);
 }
 
 int mk_sync_status(mk_handle *h) {

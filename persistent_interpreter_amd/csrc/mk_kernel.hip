@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <mutex>
 
 #include "mk_layout.hpp"
 #include "mk_plan.hpp"
@@ -2537,6 +2539,49 @@ hipError_t kernel_setup(int *blocks_per_cu) {
     if (nb < *blocks_per_cu) *blocks_per_cu = nb;
   }
   return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for callers that cannot allocate (mk_decode_step_static):
+// one array per GPU, held until the process ends.  Host code never passes
+// the array's name to a kernel (in host code it is a stand-in, not a device
+// address): set-up resolves its device address once per device with
+// hipGetSymbolAddress and every use goes through that pointer.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(int device, void **ptr) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device) return hipErrorInvalidDevice;  // the device must be current
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = p;
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
+}
+
+// Zero `words` 32-bit words with vector stores (a kernel rather than a
+// memset node, so that the step can be captured into a graph).
+__global__ void __launch_bounds__(256) mk_fill_zero(uint32_t *__restrict__ p, uint32_t words) {
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < words; i += gridDim.x * 256u) p[i] = 0u;
+}
+
+hipError_t fill_zero(void *p, size_t words, hipStream_t stream) {
+  const uint32_t blocks = (uint32_t)std::min<size_t>((words + 255) / 256, 1024);
+  hipLaunchKernelGGL(mk_fill_zero, dim3(blocks ? blocks : 1), dim3(256), 0, stream, (uint32_t *)p,
+                     (uint32_t)words);
+  return hipGetLastError();
 }
 
 hipError_t kernel_launch(const Args &a0, int grid, bool cooperative, bool paged, hipStream_t stream) {

@@ -54,6 +54,10 @@ constexpr int kMfmaKc = 256;
 // Attention splits of at most this many positions run on registers (head
 // dim 64); longer ones, and head_dim 128, stream their K/V through pages.
 constexpr int kAttnRegRows = 20;
+// The static scratch of mk_decode_step_static (per GPU) and the number of
+// GPUs the library keeps one for.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
 constexpr int kMfmaRows = 64;
 
 // One queued instruction (96 bytes).  An instruction's weight stream is the
