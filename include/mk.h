@@ -55,6 +55,18 @@ extern "C" {
  * more per step on MI355X).  A plain launch whose workgroups cannot all run
  * ends in the watchdog: mk_sync_status reports MK_ERR_DEVICE_TIMEOUT. */
 #define MK_FLAG_COOPERATIVE 2u
+/* Test instruments ("Quand ne pas le faire", section 9.3: an ordering bug of
+ * a persistent kernel shows as a rare wrong token, not as a failed check):
+ * MK_FLAG_PERTURB makes every wave sleep a seeded pseudo-random time (0 to
+ * 31 units of 64 clocks, different for every step, workgroup, instruction
+ * and wave) before each instruction, so the same schedule runs under other
+ * interleavings; results must be bitwise the same.  MK_FLAG_TEST_STALL
+ * raises, on the host, the target of the counter the LM units wait on by
+ * one, so that wait can never complete: the step must end through the
+ * watchdog (MK_ERR_DEVICE_TIMEOUT from mk_sync_status) with every wave
+ * exiting.  Neither is meant for production use. */
+#define MK_FLAG_PERTURB     4u
+#define MK_FLAG_TEST_STALL  8u
 
 /* ---- model and schedule configuration ---------------------------------- */
 /* All sizes in elements.  The model is a pre-norm Llama-style decoder with

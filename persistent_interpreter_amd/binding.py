@@ -32,6 +32,8 @@ MK_ERR_BAD_POSITION = -12
 
 MK_FLAG_TRACE = 1
 MK_FLAG_COOPERATIVE = 2
+MK_FLAG_PERTURB = 4
+MK_FLAG_TEST_STALL = 8
 
 MK_BUF_H, MK_BUF_Q, MK_BUF_ATTN, MK_BUF_A, MK_BUF_TRACE = 1, 2, 3, 4, 5
 

@@ -336,6 +336,17 @@ static int get_plan(mk_handle *h, int batch, DevPlan **out) {
     free_plan(*dp);
     return rc;
   }
+  if (h->cfg.flags & MK_FLAG_TEST_STALL) {
+    // test instrument: the last counter group (every LM unit waits on it)
+    // gets one arrival more than its producers give, so that wait cannot
+    // complete and the step must end in the watchdog
+    std::vector<uint32_t> t = P.grp_target;
+    t[(size_t)(P.n_groups - 1) * kSlots] += 1;
+    if (hipMemcpy(dp->d_target, t.data(), t.size() * 4, hipMemcpyHostToDevice) != hipSuccess) {
+      free_plan(*dp);
+      return MK_ERR_HIP;
+    }
+  }
   if (hipMemset(dp->d_ctr, 0, dp->ctr_bytes) != hipSuccess || hipMemset(dp->d_part, 0, part) != hipSuccess) {
     free_plan(*dp);
     return MK_ERR_HIP;

@@ -252,7 +252,22 @@ struct Env {
   uint32_t nq;       // its length
   int cu;
   int pos0;          // positions[0], read once at kernel start (batch 1)
+  int flags;         // MK_FLAG_* of the handle
 };
+
+// MK_FLAG_PERTURB: a seeded pseudo-random delay (0..31 sleeps of 64 clocks)
+// before each instruction of each wave, different for every step (tag),
+// workgroup, instruction and wave, so that the same schedule runs under
+// other interleavings.
+constexpr int kFlagPerturb = 4;
+__device__ __forceinline__ void perturb(const Env &e, uint32_t tag, uint32_t qi, uint32_t wave) {
+  if (!(e.flags & kFlagPerturb)) return;
+  uint32_t x = tag * 0x9E3779B9u ^ (uint32_t)e.cu * 0x85EBCA6Bu ^ qi * 0xC2B2AE35u ^ wave * 0x27D4EB2Fu;
+  x ^= x >> 15;
+  x *= 0x2C1B3C6Du;
+  x ^= x >> 12;
+  for (uint32_t i = __builtin_amdgcn_readfirstlane(x & 31u); i > 0; --i) __builtin_amdgcn_s_sleep(1);
+}
 
 __device__ __forceinline__ int64_t now() { return (int64_t)wall_clock64(); }
 
@@ -493,6 +508,7 @@ __device__ __forceinline__ void loader_role(const Env &e, const Args &a, int lw)
   uint32_t n = 0;  // global page index
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
+    perturb(e, a.tag, qi, (uint32_t)(threadIdx.x >> 6));
     if (PAGED && d.op == OP_ATTN) {
       int lo, hi;
       uint32_t nr;
@@ -665,6 +681,7 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
   float rs = 0.f;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
+    perturb(e, a.tag, qi, (uint32_t)(threadIdx.x >> 6));
     const uint32_t nx = is_gemv(d.op) ? d.nk : 1;
     const bool normed = d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM;
     float *accs = reinterpret_cast<float *>(smem + L_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4);
@@ -1584,6 +1601,7 @@ __device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw
   uint32_t n = 0, seq = 0, aq_t = 0, am_t = 0;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
+    perturb(e, a.tag, qi, (uint32_t)(threadIdx.x >> 6));
     const bool gv = is_gemv(d.op);
     const uint32_t nx = gv ? d.nk : 1;
     uint32_t upages = d.pages;
@@ -1809,6 +1827,7 @@ __device__ __forceinline__ void loader_role_b(const Env &e, const Args &a, int l
   uint32_t n = 0;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
+    perturb(e, a.tag, qi, (uint32_t)(threadIdx.x >> 6));
     if (PAGED && d.op == OP_ATTN) {
       const DevCtx &c = *e.cp;
       int lo, hi;
@@ -1945,6 +1964,7 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
   uint32_t seq = 0;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
+    perturb(e, a.tag, qi, (uint32_t)(threadIdx.x >> 6));
     const bool gv = is_gemv(d.op);
     const uint32_t nx = gv ? d.nk : 1;
     const bool normed = d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM;
@@ -2294,6 +2314,7 @@ __device__ __forceinline__ void compute_role_b(const Env &e, const Args &a, int 
   uint32_t n = 0, seq = 0, aq_t = 0, am_t = 0;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
+    perturb(e, a.tag, qi, (uint32_t)(threadIdx.x >> 6));
     const bool gv = is_gemv(d.op);
     const uint32_t nx = gv ? d.nk : 1;
     uint32_t upages = d.pages;
@@ -2467,6 +2488,7 @@ mk_interp_b(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, con
   e.nq = q1 - q0;
   e.trace = a.trace ? a.trace + 4 + (size_t)e.cu * a.trace_stride * kTraceWords : nullptr;
   e.pos0 = 0;  // unused: batched roles read each sequence's own position
+  e.flags = e.cp->flags;
   if (threadIdx.x < 64) lds_u32(threadIdx.x * 4) = 0;  // control words
   for (int i = (int)threadIdx.x; i < kRingPagesB * kSentBytes / 4; i += kThreads)
     lds_u32(LB_SENT + 4 * i) = 0xffffffffu;
@@ -2502,6 +2524,7 @@ mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const
   // step is abandoned
   e.pos0 = a.positions[0];
   if (e.pos0 < 0 || e.pos0 >= e.cp->max_seq) e.pos0 = 0;
+  e.flags = e.cp->flags;
   if (threadIdx.x < 64) lds_u32(threadIdx.x * 4) = 0;  // control words
   // no page has landed: sentinels hold an index no page has
   for (int i = (int)threadIdx.x; i < kRingPages * kSentBytes / 4; i += kThreads)
