@@ -1748,21 +1748,43 @@ __device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw
 
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 
+#ifndef MK_BROT
+#define MK_BROT 1
+#endif
+// K-piece order of a batched GEMV unit: unit u takes its pieces starting at
+// piece u mod nk, so that at any moment the units of one instruction read
+// different activation pieces instead of all reading the same bytes.  The
+// loader (weights) and the sync wave (activations) map a unit's logical
+// piece k to the same physical piece; the compute waves only see logical
+// pieces.
+__device__ __forceinline__ uint32_t phys_k(const Instr &d, uint32_t k) {
+  if (!MK_BROT) return k;
+  const uint32_t nk = d.nk, r = d.unit % nk, kk = k + r;
+  return kk >= nk ? kk - nk : kk;
+}
+
 // LDS layout of the batched kernel (bytes; control words as above)
 constexpr int LB_AMAX = 192;    // u64[8]  running greedy best per sequence of this workgroup
 constexpr int LB_ACC = 256;     // f32 [kAccSlots][kAccFloats]: residual rows [row][seq], RoPE staging
 constexpr int LB_PART = LB_ACC + kAccSlots * kAccFloats * 4;  // f32 [2][kNCW][128] partial tiles
 // Activation staging: a piece's fp32 inputs of up to 8 sequences (rows of
 // 256 elements, 1040 bytes apart so that the 8 sequences of one k-offset
-// fall in different LDS banks) and its 256 bf16 norm weights; three slots,
-// so that two pieces are in flight while the compute waves use a third.
-constexpr int kNXSB = 3;
+// fall in different LDS banks) and its 256 bf16 norm weights.  kInflB pieces
+// are in flight while the compute waves use another: a unit's pieces cost
+// one memory round trip per kInflB of them, not one each.
+#ifndef MK_BINFL
+#define MK_BINFL 4
+#endif
+constexpr int kInflB = MK_BINFL;
+constexpr int kNXSB = kInflB + 1;
 constexpr int kXRowB = 1040;
 constexpr int kXNwB = 8 * kXRowB;                              // norm weights within a slot
 constexpr int kXSlotB = kXNwB + 512;
 constexpr int LB_XS = LB_PART + 2 * kNCW * 128 * 4;
 constexpr int LB_RING = ((LB_XS + kNXSB * kXSlotB + 1023) / 1024) * 1024;
-constexpr int kRingPagesB = 7;
+// the weight ring takes what is left
+constexpr int kRingPagesB = (kLdsBytes - LB_RING) / (kPageBytes + kSentBytes);
+static_assert(kRingPagesB >= 4, "batched ring");
 constexpr int LB_SENT = LB_RING + kRingPagesB * kPageBytes;
 static_assert(LB_SENT + kRingPagesB * kSentBytes <= kLdsBytes, "batched LDS budget");
 static_assert(LB_AMAX + 8 * 8 <= LB_ACC && L_EPI < LB_AMAX, "control words");
@@ -1772,18 +1794,27 @@ __device__ __forceinline__ int seq_pos(const Args &a, const DevCtx &c, int b) {
   return (p < 0 || p >= c.max_seq) ? 0 : p;
 }
 
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to bf16 (RNE) by the hardware conversion
+// (v_cvt_pk_bf16_f32), first value in the low half.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2v{a, b}, bf2v));
+}
+
 // 8 consecutive fp32 values as the A operand of one lane: their hi parts, or
-// (lo) what is left of each after its hi part, both bf16 (RNE).
+// (lo) what is left of each after its hi part, both bf16 (RNE).  x - hi is
+// exact in fp32.  Branch-free: every lane converts twice and keeps the
+// operand of its half of the wave.
 __device__ __forceinline__ u4 pack_hilo(const float (&x)[8], bool lo) {
   uint32_t w[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    uint16_t h0 = f2bf(x[2 * j]), h1 = f2bf(x[2 * j + 1]);
-    if (lo) {
-      h0 = f2bf(x[2 * j] - bf16f(h0));
-      h1 = f2bf(x[2 * j + 1] - bf16f(h1));
-    }
-    w[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    const float x0 = x[2 * j], x1 = x[2 * j + 1];
+    const uint32_t h = cvt_pk_bf16(x0, x1);
+    const float r0 = x0 - __uint_as_float(h << 16), r1 = x1 - __uint_as_float(h & 0xffff0000u);
+    w[j] = cvt_pk_bf16(lo ? r0 : x0, lo ? r1 : x1);
   }
   return u4{w[0], w[1], w[2], w[3]};
 }
@@ -1894,7 +1925,7 @@ __device__ __forceinline__ void loader_role_b(const Env &e, const Args &a, int l
           cur_rb = rb;
           rowp = row_start(d, a.rowtab, rb, R, lane);
         }
-        const uint32_t kk = k * kMfmaKc + kb * 64 + 8 * (uint32_t)(lane >> 3);
+        const uint32_t kk = phys_k(d, k) * kMfmaKc + kb * 64 + 8 * (uint32_t)(lane >> 3);
         const char *src = kk < K ? rowp + (size_t)kk * 2 : zero;
         __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)(slot + j * 1024), 16, 0, kWPol);
       }
@@ -1906,41 +1937,20 @@ __device__ __forceinline__ void loader_role_b(const Env &e, const Args &a, int l
 }
 
 // Load-count wait for the batched sync wave's pipeline: the loads of the
-// younger pieces in flight (at most 2 pieces of at most kMaxBatch + 1
-// loads; piece 0 of O and DOWN adds kMaxBatch residual loads, but it is
-// never a younger piece).
-__device__ __forceinline__ void wait_vm_le(uint32_t n) {
-  switch (n) {
-    case 0: wait_vm_n<0>(); break;
-    case 1: wait_vm_n<1>(); break;
-    case 2: wait_vm_n<2>(); break;
-    case 3: wait_vm_n<3>(); break;
-    case 4: wait_vm_n<4>(); break;
-    case 5: wait_vm_n<5>(); break;
-    case 6: wait_vm_n<6>(); break;
-    case 7: wait_vm_n<7>(); break;
-    case 8: wait_vm_n<8>(); break;
-    case 9: wait_vm_n<9>(); break;
-    case 10: wait_vm_n<10>(); break;
-    case 11: wait_vm_n<11>(); break;
-    case 12: wait_vm_n<12>(); break;
-    case 13: wait_vm_n<13>(); break;
-    case 14: wait_vm_n<14>(); break;
-    case 15: wait_vm_n<15>(); break;
-    case 16: wait_vm_n<16>(); break;
-    case 17: wait_vm_n<17>(); break;
-    case 18: wait_vm_n<18>(); break;
-    case 19: wait_vm_n<19>(); break;
-    case 20: wait_vm_n<20>(); break;
-    case 21: wait_vm_n<21>(); break;
-    case 22: wait_vm_n<22>(); break;
-    case 23: wait_vm_n<23>(); break;
-    case 24: wait_vm_n<24>(); break;
-    case 25: wait_vm_n<25>(); break;
-    case 26: wait_vm_n<26>(); break;
-    default: wait_vm_n<27>(); break;
+// younger pieces in flight (at most kInflB - 1 pieces of at most
+// kMaxBatch + 1 loads; piece 0 of O and DOWN adds kMaxBatch residual
+// loads, but it is never a younger piece).
+template <int N>
+__device__ __forceinline__ void wait_vm_sel(uint32_t n) {
+  if constexpr (N == 0) {
+    wait_vm_n<0>();
+  } else {
+    if (n >= (uint32_t)N) wait_vm_n<N>();
+    else wait_vm_sel<N - 1>(n);
   }
 }
+static_assert((kInflB - 1) * (kMaxBatch + 1) <= 63, "load counter range");
+__device__ __forceinline__ void wait_vm_le(uint32_t n) { wait_vm_sel<(kInflB - 1) * (kMaxBatch + 1)>(n); }
 
 // The batched sync wave.  For each GEMV unit it copies the activation pieces
 // (fp32 rows of every sequence, and the norm weights of normed units)
@@ -2016,37 +2026,49 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
       continue;
     }
     const uint32_t K = d.rowb >> 1;
-    // this lane's part of a piece: sequence b's elements 4*lane .. 4*lane+3
-    // (fp32 rows), norm weights 8*lane .. 8*lane+7 (lanes < 32)
-    auto src_of = [&](int b) -> const char * {
-      if (d.op == OP_O) return reinterpret_cast<const char *>(c.attn_buf + lay::attn(c.max_batch, c.nq, c.hd, d.layer, b));
-      if (d.op == OP_DOWN) return reinterpret_cast<const char *>(c.a_buf + lay::a(c.max_batch, c.F, d.layer, b));
-      const float *h;
-      const uint16_t *emb, *w;
-      norm_src(e, a, d, b, h, emb, w);
-      return reinterpret_cast<const char *>(h);
-    };
+    // The unit's input rows: sequence b's starts at src0 + b * sstr bytes,
+    // its residual row (O, DOWN) at res0 + b * rstr.  They are computed once
+    // per unit into registers: the compiler treats every direct-to-LDS load
+    // as a possible store, and would re-read the context with a scalar
+    // round trip per sequence if the issue loop derived them from it.
+    const char *src0 = zero, *res0 = zero;
+    uint32_t sstr = 0, rstr = (uint32_t)c.H * 4;
     const uint16_t *nw = nullptr;
-    if (normed) {
+    if (d.op == OP_O) {
+      src0 = reinterpret_cast<const char *>(c.attn_buf + lay::attn(c.max_batch, c.nq, c.hd, d.layer, 0));
+      sstr = (uint32_t)(c.nq * c.hd) * 4;
+      res0 = reinterpret_cast<const char *>(c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer, 0) + d.item0 + lane);
+    } else if (d.op == OP_DOWN) {
+      src0 = reinterpret_cast<const char *>(c.a_buf + lay::a(c.max_batch, c.F, d.layer, 0));
+      sstr = (uint32_t)c.F * 4;
+      res0 = reinterpret_cast<const char *>(c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer + 1, 0) + d.item0 + lane);
+    } else {
       const float *h;
       const uint16_t *emb;
       norm_src(e, a, d, 0, h, emb, nw);
+      if (h) src0 = reinterpret_cast<const char *>(h);
+      sstr = (uint32_t)c.H * 4;
     }
+    // layer 0's QKV widens the bf16 embedding rows of the step's tokens
+    const uint16_t *embed = c.embed;
+    const uint32_t Hs = (uint32_t)c.H;
+    const int32_t tok_l = emb_in && lane < B ? a.tokens[lane] : 0;
     const uint32_t loads = (emb_in ? 0u : (uint32_t)B) + (normed ? 1u : 0u);
     float ss = 0.f;  // sum of squares of sequence lane >> 3, over this lane's part
     auto issue = [&](uint32_t k, uint32_t sq) -> uint32_t {
       LDS_AS char *slot = (LDS_AS char *)smem + LB_XS + (sq % kNXSB) * kXSlotB;
-      const uint32_t e0 = k * kMfmaKc + 4 * (uint32_t)lane;
+      const uint32_t kp = phys_k(d, k);
+      const uint32_t e0 = kp * kMfmaKc + 4 * (uint32_t)lane;
       uint32_t nl = 0;
       if (!emb_in) {
-        for (int b = 0; b < B; ++b) {
-          const char *src = e0 < K ? src_of(b) + (size_t)e0 * 4 : zero;
-          __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)(slot + b * kXRowB), 16, 0, kSC1);
+        const char *src = src0 + (size_t)e0 * 4;
+        for (int b = 0; b < B; ++b, src += sstr) {
+          __builtin_amdgcn_global_load_lds(e0 < K ? src : zero, (LDS_AS void *)(slot + b * kXRowB), 16, 0, kSC1);
           ++nl;
         }
       }
       if (normed) {
-        const uint32_t w0 = k * kMfmaKc + 8 * (uint32_t)lane;
+        const uint32_t w0 = kp * kMfmaKc + 8 * (uint32_t)lane;
         if (lane < 32)
           __builtin_amdgcn_global_load_lds(w0 < K ? reinterpret_cast<const char *>(nw + w0) : zero,
                                            (LDS_AS void *)(slot + kXNwB), 16, 0, 0);
@@ -2055,13 +2077,13 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
       if (k == 0 && (d.op == OP_O || d.op == OP_DOWN)) {
         // residual rows [sequence][64]: lane r < rows takes row r
         LDS_AS char *accl = (LDS_AS char *)smem + LB_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4;
-        for (int b = 0; b < B; ++b) {
-          if (d.op == OP_O && d.layer == 0) continue;  // bf16 embedding: loaded below
-          const float *res =
-              c.h_buf + lay::h(c.max_batch, c.H, d.op == OP_O ? 2 * d.layer : 2 * d.layer + 1, b) + d.item0 + lane;
-          if (lane < (int)d.n_items)
-            __builtin_amdgcn_global_load_lds(res, (LDS_AS void *)(accl + b * 64 * 4), 4, 0, kSC1);
-          ++nl;
+        if (!(d.op == OP_O && d.layer == 0)) {  // (layer 0's O: the bf16 embedding, below)
+          const char *res = res0;
+          for (int b = 0; b < B; ++b, res += rstr) {
+            if (lane < (int)d.n_items)
+              __builtin_amdgcn_global_load_lds(res, (LDS_AS void *)(accl + b * 64 * 4), 4, 0, kSC1);
+            ++nl;
+          }
         }
       }
       return nl;
@@ -2072,10 +2094,11 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
       if (emb_in) {
         // bf16 embedding rows of every sequence, widened into the slot
         for (int b = 0; b < B; ++b) {
-          const uint32_t e0 = k * kMfmaKc + 4 * (uint32_t)lane;
+          const uint32_t e0 = phys_k(d, k) * kMfmaKc + 4 * (uint32_t)lane;
+          const int32_t tk = __builtin_amdgcn_readlane(tok_l, b);
           f4 v = {0.f, 0.f, 0.f, 0.f};
           if (e0 < K) {
-            const uint64_t uu = *G(reinterpret_cast<const uint64_t *>(c.embed + (size_t)a.tokens[b] * c.H + e0));
+            const uint64_t uu = *G(reinterpret_cast<const uint64_t *>(embed + (size_t)tk * Hs + e0));
             v = f4{bf_lo((uint32_t)uu), bf_hi((uint32_t)uu), bf_lo((uint32_t)(uu >> 32)), bf_hi((uint32_t)(uu >> 32))};
           }
           *reinterpret_cast<LDS_AS f4 *>(slot + b * kXRowB + lane * 16) = v;
@@ -2097,14 +2120,15 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
     };
     int64_t t_first = 0, t_last = 0;
     uint32_t issued = 0, done = 0;
-    uint32_t nl[kNXSB] = {0, 0, 0};  // loads of each piece in flight (by piece % kNXSB)
+    uint32_t nl[kNXSB] = {};  // loads of each piece in flight (by piece % kNXSB)
     while (done < nx) {
-      if (issued < nx && issued - done < 2) {  // two pieces in flight (three measured slower)
+      if (issued < nx && issued - done < (uint32_t)kInflB) {
         // waits of piece `issued`, then a free slot (every compute wave
         // released the piece kNXSB before it)
         while (wi < d.wait_n) {
           const Wait wt = a.waits[d.wait_off + wi];
-          if (wt.before_k > issued) break;
+          // (a rotated piece order takes every wait before its first piece)
+          if (!MK_BROT && wt.before_k > issued) break;
           if (!wait_group(e, a, wt, qi)) { wait_vm0(); return; }
           ++wi;
         }
@@ -2351,18 +2375,20 @@ __device__ __forceinline__ void compute_role_b(const Env &e, const Args &a, int 
       const uint32_t kA = 8 * (uint32_t)(lane >> 4);
       f4 acc = {0.f, 0.f, 0.f, 0.f};
       uint32_t rel = n, v0 = 0xffffffffu, v1 = 0xffffffffu;
-      for (uint32_t k = 0; k < d.nk; ++k) {
-        if (k > 0) {
-          if (lane == 0) lds_st(L_XCONS + 4 * cw, seq + k);
-          wake();
-        }
-        bool ready = false;
-        for (uint32_t ks = 0; ks < 8; ++ks) {
-          if ((k * 8 + ks) % nwt != kg) continue;
-          if (!ready) {
-            if (!spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq + k; }, 0x400 | qi)) return;
-            ready = true;
+      // this wave's K steps of 32: j = kg, kg + nwt, ... (nwt <= 8, so every
+      // piece k = j / 8 holds at least one of them)
+      uint32_t kcur = 0xffffffffu;
+      for (uint32_t j = kg; j < (uint32_t)d.nk * 8; j += nwt) {
+        const uint32_t k = j >> 3, ks = j & 7;
+        if (k != kcur) {
+          if (k > 0) {  // every earlier piece is released
+            if (lane == 0) lds_st(L_XCONS + 4 * cw, seq + k);
+            wake();
           }
+          if (!spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq + k; }, 0x400 | qi)) return;
+          kcur = k;
+        }
+        {
           const uint32_t L0 = (k * nrb + rb_lo) * 4 + (ks >> 1), L1 = (k * nrb + rb_hi) * 4 + (ks >> 1);
           const uint32_t pg0 = n + (L0 >> 4), pg1 = n + (L1 >> 4);
           if (pg0 > rel) {
@@ -2493,7 +2519,9 @@ mk_interp_b(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, con
   for (int i = (int)threadIdx.x; i < kRingPagesB * kSentBytes / 4; i += kThreads)
     lds_u32(LB_SENT + 4 * i) = 0xffffffffu;
   __syncthreads();
-  const int w = (int)(threadIdx.x >> 6);
+  // the wave index is uniform within a wave: saying so keeps each role's
+  // control flow on the scalar unit instead of exec-masked vector code
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   if (w < kNCW) compute_role_b<PAGED>(e, a, w);
   else if (w < kNCW + kNLW) loader_role_b<PAGED>(e, a, w - kNCW);
   else sync_role_b(e, a);
@@ -2530,7 +2558,9 @@ mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const
   for (int i = (int)threadIdx.x; i < kRingPages * kSentBytes / 4; i += kThreads)
     lds_u32(L_SENT + 4 * i) = 0xffffffffu;
   __syncthreads();
-  const int w = (int)(threadIdx.x >> 6);
+  // the wave index is uniform within a wave: saying so keeps each role's
+  // control flow on the scalar unit instead of exec-masked vector code
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 #if MK_PRIO
   // issue priority: the sync wave (critical-path waits and activation
   // pieces) first, compute waves next, weight streaming last
