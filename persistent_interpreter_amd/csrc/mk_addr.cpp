@@ -221,8 +221,9 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
           norm_src(d, 0, h, emb, nw);
         }
         for (uint32_t k = 0; k < nx; ++k) {
+          const uint32_t kp = lay::mfma_phys_k(k, d.nk, d.unit);  // the piece logical piece k stages
           for (int lane = 0; lane < 64; ++lane) {
-            const uint32_t e0 = k * kMfmaKc + 4 * (uint32_t)lane;
+            const uint32_t e0 = kp * kMfmaKc + 4 * (uint32_t)lane;
             for (int b = 0; b < batch; ++b) {
               if (emb_in) {
                 if (e0 < K) M.at(B.embed + ((uint64_t)tokens[b] * H + e0) * 2, 8, B.embed, "sync(b): embedding piece");
@@ -236,7 +237,7 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
               else M.at(B.zero, 16, B.zero, "sync(b): zero padding");
             }
             if (normed && lane < 32) {
-              const uint32_t w0 = k * kMfmaKc + 8 * (uint32_t)lane;
+              const uint32_t w0 = kp * kMfmaKc + 8 * (uint32_t)lane;
               if (w0 < K) M.at(nw + (uint64_t)w0 * 2, 16, nw, "sync(b): staged norm weights");
               else M.at(B.zero, 16, B.zero, "sync(b): zero padding");
             }
@@ -263,11 +264,14 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
       if (!is_gemv(d.op)) continue;
       const uint32_t R = d.n_items * d.ipw, nrb = d.ppp, K = d.rowb >> 1;
       const uint32_t nblk = (uint32_t)d.nk * nrb * 4;
+      const bool wide = lay::mfma_wide(nrb);
       for (uint32_t p = 0; p < d.pages; ++p, ++n) {
         for (uint32_t j = 0; j < 16; ++j) {
           uint32_t Lb = p * 16 + j;
           if (Lb >= nblk) Lb = 0;
-          const uint32_t kb = Lb & 3, rbk = Lb >> 2, rb = rbk % nrb, k = rbk / nrb;
+          uint32_t k, kb, rb;
+          lay::mfma_block(Lb, nrb, wide, k, kb, rb);
+          k = lay::mfma_phys_k(k, d.nk, d.unit);
           if (d.tab >= 0)
             for (uint32_t i = 0; i < 8; ++i)
               M.el(B.rowtab, (uint64_t)d.tab + std::min(rb * 8 + i, R - 1), 8, 8, "loader(b): row table");

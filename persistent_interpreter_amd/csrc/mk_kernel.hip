@@ -141,6 +141,9 @@ __device__ __forceinline__ void wake() { asm volatile("s_wakeup" ::: "memory"); 
 #ifndef MK_PRIO
 #define MK_PRIO 0  // wave issue priorities by role (s_setprio)
 #endif
+#ifndef MK_BPRIO
+#define MK_BPRIO 1  // the same for the batched kernel
+#endif
 #ifndef MK_WSLEEP
 #define MK_WSLEEP 1  // counter polls: s_sleep units (64 clocks) between polls
 #endif
@@ -1748,20 +1751,7 @@ __device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw
 
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 
-#ifndef MK_BROT
-#define MK_BROT 1
-#endif
-// K-piece order of a batched GEMV unit: unit u takes its pieces starting at
-// piece u mod nk, so that at any moment the units of one instruction read
-// different activation pieces instead of all reading the same bytes.  The
-// loader (weights) and the sync wave (activations) map a unit's logical
-// piece k to the same physical piece; the compute waves only see logical
-// pieces.
-__device__ __forceinline__ uint32_t phys_k(const Instr &d, uint32_t k) {
-  if (!MK_BROT) return k;
-  const uint32_t nk = d.nk, r = d.unit % nk, kk = k + r;
-  return kk >= nk ? kk - nk : kk;
-}
+__device__ __forceinline__ uint32_t phys_k(const Instr &d, uint32_t k) { return lay::mfma_phys_k(k, d.nk, d.unit); }
 
 // LDS layout of the batched kernel (bytes; control words as above)
 constexpr int LB_AMAX = 192;    // u64[8]  running greedy best per sequence of this workgroup
@@ -1773,7 +1763,7 @@ constexpr int LB_PART = LB_ACC + kAccSlots * kAccFloats * 4;  // f32 [2][kNCW][1
 // are in flight while the compute waves use another: a unit's pieces cost
 // one memory round trip per kInflB of them, not one each.
 #ifndef MK_BINFL
-#define MK_BINFL 4
+#define MK_BINFL 3
 #endif
 constexpr int kInflB = MK_BINFL;
 constexpr int kNXSB = kInflB + 1;
@@ -1896,6 +1886,7 @@ __device__ __forceinline__ void loader_role_b(const Env &e, const Args &a, int l
     if (!is_gemv(d.op)) continue;
     const uint32_t R = d.n_items * d.ipw, nrb = d.ppp, K = d.rowb >> 1;
     const uint32_t nblk = (uint32_t)d.nk * nrb * 4;
+    const bool wide = lay::mfma_wide(nrb);
     uint32_t cur_rb = 0xffffffffu;
     const char *rowp = nullptr;
     for (uint32_t p = 0; p < d.pages; ++p, ++n) {
@@ -1920,7 +1911,8 @@ __device__ __forceinline__ void loader_role_b(const Env &e, const Args &a, int l
       for (uint32_t j = 0; j < 16; ++j) {
         uint32_t L = p * 16 + j;
         if (L >= nblk) L = 0;  // tail of the last page: re-read the first block
-        const uint32_t kb = L & 3, rbk = L >> 2, rb = rbk % nrb, k = rbk / nrb;
+        uint32_t k, kb, rb;
+        lay::mfma_block(L, nrb, wide, k, kb, rb);
         if (rb != cur_rb) {
           cur_rb = rb;
           rowp = row_start(d, a.rowtab, rb, R, lane);
@@ -2206,6 +2198,39 @@ __device__ __forceinline__ void unit_epilogue_b(const Env &e, const Args &a, con
   const int lane = lane_id();
   const uint32_t B = (uint32_t)a.batch;
   const uint32_t T = ((uint32_t)d.ppp + 1) >> 1;
+  if (T > (uint32_t)kNCW) {
+    // a wide LM unit: the waves stored the logits; merge their candidates
+    // (in wave order) into the workgroup's running best per sequence
+    if (!a.next_tok) return;
+    uint64_t *run = reinterpret_cast<uint64_t *>(smem + LB_AMAX);
+    const uint64_t *cand = reinterpret_cast<const uint64_t *>(Pb);
+    if ((uint32_t)lane < B) {
+      float bv = -INFINITY;
+      uint32_t bi = 0xffffffffu;
+      for (int w = 0; w < kNCW; ++w) {
+        const uint64_t x = cand[w * 8 + lane];
+        const float v = __uint_as_float((uint32_t)x);
+        const uint32_t i = (uint32_t)(x >> 32);
+        if (amax_better(v, i, bv, bi)) {
+          bv = v;
+          bi = i;
+        }
+      }
+      if (!(d.aux1 & 1u)) {
+        const uint64_t w = run[lane];
+        const float ov = __uint_as_float((uint32_t)w);
+        const uint32_t oi = (uint32_t)(w >> 32);
+        if (amax_better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      run[lane] = ((uint64_t)bi << 32) | __float_as_uint(bv);
+      if (d.aux1 & 2u) st_tag(a.amax + (size_t)d.aux0 * B + lane, bv, bi);
+    }
+    wait_lgkm0();
+    return;
+  }
   // normed units: the sequence's 1/rms (accs[b]); O, DOWN: residual rows
   // accs[b * 64 + row]
   for (uint32_t x = (uint32_t)lane; x < d.n_items * B; x += 64) {
@@ -2330,6 +2355,150 @@ __device__ __forceinline__ void lm_greedy_finish_b(const Env &e, const Args &a) 
   }
 }
 
+// A wide LM-head unit (more than 8 row tiles): compute wave cw owns the
+// whole tiles t = cw, cw + 8, ... (at most 4), so no partial tiles are summed
+// across waves.  Per piece it builds the 8 A operands once and runs them
+// against each of its tiles in turn; tile by tile, the waves walk the pages
+// of a piece in order.  The wave then stores its rows' logits and leaves
+// each sequence's best (logit, row) of its rows in the candidate area.
+__device__ bool gemv_wide_b(const Env &e, const Args &a, const Instr &d, int cw, uint32_t n, uint32_t seq,
+                            uint32_t qi, const float *accs, uint64_t *cand) {
+  const DevCtx &c = *e.cp;
+  const int lane = lane_id();
+  constexpr uint32_t P = kRingPagesB;
+  const uint32_t nrb = d.ppp, T = (nrb + 1) >> 1, R = d.n_items;
+  const uint32_t ntw = (T - (uint32_t)cw + kNCW - 1) / kNCW;
+  const bool upper = (lane & 15) >= 8;
+  const uint32_t brow = (uint32_t)(((lane >> 4) * 8 + (lane & 7)) * 16);
+  const int sA = lane & 7;
+  const bool loA = (lane & 15) >= 8, liveA = sA < a.batch;
+  const uint32_t kA = 8 * (uint32_t)(lane >> 4);
+  f4 acc[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = f4{0.f, 0.f, 0.f, 0.f};
+  uint32_t rel = n, v0 = 0xffffffffu, v1 = 0xffffffffu;
+  for (uint32_t k = 0; k < d.nk; ++k) {
+    if (k > 0) {
+      if (lane == 0) lds_st(L_XCONS + 4 * cw, seq + k);
+      wake();
+    }
+    if (!spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq + k; }, 0x400 | qi)) return false;
+    const uint32_t slot = (uint32_t)LB_XS + ((seq + k) % kNXSB) * kXSlotB;
+    for (uint32_t kb = 0; kb < 4; ++kb) {
+      // the A operands of K steps 2kb and 2kb + 1 (64 elements of the piece)
+      u4 A[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t ks = 2 * kb + (uint32_t)h;
+        const uint32_t xaddr = lds_addr((int)(slot + sA * kXRowB + (ks * 32 + kA) * 4));
+        const uint32_t waddr = lds_addr((int)(slot + kXNwB + (ks * 32 + kA) * 2));
+        u4 x0, x1, wv;
+        asm volatile(
+            "ds_read_b128 %0, %3\n\t"
+            "ds_read_b128 %1, %3 offset:16\n\t"
+            "ds_read_b128 %2, %4\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(x0), "=&v"(x1), "=&v"(wv)
+            : "v"(xaddr), "v"(waddr));
+        float x[8] = {__uint_as_float(x0.x), __uint_as_float(x0.y), __uint_as_float(x0.z), __uint_as_float(x0.w),
+                      __uint_as_float(x1.x), __uint_as_float(x1.y), __uint_as_float(x1.z), __uint_as_float(x1.w)};
+        x[0] *= bf_lo(wv.x); x[1] *= bf_hi(wv.x); x[2] *= bf_lo(wv.y); x[3] *= bf_hi(wv.y);
+        x[4] *= bf_lo(wv.z); x[5] *= bf_hi(wv.z); x[6] *= bf_lo(wv.w); x[7] *= bf_hi(wv.w);
+        if (!liveA) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = 0.f;
+        }
+        A[h] = pack_hilo(x, loA);
+      }
+#pragma unroll
+      for (uint32_t r = 0; r < 4; ++r) {
+        if (r >= ntw) break;
+        const uint32_t t = (uint32_t)cw + kNCW * r;
+        const uint32_t Llo = lay::mfma_block_index(k, kb, 2 * t, nrb, true);
+        const uint32_t Lhi = lay::mfma_block_index(k, kb, min(2 * t + 1, nrb - 1), nrb, true);
+        const uint32_t pgA = n + (Llo >> 4), pgB = n + (Lhi >> 4);
+        if (pgA > rel) {
+          if (lane == 0) lds_st(L_CONS + 4 * cw, pgA);
+          rel = pgA;
+          wake();
+        }
+        for (uint32_t pg = pgA; pg <= pgB; ++pg) {
+          if (pg == v0 || pg == v1) continue;
+          if (!spin_lds_fast(e, [&]() { return lds_ld(LB_SENT + (pg % P) * kSentBytes) == pg; }, 0x300 | qi))
+            return false;
+          v0 = v1;
+          v1 = pg;
+        }
+        const uint32_t Lb = upper ? Lhi : Llo, pg = n + (Lb >> 4);
+        const uint32_t baddr = lds_addr(LB_RING + (int)((pg % P) * kPageBytes + (Lb & 15) * 1024 + brow));
+        u4 b0, b1;
+        asm volatile(
+            "ds_read_b128 %0, %2\n\t"
+            "ds_read_b128 %1, %2 offset:512\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(b0), "=&v"(b1)
+            : "v"(baddr));
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, A[0]), __builtin_bit_cast(bf8v, b0),
+                                                        acc[r], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, A[1]), __builtin_bit_cast(bf8v, b1),
+                                                        acc[r], 0, 0, 0);
+      }
+    }
+  }
+  // hi + lo halves (lanes l and l + 32), then lane l < 32 holds rows
+  // t*16 + l % 16 for sequences 4*(l/16) .. 4*(l/16) + 3
+  float bvv[4];
+  uint32_t bii[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bvv[j] = -INFINITY;
+    bii[j] = 0xffffffffu;
+  }
+  const uint32_t B = (uint32_t)a.batch;
+#pragma unroll
+  for (uint32_t r = 0; r < 4; ++r) {
+    if (r >= ntw) break;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[r][j] += __shfl_xor(acc[r][j], 32);
+    const uint32_t row = ((uint32_t)cw + kNCW * r) * 16 + (uint32_t)(lane & 15);
+    if (lane < 32 && row < R) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t sq = 4 * (uint32_t)(lane >> 4) + (uint32_t)j;
+        if (sq < B) {
+          const float v = acc[r][j] * accs[sq];
+          G(a.logits)[lay::logits(c.V, (int)sq) + d.item0 + row] = v;
+          if (amax_better(v, d.item0 + row, bvv[j], bii[j])) {
+            bvv[j] = v;
+            bii[j] = d.item0 + row;
+          }
+        }
+      }
+    }
+  }
+  if (a.next_tok) {
+    // best of the 16 lanes that share a sequence group
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const float ov = __shfl_xor(bvv[j], off);
+        const uint32_t oi = (uint32_t)__shfl_xor((int)bii[j], off);
+        if (amax_better(ov, oi, bvv[j], bii[j])) {
+          bvv[j] = ov;
+          bii[j] = oi;
+        }
+      }
+    }
+    if (lane == 0 || lane == 16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        cand[cw * 8 + 4 * (lane >> 4) + j] = ((uint64_t)bii[j] << 32) | __float_as_uint(bvv[j]);
+    }
+  }
+  return true;
+}
+
 template <bool PAGED>
 __device__ __forceinline__ void compute_role_b(const Env &e, const Args &a, int cw) {
   const DevCtx &c = *e.cp;
@@ -2361,7 +2530,15 @@ __device__ __forceinline__ void compute_role_b(const Env &e, const Args &a, int 
     if (cw == 0 && lane == 0) trace_now(e, qi, 2);
     const float *accs = reinterpret_cast<const float *>(smem + LB_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4);
     float *Pb = reinterpret_cast<float *>(smem + LB_PART + (qi & 1) * kNCW * 128 * 4);
-    if (gv) {
+    if (gv && ((uint32_t)d.ppp + 1) / 2 > (uint32_t)kNCW) {
+      // (the candidate area is the partial-tile buffer, last read by unit
+      // qi - 2's epilogue)
+      if (qi >= 2 && !spin_lds(e, [&]() { return lds_ld(L_EPI) + 1 >= qi; }, 0x600 | qi)) return;
+      if (!gemv_wide_b(e, a, d, cw, n, seq, qi, accs, reinterpret_cast<uint64_t *>(Pb))) return;
+      wait_lgkm0();
+      if (lane == 0) lds_st(L_CONS + 4 * cw, n + d.pages);
+      wake();
+    } else if (gv) {
       const uint32_t nrb = d.ppp, T = (nrb + 1) >> 1;
       const uint32_t t = (uint32_t)cw % T, nwt = ((uint32_t)kNCW - 1 - t) / T + 1, kg = (uint32_t)cw / T;
       const uint32_t rb_lo = 2 * t, rb_hi = min(2 * t + 1, nrb - 1);
@@ -2522,6 +2699,12 @@ mk_interp_b(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, con
   // the wave index is uniform within a wave: saying so keeps each role's
   // control flow on the scalar unit instead of exec-masked vector code
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+#if MK_BPRIO
+  // issue priority: the sync wave's activation pieces ahead of the weight
+  // stream, whose loads otherwise fill the CU's memory queue first
+  if (w >= kNCW + kNLW) __builtin_amdgcn_s_setprio(3);
+  else if (w < kNCW) __builtin_amdgcn_s_setprio(2);
+#endif
   if (w < kNCW) compute_role_b<PAGED>(e, a, w);
   else if (w < kNCW + kNLW) loader_role_b<PAGED>(e, a, w - kNCW);
   else sync_role_b(e, a);

@@ -67,5 +67,46 @@ MK_HD size_t rope_size(int S, int hd) { return (size_t)S * hd; }
 
 MK_HD size_t logits(int V, int b) { return (size_t)b * V; }
 
+// Batched GEMV units (MFMA): the weight stream is a sequence of 1 KB blocks,
+// each 8 rows x 64 elements of one K piece (256 elements).  `nrb` row blocks
+// of 8 rows.  Block L of a unit's stream holds K piece k, 64-wide chunk kb
+// (0..3) of row block rb.  Ordinary units go row block by row block within a
+// piece (a row block's 4 chunks together); wide units (more than 8 tiles of
+// 16 rows: the batched LM head) go chunk by chunk, every row block of chunk
+// kb before chunk kb + 1, so that a compute wave builds the A operands of a
+// chunk once for all its tiles.
+MK_HD bool mfma_wide(uint32_t nrb) { return (nrb + 1) / 2 > 8; }
+MK_HD void mfma_block(uint32_t L, uint32_t nrb, bool wide, uint32_t &k, uint32_t &kb, uint32_t &rb) {
+  if (wide) {
+    rb = L % nrb;
+    const uint32_t rest = L / nrb;
+    kb = rest & 3;
+    k = rest >> 2;
+  } else {
+    kb = L & 3;
+    const uint32_t rbk = L >> 2;
+    rb = rbk % nrb;
+    k = rbk / nrb;
+  }
+}
+MK_HD uint32_t mfma_block_index(uint32_t k, uint32_t kb, uint32_t rb, uint32_t nrb, bool wide) {
+  return wide ? (k * 4 + kb) * nrb + rb : (k * nrb + rb) * 4 + kb;
+}
+
+#ifndef MK_BROT
+#define MK_BROT 1
+#endif
+// K-piece order of a batched GEMV unit: unit u takes its pieces starting at
+// piece u mod nk, so that at any moment the units of one instruction read
+// different activation pieces instead of all reading the same bytes.  The
+// loader (weights) and the sync wave (activations) map a unit's logical
+// piece k to the same physical piece; the compute waves only see logical
+// pieces.
+MK_HD uint32_t mfma_phys_k(uint32_t k, uint32_t nk, uint32_t unit) {
+  if (!MK_BROT) return k;
+  const uint32_t kk = k + unit % nk;
+  return kk >= nk ? kk - nk : kk;
+}
+
 }  // namespace lay
 }  // namespace mk

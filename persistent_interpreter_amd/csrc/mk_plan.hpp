@@ -59,6 +59,10 @@ constexpr int kAttnRegRows = 20;
 constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
 constexpr int kMaxDevices = 64;
 constexpr int kMfmaRows = 64;
+// Batched LM-head units are wider: one per workgroup, each compute wave
+// owning whole 16-row tiles (at most 4 of them), so the final-normed
+// activation is staged once per workgroup.
+constexpr int kMfmaWideRows = 512;
 
 // One queued instruction (96 bytes).  An instruction's weight stream is the
 // sequence of pieces t = 0 .. n_items*ipw*nk - 1 in k-major order:

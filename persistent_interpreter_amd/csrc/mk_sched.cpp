@@ -205,7 +205,12 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
   const uint32_t n_qkv = units_for(TP, 2, (uint32_t)nkv, kAccFloats / 2);
   const uint32_t n_o = units_for(H, 1, 1), n_down = units_for(H, 1, 1);
   const uint32_t n_ffn = units_for(F, 2, (uint32_t)chunks);
-  const uint32_t n_lm = units_for(V, 1, 1);
+  // batched: wide LM units (their results leave from registers, so the LDS
+  // result-slot bound does not apply)
+  const uint32_t n_lm = mfma ? std::min<uint32_t>(std::max<uint32_t>(std::min<uint32_t>((uint32_t)C, V),
+                                                                     (V + kMfmaWideRows - 1) / kMfmaWideRows),
+                                                  V)
+                             : units_for(V, 1, 1);
 
   auto chunk_k0 = [&](int ch) { return (uint32_t)((uint64_t)ch * nk_f / chunks); };
   // first element of chunk ch (F for ch == chunks)
@@ -380,12 +385,14 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
         cu_bytes[cu] += bytes;
         P.weight_bytes += bytes;
         P.n_pages += (int)in.pages;
-        if ((int64_t)in.n_items * in.ipw * B > kAccFloats ||
+        const bool wide = mfma && in.op == OP_LM;
+        if ((!wide && (int64_t)in.n_items * in.ipw * B > kAccFloats) ||
             (in.op == OP_QKV && (int64_t)in.n_items * in.ipw * B > kAccFloats / 2)) {
           err = "internal: too many rows in a unit";
           return MK_ERR_UNSUPPORTED;
         }
-        if (mfma && (in.kc != (uint32_t)kMfmaKc || in.n_items * in.ipw > (uint32_t)kMfmaRows)) {
+        if (mfma && (in.kc != (uint32_t)kMfmaKc ||
+                     in.n_items * in.ipw > (uint32_t)(wide ? kMfmaWideRows : kMfmaRows))) {
           err = "internal: MFMA unit shape";
           return MK_ERR_UNSUPPORTED;
         }

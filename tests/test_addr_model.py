@@ -61,6 +61,17 @@ def test_planted_size_errors_are_found(name, corrupt, site):
     assert f"at {site}+" in msg, msg
 
 
+@pytest.mark.parametrize("batch,cus", [(3, 3), (8, 2), (8, 256)])
+def test_wide_lm_units_in_bounds(batch, cus):
+    """Batched LM-head units of up to 512 rows (tiny shape on 2 and 3
+    workgroups, Llama-1B shape on 256)."""
+    name = "tiny" if cus < 256 else "llama1b_b8"
+    mc = synth.CONFIGS[name].replace(batch=batch, pos_lo=4, pos_hi=40)
+    cfg = B.make_config(mc, max_batch=batch)
+    rc, rep = B.addr_check(cfg, batch, cus, 2, synth.make_positions(mc, batch), synth.make_tokens(mc, batch))
+    assert rc == 0 and rep.violations == 0, rep.msg.decode()
+
+
 def test_bad_arguments():
     mc = synth.CONFIGS["tiny"]
     cfg = B.make_config(mc)

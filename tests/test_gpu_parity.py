@@ -139,14 +139,17 @@ def test_greedy_tokens_identical(name, steps):
     assert np.array_equal(gkv[:, :, :, :, untouched], kv[:, :, :, :, untouched])
 
 
-# (shape, batch, steps, KV splits: 0 = the planner's choice; 1 makes every
-# split long enough for the paged attention body)
-BATCHED = [("tiny", 2, 32, 0), ("tiny", 3, 8, 0), ("tiny", 8, 8, 0), ("tiny", 3, 8, 1),
-           pytest.param("llama1b_b8", 8, 32, 0, marks=pytest.mark.timeout(900))]
+# (shape, batch, steps, KV splits: 0 = the planner's choice, 1 makes every
+# split long enough for the paged attention body; workgroups: 0 = every CU,
+# 2 or 3 give the tiny shape LM-head units of 512 and 342 rows, which the
+# wide LM path runs with 4 and 2-3 tiles per compute wave)
+BATCHED = [("tiny", 2, 32, 0, 0), ("tiny", 3, 8, 0, 0), ("tiny", 8, 8, 0, 0), ("tiny", 3, 8, 1, 0),
+           ("tiny", 3, 8, 0, 3), ("tiny", 8, 4, 0, 2),
+           pytest.param("llama1b_b8", 8, 32, 0, 0, marks=pytest.mark.timeout(900))]
 
 
-@pytest.mark.parametrize("name,batch,steps,splits", BATCHED)
-def test_batched_greedy_matches_oracle(name, batch, steps, splits):
+@pytest.mark.parametrize("name,batch,steps,splits,cus", BATCHED)
+def test_batched_greedy_matches_oracle(name, batch, steps, splits, cus):
     """Several sequences per step in one launch (the batched kernel: MFMA
     projections on bf16 hi + lo activations), each at its own position: the
     logits of every sequence stay within TOL of the oracle's (teacher-forced
@@ -159,8 +162,8 @@ def test_batched_greedy_matches_oracle(name, batch, steps, splits):
     W = synth.make_weights(mc)
     kv = synth.make_kv_cache(mc)
     tok, pos = synth.make_tokens(mc), synth.make_positions(mc)
-    print(f"{name}: batch {batch}, positions {pos.tolist()}", flush=True)
-    sess = harness.Session(mc, W, kv.copy(), batch=batch, kv_splits=splits)
+    print(f"{name}: batch {batch}, positions {pos.tolist()}, workgroups {cus or 'all'}", flush=True)
+    sess = harness.Session(mc, W, kv.copy(), batch=batch, kv_splits=splits, num_cus=cus)
     fed_g, out_g = harness.greedy_run(sess, tok, pos, steps)
     gkv = sess.kv_host()
     sess.close()
