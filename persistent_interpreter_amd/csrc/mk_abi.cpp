@@ -288,6 +288,13 @@ int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out) {
   return MK_OK;
 }
 
+// Attention partials, then the split-K down partials (batched plans).
+static size_t part_bytes(const mk_config &c, const Plan &P) {
+  return (lay::part_size(c.n_layers, c.max_batch, c.n_q_heads, P.n_split, c.head_dim) +
+          (P.down_splits ? lay::dpart_size(c.n_layers, P.down_splits, c.hidden, c.max_batch) : 0)) *
+         4;
+}
+
 static int get_plan(mk_handle *h, int batch, DevPlan **out) {
   auto it = h->plans.find(batch);
   if (it != h->plans.end()) {
@@ -305,15 +312,15 @@ static int get_plan(mk_handle *h, int batch, DevPlan **out) {
   // no plan reaches the device without the validator's static checks
   // (coverage of every read by waits, counter targets, extents)
   if (check_plan(h->cfg, P, 0, 0, 0, nullptr) != MK_OK) return MK_ERR_UNSUPPORTED;
-  // the counter groups, then one padded word: the greedy arrival counter
+  // the counter groups, then one padded word: the greedy arrival counter,
+  // then the arrival counters of the split-K down groups
   dp->amax_word = (size_t)P.n_groups * kSlots * kCtrStride;
-  dp->ctr_bytes = (dp->amax_word + kCtrStride) * 4;
+  dp->ctr_bytes = (dp->amax_word + kCtrStride + (size_t)P.n_down_groups) * 4;
   for (const Instr &in : P.instr) dp->n_lm += in.op == OP_LM ? 1u : 0u;
   // greedy arrivals per step: one per LM unit (batch 1), one per workgroup
   // holding LM units (batched)
   dp->n_arrive = batch > 1 ? (uint32_t)P.n_lm_groups : dp->n_lm;
-  const size_t part =
-      lay::part_size(h->cfg.n_layers, h->cfg.max_batch, h->cfg.n_q_heads, P.n_split, h->cfg.head_dim) * 4;
+  const size_t part = part_bytes(h->cfg, P);
   // page sentinels: iota[i] = i for every page index of the longest queue
   uint32_t max_pages = 0;
   for (int c = 0; c < h->num_cus; ++c) {
@@ -461,10 +468,8 @@ int mk_decode_step_static(mk_handle *h, int32_t batch, const int32_t *tokens, co
   if (it == h->plans.end()) return MK_ERR_NOT_PREPARED;
   DevPlan *dp = it->second.get();
   auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
-  const size_t part_bytes =
-      lay::part_size(h->cfg.n_layers, h->cfg.max_batch, h->cfg.n_q_heads, dp->plan.n_split, h->cfg.head_dim) * 4;
   const size_t amax_bytes = (size_t)dp->n_lm * h->cfg.max_batch * 8;
-  const size_t off_part = up(dp->ctr_bytes), off_amax = off_part + up(part_bytes);
+  const size_t off_part = up(dp->ctr_bytes), off_amax = off_part + up(part_bytes(h->cfg, dp->plan));
   if (off_amax + amax_bytes > kStaticScratchBytes) return MK_ERR_UNSUPPORTED;
   char *base = (char *)h->static_scratch;
   // counters start from zero on every call (the array keeps the previous

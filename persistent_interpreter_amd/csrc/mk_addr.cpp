@@ -214,7 +214,9 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
           M.el(B.status, 0, 4, 4, "sync(b): status poll");
         }
         if (!gv) continue;
-        const uint32_t K = d.rowb >> 1;
+        const bool split = d.op == OP_DOWN && lay::split_n(d.aux1) > 1;
+        const uint32_t koff = split ? lay::split_koff(d.aux0) : 0u;
+        const uint32_t K = split ? lay::split_klen(d.aux0) : d.rowb >> 1;
         uint64_t nw = 0;
         if (normed) {
           uint64_t h, emb;
@@ -231,7 +233,7 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
               }
               uint64_t src, want;
               if (d.op == OP_O) { src = B.attn + lay::attn(MB, nq, hd, d.layer, b) * 4; want = B.attn; }
-              else if (d.op == OP_DOWN) { src = B.a + lay::a(MB, F, d.layer, b) * 4; want = B.a; }
+              else if (d.op == OP_DOWN) { src = B.a + (lay::a(MB, F, d.layer, b) + koff) * 4; want = B.a; }
               else { uint64_t emb, w; norm_src(d, b, src, emb, w); want = B.h; }
               if (e0 < K) M.at(src + (uint64_t)e0 * 4, 16, want, "sync(b): staged activation");
               else M.at(B.zero, 16, B.zero, "sync(b): zero padding");
@@ -262,7 +264,9 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
         continue;
       }
       if (!is_gemv(d.op)) continue;
-      const uint32_t R = d.n_items * d.ipw, nrb = d.ppp, K = d.rowb >> 1;
+      const bool split = d.op == OP_DOWN && lay::split_n(d.aux1) > 1;
+      const uint32_t koff = split ? lay::split_koff(d.aux0) : 0u;
+      const uint32_t R = d.n_items * d.ipw, nrb = d.ppp, K = split ? lay::split_klen(d.aux0) : d.rowb >> 1;
       const uint32_t nblk = (uint32_t)d.nk * nrb * 4;
       const bool wide = lay::mfma_wide(nrb);
       for (uint32_t p = 0; p < d.pages; ++p, ++n) {
@@ -283,8 +287,8 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
             else row = d.w0 + (uint64_t)(d.item0 + r) * d.rowb;
             const uint32_t kk = k * kMfmaKc + kb * 64 + 8 * (uint32_t)(lane >> 3);
             if (kk < K) {
-              M.at(row + (uint64_t)kk * 2, 16, 0, "loader(b): weight block");
-              if (kk + 8 > K) M.at(~0ull, 16, 0, "loader(b): weight block crosses its row");
+              M.at(row + (uint64_t)(koff + kk) * 2, 16, 0, "loader(b): weight block");
+              if (koff + kk + 8 > (d.rowb >> 1)) M.at(~0ull, 16, 0, "loader(b): weight block crosses its row");
             } else {
               M.at(B.zero, 16, B.zero, "loader(b): zero padding");
             }
@@ -397,10 +401,26 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
             }
             case OP_O: M.el(B.h, lay::h(MB, H, 2 * d.layer + 1, b) + d.item0 + i, 4, 4, "epilogue(b): O"); break;
             case OP_FFN: M.el(B.a, lay::a(MB, F, d.layer, b) + d.item0 + i, 4, 4, "epilogue(b): FFN"); break;
-            case OP_DOWN: M.el(B.h, lay::h(MB, H, 2 * d.layer + 2, b) + d.item0 + i, 4, 4, "epilogue(b): down"); break;
+            case OP_DOWN:
+              if (lay::split_n(d.aux1) > 1) {
+                // split-K: this chunk's partial row, then (as the group's
+                // last arrival) every chunk's partial row
+                const int S2 = (int)lay::split_n(d.aux1);
+                M.el(B.part, lay::part_size(L, MB, nq, ns, hd) + lay::dpart(H, MB, S2, d.layer, (int)lay::split_s(d.aux1),
+                                                                            (int)(d.item0 + i), b),
+                     4, 4, "epilogue(b): split partial");
+                for (int s2 = 0; s2 < S2; ++s2)
+                  M.el(B.part, lay::part_size(L, MB, nq, ns, hd) + lay::dpart(H, MB, S2, d.layer, s2, (int)(d.item0 + i), b),
+                       4, 4, "epilogue(b): split partials read");
+              }
+              M.el(B.h, lay::h(MB, H, 2 * d.layer + 2, b) + d.item0 + i, 4, 4, "epilogue(b): down");
+              break;
             default: M.el(B.logits, lay::logits(V, b) + d.item0 + i, 4, 4, "epilogue(b): logits"); break;
           }
         }
+        if (d.op == OP_DOWN && lay::split_n(d.aux1) > 1)
+          M.el(B.ctr, (uint64_t)P.n_groups * kSlots * kCtrStride + kCtrStride + lay::split_group(d.aux1), 4, 4,
+               "epilogue(b): split arrival counter");
         if (d.op == OP_LM && (d.aux1 & 2u)) {
           for (int b = 0; b < batch; ++b)
             M.el(B.amax, (uint64_t)d.aux0 * batch + b, 8, 8, "epilogue(b): workgroup greedy candidate");
@@ -492,11 +512,12 @@ extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cu
   B.kvn = M.add("kvn", lay::kvn_size(L, MB, nkv, hd) * 8);
   B.attn = M.add("attn", lay::attn_size(L, MB, nq, hd) * 4);
   B.a = M.add("a", lay::a_size(L, MB, F) * 4);
-  B.part = M.add("partials", lay::part_size(L, MB, nq, ns, hd) * 4 - short_part);
+  B.part = M.add("partials", (lay::part_size(L, MB, nq, ns, hd) +
+                              (P.down_splits ? lay::dpart_size(L, P.down_splits, H, MB) : 0)) * 4 - short_part);
   B.rope = M.add("rope", lay::rope_size(S, hd) * 4 - short_rope);
   B.status = M.add("status", 256);
   const uint64_t amax_word = (uint64_t)P.n_groups * kSlots * kCtrStride;
-  B.ctr = M.add("counters", (amax_word + kCtrStride) * 4);
+  B.ctr = M.add("counters", (amax_word + kCtrStride + (uint64_t)P.n_down_groups) * 4);
   B.target = M.add("targets", P.grp_target.size() * 4);
   uint32_t n_lm = 0, max_pages = 0;
   for (const Instr &in : P.instr) n_lm += in.op == OP_LM;

@@ -705,10 +705,15 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
       norm_src(e, a, d, b, h, emb, nw);
       stage_norm_weights(0);
     }
+    // Unit qi shares its LDS result slot and its completion counter with
+    // unit qi - kAccSlots, whose epilogue must have finished before this
+    // unit's slot is written (RoPE values, residual rows, below) and before
+    // its ready flag lets the compute waves use either: every compute wave
+    // passes that flag before it touches them.
+    if (qi >= (uint32_t)kAccSlots &&
+        !spin_lds(e, [&]() { return lds_ld(L_EPI) + kAccSlots > qi; }, 0x500 | qi))
+      return;
     if (d.op == OP_QKV) {
-      if (qi >= (uint32_t)kAccSlots &&
-          !spin_lds(e, [&]() { return lds_ld(L_EPI) + kAccSlots > qi; }, 0x500 | qi))
-        return;
       const uint32_t half = (uint32_t)c.hd >> 1, ppg = (uint32_t)(c.G + 2) * half;
       for (uint32_t i = (uint32_t)lane; i < d.n_items; i += 64) {
         const uint32_t ii = ((d.item0 + i) % ppg) % half;
@@ -1646,8 +1651,10 @@ __device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw
           if (lane == 0) lds_st(L_XCONS + 4 * cw, seq + k);
           wake();  // the sync wave may wait for this activation slot
         }
-        if (r0 >= per) continue;
+        if (r0 >= per && k > 0) continue;
+        // (a wave without rows passes the first piece's flag all the same)
         if (!spin_lds(e, [&]() { return lds_ld(L_XREADY) > seq + k; }, 0x400 | qi)) return;
+        if (r0 >= per) continue;
         load_x(reinterpret_cast<const float *>(smem + L_XS + ((seq + k) % kNXS) * kXSlotBytes), n16, xr);
         const uint32_t t = k * per + r0;
         uint32_t pi = t / ppp, o = t - pi * ppp;
@@ -1752,6 +1759,18 @@ __device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ uint32_t phys_k(const Instr &d, uint32_t k) { return lay::mfma_phys_k(k, d.nk, d.unit); }
+// The K window of a batched GEMV unit: a split-K down unit covers one MLP
+// chunk [koff, koff + klen) of its rows, every other unit the whole row.
+__device__ __forceinline__ bool split_down(const Instr &d) { return d.op == OP_DOWN && lay::split_n(d.aux1) > 1; }
+__device__ __forceinline__ void kwin(const Instr &d, uint32_t &koff, uint32_t &klen) {
+  if (split_down(d)) {
+    koff = lay::split_koff(d.aux0);
+    klen = lay::split_klen(d.aux0);
+  } else {
+    koff = 0;
+    klen = d.rowb >> 1;
+  }
+}
 
 // LDS layout of the batched kernel (bytes; control words as above)
 constexpr int LB_AMAX = 192;    // u64[8]  running greedy best per sequence of this workgroup
@@ -1884,7 +1903,9 @@ __device__ __forceinline__ void loader_role_b(const Env &e, const Args &a, int l
       continue;
     }
     if (!is_gemv(d.op)) continue;
-    const uint32_t R = d.n_items * d.ipw, nrb = d.ppp, K = d.rowb >> 1;
+    const uint32_t R = d.n_items * d.ipw, nrb = d.ppp;
+    uint32_t koff, K;
+    kwin(d, koff, K);
     const uint32_t nblk = (uint32_t)d.nk * nrb * 4;
     const bool wide = lay::mfma_wide(nrb);
     uint32_t cur_rb = 0xffffffffu;
@@ -1918,7 +1939,7 @@ __device__ __forceinline__ void loader_role_b(const Env &e, const Args &a, int l
           rowp = row_start(d, a.rowtab, rb, R, lane);
         }
         const uint32_t kk = phys_k(d, k) * kMfmaKc + kb * 64 + 8 * (uint32_t)(lane >> 3);
-        const char *src = kk < K ? rowp + (size_t)kk * 2 : zero;
+        const char *src = kk < K ? rowp + (size_t)(koff + kk) * 2 : zero;
         __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)(slot + j * 1024), 16, 0, kWPol);
       }
       __builtin_amdgcn_global_load_lds(a.iota + n, (LDS_AS void *)(smem + LB_SENT + (n % P) * kSentBytes), 4, 0, 0);
@@ -1972,12 +1993,17 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
     const bool normed = d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM;
     const bool emb_in = d.op == OP_QKV && d.layer == 0;  // bf16 embedding rows
     float *accs = reinterpret_cast<float *>(smem + LB_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4);
+    // Unit qi shares its LDS result slot and its completion counter with
+    // unit qi - kAccSlots, whose epilogue must have finished before this
+    // unit's slot is written (RoPE values, residual rows, 1/rms, below) and
+    // before its ready flags let the compute waves use either: every compute
+    // wave passes such a flag before it touches them.
+    if (qi >= (uint32_t)kAccSlots &&
+        !spin_lds(e, [&]() { return lds_ld(L_EPI) + kAccSlots > qi; }, 0x500 | qi))
+      return;
     if (d.op == OP_QKV) {
       // RoPE cos/sin of each (pair, sequence) at that sequence's position,
-      // staged before the waits (the slot's previous unit must be done)
-      if (qi >= (uint32_t)kAccSlots &&
-          !spin_lds(e, [&]() { return lds_ld(L_EPI) + kAccSlots > qi; }, 0x500 | qi))
-        return;
+      // staged before the waits
       const uint32_t half = (uint32_t)c.hd >> 1, ppg = (uint32_t)(c.G + 2) * half;
       for (uint32_t x = (uint32_t)lane; x < d.n_items * (uint32_t)B; x += 64) {
         const uint32_t i = x / (uint32_t)B, b = x - i * (uint32_t)B;
@@ -2017,7 +2043,8 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
       ++seq;
       continue;
     }
-    const uint32_t K = d.rowb >> 1;
+    uint32_t koff, K;
+    kwin(d, koff, K);
     // The unit's input rows: sequence b's starts at src0 + b * sstr bytes,
     // its residual row (O, DOWN) at res0 + b * rstr.  They are computed once
     // per unit into registers: the compiler treats every direct-to-LDS load
@@ -2031,7 +2058,7 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
       sstr = (uint32_t)(c.nq * c.hd) * 4;
       res0 = reinterpret_cast<const char *>(c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer, 0) + d.item0 + lane);
     } else if (d.op == OP_DOWN) {
-      src0 = reinterpret_cast<const char *>(c.a_buf + lay::a(c.max_batch, c.F, d.layer, 0));
+      src0 = reinterpret_cast<const char *>(c.a_buf + lay::a(c.max_batch, c.F, d.layer, 0) + koff);
       sstr = (uint32_t)c.F * 4;
       res0 = reinterpret_cast<const char *>(c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer + 1, 0) + d.item0 + lane);
     } else {
@@ -2192,16 +2219,46 @@ __device__ __forceinline__ float tile_sum(const float *Pb, uint32_t T, uint32_t 
   return v;
 }
 
-__device__ __forceinline__ void unit_epilogue_b(const Env &e, const Args &a, const Instr &d, const float *accs,
+__device__ __forceinline__ bool unit_epilogue_b(const Env &e, const Args &a, const Instr &d, const float *accs,
                                                 const float *Pb) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
   const uint32_t B = (uint32_t)a.batch;
   const uint32_t T = ((uint32_t)d.ppp + 1) >> 1;
+  if (split_down(d)) {
+    // the chunk's partial rows, acknowledged, then this unit's arrival; the
+    // row group's last arrival sums the chunks in chunk order onto the
+    // residual (the same order whichever unit arrives last) and signals
+    const uint32_t S = lay::split_n(d.aux1), sp = lay::split_s(d.aux1);
+    float *dp0 = a.part_buf + lay::part_size(c.L, c.max_batch, c.nq, a.n_split, c.hd);
+    for (uint32_t x = (uint32_t)lane; x < d.n_items * B; x += 64) {
+      const uint32_t i = x / B, b = x - i * B;
+      st_c(dp0 + lay::dpart(c.H, c.max_batch, (int)S, d.layer, (int)sp, (int)(d.item0 + i), (int)b),
+           tile_sum(Pb, T, i, b));
+    }
+    wait_vm0();
+    before_signal();
+    uint32_t old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(G(a.amax_ctr) + kCtrStride + lay::split_group(d.aux1), 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old + 1u != S * a.epoch) return false;
+    poll_exit();
+    const rsrc_t pr = rsrc(dp0);
+    for (uint32_t x = (uint32_t)lane; x < d.n_items * B; x += 64) {
+      const uint32_t i = x / B, b = x - i * B;
+      float v = accs[b * 64 + i];
+      for (uint32_t s2 = 0; s2 < S; ++s2)
+        v += ldc1(pr, (uint32_t)lay::dpart(c.H, c.max_batch, (int)S, d.layer, (int)s2, (int)(d.item0 + i), (int)b) * 4);
+      st_c(c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer + 2, (int)b) + d.item0 + i, v);
+    }
+    return true;
+  }
   if (T > (uint32_t)kNCW) {
     // a wide LM unit: the waves stored the logits; merge their candidates
     // (in wave order) into the workgroup's running best per sequence
-    if (!a.next_tok) return;
+    if (!a.next_tok) return true;
     uint64_t *run = reinterpret_cast<uint64_t *>(smem + LB_AMAX);
     const uint64_t *cand = reinterpret_cast<const uint64_t *>(Pb);
     if ((uint32_t)lane < B) {
@@ -2229,7 +2286,7 @@ __device__ __forceinline__ void unit_epilogue_b(const Env &e, const Args &a, con
       if (d.aux1 & 2u) st_tag(a.amax + (size_t)d.aux0 * B + lane, bv, bi);
     }
     wait_lgkm0();
-    return;
+    return true;
   }
   // normed units: the sequence's 1/rms (accs[b]); O, DOWN: residual rows
   // accs[b * 64 + row]
@@ -2319,6 +2376,7 @@ __device__ __forceinline__ void unit_epilogue_b(const Env &e, const Args &a, con
     }
     wait_lgkm0();
   }
+  return true;
 }
 
 // The last LM workgroup of the step to count itself picks every sequence's
@@ -2642,8 +2700,9 @@ __device__ __forceinline__ void compute_role_b(const Env &e, const Args &a, int 
     if (old == kNCW - 1) {
       lds_poll_exit();  // every wave's partial tile is in LDS
       if (lane == 0) trace_now(e, qi, 6);
+      bool sig = true;  // (a split-K down unit signals only as its group's last arrival)
       if (gv) {
-        unit_epilogue_b(e, a, d, accs, Pb);
+        sig = unit_epilogue_b(e, a, d, accs, Pb);
         if (d.op != OP_QKV) wait_vm0();
       }
       if (d.op == OP_LM && a.next_tok && (d.aux1 & 2u)) {
@@ -2655,10 +2714,10 @@ __device__ __forceinline__ void compute_role_b(const Env &e, const Args &a, int 
         trace_now(e, qi, 3);
         lds_st(L_DONE + 4 * (qi & 3), 0);
         lds_st(L_EPI, qi + 1);
-        if (d.sig0 >= 0)
+        if (sig && d.sig0 >= 0)
           __hip_atomic_fetch_add(G(a.ctr) + ((size_t)d.sig0 * kSlots + d.slot0) * kCtrStride, 1u, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
-        if (d.sig1 >= 0)
+        if (sig && d.sig1 >= 0)
           __hip_atomic_fetch_add(G(a.ctr) + ((size_t)d.sig1 * kSlots + d.slot1) * kCtrStride, 1u, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
       }

@@ -93,6 +93,22 @@ MK_HD uint32_t mfma_block_index(uint32_t k, uint32_t kb, uint32_t rb, uint32_t n
   return wide ? (k * 4 + kb) * nrb + rb : (k * nrb + rb) * 4 + kb;
 }
 
+// Split-K down-projection units (batched plans): unit (row group, chunk s)
+// multiplies rows of W_down by one MLP chunk of the activation, K elements
+// [koff, koff + klen).  aux0 = koff | klen << 16; aux1 = s | S << 4 |
+// group << 8 with S the number of chunks (S <= 1: an ordinary unit over the
+// whole K) and `group` the global index of its (layer, row group).  Partial
+// results: fp32 [L][S][H][max_batch]; one arrival counter per group.
+MK_HD uint32_t split_n(uint32_t aux1) { return (aux1 >> 4) & 15u; }
+MK_HD uint32_t split_s(uint32_t aux1) { return aux1 & 15u; }
+MK_HD uint32_t split_group(uint32_t aux1) { return aux1 >> 8; }
+MK_HD uint32_t split_koff(uint32_t aux0) { return aux0 & 0xffffu; }
+MK_HD uint32_t split_klen(uint32_t aux0) { return aux0 >> 16; }
+MK_HD size_t dpart(int H, int MB, int S, int l, int s, int r, int b) {
+  return (((size_t)l * S + s) * H + r) * MB + b;
+}
+MK_HD size_t dpart_size(int L, int S, int H, int MB) { return (size_t)L * S * H * MB; }
+
 #ifndef MK_BROT
 #define MK_BROT 1
 #endif

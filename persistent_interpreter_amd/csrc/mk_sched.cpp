@@ -11,6 +11,7 @@
 // chunks by default, the chunked example of section 3.4), and whole-vector
 // edges where a RMSNorm needs every row.
 #include "mk_sched.hpp"
+#include "mk_layout.hpp"
 
 #include <algorithm>
 #include <cstdio>
@@ -62,10 +63,17 @@ struct Builder {
     return P.n_groups++;
   }
 
+  // a split-K unit other than the first of its group: the group signals
+  // once (its last arrival), with the first unit's counter slot
+  static bool split_follower(const Instr &in) {
+    return in.op == OP_DOWN && lay::split_n(in.aux1) > 1 && lay::split_s(in.aux1) > 0;
+  }
+
   void add(Unit u) {
     u.in.sig0 = u.sigs.size() > 0 ? u.sigs[0] : -1;
     u.in.sig1 = u.sigs.size() > 1 ? u.sigs[1] : -1;
-    for (int g : u.sigs) P.grp_producers[g] += 1;
+    if (!split_follower(u.in))
+      for (int g : u.sigs) P.grp_producers[g] += 1;
     units.push_back(std::move(u));
   }
 
@@ -78,12 +86,18 @@ struct Builder {
       P.grp_nslot[g] = std::max(1u, std::min(need, (uint32_t)kSlots));
     }
     std::vector<uint32_t> next(P.n_groups, 0);
-    for (Unit &u : units) {
-      for (int i = 0; i < (int)u.sigs.size() && i < 2; ++i) {
-        const int g = u.sigs[i];
-        const uint32_t slot = next[g]++ % P.grp_nslot[g];
-        P.grp_target[(size_t)g * kSlots + slot] += 1;
-        (i == 0 ? u.in.slot0 : u.in.slot1) = slot;
+    for (size_t ui = 0; ui < units.size(); ++ui) {
+      Unit &u = units[ui];
+      if (split_follower(u.in)) {  // (the group's units are consecutive)
+        u.in.slot0 = units[ui - 1].in.slot0;
+        u.in.slot1 = units[ui - 1].in.slot1;
+      } else {
+        for (int i = 0; i < (int)u.sigs.size() && i < 2; ++i) {
+          const int g = u.sigs[i];
+          const uint32_t slot = next[g]++ % P.grp_nslot[g];
+          P.grp_target[(size_t)g * kSlots + slot] += 1;
+          (i == 0 ? u.in.slot0 : u.in.slot1) = slot;
+        }
       }
       for (Wait &w : u.waits) w.nslot = (uint16_t)P.grp_nslot[w.grp];
     }
@@ -212,6 +226,14 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
                                                   V)
                              : units_for(V, 1, 1);
 
+  // batched: split-K down units, S = chunks per row group, row groups of at
+  // most kMfmaRows rows, about one unit per workgroup
+  const bool down_split = mfma && chunks > 1 && F < 65536;
+  const uint32_t n_rg = down_split ? std::min<uint32_t>((uint32_t)H, std::max<uint32_t>(
+                                         (uint32_t)C / (uint32_t)chunks, ((uint32_t)H + kMfmaRows - 1) / kMfmaRows))
+                                   : 0;
+  P.down_splits = down_split ? chunks : 0;
+  P.n_down_groups = down_split ? (int)(n_rg * (uint32_t)L) : 0;
   auto chunk_k0 = [&](int ch) { return (uint32_t)((uint64_t)ch * nk_f / chunks); };
   // first element of chunk ch (F for ch == chunks)
   auto chunk_e0 = [&](int ch) { return std::min<uint32_t>(chunk_k0(ch) * kc_f, (uint32_t)F); };
@@ -323,6 +345,37 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
       }
       bd.add(std::move(un));
     }
+    // I6, batched plans: split-K over the MLP chunks.  Every workgroup would
+    // otherwise stage the whole activation of all sequences (F x batch fp32)
+    // for a few rows; unit (row group, chunk s) stages chunk s only, waits
+    // for chunk s only, and the last unit of a row group to finish sums the
+    // chunks' partial rows in chunk order, adds the residual and signals.
+    if (down_split) {
+      for (uint32_t rg = 0; rg < n_rg; ++rg) {
+        const uint32_t r0 = part_lo(H, n_rg, rg), r1 = part_lo(H, n_rg, rg + 1);
+        const uint32_t group = (uint32_t)l * n_rg + rg;
+        for (int ch = 0; ch < chunks; ++ch) {
+          const uint32_t e0 = chunk_e0(ch), e1 = chunk_e0(ch + 1);
+          Unit un;
+          un.in = gemv(OP_DOWN, l, r0, r1 - r0, 1, F, kc_f, rg * chunks + (uint32_t)ch, mfma);
+          un.in.nk = (uint16_t)(chunk_k0(ch + 1) - chunk_k0(ch));
+          un.in.pages = (uint32_t)(((uint64_t)un.in.nk * un.in.ppp * 4 + 15) / 16);
+          un.in.aux0 = e0 | ((e1 - e0) << 16);
+          un.in.aux1 = (uint32_t)ch | ((uint32_t)chunks << 4) | (group << 8);
+          un.cu = (int)((rg * chunks + (uint32_t)ch) % C);
+          un.waits.push_back({(uint32_t)g_ffn[ch], 0});
+          for (int b = 0; b < B; ++b) {
+            un.reads.push_back({R_A, (uint16_t)l, (uint32_t)b, e0, e1, 0});
+            un.reads.push_back({R_HMID, (uint16_t)l, (uint32_t)b, r0, r1, 0});
+            un.writes.push_back({R_HOUT, (uint16_t)l, (uint32_t)b, r0, r1, 0});
+          }
+          un.sigs.push_back(g_dn);
+          bd.add(std::move(un));
+        }
+      }
+      g_down = g_dn;
+      continue;
+    }
     // I6: down projection + residual; consumes the MLP chunks in order.
     for (uint32_t u = 0; u < n_down; ++u) {
       uint32_t r0 = part_lo(H, n_down, u), r1 = part_lo(H, n_down, u + 1);
@@ -381,7 +434,10 @@ int build_plan(const mk_config &c, int B, int C, Plan &P, std::string &err) {
       in.wait_n = (uint32_t)un.waits.size();
       for (auto &w : un.waits) P.waits.push_back(w);
       if (in.pages) {
-        int64_t bytes = (int64_t)in.n_items * in.ipw * in.rowb;  // K elements per row (no padding)
+        // K elements per row (no padding; a split unit its K window)
+        const int64_t rowb = in.op == OP_DOWN && lay::split_n(in.aux1) > 1 ? 2 * (int64_t)lay::split_klen(in.aux0)
+                                                                             : (int64_t)in.rowb;
+        int64_t bytes = (int64_t)in.n_items * in.ipw * rowb;
         cu_bytes[cu] += bytes;
         P.weight_bytes += bytes;
         P.n_pages += (int)in.pages;
@@ -530,6 +586,12 @@ int check_plan(const mk_config &cfg, Plan &P, int sim_runs, int corrupt, uint64_
       if (in.b >= (uint32_t)P.batch) fail("instruction sequence out of range");
       if (in.op == OP_ATTN && (in.aux0 >= nkv || in.aux1 >= ns)) fail("attention unit head or split out of range");
       if (in.op == OP_RED && in.aux0 >= nkv) fail("reduction unit head out of range");
+      if (in.op == OP_DOWN && lay::split_n(in.aux1) > 1 &&
+          (lay::split_s(in.aux1) >= lay::split_n(in.aux1) || (int)lay::split_n(in.aux1) != P.down_splits ||
+           lay::split_group(in.aux1) >= (uint32_t)P.n_down_groups ||
+           lay::split_koff(in.aux0) + lay::split_klen(in.aux0) > F || lay::split_klen(in.aux0) == 0 ||
+           (uint32_t)in.nk * kMfmaKc < lay::split_klen(in.aux0)))
+        fail("split-K down unit out of range");
       const uint32_t lim = limit(in.op);
       if (lim && ((uint64_t)in.item0 + in.n_items > lim || in.n_items == 0)) fail("unit rows out of range");
       if (in.tab >= 0 && (size_t)in.tab + (size_t)in.n_items * in.ipw > P.rowtab.size())
@@ -595,6 +657,7 @@ int check_plan(const mk_config &cfg, Plan &P, int sim_runs, int corrupt, uint64_
     std::vector<uint32_t> cnt((size_t)P.n_groups * kSlots, 0);
     for (size_t u = 0; u < NU; ++u) {
       const Instr &in = P.instr[u];
+      if (Builder::split_follower(in)) continue;  // counted with its group's first unit
       if (in.sig0 >= 0) {
         if (in.slot0 >= P.grp_nslot[in.sig0]) fail("signal slot outside its group");
         else cnt[(size_t)in.sig0 * kSlots + in.slot0]++;
@@ -662,11 +725,17 @@ int check_plan(const mk_config &cfg, Plan &P, int sim_runs, int corrupt, uint64_
 
   // Interleavings: each CU runs its queue strictly in order, phase by phase;
   // a phase may start once its waits' groups reached their targets.
+  // split-K units signal through their group: the S-th arrival signals
+  std::vector<int> sgroup(NU, -1);
+  for (size_t u = 0; u < NU; ++u)
+    if (P.instr[u].op == OP_DOWN && lay::split_n(P.instr[u].aux1) > 1)
+      sgroup[u] = (int)lay::split_group(P.instr[u].aux1);
   int runs = 0;
   for (int run = 0; run < sim_runs && errors == 0; ++run, ++runs) {
     int strategy = run % 4;
     int delayed = (int)(rng() % C);
     std::vector<uint32_t> count(P.n_groups, 0);
+    std::vector<uint32_t> arrived(std::max(1, P.n_down_groups), 0);
     std::vector<char> done(NU, 0);
     std::vector<uint32_t> pos(C), ph(C, 0);
     for (int cu = 0; cu < C; ++cu) pos[cu] = P.q_off[cu];
@@ -725,7 +794,8 @@ int check_plan(const mk_config &cfg, Plan &P, int sim_runs, int corrupt, uint64_
       if (++ph[cu] == phases[u].size()) {
         done[u] = 1;
         --remaining;
-        for (int g : sig[u]) count[g]++;
+        if (sgroup[u] < 0 || ++arrived[sgroup[u]] == (uint32_t)P.down_splits)
+          for (int g : sig[u]) count[g]++;
         ph[cu] = 0;
         ++pos[cu];
       }

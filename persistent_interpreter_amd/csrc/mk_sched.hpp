@@ -38,6 +38,8 @@ struct Plan {
   int num_cus = 0, batch = 0, n_split = 0, split_len = 0, mlp_chunks = 0;
   int n_groups = 0;
   int n_lm_groups = 0;              // workgroups holding LM units
+  int down_splits = 0;              // split-K down units per row group (0: none)
+  int n_down_groups = 0;            // (layer, row group) arrival counters
   bool paged_kv = false;            // attention units stream K/V pages
   std::vector<Instr> instr;         // all per-CU queues back to back
   std::vector<uint32_t> q_off;      // [num_cus + 1]
