@@ -96,11 +96,17 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def profile_stem(workload: str) -> str:
+    """Name of a workload's files under profiles/ (shape and batch)."""
+    import re
+    return workload if re.search(r"_b\d+$", workload) else workload + "_b1"
+
+
 def stored_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     summary of this workload (copy-calibrated), or None when that summary is
     missing or was measured on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"mk_interp_{workload}_b1_hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"mk_interp_{profile_stem(workload)}_hbm_traffic.md")
     if not os.path.exists(path):
         return None
     digest, val = None, None
@@ -288,6 +294,11 @@ def main():
         if not np.array_equal(end_tok, want):
             raise RuntimeError(f"in-kernel greedy chain diverged: {end_tok} != {want}")
     kern = np.array([a.elapsed_time(b) * 1e-3 for a, b in ev])   # seconds
+    # the kernel instantiation the plan runs, as rocprofv3 names it
+    from persistent_interpreter_amd import binding as Bnd
+    rc_p, rep_p = Bnd.plan_check(Bnd.make_config(mc, max_batch=mc.batch, kv_splits=splits), mc.batch, 256)
+    kernel_name = ("mk::mk_interp" + ("_b" if mc.batch > 1 else "") +
+                   ("<true>" if rc_p == 0 and rep_p.paged_kv else "<false>"))
 
     stream_gbs = stream_read_gbs(torch, stream)
 
@@ -331,7 +342,7 @@ def main():
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": stored_traffic(args.workload),
-                     "kernel": "mk::mk_interp" if mc.batch == 1 else "mk::mk_interp_b",
+                     "kernel": kernel_name,
                      "launches_per_step": 1,
                      "bytes_per_step": int(bytes_per)},
     }

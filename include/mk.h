@@ -223,6 +223,13 @@ typedef struct mk_plan_report {
                                  unit of this); 0 for batch-1 plans          */
   int32_t sim_runs;           /* interleavings simulated                     */
   int32_t sim_errors;         /* missing dependencies or deadlocks found     */
+  int32_t paged_kv;           /* 1: attention units stream K/V through the
+                                 LDS page ring (the kernel instantiated for
+                                 paged attention runs the step); 0: the
+                                 register-prefetch attention body           */
+  int32_t down_splits;        /* batched plans: MLP chunks each down-
+                                 projection row group is split over (its
+                                 last arrival sums them); 0 = no split      */
   char    msg[256];           /* first error found, if any                   */
 } mk_plan_report;
 
@@ -308,7 +315,8 @@ size_t mk_stream_read_sink_words(void);
 
 /* mk_version -- ABI version of this header (major*100 + minor): 101 adds
  * mk_decode_step_greedy, 102 mk_stream_read, 103 mk_addr_check, the batched
- * (MFMA) kernel and mk_plan_report.mfma_cols_k. */
+ * (MFMA) kernel and mk_plan_report.mfma_cols_k, 104
+ * mk_plan_report.paged_kv and .down_splits. */
 int mk_version(void);
 
 #ifdef __cplusplus

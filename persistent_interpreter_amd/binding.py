@@ -75,6 +75,7 @@ class MkPlanReport(C.Structure):
                 ("weight_bytes", C.c_int64), ("max_cu_bytes", C.c_int64),
                 ("mfma_cols_k", C.c_int64),
                 ("sim_runs", C.c_int32), ("sim_errors", C.c_int32),
+                ("paged_kv", C.c_int32), ("down_splits", C.c_int32),
                 ("msg", C.c_char * 256)]
 
 

@@ -127,7 +127,7 @@ struct mk_handle {
 
 extern "C" {
 
-int mk_version(void) { return 103; }
+int mk_version(void) { return 104; }
 
 const char *mk_strerror(int code) {
   switch (code) {
@@ -174,6 +174,8 @@ int mk_plan_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int32_t 
     rep->max_queue = mq;
     rep->weight_bytes = plan.weight_bytes;
     rep->max_cu_bytes = plan.max_cu_bytes;
+    rep->paged_kv = plan.paged_kv ? 1 : 0;
+    rep->down_splits = plan.down_splits;
     rep->mfma_cols_k = 0;
     if (batch > 1)
       for (const Instr &in : plan.instr)

@@ -1908,6 +1908,8 @@ __device__ __forceinline__ void loader_role_b(const Env &e, const Args &a, int l
     kwin(d, koff, K);
     const uint32_t nblk = (uint32_t)d.nk * nrb * 4;
     const bool wide = lay::mfma_wide(nrb);
+    const uint32_t nk = d.nk, rot = MK_BROT ? d.unit % nk : 0u;  // (the piece rotation of lay::mfma_phys_k)
+    const uint32_t lane_k = 8 * (uint32_t)(lane >> 3);
     uint32_t cur_rb = 0xffffffffu;
     const char *rowp = nullptr;
     for (uint32_t p = 0; p < d.pages; ++p, ++n) {
@@ -1929,18 +1931,35 @@ __device__ __forceinline__ void loader_role_b(const Env &e, const Args &a, int l
         --npend;
       }
       LDS_AS char *slot = (LDS_AS char *)smem + LB_RING + (n % P) * kPageBytes;
+      // the page's first block by division, the rest by stepping (block
+      // order of lay::mfma_block)
+      uint32_t k, kb, rb;
+      lay::mfma_block(p * 16 < nblk ? p * 16 : 0u, nrb, wide, k, kb, rb);
       for (uint32_t j = 0; j < 16; ++j) {
-        uint32_t L = p * 16 + j;
-        if (L >= nblk) L = 0;  // tail of the last page: re-read the first block
-        uint32_t k, kb, rb;
-        lay::mfma_block(L, nrb, wide, k, kb, rb);
+        if (p * 16 + j >= nblk) k = kb = rb = 0;  // tail of the last page: re-read the first block
         if (rb != cur_rb) {
           cur_rb = rb;
           rowp = row_start(d, a.rowtab, rb, R, lane);
         }
-        const uint32_t kk = phys_k(d, k) * kMfmaKc + kb * 64 + 8 * (uint32_t)(lane >> 3);
+        const uint32_t kp = k + rot >= nk ? k + rot - nk : k + rot;
+        const uint32_t kk = kp * kMfmaKc + kb * 64 + lane_k;
         const char *src = kk < K ? rowp + (size_t)(koff + kk) * 2 : zero;
         __builtin_amdgcn_global_load_lds(src, (LDS_AS void *)(slot + j * 1024), 16, 0, kWPol);
+        if (wide) {
+          if (++rb == nrb) {
+            rb = 0;
+            if (++kb == 4) {
+              kb = 0;
+              ++k;
+            }
+          }
+        } else if (++kb == 4) {
+          kb = 0;
+          if (++rb == nrb) {
+            rb = 0;
+            ++k;
+          }
+        }
       }
       __builtin_amdgcn_global_load_lds(a.iota + n, (LDS_AS void *)(smem + LB_SENT + (n % P) * kSentBytes), 4, 0, 0);
       ++npend;

@@ -84,3 +84,66 @@ def perfetto(a: np.ndarray, path: str) -> None:
                    "args": {"unit": int(r["unit"]), "ready": float(r["t_wait"])}})
     with open(path, "w") as f:
         json.dump({"traceEvents": ev}, f)
+
+
+def main(argv=None) -> int:
+    """Run traced greedy steps of a synthetic workload on the GPU and print
+    the last step's per-(layer, instruction) summary and the per-layer
+    critical path:
+
+        python -m persistent_interpreter_amd.trace WORKLOAD [STEPS] [--kv-splits N]
+
+    Columns (microseconds from the step's first event): first/last time a
+    unit's waits were satisfied, median/last completion, and medians of the
+    unit's busy time (compute start to done), of the first activation
+    piece's production and of the epilogue."""
+    import argparse
+    import ctypes
+
+    from . import binding as B, harness, synth
+    ap = argparse.ArgumentParser(prog="python -m persistent_interpreter_amd.trace")
+    ap.add_argument("workload")
+    ap.add_argument("steps", nargs="?", type=int, default=3)
+    ap.add_argument("--kv-splits", type=int, default=0)
+    args = ap.parse_args(argv)
+    import torch
+    mc = synth.CONFIGS[args.workload]
+    W = synth.make_weights(mc, threads=16)
+    kv = synth.make_kv_cache(mc, filled=mc.prior) if mc.batch == 1 else synth.make_kv_cache(mc)
+    tok, pos = synth.make_tokens(mc), synth.make_positions(mc)
+    s = harness.Session(mc, W, kv, batch=mc.batch, flags=B.MK_FLAG_TRACE, kv_splits=args.kv_splits)
+    s.set_inputs(tok, pos)
+    for _ in range(args.steps):
+        if s.step_greedy() != 0:
+            raise RuntimeError("mk_decode_step_greedy failed")
+    torch.cuda.synchronize()
+    if s.mk.sync_status() != 0:
+        raise RuntimeError("device error")
+    ptr, nb = s.mk.buffer(B.MK_BUF_TRACE)
+    raw = np.empty(nb // 8, np.uint64)
+    hip = ctypes.CDLL("libamdhip64.so")
+    if hip.hipMemcpy(ctypes.c_void_p(raw.ctypes.data), ctypes.c_void_p(ptr), ctypes.c_size_t(nb), 2) != 0:
+        raise RuntimeError("hipMemcpy failed")
+    s.close()
+    a = decode(raw)
+    span = float(np.nanmax(a["t_done"]) - np.nanmin(a["t_begin"]))
+    print(f"{args.workload}: last of {args.steps} traced steps, span {span:.1f} us, {len(a)} records")
+    print(f"{'L':>3} {'op':>12} {'units':>5} {'1st_rdy':>8} {'last_rdy':>8} {'med_done':>8} "
+          f"{'last_done':>9} {'busy':>7} {'xprod':>6} {'epi':>6}")
+    for r in summary(a):
+        print(f"{r['layer']:>3} {r['op']:>12} {r['units']:>5} {r['first_ready']:8.1f} {r['last_ready']:8.1f} "
+              f"{r['median_done']:8.1f} {r['last_done']:9.1f} {r['busy_med']:7.2f} {r['xprod_med']:6.2f} "
+              f"{r['epi_med']:6.2f}")
+    spans = []
+    for layer in range(mc.n_layers):
+        m = a["layer"] == layer
+        q = m & (a["op"] == 1)
+        spans.append(float(np.nanmax(a["t_done"][m]) - np.nanmin(a["t_wait"][q])))
+    print(f"per-layer span (first QKV wait to last unit done), us: median {np.median(spans):.1f} "
+          f"min {np.min(spans):.1f} max {np.max(spans):.1f}")
+    return 0
+
+
+if __name__ == "__main__":
+    import sys
+    sys.exit(main())

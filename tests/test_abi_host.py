@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert B.lib().mk_version() == 103
+    assert B.lib().mk_version() == 104
     for code in (0, -1, -2, -3, -4, -5, -6, -10, -11, -12, -99):
         assert len(B.strerror(code)) > 0
 
@@ -156,6 +156,19 @@ def test_unsupported_shapes_refused_before_the_device(name, over):
     out = C.c_void_p()
     assert B.lib().mk_create(C.byref(cfg), C.byref(w), C.byref(out)) == B.MK_ERR_UNSUPPORTED
     assert not out.value
+
+
+@pytest.mark.parametrize("name,batch,paged,splits", [("llama1b", 1, 0, 0), ("qwen3_8b", 1, 1, 0),
+                                                    ("llama1b_b8", 8, 1, 4), ("tiny", 3, 0, 3)])
+def test_plan_report_kernel_choice(name, batch, paged, splits):
+    """The report names the attention body (paged K/V or register prefetch)
+    and the split-K down projection of batched plans (one split per MLP
+    chunk: 4 for Llama-1B, 3 for the tiny shape whose FFN has 3 pieces)."""
+    mc = synth.CONFIGS[name]
+    cfg = B.make_config(mc, max_batch=batch)
+    rc, rep = B.plan_check(cfg, batch, 256)
+    assert rc == B.MK_OK, rep.msg
+    assert rep.paged_kv == paged and rep.down_splits == splits
 
 
 @pytest.mark.parametrize("name", ["tiny_qk", "qwen3_8b", "llama70b"])
