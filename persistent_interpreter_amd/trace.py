@@ -55,6 +55,11 @@ def decode(raw: np.ndarray) -> np.ndarray:
     return a
 
 
+def _nanmed(x: np.ndarray) -> float:
+    x = x[~np.isnan(x)]
+    return float(np.median(x)) if len(x) else float("nan")
+
+
 def summary(a: np.ndarray) -> List[Dict]:
     """Per (layer, op): earliest wait-satisfied, median and latest finish
     across workgroups, in microseconds."""
@@ -69,8 +74,8 @@ def summary(a: np.ndarray) -> List[Dict]:
                      "median_done": float(np.median(r["t_done"])),
                      "last_done": float(r["t_done"].max()),
                      "busy_med": float(np.median(r["t_done"] - r["t_start"])),
-                     "xprod_med": float(np.nanmedian(r["t_xready"] - r["t_wait"])),
-                     "epi_med": float(np.nanmedian(r["t_done"] - r["t_epi"]))})
+                     "xprod_med": _nanmed(r["t_xready"] - r["t_wait"]),
+                     "epi_med": _nanmed(r["t_done"] - r["t_epi"])})
     return rows
 
 
