@@ -105,9 +105,13 @@ typedef struct mk_handle mk_handle;
 
 /* mk_create -- validate the configuration, query the device, allocate the
  * library's scratch (counters, activations, partials, RoPE table).  The
- * instruction schedule (chapter 3, section 3.2: queues are planned on the
- * host before launch) of a batch size is built at its first step and passes
- * the static checks of mk_plan_check before it is uploaded.
+ * instruction schedule (chapter "L'interpréteur sur GPU", section 3.2:
+ * queues are planned on the host before launch) of a batch size is built at
+ * its first step and passes the static checks of mk_plan_check before it is
+ * uploaded.  The scratch holds what that interpreter needs beside the
+ * weights: counters in global memory zeroed before use (section 3.4) and
+ * the activations that cross workgroups; the LDS page ring of section 3.3
+ * lives in each launch and needs no allocation.
  *   cfg, w  : host pointers, read during the call only.  The weight device
  *             pointers inside must stay valid and unmodified until
  *             mk_destroy; the library reads them in place and never copies,
@@ -115,16 +119,21 @@ typedef struct mk_handle mk_handle;
  *   out     : receives the handle (NULL on error).
  * Errors: MK_ERR_INVALID_ARG, MK_ERR_UNSUPPORTED, MK_ERR_NO_DEVICE,
  *         MK_ERR_OOM, MK_ERR_HIP, MK_ERR_NOT_CORESIDENT.  MK_ERR_UNSUPPORTED
- *         also for qk_norm = 1 and for head_dim 128: those attention paths
- *         are compiled but switched off (a multi-step run of them faulted
- *         the GPU, cause not yet found); mk_plan_check still accepts them. */
+ *         for shapes the kernels cannot run, refused before any device call:
+ *         head_dim other than 64 or 128, query heads per KV head not
+ *         dividing 8, qk_norm without head_dim 128, hidden or ffn_dim not a
+ *         multiple of 8, kv_splits above 64. */
 int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out);
 
 /* mk_decode_step -- one decode step for sequences b < batch on `stream`
- * (asynchronous; the call returns after enqueueing).  Each sequence is one
- * launch of the persistent kernel running the whole forward pass, the
- * launches back to back on the stream (a batch of B streams the weights B
- * times; sequences share no work yet).
+ * (asynchronous; the call returns after enqueueing): exactly one launch of
+ * the persistent kernel, which runs the whole forward pass of every
+ * sequence (the one-kernel definition on the index page of part 8, "Les
+ * megakernels"; the seven instructions of chapter "L'interpréteur sur GPU",
+ * section 3.2, with cross-workgroup dependencies through the counters of
+ * section 3.4).  One sequence runs the vector-unit kernel; 2 to 8 run the
+ * batched kernel (matrix-core products over the sequences; each weight is
+ * read once per step for the whole batch).
  *   tokens    : device int32 [batch], the token fed at this step.
  *   positions : device int32 [batch], the KV slot of that token; slots
  *               0..positions[b]-1 must already hold the sequence's K/V.
@@ -138,7 +147,8 @@ int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out);
  * The handle is not thread-safe.  Device-side errors (watchdog, bad token or
  * position) are reported by mk_sync_status after the stream is synchronised.
  * Errors returned here: MK_ERR_INVALID_ARG (null pointer, batch outside
- * [1, max_batch]), MK_ERR_HIP, MK_ERR_OOM. */
+ * [1, max_batch]), MK_ERR_UNSUPPORTED (batch above 8; qk_norm with batch
+ * above 1), MK_ERR_HIP, MK_ERR_OOM. */
 int mk_decode_step(mk_handle *h, int32_t batch, const int32_t *tokens,
                    const int32_t *positions, void *kv_cache, float *logits,
                    void *stream);
@@ -168,9 +178,9 @@ int mk_decode_step_greedy(mk_handle *h, int32_t batch, const int32_t *tokens,
 /* mk_decode_step_static -- mk_decode_step_greedy for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation.  It calls no hipMalloc, hipFree
- * or allocating library routine: the step's scratch (its counter groups and
- * greedy arrival counter, the attention partials and the greedy candidates)
- * is a static array of the library, one per GPU, of 32 MiB, held until the
+ * or allocating library routine: the step's scratch (its counter groups,
+ * the greedy and split-K arrival counters, the attention and split-K
+ * partials and the greedy candidates) is a static array of the library, one per GPU, of 32 MiB, held until the
  * process ends, and the schedule of `batch` must already exist (built by an
  * earlier mk_decode_step or mk_decode_step_greedy call of this handle with
  * the same batch size).  Each call first clears the counters with a small
@@ -192,14 +202,24 @@ int mk_decode_step_static(mk_handle *h, int32_t batch, const int32_t *tokens,
                           int32_t *next_positions, void *stream);
 
 /* mk_sync_status -- synchronise the device and return the first device-side
- * error of the steps since the last call (MK_OK if none).  After an error
- * the library re-zeroes its counters so the next step starts clean; a
- * decode step is idempotent (it rewrites slot p and the logits), so the
- * caller may simply run it again. */
+ * error of the steps since the last call (MK_OK if none): a wait that
+ * outlived the watchdog (MK_ERR_DEVICE_TIMEOUT; a missing or late
+ * dependency in a megakernel shows up as a hang or a rare wrong token, not
+ * as a clean failure: chapter "Quand ne pas le faire", section 9.3, the
+ * debugging cost), a token outside the vocabulary (MK_ERR_BAD_TOKEN) or a
+ * position outside the cache (MK_ERR_BAD_POSITION); the step that found it
+ * writes nothing further.  After an error the library re-zeroes its
+ * counters (section 3.4 of "L'interpréteur sur GPU": counters start from
+ * zero) so the next step starts clean; a decode step is idempotent (it
+ * rewrites slot p and the logits), so the caller may simply run it again. */
 int mk_sync_status(mk_handle *h);
 
-/* mk_destroy -- free everything mk_create allocated.  NULL-safe.  The
- * caller must have synchronised any stream the handle was used on. */
+/* mk_destroy -- free everything mk_create and the steps allocated: the
+ * schedules of every batch size used (the host-planned queues of chapter
+ * "L'interpréteur sur GPU", section 3.2), their counters (section 3.4) and
+ * the activation scratch.  The caller's weights, cache and outputs are not
+ * touched.  NULL-safe.  The caller must have synchronised any stream the
+ * handle was used on (the library does not wait for steps in flight). */
 void mk_destroy(mk_handle *h);
 
 /* mk_strerror -- static text for a status code (never NULL). */
