@@ -6,10 +6,12 @@ head_dim 64, SwiGLU 8192, vocab 128256, tied embeddings, RoPE theta 5e5) at
 batch 1 with 512 prior KV positions, greedy decoding.  Weights and the KV
 cache are seeded synthetic bf16 tensors (persistent_interpreter_amd.synth).
 
-A step is one ``mk_decode_step_greedy`` launch: the whole forward pass and
-the greedy next token and position in one persistent kernel, which writes
-them over its own token and position buffers, so the timed steps chain on
-the device with no other kernel or host round trip in between.  ``value``
+A step is the whole forward pass and the greedy next token and position,
+computed by the persistent kernel, which writes them over its own token and
+position buffers, so the timed steps chain on the device with no other
+kernel or host round trip in between: one ``mk_decode_step_greedy`` launch
+per step, or (``--steps-per-launch N``, the batch-8 default N = 8) one
+``mk_decode_steps_greedy`` launch per N chained steps.  ``value``
 is tokens/s over the K timed steps
 (inputs resident in HBM).  ``roofline`` prices the megakernel against
 MI355X's 8 TB/s: algorithmic bytes per launch (every weight byte once, the
@@ -51,6 +53,10 @@ H100_STEP_S = 1.0e-3   # the pages' ~1 ms Llama-1B batch-1 forward on H100
 # attention splits per (sequence, KV head) of each workload (0: the planner's
 # choice)
 DEFAULT_SPLITS = {}
+# greedy steps per launch of each workload (measured: several steps per
+# launch save about 70 us a step at batch 8 and cost about 14 us at batch 1,
+# where the step hand-over inside the launch is slower than a new launch)
+DEFAULT_SPL = {"llama1b_b8": 8}
 
 
 def overhead(t_real: float, t_min: float) -> float:
@@ -227,6 +233,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
     ap.add_argument("--kv-splits", type=int, default=-1,
                     help="attention splits per (sequence, KV head); -1: the workload's default")
+    ap.add_argument("--steps-per-launch", type=int, default=0,
+                    help="greedy steps per launch (mk_decode_steps_greedy); must divide --steps; "
+                         "0: the workload's default")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (for "
                          "scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -250,7 +259,14 @@ def main():
 
     from persistent_interpreter_amd import harness, synth
     mc = synth.CONFIGS[args.workload]
-    K, Wu = args.steps, args.warmup
+    K, Wu, spl = args.steps, args.warmup, args.steps_per_launch
+    if spl == 0:
+        spl = DEFAULT_SPL.get(args.workload, 1)
+        while K % spl:
+            spl //= 2
+    if spl < 1 or K % spl:
+        print("--steps-per-launch must be positive and divide --steps", file=sys.stderr)
+        sys.exit(2)
     mc = mc.replace(steps=max(K, 32))
     W = synth.make_weights(mc, threads=16)
     kv0 = synth.make_kv_cache(mc, filled=mc.prior)
@@ -267,20 +283,25 @@ def main():
     sess.set_inputs(tok, pos)
     for _ in range(Wu):
         sess.step_checked()
+    n_launch = K // spl
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    start_pos = torch.as_tensor(np.asarray(pos, np.int32)).cuda()
+          for _ in range(n_launch)]
+    lg_multi = torch.empty(spl, mc.batch, mc.vocab, dtype=torch.float32, device="cuda") \
+        if spl > 1 else None
     sess.set_inputs(tok, pos)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        if i and i % mc.steps == 0:
-            sess.positions.copy_(start_pos)
+    # K <= mc.steps: the cache has a slot for every timed step
+    for i in range(n_launch):
         ev[i][0].record(stream)
-        rc = sess.step_greedy()
+        if spl == 1:
+            rc = sess.step_greedy()
+        else:
+            rc = sess.mk.decode_steps_greedy(mc.batch, spl, sess.tokens, sess.positions, sess.kv,
+                                             lg_multi, sess.tokens, sess.positions)
         ev[i][1].record(stream)
         if rc != 0:
-            raise RuntimeError(f"mk_decode_step_greedy failed: {rc}")
+            raise RuntimeError(f"decode launch failed: {rc}")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     st = sess.mk.sync_status()
@@ -293,16 +314,17 @@ def main():
         want = np.argmax(gpu_logits[K - 1], axis=-1)
         if not np.array_equal(end_tok, want):
             raise RuntimeError(f"in-kernel greedy chain diverged: {end_tok} != {want}")
-    kern = np.array([a.elapsed_time(b) * 1e-3 for a, b in ev])   # seconds
+    kern = np.array([a.elapsed_time(b) * 1e-3 for a, b in ev]) / spl   # seconds per step
     # the kernel instantiation the plan runs, as rocprofv3 names it
     from persistent_interpreter_amd import binding as Bnd
     rc_p, rep_p = Bnd.plan_check(Bnd.make_config(mc, max_batch=mc.batch, kv_splits=splits), mc.batch, 256)
     kernel_name = ("mk::mk_interp" + ("_b" if mc.batch > 1 else "") +
+                   (("n" if mc.batch > 1 else "_n") if spl > 1 else "") +
                    ("<true>" if rc_p == 0 and rep_p.paged_kv else "<false>"))
 
     stream_gbs = stream_read_gbs(torch, stream)
 
-    positions = [np.asarray(pos) + (i % mc.steps) for i in range(K)]
+    positions = [np.asarray(pos) + i for i in range(K)]
     bytes_per = float(np.mean([algorithmic_bytes(mc, p) for p in positions]))
     t_kern = float(np.mean(kern))
     achieved = bytes_per / t_kern / 1e9
@@ -328,7 +350,8 @@ def main():
                                f"{prior} prior KV positions, greedy (in-kernel argmax)",
                    "batch": mc.batch, "prior_positions": prior, "accumulate": "fp32",
                    "kv_splits": sess.mk.plan_splits(mc.batch),
-                   "parallelism": "1 GPU, 1 persistent launch per step"},
+                   "parallelism": "1 GPU, 1 persistent launch per step" if spl == 1 else
+                                  f"1 GPU, 1 persistent launch per {spl} steps"},
         "kernel_us": {"mean": round(t_kern * 1e6, 2),
                       "median": round(float(np.median(kern)) * 1e6, 2),
                       "p10": round(float(np.percentile(kern, 10)) * 1e6, 2),
@@ -343,7 +366,8 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": stored_traffic(args.workload),
                      "kernel": kernel_name,
-                     "launches_per_step": 1,
+                     "launches_per_step": 1.0 / spl,
+                     "launch_us": round(t_kern * spl * 1e6, 2),
                      "bytes_per_step": int(bytes_per)},
     }
     if mc.batch > 1:

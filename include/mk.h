@@ -175,6 +175,41 @@ int mk_decode_step_greedy(mk_handle *h, int32_t batch, const int32_t *tokens,
                           float *logits, int32_t *next_tokens,
                           int32_t *next_positions, void *stream);
 
+/* mk_decode_steps_greedy -- n_steps greedy decode steps in ONE launch:
+ * step s + 1 feeds the token step s chose, at the next position, so the
+ * host sees neither the steps' tokens nor a kernel boundary between them.
+ * The pages count what each kernel launch costs (chapter "L'interpréteur
+ * sur GPU", section 3.1) and replace the boundaries between kernels by
+ * counters (section 3.4); doing the same across decode steps is not
+ * described there and is taken as the plainest extension of the in-launch
+ * greedy token: the step's last LM unit writes the tokens and counts the
+ * step on a device counter, and the next step's workgroups start once it
+ * has.
+ * The results equal those of n_steps chained mk_decode_step_greedy calls
+ * bit for bit.
+ *   n_steps        : 1 .. 65536.
+ *   tokens         : device int32 [batch], the tokens of the first step.
+ *   positions      : device int32 [batch], the first step's KV slots; step s
+ *                    writes slot positions[b] + s of every layer, so
+ *                    positions[b] + n_steps must not exceed max_seq.
+ *   logits         : device fp32 [n_steps][batch][vocab], step s in row
+ *                    block s, fully written.
+ *   next_tokens    : device int32 [batch]: written by every step (the tokens
+ *                    the next step reads), the last step's on return.  May
+ *                    be the same buffer as tokens.
+ *   next_positions : device int32 [batch]: positions[b] + n_steps, written by
+ *                    the last step only.  May be the same buffer as
+ *                    positions.
+ * Errors: as mk_decode_step_greedy, and MK_ERR_INVALID_ARG for n_steps
+ * outside [1, 65536].  A device error in step s (bad position, watchdog)
+ * ends the launch at that step; mk_sync_status reports it and the outputs
+ * of steps s and later are unspecified.  With MK_FLAG_TRACE the trace
+ * buffer holds the launch's last step. */
+int mk_decode_steps_greedy(mk_handle *h, int32_t batch, int32_t n_steps,
+                           const int32_t *tokens, const int32_t *positions,
+                           void *kv_cache, float *logits, int32_t *next_tokens,
+                           int32_t *next_positions, void *stream);
+
 /* mk_decode_step_static -- mk_decode_step_greedy for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation.  It calls no hipMalloc, hipFree
@@ -336,7 +371,7 @@ size_t mk_stream_read_sink_words(void);
 /* mk_version -- ABI version of this header (major*100 + minor): 101 adds
  * mk_decode_step_greedy, 102 mk_stream_read, 103 mk_addr_check, the batched
  * (MFMA) kernel and mk_plan_report.mfma_cols_k, 104
- * mk_plan_report.paged_kv and .down_splits. */
+ * mk_plan_report.paged_kv and .down_splits, 105 mk_decode_steps_greedy. */
 int mk_version(void);
 
 #ifdef __cplusplus

@@ -41,7 +41,7 @@ EXPORTED = ("mk_create", "mk_decode_step", "mk_decode_step_greedy",
             "mk_sync_status", "mk_destroy", "mk_strerror", "mk_plan_check",
             "mk_get_buffer", "mk_version", "mk_stream_read",
             "mk_stream_read_sink_words", "mk_addr_check",
-            "mk_decode_step_static")
+            "mk_decode_step_static", "mk_decode_steps_greedy")
 
 
 class MkConfig(C.Structure):
@@ -107,6 +107,11 @@ def lib():
                                             C.c_void_p, C.c_void_p, C.c_void_p,
                                             C.c_void_p, C.c_void_p, C.c_void_p]
         L.mk_decode_step_greedy.restype = C.c_int
+        L.mk_decode_steps_greedy.argtypes = [C.c_void_p, C.c_int32, C.c_int32,
+                                             C.c_void_p, C.c_void_p, C.c_void_p,
+                                             C.c_void_p, C.c_void_p, C.c_void_p,
+                                             C.c_void_p]
+        L.mk_decode_steps_greedy.restype = C.c_int
         L.mk_decode_step_static.argtypes = [C.c_void_p, C.c_int32, C.c_void_p,
                                             C.c_void_p, C.c_void_p, C.c_void_p,
                                             C.c_void_p, C.c_void_p, C.c_void_p]
@@ -241,6 +246,18 @@ class Megakernel:
         return lib().mk_decode_step_greedy(self.h, batch, _ptr(tokens), _ptr(positions),
                                            _ptr(kv), _ptr(logits), _ptr(next_tokens),
                                            _ptr(next_positions), stream)
+
+    def decode_steps_greedy(self, batch: int, n_steps: int, tokens, positions, kv,
+                            logits, next_tokens, next_positions,
+                            stream: Optional[int] = None) -> int:
+        """Enqueue n_steps chained greedy decode steps in one launch; logits
+        is fp32 [n_steps][batch][vocab]; returns the synchronous status."""
+        if stream is None:
+            import torch
+            stream = torch.cuda.current_stream().cuda_stream
+        return lib().mk_decode_steps_greedy(self.h, batch, n_steps, _ptr(tokens),
+                                            _ptr(positions), _ptr(kv), _ptr(logits),
+                                            _ptr(next_tokens), _ptr(next_positions), stream)
 
     def decode_step_static(self, batch: int, tokens, positions, kv, logits,
                            next_tokens=None, next_positions=None,

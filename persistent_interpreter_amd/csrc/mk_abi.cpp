@@ -127,7 +127,7 @@ struct mk_handle {
 
 extern "C" {
 
-int mk_version(void) { return 104; }
+int mk_version(void) { return 105; }
 
 const char *mk_strerror(int code) {
   switch (code) {
@@ -391,9 +391,11 @@ struct StepScratch {
   uint32_t epoch, greedy_epoch;
 };
 
+// sc.epoch and sc.greedy_epoch are the counts of the launch's first step;
+// a launch of n_steps steps runs epochs sc.epoch .. sc.epoch + n_steps - 1.
 static int launch_with(mk_handle *h, DevPlan *dp, int32_t batch, const int32_t *tokens, const int32_t *positions,
                        void *kv_cache, float *logits, int32_t *next_tokens, int32_t *next_positions,
-                       const StepScratch &sc, void *stream) {
+                       const StepScratch &sc, uint32_t n_steps, void *stream) {
   Args a;
   a.ctx = h->d_ctx;
   a.instr = dp->d_instr;
@@ -412,8 +414,12 @@ static int launch_with(mk_handle *h, DevPlan *dp, int32_t batch, const int32_t *
   a.trace_stride = dp->trace_stride;
   h->last_plan = dp;
   a.epoch = sc.epoch;
-  h->tag = h->tag + 1 == 0 ? 1 : h->tag + 1;
-  a.tag = h->tag;
+  // one activation tag per step, never 0: the launch takes the next n_steps
+  // values, starting again from 1 where they would wrap
+  uint32_t t0 = h->tag + 1;
+  if (t0 == 0 || (uint64_t)t0 + n_steps - 1 > 0xffffffffull) t0 = 1;
+  a.tag = t0;
+  h->tag = t0 + n_steps - 1;
   a.batch = batch;
   a.n_split = dp->plan.n_split;
   a.split_len = dp->plan.split_len;
@@ -423,6 +429,9 @@ static int launch_with(mk_handle *h, DevPlan *dp, int32_t batch, const int32_t *
   a.next_pos = next_positions;
   a.n_lm = dp->n_arrive;
   a.amax_target = next_tokens ? sc.greedy_epoch * dp->n_arrive : 0;
+  a.n_steps = n_steps;
+  a.tok_base = next_tokens ? sc.greedy_epoch - 1 : 0;  // greedy steps before this launch
+  a.step_off = 0;
   if (kernel_launch(a, h->num_cus, (h->cfg.flags & MK_FLAG_COOPERATIVE) != 0, dp->plan.paged_kv,
                     (hipStream_t)stream) != hipSuccess)
     return MK_ERR_HIP;
@@ -431,31 +440,43 @@ static int launch_with(mk_handle *h, DevPlan *dp, int32_t batch, const int32_t *
 
 static int launch_step(mk_handle *h, int32_t batch, const int32_t *tokens, const int32_t *positions,
                        void *kv_cache, float *logits, int32_t *next_tokens, int32_t *next_positions,
-                       void *stream) {
+                       uint32_t n_steps, void *stream) {
   if (!h || !tokens || !positions || !kv_cache || !logits) return MK_ERR_INVALID_ARG;
   if (batch < 1 || batch > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
+  if (n_steps < 1 || n_steps > (uint32_t)kMaxStepsPerLaunch || (n_steps > 1 && !next_tokens))
+    return MK_ERR_INVALID_ARG;
   // One launch for the whole batch: the batch-1 kernel (GEMV on the vector
   // units) or, for 2..8 sequences, the batched kernel (MFMA), each running
   // its batch size's plan.
   DevPlan *dp = nullptr;
   int rc = get_plan(h, batch, &dp);
   if (rc) return rc;
-  dp->epoch += 1;
-  if (next_tokens) dp->greedy_epoch += 1;
-  const StepScratch sc{dp->d_ctr, dp->d_part, dp->d_amax, dp->epoch, dp->greedy_epoch};
-  return launch_with(h, dp, batch, tokens, positions, kv_cache, logits, next_tokens, next_positions, sc, stream);
+  const uint32_t e0 = dp->epoch + 1, g0 = dp->greedy_epoch + 1;
+  dp->epoch += n_steps;
+  if (next_tokens) dp->greedy_epoch += n_steps;
+  const StepScratch sc{dp->d_ctr, dp->d_part, dp->d_amax, e0, g0};
+  return launch_with(h, dp, batch, tokens, positions, kv_cache, logits, next_tokens, next_positions, sc, n_steps,
+                     stream);
 }
 
 int mk_decode_step(mk_handle *h, int32_t batch, const int32_t *tokens, const int32_t *positions, void *kv_cache,
                    float *logits, void *stream) {
-  return launch_step(h, batch, tokens, positions, kv_cache, logits, nullptr, nullptr, stream);
+  return launch_step(h, batch, tokens, positions, kv_cache, logits, nullptr, nullptr, 1, stream);
 }
 
 int mk_decode_step_greedy(mk_handle *h, int32_t batch, const int32_t *tokens, const int32_t *positions,
                           void *kv_cache, float *logits, int32_t *next_tokens, int32_t *next_positions,
                           void *stream) {
   if (!next_tokens || !next_positions) return MK_ERR_INVALID_ARG;
-  return launch_step(h, batch, tokens, positions, kv_cache, logits, next_tokens, next_positions, stream);
+  return launch_step(h, batch, tokens, positions, kv_cache, logits, next_tokens, next_positions, 1, stream);
+}
+
+int mk_decode_steps_greedy(mk_handle *h, int32_t batch, int32_t n_steps, const int32_t *tokens,
+                           const int32_t *positions, void *kv_cache, float *logits, int32_t *next_tokens,
+                           int32_t *next_positions, void *stream) {
+  if (!next_tokens || !next_positions || n_steps < 1) return MK_ERR_INVALID_ARG;
+  return launch_step(h, batch, tokens, positions, kv_cache, logits, next_tokens, next_positions,
+                     (uint32_t)n_steps, stream);
 }
 
 int mk_decode_step_static(mk_handle *h, int32_t batch, const int32_t *tokens, const int32_t *positions,
@@ -479,7 +500,7 @@ int mk_decode_step_static(mk_handle *h, int32_t batch, const int32_t *tokens, co
   // captured into a graph
   if (fill_zero(base, dp->ctr_bytes / 4, (hipStream_t)stream) != hipSuccess) return MK_ERR_HIP;
   const StepScratch sc{(uint32_t *)base, (float *)(base + off_part), (uint64_t *)(base + off_amax), 1u, 1u};
-  return launch_with(h, dp, batch, tokens, positions, kv_cache, logits, next_tokens, next_positions, sc, stream);
+  return launch_with(h, dp, batch, tokens, positions, kv_cache, logits, next_tokens, next_positions, sc, 1, stream);
 }
 
 int mk_sync_status(mk_handle *h) {

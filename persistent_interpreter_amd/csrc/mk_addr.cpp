@@ -425,6 +425,7 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
           for (int b = 0; b < batch; ++b)
             M.el(B.amax, (uint64_t)d.aux0 * batch + b, 8, 8, "epilogue(b): workgroup greedy candidate");
           M.el(B.ctr, (uint64_t)P.n_groups * kSlots * kCtrStride, 4, 4, "greedy(b): arrival counter");
+          M.el(B.ctr, (uint64_t)P.n_groups * kSlots * kCtrStride + kTokWord, 4, 4, "greedy(b): token counter");
           for (int u = 0; u < P.n_lm_groups; ++u)
             for (int b = 0; b < batch; ++b) M.el(B.amax, (uint64_t)u * batch + b, 8, 8, "greedy(b): candidates");
           for (int b = 0; b < batch; ++b) {
@@ -846,6 +847,7 @@ extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cu
           if (d.op == OP_LM) {
             M.el(B.amax, d.unit, 8, 8, "epilogue: greedy candidate");
             M.el(B.ctr, amax_word, 4, 4, "greedy: arrival counter");
+            M.el(B.ctr, amax_word + kTokWord, 4, 4, "greedy: token counter");
             for (uint32_t u = 0; u < n_lm; ++u) M.el(B.amax, u, 8, 8, "greedy: candidates");
             M.el(B.next_tok, 0, 4, 4, "greedy: next token");
             M.el(B.next_pos, 0, 4, 4, "greedy: next position");

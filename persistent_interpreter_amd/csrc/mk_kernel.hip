@@ -66,6 +66,19 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Step s of a launch (step_off = s) runs with the launch's epoch, tag and
+// greedy target moved on by s, and writes logits row block s.  Only
+// step_off changes between steps: every other argument stays the launch's
+// own, which the compiler may re-load instead of keeping in registers.
+__device__ __forceinline__ uint32_t step_tag(const Args &a) { return a.tag + (uint32_t)a.step_off; }
+__device__ __forceinline__ uint32_t step_epoch(const Args &a) { return a.epoch + (uint32_t)a.step_off; }
+__device__ __forceinline__ uint32_t step_amax_target(const Args &a) {
+  return a.amax_target + (uint32_t)a.step_off * a.n_lm;
+}
+__device__ __forceinline__ float *step_logits(const Args &a) {
+  return a.logits + (size_t)a.step_off * (size_t)a.batch * (size_t)a.ctx->V;
+}
+
 // --------------------------------------------------------------------------
 // device-coherent accesses (relaxed agent-scope atomics -> sc1)
 __device__ __forceinline__ float ld_c(const float *p) {
@@ -254,7 +267,7 @@ struct Env {
   const Instr *q;    // this workgroup's queue
   uint32_t nq;       // its length
   int cu;
-  int pos0;          // positions[0], read once at kernel start (batch 1)
+  int pos0;          // batch 1: this step's position (positions[0] + step_off)
   int flags;         // MK_FLAG_* of the handle
 };
 
@@ -495,6 +508,28 @@ static_assert(kSentDepth >= 1 && 17 * kSentDepth <= 63, "load counter range");
 // loader: its sentinel lands after its data, so the loader only waits for a
 // free ring slot (compute waves' releases) and, to bound its load counter,
 // for its oldest page once kSentDepth are in flight.
+// A later step of a launch streams K/V pages only once the sync wave has
+// seen the step's tokens counted (L_TOKOK): rows that earlier steps of the
+// launch wrote are then complete.  Weight pages need no such wait.
+__device__ __forceinline__ bool loader_tok_gate(const Env &e, bool &tok_ok, uint32_t qi) {
+  if (tok_ok) return true;
+  Watchdog wd;
+  for (uint32_t it = 1;; ++it) {
+    if (__builtin_amdgcn_readfirstlane(asm_lds_ld(L_TOKOK))) {
+      tok_ok = true;
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(MK_LSLEEP);
+    if ((it & 63) == 0) {
+      if (__builtin_amdgcn_readfirstlane(asm_lds_ld(L_ABORT))) return false;
+      if (wd.expired(e.cp->watchdog_ticks)) {
+        raise_error(e, 0xB8000000u | qi, 0);
+        return false;
+      }
+    }
+  }
+}
+
 template <bool PAGED>
 __device__ __forceinline__ void loader_role(const Env &e, const Args &a, int lw) {
   const int lane = lane_id();
@@ -509,10 +544,15 @@ __device__ __forceinline__ void loader_role(const Env &e, const Args &a, int lw)
     return m;
   };
   uint32_t n = 0;  // global page index
+  bool tok_ok = a.step_off == 0;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
-    perturb(e, a.tag, qi, (uint32_t)(threadIdx.x >> 6));
+    perturb(e, step_tag(a), qi, (uint32_t)(threadIdx.x >> 6));
     if (PAGED && d.op == OP_ATTN) {
+      if (!loader_tok_gate(e, tok_ok, qi)) {
+        wait_vm0();
+        return;
+      }
       int lo, hi;
       uint32_t nr;
       attn_geom(a, d, e.pos0, lo, hi, nr);
@@ -629,7 +669,7 @@ __device__ __forceinline__ bool wait_group(const Env &e, const Args &a, const Wa
   const uint32_t grp = wt.grp;
   const bool mine = lane < (int)wt.nslot;
   const uint32_t *cp = a.ctr + ((size_t)grp * kSlots + (lane & (kSlots - 1))) * kCtrStride;
-  const uint32_t need = mine ? a.grp_target[grp * kSlots + lane] * a.epoch : 0u;
+  const uint32_t need = mine ? a.grp_target[grp * kSlots + lane] * step_epoch(a) : 0u;
   Watchdog wd;
   for (uint32_t it = 0;; ++it) {
     bool ok = true;
@@ -650,15 +690,52 @@ __device__ __forceinline__ bool wait_group(const Env &e, const Args &a, const Wa
   }
 }
 
+// Token b of this step, read once per step by the sync wave (the only
+// reader).  Step 0's are the caller's; those of step s > 0 were written
+// during the launch by another workgroup and are read device-coherently.
+__device__ __forceinline__ int32_t ld_tok(const Args &a, int b) {
+  if (a.step_off == 0) return a.tokens[b];
+  return (int32_t)ld_cu(reinterpret_cast<const uint32_t *>(a.next_tok) + b);
+}
+
+// Step s > 0 of a launch reads the tokens step s - 1 chose: wait until its
+// finisher has counted them (the token counter reaches tok_base + s).  The
+// finisher ran after every unit of step s - 1, so this wait also orders the
+// K/V rows that step wrote before their reads in this step; L_TOKOK tells
+// the workgroup's other waves.
+__device__ __forceinline__ bool wait_tokens(const Env &e, const Args &a) {
+  if (a.step_off == 0) return true;
+  const uint32_t *tc = a.amax_ctr + kTokWord;
+  const uint32_t need = a.tok_base + (uint32_t)a.step_off;
+  Watchdog wd;
+  for (uint32_t it = 0;; ++it) {
+    if ((int32_t)(ld_cu(tc) - need) >= 0) {
+      poll_exit();
+      lds_st(L_TOKOK, 1);
+      wake();
+      return true;
+    }
+    if ((it & 63) == 63) {
+      if (lds_ld(L_ABORT)) return false;
+      if (ld_cu(&e.cp->status[0]) != 0) { lds_st(L_ABORT, 1); return false; }
+      if (wd.expired(e.cp->watchdog_ticks)) {
+        raise_error(e, 0xC8000000u | (uint32_t)a.step_off, 0);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(MK_WSLEEP);
+  }
+}
+
 // Input vector source of the RMSNorm'd instructions.
-__device__ __forceinline__ void norm_src(const Env &e, const Args &a, const Instr &d, int b,
+__device__ __forceinline__ void norm_src(const Env &e, const Instr &d, int b, int32_t tok,
                                          const float *&h, const uint16_t *&emb, const uint16_t *&w) {
   const DevCtx &c = *e.cp;
   h = nullptr;
   emb = nullptr;
   if (d.op == OP_QKV) {
     w = G(c.layers)[d.layer].attn_norm;
-    if (d.layer == 0) emb = c.embed + (size_t)a.tokens[b] * c.H;
+    if (d.layer == 0) emb = c.embed + (size_t)tok * c.H;
     else h = c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer, b);
   } else if (d.op == OP_FFN) {
     w = G(c.layers)[d.layer].ffn_norm;
@@ -672,19 +749,21 @@ __device__ __forceinline__ void norm_src(const Env &e, const Args &a, const Inst
 __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
+  if (!wait_tokens(e, a)) return;
   // inputs are validated once per workgroup before anything depends on them
   for (int b = 0; b < a.batch; ++b) {
-    int32_t tk = a.tokens[b], ps = a.positions[b];
+    int32_t tk = ld_tok(a, b), ps = a.positions[b] + a.step_off;
     if (tk < 0 || tk >= c.V) { raise_error(e, 0xE1000000u, (uint32_t)b); return; }
     if (ps < 0 || ps >= c.max_seq) { raise_error(e, 0xE2000000u, (uint32_t)b); return; }
   }
   const int b = 0;
+  const int32_t tok = ld_tok(a, b);
   const int pos = e.pos0;
   uint32_t seq = 0;
   float rs = 0.f;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
-    perturb(e, a.tag, qi, (uint32_t)(threadIdx.x >> 6));
+    perturb(e, step_tag(a), qi, (uint32_t)(threadIdx.x >> 6));
     const uint32_t nx = is_gemv(d.op) ? d.nk : 1;
     const bool normed = d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM;
     float *accs = reinterpret_cast<float *>(smem + L_ACC + (qi & (kAccSlots - 1)) * kAccFloats * 4);
@@ -702,7 +781,7 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
         nwl[i >> 2] = *G(reinterpret_cast<const uint64_t *>(nw + k0 + i));
     };
     if (normed) {
-      norm_src(e, a, d, b, h, emb, nw);
+      norm_src(e, d, b, tok, h, emb, nw);
       stage_norm_weights(0);
     }
     // Unit qi shares its LDS result slot and its completion counter with
@@ -862,15 +941,18 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
         const uint32_t k0 = k * d.kc;
         if (c.H > 2048 || k0 != 0) load_batch(k0, hv);
         if (k > 0) stage_norm_weights(k0);
+        // one base address per lane, the 8 chunks at immediate offsets
+        const uint64_t *nwp = nwl + lane;
+        f4 *xp = reinterpret_cast<f4 *>(xs) + lane;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           const uint32_t i = (uint32_t)(lane + 64 * m) * 4;
           if (i < d.kc) {
             const f4 v = hv[m];
-            const uint64_t w4 = nwl[i >> 2];
+            const uint64_t w4 = nwp[64 * m];
             const uint32_t w0 = (uint32_t)w4, w1 = (uint32_t)(w4 >> 32);
             f4 o = {v.x * rs * bf_lo(w0), v.y * rs * bf_hi(w0), v.z * rs * bf_lo(w1), v.w * rs * bf_hi(w1)};
-            *reinterpret_cast<f4 *>(xs + i) = o;
+            xp[64 * m] = o;
           }
         }
       } else if (d.op == OP_O || d.op == OP_DOWN) {
@@ -888,7 +970,7 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
         if (k == 0) {
           float rv[kAccFloats / 64];
           if (d.op == OP_O && d.layer == 0) {
-            const GAS uint16_t *er = G(c.embed) + (size_t)a.tokens[b] * c.H + d.item0;
+            const GAS uint16_t *er = G(c.embed) + (size_t)tok * c.H + d.item0;
 #pragma unroll
             for (int m = 0; m < kAccFloats / 64; ++m) {
               const uint32_t r = (uint32_t)(lane + 64 * m);
@@ -909,10 +991,11 @@ __device__ __forceinline__ void sync_role(const Env &e, const Args &a) {
             if (r < d.n_items) accs[r] = rv[m];
           }
         }
+        f4 *xp = reinterpret_cast<f4 *>(xs) + lane;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           const uint32_t i = (uint32_t)(lane + 64 * m) * 4;
-          if (i < d.kc) *reinterpret_cast<f4 *>(xs + i) = v[m];
+          if (i < d.kc) xp[64 * m] = v[m];
         }
       }
       wait_lgkm0();
@@ -1034,23 +1117,23 @@ __device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const
           uint64_t *dst = hs < (uint32_t)c.G
                               ? c.q_buf + lay::q(c.max_batch, c.nq, c.hd, d.layer, b, (int)(g * c.G + hs))
                               : c.kvn_buf + lay::kvn(c.max_batch, c.nkv, c.hd, d.layer, b, (int)g, 0);
-          st_tag(dst + ii, v0, a.tag);
-          st_tag(dst + ii + half, v1, a.tag);
+          st_tag(dst + ii, v0, step_tag(a));
+          st_tag(dst + ii + half, v1, step_tag(a));
         } else if (hs <= (uint32_t)c.G) {
           const float cs = R[kAccFloats / 2 + 2 * i], sn = R[kAccFloats / 2 + 2 * i + 1];
           const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
           if (hs < (uint32_t)c.G) {
             uint64_t *q = c.q_buf + lay::q(c.max_batch, c.nq, c.hd, d.layer, b, (int)(g * c.G + hs));
-            st_tag(q + ii, r0, a.tag);
-            st_tag(q + ii + half, r1, a.tag);
+            st_tag(q + ii, r0, step_tag(a));
+            st_tag(q + ii + half, r1, step_tag(a));
           } else {
             uint16_t *k = a.kv + kv_off(c, d.layer, 0, b, g, p);
             const uint16_t k0 = f2bf(r0), k1 = f2bf(r1);
             st_c16(k + ii, k0);
             st_c16(k + ii + half, k1);
             uint64_t *kn = c.kvn_buf + lay::kvn(c.max_batch, c.nkv, c.hd, d.layer, b, (int)g, 0);
-            st_tag(kn + ii, bf16f(k0), a.tag);
-            st_tag(kn + ii + half, bf16f(k1), a.tag);
+            st_tag(kn + ii, bf16f(k0), step_tag(a));
+            st_tag(kn + ii + half, bf16f(k1), step_tag(a));
           }
         } else {
           uint16_t *v = a.kv + kv_off(c, d.layer, 1, b, g, p);
@@ -1058,8 +1141,8 @@ __device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const
           st_c16(v + ii, u0);
           st_c16(v + ii + half, u1);
           uint64_t *vn = c.kvn_buf + lay::kvn(c.max_batch, c.nkv, c.hd, d.layer, b, (int)g, 1);
-          st_tag(vn + ii, bf16f(u0), a.tag);
-          st_tag(vn + ii + half, bf16f(u1), a.tag);
+          st_tag(vn + ii, bf16f(u0), step_tag(a));
+          st_tag(vn + ii + half, bf16f(u1), step_tag(a));
         }
         break;
       }
@@ -1075,7 +1158,7 @@ __device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const
         st_c(c.h_buf + lay::h(c.max_batch, c.H, 2 * d.layer + 2, b) + d.item0 + i, R[i]);
         break;
       default:  // OP_LM
-        G(a.logits)[lay::logits(c.V, b) + d.item0 + i] = R[i];
+        G(step_logits(a))[lay::logits(c.V, b) + d.item0 + i] = R[i];
         break;
     }
   }
@@ -1096,6 +1179,20 @@ __device__ __forceinline__ void unit_epilogue(const Env &e, const Args &a, const
   }
 }
 
+// The greedy finisher's tokens: device-coherent stores (a later step of the
+// launch reads them on other CUs), acknowledged before the token counter
+// counts the step.  Positions are written by the launch's last step only,
+// so a caller may pass the same buffer as positions and next_positions.
+__device__ __forceinline__ void st_tok(int32_t *p, int32_t v) {
+  __hip_atomic_store(G(reinterpret_cast<uint32_t *>(p)), (uint32_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void count_tokens(const Args &a) {
+  wait_vm0();
+  before_signal();
+  if (lane_id() == 0)
+    __hip_atomic_fetch_add(G(a.amax_ctr + kTokWord), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The last LM unit of the step to count itself picks the greedy token from
 // every unit's candidate (each acknowledged before its unit counted) and
 // writes it with the next position.
@@ -1106,7 +1203,7 @@ __device__ __forceinline__ void lm_greedy_finish(const Env &e, const Args &a) {
   if (lane == 0)
     o = __hip_atomic_fetch_add(G(a.amax_ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   o = __builtin_amdgcn_readfirstlane(o);
-  if (o + 1u != a.amax_target) return;
+  if (o + 1u != step_amax_target(a)) return;
   poll_exit();  // the candidates read below were acknowledged before their units counted
   const rsrc_t r = rsrc(a.amax);
   float bv = -INFINITY;
@@ -1122,9 +1219,10 @@ __device__ __forceinline__ void lm_greedy_finish(const Env &e, const Args &a) {
   }
   amax_reduce(bv, bi);
   if (lane == 0) {
-    G(a.next_tok)[0] = (int32_t)bi;
-    G(a.next_pos)[0] = e.pos0 + 1;
+    st_tok(a.next_tok, (int32_t)bi);
+    if (a.step_off + 1 == (int32_t)a.n_steps) G(a.next_pos)[0] = e.pos0 + 1;
   }
+  count_tokens(a);
 }
 
 // I2 on registers (head_dim 64, splits of at most PF positions beyond the
@@ -1157,6 +1255,19 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, in
     }
   }
   if (!gate()) return false;
+  // rows an earlier step of this launch wrote (positions from p - step_off
+  // on) are complete only once the gate has passed: load them again
+  if (a.step_off > 0 && lo + nt0 > p - a.step_off) {
+#pragma unroll
+    for (int t = 0; t < PF; ++t) {
+      const int tt = min(t, nt0 - 1);
+#pragma unroll
+      for (int m = 0; m < DPL; ++m) {
+        kk[t][m] = ldc16(Kr, (uint32_t)(tt * hd + lane + 64 * m) * 2);
+        vv[t][m] = ldc16(Vr, (uint32_t)(tt * hd + lane + 64 * m) * 2);
+      }
+    }
+  }
   float mrun = -INFINITY, lrun = 0.f, o[DPL], q[DPL];
   uint16_t kp[DPL], vp[DPL];
 #pragma unroll
@@ -1174,13 +1285,13 @@ __device__ bool attn_body(const Env &e, const Args &a, const Instr &d, int h, in
       for (int m = 0; m < DPL; ++m) {
         const uint64_t wq = ldt(qr, (uint32_t)(lane + 64 * m));
         q[m] = tval(wq);
-        ok = ok && tok(wq, a.tag);
+        ok = ok && tok(wq, step_tag(a));
         kp[m] = vp[m] = 0;
         if (has_p) {
           const uint64_t wk = ldt(nr, (uint32_t)(lane + 64 * m)), wv = ldt(nr, (uint32_t)(hd + lane + 64 * m));
           kp[m] = (uint16_t)((uint32_t)wk >> 16);  // exact: K and V arrive rounded to bf16
           vp[m] = (uint16_t)((uint32_t)wv >> 16);
-          ok = ok && tok(wk, a.tag) && tok(wv, a.tag);
+          ok = ok && tok(wk, step_tag(a)) && tok(wv, step_tag(a));
         }
       }
       return ok;
@@ -1336,11 +1447,11 @@ __device__ bool attn_paged(const Env &e, const Args &a, const Instr &d, int cw, 
         for (int m = 0; m < DPL; ++m) {
           const uint64_t wq = ldt(qr, (uint32_t)(lane + 64 * m));
           qv[m] = tval(wq);
-          ok = ok && tok(wq, a.tag);
+          ok = ok && tok(wq, step_tag(a));
           if (has_p) {
             const uint64_t wk = ldt(nrr, (uint32_t)(lane + 64 * m)), wv = ldt(nrr, (uint32_t)(hd + lane + 64 * m));
             kpv[m] = tval(wk);
-            ok = ok && tok(wk, a.tag) && tok(wv, a.tag);
+            ok = ok && tok(wk, step_tag(a)) && tok(wv, step_tag(a));
           }
         }
         return ok;
@@ -1609,7 +1720,7 @@ __device__ __forceinline__ void compute_role(const Env &e, const Args &a, int cw
   uint32_t n = 0, seq = 0, aq_t = 0, am_t = 0;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
-    perturb(e, a.tag, qi, (uint32_t)(threadIdx.x >> 6));
+    perturb(e, step_tag(a), qi, (uint32_t)(threadIdx.x >> 6));
     const bool gv = is_gemv(d.op);
     const uint32_t nx = gv ? d.nk : 1;
     uint32_t upages = d.pages;
@@ -1799,7 +1910,7 @@ static_assert(LB_SENT + kRingPagesB * kSentBytes <= kLdsBytes, "batched LDS budg
 static_assert(LB_AMAX + 8 * 8 <= LB_ACC && L_EPI < LB_AMAX, "control words");
 
 __device__ __forceinline__ int seq_pos(const Args &a, const DevCtx &c, int b) {
-  const int p = a.positions[b];
+  const int p = a.positions[b] + a.step_off;
   return (p < 0 || p >= c.max_seq) ? 0 : p;
 }
 
@@ -1865,10 +1976,15 @@ __device__ __forceinline__ void loader_role_b(const Env &e, const Args &a, int l
     return m;
   };
   uint32_t n = 0;
+  bool tok_ok = a.step_off == 0;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
-    perturb(e, a.tag, qi, (uint32_t)(threadIdx.x >> 6));
+    perturb(e, step_tag(a), qi, (uint32_t)(threadIdx.x >> 6));
     if (PAGED && d.op == OP_ATTN) {
+      if (!loader_tok_gate(e, tok_ok, qi)) {
+        wait_vm0();
+        return;
+      }
       const DevCtx &c = *e.cp;
       int lo, hi;
       uint32_t nr;
@@ -1997,16 +2113,19 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
   const DevCtx &c = *e.cp;
   const int lane = lane_id();
   const int B = a.batch;
+  if (!wait_tokens(e, a)) return;
   for (int b = 0; b < B; ++b) {
-    int32_t tk = a.tokens[b], ps = a.positions[b];
+    int32_t tk = ld_tok(a, b), ps = a.positions[b] + a.step_off;
     if (tk < 0 || tk >= c.V) { raise_error(e, 0xE1000000u, (uint32_t)b); return; }
     if (ps < 0 || ps >= c.max_seq) { raise_error(e, 0xE2000000u, (uint32_t)b); return; }
   }
+  // lane b < B holds sequence b's token for the whole step
+  const int32_t tok_all = lane < B ? ld_tok(a, lane) : 0;
   const char *zero = reinterpret_cast<const char *>(c.zero);
   uint32_t seq = 0;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
-    perturb(e, a.tag, qi, (uint32_t)(threadIdx.x >> 6));
+    perturb(e, step_tag(a), qi, (uint32_t)(threadIdx.x >> 6));
     const bool gv = is_gemv(d.op);
     const uint32_t nx = gv ? d.nk : 1;
     const bool normed = d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM;
@@ -2083,14 +2202,14 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
     } else {
       const float *h;
       const uint16_t *emb;
-      norm_src(e, a, d, 0, h, emb, nw);
+      norm_src(e, d, 0, 0, h, emb, nw);
       if (h) src0 = reinterpret_cast<const char *>(h);
       sstr = (uint32_t)c.H * 4;
     }
     // layer 0's QKV widens the bf16 embedding rows of the step's tokens
     const uint16_t *embed = c.embed;
     const uint32_t Hs = (uint32_t)c.H;
-    const int32_t tok_l = emb_in && lane < B ? a.tokens[lane] : 0;
+    const int32_t tok_l = emb_in ? tok_all : 0;
     const uint32_t loads = (emb_in ? 0u : (uint32_t)B) + (normed ? 1u : 0u);
     float ss = 0.f;  // sum of squares of sequence lane >> 3, over this lane's part
     auto issue = [&](uint32_t k, uint32_t sq) -> uint32_t {
@@ -2205,9 +2324,9 @@ __device__ __forceinline__ void sync_role_b(const Env &e, const Args &a) {
         }
         if (d.op == OP_O && d.layer == 0 && done == 0) {
           // layer 0's residual is the bf16 embedding row
-          for (uint32_t x = (uint32_t)lane; x < d.n_items * (uint32_t)B; x += 64) {
-            const uint32_t b = x / d.n_items, r = x - b * d.n_items;
-            accs[b * 64 + r] = bf16f(G(c.embed)[(size_t)a.tokens[b] * c.H + d.item0 + r]);
+          for (int b = 0; b < B; ++b) {
+            const int32_t tk = __builtin_amdgcn_readlane(tok_all, b);
+            if ((uint32_t)lane < d.n_items) accs[b * 64 + lane] = bf16f(G(c.embed)[(size_t)tk * c.H + d.item0 + lane]);
           }
         }
         wait_lgkm0();
@@ -2262,7 +2381,7 @@ __device__ __forceinline__ bool unit_epilogue_b(const Env &e, const Args &a, con
       old = __hip_atomic_fetch_add(G(a.amax_ctr) + kCtrStride + lay::split_group(d.aux1), 1u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
     old = __builtin_amdgcn_readfirstlane(old);
-    if (old + 1u != S * a.epoch) return false;
+    if (old + 1u != S * step_epoch(a)) return false;
     poll_exit();
     const rsrc_t pr = rsrc(dp0);
     for (uint32_t x = (uint32_t)lane; x < d.n_items * B; x += 64) {
@@ -2325,16 +2444,16 @@ __device__ __forceinline__ bool unit_epilogue_b(const Env &e, const Args &a, con
           const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
           if (hs < (uint32_t)c.G) {
             uint64_t *q = c.q_buf + lay::q(c.max_batch, c.nq, c.hd, d.layer, (int)b, (int)(g * c.G + hs));
-            st_tag(q + ii, r0, a.tag);
-            st_tag(q + ii + half, r1, a.tag);
+            st_tag(q + ii, r0, step_tag(a));
+            st_tag(q + ii + half, r1, step_tag(a));
           } else {
             uint16_t *k = a.kv + kv_off(c, d.layer, 0, (int)b, (int)g, p);
             const uint16_t k0 = f2bf(r0), k1 = f2bf(r1);
             st_c16(k + ii, k0);
             st_c16(k + ii + half, k1);
             uint64_t *kn = c.kvn_buf + lay::kvn(c.max_batch, c.nkv, c.hd, d.layer, (int)b, (int)g, 0);
-            st_tag(kn + ii, bf16f(k0), a.tag);
-            st_tag(kn + ii + half, bf16f(k1), a.tag);
+            st_tag(kn + ii, bf16f(k0), step_tag(a));
+            st_tag(kn + ii + half, bf16f(k1), step_tag(a));
           }
         } else {
           uint16_t *v = a.kv + kv_off(c, d.layer, 1, (int)b, (int)g, p);
@@ -2342,8 +2461,8 @@ __device__ __forceinline__ bool unit_epilogue_b(const Env &e, const Args &a, con
           st_c16(v + ii, u0);
           st_c16(v + ii + half, u1);
           uint64_t *vn = c.kvn_buf + lay::kvn(c.max_batch, c.nkv, c.hd, d.layer, (int)b, (int)g, 1);
-          st_tag(vn + ii, bf16f(u0), a.tag);
-          st_tag(vn + ii + half, bf16f(u1), a.tag);
+          st_tag(vn + ii, bf16f(u0), step_tag(a));
+          st_tag(vn + ii + half, bf16f(u1), step_tag(a));
         }
         break;
       }
@@ -2361,7 +2480,7 @@ __device__ __forceinline__ bool unit_epilogue_b(const Env &e, const Args &a, con
              accs[b * 64 + i] + tile_sum(Pb, T, i, b));
         break;
       default:  // OP_LM
-        G(a.logits)[lay::logits(c.V, (int)b) + d.item0 + i] = tile_sum(Pb, T, i, b) * accs[b];
+        G(step_logits(a))[lay::logits(c.V, (int)b) + d.item0 + i] = tile_sum(Pb, T, i, b) * accs[b];
         break;
     }
   }
@@ -2408,7 +2527,7 @@ __device__ __forceinline__ void lm_greedy_finish_b(const Env &e, const Args &a) 
   if (lane == 0)
     o = __hip_atomic_fetch_add(G(a.amax_ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   o = __builtin_amdgcn_readfirstlane(o);
-  if (o + 1u != a.amax_target) return;
+  if (o + 1u != step_amax_target(a)) return;
   poll_exit();
   const rsrc_t r = rsrc(a.amax);
   const uint32_t B = (uint32_t)a.batch;
@@ -2426,10 +2545,11 @@ __device__ __forceinline__ void lm_greedy_finish_b(const Env &e, const Args &a) 
     }
     amax_reduce(bv, bi);
     if (lane == 0) {
-      G(a.next_tok)[b] = (int32_t)bi;
-      G(a.next_pos)[b] = seq_pos(a, c, (int)b) + 1;
+      st_tok(a.next_tok + b, (int32_t)bi);
+      if (a.step_off + 1 == (int32_t)a.n_steps) G(a.next_pos)[b] = seq_pos(a, c, (int)b) + 1;
     }
   }
+  count_tokens(a);
 }
 
 // A wide LM-head unit (more than 8 row tiles): compute wave cw owns the
@@ -2544,7 +2664,7 @@ __device__ bool gemv_wide_b(const Env &e, const Args &a, const Instr &d, int cw,
         const uint32_t sq = 4 * (uint32_t)(lane >> 4) + (uint32_t)j;
         if (sq < B) {
           const float v = acc[r][j] * accs[sq];
-          G(a.logits)[lay::logits(c.V, (int)sq) + d.item0 + row] = v;
+          G(step_logits(a))[lay::logits(c.V, (int)sq) + d.item0 + row] = v;
           if (amax_better(v, d.item0 + row, bvv[j], bii[j])) {
             bvv[j] = v;
             bii[j] = d.item0 + row;
@@ -2584,7 +2704,7 @@ __device__ __forceinline__ void compute_role_b(const Env &e, const Args &a, int 
   uint32_t n = 0, seq = 0, aq_t = 0, am_t = 0;
   for (uint32_t qi = 0; qi < e.nq; ++qi) {
     const Instr d = e.q[qi];
-    perturb(e, a.tag, qi, (uint32_t)(threadIdx.x >> 6));
+    perturb(e, step_tag(a), qi, (uint32_t)(threadIdx.x >> 6));
     const bool gv = is_gemv(d.op);
     const uint32_t nx = gv ? d.nk : 1;
     uint32_t upages = d.pages;
@@ -2745,92 +2865,183 @@ __device__ __forceinline__ void compute_role_b(const Env &e, const Args &a, int 
   }
 }
 
-// PAGED: the plan's attention units stream their K/V through pages (each
-// plan is one or the other; separate instantiations keep the register
-// allocation of the register-path kernel unchanged)
+// A step's set-up on this workgroup: its queue and (batch 1) position;
+// false for a workgroup with no units (nothing to wait for or produce; the
+// inputs are validated by the workgroups that use them).
+template <bool BATCHED>
+__device__ __forceinline__ bool step_env(const Args &a, Env &e) {
+  e.cp = a.ctx;
+  e.cu = (int)blockIdx.x;
+  const uint32_t q0 = a.q_off[e.cu], q1 = a.q_off[e.cu + 1];
+  e.q = a.instr + q0;
+  e.nq = q1 - q0;
+  if (e.nq == 0) return false;
+  e.trace = a.trace ? a.trace + 4 + (size_t)e.cu * a.trace_stride * kTraceWords : nullptr;
+  e.flags = e.cp->flags;
+  // batch 1: an out-of-range position is replaced by 0 so that every cache
+  // access stays in bounds; the sync wave reports it as an input error and
+  // the step is abandoned (batched roles read each sequence's own position)
+  e.pos0 = 0;
+  if (!BATCHED) {
+    e.pos0 = a.positions[0] + a.step_off;
+    if (e.pos0 < 0 || e.pos0 >= e.cp->max_seq) e.pos0 = 0;
+  }
+  return true;
+}
+
+// LDS control words (step 0's tokens are the caller's) and page sentinels
+// (no page has landed: they hold an index no page has), then every wave.
+template <bool BATCHED>
+__device__ __forceinline__ void step_lds(const Args &a) {
+  if (threadIdx.x < 64) lds_u32(threadIdx.x * 4) = threadIdx.x * 4 == L_TOKOK && a.step_off == 0 ? 1u : 0u;
+  constexpr int kSentWords = (BATCHED ? kRingPagesB : kRingPages) * kSentBytes / 4;
+  for (int i = (int)threadIdx.x; i < kSentWords; i += kThreads)
+    lds_u32((BATCHED ? LB_SENT : L_SENT) + 4 * i) = 0xffffffffu;
+  __syncthreads();
+}
+
+// Issue priorities by role, set once per launch.
+template <bool BATCHED>
+__device__ __forceinline__ void role_priority(int w) {
+#if MK_BPRIO
+  // the sync wave's activation pieces ahead of the weight stream, whose
+  // loads otherwise fill the CU's memory queue first
+  if (BATCHED) {
+    if (w >= kNCW + kNLW) __builtin_amdgcn_s_setprio(3);
+    else if (w < kNCW) __builtin_amdgcn_s_setprio(2);
+  }
+#endif
+#if MK_PRIO
+  // the sync wave (critical-path waits and activation pieces) first,
+  // compute waves next, weight streaming last
+  if (!BATCHED) {
+    if (w >= kNCW + kNLW) __builtin_amdgcn_s_setprio(3);
+    else if (w < kNCW) __builtin_amdgcn_s_setprio(1);
+  }
+#endif
+}
+
+constexpr int kRoleCompute = 0, kRoleLoader = 1, kRoleSync = 2;
+template <bool PAGED, bool BATCHED, int ROLE>
+__device__ __forceinline__ void run_role(const Env &e, const Args &a, int w) {
+  if (ROLE == kRoleCompute) {
+    if (BATCHED) compute_role_b<PAGED>(e, a, w);
+    else compute_role<PAGED>(e, a, w);
+  } else if (ROLE == kRoleLoader) {
+    if (BATCHED) loader_role_b<PAGED>(e, a, w - kNCW);
+    else loader_role<PAGED>(e, a, w - kNCW);
+  } else {
+    if (BATCHED) sync_role_b(e, a);
+    else sync_role(e, a);
+  }
+}
+
+// Several chained greedy steps per launch (n_steps, tok_base set).  Step s
+// runs with step_off = s: its counter targets, tags, positions, tokens and
+// logits rows follow from it.  Each role runs its own step loop, so that a
+// wave keeps across steps only the arguments its role reads; the loops meet
+// at the same barriers (set-up, end of step) in every step.
+template <bool PAGED, bool BATCHED, int ROLE>
+__device__ __forceinline__ void role_steps(const Args &a, int w) {
+  Args as = a;
+  for (int32_t s = 0;; ++s) {
+    as.step_off = s;
+    Env e;
+    if (!step_env<BATCHED>(as, e)) return;
+    step_lds<BATCHED>(as);
+    run_role<PAGED, BATCHED, ROLE>(e, as, w);
+    // a device error raised elsewhere ends the launch here too; one lane
+    // decides, so that every wave leaves at the same step
+    if (threadIdx.x == 0 && ld_cu(reinterpret_cast<const uint32_t *>(e.cp->status))) lds_u32(L_ABORT) = 1u;
+    // every wave of the workgroup is through step s (and its loads)
+    __syncthreads();
+    if (lds_u32(L_ABORT) || (uint32_t)s + 1 >= as.n_steps) return;
+  }
+}
+template <bool PAGED, bool BATCHED>
+__device__ __forceinline__ void chained_steps(const Args &a) {
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  role_priority<BATCHED>(w);
+  if (w < kNCW) role_steps<PAGED, BATCHED, kRoleCompute>(a, w);
+  else if (w < kNCW + kNLW) role_steps<PAGED, BATCHED, kRoleLoader>(a, w);
+  else role_steps<PAGED, BATCHED, kRoleSync>(a, w);
+}
+
+#define MK_STEP_PARAMS                                                                                              \
+  const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const uint32_t *__restrict__ q_off,             \
+      const Wait *__restrict__ waits, const uint64_t *__restrict__ rowtab, uint32_t *__restrict__ ctr,             \
+      const uint32_t *__restrict__ grp_target, float *__restrict__ part_buf, const uint32_t *__restrict__ iota,    \
+      const int32_t *__restrict__ tokens, const int32_t *__restrict__ positions, uint16_t *__restrict__ kv,        \
+      float *__restrict__ logits, uint64_t *__restrict__ trace, uint32_t trace_stride, uint32_t epoch,             \
+      uint32_t tag, int32_t batch, int32_t n_split, int32_t split_len, uint64_t *__restrict__ amax,               \
+      uint32_t *__restrict__ amax_ctr, int32_t *__restrict__ next_tok, int32_t *__restrict__ next_pos,            \
+      uint32_t n_lm, uint32_t amax_target, uint32_t n_steps, uint32_t tok_base
+#define MK_STEP_ARGS(NS)                                                                                            \
+  Args { ctx, instr, q_off, waits, rowtab, ctr, grp_target, part_buf, iota, tokens, positions, kv, logits, trace,  \
+         trace_stride, epoch, tag, batch, n_split, split_len, amax, amax_ctr, next_tok, next_pos, n_lm,             \
+         amax_target, NS, tok_base, 0 }
+
+// One decode step per launch.  PAGED: the plan's attention units stream
+// their K/V through pages (each plan is one or the other; separate
+// instantiations keep the register allocation of the register-path kernel
+// unchanged).
 template <bool PAGED>
-__global__ void __launch_bounds__(kThreads, 1)
-mk_interp_b(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const uint32_t *__restrict__ q_off,
-            const Wait *__restrict__ waits, const uint64_t *__restrict__ rowtab, uint32_t *__restrict__ ctr,
-            const uint32_t *__restrict__ grp_target, float *__restrict__ part_buf, const uint32_t *__restrict__ iota,
-            const int32_t *__restrict__ tokens, const int32_t *__restrict__ positions, uint16_t *__restrict__ kv,
-            float *__restrict__ logits, uint64_t *__restrict__ trace, uint32_t trace_stride, uint32_t epoch,
-            uint32_t tag, int32_t batch, int32_t n_split, int32_t split_len, uint64_t *__restrict__ amax,
-            uint32_t *__restrict__ amax_ctr, int32_t *__restrict__ next_tok, int32_t *__restrict__ next_pos,
-            uint32_t n_lm, uint32_t amax_target) {
-  const Args a{ctx, instr, q_off, waits, rowtab, ctr, grp_target, part_buf, iota, tokens, positions, kv, logits,
-               trace, trace_stride, epoch, tag, batch, n_split, split_len, amax, amax_ctr, next_tok, next_pos,
-               n_lm, amax_target};
+__global__ void __launch_bounds__(kThreads, 1) mk_interp(MK_STEP_PARAMS) {
+  const Args a = MK_STEP_ARGS(1u);
   Env e;
   e.cp = a.ctx;
   e.cu = (int)blockIdx.x;
   const uint32_t q0 = a.q_off[e.cu], q1 = a.q_off[e.cu + 1];
   e.q = a.instr + q0;
   e.nq = q1 - q0;
+  // a workgroup without units has nothing to wait for or produce (the
+  // inputs are validated by the workgroups that use them)
+  if (e.nq == 0) return;
   e.trace = a.trace ? a.trace + 4 + (size_t)e.cu * a.trace_stride * kTraceWords : nullptr;
-  e.pos0 = 0;  // unused: batched roles read each sequence's own position
   e.flags = e.cp->flags;
-  if (threadIdx.x < 64) lds_u32(threadIdx.x * 4) = 0;  // control words
-  for (int i = (int)threadIdx.x; i < kRingPagesB * kSentBytes / 4; i += kThreads)
-    lds_u32(LB_SENT + 4 * i) = 0xffffffffu;
-  __syncthreads();
   // the wave index is uniform within a wave: saying so keeps each role's
   // control flow on the scalar unit instead of exec-masked vector code
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-#if MK_BPRIO
-  // issue priority: the sync wave's activation pieces ahead of the weight
-  // stream, whose loads otherwise fill the CU's memory queue first
-  if (w >= kNCW + kNLW) __builtin_amdgcn_s_setprio(3);
-  else if (w < kNCW) __builtin_amdgcn_s_setprio(2);
-#endif
-  if (w < kNCW) compute_role_b<PAGED>(e, a, w);
-  else if (w < kNCW + kNLW) loader_role_b<PAGED>(e, a, w - kNCW);
-  else sync_role_b(e, a);
-}
-
-// --------------------------------------------------------------------------
-template <bool PAGED>
-__global__ void __launch_bounds__(kThreads, 1)
-mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const uint32_t *__restrict__ q_off,
-          const Wait *__restrict__ waits, const uint64_t *__restrict__ rowtab, uint32_t *__restrict__ ctr, const uint32_t *__restrict__ grp_target,
-          float *__restrict__ part_buf, const uint32_t *__restrict__ iota, const int32_t *__restrict__ tokens,
-          const int32_t *__restrict__ positions, uint16_t *__restrict__ kv, float *__restrict__ logits,
-          uint64_t *__restrict__ trace, uint32_t trace_stride, uint32_t epoch, uint32_t tag, int32_t batch, int32_t n_split,
-          int32_t split_len, uint64_t *__restrict__ amax, uint32_t *__restrict__ amax_ctr, int32_t *__restrict__ next_tok,
-          int32_t *__restrict__ next_pos, uint32_t n_lm, uint32_t amax_target) {
-  const Args a{ctx, instr, q_off, waits, rowtab, ctr, grp_target, part_buf, iota, tokens, positions, kv, logits,
-               trace, trace_stride, epoch, tag, batch, n_split, split_len, amax, amax_ctr, next_tok, next_pos,
-               n_lm, amax_target};
-  Env e;
-  e.cp = a.ctx;
-  e.cu = (int)blockIdx.x;
-  const uint32_t q0 = a.q_off[e.cu], q1 = a.q_off[e.cu + 1];
-  e.q = a.instr + q0;
-  e.nq = q1 - q0;
-  e.trace = a.trace ? a.trace + 4 + (size_t)e.cu * a.trace_stride * kTraceWords : nullptr;
+  role_priority<false>(w);
   // an out-of-range position is replaced by 0 so that every cache access
   // stays in bounds; the sync wave reports it as an input error and the
   // step is abandoned
   e.pos0 = a.positions[0];
   if (e.pos0 < 0 || e.pos0 >= e.cp->max_seq) e.pos0 = 0;
-  e.flags = e.cp->flags;
-  if (threadIdx.x < 64) lds_u32(threadIdx.x * 4) = 0;  // control words
-  // no page has landed: sentinels hold an index no page has
-  for (int i = (int)threadIdx.x; i < kRingPages * kSentBytes / 4; i += kThreads)
-    lds_u32(L_SENT + 4 * i) = 0xffffffffu;
-  __syncthreads();
-  // the wave index is uniform within a wave: saying so keeps each role's
-  // control flow on the scalar unit instead of exec-masked vector code
-  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-#if MK_PRIO
-  // issue priority: the sync wave (critical-path waits and activation
-  // pieces) first, compute waves next, weight streaming last
-  if (w >= kNCW + kNLW) __builtin_amdgcn_s_setprio(3);
-  else if (w < kNCW) __builtin_amdgcn_s_setprio(1);
-#endif
+  step_lds<false>(a);
   if (w < kNCW) compute_role<PAGED>(e, a, w);
   else if (w < kNCW + kNLW) loader_role<PAGED>(e, a, w - kNCW);
   else sync_role(e, a);
+}
+
+template <bool PAGED>
+__global__ void __launch_bounds__(kThreads, 1) mk_interp_b(MK_STEP_PARAMS) {
+  const Args a = MK_STEP_ARGS(1u);
+  Env e;
+  e.cp = a.ctx;
+  e.cu = (int)blockIdx.x;
+  const uint32_t q0 = a.q_off[e.cu], q1 = a.q_off[e.cu + 1];
+  e.q = a.instr + q0;
+  e.nq = q1 - q0;
+  if (e.nq == 0) return;
+  e.trace = a.trace ? a.trace + 4 + (size_t)e.cu * a.trace_stride * kTraceWords : nullptr;
+  e.pos0 = 0;  // unused: batched roles read each sequence's own position
+  e.flags = e.cp->flags;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  role_priority<true>(w);
+  step_lds<true>(a);
+  if (w < kNCW) compute_role_b<PAGED>(e, a, w);
+  else if (w < kNCW + kNLW) loader_role_b<PAGED>(e, a, w - kNCW);
+  else sync_role_b(e, a);
+}
+
+template <bool PAGED>
+__global__ void __launch_bounds__(kThreads, 1) mk_interp_n(MK_STEP_PARAMS) {
+  chained_steps<PAGED, false>(MK_STEP_ARGS(n_steps));
+}
+template <bool PAGED>
+__global__ void __launch_bounds__(kThreads, 1) mk_interp_bn(MK_STEP_PARAMS) {
+  chained_steps<PAGED, true>(MK_STEP_ARGS(n_steps));
 }
 
 }  // namespace mk
@@ -2839,8 +3050,12 @@ mk_interp(const DevCtx *__restrict__ ctx, const Instr *__restrict__ instr, const
 // Host-side launch helpers (the ABI layer is plain C++).
 namespace mk {
 
-static const void *const kKernels[4] = {(const void *)mk_interp<false>, (const void *)mk_interp<true>,
-                                        (const void *)mk_interp_b<false>, (const void *)mk_interp_b<true>};
+// [batched][paged][multi-step]
+static const void *const kKernels[8] = {
+    (const void *)mk_interp<false>,   (const void *)mk_interp_n<false>,
+    (const void *)mk_interp<true>,    (const void *)mk_interp_n<true>,
+    (const void *)mk_interp_b<false>, (const void *)mk_interp_bn<false>,
+    (const void *)mk_interp_b<true>,  (const void *)mk_interp_bn<true>};
 
 hipError_t kernel_setup(int *blocks_per_cu) {
   *blocks_per_cu = 1 << 30;
@@ -2903,13 +3118,13 @@ hipError_t kernel_launch(const Args &a0, int grid, bool cooperative, bool paged,
   void *params[] = {&a.ctx, &a.instr, &a.q_off, &a.waits, &a.rowtab, &a.ctr, &a.grp_target, &a.part_buf, &a.iota,
                     &a.tokens, &a.positions, &a.kv, &a.logits, &a.trace, &a.trace_stride, &a.epoch, &a.tag,
                     &a.batch, &a.n_split, &a.split_len, &a.amax, &a.amax_ctr, &a.next_tok, &a.next_pos,
-                    &a.n_lm, &a.amax_target};
+                    &a.n_lm, &a.amax_target, &a.n_steps, &a.tok_base};
   // One workgroup per CU fits (checked at create); a plain launch places all
   // of them at once on an otherwise idle device, a cooperative one also
   // waits for room when other work holds CUs (about 23 us more per launch).
   // batches of 2 or more sequences run the MFMA kernel; plans whose
   // attention streams paged K/V run that instantiation
-  const void *fn = kKernels[(a.batch > 1 ? 2 : 0) + (paged ? 1 : 0)];
+  const void *fn = kKernels[(a.batch > 1 ? 4 : 0) + (paged ? 2 : 0) + (a.n_steps > 1 ? 1 : 0)];
   if (cooperative) return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), params, kLdsBytes, stream);
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), params, kLdsBytes, stream);
 }

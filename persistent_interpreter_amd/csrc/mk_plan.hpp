@@ -58,6 +58,7 @@ constexpr int kAttnRegRows = 20;
 // GPUs the library keeps one for.
 constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
 constexpr int kMaxDevices = 64;
+constexpr int kMaxStepsPerLaunch = 65536;  // decode steps one launch may run
 constexpr int kMfmaRows = 64;
 // Batched LM-head units are wider: one per workgroup, each compute wave
 // owning whole 16-row tiles (at most 4 of them), so the final-normed
@@ -143,6 +144,7 @@ constexpr int L_ABORT = 148;    // u32      nonzero: every wave exits
 constexpr int L_EPI = 152;      // u32      units whose epilogue has finished
 constexpr int L_AQ = 156;       // u32      paged attention: heads whose q is staged in LDS
 constexpr int L_AM = 160;       // u32      paged attention: partials written for the merge
+constexpr int L_TOKOK = 164;    // u32      this step's input tokens are in (earlier steps of the launch are done)
 constexpr int kMaxBatch = 8;    // sequences per step the plans are built for
 constexpr int L_ACC = 256;      // fp32 row results, kAccSlots x kAccFloats
 constexpr int L_XS = L_ACC + kAccSlots * kAccFloats * 4;  // activation ring
@@ -191,6 +193,20 @@ struct Args {
   int32_t *next_pos;          // [batch]: positions + 1
   uint32_t n_lm;              // LM units in the plan
   uint32_t amax_target;       // counter value once this step's LM units are in
+  // Several greedy steps per launch: step s (0-based, step_off) runs with
+  // epoch epoch + s, tag tag + s, greedy target amax_target + s * n_lm,
+  // positions + s, logits row block s and (s > 0) the tokens the step
+  // before wrote to next_tok; the step's finisher stores the tokens, waits
+  // for their acknowledgement and counts the step on the token counter
+  // (amax_ctr + kTokWord), which step s + 1's sync waves wait for
+  // (>= tok_base + s + 1) before they read a token.  The other fields are
+  // the launch's own.
+  uint32_t n_steps;           // >= 1 (> 1 only with next_tok)
+  uint32_t tok_base;          // greedy steps counted before this launch
+  int32_t step_off;           // device side: this step's index s
 };
+// The token counter word, in the greedy arrival counter's padded block.
+constexpr int kTokWord = 16;
+static_assert(kTokWord > 0 && kTokWord < kCtrStride, "token counter inside the greedy counter's block");
 
 }  // namespace mk

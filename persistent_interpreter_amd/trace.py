@@ -97,6 +97,10 @@ def main(argv=None) -> int:
     critical path:
 
         python -m persistent_interpreter_amd.trace WORKLOAD [STEPS] [--kv-splits N]
+                                                   [--steps-per-launch N]
+
+With --steps-per-launch N each launch runs N chained greedy steps
+(mk_decode_steps_greedy) and the trace holds the last launch's last step.
 
     Columns (microseconds from the step's first event): first/last time a
     unit's waits were satisfied, median/last completion, and medians of the
@@ -110,17 +114,26 @@ def main(argv=None) -> int:
     ap.add_argument("workload")
     ap.add_argument("steps", nargs="?", type=int, default=3)
     ap.add_argument("--kv-splits", type=int, default=0)
+    ap.add_argument("--steps-per-launch", type=int, default=1)
     args = ap.parse_args(argv)
+    spl = max(1, args.steps_per_launch)
     import torch
     mc = synth.CONFIGS[args.workload]
+    mc = mc.replace(steps=max(mc.steps, args.steps * spl))
     W = synth.make_weights(mc, threads=16)
     kv = synth.make_kv_cache(mc, filled=mc.prior) if mc.batch == 1 else synth.make_kv_cache(mc)
     tok, pos = synth.make_tokens(mc), synth.make_positions(mc)
     s = harness.Session(mc, W, kv, batch=mc.batch, flags=B.MK_FLAG_TRACE, kv_splits=args.kv_splits)
     s.set_inputs(tok, pos)
+    lg = torch.empty(spl, mc.batch, mc.vocab, dtype=torch.float32, device="cuda")
     for _ in range(args.steps):
-        if s.step_greedy() != 0:
-            raise RuntimeError("mk_decode_step_greedy failed")
+        if spl == 1:
+            rc = s.step_greedy()
+        else:
+            rc = s.mk.decode_steps_greedy(mc.batch, spl, s.tokens, s.positions, s.kv, lg,
+                                          s.tokens, s.positions)
+        if rc != 0:
+            raise RuntimeError(f"decode launch failed: {rc}")
     torch.cuda.synchronize()
     if s.mk.sync_status() != 0:
         raise RuntimeError("device error")
@@ -132,7 +145,8 @@ def main(argv=None) -> int:
     s.close()
     a = decode(raw)
     span = float(np.nanmax(a["t_done"]) - np.nanmin(a["t_begin"]))
-    print(f"{args.workload}: last of {args.steps} traced steps, span {span:.1f} us, {len(a)} records")
+    what = "steps" if spl == 1 else f"launches of {spl} steps (the last step)"
+    print(f"{args.workload}: last of {args.steps} traced {what}, span {span:.1f} us, {len(a)} records")
     print(f"{'L':>3} {'op':>12} {'units':>5} {'1st_rdy':>8} {'last_rdy':>8} {'med_done':>8} "
           f"{'last_done':>9} {'busy':>7} {'xprod':>6} {'epi':>6}")
     for r in summary(a):

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert B.lib().mk_version() == 104
+    assert B.lib().mk_version() == 105
     for code in (0, -1, -2, -3, -4, -5, -6, -10, -11, -12, -99):
         assert len(B.strerror(code)) > 0
 
@@ -53,6 +53,8 @@ def test_null_arguments_rejected_without_gpu():
     assert L.mk_decode_step(None, 1, None, None, None, None, None) == B.MK_ERR_INVALID_ARG
     assert L.mk_decode_step_greedy(None, 1, None, None, None, None, None, None,
                                    None) == B.MK_ERR_INVALID_ARG
+    assert L.mk_decode_steps_greedy(None, 1, 4, None, None, None, None, None, None,
+                                    None) == B.MK_ERR_INVALID_ARG
     assert L.mk_sync_status(None) == B.MK_ERR_INVALID_ARG
     assert L.mk_stream_read(None, 16, None, None) == B.MK_ERR_INVALID_ARG
     L.mk_destroy(None)  # NULL-safe
