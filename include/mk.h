@@ -331,14 +331,26 @@ typedef struct mk_addr_report {
  *   corrupt : 0, or a planted size error for the model's self-tests: the
  *             model's copy of one buffer is one record short (1: the KV
  *             cache's last slot, 2: the last attention partial, 3: the last
- *             RoPE row, 4: the last q head, 5: the final residual row), so
- *             a run that reaches that record must report it.
+ *             RoPE row, 4: the last q head, 5: the final residual row, 6:
+ *             the last sequence's logits row), so a run that reaches that
+ *             record must report it.
  * Returns MK_OK if no access falls outside its buffer, MK_ERR_INVALID_ARG
  * (rep->msg names the first) otherwise, or the plan's own error.  Host only. */
 int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cus,
                   int32_t steps, const int32_t *positions,
                   const int32_t *tokens, int32_t corrupt,
                   mk_addr_report *rep);
+
+/* mk_addr_check_launch -- the same model for ONE launch of `steps` chained
+ * greedy steps (mk_decode_steps_greedy): step s writes logits row block s of
+ * a [steps][batch][vocab] buffer, reads its tokens from next_tokens for
+ * s > 0 (the caller's tokens for s = 0) after waiting on the token counter,
+ * and its positions at positions[b] + s.  Arguments, returns and errors as
+ * mk_addr_check.  Host only. */
+int mk_addr_check_launch(const mk_config *cfg, int32_t batch, int32_t num_cus,
+                         int32_t steps, const int32_t *positions,
+                         const int32_t *tokens, int32_t corrupt,
+                         mk_addr_report *rep);
 
 /* Internal activation buffers, for stage-by-stage comparison in tests. */
 #define MK_BUF_H      1   /* fp32 [2L+1][max_batch][hidden]: index 2l+1 is the
@@ -371,7 +383,8 @@ size_t mk_stream_read_sink_words(void);
 /* mk_version -- ABI version of this header (major*100 + minor): 101 adds
  * mk_decode_step_greedy, 102 mk_stream_read, 103 mk_addr_check, the batched
  * (MFMA) kernel and mk_plan_report.mfma_cols_k, 104
- * mk_plan_report.paged_kv and .down_splits, 105 mk_decode_steps_greedy. */
+ * mk_plan_report.paged_kv and .down_splits, 105 mk_decode_steps_greedy,
+ * 106 mk_addr_check_launch. */
 int mk_version(void);
 
 #ifdef __cplusplus

@@ -41,7 +41,8 @@ EXPORTED = ("mk_create", "mk_decode_step", "mk_decode_step_greedy",
             "mk_sync_status", "mk_destroy", "mk_strerror", "mk_plan_check",
             "mk_get_buffer", "mk_version", "mk_stream_read",
             "mk_stream_read_sink_words", "mk_addr_check",
-            "mk_decode_step_static", "mk_decode_steps_greedy")
+            "mk_decode_step_static", "mk_decode_steps_greedy",
+            "mk_addr_check_launch")
 
 
 class MkConfig(C.Structure):
@@ -139,6 +140,11 @@ def lib():
                                     C.POINTER(C.c_int32), C.c_int32,
                                     C.POINTER(MkAddrReport)]
         L.mk_addr_check.restype = C.c_int
+        L.mk_addr_check_launch.argtypes = [C.POINTER(MkConfig), C.c_int32, C.c_int32,
+                                    C.c_int32, C.POINTER(C.c_int32),
+                                    C.POINTER(C.c_int32), C.c_int32,
+                                    C.POINTER(MkAddrReport)]
+        L.mk_addr_check_launch.restype = C.c_int
         L.mk_version.argtypes = []
         L.mk_version.restype = C.c_int
         _lib = L
@@ -175,13 +181,14 @@ def plan_check(cfg: MkConfig, batch: int, num_cus: int, sim_runs: int = 0,
 
 
 def addr_check(cfg: MkConfig, batch: int, num_cus: int, steps: int,
-               positions, tokens, corrupt: int = 0):
-    """Run the host address model (mk_addr_check); returns (rc, report)."""
+               positions, tokens, corrupt: int = 0, one_launch: bool = False):
+    """Run the host address model (mk_addr_check, or with one_launch
+    mk_addr_check_launch: the steps as one launch); returns (rc, report)."""
     rep = MkAddrReport()
     pos = (C.c_int32 * batch)(*[int(x) for x in positions])
     tok = (C.c_int32 * batch)(*[int(x) for x in tokens])
-    rc = lib().mk_addr_check(C.byref(cfg), batch, num_cus, steps, pos, tok,
-                             corrupt, C.byref(rep))
+    fn = lib().mk_addr_check_launch if one_launch else lib().mk_addr_check
+    rc = fn(C.byref(cfg), batch, num_cus, steps, pos, tok, corrupt, C.byref(rep))
     return rc, rep
 
 

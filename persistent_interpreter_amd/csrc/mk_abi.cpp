@@ -127,7 +127,7 @@ struct mk_handle {
 
 extern "C" {
 
-int mk_version(void) { return 105; }
+int mk_version(void) { return 106; }
 
 const char *mk_strerror(int code) {
   switch (code) {

@@ -73,6 +73,12 @@ struct Model {
 
 struct Bases {
   uint64_t tokens, positions, kv, logits, next_tok, next_pos;
+  // the step being walked: where its tokens come from (the caller's, or for
+  // step s > 0 of a launch of several steps the ones step s - 1 wrote), the
+  // first logits element of its row block, and whether its sync waves wait
+  // on the token counter
+  uint64_t tok_src = 0, logit_off = 0;
+  bool tok_wait = false;
   uint64_t h, q, kvn, attn, a, part, rope, status, ctr, target, amax, rowtab, iota;
   uint64_t embed, lm_head, final_norm, zero;
   std::vector<uint64_t> attn_norm, q_norm, k_norm, ffn_norm;
@@ -188,7 +194,7 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
     const uint32_t q0 = P.q_off[cu], q1 = P.q_off[cu + 1];
     // ---- sync wave (sync_role_b: staging pipeline)
     for (int b = 0; b < batch; ++b) {
-      M.el(B.tokens, b, 4, 4, "sync(b): tokens[b]");
+      M.el(B.tok_src, b, 4, 4, "sync(b): tokens[b]");
       M.el(B.positions, b, 4, 4, "sync(b): positions[b]");
     }
     if (inputs_ok)
@@ -415,7 +421,7 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
               }
               M.el(B.h, lay::h(MB, H, 2 * d.layer + 2, b) + d.item0 + i, 4, 4, "epilogue(b): down");
               break;
-            default: M.el(B.logits, lay::logits(V, b) + d.item0 + i, 4, 4, "epilogue(b): logits"); break;
+            default: M.el(B.logits, B.logit_off + lay::logits(V, b) + d.item0 + i, 4, 4, "epilogue(b): logits"); break;
           }
         }
         if (d.op == OP_DOWN && lay::split_n(d.aux1) > 1)
@@ -444,9 +450,10 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
   }
 }
 
-extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int32_t steps,
-                             const int32_t *positions, const int32_t *tokens, int32_t corrupt,
-                             mk_addr_report *rep) {
+// `steps` steps, as that many one-step launches, or (one_launch) as one
+// launch of `steps` chained steps.
+static int addr_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int32_t steps, bool one_launch,
+                      const int32_t *positions, const int32_t *tokens, int32_t corrupt, mk_addr_report *rep) {
   if (rep) std::memset(rep, 0, sizeof *rep);
   if (!cfg || !positions || !tokens || batch < 1 || num_cus < 1 || steps < 1) return MK_ERR_INVALID_ARG;
   const mk_config &c = *cfg;
@@ -502,9 +509,9 @@ extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cu
   // planted size errors for the model's self-tests: one record short
   const uint64_t short_kv = corrupt == 1 ? (uint64_t)hd * 2 : 0, short_part = corrupt == 2 ? (hd + 4) * 4 : 0;
   const uint64_t short_rope = corrupt == 3 ? (uint64_t)hd * 4 : 0, short_q = corrupt == 4 ? (uint64_t)hd * 8 : 0;
-  const uint64_t short_h = corrupt == 5 ? (uint64_t)H * 4 : 0;
+  const uint64_t short_h = corrupt == 5 ? (uint64_t)H * 4 : 0, short_logits = corrupt == 6 ? (uint64_t)V * 4 : 0;
   B.kv = M.add("kv_cache", lay::kv_size(L, MB, nkv, S, hd) * 2 - short_kv);
-  B.logits = M.add("logits", (uint64_t)batch * V * 4);
+  B.logits = M.add("logits", (uint64_t)(one_launch ? steps : 1) * batch * V * 4 - short_logits);
   B.next_tok = M.add("next_tokens", (uint64_t)batch * 4);
   B.next_pos = M.add("next_positions", (uint64_t)batch * 4);
   // library buffers, sized as mk_create and the plan upload size them
@@ -538,6 +545,10 @@ extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cu
   for (int step = 0; step < steps; ++step) {
     std::vector<int> pos(batch);
     for (int b = 0; b < batch; ++b) pos[b] = positions[b] + step;
+    B.tok_src = one_launch && step > 0 ? B.next_tok : B.tokens;
+    B.logit_off = one_launch ? (uint64_t)step * batch * V : 0;
+    B.tok_wait = one_launch && step > 0;
+    if (B.tok_wait) M.el(B.ctr, amax_word + kTokWord, 4, 4, "sync: token counter wait");
     // the launch clamps an invalid position to 0 for the cache accesses (the
     // sync wave reports it and abandons the step)
     const int pos0 = (pos[0] < 0 || pos[0] >= S) ? 0 : pos[0];
@@ -554,7 +565,7 @@ extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cu
       const uint32_t q0 = P.q_off[cu], q1 = P.q_off[cu + 1];
       // ---- sync wave ----------------------------------------------------
       for (int b = 0; b < batch; ++b) {
-        M.el(B.tokens, b, 4, 4, "sync: tokens[b]");
+        M.el(B.tok_src, b, 4, 4, "sync: tokens[b]");
         M.el(B.positions, b, 4, 4, "sync: positions[b]");
       }
       if (inputs_ok)
@@ -841,7 +852,7 @@ extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cu
               case OP_DOWN:
                 M.el(B.h, lay::h(MB, H, 2 * d.layer + 2, b) + d.item0 + i, 4, 4, "epilogue: down rows");
                 break;
-              default: M.el(B.logits, lay::logits(V, b) + d.item0 + i, 4, 4, "epilogue: logits"); break;
+              default: M.el(B.logits, B.logit_off + lay::logits(V, b) + d.item0 + i, 4, 4, "epilogue: logits"); break;
             }
           }
           if (d.op == OP_LM) {
@@ -869,4 +880,16 @@ extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cu
     std::snprintf(rep->msg, sizeof rep->msg, "%s", M.first.c_str());
   }
   return M.bad ? MK_ERR_INVALID_ARG : MK_OK;
+}
+
+extern "C" int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int32_t steps,
+                             const int32_t *positions, const int32_t *tokens, int32_t corrupt,
+                             mk_addr_report *rep) {
+  return addr_check(cfg, batch, num_cus, steps, false, positions, tokens, corrupt, rep);
+}
+
+extern "C" int mk_addr_check_launch(const mk_config *cfg, int32_t batch, int32_t num_cus, int32_t steps,
+                                    const int32_t *positions, const int32_t *tokens, int32_t corrupt,
+                                    mk_addr_report *rep) {
+  return addr_check(cfg, batch, num_cus, steps, true, positions, tokens, corrupt, rep);
 }

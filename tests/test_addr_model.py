@@ -77,3 +77,38 @@ def test_bad_arguments():
     cfg = B.make_config(mc)
     assert B.addr_check(cfg, 1, CUS, 0, [16], [1])[0] == B.MK_ERR_INVALID_ARG
     assert B.addr_check(cfg, 2, CUS, 1, [16, 16], [1, 1])[0] != 0   # batch > max_batch
+
+
+@pytest.mark.parametrize("name,batch,steps", [("tiny", 1, 12), ("tiny_qk", 1, 8), ("tiny", 3, 8),
+                                              ("tiny", 8, 4), ("llama1b", 1, 2)])
+def test_one_launch_of_several_steps_in_bounds(name, batch, steps):
+    """mk_decode_steps_greedy: the steps as one launch (logits row block per
+    step, in-launch tokens, the token counter, positions + s)."""
+    mc = synth.CONFIGS[name]
+    if batch > 1 and mc.batch != batch:
+        mc = mc.replace(batch=batch, pos_lo=4, pos_hi=40)
+    mc = mc.replace(steps=steps)
+    cfg = B.make_config(mc, max_batch=batch)
+    rc, rep = B.addr_check(cfg, batch, CUS, steps, synth.make_positions(mc, batch),
+                           synth.make_tokens(mc, batch), one_launch=True)
+    assert rep.accesses > 0
+    assert rc == 0 and rep.violations == 0, rep.msg.decode()
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_launch_logits_blocks_are_modelled(batch):
+    """A logits buffer one row short: one step per launch writes its single
+    row block, so the last row is reached at once; as one launch of several
+    steps only the last step's last row falls outside, which the model must
+    find (it would not if every step wrote the first row block)."""
+    mc = synth.CONFIGS["tiny"]
+    if batch > 1:
+        mc = mc.replace(batch=batch, pos_lo=4, pos_hi=40)
+    mc = mc.replace(steps=4)
+    cfg = B.make_config(mc, max_batch=batch)
+    pos, tok = synth.make_positions(mc, batch), synth.make_tokens(mc, batch)
+    rc, rep = B.addr_check(cfg, batch, CUS, 4, pos, tok, corrupt=6, one_launch=True)
+    assert rc != 0 and rep.violations > 0 and "logits" in rep.msg.decode()
+    rc, rep = B.addr_check(cfg, batch, CUS, 3, pos, tok, one_launch=True)
+    assert rc == 0, rep.msg.decode()
+
