@@ -306,6 +306,31 @@ int mk_plan_check(const mk_config *cfg, int32_t batch, int32_t num_cus,
                   int32_t sim_runs, int32_t corrupt, uint64_t seed,
                   mk_plan_report *rep);
 
+/* One queued unit of a schedule, as mk_plan_units reports it. */
+typedef struct mk_unit_info {
+  int32_t op;       /* 1 QKV, 2 attention, 3 reduction, 4 O, 5 FFN, 6 down, 7 LM head */
+  int32_t layer;
+  int32_t nk;       /* activation pieces per row (projections)                       */
+  int32_t pages;    /* 16 KB weight pages streamed (projections); paged attention:
+                       rows per page in ppp, pages from the step's position         */
+  int32_t ppp;      /* weight pieces per page, or K/V rows per page (paged attention) */
+  int32_t n_items;  /* output rows (items) of the unit                               */
+  int32_t ipw;      /* pieces (rows) per item: 2 for RoPE pairs and gate/up          */
+  int32_t wait_n;   /* counter groups it waits on                                    */
+} mk_unit_info;
+
+/* mk_plan_units -- the schedule mk_plan_check builds for (cfg, batch) on
+ * `num_cus` workgroups, unit by unit: the per-workgroup queues back to back,
+ * workgroup c's units at [q_off[c], q_off[c + 1]).  It lets tests model
+ * what happens inside a workgroup (the ordering between its loader, sync
+ * and compute waves) over the library's own schedules.  Host only.
+ *   units : host array of `cap` entries, or NULL with cap 0 (count only).
+ *   q_off : host int32 [num_cus + 1], or NULL.
+ * Returns the number of units (entries beyond cap are not written), or an
+ * MK_ERR_* code. */
+int mk_plan_units(const mk_config *cfg, int32_t batch, int32_t num_cus,
+                  mk_unit_info *units, int32_t cap, int32_t *q_off);
+
 /* Result of the address model below. */
 typedef struct mk_addr_report {
   int64_t accesses;           /* global accesses evaluated (per lane)        */
@@ -384,7 +409,7 @@ size_t mk_stream_read_sink_words(void);
  * mk_decode_step_greedy, 102 mk_stream_read, 103 mk_addr_check, the batched
  * (MFMA) kernel and mk_plan_report.mfma_cols_k, 104
  * mk_plan_report.paged_kv and .down_splits, 105 mk_decode_steps_greedy,
- * 106 mk_addr_check_launch. */
+ * 106 mk_addr_check_launch, 107 mk_plan_units. */
 int mk_version(void);
 
 #ifdef __cplusplus

@@ -42,7 +42,7 @@ EXPORTED = ("mk_create", "mk_decode_step", "mk_decode_step_greedy",
             "mk_get_buffer", "mk_version", "mk_stream_read",
             "mk_stream_read_sink_words", "mk_addr_check",
             "mk_decode_step_static", "mk_decode_steps_greedy",
-            "mk_addr_check_launch")
+            "mk_addr_check_launch", "mk_plan_units")
 
 
 class MkConfig(C.Structure):
@@ -78,6 +78,12 @@ class MkPlanReport(C.Structure):
                 ("sim_runs", C.c_int32), ("sim_errors", C.c_int32),
                 ("paged_kv", C.c_int32), ("down_splits", C.c_int32),
                 ("msg", C.c_char * 256)]
+
+
+class MkUnitInfo(C.Structure):
+    _fields_ = [("op", C.c_int32), ("layer", C.c_int32), ("nk", C.c_int32),
+                ("pages", C.c_int32), ("ppp", C.c_int32), ("n_items", C.c_int32),
+                ("ipw", C.c_int32), ("wait_n", C.c_int32)]
 
 
 class MkAddrReport(C.Structure):
@@ -135,6 +141,9 @@ def lib():
                                     C.POINTER(C.c_void_p),
                                     C.POINTER(C.c_size_t)]
         L.mk_get_buffer.restype = C.c_int
+        L.mk_plan_units.argtypes = [C.POINTER(MkConfig), C.c_int32, C.c_int32,
+                                    C.POINTER(MkUnitInfo), C.c_int32, C.POINTER(C.c_int32)]
+        L.mk_plan_units.restype = C.c_int
         L.mk_addr_check.argtypes = [C.POINTER(MkConfig), C.c_int32, C.c_int32,
                                     C.c_int32, C.POINTER(C.c_int32),
                                     C.POINTER(C.c_int32), C.c_int32,
@@ -190,6 +199,19 @@ def addr_check(cfg: MkConfig, batch: int, num_cus: int, steps: int,
     fn = lib().mk_addr_check_launch if one_launch else lib().mk_addr_check
     rc = fn(C.byref(cfg), batch, num_cus, steps, pos, tok, corrupt, C.byref(rep))
     return rc, rep
+
+
+def plan_units(cfg: MkConfig, batch: int, num_cus: int):
+    """The schedule's units (mk_plan_units): (list of MkUnitInfo, q_off)."""
+    n = lib().mk_plan_units(C.byref(cfg), batch, num_cus, None, 0, None)
+    if n < 0:
+        raise MkError(n, "mk_plan_units")
+    units = (MkUnitInfo * max(n, 1))()
+    q_off = (C.c_int32 * (num_cus + 1))()
+    rc = lib().mk_plan_units(C.byref(cfg), batch, num_cus, units, n, q_off)
+    if rc != n:
+        raise MkError(rc, "mk_plan_units")
+    return list(units)[:n], list(q_off)
 
 
 def _ptr(t) -> int:

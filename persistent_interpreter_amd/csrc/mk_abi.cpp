@@ -127,7 +127,7 @@ struct mk_handle {
 
 extern "C" {
 
-int mk_version(void) { return 106; }
+int mk_version(void) { return 107; }
 
 const char *mk_strerror(int code) {
   switch (code) {
@@ -144,6 +144,34 @@ const char *mk_strerror(int code) {
     case MK_ERR_BAD_POSITION: return "position outside [0, max_seq)";
     default: return "unknown status code";
   }
+}
+
+int mk_plan_units(const mk_config *cfg, int32_t batch, int32_t num_cus, mk_unit_info *units, int32_t cap,
+                  int32_t *q_off) {
+  std::string err;
+  int rc = check_config(cfg, err);
+  if (rc != MK_OK) return rc;
+  if (batch < 1 || batch > cfg->max_batch || num_cus < 1 || cap < 0 || (cap > 0 && !units))
+    return MK_ERR_INVALID_ARG;
+  Plan plan;
+  rc = build_plan(*cfg, batch, num_cus, plan, err);
+  if (rc != MK_OK) return rc;
+  const int32_t n = (int32_t)plan.instr.size();
+  if (q_off)
+    for (int c = 0; c <= num_cus; ++c) q_off[c] = (int32_t)plan.q_off[c];
+  for (int32_t i = 0; i < n && i < cap; ++i) {
+    const Instr &in = plan.instr[i];
+    mk_unit_info &u = units[i];
+    u.op = in.op;
+    u.layer = in.layer;
+    u.nk = in.nk;
+    u.pages = (int32_t)in.pages;
+    u.ppp = in.ppp;
+    u.n_items = (int32_t)in.n_items;
+    u.ipw = in.ipw;
+    u.wait_n = (int32_t)in.wait_n;
+  }
+  return n;
 }
 
 int mk_plan_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int32_t sim_runs, int32_t corrupt,
