@@ -1,7 +1,7 @@
-"""The ordering inside a workgroup of the batch-1 kernel, on the host
-(tests/wg_model.py): the library's own queues (mk_plan_units) run through a
-model of the loader, sync and compute waves' LDS protocol under random
-schedules with long stalls of single waves.  check_plan covers the ordering
+"""The ordering inside a workgroup of the batch-1 and batched kernels, on
+the host (tests/wg_model.py): the library's own queues (mk_plan_units) run
+through a model of the loader, sync and compute waves' LDS protocol under
+random schedules with long stalls of single waves.  check_plan covers the ordering
 between workgroups and mk_addr_check the addresses; this covers the
 handshakes between the waves of one workgroup: page ring slots and their
 sentinels, activation slots, result slots and the epilogue that frees them.
@@ -16,8 +16,9 @@ from persistent_interpreter_amd import binding as B, synth
 CUS = 256
 
 
-def _queues(name):
-    units, q = B.plan_units(B.make_config(synth.CONFIGS[name]), 1, CUS)
+def _queues(name, batch=1):
+    mc = synth.CONFIGS[name]
+    units, q = B.plan_units(B.make_config(mc, max_batch=max(batch, mc.batch)), batch, CUS)
     return [units[q[c]:q[c + 1]] for c in range(CUS) if q[c + 1] > q[c]]
 
 
@@ -66,5 +67,53 @@ def test_planted_protocol_errors_are_caught(name, knob, kw, what):
             W.simulate(qu, seed=seed, knobs=(knob,), budget=3_000_000, **kw)
         except W.ProtocolError as e:
             caught.append(str(e))
+            break
     assert caught, f"{knob} was not caught on {name}"
+    assert any(w in caught[0] for w in what), caught[0]
+
+
+# ---- the batched kernel: six-page ring, four activation slots with three
+# pieces in flight, MFMA tiles, two partial-tile buffers
+
+@pytest.mark.parametrize("name,batch", [("tiny", 3), ("tiny", 8), ("llama1b_b8", 8)])
+def test_batched_queues_run_clean(name, batch):
+    qs = _queues(name, batch)
+    pick = qs if name == "tiny" else [qs[i] for i in (0, 1, 63, 128, 191, len(qs) - 1)]
+    for i, qu in enumerate(pick):
+        for seed in range(2):
+            W.simulate_batched(qu, seed=seed * 1000 + i)
+
+
+def test_batched_ring_of_fewer_pages_still_clean():
+    """A 16-row tile pair spans at most two pages, so 3 and 4 ring pages
+    still let every wave finish."""
+    qu = max(_queues("llama1b_b8", 8)[:8], key=len)
+    for p in (3, 4):
+        W.simulate_batched(qu, seed=p, ring_pages=p)
+
+
+# Each plant is checked on a queue where it can bite.  With Llama-1B's four
+# pieces per projection the activation-slot wait alone keeps the sync wave
+# within one unit of the slowest compute wave, which already orders the
+# result slots and partial-tile buffers; the tiny shape's one-piece units
+# leave those guards as the only order.  Conversely, on the tiny shape the
+# result-slot guard keeps the sync wave from reaching a slot still being
+# read, so an early activation-slot release shows only on Llama-1B.
+@pytest.mark.parametrize("name,batch,knob,what", [
+    ("tiny", 3, "early_slot", ("page", "deadlock")),
+    ("llama1b_b8", 8, "early_slot", ("page", "deadlock")),
+    ("llama1b_b8", 8, "early_xs", ("activation piece",)),
+    ("tiny", 3, "no_guard", ("result slot",)),
+    ("tiny", 8, "no_part_guard", ("partial tile", "candidate area")),
+])
+def test_batched_planted_protocol_errors_are_caught(name, batch, knob, what):
+    qu = max(_queues(name, batch)[:8], key=len)
+    caught = []
+    for seed in range(8):
+        try:
+            W.simulate_batched(qu, seed=seed, knobs=(knob,), budget=3_000_000)
+        except W.ProtocolError as e:
+            caught.append(str(e))
+            break
+    assert caught, f"{knob} was not caught on {name} batch {batch}"
     assert any(w in caught[0] for w in what), caught[0]
