@@ -122,7 +122,9 @@ typedef struct mk_handle mk_handle;
  *         for shapes the kernels cannot run, refused before any device call:
  *         head_dim other than 64 or 128, query heads per KV head not
  *         dividing 8, qk_norm without head_dim 128, hidden or ffn_dim not a
- *         multiple of 8, kv_splits above 64. */
+ *         multiple of 8, kv_splits above 64, n_layers above 4096, hidden,
+ *         ffn_dim or n_q_heads*head_dim above 2^20 (a descriptor holds the
+ *         layer and a row's K pieces in 16 bits). */
 int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out);
 
 /* mk_decode_step -- one decode step for sequences b < batch on `stream`
@@ -409,7 +411,9 @@ size_t mk_stream_read_sink_words(void);
  * mk_decode_step_greedy, 102 mk_stream_read, 103 mk_addr_check, the batched
  * (MFMA) kernel and mk_plan_report.mfma_cols_k, 104
  * mk_plan_report.paged_kv and .down_splits, 105 mk_decode_steps_greedy,
- * 106 mk_addr_check_launch, 107 mk_plan_units. */
+ * 106 mk_addr_check_launch, 107 mk_plan_units, 108 size limits that keep
+ * every descriptor field in range (mk_create and mk_plan_check refuse
+ * larger shapes). */
 int mk_version(void);
 
 #ifdef __cplusplus

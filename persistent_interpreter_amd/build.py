@@ -11,6 +11,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -24,6 +25,11 @@ DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__",
               f"-I{ROCM}/include", "-Wall", "-Wno-unused-function"]
+# host-only checking build: the C++ scheduler, plan checker and address
+# model under AddressSanitizer and UBSan (g++ only; device code is untouched)
+SAN_LIB = os.path.join(OUT_DIR, "libmk_san.so")
+SAN_HOST_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer",
+                  "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
 
 
 def _run(cmd):
@@ -59,6 +65,43 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     if verbose:
         print(f"built {out}")
     return out
+
+
+def build_sanitized(out: str = SAN_LIB) -> str:
+    """The library with its host code under AddressSanitizer and UBSan, for
+    CPU-only checks of the host entry points (mk_plan_check, mk_plan_units,
+    mk_addr_check*).  The device objects are the plain build's (built first
+    if missing).  A process that loads it needs the sanitizer runtimes
+    preloaded (``sanitizer_preload()``)."""
+    kobj = os.path.join(OUT_DIR, "libmk_mk_kernel.o")
+    pobj = os.path.join(OUT_DIR, "libmk_mk_probe.o")
+    if not (os.path.exists(kobj) and os.path.exists(pobj)):
+        build()
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    stem = os.path.splitext(os.path.basename(out))[0]
+    objs = [kobj, pobj]
+    for src in ("mk_sched.cpp", "mk_abi.cpp", "mk_addr.cpp"):
+        o = os.path.join(os.path.dirname(out), f"{stem}_" + src.replace(".cpp", ".o"))
+        _run(["g++", *HOST_FLAGS, *SAN_HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", o])
+        objs.append(o)
+    tmp = out + ".tmp"
+    _run(["g++", "-shared", *SAN_HOST_FLAGS, *objs, "-o", tmp, f"-L{ROCM}/lib", "-lamdhip64",
+          f"-Wl,-rpath,{ROCM}/lib"])
+    os.replace(tmp, out)
+    return out
+
+
+def sanitizer_preload() -> Optional[str]:
+    """LD_PRELOAD value with g++'s ASan and UBSan runtimes, or None if the
+    toolchain has none."""
+    libs = []
+    for name in ("libasan.so", "libubsan.so"):
+        r = subprocess.run(["g++", f"-print-file-name={name}"], stdout=subprocess.PIPE, text=True)
+        path = r.stdout.strip()
+        if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+            return None
+        libs.append(path)
+    return " ".join(libs)
 
 
 if __name__ == "__main__":

@@ -79,6 +79,9 @@ void free_plan(DevPlan &p) {
   hipFree(p.d_amax);
 }
 
+constexpr int kMaxLayers = 4096;
+constexpr int kMaxDim = 1 << 20;
+
 int check_config(const mk_config *c, std::string &err) {
   if (!c) { err = "null config"; return MK_ERR_INVALID_ARG; }
   if (c->n_layers < 1 || c->hidden < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1 ||
@@ -96,6 +99,13 @@ int check_config(const mk_config *c, std::string &err) {
   if (c->qk_norm && c->head_dim != 128) { err = "q/k norm needs head_dim 128"; return MK_ERR_UNSUPPORTED; }
   if (c->hidden % 8 || c->ffn_dim % 8) { err = "hidden and ffn_dim must be multiples of 8"; return MK_ERR_UNSUPPORTED; }
   if (c->kv_splits > kMaxSplits || c->kv_splits < 0) { err = "kv_splits must be in [0, 64]"; return MK_ERR_UNSUPPORTED; }
+  // a descriptor keeps the layer index (the LM head's units take n_layers)
+  // and the K pieces of a row (256-element MFMA pieces) in 16 bits
+  if (c->n_layers > kMaxLayers || c->hidden > kMaxDim || c->ffn_dim > kMaxDim ||
+      (int64_t)c->n_q_heads * c->head_dim > kMaxDim) {
+    err = "n_layers above 4096, or hidden, ffn_dim or n_q_heads*head_dim above 2^20";
+    return MK_ERR_UNSUPPORTED;
+  }
   if (c->mlp_chunks < 0 || c->num_cus < 0 || c->watchdog_ms < 0) { err = "negative knob"; return MK_ERR_INVALID_ARG; }
   if ((int64_t)c->vocab * c->hidden >= (1ll << 40)) { err = "model too large"; return MK_ERR_UNSUPPORTED; }
   return MK_OK;
@@ -127,7 +137,7 @@ struct mk_handle {
 
 extern "C" {
 
-int mk_version(void) { return 107; }
+int mk_version(void) { return 108; }
 
 const char *mk_strerror(int code) {
   switch (code) {

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert B.lib().mk_version() == 107
+    assert B.lib().mk_version() == 108
     for code in (0, -1, -2, -3, -4, -5, -6, -10, -11, -12, -99):
         assert len(B.strerror(code)) > 0
 
@@ -67,12 +67,26 @@ def test_null_arguments_rejected_without_gpu():
     ("kv_splits", 65, B.MK_ERR_UNSUPPORTED),
     ("n_layers", 0, B.MK_ERR_INVALID_ARG),
     ("max_seq", 0, B.MK_ERR_INVALID_ARG),
+    ("n_layers", 4097, B.MK_ERR_UNSUPPORTED),    # layer index is 16-bit
+    ("hidden", (1 << 20) + 8, B.MK_ERR_UNSUPPORTED),   # K pieces per row are 16-bit
+    ("ffn_dim", (1 << 20) + 8, B.MK_ERR_UNSUPPORTED),
 ])
 def test_bad_configs(field, value, code):
     cfg = B.make_config(synth.CONFIGS["tiny"])
     setattr(cfg, field, value)
     rc, rep = B.plan_check(cfg, 1, 8)
     assert rc == code, rep.msg
+
+
+def test_attention_width_limit():
+    """The O projection's contraction (n_q_heads * head_dim) has the same
+    16-bit piece count as hidden and ffn_dim."""
+    cfg = B.make_config(synth.CONFIGS["tiny"])
+    cfg.n_kv_heads, cfg.n_q_heads = 8192, 16384      # 16384 x 64 = 2^20: the limit
+    assert b"2^20" not in B.plan_check(cfg, 1, 8)[1].msg
+    cfg.n_kv_heads, cfg.n_q_heads = 8200, 16400
+    rc, rep = B.plan_check(cfg, 1, 8)
+    assert rc == B.MK_ERR_UNSUPPORTED and b"2^20" in rep.msg
 
 
 def test_batch_out_of_range():
