@@ -196,3 +196,40 @@ def test_qk_norm_makes_logits_invariant_to_scaling_wq_wk():
             assert d < 1e-5 * scale, (d, scale)
         else:    # scores grow four-fold
             assert d > 1e-2 * scale, (d, scale)
+
+
+def _first_max_loop(row):
+    """The arg max by a plain scan: the first index holding the largest
+    value, where a NaN counts as larger than every number and the first NaN
+    wins."""
+    best, bi = None, -1
+    for i, v in enumerate(row):
+        if bi < 0:
+            best, bi = v, i
+        elif math.isnan(best):
+            break
+        elif math.isnan(v) or v > best:
+            best, bi = v, i
+    return bi
+
+
+def test_greedy_lowest_index_on_exact_ties():
+    """The greedy choice (reading: ties go to the lowest index) against a
+    plain scan, on rows built with exact ties at the front, the back and in
+    between, all-equal rows, -inf entries, signed zeros and NaN."""
+    rng = np.random.default_rng(11)
+    rows = [np.zeros(7, np.float32), np.full(5, -np.inf, np.float32),
+            np.array([-0.0, 0.0, 0.0], np.float32),
+            np.array([1.0, np.nan, 3.0, np.nan], np.float32)]
+    for _ in range(200):
+        n = int(rng.integers(1, 40))
+        r = rng.integers(-3, 4, n).astype(np.float32)       # many exact ties
+        if rng.random() < 0.3:
+            r[rng.integers(0, n)] = -np.inf
+        rows.append(r)
+    for r in rows:
+        got = int(O.greedy(r[None, :])[0])
+        assert got == _first_max_loop(list(r)), r
+    # a batch of rows is row by row
+    B = np.stack([rng.integers(-2, 3, 16).astype(np.float32) for _ in range(6)])
+    assert list(O.greedy(B)) == [_first_max_loop(list(b)) for b in B]
