@@ -493,8 +493,15 @@ static int launch_step(mk_handle *h, int32_t batch, const int32_t *tokens, const
   dp->epoch += n_steps;
   if (next_tokens) dp->greedy_epoch += n_steps;
   const StepScratch sc{dp->d_ctr, dp->d_part, dp->d_amax, e0, g0};
-  return launch_with(h, dp, batch, tokens, positions, kv_cache, logits, next_tokens, next_positions, sc, n_steps,
-                     stream);
+  rc = launch_with(h, dp, batch, tokens, positions, kv_cache, logits, next_tokens, next_positions, sc, n_steps,
+                   stream);
+  if (rc != MK_OK) {
+    // nothing was enqueued, so the counters did not move: the next launch
+    // must wait for the same targets as this one would have
+    dp->epoch -= n_steps;
+    if (next_tokens) dp->greedy_epoch -= n_steps;
+  }
+  return rc;
 }
 
 int mk_decode_step(mk_handle *h, int32_t batch, const int32_t *tokens, const int32_t *positions, void *kv_cache,
