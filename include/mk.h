@@ -319,6 +319,10 @@ typedef struct mk_unit_info {
   int32_t n_items;  /* output rows (items) of the unit                               */
   int32_t ipw;      /* pieces (rows) per item: 2 for RoPE pairs and gate/up          */
   int32_t wait_n;   /* counter groups it waits on                                    */
+  int32_t b;        /* sequence (attention and reduction units; 0 otherwise)          */
+  int32_t aux0;     /* attention and reduction units: KV head                         */
+  int32_t aux1;     /* attention units: KV split (positions [aux1*split_len, ...))    */
+  int32_t split_len;/* KV positions per split (the plan's; the same for every unit)   */
 } mk_unit_info;
 
 /* mk_plan_units -- the schedule mk_plan_check builds for (cfg, batch) on
@@ -413,7 +417,7 @@ size_t mk_stream_read_sink_words(void);
  * mk_plan_report.paged_kv and .down_splits, 105 mk_decode_steps_greedy,
  * 106 mk_addr_check_launch, 107 mk_plan_units, 108 size limits that keep
  * every descriptor field in range (mk_create and mk_plan_check refuse
- * larger shapes). */
+ * larger shapes), 109 mk_unit_info.b, .aux0, .aux1 and .split_len. */
 int mk_version(void);
 
 #ifdef __cplusplus

@@ -83,7 +83,8 @@ class MkPlanReport(C.Structure):
 class MkUnitInfo(C.Structure):
     _fields_ = [("op", C.c_int32), ("layer", C.c_int32), ("nk", C.c_int32),
                 ("pages", C.c_int32), ("ppp", C.c_int32), ("n_items", C.c_int32),
-                ("ipw", C.c_int32), ("wait_n", C.c_int32)]
+                ("ipw", C.c_int32), ("wait_n", C.c_int32), ("b", C.c_int32),
+                ("aux0", C.c_int32), ("aux1", C.c_int32), ("split_len", C.c_int32)]
 
 
 class MkAddrReport(C.Structure):

@@ -137,7 +137,7 @@ struct mk_handle {
 
 extern "C" {
 
-int mk_version(void) { return 108; }
+int mk_version(void) { return 109; }
 
 const char *mk_strerror(int code) {
   switch (code) {
@@ -180,6 +180,11 @@ int mk_plan_units(const mk_config *cfg, int32_t batch, int32_t num_cus, mk_unit_
     u.n_items = (int32_t)in.n_items;
     u.ipw = in.ipw;
     u.wait_n = (int32_t)in.wait_n;
+    const bool kv_unit = in.op == OP_ATTN || in.op == OP_RED;
+    u.b = kv_unit ? (int32_t)in.b : 0;
+    u.aux0 = kv_unit ? (int32_t)in.aux0 : 0;
+    u.aux1 = in.op == OP_ATTN ? (int32_t)in.aux1 : 0;
+    u.split_len = plan.split_len;
   }
   return n;
 }

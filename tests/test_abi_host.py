@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert B.lib().mk_version() == 108
+    assert B.lib().mk_version() == 109
     for code in (0, -1, -2, -3, -4, -5, -6, -10, -11, -12, -99):
         assert len(B.strerror(code)) > 0
 

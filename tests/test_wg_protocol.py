@@ -16,9 +16,10 @@ from persistent_interpreter_amd import binding as B, synth
 CUS = 256
 
 
-def _queues(name, batch=1):
+def _queues(name, batch=1, splits=0):
     mc = synth.CONFIGS[name]
-    units, q = B.plan_units(B.make_config(mc, max_batch=max(batch, mc.batch)), batch, CUS)
+    cfg = B.make_config(mc, max_batch=max(batch, mc.batch), kv_splits=splits)
+    units, q = B.plan_units(cfg, batch, CUS)
     return [units[q[c]:q[c + 1]] for c in range(CUS) if q[c + 1] > q[c]]
 
 
@@ -33,6 +34,21 @@ def test_plan_units_matches_the_report():
     assert ops == {W.OP_QKV, W.OP_ATTN, W.OP_RED, W.OP_O, W.OP_FFN, W.OP_DOWN, W.OP_LM}
 
 
+def test_plan_units_name_every_attention_split():
+    """Attention units carry (sequence, KV head, split) and the split length:
+    one unit per combination and layer, splits covering the cache."""
+    mc = synth.CONFIGS["llama1b_b8"]
+    cfg = B.make_config(mc, max_batch=8)
+    units, _ = B.plan_units(cfg, 8, CUS)
+    rc, rep = B.plan_check(cfg, 8, CUS)
+    at = [(u.layer, u.b, u.aux0, u.aux1) for u in units if u.op == W.OP_ATTN]
+    want = {(l, b, g, s) for l in range(mc.n_layers) for b in range(8)
+            for g in range(mc.n_kv_heads) for s in range(rep.kv_splits)}
+    assert len(at) == len(want) and set(at) == want
+    sl = {u.split_len for u in units}
+    assert len(sl) == 1 and sl.pop() * rep.kv_splits >= mc.max_seq
+
+
 @pytest.mark.parametrize("name", ["tiny", "llama1b"])
 def test_queues_run_clean(name):
     """Every tiny queue and a spread of Llama-1B queues (first, middle,
@@ -41,7 +57,7 @@ def test_queues_run_clean(name):
     qs = _queues(name)
     pick = qs if name == "tiny" else [qs[i] for i in (0, 1, 63, 128, 191, len(qs) - 1)]
     for i, qu in enumerate(pick):
-        for seed in range(3):
+        for seed in range(2):
             W.simulate(qu, seed=seed * 1000 + i)
 
 
@@ -117,3 +133,53 @@ def test_batched_planted_protocol_errors_are_caught(name, batch, knob, what):
             break
     assert caught, f"{knob} was not caught on {name} batch {batch}"
     assert any(w in caught[0] for w in what), caught[0]
+
+
+# ---- paged attention: K/V pages through the ring, q and the merge partials
+# in the unit's activation slot, two cumulative LDS counters
+
+PAGED = [("tiny_qk", 1, 0), ("qwen3_8b", 1, 0), ("llama1b", 1, 1), ("llama1b", 1, 4),
+         ("llama1b_b8", 8, 0)]
+
+
+def _paged_queues(name, batch, splits):
+    mc = synth.CONFIGS[name]
+    pos = [int(p) for p in synth.make_positions(mc, batch)]
+    qs = [qu for qu in _queues(name, batch, splits) if any(u.op == W.OP_ATTN and u.ppp for u in qu)]
+    assert qs, "the plan has no paged attention"
+    pages = [sum(W.attn_geom(u, pos[u.b])[0] for u in qu if u.op == W.OP_ATTN and u.ppp) for qu in qs]
+    return qs, pages, (pos, mc.n_q_heads // mc.n_kv_heads)
+
+
+@pytest.mark.parametrize("name,batch,splits", PAGED)
+def test_paged_attention_queues_run_clean(name, batch, splits):
+    """Queues with the most and the fewest K/V pages (Llama-1B on one and on
+    four splits per KV head, so that its attention is paged too)."""
+    qs, pages, attn = _paged_queues(name, batch, splits)
+    sim = W.simulate if batch == 1 else W.simulate_batched
+    pick = {max(range(len(qs)), key=pages.__getitem__), min(range(len(qs)), key=pages.__getitem__)}
+    for i in sorted(pick):
+        sim(qs[i], seed=i, attn=attn)
+
+
+@pytest.mark.parametrize("name,batch,splits,knob,what", [
+    ("llama1b", 1, 4, "no_aq_wait", "reads q"),
+    ("llama1b", 1, 4, "no_am_wait", "merges partial"),
+    ("qwen3_8b", 1, 0, "no_aq_wait", "reads q"),
+    ("llama1b_b8", 8, 0, "no_aq_wait", "reads q"),
+    ("llama1b_b8", 8, 0, "no_am_wait", "merges partial"),
+])
+def test_paged_attention_planted_errors_are_caught(name, batch, splits, knob, what):
+    """A head's other waves reading q without waiting for it, or its first
+    wave merging without waiting for the partials."""
+    qs, pages, attn = _paged_queues(name, batch, splits)
+    qu = qs[max(range(len(qs)), key=pages.__getitem__)]
+    sim = W.simulate if batch == 1 else W.simulate_batched
+    caught = []
+    for seed in range(8):
+        try:
+            sim(qu, seed=seed, attn=attn, knobs=(knob,), budget=3_000_000)
+        except W.ProtocolError as e:
+            caught.append(str(e))
+            break
+    assert caught and what in caught[0], caught

@@ -23,6 +23,16 @@ arithmetic):
   activation slot, and counts itself done; the last wave to do so runs the
   epilogue and frees the slot.
 
+With `attn` (the positions of the step and the query heads per KV head),
+attention units of paged plans stream their K/V rows through the same ring
+(pages counted from the unit's split and the position), and their compute
+waves follow the paged attention body: the first wave of each head writes
+the head's q into the unit's activation slot and counts itself on a
+cumulative LDS counter that the head's other waves wait on; each wave reads
+pages rp, rp + WPH, ... of the unit (WPH waves per head); the other waves
+leave their partial (m, l, o) in the slot and count themselves on a second
+cumulative counter, which the first wave waits on before merging.
+
 Checks: no deadlock; a page is read only from the slot it landed in and is
 not replaced before the wave's read ends; an activation piece read is the
 one for that unit and piece; a result slot is written only by its own unit
@@ -44,11 +54,107 @@ class ProtocolError(AssertionError):
     pass
 
 
+def attn_geom(u, p: int):
+    """(K/V pages, whether the split holds any row) of a paged attention
+    unit at position p: rows [lo, min(lo + split_len, p + 1)) of which those
+    before p come from the cache, ppp rows per page."""
+    lo = u.aux1 * u.split_len
+    hi = min(lo + u.split_len, p + 1)
+    nr = max(0, min(hi, p) - lo)
+    return (nr + u.ppp - 1) // u.ppp, lo < hi
+
+
+def paged(u, attn) -> bool:
+    return attn is not None and u.op == OP_ATTN and u.ppp > 0
+
+
+class _Attn:
+    """LDS state of the paged attention body shared by a workgroup's
+    compute waves: the two cumulative counters, which unit's q (per head)
+    and partials (per head and wave) each activation slot holds."""
+
+    def __init__(self, group: int, knobs):
+        self.G = group
+        self.WPH = NCW // group
+        self.aq = 0
+        self.am = 0
+        self.q = {}      # (slot, head) -> unit
+        self.mg = {}     # (slot, head, rp) -> unit
+        self.tgt = [[0, 0] for _ in range(NCW)]   # each wave's running targets
+        self.no_aq_wait = "no_aq_wait" in knobs
+        self.no_am_wait = "no_am_wait" in knobs
+
+    def clobber(self, slot, by):
+        """Another unit's activation piece is written into the slot."""
+        for k in [k for k in self.q if k[0] == slot]:
+            self.q[k] = ("overwritten by", by)
+        for k in [k for k in self.mg if k[0] == slot]:
+            self.mg[k] = ("overwritten by", by)
+
+    def wave(self, sim, cw, vq, u, n, seq, np_, rows, nxs):
+        """Compute wave cw through a paged attention unit whose pages start
+        at stream index n (a generator, like the waves)."""
+        G, WPH = self.G, self.WPH
+        h, rp = cw % G, cw // G
+        self.tgt[cw][0] += G
+        self.tgt[cw][1] += G * (WPH - 1)
+        while not sim.st["xready"] > seq:
+            yield 0
+        slot = seq % nxs
+        if rp == 0:
+            if rows:
+                self.q[(slot, h)] = vq
+                yield 1
+            self.aq += 1
+        elif not self.no_aq_wait:
+            while not self.aq >= self.tgt[cw][0]:
+                yield 0
+        rel = n
+        for jp in range(rp, np_, WPH):
+            pg = n + jp
+            if pg > rel:
+                sim.cons[cw] = pg
+                rel = pg
+            while sim.sent[pg % sim.P] != pg:
+                yield 0
+            if self.q.get((slot, h)) != vq:
+                sim.err(f"wave {cw} reads q of head {h} for unit {vq} from slot {slot} holding "
+                        f"{self.q.get((slot, h))}")
+            sim.read_page(pg, cw)
+            yield 1
+            sim.read_page(pg, cw)
+        if WPH > 1:
+            if rp > 0:
+                self.mg[(slot, h, rp)] = vq
+                yield 1
+                self.am += 1
+            else:
+                if not self.no_am_wait:
+                    while not self.am >= self.tgt[cw][1]:
+                        yield 0
+                for r in range(1, WPH):
+                    got = self.mg.get((slot, h, r))
+                    if got != vq:
+                        sim.err(f"wave {cw} merges partial {r} of head {h} for unit {vq} "
+                                f"from slot {slot} holding {got}")
+                yield 1
+        sim.cons[cw] = n + np_
+
+
+class _Sim:
+    """What the attention body needs of a model's state."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
 def simulate(units, seed: int, ring_pages: int = 8, nxs: int = 2, depth: int = 3,
-             stall_p: float = 0.01, max_stall: int = 2000, knobs=(), budget: int = 20_000_000):
+             stall_p: float = 0.01, max_stall: int = 2000, knobs=(), budget: int = 20_000_000,
+             attn=None):
     """Run one workgroup's queue (a list of mk_unit_info) once; raises
     ProtocolError on a violated check.  Returns the number of scheduler
-    steps taken."""
+    steps taken.  attn = (positions, query heads per KV head) models the
+    K/V pages of paged attention units (None: they carry no pages)."""
     rng = random.Random(seed)
     P = ring_pages
     early_slot = "early_slot" in knobs
@@ -65,6 +171,8 @@ def simulate(units, seed: int, ring_pages: int = 8, nxs: int = 2, depth: int = 3
     acc = [None] * ACC     # owning unit
     epis = [0] * len(units)
     now = [0]
+    geo = [attn_geom(u, attn[0][u.b]) if paged(u, attn) else (0, False) for u in units]
+    att = _Attn(attn[1], knobs) if attn is not None else None
 
     def err(msg):
         raise ProtocolError(msg)
@@ -72,14 +180,21 @@ def simulate(units, seed: int, ring_pages: int = 8, nxs: int = 2, depth: int = 3
     def nx_of(u):
         return u.nk if u.op in GEMV else 1
 
-    def pages_of(u):
-        return u.pages if u.op in GEMV else 0
+    def pages_of(vq):
+        u = units[vq]
+        return u.pages if u.op in GEMV else geo[vq][0]
+
+    def read_page(pg, cw):
+        if ring[pg % P] != pg:
+            err(f"page {pg} read from slot {pg % P} holding {ring[pg % P]}")
+
+    sim = _Sim(st=None, cons=cons, sent=sent, P=P, err=err, read_page=read_page)
 
     def loader(lw):
         n = 0
         for vq, u in enumerate(units):
             yield 1
-            for _ in range(pages_of(u)):
+            for _ in range(pages_of(vq)):
                 if n % NLW == lw:
                     lag = P + 1 if early_slot else P
                     while not (n < P or min(cons) >= n - lag + 1):
@@ -114,8 +229,11 @@ def simulate(units, seed: int, ring_pages: int = 8, nxs: int = 2, depth: int = 3
                 need = s - nxs + (0 if early_xs else 1)
                 while not (s < nxs or min(xcons) >= need):
                     yield 0
-                xs[s % nxs] = (vq, k)
-                yield 1
+                if u.op in GEMV:     # (an attention unit's slot is its compute waves')
+                    xs[s % nxs] = (vq, k)
+                    if att:
+                        att.clobber(s % nxs, vq)
+                    yield 1
                 st["xready"] = s + 1
             seq += nx_of(u)
 
@@ -124,9 +242,11 @@ def simulate(units, seed: int, ring_pages: int = 8, nxs: int = 2, depth: int = 3
         seq = 0
         for vq, u in enumerate(units):
             yield 1
+            a = vq % ACC
+            if paged(u, attn):
+                yield from att.wave(sim, cw, vq, u, n, seq, geo[vq][0], geo[vq][1], nxs)
             while not st["xready"] > seq:
                 yield 0
-            a = vq % ACC
             if u.op in GEMV:
                 per = u.n_items * u.ipw
                 rel = n
@@ -151,16 +271,15 @@ def simulate(units, seed: int, ring_pages: int = 8, nxs: int = 2, depth: int = 3
                             rel = pg
                         while sent[pg % P] != pg:
                             yield 0
-                        if ring[pg % P] != pg:
-                            err(f"page {pg} read from slot {pg % P} holding {ring[pg % P]}")
+                        read_page(pg, cw)
                         yield 1
                         if ring[pg % P] != pg:
                             err(f"page {pg} replaced in slot {pg % P} during its read")
                         if acc[a] not in (None, vq):
                             err(f"wave {cw} writes unit {vq} into result slot {a} held by unit {acc[a]}")
                         acc[a] = vq
-                cons[cw] = n + pages_of(u)
-            n += pages_of(u)
+                cons[cw] = n + pages_of(vq)
+            n += pages_of(vq)
             seq += nx_of(u)
             xcons[cw] = seq
             yield 1
@@ -175,6 +294,7 @@ def simulate(units, seed: int, ring_pages: int = 8, nxs: int = 2, depth: int = 3
                 done[a] = 0
                 st["epi"] = vq + 1
 
+    sim.st = st
     waves = [loader(i) for i in range(NLW)] + [sync()] + [compute(i) for i in range(NCW)]
     alive = list(range(len(waves)))
     asleep = [0] * len(waves)
@@ -210,7 +330,7 @@ def simulate(units, seed: int, ring_pages: int = 8, nxs: int = 2, depth: int = 3
 
 def simulate_batched(units, seed: int, ring_pages: int = 6, nxs: int = 4, inflight_pieces: int = 3,
                      depth: int = 3, stall_p: float = 0.01, max_stall: int = 2000, knobs=(),
-                     budget: int = 20_000_000):
+                     budget: int = 20_000_000, attn=None):
     """The same for the batched (MFMA) kernel.  Its protocol differs in the
     sync wave, which keeps up to three activation pieces of a unit in
     flight (each waits for its slot of four, lands in order and is then
@@ -219,10 +339,10 @@ def simulate_batched(units, seed: int, ring_pages: int = 6, nxs: int = 4, inflig
     steps kg, kg + nwt, ...; wide LM units: whole tiles cw, cw + 8, ...);
     and in the partial-tile buffer of each unit (two, alternating), which
     its waves fill after their K steps once the unit two before has run its
-    epilogue, and which that epilogue sums.  Attention units carry no pages
-    here (paged attention's K/V stream is not modelled).  Knobs as
-    `simulate`, plus "no_part_guard" (waves fill the partial-tile buffer
-    without waiting)."""
+    epilogue, and which that epilogue sums.  Paged attention (`attn`) as in
+    `simulate`, each sequence at its own position.  Knobs as `simulate`,
+    plus "no_part_guard" (waves fill the partial-tile buffer without
+    waiting)."""
     rng = random.Random(seed)
     P = ring_pages
     early_slot = "early_slot" in knobs
@@ -242,6 +362,8 @@ def simulate_batched(units, seed: int, ring_pages: int = 6, nxs: int = 4, inflig
     part = [None] * 2
     epis = [0] * len(units)
     now = [0]
+    geo = [attn_geom(u, attn[0][u.b]) if paged(u, attn) else (0, False) for u in units]
+    att = _Attn(attn[1], knobs) if attn is not None else None
 
     def err(msg):
         raise ProtocolError(msg)
@@ -252,8 +374,9 @@ def simulate_batched(units, seed: int, ring_pages: int = 6, nxs: int = 4, inflig
     def nx_of(u):
         return u.nk if gv(u) else 1
 
-    def pages_of(u):
-        return u.pages if gv(u) else 0
+    def pages_of(vq):
+        u = units[vq]
+        return u.pages if gv(u) else geo[vq][0]
 
     def wide(u):
         return gv(u) and (u.ppp + 1) // 2 > NCW
@@ -268,7 +391,7 @@ def simulate_batched(units, seed: int, ring_pages: int = 6, nxs: int = 4, inflig
         n = 0
         for vq, u in enumerate(units):
             yield 1
-            for _ in range(pages_of(u)):
+            for _ in range(pages_of(vq)):
                 if n % NLW == lw:
                     lag = P + 1 if early_slot else P
                     while not (n < P or min(cons) >= n - lag + 1):
@@ -309,6 +432,8 @@ def simulate_batched(units, seed: int, ring_pages: int = 6, nxs: int = 4, inflig
                     while not (s < nxs or min(xcons) >= need):
                         yield 0
                     xs[s % nxs] = ("loading", vq, issued)
+                    if att:
+                        att.clobber(s % nxs, vq)
                     if issued == 0 and u.op in (OP_O, OP_DOWN):
                         take_acc(vq, "sync (residual rows)")
                     t = now[0] + rng.randint(1, 40)
@@ -331,6 +456,8 @@ def simulate_batched(units, seed: int, ring_pages: int = 6, nxs: int = 4, inflig
         if ring[pg % P] != pg:
             err(f"wave {cw} reads page {pg} from slot {pg % P} holding {ring[pg % P]}")
 
+    sim = _Sim(st=st, cons=cons, sent=sent, P=P, err=err, read_page=read_page)
+
     def read_piece(vq, k, seq, cw):
         got = xs[(seq + k) % nxs]
         if got != (vq, k):
@@ -341,7 +468,9 @@ def simulate_batched(units, seed: int, ring_pages: int = 6, nxs: int = 4, inflig
         seq = 0
         for vq, u in enumerate(units):
             yield 1
-            if not gv(u):
+            if paged(u, attn):
+                yield from att.wave(sim, cw, vq, u, n, seq, geo[vq][0], geo[vq][1], nxs)
+            elif not gv(u):
                 while not st["xready"] > seq:
                     yield 0
             else:
@@ -416,8 +545,8 @@ def simulate_batched(units, seed: int, ring_pages: int = 6, nxs: int = 4, inflig
                     if part[vq % 2] not in (None, vq):
                         err(f"wave {cw} writes its partial tile of unit {vq} over unit {part[vq % 2]}")
                     part[vq % 2] = vq
-                cons[cw] = n + pages_of(u)
-            n += pages_of(u)
+                cons[cw] = n + pages_of(vq)
+            n += pages_of(vq)
             seq += nx_of(u)
             xcons[cw] = seq
             yield 1
