@@ -183,3 +183,39 @@ def test_paged_attention_planted_errors_are_caught(name, batch, splits, knob, wh
             caught.append(str(e))
             break
     assert caught and what in caught[0], caught
+
+
+# ---- several steps per launch: what orders step s's K/V rows before step
+# s + 1 reads them
+
+def _qkv_without_later_wait(name, batch):
+    """Workgroups holding a QKV unit after which no attention or reduction
+    unit follows in their queue (at the end of those units every compute
+    wave waits for its stores before counting itself done)."""
+    mc = synth.CONFIGS[name]
+    units, q = B.plan_units(B.make_config(mc, max_batch=max(batch, mc.batch)), batch, CUS)
+    bad = 0
+    for c in range(CUS):
+        qu = units[q[c]:q[c + 1]]
+        last = max([i for i, u in enumerate(qu) if u.op == W.OP_QKV], default=-1)
+        if last >= 0 and not any(u.op in (W.OP_ATTN, W.OP_RED) for u in qu[last + 1:]):
+            bad += 1
+    return bad
+
+
+@pytest.mark.parametrize("name,batch", [("llama1b", 1), ("llama1b_b8", 8), ("qwen3_8b", 1)])
+def test_kv_stores_acknowledged_before_the_finisher(name, batch):
+    """In these schedules every workgroup's QKV units are followed by an
+    attention or reduction unit, so a QKV epilogue's K/V stores are
+    acknowledged before a signal that leads to the LM head and the step's
+    finisher, whose token counter the next step of the launch waits on."""
+    assert _qkv_without_later_wait(name, batch) == 0
+
+
+def test_tiny_schedules_leave_the_kv_ordering_to_timing():
+    """The tiny shape has 6 attention units a layer for 256 workgroups: most
+    workgroups never wait for their QKV epilogue's stores within the step
+    (the ordering there rests on the rest of the step outlasting a store's
+    acknowledgement).  Recorded so that a change of the planner or of the
+    kernel's waits shows here."""
+    assert _qkv_without_later_wait("tiny", 1) > 200
