@@ -241,9 +241,10 @@ def main():
                          "scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU "
-              "path (batched configs shard as independent replicas, see "
-              "DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: there is no multi-GPU path "
+              "(batched workloads would shard as independent replicas, one per "
+              "GPU, with no exchange; batch 1 would need tensor parallelism)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
