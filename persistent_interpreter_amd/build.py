@@ -42,9 +42,39 @@ def _run(cmd):
     return out
 
 
+def parse_resource_usage(text: str) -> dict:
+    """The compiler's per-kernel resource remarks (VGPRs, AGPRs, SGPRs,
+    spills, scratch bytes per lane, occupancy in waves per SIMD, static LDS)
+    as {kernel: {field: int}}, kernels named as in the source
+    (``mk_interp<false>`` ...)."""
+    import re
+    res, cur = {}, None
+    for line in text.splitlines():
+        m = re.search(r"remark: (.*?) \[-Rpass-analysis=kernel-resource-usage\]", line)
+        if not m:
+            continue
+        t = m.group(1).strip()
+        if t.startswith("Function Name:"):
+            mangled = t.split(":", 1)[1].strip()
+            k = re.match(r"_ZN2mk(\d+)(\w+)", mangled)
+            name = k.group(2)[:int(k.group(1))] if k else mangled
+            tpl = re.match(r"_ZN2mk\d+\w+?ILb([01])EE", mangled)
+            if tpl:
+                name += "<true>" if tpl.group(1) == "1" else "<false>"
+            cur = res.setdefault(name, {})
+        elif cur is not None and ":" in t:
+            key, val = t.split(":", 1)
+            try:
+                cur[key.strip()] = int(val.strip())
+            except ValueError:
+                cur[key.strip()] = val.strip()
+    return res
+
+
 def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     """Compile every source and link the library; returns its path.
-    ``defines`` (e.g. ``["MK_SDEPTH=2"]``) override compile-time knobs."""
+    ``defines`` (e.g. ``["MK_SDEPTH=2"]``) override compile-time knobs.
+    The kernels' resource usage goes to ``<stem>_resources.json`` beside it."""
     out_dir = os.path.dirname(out)
     os.makedirs(out_dir, exist_ok=True)
     dflags = [f"-D{d}" for d in defines]
@@ -52,7 +82,12 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     stem = os.path.splitext(os.path.basename(out))[0]
     for src in ("mk_kernel.hip", "mk_probe.hip"):
         o = os.path.join(out_dir, f"{stem}_" + src.replace(".hip", ".o"))
-        _run([HIPCC, *DEVICE_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", o])
+        remarks = ["-Rpass-analysis=kernel-resource-usage"] if src == "mk_kernel.hip" else []
+        text = _run([HIPCC, *DEVICE_FLAGS, *remarks, *dflags, "-c", os.path.join(CSRC, src), "-o", o])
+        if remarks:
+            import json
+            with open(os.path.join(out_dir, f"{stem}_resources.json"), "w") as f:
+                json.dump(parse_resource_usage(text), f, indent=1, sort_keys=True)
         objs.append(o)
     for src in ("mk_sched.cpp", "mk_abi.cpp", "mk_addr.cpp"):
         o = os.path.join(out_dir, f"{stem}_" + src.replace(".cpp", ".o"))
