@@ -80,10 +80,12 @@ def test_bad_arguments():
 
 
 @pytest.mark.parametrize("name,batch,steps", [("tiny", 1, 12), ("tiny_qk", 1, 8), ("tiny", 3, 8),
-                                              ("tiny", 8, 4), ("llama1b", 1, 2)])
+                                              ("tiny", 8, 4), ("llama1b", 1, 2), ("qwen3_8b", 1, 2),
+                                              ("llama1b_b8", 8, 8)])
 def test_one_launch_of_several_steps_in_bounds(name, batch, steps):
     """mk_decode_steps_greedy: the steps as one launch (logits row block per
-    step, in-launch tokens, the token counter, positions + s)."""
+    step, in-launch tokens, the token counter, positions + s); Llama-1B at
+    batch 8 with 8 steps a launch is the benchmark's own launch."""
     mc = synth.CONFIGS[name]
     if batch > 1 and mc.batch != batch:
         mc = mc.replace(batch=batch, pos_lo=4, pos_hi=40)
