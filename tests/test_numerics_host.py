@@ -1,5 +1,7 @@
-"""The arithmetic arguments behind the batched path's tolerance, checked on
-the CPU: each fp32 activation x enters the matrix cores as two bf16 terms,
+"""The arithmetic arguments behind the K/V parity tolerances, checked on the
+CPU.  Batch 1: the GPU and the oracle add the same fp32 products in
+different orders.  Batched: each fp32 activation x enters the matrix cores
+as two bf16 terms,
 hi = bf16(x) and lo = bf16(x - hi) (round to nearest even, the bf16
 multi-term split of Henry, Tang and Heinecke, 2019).
 
@@ -60,3 +62,41 @@ def test_projection_error_within_the_parity_bar(K):
     assert np.all(d <= 2.0 ** -16 * (np.abs(W) @ np.abs(x.astype(np.float64))))   # hard bound
     rms = np.sqrt(np.mean(y * y))
     assert d.max() <= 2 * 2.0 ** -16 * np.sqrt(K) * rms                        # the parity bar
+
+
+def _fp32_seq(W, x):
+    """Row sums accumulated in fp32 one product after another."""
+    acc = np.zeros(W.shape[0], np.float32)
+    for k in range(W.shape[1]):
+        acc = (acc + (W[:, k] * x[k]).astype(np.float32)).astype(np.float32)
+    return acc
+
+
+def _fp32_lanes(W, x, lanes=64):
+    """The same sums in a GEMV kernel's order: lane l accumulates products
+    l, l + 64, ... in fp32, then the 64 partials are added pairwise."""
+    K = W.shape[1]
+    p = np.zeros((W.shape[0], lanes), np.float32)
+    for k0 in range(0, K, lanes):
+        blk = (W[:, k0:k0 + lanes] * x[k0:k0 + lanes]).astype(np.float32)
+        p[:, :blk.shape[1]] = (p[:, :blk.shape[1]] + blk).astype(np.float32)
+    while p.shape[1] > 1:
+        h = p.shape[1] // 2
+        p = (p[:, :h] + p[:, h:]).astype(np.float32)
+    return p[:, 0]
+
+
+@pytest.mark.parametrize("K", [256, 2048])
+def test_fp32_summation_orders_within_the_batch1_bar(K):
+    """The batch-1 K/V bar's slack, 2^-20 sqrt(K) times the outputs' RMS,
+    covers two fp32 summation orders of the same products (about
+    2^-24 sqrt(K) RMS apart for random signs)."""
+    rng = np.random.default_rng(K + 1)
+    W = _bf16(rng.standard_normal((256, K)).astype(np.float32) * 0.02)
+    x = rng.standard_normal(K).astype(np.float32)
+    a, b = _fp32_seq(W, x), _fp32_lanes(W, x)
+    y = W.astype(np.float64) @ x.astype(np.float64)
+    rms = np.sqrt(np.mean(y * y))
+    d = np.abs(a.astype(np.float64) - b.astype(np.float64))
+    assert d.max() > 0                                   # the orders do differ
+    assert d.max() <= 2.0 ** -20 * np.sqrt(K) * rms
