@@ -2,8 +2,8 @@
  * mk.h -- C ABI of the persistent decode megakernel for MI355X (gfx950).
  *
  * One call of mk_decode_step runs one decode step of a Llama-style decoder
- * (every layer, then the LM head) in ONE persistent kernel launch per
- * sequence of the batch (a batch-1 step is a single launch).  The method is the GPU interpreter of the megakernel chapter
+ * (every layer, then the LM head) for 1 to 8 sequences in ONE persistent
+ * kernel launch.  The method is the GPU interpreter of the megakernel chapter
  * "L'interpréteur sur GPU": each compute unit's workgroup runs a queue of
  * instructions that the host scheduled before launch (section 3.2), drawn
  * from seven fused instructions (table of section 3.2): RMSNorm + QKV + RoPE,
