@@ -188,7 +188,13 @@ int mk_decode_step_greedy(mk_handle *h, int32_t batch, const int32_t *tokens,
  * step on a device counter, and the next step's workgroups start once it
  * has.
  * The results equal those of n_steps chained mk_decode_step_greedy calls
- * bit for bit.
+ * bit for bit.  Ordering between the steps of a launch: step s + 1 reads
+ * the K/V rows step s wrote only after step s's token counter moved; the
+ * stores of those rows are acknowledged before that counter moves where
+ * every workgroup runs an attention or reduction unit after its QKV units
+ * (the Llama-1B and Qwen3-8B schedules on 256 CUs); in schedules with fewer
+ * attention units than workgroups, what orders them is the rest of the step
+ * outlasting a store's acknowledgement, not a wait.
  *   n_steps        : 1 .. 65536.
  *   tokens         : device int32 [batch], the tokens of the first step.
  *   positions      : device int32 [batch], the first step's KV slots; step s
