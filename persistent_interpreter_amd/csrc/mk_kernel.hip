@@ -134,10 +134,10 @@ __device__ __forceinline__ uint16_t ldc16(rsrc_t r, uint32_t off) {
 }
 
 // Tagged activation words: value in the low half, the step's tag in the
-// high half, written as one 64-bit store.  A producer stores them and
-// signals its counter without waiting for the stores to be acknowledged;
-// a consumer that found the counter complete re-reads any word whose tag
-// is not yet this step's.
+// high half, written as one 64-bit store.  Each word is its own flag: the
+// producer (a QKV epilogue: q and the new K/V slot) stores them with no
+// counter and no wait for their acknowledgement, and a consumer re-reads any
+// word whose tag is not yet this step's.
 __device__ __forceinline__ void st_tag(uint64_t *p, float v, uint32_t tag) {
   __hip_atomic_store(G(p), ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
@@ -194,7 +194,9 @@ __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" :
 // it from moving a later plain (buffer) load above the poll, so every poll
 // exit is a compiler fence.  MK_ACQ=1 adds the memory model's own agent-scope
 // acquire fence at every poll exit and a release fence before every counter
-// increment (measured cost in the design notes).
+// increment (measured on the Llama-1B shape at batch 1: 1855 us a step
+// against 903 us, the fences writing back and invalidating caches at every
+// hop).
 #ifndef MK_ACQ
 #define MK_ACQ 0
 #endif
