@@ -511,8 +511,8 @@ static_assert(kSentDepth >= 1 && 17 * kSentDepth <= 63, "load counter range");
 // free ring slot (compute waves' releases) and, to bound its load counter,
 // for its oldest page once kSentDepth are in flight.
 // A later step of a launch streams K/V pages only once the sync wave has
-// seen the step's tokens counted (L_TOKOK): rows that earlier steps of the
-// launch wrote are then complete.  Weight pages need no such wait.
+// seen the step's tokens counted (L_TOKOK; see wait_tokens for what that
+// orders).  Weight pages need no such wait.
 __device__ __forceinline__ bool loader_tok_gate(const Env &e, bool &tok_ok, uint32_t qi) {
   if (tok_ok) return true;
   Watchdog wd;
@@ -703,8 +703,13 @@ __device__ __forceinline__ int32_t ld_tok(const Args &a, int b) {
 // Step s > 0 of a launch reads the tokens step s - 1 chose: wait until its
 // finisher has counted them (the token counter reaches tok_base + s).  The
 // finisher ran after every unit of step s - 1, so this wait also orders the
-// K/V rows that step wrote before their reads in this step; L_TOKOK tells
-// the workgroup's other waves.
+// K/V rows that step wrote before their reads in this step, provided their
+// stores were acknowledged before some signal on the way to the finisher: a
+// QKV epilogue does not wait for its stores (no counter follows it), and its
+// wave acknowledges them at the end of its next attention or reduction unit,
+// which every workgroup of the Llama-1B and Qwen3-8B schedules has; where a
+// workgroup has none, the rest of the step outlasting the stores is what
+// orders them.  L_TOKOK tells the workgroup's other waves.
 __device__ __forceinline__ bool wait_tokens(const Env &e, const Args &a) {
   if (a.step_off == 0) return true;
   const uint32_t *tc = a.amax_ctr + kTokWord;
