@@ -2109,7 +2109,7 @@ __device__ __forceinline__ void wait_vm_le(uint32_t n) { wait_vm_sel<(kInflB - 1
 
 // The batched sync wave.  For each GEMV unit it copies the activation pieces
 // (fp32 rows of every sequence, and the norm weights of normed units)
-// global -> LDS with direct-to-LDS loads, two pieces in flight, and
+// global -> LDS with direct-to-LDS loads, kInflB pieces in flight, and
 // publishes each piece once it has landed.  RMSNorm's scale 1/rms is a
 // factor per sequence, so the product runs on the unnormalised h (times the
 // norm weight) and the epilogue applies the factor: W (rs * h * w) =
