@@ -194,3 +194,27 @@ def test_head_dim_128_shapes_plan(name):
     cfg = B.make_config(synth.CONFIGS[name], max_batch=1)
     rc, rep = B.plan_check(cfg, 1, 256, sim_runs=2)
     assert rc == B.MK_OK, rep.msg
+
+
+def _declared_params():
+    """name -> number of parameters, from the declarations in include/mk.h."""
+    src = open(os.path.join(ROOT, "include", "mk.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(mk_[a-z_]+)\s*\(([^;{]*?)\)\s*;", src, flags=re.S):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_signatures_match_the_header():
+    """Every entry point is called through a ctypes prototype with as many
+    arguments as the header declares (a missing prototype would pass 64-bit
+    pointers as 32-bit ints)."""
+    L = B.lib()
+    decl = _declared_params()
+    assert set(decl) == set(B.EXPORTED)
+    for name, n in decl.items():
+        f = getattr(L, name)
+        assert f.argtypes is not None, name
+        assert len(f.argtypes) == n, (name, len(f.argtypes), n)
