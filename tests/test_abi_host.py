@@ -197,24 +197,35 @@ def test_head_dim_128_shapes_plan(name):
 
 
 def _declared_params():
-    """name -> number of parameters, from the declarations in include/mk.h."""
+    """name -> parameter declarations, from include/mk.h."""
     src = open(os.path.join(ROOT, "include", "mk.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     out = {}
     for m in re.finditer(r"\b(mk_[a-z_]+)\s*\(([^;{]*?)\)\s*;", src, flags=re.S):
         params = m.group(2).strip()
-        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+        out[m.group(1)] = [] if params in ("", "void") else [" ".join(p.split()) for p in params.split(",")]
     return out
 
 
+_SCALARS = {"int32_t": (4, True), "int": (4, True), "uint32_t": (4, False),
+            "uint64_t": (8, False), "size_t": (8, False)}
+
+
 def test_binding_signatures_match_the_header():
-    """Every entry point is called through a ctypes prototype with as many
-    arguments as the header declares (a missing prototype would pass 64-bit
-    pointers as 32-bit ints)."""
+    """Every entry point is called through a ctypes prototype that matches
+    the header argument by argument: pointers as pointers, integers with the
+    declared width and signedness (a missing or short prototype would pass a
+    64-bit pointer as a 32-bit int)."""
     L = B.lib()
     decl = _declared_params()
     assert set(decl) == set(B.EXPORTED)
-    for name, n in decl.items():
+    for name, params in decl.items():
         f = getattr(L, name)
-        assert f.argtypes is not None, name
-        assert len(f.argtypes) == n, (name, len(f.argtypes), n)
+        assert f.argtypes is not None and len(f.argtypes) == len(params), name
+        for p, t in zip(params, f.argtypes):
+            if "*" in p:
+                assert t is C.c_void_p or issubclass(t, C._Pointer), (name, p, t)
+            else:
+                size, signed = _SCALARS[p.split()[0]]
+                assert C.sizeof(t) == size, (name, p, t)
+                assert (t(-1).value < 0) == signed, (name, p, t)
