@@ -2,7 +2,10 @@
 compiles with every warning an error, links against the library, and runs
 the host-only entry points (version, error strings, the plan check, the unit
 listing, the address model, argument checks of the GPU entry points) with no
-GPU and no Python in between."""
+GPU and no Python in between; and every structure it declares has the
+layout (size, each field's offset and size) the binding's ctypes mirror
+assumes."""
+import ctypes as C
 import os
 import shutil
 import subprocess
@@ -83,3 +86,38 @@ def test_header_compiles_as_c99_and_links(tmp_path):
     out = run.stdout
     assert f"version {B.lib().mk_version()}" in out and out.rstrip().endswith("ok")
     assert "sim 0/20" in out
+
+
+STRUCTS = {"mk_config": B.MkConfig, "mk_layer_weights": B.MkLayerWeights, "mk_weights": B.MkWeights,
+           "mk_plan_report": B.MkPlanReport, "mk_unit_info": B.MkUnitInfo,
+           "mk_addr_report": B.MkAddrReport}
+
+
+def test_struct_layouts_match_the_binding(tmp_path):
+    """Every structure the header declares has, field by field, the offset
+    and the size the ctypes mirror in the binding gives it."""
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "mk.h"', "int main(void) {"]
+    for cname, py in STRUCTS.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname}.{f} %zu %zu\\n", offsetof({cname}, {f}), '
+                         f'sizeof((({cname} *)0)->{f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                        "-o", str(exe)], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout
+    got = {}
+    for line in subprocess.run([str(exe)], stdout=subprocess.PIPE, text=True, check=True).stdout.splitlines():
+        key, *vals = line.split()
+        got[key] = tuple(int(v) for v in vals if v.isdigit())
+    for cname, py in STRUCTS.items():
+        assert got[cname] == (C.sizeof(py),), cname
+        for f, _ in py._fields_:
+            d = getattr(py, f)
+            assert got[f"{cname}.{f}"] == (d.offset, d.size), (cname, f)
