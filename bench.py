@@ -144,9 +144,12 @@ def host_info() -> dict:
     return {"cpu_model": model, "ram_gib": ram}
 
 
-def cpu_baseline(mc, W, kv0, tok, pos, fed, gpu_logits, budget_s=20.0):
-    """Time the CPU oracle on the first steps of the same greedy run (teacher
-    forced on the GPU's tokens) and compare its logits with the GPU's."""
+def cpu_baseline(mc, W, kv0, tok, pos, fed, gpu_logits, min_s=10.0, budget_s=30.0):
+    """Time the CPU oracle on the same greedy run (teacher forced on the
+    GPU's tokens) and compare its logits with the GPU's on the first pass.
+    The run is repeated from the same starting cache until at least min_s
+    seconds of oracle steps are timed (stopping at budget_s), so that the
+    rate rests on seconds of CPU work even where the oracle is fast."""
     import oracle as O
     try:
         cores = len(os.sched_getaffinity(0))
@@ -154,25 +157,34 @@ def cpu_baseline(mc, W, kv0, tok, pos, fed, gpu_logits, budget_s=20.0):
         cores = os.cpu_count() or 1
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     Wf = O.upcast_weights(W)            # one-time decode of bf16 weights
-    kv = kv0.copy()
-    times, worst, match = [], 0.0, 0
+    times, worst, match, compared, passes = [], 0.0, 0, 0, 0
     t_all = time.perf_counter()
-    for i in range(len(fed)):
-        t0 = time.perf_counter()
-        ref = O.decode_step(mc, Wf, fed[i], pos + i, kv)
-        times.append(time.perf_counter() - t0)
-        worst = max(worst, float(np.abs(ref - gpu_logits[i]).max()))
-        match += int(np.array_equal(np.argmax(ref, -1), np.argmax(gpu_logits[i], -1)))
-        if time.perf_counter() - t_all > budget_s and i >= 1:
-            break
+    done = False
+    while not done:
+        kv = kv0.copy()
+        for i in range(len(fed)):
+            t0 = time.perf_counter()
+            ref = O.decode_step(mc, Wf, fed[i], pos + i, kv)
+            times.append(time.perf_counter() - t0)
+            if passes == 0:
+                worst = max(worst, float(np.abs(ref - gpu_logits[i]).max()))
+                match += int(np.array_equal(np.argmax(ref, -1), np.argmax(gpu_logits[i], -1)))
+                compared += 1
+            if time.perf_counter() - t_all > budget_s and len(times) >= 2:
+                done = True
+                break
+        passes += 1
+        if time.perf_counter() - t_all >= min_s:
+            done = True
     n = len(times)
     med = float(np.median(times))
     return ({"value": round(len(tok) / med, 3), "unit": "tokens/s", "cores": threads,
              "kind": "oracle", **host_info(),
-             "sample": f"{n} greedy decode steps of the same workload (numpy fp32 "
+             "sample": f"{n} decode steps ({passes} pass(es) over the {len(fed)} greedy steps of "
+                       f"the same workload, {sum(times):.1f} s of oracle steps; numpy fp32 "
                        f"oracle, weights decoded to fp32 once beforehand), median "
                        f"{med * 1e3:.1f} ms/step"},
-            {"max_abs_dlogit": worst, "greedy_match": f"{match}/{n}"})
+            {"max_abs_dlogit": worst, "greedy_match": f"{match}/{compared}"})
 
 
 def mfma_util(mc, t_step: float) -> dict:

@@ -65,3 +65,21 @@ def test_algorithmic_bytes_count_weights_once_per_step():
     assert eight - one == 7 * (2 * mc.hidden + kv_row * 2001)
     assert one - bench.algorithmic_bytes(mc, [1999]) == kv_row
     assert bench.algorithmic_bytes(mc, []) == mc.weight_bytes()
+
+
+def test_cpu_baseline_repeats_the_run_and_compares_the_first_pass():
+    """The oracle leg on the tiny shape, with the oracle's own tokens and
+    logits standing in for the GPU's: the first pass matches exactly, and
+    the run repeats until the minimum time is reached."""
+    import oracle as O
+    from persistent_interpreter_amd import synth
+    mc = synth.CONFIGS["tiny"].replace(steps=4)
+    W = synth.make_weights(mc)
+    kv0 = synth.make_kv_cache(mc, filled=mc.prior)
+    tok, pos = synth.make_tokens(mc), synth.make_positions(mc)
+    fed, lg = O.generate(mc, O.upcast_weights(W), tok, pos, kv0.copy(), 4)
+    cpu, parity = bench.cpu_baseline(mc, W, kv0, tok, pos, fed, lg, min_s=0.3, budget_s=5.0)
+    assert parity == {"max_abs_dlogit": 0.0, "greedy_match": "4/4"}
+    assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1
+    n = int(cpu["sample"].split()[0])
+    assert n >= 8 and n % 4 == 0            # whole passes over the 4 steps
