@@ -299,10 +299,13 @@ typedef struct mk_plan_report {
 /* mk_plan_check -- build the schedule for (cfg, batch) on `num_cus`
  * workgroups, validate it statically (every read is covered by a wait on
  * every writer of that data; counter targets match their producers) and run
- * `sim_runs` seeded interleavings of the per-CU queues that respect only the
- * counter waits (some adversarial: one CU delayed, stage-reversed
- * priorities), checking that every read sees its producers finished and that
- * no interleaving deadlocks; every unit's rows, heads, splits, row-table
+ * a static happens-before check (every read ordered after each of its
+ * writers by the counter waits and tagged reads, never by queue order: the
+ * waves of a workgroup pipeline across units), then `sim_runs` seeded
+ * interleavings of the per-CU queues that respect only the counter waits
+ * (some adversarial: one CU delayed, stage-reversed priorities), checking
+ * that every read sees its producers finished and that no interleaving
+ * deadlocks; every unit's rows, heads, splits, row-table
  * and wait entries and every recorded access must lie inside the buffers
  * they index.  `corrupt` != 0 deliberately breaks the plan (1: drop a
  * signal, 2: lower a wait target, 3: drop a wait, 4: move an attention unit

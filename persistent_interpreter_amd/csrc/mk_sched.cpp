@@ -16,6 +16,8 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <functional>
+#include <map>
 #include <random>
 
 #ifndef MK_XCDMAP
@@ -713,6 +715,102 @@ int check_plan(const mk_config &cfg, Plan &P, int sim_runs, int corrupt, uint64_
       if (cov < r.hi) fail("a read has elements no unit writes");
       (r.tagged ? rt : rw)[u].push_back({r.phase, std::move(ws)});
     }
+
+  // Happens-before, statically.  Inside a workgroup the roles pipeline: the
+  // sync wave stages unit u's inputs while the compute waves may still be on
+  // units u - 1 .. u - 3, so queue order orders nothing in global memory.
+  // What does: a counter wait (its group's target implies every producer of
+  // the group finished, and with it everything those producers waited for)
+  // and a tagged read (the writer's words are there, so the writer passed
+  // its own waits).  Every counter-guarded read must find each of its
+  // writers among the units its waits (before the read's piece) and its
+  // tagged reads imply.  (The interleavings below run each queue in order,
+  // so they cannot see a missing wait on a producer of the same workgroup.)
+  if (errors == 0) {
+    const size_t words = (NU + 63) / 64;
+    using Bits = std::vector<uint64_t>;
+    std::vector<std::vector<int>> prod(P.n_groups);
+    for (size_t u = 0; u < NU; ++u)
+      for (int g : sig[u]) prod[g].push_back((int)u);
+    std::vector<Bits> done_g(P.n_groups);
+    std::vector<char> state(P.n_groups, 0);  // 0 new, 1 in progress, 2 done
+    std::map<std::vector<int64_t>, Bits> pre_cache;
+    auto has = [](const Bits &b, size_t i) { return (b[i >> 6] >> (i & 63)) & 1; };
+    auto or_into = [](Bits &a, const Bits &b) {
+      for (size_t i = 0; i < a.size(); ++i) a[i] |= b[i];
+    };
+    bool cyclic = false;
+    std::function<const Bits &(int)> done_of;
+    // units finished once unit p can start its reads: its waits' groups and
+    // its tagged writers (each with what its own waits imply)
+    auto pre_of = [&](int p) -> const Bits & {
+      std::vector<int64_t> key;
+      for (auto &w : waits[p]) key.push_back(w.grp);
+      for (auto &rp : rt[p])
+        for (int t : rp.second) key.push_back(-1 - (int64_t)t);
+      std::sort(key.begin(), key.end());
+      key.erase(std::unique(key.begin(), key.end()), key.end());
+      auto it = pre_cache.find(key);
+      if (it != pre_cache.end()) return it->second;
+      Bits b(words, 0);
+      for (int64_t k : key) {
+        if (k >= 0) {
+          or_into(b, done_of((int)k));
+        } else {
+          const int t = (int)(-1 - k);
+          b[(size_t)t >> 6] |= 1ull << (t & 63);
+          for (auto &w : waits[t]) or_into(b, done_of((int)w.grp));
+        }
+      }
+      return pre_cache.emplace(key, std::move(b)).first->second;
+    };
+    // A group guarantees its producers (and what they waited for) only if
+    // its target counts every one of them.
+    done_of = [&](int g) -> const Bits & {
+      if (state[g] == 2) return done_g[g];
+      Bits b(words, 0);
+      if (state[g] == 1) {
+        cyclic = true;
+        done_g[g] = std::move(b);
+        return done_g[g];
+      }
+      state[g] = 1;
+      if (target[g] >= P.grp_producers[g])
+        for (int p : prod[g]) {
+          b[(size_t)p >> 6] |= 1ull << (p & 63);
+          or_into(b, pre_of(p));
+        }
+      done_g[g] = std::move(b);
+      state[g] = 2;
+      return done_g[g];
+    };
+    for (size_t u = 0; u < NU && errors == 0; ++u)
+      for (auto &rp : rw[u]) {
+        for (int wu : rp.second) {
+          if (wu == (int)u) continue;
+          bool ok = false;
+          for (auto &w : waits[u])
+            if (!ok && w.before_k <= rp.first && has(done_of((int)w.grp), (size_t)wu)) ok = true;
+          for (auto &tp : rt[u])
+            if (!ok && tp.first <= rp.first)
+              for (int t : tp.second) {
+                if (t == wu) ok = true;
+                for (auto &w : waits[t])
+                  if (!ok && has(done_of((int)w.grp), (size_t)wu)) ok = true;
+                if (ok) break;
+              }
+          if (!ok) {
+            char m[200];
+            std::snprintf(m, sizeof m, "unit %zu (op %d layer %d) reads data of unit %d (op %d) no wait orders",
+                          u, P.instr[u].op, P.instr[u].layer, wu, P.instr[wu].op);
+            fail(m);
+            break;
+          }
+        }
+        if (errors) break;
+      }
+    if (cyclic) fail("the counter waits form a cycle");
+  }
 
   // Phases of each unit: sorted distinct before_k values (always 0).
   std::vector<std::vector<uint32_t>> phases(NU);

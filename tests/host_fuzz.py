@@ -7,7 +7,10 @@ batches), the rest stay within what the kernels support.  Every case goes
 through mk_plan_check (with two simulated interleavings); an accepted plan
 must have no simulation error, mk_plan_units must give the same units and
 pages, and mk_addr_check (one-step launches or one launch of several steps)
-must find every access in bounds at random in-range positions and tokens.
+must find every access in bounds at random in-range positions and tokens;
+on about a third of the accepted plans a planted plan error (a dropped
+signal, a short counter target, a dropped wait, an attention split out of
+range) must be caught.
 A refused plan must be refused with an argument or shape error.
 
 The same cases run against the plain library and, in a child process,
@@ -74,6 +77,13 @@ def run(seed: int, cases: int) -> collections.Counter:
         assert len(units) == rep.n_instr and q[-1] == len(units), what
         assert all(a <= b for a, b in zip(q, q[1:])), what
         assert sum(u.pages for u in units) == rep.n_pages, what
+        if r.random() < 0.3:
+            # a planted plan error (dropped signal, short target, dropped
+            # wait, attention split out of range) must be caught
+            corrupt = r.randint(1, 4)
+            rcc, repc = B.plan_check(cfg, batch, cus, sim_runs=4, corrupt=corrupt, seed=i)
+            assert rcc != B.MK_OK and repc.msg, (corrupt, what)
+            out[f"corrupt{corrupt} caught"] += 1
         steps = r.randint(1, 3)
         if ms >= steps:
             pos = [r.randint(0, ms - steps) for _ in range(batch)]

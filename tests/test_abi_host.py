@@ -142,6 +142,20 @@ def test_corrupted_plans_are_caught(corrupt, seed):
     assert rep.sim_errors > 0 and rep.msg
 
 
+@pytest.mark.parametrize("corrupt", [1, 2, 3])
+@pytest.mark.parametrize("name,batch", [("tiny", 1), ("tiny", 3), ("llama1b", 1)])
+def test_plan_errors_in_one_workgroup_are_caught(name, batch, corrupt):
+    """On one workgroup every producer is in the consumer's own queue, which
+    the interleavings run in order; the static happens-before check must
+    still find the dropped signal, the short target or the dropped wait (the
+    kernel's roles pipeline, so queue order orders nothing in memory)."""
+    mc = synth.CONFIGS[name]
+    cfg = B.make_config(mc, max_batch=batch)
+    assert B.plan_check(cfg, batch, 1)[0] == B.MK_OK
+    rc, rep = B.plan_check(cfg, batch, 1, sim_runs=0, corrupt=corrupt, seed=3)
+    assert rc != B.MK_OK and b"no wait orders" in rep.msg, rep.msg
+
+
 @pytest.mark.parametrize("name", ["tiny", "llama1b", "tiny_qk", "llama70b"])
 def test_out_of_range_split_is_caught(name):
     """The extent check: an attention unit whose split index is one past
