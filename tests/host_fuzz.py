@@ -10,7 +10,8 @@ pages, and mk_addr_check (one-step launches or one launch of several steps)
 must find every access in bounds at random in-range positions and tokens;
 on about a third of the accepted plans a planted plan error (a dropped
 signal, a short counter target, a dropped wait, an attention split out of
-range) must be caught.
+range) must be caught, and on about a third a buffer one record short must
+be found by the address model.
 A refused plan must be refused with an argument or shape error.
 
 The same cases run against the plain library and, in a child process,
@@ -90,6 +91,20 @@ def run(seed: int, cases: int) -> collections.Counter:
             tok = [r.randrange(mc.vocab) for _ in range(batch)]
             rc2, rep2 = B.addr_check(cfg, batch, cus, steps, pos, tok, one_launch=r.random() < 0.5)
             assert rc2 == 0 and rep2.violations == 0, (rep2.msg, pos, steps, what)
+            if r.random() < 0.3:
+                # a buffer one record short (K/V cache, partials, RoPE table,
+                # q, h, logits) must be found by a run that reaches its last
+                # record: the last slots, and for the buffers sized by
+                # max_batch a step of max_batch sequences; a single split per
+                # KV head uses no partials
+                per_seq = (1, 2, 4, 5)
+                corrupt = r.choice([c for c in (1, 2, 3, 4, 5, 6)
+                                    if (c != 2 or rep.kv_splits > 1) and (c not in per_seq or mb == batch)])
+                last = [ms - steps] * batch
+                rc3, rep3 = B.addr_check(cfg, batch, cus, steps, last, [mc.vocab - 1] * batch,
+                                         corrupt=corrupt, one_launch=corrupt == 6)
+                assert rc3 != 0 and rep3.violations > 0, (corrupt, what)
+                out[f"short buffer {corrupt} found"] += 1
     return out
 
 
