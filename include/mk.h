@@ -363,7 +363,11 @@ typedef struct mk_addr_report {
  * residual rows, weight pieces and page sentinels, attention K/V rows and
  * the new slot, tagged q/K/V words, partials, reduction, epilogue stores,
  * greedy candidates, counters), per lane, with the kernel's own offset
- * arithmetic; every access must lie inside the buffer it addresses.  This is
+ * arithmetic; every access must lie inside the buffer it addresses, and
+ * every access a unit makes to an activation buffer (h, attention output,
+ * MLP activation, attention partials, tagged q/K/V) must fall in a read or
+ * write the plan records for that unit, the records mk_plan_check's
+ * dependency checks are made on.  This is
  * the gate every new kernel path passes before it runs on a GPU (the
  * megakernel chapter "Quand ne pas le faire", section 9.3: an error of this
  * kind shows as a rare wrong token or a fault, not as a failed assertion).
@@ -373,9 +377,12 @@ typedef struct mk_addr_report {
  *             cache's last slot, 2: the last attention partial, 3: the last
  *             RoPE row, 4: the last q head, 5: the final residual row, 6:
  *             the last sequence's logits row), so a run that reaches that
- *             record must report it.
- * Returns MK_OK if no access falls outside its buffer, MK_ERR_INVALID_ARG
- * (rep->msg names the first) otherwise, or the plan's own error.  Host only. */
+ *             record must report it; or a planted record error: the plan
+ *             forgets the first FFN unit's residual read (7) or the first
+ *             attention unit's tagged q/K/V read (8).
+ * Returns MK_OK if every access is in its buffer and recorded,
+ * MK_ERR_INVALID_ARG (rep->msg names the first) otherwise, or the plan's own
+ * error.  Host only. */
 int mk_addr_check(const mk_config *cfg, int32_t batch, int32_t num_cus,
                   int32_t steps, const int32_t *positions,
                   const int32_t *tokens, int32_t corrupt,

@@ -41,6 +41,118 @@ struct Model {
   int bad = 0;
   std::string first;
 
+  // Dependency records: every access of the unit being walked (`unit`, -1
+  // outside units) to an activation buffer must fall in a range the plan
+  // recorded as that unit's read or write, since the plan checker orders
+  // exactly the recorded accesses.  The split-K partial rows after the
+  // attention partials are private to a down-projection group and are not
+  // recorded.
+  int unit = -1;
+  const Plan *plan = nullptr;
+  uint64_t id_h = 0, id_attn = 0, id_a = 0, id_part = 0, id_q = 0, id_kvn = 0;
+  uint64_t MB = 1, H = 1, nq = 1, hd = 1, F = 1, nkv = 1, ns = 1, G = 1, half = 1, ppg = 1, part_elems = 0;
+  int64_t meta_n = 0;
+
+  // the record found last and the absolute element interval of this
+  // buffer it covers around the element asked for (accesses of one unit
+  // mostly fall in the interval found just before)
+  int c_unit = -1;
+  uint64_t c_id = 0, c_lo = 0, c_hi = 0;
+
+  const Access *find(uint8_t res, uint64_t layer, uint64_t b, uint64_t x) const {
+    for (const auto *lst : {&plan->reads[unit], &plan->writes[unit]})
+      for (const Access &r : *lst)
+        if (r.res == res && r.layer == layer && r.b == b && r.lo <= x && x < r.hi) return &r;
+    return nullptr;
+  }
+  // element e of buffer `id`: recorded for the current unit?  On success
+  // [lo, hi) is an interval of elements around e that the same record covers
+  bool covered(uint64_t id, uint64_t e, uint64_t &lo, uint64_t &hi) const {
+    lo = e;
+    hi = e + 1;
+    if (id == id_h) {
+      const uint64_t idx = e / (MB * H), b = (e / H) % MB, base = (idx * MB + b) * H;
+      if (idx == 0) return false;  // the embedding's slot: never read or written as h
+      const Access *r = (idx & 1) ? find(R_HMID, (idx - 1) / 2, b, e - base) : find(R_HOUT, idx / 2 - 1, b, e - base);
+      if (!r) return false;
+      lo = base + r->lo;
+      hi = base + r->hi;
+      return true;
+    }
+    if (id == id_attn || id == id_a) {
+      const uint64_t row = id == id_attn ? nq * hd : F, lb = e / row, base = lb * row;
+      const Access *r = find(id == id_attn ? R_ATTN : R_A, lb / MB, lb % MB, e - base);
+      if (!r) return false;
+      lo = base + r->lo;
+      hi = base + r->hi;
+      return true;
+    }
+    if (id == id_part) {
+      if (e >= part_elems) {  // split-K partial rows: private to their group
+        lo = part_elems;
+        hi = ~0ull;
+        return true;
+      }
+      const uint64_t rec = e / (hd + 4), s = rec % ns, j = (rec / ns) % nq, lb = rec / (ns * nq);
+      if (!find(R_PART, lb / MB, lb % MB, (j / G) * ns + s)) return false;
+      lo = rec * (hd + 4);
+      hi = lo + hd + 4;
+      return true;
+    }
+    // tagged q or this step's K/V words: QKV row pairs (i, i + hd/2) of a KV
+    // head's group (its G query heads, then K, then V)
+    uint64_t head, lb, pair0;
+    if (id == id_q) {
+      head = e / hd;
+      const uint64_t j = head % nq;
+      lb = head / nq;
+      pair0 = (j / G) * ppg + (j % G) * half;
+    } else {
+      head = e / hd;  // (l, b, g, t) flattened
+      const uint64_t t = head % 2, g = (head / 2) % nkv;
+      lb = head / (2 * nkv);
+      pair0 = g * ppg + (G + t) * half;
+    }
+    const uint64_t x = pair0 + (e % hd) % half;
+    const Access *r = find(R_QKV, lb / MB, lb % MB, x);
+    if (!r) return false;
+    if (r->lo <= pair0 && pair0 + half <= r->hi) {  // the whole head
+      lo = head * hd;
+      hi = lo + hd;
+    }
+    return true;
+  }
+  void meta(uint64_t id, uint64_t off, uint32_t bytes, const char *site) {
+    uint64_t es;
+    if (id == id_h || id == id_attn || id == id_a || id == id_part) es = 4;
+    else if (id == id_q || id == id_kvn) es = 8;
+    else return;
+    const uint64_t e0 = off / es, e1 = (off + bytes - 1) / es;
+    ++meta_n;
+    if (c_unit == unit && c_id == id && c_lo <= e0 && e1 < c_hi) return;
+    // the first and the last element (the records are ranges of elements,
+    // so an access whose ends are covered by one record is covered)
+    uint64_t lo, hi, lo1, hi1;
+    const bool ok0 = covered(id, e0, lo, hi);
+    const bool ok1 = ok0 && (e1 < hi || covered(id, e1, lo1, hi1));
+    if (ok0 && ok1) {
+      c_unit = unit;
+      c_id = id;
+      c_lo = lo;
+      c_hi = hi;
+      return;
+    }
+    if (first.empty()) {
+      char m[256];
+      std::snprintf(m, sizeof m, "%s: unit %d (op %d layer %d) touches %s element %llu, which the plan "
+                    "does not record for it", site, unit, (int)plan->instr[unit].op,
+                    (int)plan->instr[unit].layer, bufs[id - 1].name.c_str(),
+                    (unsigned long long)(ok0 ? e1 : e0));
+      first = m;
+    }
+    ++bad;
+  }
+
   uint64_t add(const std::string &name, uint64_t bytes) {
     bufs.push_back({name, bytes});
     return (uint64_t)bufs.size() << kShift;
@@ -53,6 +165,7 @@ struct Model {
     const uint64_t id = addr >> kShift, off = addr & ((1ull << kShift) - 1);
     const bool in = id >= 1 && id <= bufs.size() && off + bytes <= bufs[id - 1].bytes &&
                     (want == 0 || (want >> kShift) == id);
+    if (in && unit >= 0 && plan) meta(id, off, bytes, site);
     if (!in) {
       if (first.empty()) {
         char m[256];
@@ -191,6 +304,7 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
     }
   };
   for (int cu = 0; cu < num_cus; ++cu) {
+    M.unit = -1;
     const uint32_t q0 = P.q_off[cu], q1 = P.q_off[cu + 1];
     // ---- sync wave (sync_role_b: staging pipeline)
     for (int b = 0; b < batch; ++b) {
@@ -200,6 +314,7 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
     if (inputs_ok)
       for (uint32_t qi = q0; qi < q1; ++qi) {
         const Instr &d = P.instr[qi];
+        M.unit = (int)qi;
         const bool gv = is_gemv(d.op);
         const uint32_t nx = gv ? d.nk : 1;
         const bool normed = d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM;
@@ -265,6 +380,7 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
     uint32_t n = 0;
     for (uint32_t qi = q0; qi < q1; ++qi) {
       const Instr &d = P.instr[qi];
+      M.unit = (int)qi;
       if (d.op == OP_ATTN && d.ppp) {
         paged_kv_loads(M, B, P, c, d, pos[d.b], n);
         continue;
@@ -307,6 +423,7 @@ static void walk_batched(Model &M, const Bases &B, const Plan &P, const mk_confi
     if (!inputs_ok) continue;
     for (uint32_t qi = q0; qi < q1; ++qi) {
       const Instr &d = P.instr[qi];
+      M.unit = (int)qi;
       const int b0 = (int)d.b;
       if (d.op == OP_ATTN && d.ppp) {
         paged_attn_compute(M, B, P, c, d, pos[b0]);
@@ -504,6 +621,15 @@ static int addr_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int3
     if (rep) std::snprintf(rep->msg, sizeof rep->msg, "the plan fails its static checks");
     return MK_ERR_UNSUPPORTED;
   }
+  // planted record errors: the plan forgets one read of the first FFN unit
+  // (its residual input, 7) or of the first attention unit (its tagged q/K/V,
+  // 8), which the walk must then report
+  if (corrupt == 7 || corrupt == 8)
+    for (size_t u = 0; u < P.instr.size(); ++u)
+      if (P.instr[u].op == (corrupt == 7 ? OP_FFN : OP_ATTN) && !P.reads[u].empty()) {
+        P.reads[u].erase(P.reads[u].begin());
+        break;
+      }
   B.tokens = M.add("tokens", (uint64_t)batch * 4);
   B.positions = M.add("positions", (uint64_t)batch * 4);
   // planted size errors for the model's self-tests: one record short
@@ -523,6 +649,17 @@ static int addr_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int3
   B.part = M.add("partials", (lay::part_size(L, MB, nq, ns, hd) +
                               (P.down_splits ? lay::dpart_size(L, P.down_splits, H, MB) : 0)) * 4 - short_part);
   B.rope = M.add("rope", lay::rope_size(S, hd) * 4 - short_rope);
+  M.plan = &P;
+  M.id_h = B.h >> kShift;
+  M.id_q = B.q >> kShift;
+  M.id_kvn = B.kvn >> kShift;
+  M.id_attn = B.attn >> kShift;
+  M.id_a = B.a >> kShift;
+  M.id_part = B.part >> kShift;
+  M.MB = (uint64_t)MB; M.H = (uint64_t)H; M.nq = (uint64_t)nq; M.hd = (uint64_t)hd; M.F = (uint64_t)F;
+  M.nkv = (uint64_t)nkv; M.ns = (uint64_t)ns; M.G = (uint64_t)G; M.half = (uint64_t)half;
+  M.ppg = (uint64_t)(G + 2) * half;
+  M.part_elems = lay::part_size(L, MB, nq, ns, hd);
   B.status = M.add("status", 256);
   const uint64_t amax_word = (uint64_t)P.n_groups * kSlots * kCtrStride;
   B.ctr = M.add("counters", (amax_word + kCtrStride + (uint64_t)P.n_down_groups) * 4);
@@ -530,6 +667,7 @@ static int addr_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int3
   uint32_t n_lm = 0, max_pages = 0;
   for (const Instr &in : P.instr) n_lm += in.op == OP_LM;
   for (int cu = 0; cu < num_cus; ++cu) {
+    M.unit = -1;
     uint32_t np = 0;
     for (uint32_t qi = P.q_off[cu]; qi < P.q_off[cu + 1]; ++qi) {
       const Instr &in = P.instr[qi];
@@ -562,6 +700,7 @@ static int addr_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int3
       continue;
     }
     for (int cu = 0; cu < num_cus; ++cu) {
+      M.unit = -1;
       const uint32_t q0 = P.q_off[cu], q1 = P.q_off[cu + 1];
       // ---- sync wave ----------------------------------------------------
       for (int b = 0; b < batch; ++b) {
@@ -571,6 +710,7 @@ static int addr_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int3
       if (inputs_ok)
         for (uint32_t qi = q0; qi < q1; ++qi) {
           const Instr &d = P.instr[qi];
+          M.unit = (int)qi;
           const bool gv = d.op == OP_QKV || d.op == OP_O || d.op == OP_FFN || d.op == OP_DOWN || d.op == OP_LM;
           const uint32_t nx = gv ? d.nk : 1;
           const bool normed = d.op == OP_QKV || d.op == OP_FFN || d.op == OP_LM;
@@ -666,6 +806,7 @@ static int addr_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int3
       uint32_t n = 0;
       for (uint32_t qi = q0; qi < q1; ++qi) {
         const Instr &d = P.instr[qi];
+        M.unit = (int)qi;
         if (d.op == OP_ATTN && d.ppp) {
           paged_kv_loads(M, B, P, c, d, pos0, n);
           continue;
@@ -730,6 +871,7 @@ static int addr_check(const mk_config *cfg, int32_t batch, int32_t num_cus, int3
       if (!inputs_ok) continue;
       for (uint32_t qi = q0; qi < q1; ++qi) {
         const Instr &d = P.instr[qi];
+        M.unit = (int)qi;
         const int b = (int)d.b;
         if (d.op == OP_ATTN && d.ppp) {
           paged_attn_compute(M, B, P, c, d, pos0);

@@ -114,3 +114,21 @@ def test_launch_logits_blocks_are_modelled(batch):
     rc, rep = B.addr_check(cfg, batch, CUS, 3, pos, tok, one_launch=True)
     assert rc == 0, rep.msg.decode()
 
+
+
+@pytest.mark.parametrize("name,batch", [("tiny", 1), ("tiny_qk", 1), ("tiny", 3)])
+@pytest.mark.parametrize("corrupt,sites", [(7, ("residual", "staged activation")), (8, ("tagged q",))])
+def test_accesses_the_plan_does_not_record_are_found(name, batch, corrupt, sites):
+    """The walk also checks every access to an activation buffer against the
+    reads and writes the plan records for the unit (what the plan checker's
+    dependency analysis sees): a plan that forgets the first FFN unit's
+    residual read (7) or the first attention unit's tagged q/K/V read (8)
+    must be reported where the kernel makes that access."""
+    mc = synth.CONFIGS[name]
+    if batch > 1:
+        mc = mc.replace(batch=batch, pos_lo=4, pos_hi=40)
+    cfg = B.make_config(mc, max_batch=batch)
+    rc, rep = B.addr_check(cfg, batch, CUS, 1, synth.make_positions(mc, batch), synth.make_tokens(mc, batch),
+                           corrupt=corrupt)
+    msg = rep.msg.decode()
+    assert rc != 0 and "does not record" in msg and any(x in msg for x in sites), msg
