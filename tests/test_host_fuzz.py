@@ -16,8 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 @pytest.mark.parametrize("seed", [1, 2])
 def test_random_shapes_plan_and_stay_in_bounds(seed):
-    res = host_fuzz.run(seed, 80)
-    assert res[B.MK_OK] >= 40 and res[B.MK_ERR_INVALID_ARG] > 0
+    res = host_fuzz.run(seed, 60)
+    assert res[B.MK_OK] >= 30 and res[B.MK_ERR_INVALID_ARG] > 0
 
 
 def test_random_shapes_under_host_sanitizers(tmp_path):
@@ -28,7 +28,7 @@ def test_random_shapes_under_host_sanitizers(tmp_path):
     env = dict(os.environ, MK_LIB_PATH=lib, LD_PRELOAD=pre,
                ASAN_OPTIONS="detect_leaks=0:halt_on_error=1",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
-    r = subprocess.run([sys.executable, os.path.join(HERE, "host_fuzz.py"), "3", "40"], env=env,
+    r = subprocess.run([sys.executable, os.path.join(HERE, "host_fuzz.py"), "3", "30"], env=env,
                        stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=900)
     assert r.returncode == 0 and "clean" in r.stdout, r.stdout[-4000:]
     assert "ERROR: AddressSanitizer" not in r.stdout and "runtime error" not in r.stdout
