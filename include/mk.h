@@ -305,12 +305,13 @@ typedef struct mk_plan_report {
  * interleavings of the per-CU queues that respect only the counter waits
  * (some adversarial: one CU delayed, stage-reversed priorities), checking
  * that every read sees its producers finished and that no interleaving
- * deadlocks; every unit's rows, heads, splits, row-table
+ * deadlocks; no two units write the same elements; every unit's rows,
+ * heads, splits, row-table
  * and wait entries and every recorded access must lie inside the buffers
  * they index.  `corrupt` != 0 deliberately breaks the plan (1: drop a
  * signal, 2: lower a wait target, 3: drop a wait, 4: move an attention unit
- * one split past the last) so tests can check that the validator catches
- * it.  Host only; no GPU needed.
+ * one split past the last, 5: let two units write the same rows) so tests
+ * can check that the validator catches it.  Host only; no GPU needed.
  * Returns MK_OK if the plan is valid, MK_ERR_UNSUPPORTED for shapes the
  * decomposition rejects, MK_ERR_INVALID_ARG otherwise; rep is filled. */
 int mk_plan_check(const mk_config *cfg, int32_t batch, int32_t num_cus,

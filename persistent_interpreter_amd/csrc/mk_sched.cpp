@@ -716,6 +716,45 @@ int check_plan(const mk_config &cfg, Plan &P, int sim_runs, int corrupt, uint64_
       (r.tagged ? rt : rw)[u].push_back({r.phase, std::move(ws)});
     }
 
+  // Every element has one writer: two units writing the same activation
+  // elements would leave the step's result to whichever finished last.  (The
+  // units of a split-K down group record the group's rows each; the group's
+  // last arrival writes them once.)
+  {
+    if (corrupt == 5)  // self-test: one O unit's rows grow into the next O unit's
+      for (size_t u = 0; u + 1 < NU; ++u)
+        if (P.instr[u].op == OP_O && !P.writes[u].empty()) {
+          bool grown = false;
+          for (size_t v = u + 1; v < NU && !grown; ++v)
+            if (P.instr[v].op == OP_O && P.instr[v].layer == P.instr[u].layer)
+              for (auto &w : P.writes[v])
+                if (key_of(w) == key_of(P.writes[u][0]) && w.lo >= P.writes[u][0].hi) {
+                  P.writes[u][0].hi = w.lo + 1;
+                  grown = true;
+                  break;
+                }
+          if (grown) break;
+        }
+    auto one_writer = [&](int x, int y) {
+      const Instr &a = P.instr[x], &b = P.instr[y];
+      return x == y || (a.op == OP_DOWN && b.op == OP_DOWN && lay::split_n(a.aux1) > 1 &&
+                        lay::split_n(b.aux1) > 1 && lay::split_group(a.aux1) == lay::split_group(b.aux1));
+    };
+    std::vector<std::pair<std::pair<uint64_t, uint32_t>, std::pair<uint32_t, int>>> ws;  // (key, lo) -> (hi, unit)
+    for (size_t u = 0; u < NU; ++u)
+      for (auto &w : P.writes[u]) ws.push_back({{key_of(w), w.lo}, {w.hi, (int)u}});
+    std::sort(ws.begin(), ws.end());
+    for (size_t i = 1; i < ws.size(); ++i)
+      if (ws[i].first.first == ws[i - 1].first.first && ws[i].first.second < ws[i - 1].second.first &&
+          !one_writer(ws[i].second.second, ws[i - 1].second.second)) {
+        char m[200];
+        std::snprintf(m, sizeof m, "units %d and %d (op %d, %d) write the same elements", ws[i - 1].second.second,
+                      ws[i].second.second, P.instr[ws[i - 1].second.second].op, P.instr[ws[i].second.second].op);
+        fail(m);
+        break;
+      }
+  }
+
   // Happens-before, statically.  Inside a workgroup the roles pipeline: the
   // sync wave stages unit u's inputs while the compute waves may still be on
   // units u - 1 .. u - 3, so queue order orders nothing in global memory.

@@ -156,6 +156,19 @@ def test_plan_errors_in_one_workgroup_are_caught(name, batch, corrupt):
     assert rc != B.MK_OK and b"no wait orders" in rep.msg, rep.msg
 
 
+@pytest.mark.parametrize("name,batch,cus", [("tiny", 1, 256), ("tiny", 3, 3), ("llama1b", 1, 256),
+                                           ("llama1b_b8", 8, 256)])
+def test_two_writers_of_the_same_rows_are_caught(name, batch, cus):
+    """One O unit's rows grown into the next O unit's: every activation
+    element must have exactly one writer (a split-K down group counts as one,
+    its last arrival writing the rows)."""
+    mc = synth.CONFIGS[name]
+    cfg = B.make_config(mc, max_batch=batch)
+    assert B.plan_check(cfg, batch, cus)[0] == B.MK_OK
+    rc, rep = B.plan_check(cfg, batch, cus, corrupt=5)
+    assert rc != B.MK_OK and b"write the same elements" in rep.msg, rep.msg
+
+
 @pytest.mark.parametrize("name", ["tiny", "llama1b", "tiny_qk", "llama70b"])
 def test_out_of_range_split_is_caught(name):
     """The extent check: an attention unit whose split index is one past
