@@ -1,8 +1,10 @@
-"""A host model of what happens inside one workgroup of the batch-1 decode
-kernel: the ordering between its 3 loader waves, its sync wave and its 8
+"""A host model of what happens inside one workgroup of the decode kernels
+(`simulate`: batch 1; `simulate_batched`: the MFMA kernel for 2 to 8
+sequences): the ordering between its 3 loader waves, its sync wave and its 8
 compute waves, through the LDS words they share, over a real queue of the
 library's schedule (mk_plan_units), under random schedules with long random
-stalls of single waves.
+stalls of single waves.  The description below is the batch-1 kernel's;
+`simulate_batched` says how the batched one differs.
 
 What it models, wave by wave (the kernel's LDS protocol, not its
 arithmetic):
