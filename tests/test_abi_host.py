@@ -256,3 +256,22 @@ def test_binding_signatures_match_the_header():
                 size, signed = _SCALARS[p.split()[0]]
                 assert C.sizeof(t) == size, (name, p, t)
                 assert (t(-1).value < 0) == signed, (name, p, t)
+
+
+def test_plan_units_count_only_and_partial_fill():
+    """mk_plan_units: with no array it returns the count; with a short array
+    it fills that many entries, leaves the rest alone and still returns the
+    full count; bad arguments are refused."""
+    L = B.lib()
+    cfg = B.make_config(synth.CONFIGS["tiny"])
+    n = L.mk_plan_units(C.byref(cfg), 1, 16, None, 0, None)
+    assert n > 0
+    units = (B.MkUnitInfo * 8)()
+    for u in units:
+        u.op = -7
+    assert L.mk_plan_units(C.byref(cfg), 1, 16, units, 5, None) == n
+    assert all(units[i].op in range(1, 8) for i in range(5))
+    assert all(units[i].op == -7 for i in range(5, 8))
+    assert L.mk_plan_units(C.byref(cfg), 1, 16, None, 5, None) == B.MK_ERR_INVALID_ARG
+    assert L.mk_plan_units(C.byref(cfg), 0, 16, None, 0, None) == B.MK_ERR_INVALID_ARG
+    assert L.mk_plan_units(None, 1, 16, None, 0, None) == B.MK_ERR_INVALID_ARG
