@@ -121,3 +121,23 @@ def test_struct_layouts_match_the_binding(tmp_path):
         for f, _ in py._fields_:
             d = getattr(py, f)
             assert got[f"{cname}.{f}"] == (d.offset, d.size), (cname, f)
+
+
+def test_readme_c_example_compiles(tmp_path):
+    """The C usage example of the README compiles against the header as
+    strict C99 and links against the library."""
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    import re
+    text = open(os.path.join(ROOT, "README.md")).read()
+    m = re.search(r"<!-- c-example -->\s*```c\n(.*?)```\s*<!-- /c-example -->", text, flags=re.S)
+    assert m, "the README has no C example"
+    src = tmp_path / "example.c"
+    src.write_text(m.group(1) + "\nint main(void) { return 0; }\n")
+    lib_dir = os.path.dirname(os.path.abspath(B.LIB_PATH))
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I",
+                        os.path.join(ROOT, "include"), str(src), "-o", str(tmp_path / "example"),
+                        B.LIB_PATH, f"-Wl,-rpath,{lib_dir}"],
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout
